@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the block-diffusion denoise loop on one MI355X.
+
+One timed "step" is one whole canvas: dg_canvas_init followed by
+dg_generate_canvas, i.e. denoise steps (forward over every layer, fused LM head
+with entropy/argmax, commit, re-noise) until the canvas is committed or the
+48-step cap is reached.  Inputs (weights, prompt KV cache) are synthetic,
+seeded, and resident in HBM before the timed region starts.
+
+Prints one JSON line: canvas tokens/s (value), denoise steps/s, the roofline
+fraction of the dominant kernel (timed live with HIP events on its own stream
+inside the timed region), and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "canvas tokens/s & denoise steps/s, bs=1 256-tok canvas; % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, kernel: str):
+    """(bytes, flops) one launch of `kernel` must move/perform, per layer and step."""
+    T = cfg.batch * cfg.canvas_len
+    d, E, k, de, ds = cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_expert, cfg.d_shared
+    wb = 1 if cfg.expert_dtype == "fp8" else 2
+    ab = 2 if cfg.act_dtype == "bf16" else 4
+    if kernel == "moe_gateup":
+        w = E * 2 * de * d * wb + (E * 2 * de * 4 if wb == 1 else 0)
+        return w + T * d * ab + T * k * de * ab, 2.0 * T * k * 2 * de * d
+    if kernel == "moe_down":
+        w = E * d * de * wb + (E * d * 4 if wb == 1 else 0)
+        return w + T * k * de * ab + T * k * d * 4, 2.0 * T * k * de * d
+    if kernel == "lm_head":
+        return cfg.vocab * d * ab + T * d * ab, 2.0 * T * cfg.vocab * d
+    if kernel == "attn":
+        keys = cfg.prompt_len + cfg.canvas_len
+        A = cfg.attn_dim
+        return (cfg.batch * keys * A * 2 * ab + 2 * T * A * ab,
+                4.0 * cfg.batch * cfg.canvas_len * keys * A)
+    raise ValueError(kernel)
+
+
+def cpu_baseline(inp, cfg, steps_per_canvas: float, layers: int):
+    """Oracle time for a sampled step: `layers` layers + LM head + commit,
+    extrapolated to a full step and a full canvas."""
+    import numpy as np
+
+    from oracle import model as om
+
+    cores = len(os.sched_getaffinity(0))
+    W = om.Weights(inp)
+    kv = om.KV(inp.kv_k[:layers], inp.kv_v[:layers], inp.kv_len, bf16=cfg.act_dtype == "bf16")
+    st = om.init_state(cfg, cfg.seed)
+    prec = om.Prec(cfg.act_dtype)
+    t0 = time.perf_counter()
+    x = prec.act(W.embed_rows(st.tokens[0]))
+    for l in range(layers):
+        kvk, kvv = kv.get(l, 0)
+        x, _, _ = om.layer_forward(x, W, l, kvk, kvv, kv.length, prec, cfg)
+    t1 = time.perf_counter()
+    hf = prec.act(om.rmsnorm(x, cfg.rms_eps))
+    z = om.lm_head_logits(hf, W)
+    H, a, _ = om.confidence(z)
+    om.commit_select(H, a, st.tokens[0].copy(), st.committed[0].copy(), 0, cfg.max_steps,
+                     cfg.threshold)
+    t2 = time.perf_counter()
+    per_layer = (t1 - t0) / layers
+    t_step = per_layer * cfg.n_layers + (t2 - t1)
+    t_canvas = t_step * steps_per_canvas
+    return {
+        "value": cfg.canvas_len / t_canvas,  # the oracle runs one canvas at a time
+        "unit": "canvas tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{layers} of {cfg.n_layers} layers + LM head + commit of one denoise step of "
+                   f"canvas 0 ({t2 - t0:.1f} s measured); extrapolated x{cfg.n_layers}/{layers} "
+                   f"layers and x{steps_per_canvas:g} steps per canvas"),
+        "seconds_per_step": t_step,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3, help="timed canvases")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed canvases")
+    ap.add_argument("--config", default="c2", help="c2 (batch 1) or c3 (batch 4)")
+    ap.add_argument("--kernel", default="moe_gateup",
+                    help="kernel class timed for the roofline (moe_gateup, moe_down, lm_head, attn)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--breakdown", action="store_true",
+                    help="after the timed region, time every kernel class (stderr)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).")
+        print(msg, file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from diffusion_decoding_amd import _lib
+    from diffusion_decoding_amd import runtime as rt
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(args.config)
+    if cfg.prompt_mode != "kv":
+        raise SystemExit("bench.py times the denoise loop over a given prompt KV cache (c2, c3)")
+    torch.cuda.set_device(0)
+    log(f"[bench] generating inputs for {cfg.name} on the GPU")
+    inp = make_inputs(cfg, device="cuda")
+    torch.cuda.synchronize()
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k, inp.kv_v, inp.kv_len)
+    B, N = cfg.batch, cfg.canvas_len
+    canvas = rt.Canvas.empty(B, N, cfg.seed)
+
+    for w in range(args.warmup):
+        rt.canvas_init(model, canvas)
+        n = rt.generate_canvas(model, canvas, kv)
+        log(f"[bench] warmup canvas {w}: {n} steps")
+    torch.cuda.synchronize()
+
+    _lib.dg_profile_kernel(model.handle, _lib.DG_PROF[args.kernel])
+    total_steps = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        rt.canvas_init(model, canvas)
+        total_steps += rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof_ms, launches = _lib.dg_profile_read(model.handle)
+    _lib.dg_profile_kernel(model.handle, 0)
+    elapsed = t1 - t0
+    log(f"[bench] {args.steps} canvases, {total_steps} denoise steps in {elapsed:.3f} s")
+
+    bytes_, flops = algorithmic(cfg, args.kernel)
+    avg_s = prof_ms / 1e3 / max(launches, 1)
+    if args.kernel in ("lm_head",):
+        bound, achieved, peak, unit = "mfma", flops / avg_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", bytes_ / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": None, "kernel": args.kernel,
+                "avg_launch_us": avg_s * 1e6, "launches": launches,
+                "algorithmic_bytes_per_launch": bytes_, "algorithmic_flops_per_launch": flops}
+
+    steps_per_canvas = total_steps / args.steps
+    out = {
+        "metric": METRIC,
+        "value": B * N * args.steps / elapsed,
+        "unit": "canvas tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act_dtype if cfg.expert_dtype != "fp8" else "bf16+fp8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "batch": B, "canvas": N,
+                   "prompt_kv": cfg.prompt_len, "experts": f"{cfg.n_experts} top-{cfg.top_k} + shared",
+                   "d_model": cfg.d_model, "vocab": cfg.vocab,
+                   "denoise_steps_per_canvas": steps_per_canvas},
+        "denoise_steps_per_s": total_steps / elapsed,
+        "ms_per_denoise_step": elapsed / total_steps * 1e3,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if args.breakdown:
+        for name in ("attn", "qkv", "router", "moe_gateup", "moe_down", "shared", "lm_head", "commit"):
+            _lib.dg_profile_kernel(model.handle, _lib.DG_PROF[name])
+            rt.canvas_init(model, canvas)
+            n = rt.generate_canvas(model, canvas, kv)
+            ms, cnt = _lib.dg_profile_read(model.handle)
+            log(f"[breakdown] {name:11s} {ms / n:8.3f} ms/step  {ms / max(cnt, 1) * 1e3:9.1f} us/launch "
+                f"({cnt} launches)")
+        _lib.dg_profile_kernel(model.handle, 0)
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sampled step")
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, steps_per_canvas, max(1, min(args.cpu_layers, cfg.n_layers)))
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

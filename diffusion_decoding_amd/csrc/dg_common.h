@@ -1,0 +1,125 @@
+// Shared device helpers for the gfx950 kernels: element types, conversions,
+// MFMA fragment wrappers, wave reductions and the Philox4x32-10 generator.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// ---------------------------------------------------------------------------- element types
+
+// bfloat16 kept as its raw 16 bits.
+struct bf16 {
+  uint16_t v;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.v) << 16); }
+
+// binary32 -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{uint16_t((u >> 16) | 0x40)};
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16{uint16_t(u >> 16)};
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { return f32_to_bf16(f); }
+
+// Round a binary32 value to the storage precision of T and back.
+template <typename T> __device__ __forceinline__ float round_to(float f) {
+  return to_f32(from_f32<T>(f));
+}
+
+// OCP E4M3FN code -> bfloat16 bits (exact: 3 mantissa bits fit in 7).
+// Normal codes map exponent e (bias 7) to e + 120 (bias 127); subnormal codes
+// (exponent field 0) encode m * 2^-9 and are rebuilt from their integer m.
+// The NaN codes (S.1111.111) map to a bf16 NaN.
+__device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 8;
+  uint32_t em = c & 0x7fu;
+  uint32_t normal = (em << 4) + (120u << 7);
+  uint32_t sub = __float_as_uint(float(em) * 0x1p-9f) >> 16;   // exact for em < 8
+  uint32_t r = (em >= 8u) ? normal : sub;
+  if (em == 0x7fu) r = 0x7fc0u;
+  return uint16_t(s | r);
+}
+
+// ---------------------------------------------------------------------------- vector types
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ---------------------------------------------------------------------------- MFMA
+
+// D = A(16x32) * B(32x16) + C on one wave; lane l supplies row/col (l % 16)
+// and k-slots 8*(l/16)..8*(l/16)+7 of its operand; D lane l holds column
+// (l % 16), rows 4*(l/16)+0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// fp32 variant: A(16x4) * B(4x16); lane l supplies row/col (l % 16), k-slot l/16.
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------- Philox4x32-10
+
+// Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011):
+// ten rounds; each multiplies words 0 and 2 by M0/M1, mixes the product
+// halves with words 1 and 3 and the round key; the key advances by W0/W1.
+struct u32x4s {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4s philox4x32_10(u32x4s c, uint32_t k0, uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
+    uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+    c = u32x4s{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+// Token draw for a canvas position: word 0 of counter (pos, tag, canvas, block).
+__device__ __forceinline__ uint32_t canvas_draw(uint64_t seed, uint32_t pos, uint32_t tag,
+                                                uint32_t canvas, uint32_t block, uint32_t vocab) {
+  u32x4s r = philox4x32_10(u32x4s{pos, tag, canvas, block}, uint32_t(seed), uint32_t(seed >> 32));
+  return vocab ? r.x % vocab : r.x;
+}
+
+}  // namespace dg

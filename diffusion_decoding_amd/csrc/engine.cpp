@@ -1,0 +1,540 @@
+// Step engine and C ABI of the block-diffusion denoise library.
+//
+// One denoise step (DiffusionGemma解析, "换个路数：整片并行去噪的生成机制"; ipcmen.com,
+// "工作原理：并行精炼与自我修正"): embed the canvas, run every layer with
+// bidirectional attention over [prompt KV ; canvas KV] and the routed + shared
+// expert FFN (zhichai.net 深度拆解, "MoE 效率"), apply the final RMSNorm, score
+// every position with the fused LM head (entropy + argmax), commit, re-noise.
+// The causal commit pass appends a finished canvas to the KV cache
+// (zhichai.net 深度拆解, "Block-Autoregressive").  All workspace is allocated
+// once at model creation; steps allocate nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "kernels.h"
+
+using namespace dg;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+#define HIP_OK(expr)                                                                        \
+  do {                                                                                      \
+    int _e = int(expr);                                                                     \
+    if (_e) return fail(DG_ERR_HIP, "%s failed: %s (%d)", #expr,                           \
+                        hipGetErrorString(hipError_t(_e)), _e);                             \
+  } while (0)
+
+}  // namespace
+
+struct dg_model {
+  dg_config cfg{};
+  std::vector<dg_layer_weights> layers;
+  const void* embed = nullptr;
+  const void* lm_head = nullptr;
+  int max_batch = 0, max_tokens = 0, max_kv = 0;
+  int Tmax = 0;  // max_batch * max(max_tokens, canvas_len)
+  size_t esz = 0;
+  ActType at = ACT_BF16;
+  WType wt = W_BF16;
+  std::vector<void*> allocs;
+  // workspace
+  void *x = nullptr, *a = nullptr, *qkv = nullptr, *q = nullptr, *kc = nullptr, *vc = nullptr,
+       *o = nullptr, *h = nullptr, *hs = nullptr;
+  float *attn_po = nullptr, *attn_ml = nullptr;
+  int attn_max_splits = 8;
+  float *rlog = nullptr, *topk_w = nullptr, *y = nullptr, *ys = nullptr, *lm_part = nullptr;
+  int *topk_ids = nullptr, *off = nullptr, *pair_row = nullptr, *pos = nullptr;
+  int lm_ntiles = 0;
+  float *H = nullptr, *gap = nullptr;
+  int *am = nullptr, *n_unc = nullptr, *u_total = nullptr;
+  int* u_host = nullptr;  // pinned
+  // kernel timing
+  int prof_id = DG_PROF_NONE;
+  std::vector<hipEvent_t> prof_ev;  // start/stop pairs
+  int prof_n = 0;
+  double prof_ms = 0.0;
+  long long prof_launches = 0;
+};
+
+namespace {
+
+int alloc(dg_model* m, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  if (hipMalloc(p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DG_ERR_OOM, "hipMalloc(%zu) failed", bytes);
+  }
+  m->allocs.push_back(*p);
+  return DG_OK;
+}
+
+void free_all(dg_model* m) {
+  for (hipEvent_t e : m->prof_ev) (void)hipEventDestroy(e);
+  m->prof_ev.clear();
+  for (void* p : m->allocs) (void)hipFree(p);
+  m->allocs.clear();
+  if (m->u_host) (void)hipHostFree(m->u_host);
+  m->u_host = nullptr;
+}
+
+constexpr int PROF_PAIRS = 1024;
+
+// Accumulate the recorded pairs (waits for the last stop event) and reset.
+int prof_drain(dg_model* m) {
+  if (m->prof_n == 0) return DG_OK;
+  HIP_OK(hipEventSynchronize(m->prof_ev[2 * (m->prof_n - 1) + 1]));
+  for (int i = 0; i < m->prof_n; ++i) {
+    float ms = 0.f;
+    HIP_OK(hipEventElapsedTime(&ms, m->prof_ev[2 * i], m->prof_ev[2 * i + 1]));
+    m->prof_ms += ms;
+  }
+  m->prof_launches += m->prof_n;
+  m->prof_n = 0;
+  return DG_OK;
+}
+
+// Brackets the launches of one kernel class with events when it is selected.
+struct ProfScope {
+  dg_model* m;
+  hipStream_t st;
+  bool on;
+  ProfScope(dg_model* m_, int id, hipStream_t st_) : m(m_), st(st_), on(m_->prof_id == id) {
+    if (on && m->prof_n >= PROF_PAIRS) on = prof_drain(m) == DG_OK;
+    if (on) on = hipEventRecord(m->prof_ev[2 * m->prof_n], st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (on && hipEventRecord(m->prof_ev[2 * m->prof_n + 1], st) == hipSuccess) m->prof_n++;
+  }
+};
+
+int check_config(const dg_config& c) {
+  if (c.n_layers <= 0 || c.d_model <= 0 || c.n_heads <= 0 || c.head_dim <= 0 || c.n_experts <= 0 ||
+      c.top_k <= 0 || c.d_expert <= 0 || c.d_shared <= 0 || c.vocab <= 0 || c.canvas_len <= 0 ||
+      c.max_steps <= 0)
+    return fail(DG_ERR_INVALID_ARG, "config fields must be positive");
+  if (c.act_dtype != DG_DTYPE_FP32 && c.act_dtype != DG_DTYPE_BF16)
+    return fail(DG_ERR_INVALID_ARG, "act_dtype must be FP32 or BF16");
+  if (c.act_dtype == DG_DTYPE_FP32 && c.expert_dtype != DG_DTYPE_FP32)
+    return fail(DG_ERR_INVALID_ARG, "FP32 activations need FP32 experts");
+  if (c.act_dtype == DG_DTYPE_BF16 && c.expert_dtype != DG_DTYPE_BF16 &&
+      c.expert_dtype != DG_DTYPE_FP8_E4M3)
+    return fail(DG_ERR_INVALID_ARG, "BF16 activations need BF16 or FP8_E4M3 experts");
+  const int A = c.n_heads * c.head_dim;
+  if (c.d_model % 32 || A % 32 || c.d_expert % 32 || c.d_shared % 32)
+    return fail(DG_ERR_SHAPE, "d_model, n_heads*head_dim, d_expert, d_shared must be multiples of 32");
+  const bool bf = c.act_dtype == DG_DTYPE_BF16;
+  const int dh = c.head_dim;
+  if (!(dh == 128 || dh == 64 || dh == 32 || (!bf && dh == 16)))
+    return fail(DG_ERR_SHAPE, "head_dim %d unsupported (bf16: 32/64/128, fp32: 16/32/64/128)", dh);
+  if (c.n_experts > 256 || c.top_k > 8 || c.top_k > c.n_experts)
+    return fail(DG_ERR_SHAPE, "need n_experts <= 256 and top_k <= min(8, n_experts)");
+  if (c.canvas_len > 1024) return fail(DG_ERR_SHAPE, "canvas_len must be <= 1024");
+  if (!(c.rope_theta >= 0.f) || !(c.rms_eps >= 0.f))
+    return fail(DG_ERR_INVALID_ARG, "rope_theta and rms_eps must be >= 0");
+  return DG_OK;
+}
+
+// One pre-norm block over T = B * n rows.  causal: rows are new tokens at
+// positions P.. written into the cache; otherwise canvas rows attend to the
+// first P cache rows plus the canvas.
+int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool causal, bool kv_only,
+                  hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const dg_layer_weights& w = m->layers[l];
+  const int T = B * n, d = c.d_model, H = c.n_heads, dh = c.head_dim, A = H * dh;
+  const int E = c.n_experts, k = c.top_k, de = c.d_expert, ds = c.d_shared;
+  const ActType at = m->at;
+  const long long cap = kv->capacity;
+  const long long layer_stride = (long long)kv->batch * H * cap * dh;
+  char* kcache = (char*)kv->k + l * layer_stride * m->esz;
+  char* vcache = (char*)kv->v + l * layer_stride * m->esz;
+
+  HIP_OK(rmsnorm(at, m->x, T, d, c.rms_eps, m->a, st));
+  {
+    ProfScope ps(m, DG_PROF_QKV, st);
+    GemmArgs g;
+    g.A = m->a; g.lda = d; g.B = w.wqkv; g.ldb = d; g.M = T; g.N = 3 * A; g.K = d;
+    g.C = m->qkv; g.ldc = 3 * A;
+    HIP_OK(gemm(at, at == ACT_BF16 ? W_BF16 : W_F32, EPI_ACT, g, 1, st));
+  }
+  AttnArgs aa{};
+  aa.q = m->q; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = m->o;
+  aa.part_o = m->attn_po; aa.part_ml = m->attn_ml;
+  if (!causal) {
+    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, P, c.rope_theta, m->q, m->kc, m->vc,
+                        (long long)n * dh, 0, st));
+    aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P;
+    aa.k1 = m->kc; aa.v1 = m->vc; aa.s1_bh = (long long)n * dh; aa.len1 = n;
+    aa.causal_base = -1;
+  } else {
+    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, P, c.rope_theta, m->q, kcache, vcache, cap * dh, P, st));
+    if (kv_only) return DG_OK;
+    aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P + n;
+    aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;
+    aa.causal_base = P;
+  }
+  aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1));
+  {
+    ProfScope ps(m, DG_PROF_ATTN, st);
+    HIP_OK(attention(at, aa, st));
+  }
+  const WType dw = at == ACT_BF16 ? W_BF16 : W_F32;
+  {
+    GemmArgs g;
+    g.A = m->o; g.lda = A; g.B = w.wo; g.ldb = A; g.M = T; g.N = d; g.K = A; g.C = m->x; g.ldc = d;
+    HIP_OK(gemm(at, dw, EPI_RESID, g, 1, st));
+  }
+  HIP_OK(rmsnorm(at, m->x, T, d, c.rms_eps, m->a, st));
+  {
+    ProfScope ps(m, DG_PROF_ROUTER, st);
+    GemmArgs g;
+    g.A = m->a; g.lda = d; g.B = w.wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = m->rlog; g.ldc = E;
+    HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
+    HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
+    HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
+  }
+  {
+    ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
+    GemmArgs g;  // routed gate/up + SwiGLU, rows gathered per expert
+    g.A = m->a; g.lda = d; g.a_rows = m->pair_row; g.B = w.w_gu; g.ldb = d;
+    g.b_gstride = 2LL * de * d; g.b_scale = w.s_gu; g.s_gstride = 2LL * de;
+    g.M = T * k; g.N = de; g.K = d; g.g_off = m->off; g.C = m->h; g.ldc = de; g.swiglu_half = de;
+    HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, E, st));
+  }
+  {
+    ProfScope ps(m, DG_PROF_MOE_DOWN, st);
+    GemmArgs g;  // routed down
+    g.A = m->h; g.lda = de; g.B = w.w_d; g.ldb = de; g.b_gstride = (long long)d * de;
+    g.b_scale = w.s_d; g.s_gstride = d;
+    g.M = T * k; g.N = d; g.K = de; g.g_off = m->off; g.C = m->y; g.ldc = d;
+    HIP_OK(gemm(at, m->wt, EPI_F32, g, E, st));
+  }
+  {
+    ProfScope ps(m, DG_PROF_SHARED, st);
+    GemmArgs g;  // shared gate/up + SwiGLU
+    g.A = m->a; g.lda = d; g.B = w.ws_gu; g.ldb = d; g.b_scale = w.ss_gu;
+    g.M = T; g.N = ds; g.K = d; g.C = m->hs; g.ldc = ds; g.swiglu_half = ds;
+    HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, 1, st));
+    GemmArgs g2;  // shared down
+    g2.A = m->hs; g2.lda = ds; g2.B = w.ws_d; g2.ldb = ds; g2.b_scale = w.ss_d;
+    g2.M = T; g2.N = d; g2.K = ds; g2.C = m->ys; g2.ldc = d;
+    HIP_OK(gemm(at, m->wt, EPI_F32, g2, 1, st));
+  }
+  HIP_OK(moe_combine(at, m->x, m->y, m->ys, m->topk_w, m->pos, T, k, d, st));
+  return DG_OK;
+}
+
+int lm_head_confidence(dg_model* m, const void* hf, int T, float* H, int* am, float* gap,
+                       hipStream_t st) {
+  ProfScope ps(m, DG_PROF_LM_HEAD, st);
+  const dg_config& c = m->cfg;
+  GemmArgs g;
+  g.A = hf; g.lda = c.d_model; g.B = m->lm_head; g.ldb = c.d_model; g.M = T; g.N = c.vocab;
+  g.K = c.d_model; g.part = m->lm_part;
+  HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_LM, g, 1, st));
+  HIP_OK(lm_merge(m->lm_part, T, m->lm_ntiles, H, am, gap, st));
+  return DG_OK;
+}
+
+int check_canvas(dg_model* m, const dg_canvas* c) {
+  if (!c || !c->tokens || !c->committed) return fail(DG_ERR_INVALID_ARG, "null canvas pointer");
+  if (c->batch <= 0 || c->batch > m->max_batch)
+    return fail(DG_ERR_SHAPE, "canvas batch %d outside [1, %d]", c->batch, m->max_batch);
+  return DG_OK;
+}
+
+int check_kv(const dg_kv* kv, int batch, int extra) {
+  if (!kv || !kv->k || !kv->v) return fail(DG_ERR_INVALID_ARG, "null kv pointer");
+  if (kv->batch != batch) return fail(DG_ERR_SHAPE, "kv batch %d != %d", kv->batch, batch);
+  if (kv->length < 0 || kv->capacity <= 0 || kv->length + extra > kv->capacity)
+    return fail(DG_ERR_SHAPE, "kv length %d + %d exceeds capacity %d", kv->length, extra, kv->capacity);
+  return DG_OK;
+}
+
+int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, hipStream_t st) {
+  const dg_config& cfg = m->cfg;
+  const int B = c->batch, N = cfg.canvas_len, T = B * N, P = kv->length;
+  HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, m->x, st));
+  for (int l = 0; l < cfg.n_layers; ++l) {
+    int s = layer_forward(m, l, B, N, P, kv, false, false, st);
+    if (s) return s;
+  }
+  HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
+  if (out && out->hidden)
+    HIP_OK(hipMemcpyAsync(out->hidden, m->a, (size_t)T * cfg.d_model * m->esz, hipMemcpyDeviceToDevice, st));
+  float* H = (out && out->entropy) ? out->entropy : m->H;
+  int* am = (out && out->argmax) ? out->argmax : m->am;
+  float* gap = (out && out->top2_gap) ? out->top2_gap : nullptr;
+  int s = lm_head_confidence(m, m->a, T, H, am, gap, st);
+  if (s) return s;
+  if (out && out->logits) {
+    GemmArgs g;
+    g.A = m->a; g.lda = cfg.d_model; g.B = m->lm_head; g.ldb = cfg.d_model; g.M = T; g.N = cfg.vocab;
+    g.K = cfg.d_model; g.C = out->logits; g.ldc = cfg.vocab;
+    HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_F32, g, 1, st));
+  }
+  {
+    ProfScope ps(m, DG_PROF_COMMIT, st);
+    HIP_OK(commit_renoise(H, am, c->tokens, c->committed, B, N, c->step, cfg.max_steps,
+                          cfg.commit_threshold, c->seed, c->block, cfg.vocab, m->n_unc, st));
+  }
+  if (out && out->n_uncommitted)
+    HIP_OK(hipMemcpyAsync(out->n_uncommitted, m->n_unc, sizeof(int) * B, hipMemcpyDeviceToDevice, st));
+  c->step += 1;
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_status_str(int s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_SHAPE: return "shape error";
+    case DG_ERR_HIP: return "HIP error";
+    case DG_ERR_OOM: return "out of device memory";
+    case DG_ERR_STATE: return "invalid state";
+    case DG_ERR_NUMERIC: return "numeric error";
+    case DG_ERR_UNIMPLEMENTED: return "unimplemented";
+  }
+  return "unknown status";
+}
+
+const char* dg_last_error(void) { return g_err.c_str(); }
+
+const char* dg_version(void) { return "dg 0.1 gfx950"; }
+
+int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch, int32_t max_tokens,
+                    int32_t max_kv, dg_model** out) {
+  if (!cfg || !w || !out) return fail(DG_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  int s = check_config(*cfg);
+  if (s) return s;
+  if (!w->embed || !w->lm_head || !w->layers) return fail(DG_ERR_INVALID_ARG, "null weight pointer");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dg_layer_weights& L = w->layers[l];
+    if (!L.wqkv || !L.wo || !L.wr || !L.w_gu || !L.w_d || !L.ws_gu || !L.ws_d)
+      return fail(DG_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
+    const bool fp8 = cfg->expert_dtype == DG_DTYPE_FP8_E4M3;
+    if (fp8 != (L.s_gu && L.s_d && L.ss_gu && L.ss_d) || (!fp8 && (L.s_gu || L.s_d || L.ss_gu || L.ss_d)))
+      return fail(DG_ERR_INVALID_ARG, "fp8 scales must be given exactly when expert_dtype is FP8 (layer %d)", l);
+  }
+  if (max_batch <= 0 || max_tokens < 0 || max_kv < 0)
+    return fail(DG_ERR_INVALID_ARG, "max_batch must be > 0, max_tokens and max_kv >= 0");
+  const int ntok = std::max(max_tokens, cfg->canvas_len);
+  if ((long long)max_batch * ntok * cfg->top_k > 8192)
+    return fail(DG_ERR_SHAPE, "max_batch * tokens * top_k must be <= 8192");
+
+  dg_model* m = new dg_model();
+  m->cfg = *cfg;
+  m->layers.assign(w->layers, w->layers + cfg->n_layers);
+  m->embed = w->embed;
+  m->lm_head = w->lm_head;
+  m->max_batch = max_batch;
+  m->max_tokens = ntok;
+  m->max_kv = max_kv;
+  m->Tmax = max_batch * ntok;
+  m->at = cfg->act_dtype == DG_DTYPE_BF16 ? ACT_BF16 : ACT_F32;
+  m->wt = cfg->expert_dtype == DG_DTYPE_FP8_E4M3 ? W_FP8 : (m->at == ACT_BF16 ? W_BF16 : W_F32);
+  m->esz = m->at == ACT_BF16 ? 2 : 4;
+  const size_t T = m->Tmax, d = cfg->d_model, A = (size_t)cfg->n_heads * cfg->head_dim;
+  const size_t E = cfg->n_experts, k = cfg->top_k, de = cfg->d_expert, ds = cfg->d_shared;
+  const size_t Tc = (size_t)max_batch * cfg->canvas_len;
+  m->lm_ntiles = lm_tiles(cfg->vocab);
+  const size_t es = m->esz;
+  struct Req {
+    void** p;
+    size_t bytes;
+  } reqs[] = {
+      {&m->x, T * d * es},
+      {&m->a, T * d * es},
+      {&m->qkv, T * 3 * A * es},
+      {&m->q, T * A * es},
+      {&m->kc, T * A * es},
+      {&m->vc, T * A * es},
+      {&m->o, T * A * es},
+      {(void**)&m->attn_po, (size_t)m->attn_max_splits * T * A * 4},
+      {(void**)&m->attn_ml, (size_t)m->attn_max_splits * T * cfg->n_heads * 2 * 4},
+      {(void**)&m->rlog, T * E * 4},
+      {(void**)&m->topk_ids, T * k * 4},
+      {(void**)&m->topk_w, T * k * 4},
+      {(void**)&m->off, (E + 1) * 4},
+      {(void**)&m->pair_row, T * k * 4},
+      {(void**)&m->pos, T * k * 4},
+      {&m->h, T * k * de * es},
+      {(void**)&m->y, T * k * d * 4},
+      {&m->hs, T * ds * es},
+      {(void**)&m->ys, T * d * 4},
+      {(void**)&m->lm_part, Tc * m->lm_ntiles * 5 * 4},
+      {(void**)&m->H, Tc * 4},
+      {(void**)&m->gap, Tc * 4},
+      {(void**)&m->am, Tc * 4},
+      {(void**)&m->n_unc, (size_t)max_batch * 4},
+      {(void**)&m->u_total, 4},
+  };
+  for (auto& r : reqs) {
+    s = alloc(m, r.p, r.bytes);
+    if (s) {
+      free_all(m);
+      delete m;
+      return s;
+    }
+  }
+  if (hipHostMalloc((void**)&m->u_host, sizeof(int), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    free_all(m);
+    delete m;
+    return fail(DG_ERR_OOM, "hipHostMalloc failed");
+  }
+  *out = m;
+  return DG_OK;
+}
+
+int dg_model_destroy(dg_model* m) {
+  if (!m) return DG_OK;
+  (void)hipDeviceSynchronize();
+  free_all(m);
+  delete m;
+  return DG_OK;
+}
+
+int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream) {
+  if (!m) return fail(DG_ERR_INVALID_ARG, "null model");
+  int s = check_canvas(m, c);
+  if (s) return s;
+  HIP_OK(canvas_init(c->tokens, c->committed, c->batch, m->cfg.canvas_len, c->seed, c->block,
+                     m->cfg.vocab, (hipStream_t)stream));
+  c->step = 0;
+  return DG_OK;
+}
+
+int dg_denoise_step(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, void* stream) {
+  if (!m) return fail(DG_ERR_INVALID_ARG, "null model");
+  int s = check_canvas(m, c);
+  if (s) return s;
+  s = check_kv(kv, c->batch, 0);
+  if (s) return s;
+  if (c->step < 0 || c->step >= m->cfg.max_steps)
+    return fail(DG_ERR_STATE, "step %d outside [0, max_steps=%d)", c->step, m->cfg.max_steps);
+  return denoise_step_impl(m, c, kv, out, (hipStream_t)stream);
+}
+
+int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* steps_taken, void* stream) {
+  if (!m || !steps_taken) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_canvas(m, c);
+  if (s) return s;
+  s = check_kv(kv, c->batch, 0);
+  if (s) return s;
+  if (c->step < 0 || c->step > m->cfg.max_steps)
+    return fail(DG_ERR_STATE, "step %d outside [0, max_steps]", c->step);
+  hipStream_t st = (hipStream_t)stream;
+  int taken = 0;
+  while (c->step < m->cfg.max_steps) {
+    s = denoise_step_impl(m, c, kv, nullptr, st);
+    if (s) {
+      *steps_taken = taken;
+      return s;
+    }
+    ++taken;
+    HIP_OK(reduce_sum_i32(m->n_unc, c->batch, m->u_total, st));
+    HIP_OK(hipMemcpyAsync(m->u_host, m->u_total, sizeof(int), hipMemcpyDeviceToHost, st));
+    HIP_OK(hipStreamSynchronize(st));
+    if (*m->u_host == 0) break;
+  }
+  *steps_taken = taken;
+  return DG_OK;
+}
+
+int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, void* stream) {
+  if (!m || !tokens) return fail(DG_ERR_INVALID_ARG, "null argument");
+  if (!kv) return fail(DG_ERR_INVALID_ARG, "null kv");
+  if (n <= 0 || n > m->max_tokens) return fail(DG_ERR_SHAPE, "n=%d outside [1, max_tokens=%d]", n, m->max_tokens);
+  if (kv->batch <= 0 || kv->batch > m->max_batch) return fail(DG_ERR_SHAPE, "kv batch %d", kv->batch);
+  int s = check_kv(kv, kv->batch, n);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const dg_config& cfg = m->cfg;
+  const int B = kv->batch, T = B * n, P = kv->length;
+  HIP_OK(embed_gather(m->at, tokens, T, m->embed, cfg.d_model, m->x, st));
+  for (int l = 0; l < cfg.n_layers; ++l) {
+    s = layer_forward(m, l, B, n, P, kv, true, l == cfg.n_layers - 1, st);
+    if (s) return s;
+  }
+  kv->length = P + n;
+  return DG_OK;
+}
+
+int dg_profile_kernel(dg_model* m, int32_t kernel_id) {
+  if (!m) return fail(DG_ERR_INVALID_ARG, "null model");
+  if (kernel_id < DG_PROF_NONE || kernel_id > DG_PROF_COMMIT) return fail(DG_ERR_INVALID_ARG, "bad kernel id");
+  int s = prof_drain(m);
+  if (s) return s;
+  if (kernel_id != DG_PROF_NONE && m->prof_ev.empty()) {
+    m->prof_ev.resize(2 * PROF_PAIRS);
+    for (auto& e : m->prof_ev) HIP_OK(hipEventCreate(&e));
+  }
+  m->prof_id = kernel_id;
+  m->prof_ms = 0.0;
+  m->prof_launches = 0;
+  return DG_OK;
+}
+
+int dg_profile_read(dg_model* m, double* total_ms, int64_t* launches) {
+  if (!m || !total_ms || !launches) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = prof_drain(m);
+  if (s) return s;
+  *total_ms = m->prof_ms;
+  *launches = m->prof_launches;
+  m->prof_ms = 0.0;
+  m->prof_launches = 0;
+  return DG_OK;
+}
+
+int dg_test_philox(uint64_t seed, uint32_t pos0, uint32_t step_tag, uint32_t canvas, uint32_t block,
+                   uint32_t modulus, int32_t n, uint32_t* out, void* stream) {
+  if (!out || n < 0 || n > (1 << 24)) return fail(DG_ERR_INVALID_ARG, "bad philox arguments");
+  HIP_OK(philox_fill(seed, pos0, step_tag, canvas, block, modulus, n, out, (hipStream_t)stream));
+  return DG_OK;
+}
+
+int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int32_t* argmax,
+                    float* top2_gap, void* stream) {
+  if (!m || !hf) return fail(DG_ERR_INVALID_ARG, "null argument");
+  if (T <= 0 || T > m->max_batch * m->cfg.canvas_len) return fail(DG_ERR_SHAPE, "T=%d out of range", T);
+  return lm_head_confidence(m, hf, T, entropy, argmax, top2_gap, (hipStream_t)stream);
+}
+
+int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_t* argmax,
+                   int32_t* n_uncommitted, void* stream) {
+  if (!m || !entropy || !argmax || !n_uncommitted) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_canvas(m, c);
+  if (s) return s;
+  if (c->step < 0 || c->step >= m->cfg.max_steps) return fail(DG_ERR_STATE, "step out of range");
+  HIP_OK(commit_renoise(entropy, argmax, c->tokens, c->committed, c->batch, m->cfg.canvas_len, c->step,
+                        m->cfg.max_steps, m->cfg.commit_threshold, c->seed, c->block, m->cfg.vocab,
+                        n_uncommitted, (hipStream_t)stream));
+  return DG_OK;
+}
+
+}  // extern "C"

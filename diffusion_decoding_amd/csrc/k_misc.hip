@@ -1,0 +1,256 @@
+// Small kernels of the denoise step: embedding gather, RMSNorm, RoPE + K/V
+// scatter, MoE combine, canvas initialisation, entropy-ranked commit with
+// re-noise, and Philox draws.
+//
+// Commit rule (DiffusionGemma解析, "换个路数：整片并行去噪的生成机制": positions are
+// ranked by entropy from low to high and the most certain are frozen; ipcmen.com
+// "工作原理：并行精炼与自我修正": the most confident tokens are locked and the
+// uncertain positions are randomised for the next step).  With U uncommitted
+// positions before step s (0-based) of at most S_max, the m = ceil(U/(S_max-s))
+// uncommitted positions with the smallest (entropy, index) commit, together
+// with every uncommitted position whose entropy is below the threshold; each
+// takes its argmax token.  The last allowed step therefore commits everything
+// (DiffusionGemma解析, "自适应停步机制": at most 48 steps).  The rest are redrawn
+// uniformly (zhichai.net 深度拆解, "统一状态扩散").
+#include <cmath>
+#include <type_traits>
+
+#include "dg_common.h"
+#include "kernels.h"
+
+namespace dg {
+namespace {
+
+template <typename T>
+__global__ void embed_kernel(const int* tok, int T_, const T* E, int d, T* x) {
+  const int t = blockIdx.x;
+  const long long src = (long long)tok[t] * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) x[(long long)t * d + c] = E[src + c];
+}
+
+// one workgroup (256 threads) per row
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, int d, float eps, T* y) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const T* xr = x + (long long)t * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = to_f32(xr[c]);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(ss / float(d) + eps);
+  T* yr = y + (long long)t * d;
+  for (int c = threadIdx.x; c < d; c += 256) yr[c] = from_f32<T>(to_f32(xr[c]) * inv);
+}
+
+// one thread per (token, head, pair j < dh/2); cos/sin of pos * theta^(-2j/dh)
+// evaluated in double precision and rounded to binary32.
+template <typename T>
+__global__ void rope_kernel(const T* qkv, int B, int n, int H, int dh, int pos0, float theta,
+                            T* q_out, T* kdst, T* vdst, long long dst_bh, int row0) {
+  const int half = dh / 2;
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)B * n * H * half;
+  if (e >= total) return;
+  const int j = int(e % half);
+  const int h = int((e / half) % H);
+  const int i = int((e / ((long long)half * H)) % n);
+  const int b = int(e / ((long long)half * H * n));
+  const int A = H * dh;
+  const T* row = qkv + (long long)(b * n + i) * 3 * A;
+  float c = 1.f, s = 0.f;
+  if (theta > 0.f) {
+    const double inv = pow((double)theta, -2.0 * j / dh);
+    const double ang = (double)(pos0 + i) * inv;
+    c = (float)cos(ang);
+    s = (float)sin(ang);
+  }
+  const int bh = b * H + h;
+  // q
+  {
+    float x1 = to_f32(row[h * dh + j]), x2 = to_f32(row[h * dh + j + half]);
+    T* qo = q_out + ((long long)bh * n + i) * dh;
+    qo[j] = from_f32<T>(x1 * c - x2 * s);
+    qo[j + half] = from_f32<T>(x2 * c + x1 * s);
+  }
+  // k, v
+  {
+    float x1 = to_f32(row[A + h * dh + j]), x2 = to_f32(row[A + h * dh + j + half]);
+    T* ko = kdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
+    ko[j] = from_f32<T>(x1 * c - x2 * s);
+    ko[j + half] = from_f32<T>(x2 * c + x1 * s);
+    T* vo = vdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
+    vo[j] = row[2 * A + h * dh + j];
+    vo[j + half] = row[2 * A + h * dh + j + half];
+  }
+}
+
+template <typename T>
+__global__ void combine_kernel(T* x, const float* y, const float* ys, const float* w, const int* pos,
+                               int k, int d) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc += w[t * k + j] * y[(long long)pos[t * k + j] * d + c];
+    acc += ys[(long long)t * d + c];
+    T* xp = x + (long long)t * d + c;
+    *xp = from_f32<T>(to_f32(*xp) + acc);
+  }
+}
+
+__global__ void canvas_init_kernel(int* tok, uint8_t* committed, int N, uint64_t seed, uint32_t block,
+                                   int vocab) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  tok[b * N + i] = int(canvas_draw(seed, uint32_t(i), 0u, uint32_t(b), block, uint32_t(vocab)));
+  committed[b * N + i] = 0;
+}
+
+// (entropy, index) order with NaN entropies after every number
+__device__ __forceinline__ bool rank_before(float hj, int j, float hi, int i) {
+  const bool nj = hj != hj, ni = hi != hi;
+  if (nj || ni) return ni && (!nj || j < i);
+  return hj < hi || (hj == hi && j < i);
+}
+
+// one workgroup of 1024 threads per canvas; N <= 1024
+__global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int* am, int* tok,
+                                                      uint8_t* committed, int N, int step,
+                                                      int max_steps, float threshold, uint64_t seed,
+                                                      uint32_t block, int vocab, int* n_unc) {
+  __shared__ float hs[1024];
+  __shared__ int unc_s[1024];
+  __shared__ int red[16];
+  const int b = blockIdx.x, i = threadIdx.x;
+  const bool in = i < N;
+  const int base = b * N;
+  const bool unc = in && committed[base + i] == 0;
+  const float hi = in ? H[base + i] : 0.f;
+  hs[i] = hi;
+  unc_s[i] = unc;
+  // U = number of uncommitted positions
+  int cnt = wave_sum_i(unc ? 1 : 0);
+  if ((i & 63) == 0) red[i >> 6] = cnt;
+  __syncthreads();
+  int U = 0;
+  for (int w = 0; w < 16; ++w) U += red[w];
+  const int m = U ? (U + (max_steps - step) - 1) / (max_steps - step) : 0;
+  bool take = false;
+  if (unc) {
+    int before = 0;
+    for (int j = 0; j < N; ++j) before += (unc_s[j] && rank_before(hs[j], j, hi, i)) ? 1 : 0;
+    take = before < m || hi < threshold;
+  }
+  if (take) {
+    tok[base + i] = am[base + i];
+    committed[base + i] = 1;
+  }
+  const bool still = unc && !take;
+  __syncthreads();
+  int c2 = wave_sum_i(still ? 1 : 0);
+  if ((i & 63) == 0) red[i >> 6] = c2;
+  __syncthreads();
+  if (still)
+    tok[base + i] =
+        int(canvas_draw(seed, uint32_t(i), uint32_t(step + 1), uint32_t(b), block, uint32_t(vocab)));
+  if (i == 0) {
+    int Up = 0;
+    for (int w = 0; w < 16; ++w) Up += red[w];
+    n_unc[b] = Up;
+  }
+}
+
+__global__ void philox_kernel(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas,
+                              uint32_t block, uint32_t modulus, int n, uint32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = canvas_draw(seed, pos0 + uint32_t(i), tag, canvas, block, modulus);
+}
+
+__global__ void sum_i32_kernel(const int* v, int n, int* out) {
+  int s = 0;
+  for (int i = threadIdx.x; i < n; i += 64) s += v[i];
+  s = wave_sum_i(s);
+  if (threadIdx.x == 0) *out = s;
+}
+
+}  // namespace
+
+int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st) {
+  if (T <= 0) return 0;
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(T), dim3(256), 0, st, tok, T, (const bf16*)E, d, (bf16*)x);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, st, tok, T, (const float*)E, d, (float*)x);
+  return int(hipGetLastError());
+}
+
+int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st) {
+  if (T <= 0) return 0;
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(T), dim3(256), 0, st, (const bf16*)x, d, eps, (bf16*)y);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)x, d, eps, (float*)y);
+  return int(hipGetLastError());
+}
+
+int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, int pos0, float theta,
+                 void* q_out, void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st) {
+  const long long total = (long long)B * n * H * (dh / 2);
+  if (total <= 0) return 0;
+  dim3 grid(unsigned((total + 255) / 256));
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)qkv, B, n, H, dh, pos0,
+                       theta, (bf16*)q_out, (bf16*)kdst, (bf16*)vdst, dst_bh, row0);
+  else
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, st, (const float*)qkv, B, n, H, dh, pos0,
+                       theta, (float*)q_out, (float*)kdst, (float*)vdst, dst_bh, row0);
+  return int(hipGetLastError());
+}
+
+int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
+                int T, int k, int d, hipStream_t st) {
+  if (T <= 0) return 0;
+  if (at == ACT_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16>, dim3(T), dim3(256), 0, st, (bf16*)x, y, ys, w, pos, k, d);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (float*)x, y, ys, w, pos, k, d);
+  return int(hipGetLastError());
+}
+
+int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block, int vocab,
+                hipStream_t st) {
+  hipLaunchKernelGGL(canvas_init_kernel, dim3((N + 255) / 256, B), dim3(256), 0, st, tok, committed, N,
+                     seed, block, vocab);
+  return int(hipGetLastError());
+}
+
+int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N, int step,
+                   int max_steps, float threshold, uint64_t seed, uint32_t block, int vocab, int* n_unc,
+                   hipStream_t st) {
+  if (N > 1024) return int(hipErrorInvalidValue);
+  hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(1024), 0, st, H, am, tok, committed, N, step,
+                     max_steps, threshold, seed, block, vocab, n_unc);
+  return int(hipGetLastError());
+}
+
+int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uint32_t block,
+                uint32_t modulus, int n, uint32_t* out, hipStream_t st) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(philox_kernel, dim3((n + 255) / 256), dim3(256), 0, st, seed, pos0, tag, canvas,
+                     block, modulus, n, out);
+  return int(hipGetLastError());
+}
+
+int reduce_sum_i32(const int* v, int n, int* out, hipStream_t st) {
+  hipLaunchKernelGGL(sum_i32_kernel, dim3(1), dim3(64), 0, st, v, n, out);
+  return int(hipGetLastError());
+}
+
+}  // namespace dg

@@ -1,0 +1,96 @@
+// Host-side launch interfaces of the gfx950 kernels.  Every launcher enqueues
+// on `st` and performs no synchronisation and no allocation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+// ---------------------------------------------------------------- GEMM (k_gemm.hip)
+// C[m][n] = sum_k A[row(m)][k] * B[n][k]; epilogue by kind.
+enum GemmEpi {
+  EPI_F32 = 0,     // C fp32 [m][n]
+  EPI_ACT = 1,     // C act  [m][n] (rounded)
+  EPI_RESID = 2,   // C act  [m][n] = round(C + acc)
+  EPI_SWIGLU = 3,  // C act  [m][j] = round(silu(gate_j) * up_j); B rows: gate j, up half+j
+  EPI_LM = 4,      // per-row (max, idx, second, sum e^(z-max), sum e^(z-max)(z-max)) over the tile
+};
+
+struct GemmArgs {
+  const void* A = nullptr;
+  long long lda = 0;
+  const int* a_rows = nullptr;     // optional gather: A row of output row m is a_rows[m]
+  const void* B = nullptr;
+  long long ldb = 0;
+  long long b_gstride = 0;         // elements between consecutive groups' B
+  const float* b_scale = nullptr;  // fp8 row scales of B (per output row of B)
+  long long s_gstride = 0;
+  int M = 0, N = 0, K = 0;         // N: output columns (SWIGLU: outputs j, i.e. gate rows)
+  const int* g_off = nullptr;      // [G+1] row ranges of groups (grid.z = G); null: one group
+  void* C = nullptr;
+  long long ldc = 0;
+  int swiglu_half = 0;             // SWIGLU: B row of up_j is swiglu_half + j
+  float* part = nullptr;           // EPI_LM partials [M][n_tiles][5]
+};
+
+// Returns 0 or a HIP error code.
+int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st);
+// Number of vocab tiles the LM epilogue writes per row.
+int lm_tiles(int vocab);
+// Merge LM partials of T rows into entropy / argmax / top-2 gap.
+int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap,
+             hipStream_t st);
+
+// ---------------------------------------------------------------- attention (k_attn.hip)
+struct AttnArgs {
+  const void* q;          // [B][H][n][dh]
+  const void* k0;         // segment 0 keys: (b,h) at k0 + (b*H+h)*s0_bh, rows [0, len0)
+  const void* v0;
+  long long s0_bh;        // elements between (b,h) planes of segment 0
+  int len0;
+  const void* k1;         // segment 1 keys (may be null if len1 == 0)
+  const void* v1;
+  long long s1_bh;
+  int len1;
+  int causal_base;        // -1: bidirectional; else query i sees keys j <= causal_base + i
+  int B, H, n, dh;
+  void* out;              // [B*n][H*dh] act
+  float* part_o;          // split partials [splits][B*H][n][dh]
+  float* part_ml;         // [splits][B*H][n][2]
+  int splits;
+};
+int attention(ActType at, const AttnArgs& a, hipStream_t st);
+int attn_splits_for(int B, int H, int n, int keys);
+
+// ---------------------------------------------------------------- misc (k_misc.hip)
+int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st);
+int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st);
+// RoPE on q,k from qkv [T][3A] (T = B*n, positions pos0 + i) and scatter:
+// q -> q_out [B][H][n][dh]; k,v -> (b,h) planes at kdst/vdst + (b*H+h)*dst_bh + (row0+i)*dh.
+int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, int pos0, float theta,
+                 void* q_out, void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st);
+// x[t] = round(x[t] + sum_j w[t][j] * y[pos[t][j]] + ys[t])
+int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w,
+                const int* pos, int T, int k, int d, hipStream_t st);
+int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block,
+                int vocab, hipStream_t st);
+int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N,
+                   int step, int max_steps, float threshold, uint64_t seed, uint32_t block,
+                   int vocab, int* n_unc, hipStream_t st);
+int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uint32_t block,
+                uint32_t modulus, int n, uint32_t* out, hipStream_t st);
+int reduce_sum_i32(const int* v, int n, int* out, hipStream_t st);
+
+// ---------------------------------------------------------------- router (k_router.hip)
+// logits [T][E] fp32 -> ids [T][k], w [T][k]
+int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hipStream_t st);
+// ids [T][k] -> cnt[E], off[E+1], pair_row[T*k] (token of each pair slot, expert-major,
+// token-ascending), pos[T][k] (slot of pair (t, j)).
+int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,
+                   hipStream_t st);
+
+}  // namespace dg

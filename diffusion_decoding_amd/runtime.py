@@ -1,0 +1,155 @@
+"""Torch-facing wrappers over the C ABI: device memory and streams come from
+torch, every step of the path runs in libdg.so.  Nothing here computes."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (DG_DTYPE_BF16, DG_DTYPE_FP8_E4M3, DG_DTYPE_FP32, dg_canvas, dg_config, dg_kv,
+                   dg_layer_weights, dg_step_out, dg_weights)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_DT = {"fp32": DG_DTYPE_FP32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3}
+
+
+def make_config(cfg) -> dg_config:
+    return dg_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_experts, cfg.top_k,
+                     cfg.d_expert, cfg.d_shared, cfg.vocab, cfg.canvas_len, cfg.max_steps,
+                     float(cfg.rope_theta), float(cfg.rms_eps), float(cfg.threshold),
+                     _DT[cfg.act_dtype], _DT[cfg.expert_dtype])
+
+
+class Model:
+    """A libdg model over the weights of an ``Inputs`` set (tensors stay referenced)."""
+
+    def __init__(self, inputs, max_batch: Optional[int] = None, max_tokens: Optional[int] = None,
+                 max_kv: Optional[int] = None):
+        cfg = inputs.cfg
+        self.cfg = cfg
+        self.inputs = inputs
+        L = cfg.n_layers
+        self._layers = (dg_layer_weights * L)()
+        for l, lw in enumerate(inputs.layers):
+            self._layers[l] = dg_layer_weights(
+                _ptr(lw["wqkv"]), _ptr(lw["wo"]), _ptr(lw["wr"]), _ptr(lw["w_gu"]), _ptr(lw["w_d"]),
+                _ptr(lw.get("s_gu")), _ptr(lw.get("s_d")), _ptr(lw["ws_gu"]), _ptr(lw["ws_d"]),
+                _ptr(lw.get("ss_gu")), _ptr(lw.get("ss_d")))
+        self._weights = dg_weights(_ptr(inputs.embed), _ptr(inputs.lm_head), self._layers)
+        self._cfg = make_config(cfg)
+        self.max_batch = max_batch or cfg.batch
+        self.max_tokens = max_tokens or max(cfg.canvas_len, cfg.prompt_len if cfg.prompt_mode == "tokens" else 0)
+        self.max_kv = max_kv or inputs.kv_k.shape[3]
+        self.handle = _lib.dg_model_create(self._cfg, self._weights, self.max_batch, self.max_tokens,
+                                           self.max_kv)
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            _lib.dg_model_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+@dataclass
+class Canvas:
+    tokens: torch.Tensor      # int32 [B, N]
+    committed: torch.Tensor   # uint8 [B, N]
+    seed: int
+    block: int = 0
+    step: int = 0
+
+    @classmethod
+    def empty(cls, batch: int, n: int, seed: int, block: int = 0, device="cuda"):
+        return cls(torch.zeros(batch, n, dtype=torch.int32, device=device),
+                   torch.zeros(batch, n, dtype=torch.uint8, device=device), seed, block, 0)
+
+    def struct(self) -> dg_canvas:
+        return dg_canvas(_ptr(self.tokens), _ptr(self.committed), self.tokens.shape[0], self.step,
+                         self.seed, self.block)
+
+
+@dataclass
+class KVCache:
+    k: torch.Tensor   # [L, B, H, cap, dh]
+    v: torch.Tensor
+    length: int
+
+    def struct(self) -> dg_kv:
+        return dg_kv(_ptr(self.k), _ptr(self.v), self.k.shape[1], self.k.shape[3], self.length)
+
+
+def canvas_init(model: Model, canvas: Canvas, stream=None):
+    s = canvas.struct()
+    _lib.dg_canvas_init(model.handle, s, _stream(stream))
+    canvas.step = s.step
+
+
+def denoise_step(model: Model, canvas: Canvas, kv: KVCache, entropy=None, argmax=None, top2_gap=None,
+                 n_uncommitted=None, logits=None, hidden=None, stream=None):
+    s = canvas.struct()
+    out = dg_step_out(_ptr(entropy), _ptr(argmax), _ptr(top2_gap), _ptr(n_uncommitted), _ptr(logits),
+                      _ptr(hidden))
+    _lib.dg_denoise_step(model.handle, s, kv.struct(), out, _stream(stream))
+    canvas.step = s.step
+
+
+def generate_canvas(model: Model, canvas: Canvas, kv: KVCache, stream=None) -> int:
+    s = canvas.struct()
+    taken = _lib.dg_generate_canvas(model.handle, s, kv.struct(), _stream(stream))
+    canvas.step = s.step
+    return taken
+
+
+def commit_canvas(model: Model, tokens: torch.Tensor, kv: KVCache, stream=None):
+    if tokens.dtype != torch.int32 or tokens.dim() != 2:
+        raise ValueError("tokens must be int32 [batch, n]")
+    s = kv.struct()
+    _lib.dg_commit_canvas(model.handle, _ptr(tokens), tokens.shape[1], s, _stream(stream))
+    kv.length = s.length
+
+
+def test_philox(seed, pos0, tag, canvas, block, modulus, n, stream=None) -> torch.Tensor:
+    out = torch.empty(n, dtype=torch.int64, device="cuda")
+    buf = torch.empty(n, dtype=torch.int32, device="cuda")
+    _lib.dg_test_philox(seed, pos0, tag, canvas, block, modulus, n, _ptr(buf), _stream(stream))
+    out.copy_(buf.to(torch.int64) & 0xFFFFFFFF)
+    return out
+
+
+def test_lm_head(model: Model, hf: torch.Tensor, stream=None):
+    T = hf.shape[0]
+    ent = torch.empty(T, dtype=torch.float32, device=hf.device)
+    am = torch.empty(T, dtype=torch.int32, device=hf.device)
+    gap = torch.empty(T, dtype=torch.float32, device=hf.device)
+    _lib.dg_test_lm_head(model.handle, _ptr(hf), T, _ptr(ent), _ptr(am), _ptr(gap), _stream(stream))
+    return ent, am, gap
+
+
+def test_commit(model: Model, canvas: Canvas, entropy: torch.Tensor, argmax: torch.Tensor, stream=None):
+    nunc = torch.empty(canvas.tokens.shape[0], dtype=torch.int32, device=entropy.device)
+    _lib.dg_test_commit(model.handle, canvas.struct(), _ptr(entropy), _ptr(argmax), _ptr(nunc),
+                        _stream(stream))
+    return nunc

@@ -1,0 +1,219 @@
+/*
+ * dg.h -- C ABI of the block-diffusion denoise library for MI355X (gfx950).
+ *
+ * The library runs the hot path of DiffusionGemma-style block diffusion
+ * decoding on one GPU.  A canvas of `canvas_len` tokens starts from uniform
+ * random ids and is refined in denoise steps.  Every step
+ *   1. runs the backbone over all canvas positions with bidirectional,
+ *      unmasked attention over the prompt KV cache plus the whole canvas
+ *      (DiffusionGemma解析, "换个路数：整片并行去噪的生成机制"; zhichai.net
+ *      深度拆解, "双向注意力: BERT 的遗产"), each layer holding a mixture of
+ *      experts with top-k routing and one shared expert (zhichai.net 深度拆解,
+ *      "MoE 效率：128 专家，8 活跃");
+ *   2. scores each position by the entropy of its output distribution and
+ *      takes its argmax (DiffusionGemma解析, same section: lower entropy means
+ *      more certain);
+ *   3. commits the most certain uncommitted positions, ranked by entropy
+ *      (ipcmen.com, "工作原理：并行精炼与自我修正": lock the most confident
+ *      tokens), and
+ *   4. redraws every still-uncommitted position uniformly at random
+ *      (zhichai.net 深度拆解, "统一状态扩散 vs 掩码扩散").
+ * Steps repeat until every position is committed or `max_steps` (48 in the
+ * pages: DiffusionGemma解析, "自适应停步机制") have run.  A committed canvas is
+ * appended to the KV cache by a causal pass before the next canvas starts
+ * (zhichai.net 深度拆解, "Block-Autoregressive：块内并行，块间串行").
+ *
+ * Conventions for every entry point:
+ *  - All pointers inside the structs below are DEVICE pointers unless a field
+ *    says "host".  The library never frees caller memory; it owns only the
+ *    workspace it allocates in dg_model_create and frees in dg_model_destroy.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it asynchronously; only dg_generate_canvas blocks (it reads back the
+ *    4-byte count of uncommitted positions after every step).
+ *  - Arguments are validated before anything is launched.  On failure the
+ *    call returns a negative dg_status, enqueues nothing, and leaves caller
+ *    state unchanged; dg_last_error() then describes the failure (per thread).
+ *  - Calls on one model must not overlap (the workspace is shared).
+ *
+ * Layouts (row-major, innermost dimension last; T = batch * tokens):
+ *  - activations/weights in `act_dtype` (FP32 or BF16); routed and shared
+ *    expert weights in `expert_dtype` (FP32, BF16, or FP8_E4M3 codes with one
+ *    fp32 scale per output row: w = decode(code) * scale[row]).
+ *  - weight matrices are [out][in]: y = W x.
+ *  - KV cache: k and v are each [n_layers][batch][n_heads][capacity][head_dim]
+ *    in act_dtype, holding rotary-embedded keys and the values.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, unsupported combination */
+  DG_ERR_SHAPE = -2,         /* sizes inconsistent or beyond what the model was created for */
+  DG_ERR_HIP = -3,           /* a HIP runtime call failed (message in dg_last_error) */
+  DG_ERR_OOM = -4,           /* workspace allocation failed */
+  DG_ERR_STATE = -5,         /* step counter already at max_steps, or similar */
+  DG_ERR_NUMERIC = -6,       /* reserved: non-finite values detected */
+  DG_ERR_UNIMPLEMENTED = -7
+} dg_status;
+
+enum { DG_DTYPE_FP32 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP8_E4M3 = 2 };
+
+/* Model shape and decoding rule.  All fields are plain values (host). */
+typedef struct dg_config {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t head_dim;        /* even; attention scale 1/sqrt(head_dim) */
+  int32_t n_experts;       /* routed experts, <= 256 */
+  int32_t top_k;           /* experts per token, <= min(n_experts, 8) */
+  int32_t d_expert;        /* SwiGLU width of a routed expert */
+  int32_t d_shared;        /* SwiGLU width of the shared expert */
+  int32_t vocab;
+  int32_t canvas_len;      /* positions per canvas, <= 1024 */
+  int32_t max_steps;       /* denoise step cap S_max */
+  float rope_theta;        /* RoPE base; 0 disables rotary embedding */
+  float rms_eps;           /* RMSNorm epsilon (inside the square root) */
+  float commit_threshold;  /* nats: uncommitted positions with entropy below it commit */
+  int32_t act_dtype;       /* DG_DTYPE_FP32 or DG_DTYPE_BF16 */
+  int32_t expert_dtype;    /* FP32 (with act FP32), BF16 or FP8_E4M3 (with act BF16) */
+} dg_config;
+
+/* One layer's weights (device pointers, borrowed for the model's lifetime). */
+typedef struct dg_layer_weights {
+  const void* wqkv;    /* [3*n_heads*head_dim][d_model]: q rows, k rows, v rows */
+  const void* wo;      /* [d_model][n_heads*head_dim] */
+  const void* wr;      /* router [n_experts][d_model] (act_dtype) */
+  const void* w_gu;    /* [n_experts][2*d_expert][d_model]: gate rows then up rows */
+  const void* w_d;     /* [n_experts][d_model][d_expert] */
+  const float* s_gu;   /* FP8 only: [n_experts][2*d_expert] row scales, else NULL */
+  const float* s_d;    /* FP8 only: [n_experts][d_model] */
+  const void* ws_gu;   /* shared expert [2*d_shared][d_model] */
+  const void* ws_d;    /* shared expert [d_model][d_shared] */
+  const float* ss_gu;  /* FP8 only: [2*d_shared] */
+  const float* ss_d;   /* FP8 only: [d_model] */
+} dg_layer_weights;
+
+typedef struct dg_weights {
+  const void* embed;                  /* [vocab][d_model], act_dtype */
+  const void* lm_head;                /* [vocab][d_model], act_dtype (untied) */
+  const dg_layer_weights* layers;     /* host array of n_layers entries (copied at create) */
+} dg_weights;
+
+/* KV cache (caller-owned device memory, layout in the header comment). */
+typedef struct dg_kv {
+  void* k;
+  void* v;
+  int32_t batch;       /* canvases; each has its own cache rows */
+  int32_t capacity;    /* rows per (layer, canvas, head) */
+  int32_t length;      /* rows in use; advanced by dg_commit_canvas */
+} dg_kv;
+
+/* Canvas state.  tokens/committed are device arrays of [batch][canvas_len].
+ * Random draws use Philox4x32-10 with key (seed mod 2^32, seed >> 32) and
+ * counter (position, step_tag, canvas index b, block): step_tag 0 for
+ * dg_canvas_init, s + 1 for the re-noise after step s.  */
+typedef struct dg_canvas {
+  int32_t* tokens;
+  uint8_t* committed;  /* 0 or 1; only ever goes 0 -> 1 */
+  int32_t batch;
+  int32_t step;        /* host: steps already taken (0-based index of the next step) */
+  uint64_t seed;
+  uint32_t block;      /* canvas ordinal in block-autoregressive generation */
+} dg_canvas;
+
+/* Optional per-step outputs (each pointer may be NULL = not written). */
+typedef struct dg_step_out {
+  float* entropy;          /* [batch][canvas_len] nats, from the fp32 logits */
+  int32_t* argmax;         /* [batch][canvas_len] lowest id among maxima */
+  float* top2_gap;         /* [batch][canvas_len] largest minus second-largest logit */
+  int32_t* n_uncommitted;  /* [batch] after this step's commit */
+  float* logits;           /* test/diagnostic: [batch*canvas_len][vocab] fp32 (extra GEMM) */
+  void* hidden;            /* test/diagnostic: final normed hidden [batch*canvas_len][d_model] */
+} dg_step_out;
+
+typedef struct dg_model dg_model;
+
+const char* dg_status_str(int status);
+const char* dg_last_error(void);
+/* Library version string. */
+const char* dg_version(void);
+
+/* Create a model over borrowed weights.  `max_batch` canvases per call and up
+ * to `max_tokens` tokens per canvas in dg_commit_canvas (>= canvas_len) size
+ * the workspace, which is allocated here once; `max_kv` bounds the KV rows
+ * attention reads (capacity of the largest cache used).  Must be called with
+ * the target device current. */
+int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch,
+                    int32_t max_tokens, int32_t max_kv, dg_model** out);
+int dg_model_destroy(dg_model* m);
+
+/* Draw the initial canvas (step_tag 0) and clear `committed`; sets step = 0. */
+int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream);
+
+/* One denoise step (forward, confidence, commit, re-noise) on every canvas of
+ * `c` against the first kv->length cache rows.  Requires c->step < max_steps;
+ * increments c->step.  kv->batch must equal c->batch. */
+int dg_denoise_step(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, void* stream);
+
+/* Run denoise steps from the canvas's current state until every position of
+ * every canvas is committed or max_steps is reached.  Blocks; writes the
+ * number of steps this call ran to *steps_taken (host). */
+int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* steps_taken,
+                       void* stream);
+
+/* Causal pass over tokens[batch][n] (device) at positions kv->length ..
+ * kv->length+n-1: writes their rotary-embedded keys and values into every
+ * layer's cache rows [length, length+n) and advances kv->length by n.  Token i
+ * attends to all cached rows and to new tokens j <= i.  Requires
+ * length + n <= capacity and n <= max_tokens. */
+int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, void* stream);
+
+/* ---- kernel timing ---------------------------------------------------------
+ * Measures one kernel class with HIP events recorded on the stream each of its
+ * launches goes to (start before, stop after the launch), so a benchmark can
+ * time it inside its own timed region.  dg_profile_kernel selects the class
+ * (DG_PROF_NONE disables) and allocates the event pool (1024 pairs) -- call it
+ * outside timed or captured regions; dg_profile_read waits for the recorded
+ * events, returns the summed duration (ms) and the launch count, and resets. */
+enum {
+  DG_PROF_NONE = 0,
+  DG_PROF_ATTN = 1,        /* canvas attention (+ split merge) */
+  DG_PROF_MOE_GATEUP = 2,  /* routed experts: gate/up GEMM + SwiGLU */
+  DG_PROF_MOE_DOWN = 3,    /* routed experts: down GEMM */
+  DG_PROF_LM_HEAD = 4,     /* LM head + entropy/argmax epilogue + merge */
+  DG_PROF_QKV = 5,         /* QKV projection */
+  DG_PROF_SHARED = 6,      /* shared expert (gate/up + down) */
+  DG_PROF_ROUTER = 7,      /* router GEMM + top-k + permutation */
+  DG_PROF_COMMIT = 8       /* commit selection + re-noise */
+};
+int dg_profile_kernel(dg_model* m, int32_t kernel_id);
+int dg_profile_read(dg_model* m, double* total_ms, int64_t* launches);
+
+/* ---- test-only entry points (not part of the product API) ---------------- */
+
+/* out[i] = Philox4x32-10 word 0 of counter (pos0+i, step_tag, canvas, block)
+ * under key `seed`, modulo `modulus` (0 = no reduction).  n <= 2^24. */
+int dg_test_philox(uint64_t seed, uint32_t pos0, uint32_t step_tag, uint32_t canvas,
+                   uint32_t block, uint32_t modulus, int32_t n, uint32_t* out, void* stream);
+
+/* Fused LM head + confidence on given normed hidden rows hf[T][d_model]
+ * (act_dtype): writes entropy/argmax/top2_gap for T rows (T <= workspace). */
+int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int32_t* argmax,
+                    float* top2_gap, void* stream);
+
+/* Commit selection + re-noise alone, on given entropy/argmax [batch][canvas_len]. */
+int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_t* argmax,
+                   int32_t* n_uncommitted, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer work (Philox draws, commit masks, committed tokens) is compared
+bit-exactly; floating point within the tolerances in tests/parity.py; the
+denoise loop is compared step-locked with resynchronisation of flagged cases.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from oracle import philox
+from tests.parity import H_TOL, compare_step, logits_tol, to_host
+from workloads import get_config, make_inputs, tiny_config
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rt():
+    from diffusion_decoding_amd import runtime
+    runtime._lib.load()
+    return runtime
+
+
+def _gpu_setup(rt, cfg, device="cuda", kv_capacity=None):
+    inp = make_inputs(cfg, device=device, kv_capacity=kv_capacity)
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k.clone(), inp.kv_v.clone(), inp.kv_len)
+    return inp, model, kv
+
+
+# ----------------------------------------------------------------------------- Philox
+
+def test_philox_bit_exact(rt):
+    say("philox: 3 counter layouts x 65536 draws")
+    for seed, pos0, tag, canvas, block, mod in [(0, 0, 0, 0, 0, 0), (2**64 - 1, 7, 48, 3, 9, 262144),
+                                                (12345, 2**32 - 1000, 1, 0, 7, 512)]:
+        n = 65536 if pos0 < 2**31 else 1000
+        got = to_host(rt.test_philox(seed, pos0, tag, canvas, block, mod, n))
+        torch.cuda.synchronize()
+        pos = (np.arange(n, dtype=np.uint64) + np.uint64(pos0)) & np.uint64(0xFFFFFFFF)
+        ctr = np.stack([pos, np.full(n, tag, np.uint64), np.full(n, canvas, np.uint64),
+                        np.full(n, block, np.uint64)])
+        ref = philox.philox4x32_10(ctr, philox.seed_key(seed))[0]
+        if mod:
+            ref = ref % np.uint64(mod)
+        np.testing.assert_array_equal(got.astype(np.uint64), ref)
+
+
+# ----------------------------------------------------------------------------- commit kernel
+
+def test_commit_kernel_bit_exact(rt):
+    say("commit kernel: random entropies with ties, several steps, batch 3")
+    cfg = tiny_config(batch=3, canvas_len=40, max_steps=6, threshold=0.5)
+    inp, model, _ = _gpu_setup(rt, cfg)
+    rng = np.random.default_rng(1)
+    B, N = 3, 40
+    tok = rng.integers(0, cfg.vocab, (B, N)).astype(np.int32)
+    com = (rng.random((B, N)) < 0.2)
+    canvas = rt.Canvas(torch.from_numpy(tok).cuda(), torch.from_numpy(com.astype(np.uint8)).cuda(),
+                       seed=99, block=2)
+    for s in range(cfg.max_steps):
+        H = (rng.integers(0, 8, (B, N)) * 0.25).astype(np.float32)   # ties + below threshold
+        H[0, 3] = np.nan
+        am = rng.integers(0, cfg.vocab, (B, N)).astype(np.int32)
+        canvas.step = s
+        nunc = rt.test_commit(model, canvas, torch.from_numpy(H).cuda(), torch.from_numpy(am).cuda())
+        torch.cuda.synchronize()
+        for b in range(B):
+            om.commit_select(H[b].astype(np.float64), am[b], tok[b], com[b], s, cfg.max_steps,
+                             cfg.threshold)
+            om.renoise(tok[b], com[b], 99, s, b, 2, cfg.vocab)
+        np.testing.assert_array_equal(to_host(canvas.committed).astype(bool), com)
+        np.testing.assert_array_equal(to_host(canvas.tokens), tok)
+        np.testing.assert_array_equal(to_host(nunc), (~com).sum(1))
+    assert com.all()
+
+
+# ----------------------------------------------------------------------------- step-locked loop
+
+def _run_locked(rt, cfg, max_steps=None, keep_logits=True):
+    inp, model, kv = _gpu_setup(rt, cfg)
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=cfg.act_dtype == "bf16")
+    ost = om.init_state(cfg, cfg.seed)
+    B, N = cfg.batch, cfg.canvas_len
+    canvas = rt.Canvas.empty(B, N, cfg.seed)
+    rt.canvas_init(model, canvas)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+    ent = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    am = torch.empty(B, N, dtype=torch.int32, device="cuda")
+    gap = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    nunc = torch.empty(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B * N, cfg.vocab, dtype=torch.float32, device="cuda") if keep_logits else None
+    reps = []
+    steps = max_steps or cfg.max_steps
+    for s in range(steps):
+        say(f"  {cfg.name}: step {s}")
+        prev = ost.committed.copy()
+        rt.denoise_step(model, canvas, kv, entropy=ent, argmax=am, top2_gap=gap, n_uncommitted=nunc,
+                        logits=logits)
+        torch.cuda.synchronize()
+        ores = om.denoise_step(W, okv, ost, cfg, keep_logits=keep_logits)
+        gpu = dict(entropy=to_host(ent), argmax=to_host(am), tokens=to_host(canvas.tokens),
+                   committed=to_host(canvas.committed),
+                   logits=to_host(logits) if keep_logits else None)
+        rep = compare_step(cfg, ores, ost, gpu, prev)
+        say("   ", rep)
+        reps.append(rep)
+        assert canvas.step == ost.step
+        # resync to the oracle's state
+        canvas.tokens.copy_(torch.from_numpy(ost.tokens.astype(np.int32)))
+        canvas.committed.copy_(torch.from_numpy(ost.committed.astype(np.uint8)))
+        if int(ores.n_uncommitted.sum()) == 0:
+            break
+    model.close()
+    return reps
+
+
+def _assert_reports(cfg, reps):
+    for r in reps:
+        if not math.isnan(r.logits_rel):
+            assert r.logits_rel <= logits_tol(cfg), r
+        assert r.max_dH <= H_TOL, r
+        assert r.mism_argmax == 0, r
+        assert r.mism_commit == 0, r
+        assert r.mism_tokens == 0, r
+
+
+def test_c0_loop_step_locked(rt):
+    cfg = get_config("c0")
+    say("c0 full loop, fp32")
+    reps = _run_locked(rt, cfg)
+    _assert_reports(cfg, reps)
+
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_tiny_ragged_batch2_step_locked(rt, act):
+    # ragged canvas (40) and prompt (100) lengths, 2 canvases, several key tiles.
+    # The bf16 case uses the bf16 workloads' logit scale (LM head N(0, 1/d), logit
+    # std ~1): with std-6 logits over 512 ids a single bf16 rounding flip in the
+    # final hidden state already moves an entropy by ~1e-2 nats, so the 1e-3-nat
+    # entropy tolerance is only meaningful at the scale the bf16 workloads use.
+    cfg = tiny_config(name=f"tiny_ragged_{act}", act_dtype=act, expert_dtype=act, canvas_len=40,
+                      prompt_len=100, batch=2, head_dim=32, n_heads=2, seed=5, max_steps=5,
+                      lm_scale=6.0 if act == "fp32" else 1.0)
+    say(f"tiny ragged batch 2, {act}")
+    reps = _run_locked(rt, cfg)
+    _assert_reports(cfg, reps)
+
+
+def test_generate_canvas_matches_oracle_c0(rt):
+    cfg = get_config("c0")
+    say("c0 dg_generate_canvas vs oracle loop")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    steps = rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=False)
+    ost, osteps = om.generate_canvas(W, okv, cfg, cfg.seed)
+    assert steps == osteps
+    assert to_host(canvas.committed).all()
+    np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+    model.close()
+
+
+# ----------------------------------------------------------------------------- commit pass
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_commit_pass_matches_oracle(rt, act):
+    cfg = tiny_config(name=f"tiny_commit_{act}", act_dtype=act, expert_dtype=act, n_layers=2,
+                      head_dim=32, n_heads=2, prompt_mode="tokens", prompt_len=70, n_canvases=2,
+                      seed=8)
+    say(f"commit pass {act}: prompt 70 then a canvas of {cfg.canvas_len}")
+    inp = make_inputs(cfg, device="cuda")
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k.clone(), inp.kv_v.clone(), 0)
+    rt.commit_canvas(model, inp.prompt_tokens, kv)
+    canvas_tok = torch.randint(0, cfg.vocab, (1, cfg.canvas_len), dtype=torch.int32, device="cuda",
+                               generator=torch.Generator("cuda").manual_seed(3))
+    rt.commit_canvas(model, canvas_tok, kv)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, 0, bf16=act == "bf16")
+    om.commit_canvas(W, okv, to_host(inp.prompt_tokens).astype(np.int64), cfg)
+    om.commit_canvas(W, okv, to_host(canvas_tok).astype(np.int64), cfg)
+    assert kv.length == okv.length == 70 + cfg.canvas_len
+    n = kv.length
+    for name, g, o in (("k", kv.k, okv.k), ("v", kv.v, okv.v)):
+        gg = g[:, :, :, :n].double().cpu().numpy()
+        oo = o[:, :, :, :n].double().numpy()
+        rel = np.linalg.norm(gg - oo) / np.linalg.norm(oo)
+        say(f"   {name}: rel-L2 {rel:.3e}")
+        assert rel <= (1e-5 if act == "fp32" else 1e-2)
+    model.close()
+
+
+# ----------------------------------------------------------------------------- LM head alone
+
+def test_lm_head_c1_shape(rt):
+    cfg = get_config("c1")
+    say("LM head + confidence at 256 x 2048 x 262144")
+    g = torch.Generator("cuda").manual_seed(11)
+    lm = (torch.randn(cfg.vocab, cfg.d_model, device="cuda", generator=g) * cfg.d_model ** -0.5).to(
+        torch.bfloat16)
+    hf = torch.randn(256, cfg.d_model, device="cuda", generator=g).to(torch.bfloat16)
+    # a model with 1 tiny layer is enough to own the LM-head workspace
+    small = tiny_config(act_dtype="bf16", expert_dtype="bf16", vocab=cfg.vocab, d_model=cfg.d_model,
+                        canvas_len=256, head_dim=128, n_heads=16, d_expert=32, d_shared=32,
+                        prompt_len=64)
+    inp = make_inputs(small, device="cuda")
+    inp.lm_head = lm
+    model = rt.Model(inp)
+    ent, am, gap = rt.test_lm_head(model, hf)
+    torch.cuda.synchronize()
+    z = hf.double().cpu().numpy() @ lm.double().cpu().numpy().T
+    H, a, gp = om.confidence(z)
+    dH = np.abs(to_host(ent) - H).max()
+    say(f"   max |dH| = {dH:.3e}")
+    assert dH <= H_TOL
+    ok = gp >= 1e-3
+    assert (to_host(am)[ok] == a[ok]).all()
+    np.testing.assert_allclose(to_host(gap)[ok], gp[ok], atol=2e-3)
+    model.close()
+
+
+# ----------------------------------------------------------------------------- c1 step
+
+def test_c1_single_step(rt):
+    cfg = get_config("c1")
+    say("c1 single denoise step (bf16, 1 layer, P=1024, 128 experts, V=262144)")
+    reps = _run_locked(rt, cfg, max_steps=1)
+    _assert_reports(cfg, reps)

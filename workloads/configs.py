@@ -90,4 +90,5 @@ def get_config(name: str) -> Config:
 
 def tiny_config(**kw) -> Config:
     """A c0-shaped config with overrides, for unit tests."""
-    return _C0.replace(name="tiny", **kw)
+    kw.setdefault("name", "tiny")
+    return _C0.replace(**kw)
