@@ -103,6 +103,9 @@ def main():
                     help="kernel class timed for the roofline (moe_gateup, moe_down, lm_head, attn)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times and exit "
+                         "(reference for the HBM byte counters)")
     ap.add_argument("--breakdown", action="store_true",
                     help="after the timed region, time every kernel class (stderr)")
     args = ap.parse_args()
@@ -115,6 +118,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calib:
+        n = args.copy_calib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "copies": 5}), flush=True)
+        return
 
     from diffusion_decoding_amd import _lib
     from diffusion_decoding_amd import runtime as rt
