@@ -91,6 +91,61 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------- LM-head partials
+
+// Online-softmax summary of a set of logits z of one row: m = max z,
+// s = sum e^(z-m), t = sum e^(z-m)(z-m), sec = second largest z, idx = lowest
+// column holding the max (INT_MAX: empty set).  The row's entropy is
+// ln(s) - t/s.
+struct LmPart {
+  float m, s, t, sec;
+  int idx;
+};
+
+__device__ __forceinline__ LmPart lm_empty_part() {
+  LmPart p;
+  p.m = -INFINITY;
+  p.s = 0.f;
+  p.t = 0.f;
+  p.sec = -INFINITY;
+  p.idx = 0x7fffffff;
+  return p;
+}
+
+// Summary of the union of two disjoint column sets; equal maxima keep the
+// lower index and make the second max equal to the max.
+__device__ __forceinline__ LmPart lm_combine(LmPart a, LmPart b) {
+  if (b.idx == 0x7fffffff) return a;
+  if (a.idx == 0x7fffffff) return b;
+  LmPart r;
+  const float M = fmaxf(a.m, b.m);
+  const float ea = __expf(a.m - M), eb = __expf(b.m - M);
+  r.s = a.s * ea + b.s * eb;
+  r.t = ea * (a.t + (a.m - M) * a.s) + eb * (b.t + (b.m - M) * b.s);
+  r.m = M;
+  if (a.m > b.m) {
+    r.idx = a.idx;
+    r.sec = fmaxf(a.sec, b.m);
+  } else if (b.m > a.m) {
+    r.idx = b.idx;
+    r.sec = fmaxf(b.sec, a.m);
+  } else {
+    r.idx = min(a.idx, b.idx);
+    r.sec = a.m;
+  }
+  return r;
+}
+
+__device__ __forceinline__ LmPart lm_shfl_xor(const LmPart& a, int o) {
+  LmPart r;
+  r.m = __shfl_xor(a.m, o, 64);
+  r.s = __shfl_xor(a.s, o, 64);
+  r.t = __shfl_xor(a.t, o, 64);
+  r.sec = __shfl_xor(a.sec, o, 64);
+  r.idx = __shfl_xor(a.idx, o, 64);
+  return r;
+}
+
 // ---------------------------------------------------------------------------- Philox4x32-10
 
 // Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011):

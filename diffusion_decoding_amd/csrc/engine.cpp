@@ -212,21 +212,32 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
     HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
   }
-  {
-    ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
-    GemmArgs g;  // routed gate/up + SwiGLU, rows gathered per expert
-    g.A = m->a; g.lda = d; g.a_rows = m->pair_row; g.B = w.w_gu; g.ldb = d;
-    g.b_gstride = 2LL * de * d; g.b_scale = w.s_gu; g.s_gstride = 2LL * de;
-    g.M = T * k; g.N = de; g.K = d; g.g_off = m->off; g.C = m->h; g.ldc = de; g.swiglu_half = de;
-    HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, E, st));
-  }
-  {
-    ProfScope ps(m, DG_PROF_MOE_DOWN, st);
-    GemmArgs g;  // routed down
-    g.A = m->h; g.lda = de; g.B = w.w_d; g.ldb = de; g.b_gstride = (long long)d * de;
-    g.b_scale = w.s_d; g.s_gstride = d;
-    g.M = T * k; g.N = d; g.K = de; g.g_off = m->off; g.C = m->y; g.ldc = d;
-    HIP_OK(gemm(at, m->wt, EPI_F32, g, E, st));
+  if (at == ACT_BF16) {
+    {
+      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU
+      HIP_OK(moe_experts(m->wt, true, m->a, m->pair_row, m->off, E, w.w_gu, w.s_gu, d, de, m->h, st));
+    }
+    {
+      ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down
+      HIP_OK(moe_experts(m->wt, false, m->h, m->pair_row, m->off, E, w.w_d, w.s_d, de, d, m->y, st));
+    }
+  } else {
+    {
+      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
+      GemmArgs g;  // routed gate/up + SwiGLU, rows gathered per expert
+      g.A = m->a; g.lda = d; g.a_rows = m->pair_row; g.B = w.w_gu; g.ldb = d;
+      g.b_gstride = 2LL * de * d; g.b_scale = w.s_gu; g.s_gstride = 2LL * de;
+      g.M = T * k; g.N = de; g.K = d; g.g_off = m->off; g.C = m->h; g.ldc = de; g.swiglu_half = de;
+      HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, E, st));
+    }
+    {
+      ProfScope ps(m, DG_PROF_MOE_DOWN, st);
+      GemmArgs g;  // routed down
+      g.A = m->h; g.lda = de; g.B = w.w_d; g.ldb = de; g.b_gstride = (long long)d * de;
+      g.b_scale = w.s_d; g.s_gstride = d;
+      g.M = T * k; g.N = d; g.K = de; g.g_off = m->off; g.C = m->y; g.ldc = d;
+      HIP_OK(gemm(at, m->wt, EPI_F32, g, E, st));
+    }
   }
   {
     ProfScope ps(m, DG_PROF_SHARED, st);
@@ -343,8 +354,8 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   if (max_batch <= 0 || max_tokens < 0 || max_kv < 0)
     return fail(DG_ERR_INVALID_ARG, "max_batch must be > 0, max_tokens and max_kv >= 0");
   const int ntok = std::max(max_tokens, cfg->canvas_len);
-  if ((long long)max_batch * ntok * cfg->top_k > 8192)
-    return fail(DG_ERR_SHAPE, "max_batch * tokens * top_k must be <= 8192");
+  if ((long long)max_batch * ntok > 1024)
+    return fail(DG_ERR_SHAPE, "max_batch * max(max_tokens, canvas_len) must be <= 1024");
 
   dg_model* m = new dg_model();
   m->cfg = *cfg;
@@ -361,7 +372,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   const size_t T = m->Tmax, d = cfg->d_model, A = (size_t)cfg->n_heads * cfg->head_dim;
   const size_t E = cfg->n_experts, k = cfg->top_k, de = cfg->d_expert, ds = cfg->d_shared;
   const size_t Tc = (size_t)max_batch * cfg->canvas_len;
-  m->lm_ntiles = lm_tiles(cfg->vocab);
+  m->lm_ntiles = lm_tiles(m->at, cfg->d_model, cfg->vocab);
   const size_t es = m->esz;
   struct Req {
     void** p;

@@ -49,45 +49,6 @@ __device__ __forceinline__ u32x4 load_chunk_bf(const fp8* p) {
 }
 __device__ __forceinline__ u32x4 load_chunk_f(const float* p) { return *(const u32x4*)p; }
 
-struct LmPart {
-  float m, s, t, sec;
-  int idx;
-};
-
-__device__ __forceinline__ bool lm_empty(const LmPart& a) { return a.idx == INT_MAX; }
-
-__device__ __forceinline__ LmPart lm_combine(LmPart a, LmPart b) {
-  if (lm_empty(b)) return a;
-  if (lm_empty(a)) return b;
-  LmPart r;
-  float M = fmaxf(a.m, b.m);
-  float ea = __expf(a.m - M), eb = __expf(b.m - M);
-  r.s = a.s * ea + b.s * eb;
-  r.t = ea * (a.t + (a.m - M) * a.s) + eb * (b.t + (b.m - M) * b.s);
-  r.m = M;
-  if (a.m > b.m) {
-    r.idx = a.idx;
-    r.sec = fmaxf(a.sec, b.m);
-  } else if (b.m > a.m) {
-    r.idx = b.idx;
-    r.sec = fmaxf(b.sec, a.m);
-  } else {
-    r.idx = min(a.idx, b.idx);
-    r.sec = a.m;
-  }
-  return r;
-}
-
-__device__ __forceinline__ LmPart lm_shfl_xor(const LmPart& a, int o) {
-  LmPart r;
-  r.m = __shfl_xor(a.m, o, 64);
-  r.s = __shfl_xor(a.s, o, 64);
-  r.t = __shfl_xor(a.t, o, 64);
-  r.sec = __shfl_xor(a.sec, o, 64);
-  r.idx = __shfl_xor(a.idx, o, 64);
-  return r;
-}
-
 template <typename TA, typename TB, int BM, int BN, int EPI>
 __global__ __launch_bounds__(NT) void gemm_nt(GemmArgs g) {
   constexpr bool F32 = std::is_same<TA, float>::value;
@@ -278,12 +239,7 @@ __global__ __launch_bounds__(NT) void gemm_nt(GemmArgs g) {
       constexpr int TPR = NT / BM, CPT = BN / TPR;
       static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0, "row split");
       const int r = tid / TPR, sub = tid % TPR;
-      LmPart p;
-      p.m = -INFINITY;
-      p.sec = -INFINITY;
-      p.idx = INT_MAX;
-      p.s = 0.f;
-      p.t = 0.f;
+      LmPart p = lm_empty_part();
 #pragma unroll 4
       for (int c = sub * CPT; c < sub * CPT + CPT; ++c) {
         int n = n0 + c;
@@ -297,7 +253,7 @@ __global__ __launch_bounds__(NT) void gemm_nt(GemmArgs g) {
           p.sec = z;
         }
       }
-      if (!lm_empty(p)) {
+      if (p.idx != INT_MAX) {
         for (int c = sub * CPT; c < sub * CPT + CPT; ++c) {
           int n = n0 + c;
           if (n >= g.N) break;
@@ -328,12 +284,7 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const float* part, int T,
                                                        float* H, int* am, float* gap) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= T) return;
-  LmPart acc;
-  acc.m = -INFINITY;
-  acc.sec = -INFINITY;
-  acc.idx = INT_MAX;
-  acc.s = 0.f;
-  acc.t = 0.f;
+  LmPart acc = lm_empty_part();
   const float* base = part + (long long)row * n_tiles * 5;
   for (int t = lane; t < n_tiles; t += 64) {
     LmPart p;
@@ -377,10 +328,13 @@ int launch_epi(GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st) {
 
 }  // namespace
 
-int lm_tiles(int vocab) { return (vocab + 63) / 64; }
+int lm_tiles(ActType at, int K, int vocab) {
+  return tgemm_supported(at, K) ? lm_tiles_tiled(vocab) : (vocab + 63) / 64;
+}
 
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st) {
   if (g.K % BK) return int(hipErrorInvalidValue);
+  if (!g.g_off && tgemm_supported(at, g.K)) return tgemm(wt, epi, g, st);
   if (at == ACT_F32 && wt == W_F32) return launch_epi<float, float>(epi, g, groups, st);
   if (at == ACT_BF16 && wt == W_BF16) return launch_epi<bf16, bf16>(epi, g, groups, st);
   if (at == ACT_BF16 && wt == W_FP8) {

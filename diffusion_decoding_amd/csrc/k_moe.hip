@@ -1,0 +1,299 @@
+// Routed-expert GEMMs of the MoE FFN on gfx950 (zhichai.net 深度拆解, "MoE 效率":
+// 128 fine-grained experts, each token routed to 8 of them).  At a 256-token
+// canvas an expert sees about 16 tokens per step, so the work is a stream of
+// every expert's weights through the MFMA units at 16 FLOP per byte: the
+// kernels are written for HBM bandwidth, not for MFMA throughput.
+//
+// Layout of the work: a few workgroups per expert (gate/up: 2, one per CU at
+// 128 experts), each owning a contiguous range of the expert's output rows, so every
+// workgroup streams the same number of weight bytes and the grid is balanced
+// whatever the routing.  A workgroup first stages the expert's token rows (up
+// to 32, all K) in LDS once -- they are the other MFMA operand and are read
+// by all of its waves -- then each wave streams its own 16 NB weight rows
+// (gate/up: 16 NB gate rows and the matching up rows) from HBM straight into
+// MFMA operand registers, MD k-steps ahead.  Staging the tokens once per
+// workgroup matters: token loads issued inside the k loop compete with the
+// weight stream for the same load path and cut its bandwidth by a third.
+// Every weight byte is read once per step (experts with more than 32 pairs
+// take one pass per 32).  Weight loads are unconditional -- rows past the end
+// are clamped to a valid row and their results are never stored -- so the
+// compiler waits for exactly the oldest stage.
+//
+// MFMA 16x16x32 bf16 with the weights as operand A (16 weight rows) and the
+// tokens as operand B (16 tokens): lane l then holds token l % 16 and weight
+// rows 4 (l / 16) + 0..3 of the 16x16 result, i.e. four consecutive outputs of
+// one token, stored as one 8-byte (bf16) or 16-byte (fp32) write.
+//
+// gate/up: h[p][j] = bf16(silu(g) * u), g = x_p . W_gate[j], u = x_p . W_up[j]
+// down:    y[p][n] = h_p . W_down[n]  (fp32; combined per token later)
+// fp8 weights (E4M3FN codes) are widened exactly to bf16 in registers and the
+// per-row scale is applied to the fp32 accumulator.
+#include <type_traits>
+
+#include "dg_common.h"
+#include "kernels.h"
+
+namespace dg {
+namespace {
+
+constexpr int MTMAX = 2;   // 16-token tiles per pass over the weights
+
+struct f8 {
+  uint8_t v;
+};
+
+// 8 consecutive weights of a row as an MFMA operand (8 bf16), loaded through
+// a buffer resource over one expert's weights: lane offsets are 32-bit,
+// fragment offsets are uniform (scalar), stage offsets are immediates, and
+// rows past the expert's end read as zero -- a handful of registers however
+// many fragments and stages are in flight.
+template <typename TW> struct WLoad;
+template <> struct WLoad<bf16> {
+  using raw = u32x4;
+  static constexpr int BYTES = 2;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ u32x4 widen(raw v) { return v; }
+};
+template <> struct WLoad<f8> {
+  using raw = u32x2;
+  static constexpr int BYTES = 1;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ u32x4 widen(raw c) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w = c[h];
+      r[2 * h] = uint32_t(e4m3_to_bf16_bits(w & 0xffu)) |
+                 (uint32_t(e4m3_to_bf16_bits((w >> 8) & 0xffu)) << 16);
+      r[2 * h + 1] = uint32_t(e4m3_to_bf16_bits((w >> 16) & 0xffu)) |
+                     (uint32_t(e4m3_to_bf16_bits(w >> 24)) << 16);
+    }
+    return r;
+  }
+};
+
+struct MoeArgs {
+  const bf16* X;        // token activations: gate/up [T][K] (rows gathered), down [pairs][K]
+  const int* pair_row;  // gate/up: token of each pair slot; down: unused (row = pair)
+  const int* off;       // [E+1] pair ranges per expert
+  const void* W;        // gate/up [E][2*Nout][K]; down [E][Nout][K]
+  const float* scale;   // fp8: [E][rows of W per expert]
+  int K;                // reduction length (multiple of 32)
+  int Nout;             // outputs per token: d_expert (gate/up) or d_model (down)
+  void* out;            // gate/up: h bf16 [pairs][Nout]; down: y fp32 [pairs][Nout]
+};
+
+// The expert's token rows of one pass (up to 16 MTMAX of them, all K) are
+// staged once per workgroup in LDS, zero-filled past the last pair; the four
+// waves read their operand-B fragments from there, so the only global loads
+// in the k loop are the weight stream.
+template <int MT>
+__device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pitch, int pbeg, int rows,
+                                             bool gather) {
+  const int cpr = a.K / 8;  // 16-byte chunks per row
+  const int total = 16 * MT * cpr, nt = blockDim.x;
+  // batches of 4 loads per thread in flight before their LDS stores
+  for (int c0 = threadIdx.x; c0 < total; c0 += 4 * nt) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * nt, r = c / cpr, k = (c - r * cpr) * 8;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (c < total && r < rows) {
+        const long long row = gather ? (long long)a.pair_row[pbeg + r] : (long long)(pbeg + r);
+        v[u] = *(const u32x4*)(a.X + row * a.K + k);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * nt, r = c / cpr, k = (c - r * cpr) * 8;
+      if (c < total) *(u32x4*)(xs + r * pitch + k) = v[u];
+    }
+  }
+}
+
+// One wave: output rows n0 .. n0 + 16 NB - 1 (for gate/up: those gate rows
+// and the matching up rows) of expert e against the MT 16-token tiles staged
+// in xs (pass rows pbeg .. pbeg + rows - 1 of the expert's pairs).
+template <typename TW, bool GU, int NB, int MD, int MT>
+__device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int pitch, int e, int n0,
+                                         int pbeg, int rows) {
+  using WL = WLoad<TW>;
+  using wraw = typename WL::raw;
+  constexpr int NW = GU ? 2 * NB : NB;    // weight fragments per k-step: gate blocks, then up blocks
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+  const int K = a.K;
+  const long long wrows = GU ? 2LL * a.Nout : a.Nout;
+  const TW* We = (const TW*)a.W + (long long)e * wrows * K;
+  constexpr int WB = WL::BYTES;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)We, (short)0, int(wrows * K * WB), 0x00020000);
+  // lane: row n0 + c16 of each fragment, k-slots 8 g4 .. 8 g4 + 7 of each 32-k step;
+  // fragment f adds a uniform row offset (block f % NB; up rows for f >= NB)
+  const int voff0 = ((n0 + c16) * K + 8 * g4) * WB;
+  int soff[NW];
+#pragma unroll
+  for (int f = 0; f < NW; ++f) soff[f] = (16 * (f % NB) + (f < NB ? 0 : a.Nout)) * K * WB;
+  const bf16* xr = xs + c16 * pitch + 8 * g4;
+
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KS = K / 32;
+  wraw rw[MD][NW];
+  auto ld = [&](int ks, wraw* rw_) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rw_[w] = WL::load(rsrc, voff0 + ks * 32 * WB, soff[w]);
+  };
+  // Slot u of the register ring holds weight stage k with k % MD == u.  The
+  // main loop has no conditions and the MFMAs read a slot before its refill
+  // is issued into the same registers, so the ring needs no copies and the
+  // compiler's wait before a slot is for exactly that slot's loads (the
+  // MD - 1 later stages stay in flight); the scheduling barriers keep the
+  // loads in stage order.
+  auto step = [&](int ks, wraw* rw_, bool refill, int next) {
+    u32x4 xv[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * 32);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const u32x4 wv = WL::widen(rw_[w]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) ld(next, rw_);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int s = 0; s < MD; ++s) ld(min(s, KS - 1), rw[s]);
+  int k0 = 0;
+  for (; k0 + 2 * MD <= KS; k0 += MD) {
+#pragma unroll
+    for (int u = 0; u < MD; ++u) step(k0 + u, rw[u], true, k0 + u + MD);
+  }
+  // the last 1 .. 2*MD - 1 stages
+#pragma unroll
+  for (int u = 0; u < MD; ++u)
+    if (k0 + u < KS) step(k0 + u, rw[u], k0 + u + MD < KS, k0 + u + MD);
+#pragma unroll
+  for (int u = 0; u < MD; ++u)
+    if (k0 + MD + u < KS) step(k0 + MD + u, rw[u], false, 0);
+
+  // lane: token 16 t + c16 of the pass; outputs nb + 0..3 of block b
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int nb = n0 + 16 * b + 4 * g4;
+    if (nb >= a.Nout) continue;
+    float sc[GU ? 2 : 1][4];
+#pragma unroll
+    for (int h = 0; h < (GU ? 2 : 1); ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = min(nb + r, a.Nout - 1);
+        sc[h][r] = a.scale ? a.scale[(long long)e * wrows + (h ? a.Nout : 0) + n] : 1.f;
+      }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int r = 16 * t + c16;
+      if (r >= rows) continue;
+      const long long p = pbeg + r;
+      if constexpr (GU) {
+        bf16 hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float gt = acc[b][t][q] * sc[0][q], up = acc[NB + b][t][q] * sc[1][q];
+          hv[q] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
+        }
+        bf16* h = (bf16*)a.out + p * a.Nout + nb;
+        if (nb + 3 < a.Nout) {
+          *(u32x2*)h = u32x2{uint32_t(hv[0].v) | (uint32_t(hv[1].v) << 16),
+                             uint32_t(hv[2].v) | (uint32_t(hv[3].v) << 16)};
+        } else {
+          for (int q = 0; q < 4 && nb + q < a.Nout; ++q) h[q] = hv[q];
+        }
+      } else {
+        float* y = (float*)a.out + p * a.Nout + nb;
+        if (nb + 3 < a.Nout) {
+          *(f32x4*)y = f32x4{acc[b][t][0] * sc[0][0], acc[b][t][1] * sc[0][1], acc[b][t][2] * sc[0][2],
+                             acc[b][t][3] * sc[0][3]};
+        } else {
+          for (int q = 0; q < 4 && nb + q < a.Nout; ++q) y[q] = acc[b][t][q] * sc[0][q];
+        }
+      }
+    }
+  }
+}
+
+// grid (split, E), blockDim = 64 * waves, dynamic LDS = 16 MTMAX rows of
+// K + 8 bf16.  Workgroup x of expert e owns output rows [x * rows_per_wg,
+// (x + 1) * rows_per_wg); wave w of it owns 16 NB of them.  The expert's pairs
+// go in passes of up to 16 MTMAX tokens, each pass staging its tokens in LDS
+// and streaming the wave's weights once.
+template <typename TW, bool GU, int NB, int MD, int TMAX>
+__global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
+  extern __shared__ __attribute__((aligned(16))) bf16 xs[];
+  const int pitch = a.K + 8;
+  const int e = blockIdx.y;
+  const int pbeg = a.off[e], pcnt = a.off[e + 1] - pbeg;
+  if (pcnt <= 0) return;  // uniform over the workgroup
+  const int n0 = blockIdx.x * rows_per_wg + (threadIdx.x >> 6) * 16 * NB;
+  const bool active = n0 < min(a.Nout, (blockIdx.x + 1) * rows_per_wg);
+  for (int p0 = 0; p0 < pcnt; p0 += 16 * MTMAX) {
+    const int rows = min(16 * MTMAX, pcnt - p0);
+    if (p0) __syncthreads();  // the previous pass is done with xs
+    if (rows <= 16) stage_tokens<1>(a, xs, pitch, pbeg + p0, rows, GU);
+    else stage_tokens<MTMAX>(a, xs, pitch, pbeg + p0, rows, GU);
+    __syncthreads();
+    if (active) {
+      if (rows <= 16) moe_wave<TW, GU, NB, MD, 1>(a, xs, pitch, e, n0, pbeg + p0, rows);
+      else moe_wave<TW, GU, NB, MD, MTMAX>(a, xs, pitch, e, n0, pbeg + p0, rows);
+    }
+  }
+}
+
+template <typename TW, bool GU, int NB, int MD, int TMAX>
+int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
+  const int blocks = (a.Nout + 16 * NB - 1) / (16 * NB);       // 16 NB-row wave blocks per expert
+  const int waves = (blocks + split - 1) / split;              // per workgroup
+  if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
+  const size_t lds = size_t(16 * MTMAX) * (a.K + 8) * sizeof(bf16);
+  if (lds > 160 * 1024) return int(hipErrorInvalidValue);
+  (void)hipFuncSetAttribute((const void*)moe_kernel<TW, GU, NB, MD, TMAX>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipLaunchKernelGGL((moe_kernel<TW, GU, NB, MD, TMAX>), dim3(split, E), dim3(64 * waves), lds, st, a,
+                     waves * 16 * NB);
+  return int(hipGetLastError());
+}
+
+// gate/up: 32 outputs (64 weight rows) per wave, 2 workgroups of up to 12
+// waves per expert (704 threads at d_expert 704: the token stage of all K
+// takes most of the LDS, so one workgroup per CU); down: 32 outputs per
+// wave, 4 waves per workgroup (K = d_expert is short: three workgroups share
+// a CU).  The thread bound sets the register budget.
+template <typename TW>
+int launch(bool gu, const MoeArgs& a, int E, hipStream_t st) {
+  if (gu) return launch_k<TW, true, 2, 4, 768>(a, E, 2, st);
+  const int blocks = (a.Nout + 31) / 32;
+  return launch_k<TW, false, 2, 8, 256>(a, E, (blocks + 3) / 4, st);
+}
+
+}  // namespace
+
+int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
+                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st) {
+  if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
+  MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
+  if (wt == W_BF16) return launch<bf16>(gate_up, a, E, st);
+  if (wt == W_FP8) return launch<f8>(gate_up, a, E, st);
+  return int(hipErrorInvalidValue);
+}
+
+}  // namespace dg

@@ -6,8 +6,8 @@
 // equals the full router softmax restricted to the picks and renormalised.
 // router_permute: one workgroup builds the expert histogram, its exclusive
 // scan, and the expert-major, token-ascending permutation of the (token, slot)
-// pairs with wave ballots and popcount prefix sums -- no atomics, so the
-// layout is deterministic.
+// pairs from per-expert token bitmasks and popcount prefix sums; the layout is
+// deterministic.
 #include <climits>
 
 #include "dg_common.h"
@@ -70,58 +70,73 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T, i
 }
 
 constexpr int PERM_THREADS = 1024;
-constexpr int PERM_MAX_PAIRS = 8192;
+constexpr int PERM_MAX_TOKENS = 1024;
+constexpr int PERM_WORDS = PERM_MAX_TOKENS / 64;
 
+// One workgroup.  Each expert gets a bitmask over tokens (bit t set when token
+// t routes to it), built with LDS OR-atomics -- the result does not depend on
+// their order.  Expert e's pairs occupy [off[e], off[e+1]) in token order, so
+// the slot of pair (t, j) is off[e] plus the number of earlier tokens in e's
+// mask: a per-word prefix plus one popcount.
 __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, int T, int E, int k,
                                                                int* off, int* pair_row, int* pos) {
-  __shared__ int ids_s[PERM_MAX_PAIRS];
-  __shared__ int cnt_s[257];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int NW = PERM_THREADS / 64;
+  __shared__ unsigned long long mask[256 * PERM_WORDS];
+  __shared__ unsigned short wpre[256 * PERM_WORDS];
+  __shared__ int cnt_s[256];
+  __shared__ int off_s[257];
+  const int tid = threadIdx.x;
+  const int W = (T + 63) >> 6;
   const int P = T * k;
-  for (int i = threadIdx.x; i < P; i += PERM_THREADS) ids_s[i] = ids[i];
+  for (int i = tid; i < E * W; i += PERM_THREADS) mask[(i / W) * PERM_WORDS + i % W] = 0ull;
   __syncthreads();
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int e = wave; e < E; e += NW) {
-    int c = 0;
-    for (int t0 = 0; t0 < T; t0 += 64) {
-      const int t = t0 + lane;
-      bool mem = false;
-      if (t < T)
-        for (int j = 0; j < k; ++j) mem |= ids_s[t * k + j] == e;
-      c += __popcll(__ballot(mem));
-    }
-    if (lane == 0) cnt_s[e] = c;
+  for (int p = tid; p < P; p += PERM_THREADS) {
+    const int t = p / k, e = ids[p];
+    atomicOr(&mask[e * PERM_WORDS + (t >> 6)], 1ull << (t & 63));
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  // per-expert word prefixes and counts (one thread per expert)
+  for (int e = tid; e < E; e += PERM_THREADS) {
     int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt_s[e];
-      cnt_s[e] = run;
-      off[e] = run;
-      run += c;
+    for (int w = 0; w < W; ++w) {
+      wpre[e * PERM_WORDS + w] = (unsigned short)run;
+      run += __popcll(mask[e * PERM_WORDS + w]);
     }
-    cnt_s[E] = run;
-    off[E] = run;
+    cnt_s[e] = run;
   }
   __syncthreads();
-  for (int e = wave; e < E; e += NW) {
-    int base = cnt_s[e];
-    for (int t0 = 0; t0 < T; t0 += 64) {
-      const int t = t0 + lane;
-      int slot = -1;
-      if (t < T)
-        for (int j = 0; j < k; ++j)
-          if (ids_s[t * k + j] == e) slot = j;
-      const unsigned long long mask = __ballot(slot >= 0);
-      if (slot >= 0) {
-        const int p = base + __popcll(mask & lt);
-        pair_row[p] = t;
-        pos[t * k + slot] = p;
-      }
-      base += __popcll(mask);
+  // exclusive scan of the counts by wave 0: lane l owns experts 4l .. 4l+3
+  if (tid < 64) {
+    int c[4], s = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      c[u] = e < E ? cnt_s[e] : 0;
+      s += c[u];
     }
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - s;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      if (e < E) off_s[e] = run;
+      run += c[u];
+    }
+    if (tid == 63) off_s[E] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += PERM_THREADS) off[e] = off_s[e];
+  for (int p = tid; p < P; p += PERM_THREADS) {
+    const int t = p / k, e = ids[p];
+    const unsigned long long below = (1ull << (t & 63)) - 1ull;
+    const int slot = off_s[e] + wpre[e * PERM_WORDS + (t >> 6)] +
+                     __popcll(mask[e * PERM_WORDS + (t >> 6)] & below);
+    pair_row[slot] = t;
+    pos[p] = slot;
   }
 }
 
@@ -136,7 +151,8 @@ int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hi
 
 int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,
                    hipStream_t st) {
-  if (T * k > PERM_MAX_PAIRS || E > 256) return int(hipErrorInvalidValue);
+  if (T <= 0) return 0;
+  if (T > PERM_MAX_TOKENS || E > 256 || k > E) return int(hipErrorInvalidValue);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, st, ids, T, E, k, off, pair_row,
                      pos);
   return int(hipGetLastError());

@@ -1,0 +1,335 @@
+// Tiled bf16 GEMM for the dense projections of the denoise step on gfx950
+// (QKV, O-projection, router, shared expert, LM head): C = A * B^T with A the
+// [M][K] activations and B the [N][K] weights (bf16, or OCP E4M3FN codes with
+// one fp32 scale per weight row), fp32 accumulation on MFMA 16x16x32 bf16.
+//
+// Pipeline: 64-deep k stages; each thread keeps D stages of its share of the
+// A and B tiles in flight in registers (global loads of 8 rows x 128 B per
+// wave instruction), so the HBM latency is covered by the loads of later
+// stages rather than by occupancy; stages pass through a double-buffered LDS
+// tile from which the 4 waves read their MFMA fragments.
+//
+// Tile order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets a
+// contiguous run of tiles in which the M tiles of one weight tile are
+// neighbours, so the weight tile is fetched from HBM once into that XCD's L2.
+//
+// Epilogues run from the accumulators.  The LM-head epilogue reduces each row
+// of the tile to an online-softmax partial (max, sum e^(z-max),
+// sum e^(z-max)(z-max), second max, argmax) so logits never reach HBM; the
+// merge kernel folds a row's partials into its entropy and argmax (entropy as
+// the confidence of a canvas position: DiffusionGemma解析,
+// "换个路数：整片并行去噪的生成机制").
+#include <climits>
+#include <type_traits>
+
+#include "dg_common.h"
+#include "kernels.h"
+
+namespace dg {
+namespace {
+
+constexpr int SK = 64;       // k per stage
+constexpr int TNT = 256;     // threads per workgroup
+constexpr int LDK = SK + 8;  // LDS row pitch (bf16 elements): 144 B
+
+struct f8 {
+  uint8_t v;
+};
+
+// 8 E4M3FN codes -> 8 bf16 values (exact).
+__device__ __forceinline__ u32x4 f8x8_to_bf16x8(u32x2 c) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = c[h];
+    r[2 * h] = uint32_t(e4m3_to_bf16_bits(w & 0xffu)) |
+               (uint32_t(e4m3_to_bf16_bits((w >> 8) & 0xffu)) << 16);
+    r[2 * h + 1] = uint32_t(e4m3_to_bf16_bits((w >> 16) & 0xffu)) |
+                   (uint32_t(e4m3_to_bf16_bits(w >> 24)) << 16);
+  }
+  return r;
+}
+
+template <typename TB> struct BChunk;
+template <> struct BChunk<bf16> {
+  using type = u32x4;  // 8 bf16
+  static __device__ __forceinline__ type load(const bf16* p) { return *(const u32x4*)p; }
+  static __device__ __forceinline__ u32x4 widen(type v) { return v; }
+  static __device__ __forceinline__ type zero() { return u32x4{0u, 0u, 0u, 0u}; }
+};
+template <> struct BChunk<f8> {
+  using type = u32x2;  // 8 codes
+  static __device__ __forceinline__ type load(const f8* p) { return *(const u32x2*)p; }
+  static __device__ __forceinline__ u32x4 widen(type v) { return f8x8_to_bf16x8(v); }
+  static __device__ __forceinline__ type zero() { return u32x2{0u, 0u}; }
+};
+
+// BM x BN tile, 4 waves as WAVES_M x (4 / WAVES_M), D stages in flight.
+// SWIGLU: the B tile holds gate and up rows interleaved in blocks of 16 (gate
+// rows j.., up rows half + j..), so a wave's fragment pair (2q, 2q+1) is the
+// gate/up pair of the same 16 outputs and the product is formed in registers.
+template <typename TB, int BM, int BN, int WAVES_M, int D, int EPI>
+__global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int CPR = SK / 8;  // 8-element chunks per row per stage
+  constexpr int A_PT = BM * CPR / TNT, B_PT = BN * CPR / TNT;
+  static_assert(BM * CPR % TNT == 0 && BN * CPR % TNT == 0, "tile rows must be multiples of 32");
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SWIGLU needs gate/up fragment pairs");
+  static_assert(EPI != EPI_LM || WAVES_N == 1, "LM epilogue needs whole tile rows per wave");
+  using BC = BChunk<TB>;
+  using bchunk = typename BC::type;
+
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
+
+  // XCD-aware tile index; the exit is uniform over the workgroup.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int tile = xcd * per_xcd + slot;
+  if (slot >= per_xcd || tile >= tiles_m * tiles_n) return;
+  const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int wr = (wave / WAVES_N) * WM, wc = (wave % WAVES_N) * WN;
+  const int m0 = tm * BM;
+  const int KT = g.K / SK;
+
+  const bf16* Ag = (const bf16*)g.A;
+  const TB* Bg = (const TB*)g.B;
+
+  // this thread's load slots: chunk c -> row c / CPR, k offset (c % CPR) * 8
+  const bf16* ap[A_PT];
+#pragma unroll
+  for (int u = 0; u < A_PT; ++u) {
+    const int c = tid + u * TNT, r = c / CPR, kc = (c % CPR) * 8;
+    const int m = m0 + r;
+    ap[u] = Ag + (long long)(m < g.M ? m : 0) * g.lda + kc;
+  }
+  const TB* bp[B_PT];
+#pragma unroll
+  for (int u = 0; u < B_PT; ++u) {
+    const int c = tid + u * TNT, r = c / CPR, kc = (c % CPR) * 8;
+    long long brow;
+    bool ok;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int blk = r >> 4, j = tn * (BN / 2) + (blk >> 1) * 16 + (r & 15);
+      ok = j < g.N;
+      brow = (blk & 1) ? (long long)g.swiglu_half + j : j;
+    } else {
+      const int n = tn * BN + r;
+      ok = n < g.N;
+      brow = n;
+    }
+    bp[u] = Bg + (ok ? brow : 0) * g.ldb + kc;
+  }
+
+  // Loads are unconditional (rows past M or N read row 0 and only feed
+  // accumulator rows/columns the epilogue never stores), so the compiler can
+  // wait for exactly the oldest stage instead of draining every load in flight.
+  u32x4 ra[D][A_PT];
+  bchunk rb[D][B_PT];
+  auto gload = [&](int kt, u32x4* ra_, bchunk* rb_) {
+#pragma unroll
+    for (int u = 0; u < A_PT; ++u) ra_[u] = *(const u32x4*)(ap[u] + kt * SK);
+#pragma unroll
+    for (int u = 0; u < B_PT; ++u) rb_[u] = BC::load(bp[u] + kt * SK);
+  };
+  auto lstore = [&](int buf, const u32x4* ra_, const bchunk* rb_) {
+#pragma unroll
+    for (int u = 0; u < A_PT; ++u) {
+      const int c = tid + u * TNT;
+      *(u32x4*)&As[buf][(c / CPR) * LDK + (c % CPR) * 8] = ra_[u];
+    }
+#pragma unroll
+    for (int u = 0; u < B_PT; ++u) {
+      const int c = tid + u * TNT;
+      *(u32x4*)&Bs[buf][(c / CPR) * LDK + (c % CPR) * 8] = BC::widen(rb_[u]);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < D; ++s) gload(min(s, KT - 1), ra[s], rb[s]);
+  lstore(0, ra[0], rb[0]);
+  __syncthreads();
+
+  for (int kt0 = 0; kt0 < KT; kt0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int kt = kt0 + u;
+      if (kt < KT) {
+        // ring slot u held stage kt (already in LDS): refill it with stage
+        // kt + D (past the end: the last stage again, an L2 hit)
+        gload(min(kt + D, KT - 1), ra[u], rb[u]);
+        const int buf = kt & 1;
+#pragma unroll
+        for (int s = 0; s < SK / 32; ++s) {
+          u32x4 af[FM], bfr[FN];
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            af[i] = *(const u32x4*)&As[buf][(wr + 16 * i + c16) * LDK + 32 * s + 8 * g4];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            bfr[j] = *(const u32x4*)&Bs[buf][(wc + 16 * j + c16) * LDK + 32 * s + 8 * g4];
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+        }
+        if (kt + 1 < KT) lstore(buf ^ 1, ra[(u + 1) % D], rb[(u + 1) % D]);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogues
+  const float* Sg = g.b_scale;
+  if constexpr (EPI == EPI_LM) {
+    // rows wr + 16i + 4g4 + r; this lane holds columns 16j + c16 of each
+    float* part = g.part;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        LmPart p = lm_empty_part();
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = tn * BN + wc + 16 * j + c16;
+          if (n < g.N) {
+            const float z = acc[i][j][r];
+            if (z > p.m) {
+              p.sec = p.m;
+              p.m = z;
+              p.idx = n;
+            } else if (z > p.sec) {
+              p.sec = z;
+            }
+          }
+        }
+        if (p.idx != INT_MAX) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = tn * BN + wc + 16 * j + c16;
+            if (n < g.N) {
+              const float dz = acc[i][j][r] - p.m;
+              const float e = __expf(dz);
+              p.s += e;
+              p.t += e * dz;
+            }
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) p = lm_combine(p, lm_shfl_xor(p, o));
+        const int m = m0 + wr + 16 * i + 4 * g4 + r;
+        if (c16 == 0 && m < g.M) {
+          float* o = part + ((long long)m * tiles_n + tn) * 5;
+          o[0] = p.m;
+          o[1] = p.s;
+          o[2] = p.t;
+          o[3] = p.sec;
+          o[4] = __int_as_float(p.idx);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int q = 0; q < FN / 2; ++q) {
+      const int j = tn * (BN / 2) + (wc / 2) + 16 * q + c16;
+      if (j >= g.N) continue;
+      const float sg = Sg ? Sg[j] : 1.f, su = Sg ? Sg[g.swiglu_half + j] : 1.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wr + 16 * i + 4 * g4 + r;
+          if (m >= g.M) continue;
+          const float gt = acc[i][2 * q][r] * sg, up = acc[i][2 * q + 1][r] * su;
+          const float h = gt / (1.0f + __expf(-gt)) * up;
+          ((bf16*)g.C)[(long long)m * g.ldc + j] = f32_to_bf16(h);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = tn * BN + wc + 16 * j + c16;
+      if (n >= g.N) continue;
+      const float sc = Sg ? Sg[n] : 1.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wr + 16 * i + 4 * g4 + r;
+          if (m >= g.M) continue;
+          const float v = acc[i][j][r] * sc;
+          const long long o = (long long)m * g.ldc + n;
+          if constexpr (EPI == EPI_F32) {
+            ((float*)g.C)[o] = v;
+          } else if constexpr (EPI == EPI_ACT) {
+            ((bf16*)g.C)[o] = f32_to_bf16(v);
+          } else {
+            bf16* C = (bf16*)g.C;
+            C[o] = f32_to_bf16(to_f32(C[o]) + v);
+          }
+        }
+    }
+  }
+}
+
+template <typename TB, int BM, int BN, int WAVES_M, int D, int EPI>
+int launch_t(const GemmArgs& g, hipStream_t st) {
+  const int bn_out = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + bn_out - 1) / bn_out;
+  const int total = tiles_m * tiles_n;
+  if (total == 0) return 0;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((tgemm_kernel<TB, BM, BN, WAVES_M, D, EPI>), dim3(8 * per_xcd), dim3(TNT), 0, st, g,
+                     tiles_m, tiles_n, per_xcd);
+  return int(hipGetLastError());
+}
+
+// Tile shape per epilogue and size: enough workgroups to cover 256 CUs at
+// M = 256 while keeping weight tiles shared through L2.
+template <typename TB>
+int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
+  const long long tiles64 = (long long)((g.M + 63) / 64) * ((g.N + 63) / 64);
+  switch (epi) {
+    case EPI_LM:
+      return launch_t<TB, 256, 128, 4, 2, EPI_LM>(g, st);
+    case EPI_SWIGLU:
+      return launch_t<TB, 64, 64, 2, 4, EPI_SWIGLU>(g, st);
+    case EPI_ACT:
+      if (tiles64 >= 256) return launch_t<TB, 64, 64, 2, 4, EPI_ACT>(g, st);
+      return launch_t<TB, 64, 32, 2, 4, EPI_ACT>(g, st);
+    case EPI_RESID:
+      if (tiles64 >= 256) return launch_t<TB, 64, 64, 2, 4, EPI_RESID>(g, st);
+      return launch_t<TB, 64, 32, 2, 4, EPI_RESID>(g, st);
+    case EPI_F32:
+      if (tiles64 >= 256) return launch_t<TB, 64, 64, 2, 4, EPI_F32>(g, st);
+      if (tiles64 >= 64) return launch_t<TB, 64, 32, 2, 4, EPI_F32>(g, st);
+      return launch_t<TB, 32, 32, 2, 4, EPI_F32>(g, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+}  // namespace
+
+int lm_tiles_tiled(int vocab) { return (vocab + 127) / 128; }
+
+bool tgemm_supported(ActType at, int K) { return at == ACT_BF16 && K % SK == 0; }
+
+int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st) {
+  if (g.K % SK || g.g_off) return int(hipErrorInvalidValue);
+  if (wt == W_BF16) return dispatch<bf16>(epi, g, st);
+  if (wt == W_FP8 && epi != EPI_LM) return dispatch<f8>(epi, g, st);
+  return int(hipErrorInvalidValue);
+}
+
+}  // namespace dg

@@ -39,11 +39,23 @@ struct GemmArgs {
 
 // Returns 0 or a HIP error code.
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st);
-// Number of vocab tiles the LM epilogue writes per row.
-int lm_tiles(int vocab);
+// Number of vocab tiles the LM epilogue writes per row (depends on the kernel
+// gemm() routes the LM head to).
+int lm_tiles(ActType at, int K, int vocab);
+// Tiled bf16 kernel (k_tgemm.hip): used by gemm() for ungrouped bf16 GEMMs with K % 64 == 0.
+bool tgemm_supported(ActType at, int K);
+int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st);
+int lm_tiles_tiled(int vocab);
 // Merge LM partials of T rows into entropy / argmax / top-2 gap.
 int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap,
              hipStream_t st);
+
+// ---------------------------------------------------------------- routed experts (k_moe.hip)
+// bf16 activations, bf16 or fp8 weights.  gate_up: h[p][j] = bf16(silu(x.Wg_j) * x.Wu_j) with x the
+// token row pair_row[p] of X [T][K] and W [E][2*Nout][K]; otherwise y[p][n] = X[p] . W[n] (fp32)
+// with W [E][Nout][K].  Pairs of expert e are [off[e], off[e+1]).
+int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
+                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st);
 
 // ---------------------------------------------------------------- attention (k_attn.hip)
 struct AttnArgs {
