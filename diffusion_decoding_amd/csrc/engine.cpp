@@ -206,10 +206,12 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   HIP_OK(rmsnorm(at, m->x, T, d, c.rms_eps, m->a, st));
   {
     ProfScope ps(m, DG_PROF_ROUTER, st);
-    GemmArgs g;
-    g.A = m->a; g.lda = d; g.B = w.wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = m->rlog; g.ldc = E;
-    HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
-    HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
+    {
+      GemmArgs g;
+      g.A = m->a; g.lda = d; g.B = w.wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = m->rlog; g.ldc = E;
+      HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
+      HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
+    }
     HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
   }
   if (at == ACT_BF16) {
@@ -247,7 +249,8 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, 1, st));
     GemmArgs g2;  // shared down
     g2.A = m->hs; g2.lda = ds; g2.B = w.ws_d; g2.ldb = ds; g2.b_scale = w.ss_d;
-    g2.M = T; g2.N = d; g2.K = ds; g2.C = m->ys; g2.ldc = d;
+    g2.M = T; g2.N = d; g2.K = ds; g2.ldc = d;
+    g2.C = m->ys;
     HIP_OK(gemm(at, m->wt, EPI_F32, g2, 1, st));
   }
   HIP_OK(moe_combine(at, m->x, m->y, m->ys, m->topk_w, m->pos, T, k, d, st));

@@ -223,8 +223,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
 template <int DH>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
                                                         int per_xcd) {
-  constexpr int LDKS = DH + 8;   // K row pitch (elements)
-  constexpr int LDV = 64 + 8;    // V^T row pitch
+  // row pitches: odd multiples of 32 B keep the fragment reads at full LDS rate
+  constexpr int LDKS = DH + 16;  // K row pitch (elements)
+  constexpr int LDV = 64 + 16;   // V^T row pitch
   constexpr int NDF = DH / 16;
   constexpr int NQ = DH / 32;
   constexpr int KCH = 64 * DH / 8;            // 16-byte K chunks per tile

@@ -103,6 +103,24 @@ __global__ void combine_kernel(T* x, const float* y, const float* ys, const floa
   }
 }
 
+// bf16, d % 4 == 0: grid (T, ceil(d / 1024)), thread -> 4 consecutive columns.
+// Same arithmetic order as combine_kernel: experts in slot order, then the
+// shared expert, then one rounding of the residual add.
+__global__ __launch_bounds__(256) void combine_bf16_kernel(bf16* x, const float* y, const float* ys,
+                                                           const float* w, const int* pos, int k, int d) {
+  const int t = blockIdx.x, c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= d) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) acc += w[t * k + j] * *(const f32x4*)(y + (long long)pos[t * k + j] * d + c);
+  acc += *(const f32x4*)(ys + (long long)t * d + c);
+  bf16* xp = x + (long long)t * d + c;
+  const u32x2 xv = *(const u32x2*)xp;
+  const float x0 = __uint_as_float(xv[0] << 16), x1 = __uint_as_float(xv[0] & 0xffff0000u);
+  const float x2 = __uint_as_float(xv[1] << 16), x3 = __uint_as_float(xv[1] & 0xffff0000u);
+  *(u32x2*)xp = u32x2{uint32_t(f32_to_bf16(x0 + acc[0]).v) | (uint32_t(f32_to_bf16(x1 + acc[1]).v) << 16),
+                      uint32_t(f32_to_bf16(x2 + acc[2]).v) | (uint32_t(f32_to_bf16(x3 + acc[3]).v) << 16)};
+}
+
 __global__ void canvas_init_kernel(int* tok, uint8_t* committed, int N, uint64_t seed, uint32_t block,
                                    int vocab) {
   const int b = blockIdx.y;
@@ -217,7 +235,10 @@ int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, int p
 int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
                 int T, int k, int d, hipStream_t st) {
   if (T <= 0) return 0;
-  if (at == ACT_BF16)
+  if (at == ACT_BF16 && d % 4 == 0)
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(T, (d + 1023) / 1024), dim3(256), 0, st, (bf16*)x, y, ys, w,
+                       pos, k, d);
+  else if (at == ACT_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16>, dim3(T), dim3(256), 0, st, (bf16*)x, y, ys, w, pos, k, d);
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (float*)x, y, ys, w, pos, k, d);

@@ -233,14 +233,14 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
 }
 
 // grid (split, E), blockDim = 64 * waves, dynamic LDS = 16 MTMAX rows of
-// K + 8 bf16.  Workgroup x of expert e owns output rows [x * rows_per_wg,
+// K + 16 bf16.  Workgroup x of expert e owns output rows [x * rows_per_wg,
 // (x + 1) * rows_per_wg); wave w of it owns 16 NB of them.  The expert's pairs
 // go in passes of up to 16 MTMAX tokens, each pass staging its tokens in LDS
 // and streaming the wave's weights once.
 template <typename TW, bool GU, int NB, int MD, int TMAX>
 __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
-  const int pitch = a.K + 8;
+  const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
   const int e = blockIdx.y;
   const int pbeg = a.off[e], pcnt = a.off[e + 1] - pbeg;
   if (pcnt <= 0) return;  // uniform over the workgroup
@@ -264,7 +264,7 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   const int blocks = (a.Nout + 16 * NB - 1) / (16 * NB);       // 16 NB-row wave blocks per expert
   const int waves = (blocks + split - 1) / split;              // per workgroup
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
-  const size_t lds = size_t(16 * MTMAX) * (a.K + 8) * sizeof(bf16);
+  const size_t lds = size_t(16 * MTMAX) * (a.K + 16) * sizeof(bf16);
   if (lds > 160 * 1024) return int(hipErrorInvalidValue);
   (void)hipFuncSetAttribute((const void*)moe_kernel<TW, GU, NB, MD, TMAX>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));

@@ -28,9 +28,8 @@
 namespace dg {
 namespace {
 
-constexpr int SK = 64;       // k per stage
 constexpr int TNT = 256;     // threads per workgroup
-constexpr int LDK = SK + 8;  // LDS row pitch (bf16 elements): 144 B
+constexpr int SK_MIN = 64;   // K must be a multiple of this
 
 struct f8 {
   uint8_t v;
@@ -68,8 +67,16 @@ template <> struct BChunk<f8> {
 // SWIGLU: the B tile holds gate and up rows interleaved in blocks of 16 (gate
 // rows j.., up rows half + j..), so a wave's fragment pair (2q, 2q+1) is the
 // gate/up pair of the same 16 outputs and the product is formed in registers.
-template <typename TB, int BM, int BN, int WAVES_M, int D, int EPI>
-__global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+// KG k-groups: KG x 4 waves per workgroup, group q reducing stages
+// [q KT/KG, (q+1) KT/KG) with its own LDS buffers; the groups' accumulators
+// are summed through LDS in group order at the end.  More waves per tile
+// hide the per-stage LDS and barrier latency that otherwise bounds a tile.
+template <typename TB, int BM, int BN, int WAVES_M, int D, int EPI, int SK = 64, int KG = 1>
+__global__ __launch_bounds__(TNT * KG) void tgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+  // LDS row pitch SK + 16 elements: fragment reads (16 rows x 64 B per
+  // ds_read_b128) run at full LDS rate on gfx950 when the row pitch is an odd
+  // multiple of 32 B, at half rate for other multiples of 16 B (measured).
+  constexpr int LDK = SK + 16;
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 16, FN = WN / 16;
@@ -82,8 +89,8 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
   using BC = BChunk<TB>;
   using bchunk = typename BC::type;
 
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 lds_all[KG][2][(BM + BN) * LDK];
+  static_assert(KG == 1 || (size_t)(KG - 1) * BM * BN * 4 <= sizeof(lds_all), "reduction space");
 
   // XCD-aware tile index; the exit is uniform over the workgroup.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -91,11 +98,15 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
   if (slot >= per_xcd || tile >= tiles_m * tiles_n) return;
   const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, grp = threadIdx.x / TNT;
+  const int tid = threadIdx.x % TNT, wave = tid >> 6;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int wr = (wave / WAVES_N) * WM, wc = (wave % WAVES_N) * WN;
   const int m0 = tm * BM;
-  const int KT = g.K / SK;
+  const int KT = g.K / SK / KG;           // stages per group
+  const int kbase = grp * KT * SK;        // this group's first k
+  bf16 (*As)[(BM + BN) * LDK] = lds_all[grp];
+  const int boff = BM * LDK;              // B tile follows the A tile in each buffer
 
   const bf16* Ag = (const bf16*)g.A;
   const TB* Bg = (const TB*)g.B;
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
   for (int u = 0; u < A_PT; ++u) {
     const int c = tid + u * TNT, r = c / CPR, kc = (c % CPR) * 8;
     const int m = m0 + r;
-    ap[u] = Ag + (long long)(m < g.M ? m : 0) * g.lda + kc;
+    ap[u] = Ag + (long long)(m < g.M ? m : 0) * g.lda + kbase + kc;
   }
   const TB* bp[B_PT];
 #pragma unroll
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
       ok = n < g.N;
       brow = n;
     }
-    bp[u] = Bg + (ok ? brow : 0) * g.ldb + kc;
+    bp[u] = Bg + (ok ? brow : 0) * g.ldb + kbase + kc;
   }
 
   // Loads are unconditional (rows past M or N read row 0 and only feed
@@ -146,7 +157,7 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
 #pragma unroll
     for (int u = 0; u < B_PT; ++u) {
       const int c = tid + u * TNT;
-      *(u32x4*)&Bs[buf][(c / CPR) * LDK + (c % CPR) * 8] = BC::widen(rb_[u]);
+      *(u32x4*)&As[buf][boff + (c / CPR) * LDK + (c % CPR) * 8] = BC::widen(rb_[u]);
     }
   };
 
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
             af[i] = *(const u32x4*)&As[buf][(wr + 16 * i + c16) * LDK + 32 * s + 8 * g4];
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            bfr[j] = *(const u32x4*)&Bs[buf][(wc + 16 * j + c16) * LDK + 32 * s + 8 * g4];
+            bfr[j] = *(const u32x4*)&As[buf][boff + (wc + 16 * j + c16) * LDK + 32 * s + 8 * g4];
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -188,6 +199,32 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
         __syncthreads();
       }
     }
+  }
+
+  if constexpr (KG > 1) {
+    // groups 1.. hand their accumulators to group 0, which adds them in group order
+    float* red = (float*)&lds_all[0][0][0];
+    constexpr int PER = FM * FN * 4;  // floats per lane
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red[(((grp - 1) * 4 + wave) * PER + (i * FN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int q = 1; q < KG; ++q)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] += red[(((q - 1) * 4 + wave) * PER + (i * FN + j) * 4 + r) * 64 + lane];
   }
 
   // ---------------------------------------------------------------- epilogues
@@ -283,15 +320,16 @@ __global__ __launch_bounds__(TNT) void tgemm_kernel(GemmArgs g, int tiles_m, int
   }
 }
 
-template <typename TB, int BM, int BN, int WAVES_M, int D, int EPI>
+template <typename TB, int BM, int BN, int WAVES_M, int D, int EPI, int SK = 64, int KG = 1>
 int launch_t(const GemmArgs& g, hipStream_t st) {
+  if (g.K % (SK * KG)) return int(hipErrorInvalidValue);
   const int bn_out = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + bn_out - 1) / bn_out;
   const int total = tiles_m * tiles_n;
   if (total == 0) return 0;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((tgemm_kernel<TB, BM, BN, WAVES_M, D, EPI>), dim3(8 * per_xcd), dim3(TNT), 0, st, g,
-                     tiles_m, tiles_n, per_xcd);
+  hipLaunchKernelGGL((tgemm_kernel<TB, BM, BN, WAVES_M, D, EPI, SK, KG>), dim3(8 * per_xcd), dim3(TNT * KG), 0,
+                     st, g, tiles_m, tiles_n, per_xcd);
   return int(hipGetLastError());
 }
 
@@ -323,10 +361,10 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
 
 int lm_tiles_tiled(int vocab) { return (vocab + 127) / 128; }
 
-bool tgemm_supported(ActType at, int K) { return at == ACT_BF16 && K % SK == 0; }
+bool tgemm_supported(ActType at, int K) { return at == ACT_BF16 && K % SK_MIN == 0; }
 
 int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st) {
-  if (g.K % SK || g.g_off) return int(hipErrorInvalidValue);
+  if (g.K % SK_MIN || g.g_off) return int(hipErrorInvalidValue);
   if (wt == W_BF16) return dispatch<bf16>(epi, g, st);
   if (wt == W_FP8 && epi != EPI_LM) return dispatch<f8>(epi, g, st);
   return int(hipErrorInvalidValue);
