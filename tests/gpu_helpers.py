@@ -1,0 +1,91 @@
+"""Shared driver for the GPU parity tests: run the HIP path and the oracle
+step-locked on the same canvas, compare each step, then resynchronise the GPU
+canvas to the oracle's state (test infrastructure; imports the oracle)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import model as om
+from tests.parity import compare_step, to_host
+from workloads import make_inputs
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class Pair:
+    """The GPU model + KV cache and the oracle weights + KV over one input set."""
+
+    def __init__(self, rt, cfg, kv_len=None, kv_capacity=None):
+        self.rt, self.cfg = rt, cfg
+        self.inp = make_inputs(cfg, device="cuda", kv_capacity=kv_capacity)
+        self.model = rt.Model(self.inp)
+        n = self.inp.kv_len if kv_len is None else kv_len
+        self.kv = rt.KVCache(self.inp.kv_k.clone(), self.inp.kv_v.clone(), n)
+        self.W = om.Weights(self.inp, cache=True)
+        self.okv = om.KV(self.inp.kv_k, self.inp.kv_v, n, bf16=cfg.act_dtype == "bf16")
+
+    def close(self):
+        self.model.close()
+
+    def kv_rel(self):
+        """rel-L2 of the GPU cache rows in use against the oracle's."""
+        n = self.kv.length
+        out = []
+        for g, o in ((self.kv.k, self.okv.k), (self.kv.v, self.okv.v)):
+            gg = g[:, :, :, :n].double().cpu().numpy()
+            oo = o[:, :, :, :n].double().numpy()
+            out.append(float(np.linalg.norm(gg - oo) / max(np.linalg.norm(oo), 1e-30)))
+        return out
+
+    def resync_kv(self):
+        self.kv.k.copy_(self.okv.k.to(self.kv.k.dtype).to("cuda"))
+        self.kv.v.copy_(self.okv.v.to(self.kv.v.dtype).to("cuda"))
+        self.kv.length = self.okv.length
+
+    def commit(self, tokens: np.ndarray):
+        """Causal commit pass of tokens [B, n] on both sides."""
+        t = torch.from_numpy(np.ascontiguousarray(tokens.astype(np.int32))).to("cuda")
+        self.rt.commit_canvas(self.model, t, self.kv)
+        torch.cuda.synchronize()
+        om.commit_canvas(self.W, self.okv, tokens.astype(np.int64), self.cfg)
+
+    def run_locked(self, block=0, max_steps=None, keep_logits=True):
+        """Step-locked denoise loop; returns (step reports, oracle final state)."""
+        rt, cfg = self.rt, self.cfg
+        ost = om.init_state(cfg, cfg.seed, block)
+        B, N = cfg.batch, cfg.canvas_len
+        canvas = rt.Canvas.empty(B, N, cfg.seed, block)
+        rt.canvas_init(self.model, canvas)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+        ent = torch.empty(B, N, dtype=torch.float32, device="cuda")
+        am = torch.empty(B, N, dtype=torch.int32, device="cuda")
+        gap = torch.empty(B, N, dtype=torch.float32, device="cuda")
+        nunc = torch.empty(B, dtype=torch.int32, device="cuda")
+        logits = torch.empty(B * N, cfg.vocab, dtype=torch.float32, device="cuda") if keep_logits else None
+        reps = []
+        for s in range(max_steps or cfg.max_steps):
+            say(f"  {cfg.name}: block {block} step {s}")
+            prev = ost.committed.copy()
+            rt.denoise_step(self.model, canvas, self.kv, entropy=ent, argmax=am, top2_gap=gap,
+                            n_uncommitted=nunc, logits=logits)
+            torch.cuda.synchronize()
+            ores = om.denoise_step(self.W, self.okv, ost, cfg, keep_logits=keep_logits)
+            gpu = dict(entropy=to_host(ent), argmax=to_host(am), tokens=to_host(canvas.tokens),
+                       committed=to_host(canvas.committed),
+                       logits=to_host(logits) if keep_logits else None)
+            rep = compare_step(cfg, ores, ost, gpu, prev)
+            say("   ", rep)
+            reps.append(rep)
+            assert canvas.step == ost.step
+            canvas.tokens.copy_(torch.from_numpy(ost.tokens.astype(np.int32)))
+            canvas.committed.copy_(torch.from_numpy(ost.committed.astype(np.uint8)))
+            if int(ores.n_uncommitted.sum()) == 0:
+                break
+        return reps, ost

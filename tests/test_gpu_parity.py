@@ -13,7 +13,7 @@ import torch
 
 from oracle import model as om
 from oracle import philox
-from tests.parity import H_TOL, compare_step, logits_tol, to_host
+from tests.parity import H_TOL, compare_step, h_tol, logits_tol, to_host
 from workloads import get_config, make_inputs, tiny_config
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +131,7 @@ def _assert_reports(cfg, reps):
     for r in reps:
         if not math.isnan(r.logits_rel):
             assert r.logits_rel <= logits_tol(cfg), r
-        assert r.max_dH <= H_TOL, r
+        assert r.max_dH <= h_tol(cfg), r
         assert r.mism_argmax == 0, r
         assert r.mism_commit == 0, r
         assert r.mism_tokens == 0, r
