@@ -93,6 +93,91 @@ def cpu_baseline(inp, cfg, steps_per_canvas: float, layers: int):
     }
 
 
+def free_gpu(*objs):
+    import torch
+    for o in objs:
+        if hasattr(o, "close"):
+            o.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def time_loop(cfg, canvases: int, warmup: int):
+    """Whole canvases (init + denoise loop) of a prompt-KV workload; inputs resident."""
+    import torch
+
+    from diffusion_decoding_amd import runtime as rt
+    from workloads import make_inputs
+
+    log(f"[bench] generating inputs for {cfg.name} on the GPU")
+    inp = make_inputs(cfg, device="cuda")
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k, inp.kv_v, inp.kv_len)
+    canvas = rt.Canvas.empty(cfg.batch, cfg.canvas_len, cfg.seed)
+    for _ in range(warmup):
+        rt.canvas_init(model, canvas)
+        rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    steps = 0
+    t0 = time.perf_counter()
+    for _ in range(canvases):
+        rt.canvas_init(model, canvas)
+        steps += rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    free_gpu(model)
+    del inp, kv, canvas
+    free_gpu()
+    toks = cfg.batch * cfg.canvas_len * canvases
+    log(f"[bench] {cfg.name}: {canvases} canvases x batch {cfg.batch}, {steps} steps in {dt:.3f} s")
+    return {"workload": cfg.name, "batch": cfg.batch, "prompt_kv": cfg.prompt_len,
+            "canvas_tokens_per_s": toks / dt, "denoise_steps_per_s": steps / dt,
+            "ms_per_denoise_step": dt / steps * 1e3, "denoise_steps_per_canvas": steps / canvases}
+
+
+def time_block_ar(cfg, warmup: int = 1):
+    """Block-autoregressive generation: causal encode of the prompt, then
+    n_canvases canvases, each committed to the KV cache by a causal pass."""
+    import torch
+
+    from diffusion_decoding_amd import runtime as rt
+    from workloads import make_inputs
+
+    log(f"[bench] generating inputs for {cfg.name} on the GPU")
+    inp = make_inputs(cfg, device="cuda")
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k, inp.kv_v, 0)
+    canvas = rt.Canvas.empty(cfg.batch, cfg.canvas_len, cfg.seed)
+
+    def run():
+        kv.length = 0
+        rt.commit_canvas(model, inp.prompt_tokens, kv)
+        steps = 0
+        for c in range(cfg.n_canvases):
+            canvas.block = c
+            rt.canvas_init(model, canvas)
+            steps += rt.generate_canvas(model, canvas, kv)
+            rt.commit_canvas(model, canvas.tokens, kv)
+        return steps
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    steps = run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    free_gpu(model)
+    del inp, kv, canvas
+    free_gpu()
+    toks = cfg.batch * cfg.canvas_len * cfg.n_canvases
+    log(f"[bench] {cfg.name}: prompt {cfg.prompt_len} + {cfg.n_canvases} canvases, {steps} steps in {dt:.3f} s")
+    return {"workload": cfg.name, "expert_dtype": cfg.expert_dtype, "prompt_tokens": cfg.prompt_len,
+            "canvases": cfg.n_canvases, "canvas_tokens_per_s": toks / dt,
+            "denoise_steps_per_s": steps / dt, "ms_per_denoise_step_incl_commit": dt / steps * 1e3,
+            "note": "time includes the prompt encode and every causal commit pass"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +191,8 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times and exit "
                          "(reference for the HBM byte counters)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the batch-4 (c3) and block-autoregressive fp8 (c4) measurements")
     ap.add_argument("--breakdown", action="store_true",
                     help="after the timed region, time every kernel class (stderr)")
     args = ap.parse_args()
@@ -213,7 +300,12 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sampled step")
         out["cpu_baseline"] = cpu_baseline(inp, cfg, steps_per_canvas, max(1, min(args.cpu_layers, cfg.n_layers)))
-    model.close()
+    free_gpu(model)
+    del inp, kv, canvas
+    free_gpu()
+    if not args.no_extra and args.config == "c2":
+        out["batch4"] = time_loop(get_config("c3"), canvases=1, warmup=1)
+        out["block_ar_fp8"] = time_block_ar(get_config("c4"))
     print(json.dumps(out), flush=True)
 
 

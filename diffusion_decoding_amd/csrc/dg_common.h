@@ -57,6 +57,18 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// 8 OCP E4M3FN codes (bytes of c, low first) -> 8 bf16 values, exact: the
+// gfx950 packed conversion with scale 1 (checked against e4m3_to_bf16_bits
+// for all 65536 byte pairs on the device).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true));
+  return r;
+}
+
 // ---------------------------------------------------------------------------- MFMA
 
 // D = A(16x32) * B(32x16) + C on one wave; lane l supplies row/col (l % 16)

@@ -35,18 +35,7 @@ template <> struct LdsCfg<bf16> {
 
 // 16-byte chunk of 8 elements of B converted to the bf16 compute type.
 __device__ __forceinline__ u32x4 load_chunk_bf(const bf16* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ u32x4 load_chunk_bf(const fp8* p) {
-  u32x2 c = *(const u32x2*)p;
-  u32x4 r;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t w = c[h];
-    r[2 * h] = uint32_t(e4m3_to_bf16_bits(w & 0xff)) | (uint32_t(e4m3_to_bf16_bits((w >> 8) & 0xff)) << 16);
-    r[2 * h + 1] =
-        uint32_t(e4m3_to_bf16_bits((w >> 16) & 0xff)) | (uint32_t(e4m3_to_bf16_bits(w >> 24)) << 16);
-  }
-  return r;
-}
+__device__ __forceinline__ u32x4 load_chunk_bf(const fp8* p) { return e4m3x8_to_bf16x8(*(const u32x2*)p); }
 __device__ __forceinline__ u32x4 load_chunk_f(const float* p) { return *(const u32x4*)p; }
 
 template <typename TA, typename TB, int BM, int BN, int EPI>

@@ -42,37 +42,46 @@ struct f8 {
   uint8_t v;
 };
 
-// 8 consecutive weights of a row as an MFMA operand (8 bf16), loaded through
-// a buffer resource over one expert's weights: lane offsets are 32-bit,
-// fragment offsets are uniform (scalar), stage offsets are immediates, and
-// rows past the expert's end read as zero -- a handful of registers however
-// many fragments and stages are in flight.
-template <typename TW> struct WLoad;
-template <> struct WLoad<bf16> {
+// Weight formats.  A lane loads its slice of a weight row through a buffer
+// resource over one expert's weights: lane offsets are 32-bit, fragment
+// offsets are uniform (scalar), stage offsets are immediates, and rows past
+// the expert's end read as zero -- a handful of registers however many
+// fragments and stages are in flight.  A stage is SPS 32-k MFMA steps; lane
+// (c16, g4) holds KL consecutive k of its row at k offset lane_k(g4) in the
+// stage, and x_k(g4, t) gives the k offset, in the stage, of the 8 k-slots
+// it feeds into step t -- the token operand is read at the same offsets, so
+// any order of k within a stage is a valid split of the dot product.
+template <typename TW, int SPS_> struct WFmt;
+template <> struct WFmt<bf16, 1> {  // 8 bf16 per lane per step
   using raw = u32x4;
-  static constexpr int BYTES = 2;
+  static constexpr int BYTES = 1 * 2, SPS = 1;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   }
-  static __device__ __forceinline__ u32x4 widen(raw v) { return v; }
+  static __device__ __forceinline__ int lane_k(int g4) { return 8 * g4; }
+  static __device__ __forceinline__ int x_k(int g4, int) { return 8 * g4; }
+  static __device__ __forceinline__ u32x4 get(raw v, int) { return v; }
 };
-template <> struct WLoad<f8> {
+template <> struct WFmt<f8, 1> {  // 8 E4M3FN codes per lane per step (K % 64 != 0)
   using raw = u32x2;
-  static constexpr int BYTES = 1;
+  static constexpr int BYTES = 1, SPS = 1;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   }
-  static __device__ __forceinline__ u32x4 widen(raw c) {
-    u32x4 r;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t w = c[h];
-      r[2 * h] = uint32_t(e4m3_to_bf16_bits(w & 0xffu)) |
-                 (uint32_t(e4m3_to_bf16_bits((w >> 8) & 0xffu)) << 16);
-      r[2 * h + 1] = uint32_t(e4m3_to_bf16_bits((w >> 16) & 0xffu)) |
-                     (uint32_t(e4m3_to_bf16_bits(w >> 24)) << 16);
-    }
-    return r;
+  static __device__ __forceinline__ int lane_k(int g4) { return 8 * g4; }
+  static __device__ __forceinline__ int x_k(int g4, int) { return 8 * g4; }
+  static __device__ __forceinline__ u32x4 get(raw c, int) { return e4m3x8_to_bf16x8(c); }
+};
+template <> struct WFmt<f8, 2> {  // 16 E4M3FN codes per lane: two steps per 16-byte load
+  using raw = u32x4;
+  static constexpr int BYTES = 1, SPS = 2;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ int lane_k(int g4) { return 16 * g4; }
+  static __device__ __forceinline__ int x_k(int g4, int t) { return 16 * g4 + 8 * t; }
+  static __device__ __forceinline__ u32x4 get(raw c, int t) {
+    return e4m3x8_to_bf16x8(t ? u32x2{c[2], c[3]} : u32x2{c[0], c[1]});
   }
 };
 
@@ -119,26 +128,26 @@ __device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pit
 // One wave: output rows n0 .. n0 + 16 NB - 1 (for gate/up: those gate rows
 // and the matching up rows) of expert e against the MT 16-token tiles staged
 // in xs (pass rows pbeg .. pbeg + rows - 1 of the expert's pairs).
-template <typename TW, bool GU, int NB, int MD, int MT>
+template <typename WL, bool GU, int NB, int MD, int MT>
 __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int pitch, int e, int n0,
                                          int pbeg, int rows) {
-  using WL = WLoad<TW>;
   using wraw = typename WL::raw;
+  constexpr int SPS = WL::SPS, SKE = 32 * SPS;  // steps and k per stage
   constexpr int NW = GU ? 2 * NB : NB;    // weight fragments per k-step: gate blocks, then up blocks
   const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
   const int K = a.K;
   const long long wrows = GU ? 2LL * a.Nout : a.Nout;
-  const TW* We = (const TW*)a.W + (long long)e * wrows * K;
   constexpr int WB = WL::BYTES;
+  const char* We = (const char*)a.W + (long long)e * wrows * K * WB;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)We, (short)0, int(wrows * K * WB), 0x00020000);
-  // lane: row n0 + c16 of each fragment, k-slots 8 g4 .. 8 g4 + 7 of each 32-k step;
-  // fragment f adds a uniform row offset (block f % NB; up rows for f >= NB)
-  const int voff0 = ((n0 + c16) * K + 8 * g4) * WB;
+  // lane: row n0 + c16 of each fragment; fragment f adds a uniform row offset
+  // (block f % NB; up rows for f >= NB)
+  const int voff0 = ((n0 + c16) * K + WL::lane_k(g4)) * WB;
   int soff[NW];
 #pragma unroll
   for (int f = 0; f < NW; ++f) soff[f] = (16 * (f % NB) + (f < NB ? 0 : a.Nout)) * K * WB;
-  const bf16* xr = xs + c16 * pitch + 8 * g4;
+  const bf16* xr = xs + c16 * pitch;
 
   f32x4 acc[NW][MT];
 #pragma unroll
@@ -146,11 +155,11 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KS = K / 32;
+  const int KS = K / SKE;  // stages
   wraw rw[MD][NW];
   auto ld = [&](int ks, wraw* rw_) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) rw_[w] = WL::load(rsrc, voff0 + ks * 32 * WB, soff[w]);
+    for (int w = 0; w < NW; ++w) rw_[w] = WL::load(rsrc, voff0 + ks * SKE * WB, soff[w]);
   };
   // Slot u of the register ring holds weight stage k with k % MD == u.  The
   // main loop has no conditions and the MFMAs read a slot before its refill
@@ -159,14 +168,17 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
   // MD - 1 later stages stay in flight); the scheduling barriers keep the
   // loads in stage order.
   auto step = [&](int ks, wraw* rw_, bool refill, int next) {
-    u32x4 xv[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * 32);
+    for (int t2 = 0; t2 < SPS; ++t2) {
+      u32x4 xv[MT];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const u32x4 wv = WL::widen(rw_[w]);
+      for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * SKE + WL::x_k(g4, t2));
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
+      for (int w = 0; w < NW; ++w) {
+        const u32x4 wv = WL::get(rw_[w], t2);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (refill) ld(next, rw_);
@@ -237,7 +249,7 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
 // (x + 1) * rows_per_wg); wave w of it owns 16 NB of them.  The expert's pairs
 // go in passes of up to 16 MTMAX tokens, each pass staging its tokens in LDS
 // and streaming the wave's weights once.
-template <typename TW, bool GU, int NB, int MD, int TMAX>
+template <typename WL, bool GU, int NB, int MD, int TMAX>
 __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
   const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
@@ -253,22 +265,23 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
     else stage_tokens<MTMAX>(a, xs, pitch, pbeg + p0, rows, GU);
     __syncthreads();
     if (active) {
-      if (rows <= 16) moe_wave<TW, GU, NB, MD, 1>(a, xs, pitch, e, n0, pbeg + p0, rows);
-      else moe_wave<TW, GU, NB, MD, MTMAX>(a, xs, pitch, e, n0, pbeg + p0, rows);
+      if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, e, n0, pbeg + p0, rows);
+      else moe_wave<WL, GU, NB, MD, MTMAX>(a, xs, pitch, e, n0, pbeg + p0, rows);
     }
   }
 }
 
-template <typename TW, bool GU, int NB, int MD, int TMAX>
+template <typename WL, bool GU, int NB, int MD, int TMAX>
 int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
+  if (a.K % (32 * WL::SPS)) return int(hipErrorInvalidValue);
   const int blocks = (a.Nout + 16 * NB - 1) / (16 * NB);       // 16 NB-row wave blocks per expert
   const int waves = (blocks + split - 1) / split;              // per workgroup
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
   const size_t lds = size_t(16 * MTMAX) * (a.K + 16) * sizeof(bf16);
   if (lds > 160 * 1024) return int(hipErrorInvalidValue);
-  (void)hipFuncSetAttribute((const void*)moe_kernel<TW, GU, NB, MD, TMAX>,
+  (void)hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  hipLaunchKernelGGL((moe_kernel<TW, GU, NB, MD, TMAX>), dim3(split, E), dim3(64 * waves), lds, st, a,
+  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);
   return int(hipGetLastError());
 }
@@ -278,11 +291,11 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
 // takes most of the LDS, so one workgroup per CU); down: 32 outputs per
 // wave, 4 waves per workgroup (K = d_expert is short: three workgroups share
 // a CU).  The thread bound sets the register budget.
-template <typename TW>
+template <typename WL>
 int launch(bool gu, const MoeArgs& a, int E, hipStream_t st) {
-  if (gu) return launch_k<TW, true, 2, 4, 768>(a, E, 2, st);
+  if (gu) return launch_k<WL, true, 2, 4, 768>(a, E, 2, st);
   const int blocks = (a.Nout + 31) / 32;
-  return launch_k<TW, false, 2, 8, 256>(a, E, (blocks + 3) / 4, st);
+  return launch_k<WL, false, 2, 8, 256>(a, E, (blocks + 3) / 4, st);
 }
 
 }  // namespace
@@ -291,8 +304,9 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
                 const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st) {
   if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
   MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
-  if (wt == W_BF16) return launch<bf16>(gate_up, a, E, st);
-  if (wt == W_FP8) return launch<f8>(gate_up, a, E, st);
+  if (wt == W_BF16) return launch<WFmt<bf16, 1>>(gate_up, a, E, st);
+  if (wt == W_FP8 && K % 64 == 0) return launch<WFmt<f8, 2>>(gate_up, a, E, st);
+  if (wt == W_FP8) return launch<WFmt<f8, 1>>(gate_up, a, E, st);
   return int(hipErrorInvalidValue);
 }
 

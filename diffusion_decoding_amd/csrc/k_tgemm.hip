@@ -35,20 +35,6 @@ struct f8 {
   uint8_t v;
 };
 
-// 8 E4M3FN codes -> 8 bf16 values (exact).
-__device__ __forceinline__ u32x4 f8x8_to_bf16x8(u32x2 c) {
-  u32x4 r;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t w = c[h];
-    r[2 * h] = uint32_t(e4m3_to_bf16_bits(w & 0xffu)) |
-               (uint32_t(e4m3_to_bf16_bits((w >> 8) & 0xffu)) << 16);
-    r[2 * h + 1] = uint32_t(e4m3_to_bf16_bits((w >> 16) & 0xffu)) |
-                   (uint32_t(e4m3_to_bf16_bits(w >> 24)) << 16);
-  }
-  return r;
-}
-
 template <typename TB> struct BChunk;
 template <> struct BChunk<bf16> {
   using type = u32x4;  // 8 bf16
@@ -59,7 +45,7 @@ template <> struct BChunk<bf16> {
 template <> struct BChunk<f8> {
   using type = u32x2;  // 8 codes
   static __device__ __forceinline__ type load(const f8* p) { return *(const u32x2*)p; }
-  static __device__ __forceinline__ u32x4 widen(type v) { return f8x8_to_bf16x8(v); }
+  static __device__ __forceinline__ u32x4 widen(type v) { return e4m3x8_to_bf16x8(v); }
   static __device__ __forceinline__ type zero() { return u32x2{0u, 0u}; }
 };
 
