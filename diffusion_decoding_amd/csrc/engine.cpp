@@ -164,7 +164,9 @@ int check_config(const dg_config& c) {
 
 // One pre-norm block over T = B * n rows.  causal: rows are new tokens at
 // positions P.. written into the cache; otherwise canvas rows attend to the
-// first P cache rows plus the canvas.
+// first P cache rows plus the canvas.  On entry m->a holds rmsnorm(x); on
+// return x is updated and m->a holds rmsnorm of the new x (the next block's
+// input norm, or the final norm before the LM head).
 int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool causal, bool kv_only,
                   hipStream_t st) {
   const dg_config& c = m->cfg;
@@ -177,7 +179,6 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   char* kcache = (char*)kv->k + l * layer_stride * m->esz;
   char* vcache = (char*)kv->v + l * layer_stride * m->esz;
 
-  HIP_OK(rmsnorm(at, m->x, T, d, c.rms_eps, m->a, st));
   {
     ProfScope ps(m, DG_PROF_QKV, st);
     GemmArgs g;
@@ -269,7 +270,7 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     }
   }
   HIP_OK(hipStreamWaitEvent(st, m->ev_join, 0));
-  HIP_OK(moe_combine(at, m->x, m->y, m->ys, m->topk_w, m->pos, T, k, d, st));
+  HIP_OK(moe_combine_norm(at, m->x, m->y, m->ys, m->topk_w, m->pos, T, k, d, c.rms_eps, m->a, st));
   return DG_OK;
 }
 
@@ -304,11 +305,12 @@ int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* o
   const dg_config& cfg = m->cfg;
   const int B = c->batch, N = cfg.canvas_len, T = B * N, P = kv->length;
   HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, m->x, st));
+  HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
   for (int l = 0; l < cfg.n_layers; ++l) {
     int s = layer_forward(m, l, B, N, P, kv, false, false, st);
     if (s) return s;
   }
-  HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
+  // m->a now holds the final RMSNorm of x
   if (out && out->hidden)
     HIP_OK(hipMemcpyAsync(out->hidden, m->a, (size_t)T * cfg.d_model * m->esz, hipMemcpyDeviceToDevice, st));
   float* H = (out && out->entropy) ? out->entropy : m->H;
@@ -515,6 +517,7 @@ int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, v
   const dg_config& cfg = m->cfg;
   const int B = kv->batch, T = B * n, P = kv->length;
   HIP_OK(embed_gather(m->at, tokens, T, m->embed, cfg.d_model, m->x, st));
+  HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
   for (int l = 0; l < cfg.n_layers; ++l) {
     s = layer_forward(m, l, B, n, P, kv, true, l == cfg.n_layers - 1, st);
     if (s) return s;

@@ -121,6 +121,60 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(bf16* x, const float*
                       uint32_t(f32_to_bf16(x2 + acc[2]).v) | (uint32_t(f32_to_bf16(x3 + acc[3]).v) << 16)};
 }
 
+// bf16, d % 4 == 0, d <= 4096: one workgroup per token, one thread per 4
+// columns (blockDim = d / 4, rounded up to whole waves).
+// x[t] = round(x[t] + sum_j w_j y_j + ys) as combine_bf16_kernel (experts in
+// slot order, then the shared expert, one rounding), then the next block's
+// (or the final) RMSNorm of the rounded row: a[t] = round(x[t] *
+// rsqrt(mean x^2 + eps)).
+__global__ __launch_bounds__(1024) void combine_norm_bf16_kernel(bf16* x, const float* y, const float* ys,
+                                                                 const float* w, const int* pos, int k, int d,
+                                                                 float eps, bf16* a) {
+  __shared__ float red[16];
+  const int t = blockIdx.x, tid = threadIdx.x, c = tid * 4;
+  const bool live = c < d;
+  float xv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    // all k expert rows in flight at once; slots past k reread slot 0 with weight 0
+    f32x4 yv[8];
+    float wj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int jj = j < k ? j : 0;
+      wj[j] = j < k ? w[t * k + jj] : 0.f;
+      yv[j] = *(const f32x4*)(y + (long long)pos[t * k + jj] * d + c);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += wj[j] * yv[j];
+    acc += *(const f32x4*)(ys + (long long)t * d + c);
+    bf16* xp = x + (long long)t * d + c;
+    const u32x2 xo = *(const u32x2*)xp;
+    const float x0 = __uint_as_float(xo[0] << 16), x1 = __uint_as_float(xo[0] & 0xffff0000u);
+    const float x2 = __uint_as_float(xo[1] << 16), x3 = __uint_as_float(xo[1] & 0xffff0000u);
+    const bf16 r0 = f32_to_bf16(x0 + acc[0]), r1 = f32_to_bf16(x1 + acc[1]);
+    const bf16 r2 = f32_to_bf16(x2 + acc[2]), r3 = f32_to_bf16(x3 + acc[3]);
+    *(u32x2*)xp = u32x2{uint32_t(r0.v) | (uint32_t(r1.v) << 16), uint32_t(r2.v) | (uint32_t(r3.v) << 16)};
+    xv[0] = to_f32(r0);
+    xv[1] = to_f32(r1);
+    xv[2] = to_f32(r2);
+    xv[3] = to_f32(r3);
+  }
+  float ss = wave_sum(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
+  const int nw = blockDim.x >> 6;
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  ss = 0.f;
+  for (int i = 0; i < nw; ++i) ss += red[i];
+  const float inv = 1.0f / sqrtf(ss / float(d) + eps);
+  if (live) {
+    const bf16 a0 = f32_to_bf16(xv[0] * inv), a1 = f32_to_bf16(xv[1] * inv);
+    const bf16 a2 = f32_to_bf16(xv[2] * inv), a3 = f32_to_bf16(xv[3] * inv);
+    *(u32x2*)(a + (long long)t * d + c) =
+        u32x2{uint32_t(a0.v) | (uint32_t(a1.v) << 16), uint32_t(a2.v) | (uint32_t(a3.v) << 16)};
+  }
+}
+
 __global__ void canvas_init_kernel(int* tok, uint8_t* committed, int N, uint64_t seed, uint32_t block,
                                    int vocab) {
   const int b = blockIdx.y;
@@ -243,6 +297,20 @@ int moe_combine(ActType at, void* x, const float* y, const float* ys, const floa
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (float*)x, y, ys, w, pos, k, d);
   return int(hipGetLastError());
+}
+
+int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
+                     int T, int k, int d, float eps, void* a, hipStream_t st) {
+  if (T <= 0) return 0;
+  if (at == ACT_BF16 && d % 4 == 0 && d <= 4096 && k <= 8) {
+    const int threads = ((d / 4 + 63) / 64) * 64;
+    hipLaunchKernelGGL(combine_norm_bf16_kernel, dim3(T), dim3(threads), 0, st, (bf16*)x, y, ys, w, pos, k, d,
+                       eps, (bf16*)a);
+    return int(hipGetLastError());
+  }
+  int e = moe_combine(at, x, y, ys, w, pos, T, k, d, st);
+  if (e) return e;
+  return rmsnorm(at, x, T, d, eps, a, st);
 }
 
 int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block, int vocab,

@@ -4,6 +4,7 @@
 // router_topk: one wave per token picks the k largest router logits (ties to
 // the lower expert id) and weights them by a softmax over the k picks, which
 // equals the full router softmax restricted to the picks and renormalised.
+// (A NaN logit is not ranked meaningfully; router logits are finite.)
 // router_permute: one workgroup builds the expert histogram, its exclusive
 // scan, and the expert-major, token-ascending permutation of the (token, slot)
 // pairs from per-expert token bitmasks and popcount prefix sums; the layout is
@@ -16,55 +17,55 @@
 namespace dg {
 namespace {
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T, int E, int k, int* ids,
-                                                   float* w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (t >= T) return;
-  float v[4];
-  bool live[4];
+// One wave per token.  Each (logit, expert) pair becomes one 64-bit key that
+// orders by logit, then by lower expert id (the low word holds ~id), so every
+// selection round is a single 64-bit max-reduction across the wave.
+__device__ __forceinline__ unsigned long long topk_key(float f, int e) {
+  uint32_t b = __float_as_uint(f);
+  b ^= (b >> 31) ? 0xffffffffu : 0x80000000u;  // order-preserving map to unsigned
+  return ((unsigned long long)b << 32) | (0xffffffffu - uint32_t(e));
+}
+
+__device__ __forceinline__ float topk_value(unsigned long long key) {
+  uint32_t b = uint32_t(key >> 32);
+  b = (b & 0x80000000u) ? (b ^ 0x80000000u) : ~b;
+  return __uint_as_float(b);
+}
+
+__global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, int E, int k, int* ids,
+                                                  float* w) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  unsigned long long key[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int e = lane + 64 * u;
-    live[u] = e < E;
-    v[u] = live[u] ? logits[(long long)t * E + e] : -INFINITY;
+    key[u] = e < E ? topk_key(logits[(long long)t * E + e], e) : 0ull;
   }
-  float top[8];
-  int topi[8];
+  unsigned long long top[8];
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    unsigned long long best = key[0];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = lane + 64 * u;
-      if (live[u] && (v[u] > bv || (v[u] == bv && e < bi))) {
-        bv = v[u];
-        bi = e;
-      }
-    }
+    for (int u = 1; u < 4; ++u) best = key[u] > best ? key[u] : best;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      const unsigned long long ob = __shfl_xor(best, o, 64);
+      best = ob > best ? ob : best;
     }
-    top[j] = bv;
-    topi[j] = bi;
+    top[j] = best;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (lane + 64 * u == bi) live[u] = false;
+      if (key[u] == best) key[u] = 0ull;
   }
   if (lane == 0) {
-    float s = 0.f, ex[8];
+    const float m = topk_value(top[0]);
+    float sum = 0.f, ex[8];
     for (int j = 0; j < k; ++j) {
-      ex[j] = __expf(top[j] - top[0]);
-      s += ex[j];
+      ex[j] = __expf(topk_value(top[j]) - m);
+      sum += ex[j];
     }
     for (int j = 0; j < k; ++j) {
-      ids[t * k + j] = topi[j];
-      w[t * k + j] = ex[j] / s;
+      ids[t * k + j] = int(0xffffffffu - uint32_t(top[j]));
+      w[t * k + j] = ex[j] / sum;
     }
   }
 }
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, i
 int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hipStream_t st) {
   if (T <= 0) return 0;
   if (E > 256 || k > 8 || k > E) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, k, ids, w);
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
   return int(hipGetLastError());
 }
 

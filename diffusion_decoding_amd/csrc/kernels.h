@@ -88,6 +88,9 @@ int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, int p
 // x[t] = round(x[t] + sum_j w[t][j] * y[pos[t][j]] + ys[t])
 int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w,
                 const int* pos, int T, int k, int d, hipStream_t st);
+// moe_combine, then a = rmsnorm(x) of the updated rows (one fused kernel for bf16)
+int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
+                     int T, int k, int d, float eps, void* a, hipStream_t st);
 int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block,
                 int vocab, hipStream_t st);
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N,
