@@ -66,6 +66,7 @@ _SIGS = {
     "dg_generate_canvas": [c_void_p, POINTER(dg_canvas), POINTER(dg_kv), POINTER(c_int32),
                            c_void_p],
     "dg_commit_canvas": [c_void_p, c_void_p, c_int32, POINTER(dg_kv), c_void_p],
+    "dg_pack_experts": [c_void_p, c_void_p, ctypes.c_int64, c_int32, c_int32, c_int32, c_void_p],
     "dg_profile_kernel": [c_void_p, c_int32],
     "dg_profile_read": [c_void_p, POINTER(ctypes.c_double), POINTER(ctypes.c_int64)],
     "dg_test_philox": [c_uint64, c_uint32, c_uint32, c_uint32, c_uint32, c_uint32, c_int32,
@@ -138,6 +139,10 @@ def dg_generate_canvas(handle, canvas, kv, stream) -> int:
 
 def dg_commit_canvas(handle, tokens_ptr, n, kv, stream):
     _call("dg_commit_canvas", handle, tokens_ptr, n, byref(kv), stream)
+
+
+def dg_pack_experts(src_ptr, dst_ptr, n_mats, rows, cols, dtype, stream):
+    _call("dg_pack_experts", src_ptr, dst_ptr, n_mats, rows, cols, dtype, stream)
 
 
 DG_PROF = {"none": 0, "attn": 1, "moe_gateup": 2, "moe_down": 3, "lm_head": 4, "qkv": 5,

@@ -552,6 +552,21 @@ int dg_profile_read(dg_model* m, double* total_ms, int64_t* launches) {
   return DG_OK;
 }
 
+int dg_pack_experts(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols, int32_t dtype,
+                    void* stream) {
+  if (!src || !dst) return fail(DG_ERR_INVALID_ARG, "null pointer");
+  if (dtype != DG_DTYPE_BF16 && dtype != DG_DTYPE_FP8_E4M3)
+    return fail(DG_ERR_INVALID_ARG, "dtype must be BF16 or FP8_E4M3");
+  if (n_mats <= 0 || rows <= 0 || cols <= 0 || rows % 16 || cols % 32)
+    return fail(DG_ERR_SHAPE, "need n_mats, rows, cols > 0, rows %% 16 == 0 and cols %% 32 == 0");
+  const unsigned long long bytes =
+      (unsigned long long)n_mats * rows * cols * (dtype == DG_DTYPE_BF16 ? 2u : 1u);
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(DG_ERR_INVALID_ARG, "src and dst overlap");
+  HIP_OK(moe_pack(dtype == DG_DTYPE_BF16 ? W_BF16 : W_FP8, src, dst, n_mats, rows, cols, (hipStream_t)stream));
+  return DG_OK;
+}
+
 int dg_test_philox(uint64_t seed, uint32_t pos0, uint32_t step_tag, uint32_t canvas, uint32_t block,
                    uint32_t modulus, int32_t n, uint32_t* out, void* stream) {
   if (!out || n < 0 || n > (1 << 24)) return fail(DG_ERR_INVALID_ARG, "bad philox arguments");

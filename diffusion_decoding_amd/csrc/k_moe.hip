@@ -28,6 +28,17 @@
 // down:    y[p][n] = h_p . W_down[n]  (fp32; combined per token later)
 // fp8 weights (E4M3FN codes) are widened exactly to bf16 in registers and the
 // per-row scale is applied to the fp32 accumulator.
+//
+// Expert weights are read in a tiled layout made once at load time by
+// moe_pack (below): each 16-row x SKE-column block of a matrix is one
+// contiguous tile (1 KB for bf16 and for fp8 with 64-column tiles) holding
+// exactly one wave's MFMA operand fragment, lane l's bytes at offset
+// l * (tile bytes / 64), and the tiles of a 16-row block follow each other
+// along k.  A wave's weight load is then one contiguous 1 KB read instead of
+// 16 row pieces 4 KB apart, and a wave's stream walks forward through
+// memory: pure streaming of the gate/up weights measured 6.1 TB/s this way
+// against 5.0 TB/s from the row-major matrices.
+#include <cstdint>
 #include <type_traits>
 
 #include "dg_common.h"
@@ -42,15 +53,15 @@ struct f8 {
   uint8_t v;
 };
 
-// Weight formats.  A lane loads its slice of a weight row through a buffer
+// Weight formats.  A lane loads its slice of a weight tile through a buffer
 // resource over one expert's weights: lane offsets are 32-bit, fragment
-// offsets are uniform (scalar), stage offsets are immediates, and rows past
-// the expert's end read as zero -- a handful of registers however many
-// fragments and stages are in flight.  A stage is SPS 32-k MFMA steps; lane
-// (c16, g4) holds KL consecutive k of its row at k offset lane_k(g4) in the
-// stage, and x_k(g4, t) gives the k offset, in the stage, of the 8 k-slots
-// it feeds into step t -- the token operand is read at the same offsets, so
-// any order of k within a stage is a valid split of the dot product.
+// offsets are uniform (scalar), and tiles past the expert's end read as
+// zero -- a handful of registers however many fragments and stages are in
+// flight.  A stage (one tile) is SPS 32-k MFMA steps; lane (c16, g4) holds
+// row c16 of the tile and the k range starting at lane_k(g4), and x_k(g4, t)
+// gives the k offset, in the stage, of the 8 k-slots it feeds into step t --
+// the token operand is read at the same offsets, so any order of k within a
+// stage is a valid split of the dot product.
 template <typename TW, int SPS_> struct WFmt;
 template <> struct WFmt<bf16, 1> {  // 8 bf16 per lane per step
   using raw = u32x4;
@@ -89,7 +100,7 @@ struct MoeArgs {
   const bf16* X;        // token activations: gate/up [T][K] (rows gathered), down [pairs][K]
   const int* pair_row;  // gate/up: token of each pair slot; down: unused (row = pair)
   const int* off;       // [E+1] pair ranges per expert
-  const void* W;        // gate/up [E][2*Nout][K]; down [E][Nout][K]
+  const void* W;        // tiled: gate/up [E][2*Nout][K]; down [E][Nout][K]
   const float* scale;   // fp8: [E][rows of W per expert]
   int K;                // reduction length (multiple of 32)
   int Nout;             // outputs per token: d_expert (gate/up) or d_model (down)
@@ -143,11 +154,14 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
       __builtin_amdgcn_make_buffer_rsrc((void*)We, (short)0, int(wrows * K * WB), 0x00020000);
   // lane: row n0 + c16 of each fragment; fragment f adds a uniform row offset
   // (block f % NB; up rows for f >= NB)
-  const int voff0 = ((n0 + c16) * K + WL::lane_k(g4)) * WB;
-  int soff[NW];
+  const int KS = K / SKE;                 // stages (tiles along k)
+  constexpr int TILE = 16 * SKE * WB;     // bytes of one 16-row tile
+  const int voff0 = lane * (TILE / 64);
+  int soff[NW];  // first tile of each fragment's 16-row block (n0 and Nout are multiples of 16)
 #pragma unroll
-  for (int f = 0; f < NW; ++f) soff[f] = (16 * (f % NB) + (f < NB ? 0 : a.Nout)) * K * WB;
+  for (int f = 0; f < NW; ++f) soff[f] = ((n0 + 16 * (f % NB) + (f < NB ? 0 : a.Nout)) / 16) * KS * TILE;
   const bf16* xr = xs + c16 * pitch;
+  (void)g4;
 
   f32x4 acc[NW][MT];
 #pragma unroll
@@ -155,11 +169,10 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KS = K / SKE;  // stages
   wraw rw[MD][NW];
   auto ld = [&](int ks, wraw* rw_) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) rw_[w] = WL::load(rsrc, voff0 + ks * SKE * WB, soff[w]);
+    for (int w = 0; w < NW; ++w) rw_[w] = WL::load(rsrc, voff0 + ks * TILE, soff[w]);
   };
   // Slot u of the register ring holds weight stage k with k % MD == u.  The
   // main loop has no conditions and the MFMAs read a slot before its refill
@@ -298,7 +311,55 @@ int launch(bool gu, const MoeArgs& a, int E, hipStream_t st) {
   return launch_k<WL, false, 2, 8, 256>(a, E, (blocks + 3) / 4, st);
 }
 
+// Row-major [n][rows][cols] -> tiled layout (see the top of this file): one
+// thread per lane slice of a tile.  Tile k width SKE: 32 for bf16, for fp8 64
+// when cols % 64 == 0 (16 codes per lane, two MFMA steps) and else 32.
+template <int CH>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                   long long slices, int rows, int cols, int wb, int ske) {
+  const long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= slices) return;
+  const int lane = int(c & 63);
+  const long long tile = c >> 6;
+  const int ks_n = cols / ske;
+  const int kt = int(tile % ks_n);
+  const long long rb_all = tile / ks_n;  // 16-row block over all matrices
+  const long long row = rb_all * 16 + (lane & 15);
+  const int col = kt * ske + (lane >> 4) * (ske / 4);
+  const uint8_t* s = src + (row * cols + col) * wb;
+  if constexpr (CH == 16) {
+    *(u32x4*)(dst + c * 16) = *(const u32x4*)s;
+  } else {
+    *(u32x2*)(dst + c * 8) = *(const u32x2*)s;
+  }
+}
+
 }  // namespace
+
+int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t st) {
+  if (n_mats <= 0 || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return int(hipErrorInvalidValue);
+  int wb, ske;
+  if (wt == W_BF16) {
+    wb = 2;
+    ske = 32;
+  } else if (wt == W_FP8) {
+    wb = 1;
+    ske = cols % 64 == 0 ? 64 : 32;
+  } else {
+    return int(hipErrorInvalidValue);
+  }
+  const int ch = ske / 4 * wb;  // bytes per lane slice
+  const long long slices = n_mats * rows * (long long)cols * wb / ch;
+  const long long blocks = (slices + 255) / 256;
+  if (blocks > INT32_MAX) return int(hipErrorInvalidValue);
+  if (ch == 16)
+    hipLaunchKernelGGL(pack_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)src,
+                       (uint8_t*)dst, slices, rows, cols, wb, ske);
+  else
+    hipLaunchKernelGGL(pack_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)src,
+                       (uint8_t*)dst, slices, rows, cols, wb, ske);
+  return int(hipGetLastError());
+}
 
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st) {

@@ -38,6 +38,17 @@ def make_config(cfg) -> dg_config:
                      _DT[cfg.act_dtype], _DT[cfg.expert_dtype])
 
 
+def pack_experts(w: torch.Tensor, dtype: str, stream=None) -> torch.Tensor:
+    """Tiled copy (dg_pack_experts) of row-major expert matrices w[n][rows][cols]
+    (bf16, or fp8 codes as uint8)."""
+    if w.dim() != 3:
+        raise ValueError("expert weights must be [n][rows][cols]")
+    out = torch.empty_like(w)
+    _lib.dg_pack_experts(_ptr(w), _ptr(out), w.shape[0], w.shape[1], w.shape[2], _DT[dtype],
+                         _stream(stream))
+    return out
+
+
 class Model:
     """A libdg model over the weights of an ``Inputs`` set (tensors stay referenced)."""
 
@@ -48,9 +59,16 @@ class Model:
         self.inputs = inputs
         L = cfg.n_layers
         self._layers = (dg_layer_weights * L)()
+        # bf16/fp8 routed experts go to the library in its tiled layout: one
+        # packed copy per matrix, made here once and kept alive with the model
+        self._packed = []
         for l, lw in enumerate(inputs.layers):
+            w_gu, w_d = lw["w_gu"], lw["w_d"]
+            if cfg.expert_dtype != "fp32":
+                w_gu, w_d = pack_experts(w_gu, cfg.expert_dtype), pack_experts(w_d, cfg.expert_dtype)
+                self._packed += [w_gu, w_d]
             self._layers[l] = dg_layer_weights(
-                _ptr(lw["wqkv"]), _ptr(lw["wo"]), _ptr(lw["wr"]), _ptr(lw["w_gu"]), _ptr(lw["w_d"]),
+                _ptr(lw["wqkv"]), _ptr(lw["wo"]), _ptr(lw["wr"]), _ptr(w_gu), _ptr(w_d),
                 _ptr(lw.get("s_gu")), _ptr(lw.get("s_d")), _ptr(lw["ws_gu"]), _ptr(lw["ws_d"]),
                 _ptr(lw.get("ss_gu")), _ptr(lw.get("ss_d")))
         self._weights = dg_weights(_ptr(inputs.embed), _ptr(inputs.lm_head), self._layers)

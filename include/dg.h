@@ -86,13 +86,24 @@ typedef struct dg_config {
   int32_t expert_dtype;    /* FP32 (with act FP32), BF16 or FP8_E4M3 (with act BF16) */
 } dg_config;
 
-/* One layer's weights (device pointers, borrowed for the model's lifetime). */
+/* One layer's weights (device pointers, borrowed for the model's lifetime).
+ *
+ * Routed-expert matrices w_gu and w_d in BF16 or FP8_E4M3 are passed in the
+ * tiled layout that dg_pack_experts writes from the row-major matrices above
+ * (FP32 experts stay row-major): every 16-row by TK-column block of a matrix
+ * [rows][cols] is one contiguous tile, tiles ordered by 16-row block, then by
+ * column block.  TK is 32 for BF16 and, for FP8, 64 when cols % 64 == 0, else
+ * 32.  Inside a tile, slice l = 0..63 (TK/4 elements, 16 or 8 bytes) holds
+ * row l % 16 of the block, columns (l / 16) * TK/4 .. +TK/4-1 of the tile.
+ * This is the operand layout of the 16x16x32 matrix-core instruction, so a
+ * wavefront fetches one weight fragment as a single contiguous 1 KB read.
+ * The FP8 scales s_gu/s_d stay per row in row order. */
 typedef struct dg_layer_weights {
   const void* wqkv;    /* [3*n_heads*head_dim][d_model]: q rows, k rows, v rows */
   const void* wo;      /* [d_model][n_heads*head_dim] */
   const void* wr;      /* router [n_experts][d_model] (act_dtype) */
-  const void* w_gu;    /* [n_experts][2*d_expert][d_model]: gate rows then up rows */
-  const void* w_d;     /* [n_experts][d_model][d_expert] */
+  const void* w_gu;    /* [n_experts][2*d_expert][d_model]: gate rows then up rows (tiled, below) */
+  const void* w_d;     /* [n_experts][d_model][d_expert] (tiled, below) */
   const float* s_gu;   /* FP8 only: [n_experts][2*d_expert] row scales, else NULL */
   const float* s_d;    /* FP8 only: [n_experts][d_model] */
   const void* ws_gu;   /* shared expert [2*d_shared][d_model] */
@@ -175,6 +186,13 @@ int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* step
  * attends to all cached rows and to new tokens j <= i.  Requires
  * length + n <= capacity and n <= max_tokens. */
 int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, void* stream);
+
+/* Rewrite n_mats row-major expert matrices src[n_mats][rows][cols] (BF16, or
+ * FP8_E4M3 codes) into the tiled layout dg_layer_weights describes, at dst
+ * (same byte size, must not overlap src).  rows % 16 == 0, cols % 32 == 0.
+ * Stream-ordered; done once when weights are loaded. */
+int dg_pack_experts(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
+                    int32_t dtype, void* stream);
 
 /* ---- kernel timing ---------------------------------------------------------
  * Measures one kernel class with HIP events recorded on the stream each of its
