@@ -27,18 +27,21 @@ H_TOL = 1e-3
 # activation whose exact value lies within the fp32-accumulation error
 # (~1e-7 relative) of a bf16 rounding midpoint rounds the other way on the GPU
 # than in the float64 oracle, moving that element by one bf16 ulp (2^-8
-# relative).  Measured per step: at full width (d_model 2048, 262144 ids)
-# logits rel-L2 1.1e-3 to 2.0e-3 at logit std ~1, i.e. ~1.1-1.4e-3 per logit,
-# and |dH| up to 8.4e-4 nats; on the narrow test shapes (d_model 64 and 256,
-# 512 and 4096 ids) rel-L2 2e-3 to 3.5e-3 and |dH| up to 1.9e-3 (steps with no
-# flip reach 4e-8).  A top-2 gap of 1e-3 or an entropy 1e-4 nats from the
-# cutoff is then inside the noise, so for these workloads the decision
-# windows are set at about 3-4x the measured floor (flags are still decided on
-# the oracle's values), and the entropy tolerance stays at the stated 1e-3
-# nats at full width and 5e-3 on the narrow shapes.  fp32 workloads carry no
-# rounding points and keep the stated windows.
-BF16_WIDE = dict(argmax=4e-3, cutoff=1e-3, h=1e-3)
-BF16_NARROW = dict(argmax=1e-2, cutoff=2e-3, h=5e-3)
+# relative); which elements flip depends on the summation order of every
+# GEMM, so the floor is a property of the precision, not of one kernel.
+# Measured per step: at full width (d_model 2048, 262144 ids) logits rel-L2
+# 1.1e-3 to 5.7e-3 at logit std ~1 (per-logit noise sigma up to ~6e-3) and
+# |dH| up to 8.4e-4 nats; on the narrow test shapes (d_model 64 and 256, 512
+# and 4096 ids) rel-L2 2e-3 to 3.5e-3 and |dH| up to 1.9e-3 (steps with no
+# flip reach 4e-8).  The top-2 gap is a difference of two noisy logits
+# (sigma * sqrt(2) up to ~8e-3), so an argmax is ambiguous below about 2.5-3.5
+# of those: 2e-2.  An entropy 1e-4 nats from the cutoff is likewise inside the
+# |dH| floor, so the commit window is about 1.2-1.5x the largest |dH| seen.
+# Flags are still decided on the oracle's values; the entropy tolerance stays
+# at the stated 1e-3 nats at full width and 5e-3 on the narrow shapes.  fp32
+# workloads carry no rounding points and keep the stated windows.
+BF16_WIDE = dict(argmax=2e-2, cutoff=1e-3, h=1e-3)
+BF16_NARROW = dict(argmax=2e-2, cutoff=2e-3, h=5e-3)
 
 
 def windows(cfg) -> dict:
