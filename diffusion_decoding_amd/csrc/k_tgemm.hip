@@ -158,34 +158,42 @@ __global__ __launch_bounds__(TNT * KG) void tgemm_kernel(GemmArgs g, int tiles_m
   lstore(0, ra[0], rb[0]);
   __syncthreads();
 
-  for (int kt0 = 0; kt0 < KT; kt0 += D) {
+  // One stage: ring slot u held stage kt (already in LDS) and is refilled
+  // with stage kt + D (past the end: the last stage again, an L2 hit); the
+  // MFMAs read LDS buffer kt & 1 while slot u + 1 (stage kt + 1) goes to the
+  // other buffer.
+  auto stage = [&](int kt, int u, bool store_next) {
+    gload(min(kt + D, KT - 1), ra[u], rb[u]);
+    const int buf = kt & 1;
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int kt = kt0 + u;
-      if (kt < KT) {
-        // ring slot u held stage kt (already in LDS): refill it with stage
-        // kt + D (past the end: the last stage again, an L2 hit)
-        gload(min(kt + D, KT - 1), ra[u], rb[u]);
-        const int buf = kt & 1;
+    for (int s = 0; s < SK / 32; ++s) {
+      u32x4 af[FM], bfr[FN];
 #pragma unroll
-        for (int s = 0; s < SK / 32; ++s) {
-          u32x4 af[FM], bfr[FN];
+      for (int i = 0; i < FM; ++i)
+        af[i] = *(const u32x4*)&As[buf][(wr + 16 * i + c16) * LDK + 32 * s + 8 * g4];
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            af[i] = *(const u32x4*)&As[buf][(wr + 16 * i + c16) * LDK + 32 * s + 8 * g4];
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *(const u32x4*)&As[buf][boff + (wc + 16 * j + c16) * LDK + 32 * s + 8 * g4];
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bfr[j] = *(const u32x4*)&As[buf][boff + (wc + 16 * j + c16) * LDK + 32 * s + 8 * g4];
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
-        }
-        if (kt + 1 < KT) lstore(buf ^ 1, ra[(u + 1) % D], rb[(u + 1) % D]);
-        __syncthreads();
-      }
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
     }
+    if (store_next) lstore(buf ^ 1, ra[(u + 1) % D], rb[(u + 1) % D]);
+    __syncthreads();
+  };
+  // The main loop body has no branches, so the compiler's wait before each
+  // LDS store is for exactly the oldest ring slot (a branch inside the loop
+  // makes it drain every load in flight at the loop head); the last 1..D
+  // stages run after it.
+  int kt0 = 0;
+  for (; kt0 + D < KT; kt0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) stage(kt0 + u, u, true);
   }
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (kt0 + u < KT) stage(kt0 + u, u, kt0 + u + 1 < KT);
 
   if constexpr (KG > 1) {
     // groups 1.. hand their accumulators to group 0, which adds them in group order
@@ -319,26 +327,36 @@ int launch_t(const GemmArgs& g, hipStream_t st) {
   return int(hipGetLastError());
 }
 
-// Tile shape per epilogue and size: enough workgroups to cover 256 CUs at
-// M = 256 while keeping weight tiles shared through L2.
+// Tile shape per epilogue and size (measured at M = 256, K = 2048): the
+// dense projections run on 64x64 or 64x32 tiles with two k-groups of 4 waves
+// (enough workgroups to cover 256 CUs while weight tiles are shared through
+// L2); the LM head on 128x128 tiles with each wave owning whole tile rows,
+// which keeps a wave at two per SIMD.  k-groups need K % (64 KG) == 0.
+template <typename TB, int BM, int BN, int WM, int D, int EPI>
+int launch_kg(const GemmArgs& g, hipStream_t st, int kg_max) {
+  if (kg_max >= 4 && g.K % 256 == 0) return launch_t<TB, BM, BN, WM, D, EPI, 64, 4>(g, st);
+  if (kg_max >= 2 && g.K % 128 == 0) return launch_t<TB, BM, BN, WM, D, EPI, 64, 2>(g, st);
+  return launch_t<TB, BM, BN, WM, D, EPI, 64, 1>(g, st);
+}
+
 template <typename TB>
 int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   const long long tiles64 = (long long)((g.M + 63) / 64) * ((g.N + 63) / 64);
   switch (epi) {
     case EPI_LM:
-      return launch_t<TB, 256, 128, 4, 2, EPI_LM>(g, st);
+      return launch_t<TB, 128, 128, 4, 2, EPI_LM>(g, st);
     case EPI_SWIGLU:
-      return launch_t<TB, 64, 64, 2, 4, EPI_SWIGLU>(g, st);
+      return launch_kg<TB, 64, 64, 2, 2, EPI_SWIGLU>(g, st, 2);
     case EPI_ACT:
-      if (tiles64 >= 256) return launch_t<TB, 64, 64, 2, 4, EPI_ACT>(g, st);
-      return launch_t<TB, 64, 32, 2, 4, EPI_ACT>(g, st);
+      if (tiles64 >= 256) return launch_kg<TB, 64, 64, 2, 2, EPI_ACT>(g, st, 2);
+      return launch_kg<TB, 64, 32, 2, 2, EPI_ACT>(g, st, 2);
     case EPI_RESID:
-      if (tiles64 >= 256) return launch_t<TB, 64, 64, 2, 4, EPI_RESID>(g, st);
-      return launch_t<TB, 64, 32, 2, 4, EPI_RESID>(g, st);
+      if (tiles64 >= 256) return launch_kg<TB, 64, 64, 2, 2, EPI_RESID>(g, st, 2);
+      return launch_kg<TB, 64, 32, 2, 2, EPI_RESID>(g, st, 2);
     case EPI_F32:
-      if (tiles64 >= 256) return launch_t<TB, 64, 64, 2, 4, EPI_F32>(g, st);
-      if (tiles64 >= 64) return launch_t<TB, 64, 32, 2, 4, EPI_F32>(g, st);
-      return launch_t<TB, 32, 32, 2, 4, EPI_F32>(g, st);
+      if (tiles64 >= 256) return launch_kg<TB, 64, 64, 2, 2, EPI_F32>(g, st, 2);
+      if (tiles64 >= 64) return launch_kg<TB, 64, 32, 2, 2, EPI_F32>(g, st, 2);
+      return launch_kg<TB, 32, 32, 2, 2, EPI_F32>(g, st, 4);
   }
   return int(hipErrorInvalidValue);
 }
