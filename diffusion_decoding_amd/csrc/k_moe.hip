@@ -136,32 +136,55 @@ __device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pit
   }
 }
 
+// Weight stream of one wave: a buffer resource over expert e's tiles, the
+// lane's offsets and a register ring of MD stages.  Slot u of the ring holds
+// weight stage k with k % MD == u.  The ring is filled before the workgroup
+// stages its tokens, so the first weight tiles are in flight during the
+// staging.
+template <typename WL, bool GU, int NB, int MD>
+struct WStream {
+  using wraw = typename WL::raw;
+  static constexpr int SKE = 32 * WL::SPS;            // k per stage
+  static constexpr int TILE = 16 * SKE * WL::BYTES;   // bytes of one 16-row tile
+  static constexpr int NW = GU ? 2 * NB : NB;         // fragments per stage: gate blocks, then up blocks
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff0, KS;
+  int soff[NW];
+  wraw rw[MD][NW];
+
+  __device__ __forceinline__ void init(const MoeArgs& a, int e, int n0) {
+    const long long wrows = GU ? 2LL * a.Nout : a.Nout;
+    const char* We = (const char*)a.W + (long long)e * wrows * a.K * WL::BYTES;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)We, (short)0, int(wrows * a.K * WL::BYTES), 0x00020000);
+    KS = a.K / SKE;
+    voff0 = (threadIdx.x & 63) * (TILE / 64);
+    // first tile of each fragment's 16-row block (n0 and Nout are multiples of 16)
+#pragma unroll
+    for (int f = 0; f < NW; ++f) soff[f] = ((n0 + 16 * (f % NB) + (f < NB ? 0 : a.Nout)) / 16) * KS * TILE;
+  }
+  __device__ __forceinline__ void ld(int ks, int u) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) rw[u][w] = WL::load(rsrc, voff0 + ks * TILE, soff[w]);
+  }
+  __device__ __forceinline__ void fill() {
+#pragma unroll
+    for (int s = 0; s < MD; ++s) ld(min(s, KS - 1), s);
+  }
+};
+
 // One wave: output rows n0 .. n0 + 16 NB - 1 (for gate/up: those gate rows
 // and the matching up rows) of expert e against the MT 16-token tiles staged
-// in xs (pass rows pbeg .. pbeg + rows - 1 of the expert's pairs).
+// in xs (pass rows pbeg .. pbeg + rows - 1 of the expert's pairs); the weight
+// ring of ws has been filled.
 template <typename WL, bool GU, int NB, int MD, int MT>
-__device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int pitch, int e, int n0,
-                                         int pbeg, int rows) {
-  using wraw = typename WL::raw;
-  constexpr int SPS = WL::SPS, SKE = 32 * SPS;  // steps and k per stage
-  constexpr int NW = GU ? 2 * NB : NB;    // weight fragments per k-step: gate blocks, then up blocks
+__device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int pitch,
+                                         WStream<WL, GU, NB, MD>& ws, int e, int n0, int pbeg, int rows) {
+  using WS = WStream<WL, GU, NB, MD>;
+  constexpr int SPS = WL::SPS, SKE = WS::SKE, NW = WS::NW;
   const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
-  const int K = a.K;
   const long long wrows = GU ? 2LL * a.Nout : a.Nout;
-  constexpr int WB = WL::BYTES;
-  const char* We = (const char*)a.W + (long long)e * wrows * K * WB;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)We, (short)0, int(wrows * K * WB), 0x00020000);
-  // lane: row n0 + c16 of each fragment; fragment f adds a uniform row offset
-  // (block f % NB; up rows for f >= NB)
-  const int KS = K / SKE;                 // stages (tiles along k)
-  constexpr int TILE = 16 * SKE * WB;     // bytes of one 16-row tile
-  const int voff0 = lane * (TILE / 64);
-  int soff[NW];  // first tile of each fragment's 16-row block (n0 and Nout are multiples of 16)
-#pragma unroll
-  for (int f = 0; f < NW; ++f) soff[f] = ((n0 + 16 * (f % NB) + (f < NB ? 0 : a.Nout)) / 16) * KS * TILE;
+  const int KS = ws.KS;
   const bf16* xr = xs + c16 * pitch;
-  (void)g4;
 
   f32x4 acc[NW][MT];
 #pragma unroll
@@ -169,18 +192,12 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  wraw rw[MD][NW];
-  auto ld = [&](int ks, wraw* rw_) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) rw_[w] = WL::load(rsrc, voff0 + ks * TILE, soff[w]);
-  };
-  // Slot u of the register ring holds weight stage k with k % MD == u.  The
-  // main loop has no conditions and the MFMAs read a slot before its refill
-  // is issued into the same registers, so the ring needs no copies and the
-  // compiler's wait before a slot is for exactly that slot's loads (the
-  // MD - 1 later stages stay in flight); the scheduling barriers keep the
-  // loads in stage order.
-  auto step = [&](int ks, wraw* rw_, bool refill, int next) {
+  // The main loop has no conditions and the MFMAs read a slot before its
+  // refill is issued into the same registers, so the ring needs no copies
+  // and the compiler's wait before a slot is for exactly that slot's loads
+  // (the MD - 1 later stages stay in flight); the scheduling barriers keep
+  // the loads in stage order.
+  auto step = [&](int ks, int u, bool refill, int next) {
 #pragma unroll
     for (int t2 = 0; t2 < SPS; ++t2) {
       u32x4 xv[MT];
@@ -188,29 +205,27 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
       for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * SKE + WL::x_k(g4, t2));
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const u32x4 wv = WL::get(rw_[w], t2);
+        const u32x4 wv = WL::get(ws.rw[u][w], t2);
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (refill) ld(next, rw_);
+    if (refill) ws.ld(next, u);
     __builtin_amdgcn_sched_barrier(0);
   };
-#pragma unroll
-  for (int s = 0; s < MD; ++s) ld(min(s, KS - 1), rw[s]);
   int k0 = 0;
   for (; k0 + 2 * MD <= KS; k0 += MD) {
 #pragma unroll
-    for (int u = 0; u < MD; ++u) step(k0 + u, rw[u], true, k0 + u + MD);
+    for (int u = 0; u < MD; ++u) step(k0 + u, u, true, k0 + u + MD);
   }
   // the last 1 .. 2*MD - 1 stages
 #pragma unroll
   for (int u = 0; u < MD; ++u)
-    if (k0 + u < KS) step(k0 + u, rw[u], k0 + u + MD < KS, k0 + u + MD);
+    if (k0 + u < KS) step(k0 + u, u, k0 + u + MD < KS, k0 + u + MD);
 #pragma unroll
   for (int u = 0; u < MD; ++u)
-    if (k0 + MD + u < KS) step(k0 + MD + u, rw[u], false, 0);
+    if (k0 + MD + u < KS) step(k0 + MD + u, u, false, 0);
 
   // lane: token 16 t + c16 of the pass; outputs nb + 0..3 of block b
 #pragma unroll
@@ -271,15 +286,18 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   if (pcnt <= 0) return;  // uniform over the workgroup
   const int n0 = blockIdx.x * rows_per_wg + (threadIdx.x >> 6) * 16 * NB;
   const bool active = n0 < min(a.Nout, (blockIdx.x + 1) * rows_per_wg);
+  WStream<WL, GU, NB, MD> ws;
+  ws.init(a, e, n0);
   for (int p0 = 0; p0 < pcnt; p0 += 16 * MTMAX) {
     const int rows = min(16 * MTMAX, pcnt - p0);
+    if (active) ws.fill();    // weights in flight while the tokens are staged
     if (p0) __syncthreads();  // the previous pass is done with xs
     if (rows <= 16) stage_tokens<1>(a, xs, pitch, pbeg + p0, rows, GU);
     else stage_tokens<MTMAX>(a, xs, pitch, pbeg + p0, rows, GU);
     __syncthreads();
     if (active) {
-      if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, e, n0, pbeg + p0, rows);
-      else moe_wave<WL, GU, NB, MD, MTMAX>(a, xs, pitch, e, n0, pbeg + p0, rows);
+      if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+      else moe_wave<WL, GU, NB, MD, MTMAX>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
     }
   }
 }
@@ -301,14 +319,18 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
 
 // gate/up: 32 outputs (64 weight rows) per wave, 2 workgroups of up to 12
 // waves per expert (704 threads at d_expert 704: the token stage of all K
-// takes most of the LDS, so one workgroup per CU); down: 32 outputs per
-// wave, 4 waves per workgroup (K = d_expert is short: three workgroups share
-// a CU).  The thread bound sets the register budget.
+// takes most of the LDS, so one workgroup per CU), one stage in flight per
+// wave; down: 16 outputs per wave, 8 waves per workgroup (K = d_expert is
+// short: several workgroups share a CU), 8 stages in flight.  Measured at 128
+// experts x 16 tokens: the gate/up stream is fastest with the fewest loads in
+// flight (about 11 MB over the chip; 4 stages per wave ran 10% slower), the
+// short down streams want a deep ring.  The thread bound sets the register
+// budget.
 template <typename WL>
 int launch(bool gu, const MoeArgs& a, int E, hipStream_t st) {
-  if (gu) return launch_k<WL, true, 2, 4, 768>(a, E, 2, st);
-  const int blocks = (a.Nout + 31) / 32;
-  return launch_k<WL, false, 2, 8, 256>(a, E, (blocks + 3) / 4, st);
+  if (gu) return launch_k<WL, true, 2, 1, 768>(a, E, 2, st);
+  const int blocks = (a.Nout + 15) / 16;
+  return launch_k<WL, false, 1, 8, 512>(a, E, (blocks + 7) / 8, st);
 }
 
 // Row-major [n][rows][cols] -> tiled layout (see the top of this file): one
