@@ -8,8 +8,9 @@ taken in.  Ambiguous ("flagged") positions, all decided on the oracle's values:
   * entropy within 1e-4 of the commit cutoff (the m-th smallest uncommitted
     entropy) or of the threshold (commit) -- wider for bf16/fp8;
   * router near-ties: in any layer, the gap between the k-th and (k+1)-th
-    router logit of the token below ROUTE_EPS -- a different expert pick moves
-    the whole row, so such rows are excluded from every per-row comparison.
+    router logit of the token below route_eps() -- a different expert pick
+    moves the whole row, so such rows are excluded from every per-row
+    comparison.
 After each step the GPU canvas is resynchronised to the oracle's state.
 """
 from __future__ import annotations
@@ -58,13 +59,18 @@ def logits_tol(cfg) -> float:
     return 1e-4 if cfg.act_dtype == "fp32" else 2e-2
 
 
+# A router logit is an fp32 dot product over bf16 activations that carry the
+# rounding-flip noise above, so on bf16 workloads it moves by up to ~1e-3
+# (a top-k swap was observed at a 1.2e-3 gap between the k-th and (k+1)-th
+# logit); rows with a gap below 5e-3 in any layer are ambiguous.
 def route_eps(cfg) -> float:
-    return 1e-5 if cfg.act_dtype == "fp32" else 1e-3
+    return 1e-5 if cfg.act_dtype == "fp32" else 5e-3
 
 
-def route_flags(trace: dict, k: int, B: int, N: int, eps: float) -> np.ndarray:
-    """[B, N] rows whose router top-k is ambiguous in some layer (oracle values)."""
-    flags = np.zeros(B * N, dtype=bool)
+def route_gaps(trace: dict, k: int, B: int, N: int) -> np.ndarray:
+    """[B, N] smallest gap, over the layers, between a row's k-th and (k+1)-th
+    router logit (oracle values); +inf when there is no (k+1)-th expert."""
+    gaps = np.full(B * N, np.inf)
     rs = trace.get("route_r32", [])
     # trace holds one entry per (canvas, layer) in canvas-major order
     per_canvas = len(rs) // B if B else 0
@@ -74,8 +80,13 @@ def route_flags(trace: dict, k: int, B: int, N: int, eps: float) -> np.ndarray:
             srt = -np.sort(-r, axis=1)
             if srt.shape[1] > k:
                 gap = srt[:, k - 1] - srt[:, k]
-                flags[b * N:(b + 1) * N] |= gap < eps
-    return flags.reshape(B, N)
+                gaps[b * N:(b + 1) * N] = np.minimum(gaps[b * N:(b + 1) * N], gap)
+    return gaps.reshape(B, N)
+
+
+def route_flags(trace: dict, k: int, B: int, N: int, eps: float) -> np.ndarray:
+    """[B, N] rows whose router top-k is ambiguous in some layer (oracle values)."""
+    return route_gaps(trace, k, B, N) < eps
 
 
 @dataclass
@@ -108,6 +119,12 @@ def compare_step(cfg, ores, ostate, gpu: dict, prev_committed: np.ndarray) -> St
     unc_before = ~prev_committed
     rows_h = ok_rows & unc_before
     rep.max_dH = float(dH[rows_h].max()) if rows_h.any() else 0.0
+    if rows_h.any():
+        # where the largest entropy difference sits: its router and top-2 margins
+        w = np.unravel_index(np.argmax(np.where(rows_h, dH, -1.0)), dH.shape)
+        rg = route_gaps(ores.trace, cfg.top_k, B, N)
+        rep.notes.append(f"max dH at row {tuple(int(x) for x in w)}: route gap {rg[w]:.2e}, "
+                         f"top-2 gap {ores.gap[w]:.2e}")
     win = windows(cfg)
     argmax_eps, cutoff_eps = win["argmax"], win["cutoff"]
     # argmax on uncommitted rows (only those feed a decision)
