@@ -215,22 +215,31 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
 // Per key tile (64 keys): K is staged in LDS row-major ([key][dim], the A
 // operand of S^T = K Q^T); V is staged transposed ([dim][key], the A operand
 // of O^T = V^T P^T), each thread moving a 4-key x 8-dim block (four 16-byte
-// loads, eight 8-byte LDS writes).  The next tile's loads are issued before
-// the current tile's MFMAs so their latency hides behind the compute.
+// loads, eight 8-byte LDS writes).  A register ring keeps the loads of the
+// next D key tiles in flight while a tile is computed; all loads are
+// unconditional (rows past the split end are clamped to its last key and
+// masked to -inf) and the main loop has no branches, so the compiler waits
+// for exactly the oldest tile.
 // With several splits, each workgroup writes an unnormalised partial
 // (O, running max, running sum) and a second kernel merges them in split
 // order.
-template <int DH>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
+template <int DH, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
                                                         int per_xcd) {
-  // row pitches: odd multiples of 32 B keep the fragment reads at full LDS rate
+  // K row pitch: an odd multiple of 32 B keeps the 16-row x 64-byte fragment
+  // reads at full LDS rate.  V^T row pitch 72 elements (36 dwords): the
+  // 8-byte fragment reads of 16 rows land on 16 distinct 4-bank groups, and
+  // in the transposing writes the two 16-lane row groups of a half-wave sit
+  // 32 banks apart (8 rows x 36 dwords = 32 mod 64), so neither side
+  // conflicts.
   constexpr int LDKS = DH + 16;  // K row pitch (elements)
-  constexpr int LDV = 64 + 16;   // V^T row pitch
+  constexpr int LDV = 64 + 8;    // V^T row pitch
   constexpr int NDF = DH / 16;
   constexpr int NQ = DH / 32;
   constexpr int KCH = 64 * DH / 8;            // 16-byte K chunks per tile
-  constexpr int KPT = (KCH + 255) / 256;      // per thread
+  constexpr int KPT = KCH / 256;              // per thread
   constexpr int VCH = 16 * (DH / 8);          // 4-key x 8-dim V blocks per tile
+  static_assert(KCH % 256 == 0 && VCH <= 256 && 256 % VCH == 0, "tile split");
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * LDKS];
   __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * LDV];
 
@@ -248,7 +257,6 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per
   const int total = a.len0 + a.len1;
   const int kbeg = z * keys_per_split;
   const int kend = min(total, kbeg + keys_per_split);
-  const float scale = 1.0f / sqrtf(float(DH));
 
   const bf16* K0 = (const bf16*)a.k0 + (long long)bh * a.s0_bh;
   const bf16* V0 = (const bf16*)a.v0 + (long long)bh * a.s0_bh;
@@ -272,94 +280,127 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per
   for (int df = 0; df < NDF; ++df) o[df] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  u32x4 kreg[KPT], vreg[4];
-  auto gload = [&](int kt0) {
+  const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+  // this thread's V block: 4-key block vkb (fastest over the lanes, so 16
+  // lanes write one contiguous 128-byte piece of a V^T row), dims vcol..+7.
+  // Threads past VCH repeat a block: same loads, same values stored to the
+  // same LDS words.
+  const int vb = tid % VCH, vkb = vb % 16, vcol = (vb / 16) * 8;
+  u32x4 kreg[D][KPT], vreg[D][4];
+  auto gload = [&](int t, int u) {
+    const int kt0 = kbeg + 64 * min(t, ntiles - 1);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * 256;
-      if (c < KCH) {
-        const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-        kreg[u] = *(const u32x4*)(krow(kt0 + row, K0, K1) + col);
-      }
+    for (int p = 0; p < KPT; ++p) {
+      const int c = tid + p * 256;
+      const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      kreg[u][p] = *(const u32x4*)(krow(kt0 + row, K0, K1) + col);
     }
-    if (tid < VCH) {
-      const int kb = tid / (DH / 8), col = (tid % (DH / 8)) * 8;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vreg[u] = *(const u32x4*)(krow(kt0 + 4 * kb + u, V0, V1) + col);
-    }
+    for (int p = 0; p < 4; ++p) vreg[u][p] = *(const u32x4*)(krow(kt0 + 4 * vkb + p, V0, V1) + vcol);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int u) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * 256;
-      if (c < KCH) {
-        const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-        *(u32x4*)&Ks[buf][row * LDKS + col] = kreg[u];
-      }
+    for (int p = 0; p < KPT; ++p) {
+      const int c = tid + p * 256;
+      const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      *(u32x4*)&Ks[buf][row * LDKS + col] = kreg[u][p];
     }
-    if (tid < VCH) {
-      const int kb = tid / (DH / 8), col = (tid % (DH / 8)) * 8;
-      // dim col+e: keys 4kb..4kb+3 as one 8-byte word
+    // dim vcol+e: keys 4vkb..4vkb+3 as one 8-byte word
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        const uint32_t k0 = (vreg[0][w] >> sh) & 0xffffu, k1 = (vreg[1][w] >> sh) & 0xffffu;
-        const uint32_t k2 = (vreg[2][w] >> sh) & 0xffffu, k3 = (vreg[3][w] >> sh) & 0xffffu;
-        *(u32x2*)&Vt[buf][(col + e) * LDV + 4 * kb] = u32x2{k0 | (k1 << 16), k2 | (k3 << 16)};
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const uint32_t k0 = (vreg[u][0][w] >> sh) & 0xffffu, k1 = (vreg[u][1][w] >> sh) & 0xffffu;
+      const uint32_t k2 = (vreg[u][2][w] >> sh) & 0xffffu, k3 = (vreg[u][3][w] >> sh) & 0xffffu;
+      *(u32x2*)&Vt[buf][(vcol + e) * LDV + 4 * vkb] = u32x2{k0 | (k1 << 16), k2 | (k3 << 16)};
     }
   };
 
-  const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
-  if (ntiles) {
-    gload(kbeg);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // Softmax in the log2 domain: scores scaled by log2(e)/sqrt(dh), p = 2^(s - m).
+  const float sl = 1.4426950408889634f / sqrtf(float(DH));
+  // key limit of this lane's query: the split end, or the causal bound
+  const int klim = a.causal_base < 0 ? kend : min(kend, a.causal_base + qi + 1);
+
+  // One key tile t from LDS buffer t & 1; ring slot u held tile t and is
+  // refilled with tile t + D; slot u + 1 (tile t + 1) goes to the other buffer.
+  // MASKED: some key of the tile may lie past klim (the split's last tile, or
+  // any tile of a causal pass); then a running max can still be -inf and the
+  // exponent base is taken as 0 so that no -inf - -inf arises.
+  auto tile = [&](int t, int u, bool store_next, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    gload(t + D, u);
     const int kt0 = kbeg + 64 * t, buf = t & 1;
-    if (t + 1 < ntiles) gload(kt0 + 64);
-    // S^T for 64 keys: lane holds keys 16f + 4g4 + r of query qi
+    // S^T for 64 keys: lane holds keys 16f + 4g4 + r of query qi.  Every K
+    // fragment is read before the first MFMA (the scheduling barriers keep
+    // the compiler from interleaving one read and one MFMA at a time, which
+    // exposes the LDS latency per MFMA); the V fragments are read right after
+    // the S MFMAs and arrive while the softmax runs.
+    u32x4 ka[4][NQ];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int ks = 0; ks < NQ; ++ks) ka[f][ks] = *(const u32x4*)&Ks[buf][(16 * f + c16) * LDKS + 32 * ks + 8 * g4];
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 sc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       sc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NQ; ++ks) {
-        const u32x4 ka = *(const u32x4*)&Ks[buf][(16 * f + c16) * LDKS + 32 * ks + 8 * g4];
-        sc[f] = mfma16x16x32(ka, qf[ks], sc[f]);
-      }
+      for (int ks = 0; ks < NQ; ++ks) sc[f] = mfma16x16x32(ka[f][ks], qf[ks], sc[f]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 va[2][NDF];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int df = 0; df < NDF; ++df) {
+        const bf16* vr = &Vt[buf][(16 * df + c16) * LDV + 32 * kb + 4 * g4];
+        const u32x2 lo = *(const u32x2*)vr;
+        const u32x2 hi = *(const u32x2*)(vr + 16);
+        va[kb][df] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    __builtin_amdgcn_sched_barrier(0);
     float tmax = -INFINITY;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = kt0 + 16 * f + 4 * g4 + r;
-        const bool ok = j < kend && (a.causal_base < 0 || j <= a.causal_base + qi);
-        const float v = ok ? sc[f][r] * scale : -INFINITY;
+        float v = sc[f][r] * sl;
+        if constexpr (MASKED) v = (kt0 + 16 * f + 4 * g4 + r < klim) ? v : -INFINITY;
         sc[f][r] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
+    // The exponent base m_run is raised only when some score of the wave
+    // exceeds it by more than 2^8 (or it is still -inf), so O and l are
+    // rescaled rarely; p stays below 2^8 and the result O / l is unchanged.
+    // v_exp_f32 directly: p below 2^-126 flushes to 0, far below what the sum
+    // can resolve.
+    // (A lane whose scores are all masked so far keeps m_run = -inf; its
+    // exponent base is then 0 and every p of it is exp2(-inf) = 0.)
+    const bool raise = tmax > m_run + 8.f;
+    if (__any(raise)) {  // uniform over the wave
+      const float m_new = raise ? tmax : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int df = 0; df < NDF; ++df) o[df] *= alpha;
+      m_run = m_new;
+    }
+    float m_base = m_run;
+    if constexpr (MASKED) m_base = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = (sc[f][r] == -INFINITY) ? 0.f : __expf(sc[f][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(sc[f][r] - m_base);
         sc[f][r] = p;
         psum += p;
       }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int df = 0; df < NDF; ++df) o[df] *= alpha;
+    l_run += psum;
     // 32-key blocks: k-slot t of lane group g4 <-> key 32kb + 4g4 + t (t < 4),
     // 32kb + 16 + 4g4 + t - 4.  P = P_hi + P_lo, both bf16, so P V keeps about
     // 16 significant bits of P (one bf16 P perturbs every output by up to 2^-9).
@@ -369,30 +410,46 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const f32x4& sf = sc[2 * kb + q];
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bf16 hv = f32_to_bf16(sf[r]);
-          hb[r] = hv.v;
-          lb[r] = f32_to_bf16(sf[r] - to_f32(hv)).v;
-        }
-        pb[2 * q] = hb[0] | (hb[1] << 16);
-        pb[2 * q + 1] = hb[2] | (hb[3] << 16);
-        pl[2 * q] = lb[0] | (lb[1] << 16);
-        pl[2 * q + 1] = lb[2] | (lb[3] << 16);
+        const uint32_t h01 = pack_bf16x2(sf[0], sf[1]), h23 = pack_bf16x2(sf[2], sf[3]);
+        pb[2 * q] = h01;
+        pb[2 * q + 1] = h23;
+        pl[2 * q] = pack_bf16x2(sf[0] - __uint_as_float(h01 << 16), sf[1] - __uint_as_float(h01 & 0xffff0000u));
+        pl[2 * q + 1] = pack_bf16x2(sf[2] - __uint_as_float(h23 << 16), sf[3] - __uint_as_float(h23 & 0xffff0000u));
       }
 #pragma unroll
       for (int df = 0; df < NDF; ++df) {
-        const bf16* vr = &Vt[buf][(16 * df + c16) * LDV + 32 * kb + 4 * g4];
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 16);
-        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-        o[df] = mfma16x16x32(va, pb, o[df]);
-        o[df] = mfma16x16x32(va, pl, o[df]);
+        o[df] = mfma16x16x32(va[kb][df], pb, o[df]);
+        o[df] = mfma16x16x32(va[kb][df], pl, o[df]);
       }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    if (store_next) lstore(buf ^ 1, (u + 1) % D);
     __syncthreads();
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+
+  if (ntiles) {  // uniform over the workgroup
+#pragma unroll
+    for (int s = 0; s < D; ++s) gload(s, s);
+    lstore(0, 0);
+    __syncthreads();
+    // every tile but the last lies wholly inside the split; only a causal
+    // pass masks inside the main loop
+    int t0 = 0;
+    if (a.causal_base < 0) {
+      for (; t0 + D < ntiles; t0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) tile(t0 + u, u, true, Full{});
+      }
+    } else {
+      for (; t0 + D < ntiles; t0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) tile(t0 + u, u, true, Masked{});
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+      if (t0 + u < ntiles) tile(t0 + u, u, t0 + u + 1 < ntiles, Masked{});
   }
 
   const bool qvalid = qi < a.n;
@@ -402,10 +459,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per
       bf16* out = (bf16*)a.out + ((long long)(b * a.n + qi) * a.H + h) * DH;
 #pragma unroll
       for (int df = 0; df < NDF; ++df) {
-        u32x2 w;
-        w[0] = uint32_t(f32_to_bf16(o[df][0] * inv).v) | (uint32_t(f32_to_bf16(o[df][1] * inv).v) << 16);
-        w[1] = uint32_t(f32_to_bf16(o[df][2] * inv).v) | (uint32_t(f32_to_bf16(o[df][3] * inv).v) << 16);
-        *(u32x2*)(out + 16 * df + 4 * g4) = w;
+        *(u32x2*)(out + 16 * df + 4 * g4) =
+            u32x2{pack_bf16x2(o[df][0] * inv, o[df][1] * inv), pack_bf16x2(o[df][2] * inv, o[df][3] * inv)};
       }
     }
     return;
@@ -420,7 +475,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int keys_per
   }
 }
 
-// one thread per (b, h, query, 4 dims): combine the split partials in split order
+// one thread per (b, h, query, 4 dims): combine the S split partials in split
+// order.  Partial maxima are in the log2 domain of the bf16 kernel.  S is a
+// compile-time count, so every partial's loads are issued before the first is
+// used.
+template <int S>
 __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int q4 = a.dh / 4;
@@ -429,23 +488,31 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   const int d0 = int(e % q4) * 4;
   const long long row = e / q4;  // (bh, i)
   const int i = int(row % a.n), bh = int(row / a.n);
+  const long long zstride = BH * a.n;  // rows between splits
+  const long long base0 = (long long)bh * a.n + i;
+  u32x2 ml[S];
+  f32x4 po[S];
+#pragma unroll
+  for (int z = 0; z < S; ++z) {
+    const long long base = base0 + z * zstride;
+    ml[z] = *(const u32x2*)(a.part_ml + base * 2);
+    po[z] = *(const f32x4*)(a.part_o + base * a.dh + d0);
+  }
   float M = -INFINITY;
-  for (int z = 0; z < a.splits; ++z) M = fmaxf(M, a.part_ml[((z * BH + bh) * a.n + i) * 2]);
+#pragma unroll
+  for (int z = 0; z < S; ++z) M = fmaxf(M, __uint_as_float(ml[z][0]));
   float L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < a.splits; ++z) {
-    const long long base = (z * BH + bh) * a.n + i;
-    const float mz = a.part_ml[base * 2];
-    if (mz == -INFINITY) continue;
-    const float w = __expf(mz - M);
-    L += a.part_ml[base * 2 + 1] * w;
-    O += *(const f32x4*)(a.part_o + base * a.dh + d0) * w;
+#pragma unroll
+  for (int z = 0; z < S; ++z) {
+    const float w = __builtin_amdgcn_exp2f(__uint_as_float(ml[z][0]) - M);  // an empty split (max -inf) weighs 0
+    L += __uint_as_float(ml[z][1]) * w;
+    O += po[z] * w;
   }
   const float inv = 1.f / L;
   const int b = bh / a.H, h = bh % a.H;
   bf16* out = (bf16*)a.out + ((long long)(b * a.n + i) * a.H + h) * a.dh + d0;
-  *(u32x2*)out = u32x2{uint32_t(f32_to_bf16(O[0] * inv).v) | (uint32_t(f32_to_bf16(O[1] * inv).v) << 16),
-                       uint32_t(f32_to_bf16(O[2] * inv).v) | (uint32_t(f32_to_bf16(O[3] * inv).v) << 16)};
+  *(u32x2*)out = u32x2{pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv)};
 }
 
 // one thread per (b, h, query, d): combine the split partials in split order
@@ -495,11 +562,18 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
   const int n_qt = (a.n + 63) / 64;
   const int items = a.B * a.H * a.splits * n_qt;
   const int per_xcd = (items + 7) / 8;
-  hipLaunchKernelGGL((attn_bf16_kernel<DH>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, 1>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
   int e = int(hipGetLastError());
   if (e || a.splits == 1) return e;
   const long long n4 = (long long)a.B * a.H * a.n * (DH / 4);
-  hipLaunchKernelGGL(attn_merge_bf16, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, st, a);
+  const dim3 g(unsigned((n4 + 255) / 256));
+  switch (a.splits) {
+    case 2: hipLaunchKernelGGL(attn_merge_bf16<2>, g, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(attn_merge_bf16<4>, g, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(attn_merge_bf16<8>, g, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(attn_merge_bf16<16>, g, dim3(256), 0, st, a); break;
+    default: return int(hipErrorInvalidValue);
+  }
   return int(hipGetLastError());
 }
 
@@ -508,7 +582,7 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
 int attn_splits_for(int B, int H, int n, int keys) {
   const int wgs = ((n + 63) / 64) * B * H;
   int s = 1;
-  while (wgs * s < 512 && keys / (s * 2) >= 256) s *= 2;
+  while (s < 16 && wgs * s < 512 && keys / (s * 2) >= 256) s *= 2;
   return s;
 }
 
