@@ -62,6 +62,7 @@ struct dg_model {
   float *attn_po = nullptr, *attn_ml = nullptr;
   int attn_max_splits = 8;
   float *rlog = nullptr, *topk_w = nullptr, *y = nullptr, *ys = nullptr, *lm_part = nullptr;
+  float* rope_tab = nullptr;  // [max_tokens][head_dim / 2] (cos, sin) of the current positions
   int *topk_ids = nullptr, *off = nullptr, *pair_row = nullptr, *pos = nullptr;
   int lm_ntiles = 0;
   float *H = nullptr, *gap = nullptr;
@@ -190,13 +191,12 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   aa.q = m->q; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = m->o;
   aa.part_o = m->attn_po; aa.part_ml = m->attn_ml;
   if (!causal) {
-    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, P, c.rope_theta, m->q, m->kc, m->vc,
-                        (long long)n * dh, 0, st));
+    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, m->kc, m->vc, (long long)n * dh, 0, st));
     aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P;
     aa.k1 = m->kc; aa.v1 = m->vc; aa.s1_bh = (long long)n * dh; aa.len1 = n;
     aa.causal_base = -1;
   } else {
-    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, P, c.rope_theta, m->q, kcache, vcache, cap * dh, P, st));
+    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, kcache, vcache, cap * dh, P, st));
     if (kv_only) return DG_OK;
     aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P + n;
     aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;
@@ -306,6 +306,7 @@ int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* o
   const int B = c->batch, N = cfg.canvas_len, T = B * N, P = kv->length;
   HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, m->x, st));
   HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
+  HIP_OK(rope_table(N, cfg.head_dim, P, cfg.rope_theta, m->rope_tab, st));  // canvas positions P..P+N-1
   for (int l = 0; l < cfg.n_layers; ++l) {
     int s = layer_forward(m, l, B, N, P, kv, false, false, st);
     if (s) return s;
@@ -409,6 +410,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       {(void**)&m->attn_po, (size_t)m->attn_max_splits * T * A * 4},
       {(void**)&m->attn_ml, (size_t)m->attn_max_splits * T * cfg->n_heads * 2 * 4},
       {(void**)&m->rlog, T * E * 4},
+      {(void**)&m->rope_tab, (size_t)m->max_tokens * cfg->head_dim * 4},
       {(void**)&m->topk_ids, T * k * 4},
       {(void**)&m->topk_w, T * k * 4},
       {(void**)&m->off, (E + 1) * 4},
@@ -518,6 +520,7 @@ int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, v
   const int B = kv->batch, T = B * n, P = kv->length;
   HIP_OK(embed_gather(m->at, tokens, T, m->embed, cfg.d_model, m->x, st));
   HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
+  HIP_OK(rope_table(n, cfg.head_dim, P, cfg.rope_theta, m->rope_tab, st));  // positions P..P+n-1
   for (int l = 0; l < cfg.n_layers; ++l) {
     s = layer_forward(m, l, B, n, P, kv, true, l == cfg.n_layers - 1, st);
     if (s) return s;

@@ -48,21 +48,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, int d, float e
   for (int c = threadIdx.x; c < d; c += 256) yr[c] = from_f32<T>(to_f32(xr[c]) * inv);
 }
 
-// one thread per (token, head, pair j < dh/2); cos/sin of pos * theta^(-2j/dh)
-// evaluated in double precision and rounded to binary32.
-template <typename T>
-__global__ void rope_kernel(const T* qkv, int B, int n, int H, int dh, int pos0, float theta,
-                            T* q_out, T* kdst, T* vdst, long long dst_bh, int row0) {
+// cos/sin of (pos0 + i) * theta^(-2j/dh) for i < n, j < dh/2, evaluated in
+// double precision and rounded to binary32 (binary32 angles at positions in
+// the thousands would carry ~1e-3 rad of error); theta == 0 gives the
+// identity rotation.  tab[i][j] = (cos, sin).  The table depends only on the
+// positions, so one step computes it once for all layers.
+__global__ void rope_table_kernel(int n, int dh, int pos0, float theta, float2* tab) {
   const int half = dh / 2;
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)B * n * H * half;
-  if (e >= total) return;
-  const int j = int(e % half);
-  const int h = int((e / half) % H);
-  const int i = int((e / ((long long)half * H)) % n);
-  const int b = int(e / ((long long)half * H * n));
-  const int A = H * dh;
-  const T* row = qkv + (long long)(b * n + i) * 3 * A;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n * half) return;
+  const int j = e % half, i = e / half;
   float c = 1.f, s = 0.f;
   if (theta > 0.f) {
     const double inv = pow((double)theta, -2.0 * j / dh);
@@ -70,23 +65,45 @@ __global__ void rope_kernel(const T* qkv, int B, int n, int H, int dh, int pos0,
     c = (float)cos(ang);
     s = (float)sin(ang);
   }
-  const int bh = b * H + h;
-  // q
-  {
-    float x1 = to_f32(row[h * dh + j]), x2 = to_f32(row[h * dh + j + half]);
-    T* qo = q_out + ((long long)bh * n + i) * dh;
-    qo[j] = from_f32<T>(x1 * c - x2 * s);
-    qo[j + half] = from_f32<T>(x2 * c + x1 * s);
+  tab[e] = float2{c, s};
+}
+
+// Rotate-half RoPE on q and k (pairs j, j + dh/2) and scatter q, k, v to
+// their per-head layouts; one thread per (token, head, 4 consecutive pairs).
+template <typename T>
+__global__ void rope_kernel(const T* qkv, int B, int n, int H, int dh, const float2* tab, T* q_out, T* kdst,
+                            T* vdst, long long dst_bh, int row0) {
+  const int half = dh / 2, g4 = half / 4;
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)B * n * H * g4;
+  if (e >= total) return;
+  const int j = int(e % g4) * 4;
+  const int h = int((e / g4) % H);
+  const int i = int((e / ((long long)g4 * H)) % n);
+  const int b = int(e / ((long long)g4 * H * n));
+  const int A = H * dh;
+  const T* row = qkv + (long long)(b * n + i) * 3 * A;
+  float c[4], s[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float2 cs = tab[i * half + j + u];
+    c[u] = cs.x;
+    s[u] = cs.y;
   }
-  // k, v
-  {
-    float x1 = to_f32(row[A + h * dh + j]), x2 = to_f32(row[A + h * dh + j + half]);
-    T* ko = kdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
-    ko[j] = from_f32<T>(x1 * c - x2 * s);
-    ko[j + half] = from_f32<T>(x2 * c + x1 * s);
-    T* vo = vdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
-    vo[j] = row[2 * A + h * dh + j];
-    vo[j + half] = row[2 * A + h * dh + j + half];
+  const int bh = b * H + h;
+  T* qo = q_out + ((long long)bh * n + i) * dh;
+  T* ko = kdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
+  T* vo = vdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float q1 = to_f32(row[h * dh + j + u]), q2 = to_f32(row[h * dh + j + u + half]);
+    qo[j + u] = from_f32<T>(q1 * c[u] - q2 * s[u]);
+    qo[j + u + half] = from_f32<T>(q2 * c[u] + q1 * s[u]);
+    const float k1 = to_f32(row[A + h * dh + j + u]), k2 = to_f32(row[A + h * dh + j + u + half]);
+    ko[j + u] = from_f32<T>(k1 * c[u] - k2 * s[u]);
+    ko[j + u + half] = from_f32<T>(k2 * c[u] + k1 * s[u]);
+    vo[j + u] = row[2 * A + h * dh + j + u];
+    vo[j + u + half] = row[2 * A + h * dh + j + u + half];
   }
 }
 
@@ -272,17 +289,26 @@ int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStre
   return int(hipGetLastError());
 }
 
-int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, int pos0, float theta,
-                 void* q_out, void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st) {
-  const long long total = (long long)B * n * H * (dh / 2);
+int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st) {
+  const int total = n * (dh / 2);
+  if (total <= 0) return 0;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((total + 255) / 256), dim3(256), 0, st, n, dh, pos0, theta,
+                     (float2*)tab);
+  return int(hipGetLastError());
+}
+
+int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, const float* tab, void* q_out,
+                 void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st) {
+  if (dh % 8) return int(hipErrorInvalidValue);
+  const long long total = (long long)B * n * H * (dh / 8);
   if (total <= 0) return 0;
   dim3 grid(unsigned((total + 255) / 256));
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)qkv, B, n, H, dh, pos0,
-                       theta, (bf16*)q_out, (bf16*)kdst, (bf16*)vdst, dst_bh, row0);
+    hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)qkv, B, n, H, dh,
+                       (const float2*)tab, (bf16*)q_out, (bf16*)kdst, (bf16*)vdst, dst_bh, row0);
   else
-    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, st, (const float*)qkv, B, n, H, dh, pos0,
-                       theta, (float*)q_out, (float*)kdst, (float*)vdst, dst_bh, row0);
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, st, (const float*)qkv, B, n, H, dh,
+                       (const float2*)tab, (float*)q_out, (float*)kdst, (float*)vdst, dst_bh, row0);
   return int(hipGetLastError());
 }
 

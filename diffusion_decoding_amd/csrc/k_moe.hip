@@ -48,6 +48,11 @@ namespace dg {
 namespace {
 
 constexpr int MTMAX = 2;   // 16-token tiles per pass over the weights
+// Weight loads are non-temporal (cache-policy bit nt): every weight byte is
+// read once per step, so keeping it in L2 only evicts the token rows and
+// outputs; measured at 128 experts x 16 tokens the gate/up stream went from
+// 5.9 to 6.6 TB/s and the down stream from 5.2 to 5.5 TB/s.
+constexpr int kWeightAux = 2;
 
 struct f8 {
   uint8_t v;
@@ -67,7 +72,7 @@ template <> struct WFmt<bf16, 1> {  // 8 bf16 per lane per step
   using raw = u32x4;
   static constexpr int BYTES = 1 * 2, SPS = 1;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightAux);
   }
   static __device__ __forceinline__ int lane_k(int g4) { return 8 * g4; }
   static __device__ __forceinline__ int x_k(int g4, int) { return 8 * g4; }
@@ -77,7 +82,7 @@ template <> struct WFmt<f8, 1> {  // 8 E4M3FN codes per lane per step (K % 64 !=
   using raw = u32x2;
   static constexpr int BYTES = 1, SPS = 1;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kWeightAux);
   }
   static __device__ __forceinline__ int lane_k(int g4) { return 8 * g4; }
   static __device__ __forceinline__ int x_k(int g4, int) { return 8 * g4; }
@@ -87,7 +92,7 @@ template <> struct WFmt<f8, 2> {  // 16 E4M3FN codes per lane: two steps per 16-
   using raw = u32x4;
   static constexpr int BYTES = 1, SPS = 2;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightAux);
   }
   static __device__ __forceinline__ int lane_k(int g4) { return 16 * g4; }
   static __device__ __forceinline__ int x_k(int g4, int t) { return 16 * g4 + 8 * t; }
@@ -321,16 +326,16 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
 // waves per expert (704 threads at d_expert 704: the token stage of all K
 // takes most of the LDS, so one workgroup per CU), one stage in flight per
 // wave; down: 16 outputs per wave, 8 waves per workgroup (K = d_expert is
-// short: several workgroups share a CU), 8 stages in flight.  Measured at 128
+// short: several workgroups share a CU), 4 stages in flight.  Measured at 128
 // experts x 16 tokens: the gate/up stream is fastest with the fewest loads in
-// flight (about 11 MB over the chip; 4 stages per wave ran 10% slower), the
-// short down streams want a deep ring.  The thread bound sets the register
+// flight (about 11 MB over the chip; 4 stages per wave ran 10-30% slower),
+// the short down streams want a deeper ring.  The thread bound sets the register
 // budget.
 template <typename WL>
 int launch(bool gu, const MoeArgs& a, int E, hipStream_t st) {
   if (gu) return launch_k<WL, true, 2, 1, 768>(a, E, 2, st);
   const int blocks = (a.Nout + 15) / 16;
-  return launch_k<WL, false, 1, 8, 512>(a, E, (blocks + 7) / 8, st);
+  return launch_k<WL, false, 1, 4, 512>(a, E, (blocks + 7) / 8, st);
 }
 
 // Row-major [n][rows][cols] -> tiled layout (see the top of this file): one

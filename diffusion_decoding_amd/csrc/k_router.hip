@@ -2,8 +2,9 @@
 // experts plus one shared expert, each token routed to its top 8).
 //
 // router_topk: one wave per token picks the k largest router logits (ties to
-// the lower expert id) and weights them by a softmax over the k picks, which
-// equals the full router softmax restricted to the picks and renormalised.
+// the lower expert id) by ranking every logit against all others, and weights
+// them by a softmax over the k picks, which equals the full router softmax
+// restricted to the picks and renormalised.
 // (A NaN logit is not ranked meaningfully; router logits are finite.)
 // router_permute: one workgroup builds the expert histogram, its exclusive
 // scan, and the expert-major, token-ascending permutation of the (token, slot)
@@ -17,9 +18,9 @@
 namespace dg {
 namespace {
 
-// One wave per token.  Each (logit, expert) pair becomes one 64-bit key that
-// orders by logit, then by lower expert id (the low word holds ~id), so every
-// selection round is a single 64-bit max-reduction across the wave.
+// Each (logit, expert) pair becomes one 64-bit key that orders by logit, then
+// by lower expert id (the low word holds ~id): a total order, so the top k
+// are the keys with fewer than k larger keys.
 __device__ __forceinline__ unsigned long long topk_key(float f, int e) {
   uint32_t b = __float_as_uint(f);
   b ^= (b >> 31) ? 0xffffffffu : 0x80000000u;  // order-preserving map to unsigned
@@ -32,40 +33,48 @@ __device__ __forceinline__ float topk_value(unsigned long long key) {
   return __uint_as_float(b);
 }
 
+// One wave per token.  The E keys go to LDS; every lane ranks its own keys by
+// counting the larger ones (the key order is total, so ranks are distinct),
+// reading the keys as wave-wide broadcasts, and the keys ranked below k are
+// written to their slot.  No cross-lane shuffles.
 __global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, int E, int k, int* ids,
                                                   float* w) {
+  __shared__ __attribute__((aligned(16))) unsigned long long ks[256];
+  __shared__ float sel[8];
   const int t = blockIdx.x, lane = threadIdx.x;
   unsigned long long key[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int e = lane + 64 * u;
     key[u] = e < E ? topk_key(logits[(long long)t * E + e], e) : 0ull;
+    ks[e] = key[u];  // past E: key 0, ranked below every real key
   }
-  unsigned long long top[8];
-  for (int j = 0; j < k; ++j) {
-    unsigned long long best = key[0];
+  __syncthreads();
+  const int E2 = (E + 1) & ~1;
+  int rank[4] = {0, 0, 0, 0};
+  for (int e = 0; e < E2; e += 2) {
+    const u32x4 kk = *(const u32x4*)&ks[e];
+    const unsigned long long k0 = ((unsigned long long)kk[1] << 32) | kk[0];
+    const unsigned long long k1 = ((unsigned long long)kk[3] << 32) | kk[2];
 #pragma unroll
-    for (int u = 1; u < 4; ++u) best = key[u] > best ? key[u] : best;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long ob = __shfl_xor(best, o, 64);
-      best = ob > best ? ob : best;
-    }
-    top[j] = best;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (key[u] == best) key[u] = 0ull;
+    for (int u = 0; u < 4; ++u) rank[u] += int(k0 > key[u]) + int(k1 > key[u]);
   }
-  if (lane == 0) {
-    const float m = topk_value(top[0]);
-    float sum = 0.f, ex[8];
-    for (int j = 0; j < k; ++j) {
-      ex[j] = __expf(topk_value(top[j]) - m);
-      sum += ex[j];
-    }
-    for (int j = 0; j < k; ++j) {
-      ids[t * k + j] = int(0xffffffffu - uint32_t(top[j]));
-      w[t * k + j] = ex[j] / sum;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    if (e < E && rank[u] < k) sel[rank[u]] = topk_value(key[u]);
+  }
+  __syncthreads();
+  // softmax over the k picks, summed in rank order
+  const float m = sel[0];
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __expf(sel[j] - m);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane + 64 * u;
+    if (e < E && rank[u] < k) {
+      ids[t * k + rank[u]] = e;
+      w[t * k + rank[u]] = __expf(sel[rank[u]] - m) / sum;
     }
   }
 }

@@ -85,10 +85,12 @@ int attn_splits_for(int B, int H, int n, int keys);
 // ---------------------------------------------------------------- misc (k_misc.hip)
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st);
 int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st);
-// RoPE on q,k from qkv [T][3A] (T = B*n, positions pos0 + i) and scatter:
+// tab[i][j] = (cos, sin) of (pos0 + i) * theta^(-2j/dh), i < n, j < dh/2 (float pairs)
+int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st);
+// RoPE on q,k from qkv [T][3A] (T = B*n, token i rotated by tab row i) and scatter:
 // q -> q_out [B][H][n][dh]; k,v -> (b,h) planes at kdst/vdst + (b*H+h)*dst_bh + (row0+i)*dh.
-int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, int pos0, float theta,
-                 void* q_out, void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st);
+int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, const float* tab, void* q_out,
+                 void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st);
 // x[t] = round(x[t] + sum_j w[t][j] * y[pos[t][j]] + ys[t])
 int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w,
                 const int* pos, int T, int k, int d, hipStream_t st);
