@@ -32,6 +32,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (scaled by 2.0 and 1.0, the factors a 1 GiB device copy reads) for the
+# kernels as they are now; profiles/moe_gateup_c2_loop30_bf16.md has the
+# commands.  An entry is dropped whenever its kernel changes.
+MEASURED_TRAFFIC = {
+    ("moe_gateup", "c2_loop30_bf16"): (364963 * 2 + 4207) * 1024,
+}
+
+
 def algorithmic(cfg, kernel: str):
     """(bytes, flops) one launch of `kernel` must move/perform, per layer and step."""
     T = cfg.batch * cfg.canvas_len
@@ -259,7 +268,8 @@ def main():
     else:
         bound, achieved, peak, unit = "hbm", bytes_ / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": None, "kernel": args.kernel,
+                "frac": achieved / peak, "traffic": MEASURED_TRAFFIC.get((args.kernel, cfg.name)),
+                "kernel": args.kernel,
                 "avg_launch_us": avg_s * 1e6, "launches": launches,
                 "algorithmic_bytes_per_launch": bytes_, "algorithmic_flops_per_launch": flops}
 
