@@ -240,12 +240,14 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
       HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
       HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
     }
-    HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
+    // bf16: the routed gate/up kernel derives the permutation itself
+    if (at != ACT_BF16) HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
   }
   if (at == ACT_BF16) {
     {
-      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU
-      HIP_OK(moe_experts(m->wt, true, m->a, m->pair_row, m->off, E, w.w_gu, w.s_gu, d, de, m->h, st));
+      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU, routing in the kernel
+      const MoeRoute route{m->topk_ids, T, k, m->off, m->pair_row, m->pos};
+      HIP_OK(moe_experts(m->wt, true, m->a, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, m->h, st, &route));
     }
     {
       ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down

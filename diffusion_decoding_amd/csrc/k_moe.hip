@@ -110,15 +110,73 @@ struct MoeArgs {
   int K;                // reduction length (multiple of 32)
   int Nout;             // outputs per token: d_expert (gate/up) or d_model (down)
   void* out;            // gate/up: h bf16 [pairs][Nout]; down: y fp32 [pairs][Nout]
+  // gate/up with routing in the kernel (ids != null): the top-k expert ids
+  // [T][k]; each expert's workgroups derive its pair range and token list
+  // from them, and workgroup 0 of each expert writes off, pair_row and pos
+  // (slot of pair (t, j) = off[e] + rank of t among e's tokens) for the
+  // kernels after it.
+  const int* ids;
+  int T, k;
+  int* off_out;
+  int* pair_row_out;
+  int* pos_out;
 };
+
+constexpr int ROUTE_MAX_TOKENS = 1024;
+
+// The routing of one expert e from the top-k ids: pairs of experts below e
+// (its pair offset), and its tokens in ascending order with the slot j that
+// picked e (each token picks an expert at most once).  Deterministic: the
+// order comes from a wave-0 scan over token chunks, not from atomics' order.
+struct ExpertRoute {
+  int off, cnt;
+};
+__device__ __forceinline__ ExpertRoute route_expert(const MoeArgs& a, int e, int* tok, unsigned char* slot,
+                                                    signed char* flag, int* red) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid == 0) red[0] = 0;
+  __syncthreads();
+  int less = 0;
+  for (int t = tid; t < a.T; t += nt) {
+    int m = -1;
+    for (int j = 0; j < a.k; ++j) {
+      const int id = a.ids[t * a.k + j];
+      less += id < e;
+      m = id == e ? j : m;
+    }
+    flag[t] = (signed char)m;
+  }
+  less = wave_sum_i(less);
+  if ((tid & 63) == 0) atomicAdd(&red[0], less);  // integer sum: order-free
+  __syncthreads();
+  if (tid < 64) {  // wave 0: ordered compaction, 64 tokens per round
+    int base = 0;
+    for (int t0 = 0; t0 < a.T; t0 += 64) {
+      const int t = t0 + tid;
+      const int m = t < a.T ? flag[t] : -1;
+      const unsigned long long bal = __ballot(m >= 0);
+      if (m >= 0) {
+        const int r = base + __popcll(bal & ((1ull << tid) - 1ull));
+        tok[r] = t;
+        slot[r] = (unsigned char)m;
+      }
+      base += __popcll(bal);
+    }
+    if (tid == 0) red[1] = base;
+  }
+  __syncthreads();
+  return ExpertRoute{red[0], red[1]};
+}
 
 // The expert's token rows of one pass (up to 16 MTMAX of them, all K) are
 // staged once per workgroup in LDS, zero-filled past the last pair; the four
 // waves read their operand-B fragments from there, so the only global loads
 // in the k loop are the weight stream.
+// Pass row r is token row gather[gidx0 + r] of X, or row gidx0 + r when
+// gather is null.
 template <int MT>
-__device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pitch, int pbeg, int rows,
-                                             bool gather) {
+__device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pitch, const int* gather, int gidx0,
+                                             int rows) {
   const int cpr = a.K / 8;  // 16-byte chunks per row
   const int total = 16 * MT * cpr, nt = blockDim.x;
   // batches of 4 loads per thread in flight before their LDS stores
@@ -129,7 +187,7 @@ __device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pit
       const int c = c0 + u * nt, r = c / cpr, k = (c - r * cpr) * 8;
       v[u] = u32x4{0u, 0u, 0u, 0u};
       if (c < total && r < rows) {
-        const long long row = gather ? (long long)a.pair_row[pbeg + r] : (long long)(pbeg + r);
+        const long long row = gather ? (long long)gather[gidx0 + r] : (long long)(gidx0 + r);
         v[u] = *(const u32x4*)(a.X + row * a.K + k);
       }
     }
@@ -287,18 +345,57 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
   const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
   const int e = blockIdx.y;
-  const int pbeg = a.off[e], pcnt = a.off[e + 1] - pbeg;
-  if (pcnt <= 0) return;  // uniform over the workgroup
   const int n0 = blockIdx.x * rows_per_wg + (threadIdx.x >> 6) * 16 * NB;
   const bool active = n0 < min(a.Nout, (blockIdx.x + 1) * rows_per_wg);
   WStream<WL, GU, NB, MD> ws;
   ws.init(a, e, n0);
+  if (active) ws.fill();  // the first weight tiles are in flight during the routing and staging
+  int pbeg, pcnt;
+  // token rows: pair p of the expert (p = 0 .. pcnt-1) is X row gather[gbase + p],
+  // or X row pbeg + p without a gather list (down: X holds one row per pair)
+  const int* gather = nullptr;
+  int gbase = 0;
+  if constexpr (GU) {
+    __shared__ int tok[ROUTE_MAX_TOKENS];
+    __shared__ unsigned char slot[ROUTE_MAX_TOKENS];
+    __shared__ signed char flag[ROUTE_MAX_TOKENS];
+    __shared__ int red[2];
+    if (a.ids) {
+      const ExpertRoute r = route_expert(a, e, tok, slot, flag, red);
+      pbeg = r.off;
+      pcnt = r.cnt;
+      gather = tok;
+      gbase = 0;
+      if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < pcnt; i += blockDim.x) {
+          a.pair_row_out[pbeg + i] = tok[i];
+          a.pos_out[tok[i] * a.k + slot[i]] = pbeg + i;
+        }
+        if (threadIdx.x == 0) {
+          a.off_out[e] = pbeg;
+          if (e == (int)gridDim.y - 1) a.off_out[e + 1] = pbeg + pcnt;
+        }
+      }
+    } else {
+      pbeg = a.off[e];
+      pcnt = a.off[e + 1] - pbeg;
+      gather = a.pair_row;
+      gbase = pbeg;
+    }
+  } else {
+    pbeg = a.off[e];
+    pcnt = a.off[e + 1] - pbeg;
+    gbase = pbeg;
+  }
+  if (pcnt <= 0) return;  // uniform over the workgroup; nothing was staged
   for (int p0 = 0; p0 < pcnt; p0 += 16 * MTMAX) {
     const int rows = min(16 * MTMAX, pcnt - p0);
-    if (active) ws.fill();    // weights in flight while the tokens are staged
-    if (p0) __syncthreads();  // the previous pass is done with xs
-    if (rows <= 16) stage_tokens<1>(a, xs, pitch, pbeg + p0, rows, GU);
-    else stage_tokens<MTMAX>(a, xs, pitch, pbeg + p0, rows, GU);
+    if (p0) {
+      __syncthreads();        // the previous pass is done with xs
+      if (active) ws.fill();  // the next pass streams the weights again
+    }
+    if (rows <= 16) stage_tokens<1>(a, xs, pitch, gather, gbase + p0, rows);
+    else stage_tokens<MTMAX>(a, xs, pitch, gather, gbase + p0, rows);
     __syncthreads();
     if (active) {
       if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
@@ -314,7 +411,7 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   const int waves = (blocks + split - 1) / split;              // per workgroup
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
   const size_t lds = size_t(16 * MTMAX) * (a.K + 16) * sizeof(bf16);
-  if (lds > 160 * 1024) return int(hipErrorInvalidValue);
+  if (lds + (GU ? 8192 : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
   (void)hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX>), dim3(split, E), dim3(64 * waves), lds, st, a,
@@ -389,9 +486,19 @@ int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, i
 }
 
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
-                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st) {
+                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
+                const MoeRoute* route) {
   if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
   MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
+  if (route) {
+    if (!gate_up || route->T > ROUTE_MAX_TOKENS || route->k > 8) return int(hipErrorInvalidValue);
+    a.ids = route->ids;
+    a.T = route->T;
+    a.k = route->k;
+    a.off_out = route->off;
+    a.pair_row_out = route->pair_row;
+    a.pos_out = route->pos;
+  }
   if (wt == W_BF16) return launch<WFmt<bf16, 1>>(gate_up, a, E, st);
   if (wt == W_FP8 && K % 64 == 0) return launch<WFmt<f8, 2>>(gate_up, a, E, st);
   if (wt == W_FP8) return launch<WFmt<f8, 1>>(gate_up, a, E, st);

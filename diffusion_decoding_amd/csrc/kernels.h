@@ -55,8 +55,18 @@ int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax,
 // token row pair_row[p] of X [T][K] and W [E][2*Nout][K]; otherwise y[p][n] = X[p] . W[n] (fp32)
 // with W [E][Nout][K].  Pairs of expert e are [off[e], off[e+1]).  W is in the tiled layout of
 // moe_pack (Nout and K multiples of 16 and 32).
+// route (gate/up only, may be null): derive the routing from the top-k ids in the kernel instead
+// of reading off/pair_row, and write off [E+1], pair_row [T*k] and pos [T][k] for later kernels.
+struct MoeRoute {
+  const int* ids;  // [T][k]
+  int T, k;        // T <= 1024
+  int* off;
+  int* pair_row;
+  int* pos;
+};
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
-                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st);
+                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
+                const MoeRoute* route = nullptr);
 // Row-major [n_mats][rows][cols] expert matrices -> the tiled layout moe_experts reads
 // (rows % 16 == 0, cols % 32 == 0; src and dst must not overlap).
 int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t st);
