@@ -48,6 +48,40 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, int d, float e
   for (int c = threadIdx.x; c < d; c += 256) yr[c] = from_f32<T>(to_f32(xr[c]) * inv);
 }
 
+// bf16 rows with d % 8 == 0 and d <= 8192: one 16-byte chunk of the row per
+// thread, loaded once and kept in registers between the sum of squares and
+// the scaled write.
+__global__ __launch_bounds__(1024) void rmsnorm_bf16_kernel(const bf16* x, int d, float eps, bf16* y) {
+  __shared__ float red[16];
+  const int t = blockIdx.x, tid = threadIdx.x, c = tid * 8;
+  const bool live = c < d;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const u32x4 q = *(const u32x4*)(x + (long long)t * d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+  ss = wave_sum(ss);
+  const int nw = blockDim.x >> 6;
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  ss = 0.f;
+  for (int i = 0; i < nw; ++i) ss += red[i];
+  const float inv = 1.0f / sqrtf(ss / float(d) + eps);
+  if (live) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i] * inv, v[2 * i + 1] * inv);
+    *(u32x4*)(y + (long long)t * d + c) = o;
+  }
+}
+
 // cos/sin of (pos0 + i) * theta^(-2j/dh) for i < n, j < dh/2, evaluated in
 // double precision and rounded to binary32 (binary32 angles at positions in
 // the thousands would carry ~1e-3 rad of error); theta == 0 gives the
@@ -94,16 +128,49 @@ __global__ void rope_kernel(const T* qkv, int B, int n, int H, int dh, const flo
   T* qo = q_out + ((long long)bh * n + i) * dh;
   T* ko = kdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
   T* vo = vdst + (long long)bh * dst_bh + (long long)(row0 + i) * dh;
+  if constexpr (std::is_same<T, bf16>::value) {
+    // 8-byte accesses: four bf16 of each half-row
+    auto ld4 = [](const T* p, float* f) {
+      const u32x2 w = *(const u32x2*)p;
+      f[0] = __uint_as_float(w[0] << 16);
+      f[1] = __uint_as_float(w[0] & 0xffff0000u);
+      f[2] = __uint_as_float(w[1] << 16);
+      f[3] = __uint_as_float(w[1] & 0xffff0000u);
+    };
+    auto st4 = [](T* p, const float* f) { *(u32x2*)p = u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])}; };
+    float a1[4], a2[4], o1[4], o2[4];
+    ld4(row + h * dh + j, a1);
+    ld4(row + h * dh + j + half, a2);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float q1 = to_f32(row[h * dh + j + u]), q2 = to_f32(row[h * dh + j + u + half]);
-    qo[j + u] = from_f32<T>(q1 * c[u] - q2 * s[u]);
-    qo[j + u + half] = from_f32<T>(q2 * c[u] + q1 * s[u]);
-    const float k1 = to_f32(row[A + h * dh + j + u]), k2 = to_f32(row[A + h * dh + j + u + half]);
-    ko[j + u] = from_f32<T>(k1 * c[u] - k2 * s[u]);
-    ko[j + u + half] = from_f32<T>(k2 * c[u] + k1 * s[u]);
-    vo[j + u] = row[2 * A + h * dh + j + u];
-    vo[j + u + half] = row[2 * A + h * dh + j + u + half];
+    for (int u = 0; u < 4; ++u) {
+      o1[u] = a1[u] * c[u] - a2[u] * s[u];
+      o2[u] = a2[u] * c[u] + a1[u] * s[u];
+    }
+    st4(qo + j, o1);
+    st4(qo + j + half, o2);
+    ld4(row + A + h * dh + j, a1);
+    ld4(row + A + h * dh + j + half, a2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      o1[u] = a1[u] * c[u] - a2[u] * s[u];
+      o2[u] = a2[u] * c[u] + a1[u] * s[u];
+    }
+    st4(ko + j, o1);
+    st4(ko + j + half, o2);
+    *(u32x2*)(vo + j) = *(const u32x2*)(row + 2 * A + h * dh + j);
+    *(u32x2*)(vo + j + half) = *(const u32x2*)(row + 2 * A + h * dh + j + half);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float q1 = to_f32(row[h * dh + j + u]), q2 = to_f32(row[h * dh + j + u + half]);
+      qo[j + u] = from_f32<T>(q1 * c[u] - q2 * s[u]);
+      qo[j + u + half] = from_f32<T>(q2 * c[u] + q1 * s[u]);
+      const float k1 = to_f32(row[A + h * dh + j + u]), k2 = to_f32(row[A + h * dh + j + u + half]);
+      ko[j + u] = from_f32<T>(k1 * c[u] - k2 * s[u]);
+      ko[j + u + half] = from_f32<T>(k2 * c[u] + k1 * s[u]);
+      vo[j + u] = row[2 * A + h * dh + j + u];
+      vo[j + u + half] = row[2 * A + h * dh + j + u + half];
+    }
   }
 }
 
@@ -283,7 +350,14 @@ int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* 
 int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st) {
   if (T <= 0) return 0;
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(T), dim3(256), 0, st, (const bf16*)x, d, eps, (bf16*)y);
+  {
+    if (d % 8 == 0 && d <= 8192) {
+      const int threads = ((d / 8 + 63) / 64) * 64;
+      hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3(T), dim3(threads), 0, st, (const bf16*)x, d, eps, (bf16*)y);
+    } else {
+      hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(T), dim3(256), 0, st, (const bf16*)x, d, eps, (bf16*)y);
+    }
+  }
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, st, (const float*)x, d, eps, (float*)y);
   return int(hipGetLastError());

@@ -52,6 +52,7 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, in
   __syncthreads();
   const int E2 = (E + 1) & ~1;
   int rank[4] = {0, 0, 0, 0};
+#pragma unroll 8
   for (int e = 0; e < E2; e += 2) {
     const u32x4 kk = *(const u32x4*)&ks[e];
     const unsigned long long k0 = ((unsigned long long)kk[1] << 32) | kk[0];
