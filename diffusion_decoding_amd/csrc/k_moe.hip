@@ -412,8 +412,11 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
   const size_t lds = size_t(16 * MTMAX) * (a.K + 16) * sizeof(bf16);
   if (lds + (GU ? 8192 : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
-  (void)hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  // once per kernel (not inside a graph capture): the largest dynamic LDS any launch may ask for
+  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     160 * 1024 - (GU ? 8192 : 0));
+  if (attr != hipSuccess) return int(attr);
   hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);
   return int(hipGetLastError());
