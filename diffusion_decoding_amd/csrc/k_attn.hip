@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                                                         int per_xcd) {
   // K row pitch: an odd multiple of 32 B keeps the 16-row x 64-byte fragment
   // reads at full LDS rate.  V^T row pitch 72 elements (36 dwords): the
-  // 8-byte fragment reads of 16 rows land on 16 distinct 4-bank groups, and
+  // 16-byte fragment reads of 16 rows land on 16 distinct 4-bank groups, and
   // in the transposing writes the two 16-lane row groups of a half-wave sit
   // 32 banks apart (8 rows x 36 dwords = 32 mod 64), so neither side
   // conflicts.
@@ -258,16 +258,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int kbeg = z * keys_per_split;
   const int kend = min(total, kbeg + keys_per_split);
 
-  const bf16* K0 = (const bf16*)a.k0 + (long long)bh * a.s0_bh;
-  const bf16* V0 = (const bf16*)a.v0 + (long long)bh * a.s0_bh;
-  const bf16* K1 = a.len1 ? (const bf16*)a.k1 + (long long)bh * a.s1_bh : K0;
-  const bf16* V1 = a.len1 ? (const bf16*)a.v1 + (long long)bh * a.s1_bh : V0;
-  // key row j of either segment; rows past the split end are clamped to its
-  // last key (their scores are masked to -inf)
-  auto krow = [&](int j, const bf16* S0, const bf16* S1) -> const bf16* {
-    j = min(j, kend - 1);
-    return j < a.len0 ? S0 + (long long)j * DH : S1 + (long long)(j - a.len0) * DH;
-  };
+  // Keys and values come from two segments (the cache rows, then the canvas
+  // rows), each read through a buffer resource that covers exactly its rows:
+  // a row is loaded from both at 32-bit offsets, the segment that does not
+  // hold it returns zeros (its offset is past the end, or negative and so
+  // past the end as unsigned), and the two results are OR-ed.  Rows past the
+  // split end are other splits' keys (or zeros past the last key); their
+  // scores are masked to -inf, so their values meet p = 0.
+  constexpr int RB = DH * 2;  // bytes per row
+  const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.k0 + (long long)bh * a.s0_bh), (short)0, a.len0 * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.v0 + (long long)bh * a.s0_bh), (short)0, a.len0 * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.len1 ? (const bf16*)a.k1 + (long long)bh * a.s1_bh : (const bf16*)a.k0), (short)0, a.len1 * RB,
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.len1 ? (const bf16*)a.v1 + (long long)bh * a.s1_bh : (const bf16*)a.v0), (short)0, a.len1 * RB,
+      0x00020000);
 
   // Q as the B operand of S^T = K Q^T
   const bf16* qrow = (const bf16*)a.q + ((long long)bh * a.n + min(qi, a.n - 1)) * DH;
@@ -286,18 +294,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // Threads past VCH repeat a block: same loads, same values stored to the
   // same LDS words.
   const int vb = tid % VCH, vkb = vb % 16, vcol = (vb / 16) * 8;
+  // this thread's byte offsets inside a key tile
+  int koff[KPT], voff[4];
+#pragma unroll
+  for (int p = 0; p < KPT; ++p) {
+    const int c = tid + p * 256;
+    koff[p] = (c / (DH / 8)) * RB + (c % (DH / 8)) * 16;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) voff[p] = (4 * vkb + p) * RB + vcol * 2;
   u32x4 kreg[D][KPT], vreg[D][4];
   auto gload = [&](int t, int u) {
     const int kt0 = kbeg + 64 * min(t, ntiles - 1);
+    const int b0 = kt0 * RB, b1 = (kt0 - a.len0) * RB;  // tile start in each segment
 #pragma unroll
-    for (int p = 0; p < KPT; ++p) {
-      const int c = tid + p * 256;
-      const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      kreg[u][p] = *(const u32x4*)(krow(kt0 + row, K0, K1) + col);
-    }
+    for (int p = 0; p < KPT; ++p)
+      kreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rk0, koff[p] + b0, 0, 0) |
+                   __builtin_amdgcn_raw_buffer_load_b128(rk1, koff[p] + b1, 0, 0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vreg[u][p] = *(const u32x4*)(krow(kt0 + 4 * vkb + p, V0, V1) + vcol);
+    for (int p = 0; p < 4; ++p)
+      vreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rv0, voff[p] + b0, 0, 0) |
+                   __builtin_amdgcn_raw_buffer_load_b128(rv1, voff[p] + b1, 0, 0);
   };
+  // V^T position of this thread's four keys: inside each 32-key block the
+  // keys are stored in the order the P.V MFMA consumes them (lane group g
+  // takes keys 4g..4g+3 and 16+4g..16+4g+3), so a fragment is one 16-byte read
+  const int vpos = 32 * (vkb >> 3) + 8 * (vkb & 3) + 4 * ((vkb >> 2) & 1);
   auto lstore = [&](int buf, int u) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
@@ -305,13 +327,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
       *(u32x4*)&Ks[buf][row * LDKS + col] = kreg[u][p];
     }
-    // dim vcol+e: keys 4vkb..4vkb+3 as one 8-byte word
+    // dim vcol+e: keys 4vkb..4vkb+3 as one 8-byte word at their V^T position
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1, sh = (e & 1) * 16;
       const uint32_t k0 = (vreg[u][0][w] >> sh) & 0xffffu, k1 = (vreg[u][1][w] >> sh) & 0xffffu;
       const uint32_t k2 = (vreg[u][2][w] >> sh) & 0xffffu, k3 = (vreg[u][3][w] >> sh) & 0xffffu;
-      *(u32x2*)&Vt[buf][(vcol + e) * LDV + 4 * vkb] = u32x2{k0 | (k1 << 16), k2 | (k3 << 16)};
+      *(u32x2*)&Vt[buf][(vcol + e) * LDV + vpos] = u32x2{k0 | (k1 << 16), k2 | (k3 << 16)};
     }
   };
 
@@ -352,12 +374,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int df = 0; df < NDF; ++df) {
-        const bf16* vr = &Vt[buf][(16 * df + c16) * LDV + 32 * kb + 4 * g4];
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 16);
-        va[kb][df] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
+      for (int df = 0; df < NDF; ++df) va[kb][df] = *(const u32x4*)&Vt[buf][(16 * df + c16) * LDV + 32 * kb + 8 * g4];
     __builtin_amdgcn_sched_barrier(0);
     float tmax = -INFINITY;
 #pragma unroll
