@@ -251,7 +251,8 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     }
     {
       ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down
-      HIP_OK(moe_experts(m->wt, false, m->h, m->pair_row, m->off, E, w.w_d, w.s_d, de, d, m->y, st));
+      HIP_OK(moe_experts(m->wt, false, m->h, m->pair_row, m->off, E, w.w_d, w.s_d, de, d, m->y, st, nullptr,
+                         T * k));
     }
   } else {
     {

@@ -47,7 +47,7 @@
 namespace dg {
 namespace {
 
-constexpr int MTMAX = 2;   // 16-token tiles per pass over the weights
+constexpr int MTGU = 2;    // 16-token tiles per pass over the gate/up weights (all K staged)
 // Weight loads are non-temporal (cache-policy bit nt): every weight byte is
 // read once per step, so keeping it in L2 only evicts the token rows and
 // outputs; measured at 128 experts x 16 tokens the gate/up stream went from
@@ -168,7 +168,7 @@ __device__ __forceinline__ ExpertRoute route_expert(const MoeArgs& a, int e, int
   return ExpertRoute{red[0], red[1]};
 }
 
-// The expert's token rows of one pass (up to 16 MTMAX of them, all K) are
+// The expert's token rows of one pass (up to 16 MTP of them, all K) are
 // staged once per workgroup in LDS, zero-filled past the last pair; the four
 // waves read their operand-B fragments from there, so the only global loads
 // in the k loop are the weight stream.
@@ -335,12 +335,12 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
   }
 }
 
-// grid (split, E), blockDim = 64 * waves, dynamic LDS = 16 MTMAX rows of
+// grid (split, E), blockDim = 64 * waves, dynamic LDS = 16 MTP rows of
 // K + 16 bf16.  Workgroup x of expert e owns output rows [x * rows_per_wg,
 // (x + 1) * rows_per_wg); wave w of it owns 16 NB of them.  The expert's pairs
-// go in passes of up to 16 MTMAX tokens, each pass staging its tokens in LDS
+// go in passes of up to 16 MTP tokens, each pass staging its tokens in LDS
 // and streaming the wave's weights once.
-template <typename WL, bool GU, int NB, int MD, int TMAX>
+template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP>
 __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
   const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
@@ -388,36 +388,38 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
     gbase = pbeg;
   }
   if (pcnt <= 0) return;  // uniform over the workgroup; nothing was staged
-  for (int p0 = 0; p0 < pcnt; p0 += 16 * MTMAX) {
-    const int rows = min(16 * MTMAX, pcnt - p0);
+  for (int p0 = 0; p0 < pcnt; p0 += 16 * MTP) {
+    const int rows = min(16 * MTP, pcnt - p0);
     if (p0) {
       __syncthreads();        // the previous pass is done with xs
       if (active) ws.fill();  // the next pass streams the weights again
     }
     if (rows <= 16) stage_tokens<1>(a, xs, pitch, gather, gbase + p0, rows);
-    else stage_tokens<MTMAX>(a, xs, pitch, gather, gbase + p0, rows);
+    else if (MTP > 2 && rows <= 32) stage_tokens<2>(a, xs, pitch, gather, gbase + p0, rows);
+    else stage_tokens<MTP>(a, xs, pitch, gather, gbase + p0, rows);
     __syncthreads();
     if (active) {
       if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
-      else moe_wave<WL, GU, NB, MD, MTMAX>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+      else if (MTP > 2 && rows <= 32) moe_wave<WL, GU, NB, MD, 2>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+      else moe_wave<WL, GU, NB, MD, MTP>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
     }
   }
 }
 
-template <typename WL, bool GU, int NB, int MD, int TMAX>
+template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP>
 int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   if (a.K % (32 * WL::SPS)) return int(hipErrorInvalidValue);
   const int blocks = (a.Nout + 16 * NB - 1) / (16 * NB);       // 16 NB-row wave blocks per expert
   const int waves = (blocks + split - 1) / split;              // per workgroup
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
-  const size_t lds = size_t(16 * MTMAX) * (a.K + 16) * sizeof(bf16);
+  const size_t lds = size_t(16 * MTP) * (a.K + 16) * sizeof(bf16);
   if (lds + (GU ? 8192 : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
   // once per kernel (not inside a graph capture): the largest dynamic LDS any launch may ask for
-  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      160 * 1024 - (GU ? 8192 : 0));
   if (attr != hipSuccess) return int(attr);
-  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX>), dim3(split, E), dim3(64 * waves), lds, st, a,
+  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);
   return int(hipGetLastError());
 }
@@ -431,11 +433,16 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
 // flight (about 11 MB over the chip; 4 stages per wave ran 10-30% slower),
 // the short down streams want a deeper ring.  The thread bound sets the register
 // budget.
+// Down with many pairs per expert (pooled canvases): up to 96 tokens per pass
+// (d_expert rows fit LDS whole), so the weights are streamed once.
 template <typename WL>
-int launch(bool gu, const MoeArgs& a, int E, hipStream_t st) {
-  if (gu) return launch_k<WL, true, 2, 1, 768>(a, E, 2, st);
+int launch(bool gu, const MoeArgs& a, int E, int pairs, hipStream_t st) {
+  if (gu) return launch_k<WL, true, 2, 1, 768, MTGU>(a, E, 2, st);
   const int blocks = (a.Nout + 15) / 16;
-  return launch_k<WL, false, 1, 4, 512>(a, E, (blocks + 7) / 8, st);
+  const int split = (blocks + 7) / 8;
+  if (pairs > 24 * E && size_t(96) * (a.K + 16) * sizeof(bf16) <= 160 * 1024)
+    return launch_k<WL, false, 1, 4, 512, 6>(a, E, split, st);
+  return launch_k<WL, false, 1, 4, 512, 2>(a, E, split, st);
 }
 
 // Row-major [n][rows][cols] -> tiled layout (see the top of this file): one
@@ -490,7 +497,7 @@ int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, i
 
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
-                const MoeRoute* route) {
+                const MoeRoute* route, int pairs) {
   if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
   MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
   if (route) {
@@ -502,9 +509,9 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
     a.pair_row_out = route->pair_row;
     a.pos_out = route->pos;
   }
-  if (wt == W_BF16) return launch<WFmt<bf16, 1>>(gate_up, a, E, st);
-  if (wt == W_FP8 && K % 64 == 0) return launch<WFmt<f8, 2>>(gate_up, a, E, st);
-  if (wt == W_FP8) return launch<WFmt<f8, 1>>(gate_up, a, E, st);
+  if (wt == W_BF16) return launch<WFmt<bf16, 1>>(gate_up, a, E, pairs, st);
+  if (wt == W_FP8 && K % 64 == 0) return launch<WFmt<f8, 2>>(gate_up, a, E, pairs, st);
+  if (wt == W_FP8) return launch<WFmt<f8, 1>>(gate_up, a, E, pairs, st);
   return int(hipErrorInvalidValue);
 }
 

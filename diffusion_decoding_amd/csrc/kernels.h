@@ -64,9 +64,10 @@ struct MoeRoute {
   int* pair_row;
   int* pos;
 };
+// pairs: T * k (sizes the token passes; 0 = few pairs per expert).
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
-                const MoeRoute* route = nullptr);
+                const MoeRoute* route = nullptr, int pairs = 0);
 // Row-major [n_mats][rows][cols] expert matrices -> the tiled layout moe_experts reads
 // (rows % 16 == 0, cols % 32 == 0; src and dst must not overlap).
 int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t st);
