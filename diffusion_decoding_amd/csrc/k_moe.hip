@@ -235,62 +235,13 @@ struct WStream {
   }
 };
 
-// One wave: output rows n0 .. n0 + 16 NB - 1 (for gate/up: those gate rows
-// and the matching up rows) of expert e against the MT 16-token tiles staged
-// in xs (pass rows pbeg .. pbeg + rows - 1 of the expert's pairs); the weight
-// ring of ws has been filled.
-template <typename WL, bool GU, int NB, int MD, int MT>
-__device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int pitch,
-                                         WStream<WL, GU, NB, MD>& ws, int e, int n0, int pbeg, int rows) {
-  using WS = WStream<WL, GU, NB, MD>;
-  constexpr int SPS = WL::SPS, SKE = WS::SKE, NW = WS::NW;
+// Epilogue of one wave: lane holds token 16 t + c16 of the pass and outputs
+// nb + 0..3 of block b; gate/up writes h = bf16(silu(g) * u), down writes y (fp32).
+template <typename WL, bool GU, int NB, int MT>
+__device__ __forceinline__ void moe_epilogue(const MoeArgs& a, const f32x4 (&acc)[GU ? 2 * NB : NB][MT], int e,
+                                             int n0, int pbeg, int rows) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
   const long long wrows = GU ? 2LL * a.Nout : a.Nout;
-  const int KS = ws.KS;
-  const bf16* xr = xs + c16 * pitch;
-
-  f32x4 acc[NW][MT];
-#pragma unroll
-  for (int w = 0; w < NW; ++w)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // The main loop has no conditions and the MFMAs read a slot before its
-  // refill is issued into the same registers, so the ring needs no copies
-  // and the compiler's wait before a slot is for exactly that slot's loads
-  // (the MD - 1 later stages stay in flight); the scheduling barriers keep
-  // the loads in stage order.
-  auto step = [&](int ks, int u, bool refill, int next) {
-#pragma unroll
-    for (int t2 = 0; t2 < SPS; ++t2) {
-      u32x4 xv[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * SKE + WL::x_k(g4, t2));
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const u32x4 wv = WL::get(ws.rw[u][w], t2);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (refill) ws.ld(next, u);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  int k0 = 0;
-  for (; k0 + 2 * MD <= KS; k0 += MD) {
-#pragma unroll
-    for (int u = 0; u < MD; ++u) step(k0 + u, u, true, k0 + u + MD);
-  }
-  // the last 1 .. 2*MD - 1 stages
-#pragma unroll
-  for (int u = 0; u < MD; ++u)
-    if (k0 + u < KS) step(k0 + u, u, k0 + u + MD < KS, k0 + u + MD);
-#pragma unroll
-  for (int u = 0; u < MD; ++u)
-    if (k0 + MD + u < KS) step(k0 + MD + u, u, false, 0);
-
-  // lane: token 16 t + c16 of the pass; outputs nb + 0..3 of block b
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int nb = n0 + 16 * b + 4 * g4;
@@ -335,13 +286,164 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
   }
 }
 
+// One wave: output rows n0 .. n0 + 16 NB - 1 (for gate/up: those gate rows
+// and the matching up rows) of expert e against the MT 16-token tiles staged
+// in xs (pass rows pbeg .. pbeg + rows - 1 of the expert's pairs); the weight
+// ring of ws has been filled.
+template <typename WL, bool GU, int NB, int MD, int MT>
+__device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int pitch,
+                                         WStream<WL, GU, NB, MD>& ws, int e, int n0, int pbeg, int rows) {
+  using WS = WStream<WL, GU, NB, MD>;
+  constexpr int SPS = WL::SPS, SKE = WS::SKE, NW = WS::NW;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+  const int KS = ws.KS;
+  const bf16* xr = xs + c16 * pitch;
+
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The main loop has no conditions and the MFMAs read a slot before its
+  // refill is issued into the same registers, so the ring needs no copies
+  // and the compiler's wait before a slot is for exactly that slot's loads
+  // (the MD - 1 later stages stay in flight); the scheduling barriers keep
+  // the loads in stage order.
+  auto step = [&](int ks, int u, bool refill, int next) {
+#pragma unroll
+    for (int t2 = 0; t2 < SPS; ++t2) {
+      u32x4 xv[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * SKE + WL::x_k(g4, t2));
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const u32x4 wv = WL::get(ws.rw[u][w], t2);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) ws.ld(next, u);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int k0 = 0;
+  for (; k0 + 2 * MD <= KS; k0 += MD) {
+#pragma unroll
+    for (int u = 0; u < MD; ++u) step(k0 + u, u, true, k0 + u + MD);
+  }
+  // the last 1 .. 2*MD - 1 stages
+#pragma unroll
+  for (int u = 0; u < MD; ++u)
+    if (k0 + u < KS) step(k0 + u, u, k0 + u + MD < KS, k0 + u + MD);
+#pragma unroll
+  for (int u = 0; u < MD; ++u)
+    if (k0 + MD + u < KS) step(k0 + MD + u, u, false, 0);
+
+  moe_epilogue<WL, GU, NB, MT>(a, acc, e, n0, pbeg, rows);
+}
+
+// Gate/up with more tokens than fit LDS over all of K (pooled canvases): the
+// pass's token rows are staged in chunks of KC columns, double-buffered.  The
+// loads of chunk c+1 are issued before chunk c is multiplied and stored after
+// it, and one workgroup barrier per chunk hands the buffers over; every
+// thread of the workgroup takes part in the staging, the active waves in the
+// MFMAs.  One weight stage in flight per wave (the gate/up ring depth).
+template <typename WL, int NB, int MT, int KC>
+__device__ __forceinline__ void moe_gu_chunked(const MoeArgs& a, bf16* xs, WStream<WL, true, NB, 1>& ws,
+                                               bool active, int e, int n0, int pbeg, int rows, const int* gather,
+                                               int gidx0) {
+  using WS = WStream<WL, true, NB, 1>;
+  constexpr int SPS = WL::SPS, SKE = WS::SKE, NW = WS::NW;
+  constexpr int CP = KC + 16;  // chunk row pitch: 2 (KC + 16) bytes, an odd multiple of 32
+  constexpr int ROWS = 16 * MT, CPR = KC / 8, TOTAL = ROWS * CPR, PB = 4;
+  constexpr int KCS = KC / SKE;  // weight stages per chunk
+  const int nch = a.K / KC;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  auto buf = [&](int i) { return xs + (i & 1) * (ROWS * CP); };
+  auto xrow = [&](int r) -> const bf16* {
+    const long long row = gather ? (long long)gather[gidx0 + r] : (long long)(gidx0 + r);
+    return a.X + row * a.K;
+  };
+  // staging: 16-byte piece q of the chunk is row q / CPR, columns (q % CPR) * 8;
+  // rows past the pass are zero
+  u32x4 pre[PB];
+  auto pre_load = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int q = tid + u * nt, r = q / CPR, k = (q - r * CPR) * 8;
+      pre[u] = u32x4{0u, 0u, 0u, 0u};
+      if (q < TOTAL && r < rows) pre[u] = *(const u32x4*)(xrow(r) + c * KC + k);
+    }
+  };
+  auto pre_store = [&](bf16* dst) {
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int q = tid + u * nt, r = q / CPR, k = (q - r * CPR) * 8;
+      if (q < TOTAL) *(u32x4*)(dst + r * CP + k) = pre[u];
+    }
+  };
+  auto rest = [&](int c, bf16* dst) {  // pieces past PB per thread (small workgroups)
+    for (int q = tid + PB * nt; q < TOTAL; q += nt) {
+      const int r = q / CPR, k = (q - r * CPR) * 8;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (r < rows) v = *(const u32x4*)(xrow(r) + c * KC + k);
+      *(u32x4*)(dst + r * CP + k) = v;
+    }
+  };
+
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  pre_load(0);
+  pre_store(buf(0));
+  rest(0, buf(0));
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) pre_load(c + 1);
+    if (active) {
+      const bf16* xr = buf(c) + c16 * CP;
+      for (int j = 0; j < KCS; ++j) {
+        const int ks = c * KCS + j;
+#pragma unroll
+        for (int t2 = 0; t2 < SPS; ++t2) {
+          u32x4 xv[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * CP + j * SKE + WL::x_k(g4, t2));
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const u32x4 wv = WL::get(ws.rw[0][w], t2);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < ws.KS) ws.ld(ks + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (c + 1 < nch) {
+      pre_store(buf(c + 1));
+      rest(c + 1, buf(c + 1));
+    }
+    __syncthreads();
+  }
+  if (active) moe_epilogue<WL, true, NB, MT>(a, acc, e, n0, pbeg, rows);
+}
+
 // grid (split, E), blockDim = 64 * waves, dynamic LDS = 16 MTP rows of
-// K + 16 bf16.  Workgroup x of expert e owns output rows [x * rows_per_wg,
-// (x + 1) * rows_per_wg); wave w of it owns 16 NB of them.  The expert's pairs
-// go in passes of up to 16 MTP tokens, each pass staging its tokens in LDS
-// and streaming the wave's weights once.
-template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP>
+// K + 16 bf16 (KC > 0: two buffers of 16 MTP rows of KC + 16).  Workgroup x
+// of expert e owns output rows [x * rows_per_wg, (x + 1) * rows_per_wg); wave
+// w of it owns 16 NB of them.  The expert's pairs go in passes of up to
+// 16 MTP tokens, each pass staging its tokens in LDS and streaming the wave's
+// weights once.
+template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC>
 __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
+  static_assert(KC == 0 || (GU && MD == 1), "chunked staging is the gate/up path with one stage in flight");
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
   const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
   const int e = blockIdx.y;
@@ -394,32 +496,41 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
       __syncthreads();        // the previous pass is done with xs
       if (active) ws.fill();  // the next pass streams the weights again
     }
-    if (rows <= 16) stage_tokens<1>(a, xs, pitch, gather, gbase + p0, rows);
-    else if (MTP > 2 && rows <= 32) stage_tokens<2>(a, xs, pitch, gather, gbase + p0, rows);
-    else stage_tokens<MTP>(a, xs, pitch, gather, gbase + p0, rows);
-    __syncthreads();
-    if (active) {
-      if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
-      else if (MTP > 2 && rows <= 32) moe_wave<WL, GU, NB, MD, 2>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
-      else moe_wave<WL, GU, NB, MD, MTP>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+    if constexpr (KC > 0) {
+      const int gi = gbase + p0, pb = pbeg + p0;
+      if (rows <= 16) moe_gu_chunked<WL, NB, 1, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
+      else if (rows <= 32) moe_gu_chunked<WL, NB, 2, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
+      else if (MTP > 4 && rows <= 64) moe_gu_chunked<WL, NB, 4, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
+      else moe_gu_chunked<WL, NB, MTP, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
+    } else {
+      if (rows <= 16) stage_tokens<1>(a, xs, pitch, gather, gbase + p0, rows);
+      else if (MTP > 2 && rows <= 32) stage_tokens<2>(a, xs, pitch, gather, gbase + p0, rows);
+      else stage_tokens<MTP>(a, xs, pitch, gather, gbase + p0, rows);
+      __syncthreads();
+      if (active) {
+        if (rows <= 16) moe_wave<WL, GU, NB, MD, 1>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+        else if (MTP > 2 && rows <= 32) moe_wave<WL, GU, NB, MD, 2>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+        else moe_wave<WL, GU, NB, MD, MTP>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
+      }
     }
   }
 }
 
-template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP>
+template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC = 0>
 int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
-  if (a.K % (32 * WL::SPS)) return int(hipErrorInvalidValue);
+  if (a.K % (32 * WL::SPS) || (KC > 0 && a.K % KC)) return int(hipErrorInvalidValue);
   const int blocks = (a.Nout + 16 * NB - 1) / (16 * NB);       // 16 NB-row wave blocks per expert
   const int waves = (blocks + split - 1) / split;              // per workgroup
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
-  const size_t lds = size_t(16 * MTP) * (a.K + 16) * sizeof(bf16);
+  const size_t lds = KC > 0 ? size_t(2 * 16 * MTP) * (KC + 16) * sizeof(bf16)
+                            : size_t(16 * MTP) * (a.K + 16) * sizeof(bf16);
   if (lds + (GU ? 8192 : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
   // once per kernel (not inside a graph capture): the largest dynamic LDS any launch may ask for
-  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      160 * 1024 - (GU ? 8192 : 0));
   if (attr != hipSuccess) return int(attr);
-  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP>), dim3(split, E), dim3(64 * waves), lds, st, a,
+  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);
   return int(hipGetLastError());
 }
@@ -433,11 +544,17 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
 // flight (about 11 MB over the chip; 4 stages per wave ran 10-30% slower),
 // the short down streams want a deeper ring.  The thread bound sets the register
 // budget.
-// Down with many pairs per expert (pooled canvases): up to 96 tokens per pass
-// (d_expert rows fit LDS whole), so the weights are streamed once.
+// Many pairs per expert (pooled canvases): up to 96 tokens per pass, so the
+// weights are streamed once -- down stages d_expert-wide rows whole, gate/up
+// stages d_model-wide rows in chunks.
 template <typename WL>
 int launch(bool gu, const MoeArgs& a, int E, int pairs, hipStream_t st) {
-  if (gu) return launch_k<WL, true, 2, 1, 768, MTGU>(a, E, 2, st);
+  if (gu) {
+    // many pairs per expert: up to 96 tokens per pass, staged in 256-column
+    // chunks; 16 outputs per wave keeps the 96-token accumulators in registers
+    if (pairs > 24 * E && a.K % 256 == 0) return launch_k<WL, true, 1, 1, 768, 6, 256>(a, E, 4, st);
+    return launch_k<WL, true, 2, 1, 768, MTGU>(a, E, 2, st);
+  }
   const int blocks = (a.Nout + 15) / 16;
   const int split = (blocks + 7) / 8;
   if (pairs > 24 * E && size_t(96) * (a.K + 16) * sizeof(bf16) <= 160 * 1024)
@@ -502,6 +619,7 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
   MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
   if (route) {
     if (!gate_up || route->T > ROUTE_MAX_TOKENS || route->k > 8) return int(hipErrorInvalidValue);
+    pairs = route->T * route->k;
     a.ids = route->ids;
     a.T = route->T;
     a.k = route->k;
