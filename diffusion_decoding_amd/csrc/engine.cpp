@@ -180,23 +180,35 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   char* kcache = (char*)kv->k + l * layer_stride * m->esz;
   char* vcache = (char*)kv->v + l * layer_stride * m->esz;
 
+  // bf16 with head_dim 128: RoPE and the scatter to the per-head layouts run
+  // in the projection's epilogue; otherwise a separate kernel does them
+  const bool fused_rope = at == ACT_BF16 && dh == 128 && tgemm_supported(at, d);
   {
     ProfScope ps(m, DG_PROF_QKV, st);
     GemmArgs g;
     g.A = m->a; g.lda = d; g.B = w.wqkv; g.ldb = d; g.M = T; g.N = 3 * A; g.K = d;
-    g.C = m->qkv; g.ldc = 3 * A;
-    HIP_OK(gemm(at, at == ACT_BF16 ? W_BF16 : W_F32, EPI_ACT, g, 1, st));
+    if (fused_rope) {
+      g.q_out = m->q; g.seq_n = n; g.heads = H; g.rope_tab = m->rope_tab;
+      g.k_dst = causal ? (void*)kcache : m->kc; g.v_dst = causal ? (void*)vcache : m->vc;
+      g.dst_bh = causal ? cap * dh : (long long)n * dh; g.row0 = causal ? P : 0;
+      HIP_OK(gemm(at, W_BF16, EPI_QKV, g, 1, st));
+    } else {
+      g.C = m->qkv; g.ldc = 3 * A;
+      HIP_OK(gemm(at, at == ACT_BF16 ? W_BF16 : W_F32, EPI_ACT, g, 1, st));
+    }
   }
   AttnArgs aa{};
   aa.q = m->q; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = m->o;
   aa.part_o = m->attn_po; aa.part_ml = m->attn_ml;
   if (!causal) {
-    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, m->kc, m->vc, (long long)n * dh, 0, st));
+    if (!fused_rope)
+      HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, m->kc, m->vc, (long long)n * dh, 0, st));
     aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P;
     aa.k1 = m->kc; aa.v1 = m->vc; aa.s1_bh = (long long)n * dh; aa.len1 = n;
     aa.causal_base = -1;
   } else {
-    HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, kcache, vcache, cap * dh, P, st));
+    if (!fused_rope)
+      HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, kcache, vcache, cap * dh, P, st));
     if (kv_only) return DG_OK;
     aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P + n;
     aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;

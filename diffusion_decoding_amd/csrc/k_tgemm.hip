@@ -275,6 +275,39 @@ __global__ __launch_bounds__(TNT * KG) void tgemm_kernel(GemmArgs g, int tiles_m
         }
       }
     }
+  } else if constexpr (EPI == EPI_QKV) {
+    // tile tn is one head of q, k or v (BN = head_dim = 128) and each wave
+    // holds whole tile rows, so lane column d = 16 jf + c16 (jf < 4) and its
+    // rotate-half partner d + 64 (fragment jf + 4) sit in the same lane:
+    // round q/k/v to bf16, rotate q and k in fp32 with the position's
+    // (cos, sin), round again, and store into the per-head layouts
+    static_assert(BN == 128 && WAVES_N == 1, "QKV epilogue: one head per tile, whole rows per wave");
+    const int H = g.heads, which = tn / H, h = tn - which * H;
+    const float2* tab = (const float2*)g.rope_tab;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wr + 16 * i + 4 * g4 + r;
+        if (m >= g.M) continue;
+        const int b = m / g.seq_n, ti = m - b * g.seq_n;
+        bf16* dst = which == 0 ? (bf16*)g.q_out + ((long long)(b * H + h) * g.seq_n + ti) * 128
+                               : (bf16*)(which == 1 ? g.k_dst : g.v_dst) + (long long)(b * H + h) * g.dst_bh +
+                                     (long long)(g.row0 + ti) * 128;
+        if (which == 2) {
+#pragma unroll
+          for (int jf = 0; jf < 8; ++jf) dst[16 * jf + c16] = f32_to_bf16(acc[i][jf][r]);
+        } else {
+#pragma unroll
+          for (int jf = 0; jf < 4; ++jf) {
+            const int d = 16 * jf + c16;
+            const float x1 = to_f32(f32_to_bf16(acc[i][jf][r])), x2 = to_f32(f32_to_bf16(acc[i][jf + 4][r]));
+            const float2 cs = tab[ti * 64 + d];
+            dst[d] = f32_to_bf16(x1 * cs.x - x2 * cs.y);
+            dst[d + 64] = f32_to_bf16(x2 * cs.x + x1 * cs.y);
+          }
+        }
+      }
   } else if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int q = 0; q < FN / 2; ++q) {
@@ -352,6 +385,10 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
       return launch_t<TB, LM_BM, LM_BN, LM_WM, 2, EPI_LM>(g, st);
     case EPI_SWIGLU:
       return launch_kg<TB, 64, 64, 2, 2, EPI_SWIGLU>(g, st, 2);
+    case EPI_QKV:
+      if (g.N % 128 || !g.seq_n || !g.heads || g.N != 3 * 128 * g.heads) return int(hipErrorInvalidValue);
+      if (g.K % 128 == 0) return launch_t<TB, 64, 128, 4, 2, EPI_QKV, 64, 2>(g, st);
+      return launch_t<TB, 64, 128, 4, 2, EPI_QKV, 64, 1>(g, st);
     case EPI_ACT:
       if (tiles64 >= 256) return launch_kg<TB, 64, 64, 2, 2, EPI_ACT>(g, st, 2);
       return launch_kg<TB, 64, 32, 2, 2, EPI_ACT>(g, st, 2);

@@ -18,6 +18,7 @@ enum GemmEpi {
   EPI_RESID = 2,   // C act  [m][n] = round(C + acc)
   EPI_SWIGLU = 3,  // C act  [m][j] = round(silu(gate_j) * up_j); B rows: gate j, up half+j
   EPI_LM = 4,      // per-row (max, idx, second, sum e^(z-max), sum e^(z-max)(z-max)) over the tile
+  EPI_QKV = 5,     // bf16 QKV projection with head_dim 128: round q/k/v, RoPE q and k (table), scatter
 };
 
 struct GemmArgs {
@@ -35,6 +36,15 @@ struct GemmArgs {
   long long ldc = 0;
   int swiglu_half = 0;             // SWIGLU: B row of up_j is swiglu_half + j
   float* part = nullptr;           // EPI_LM partials [M][n_tiles][5]
+  // EPI_QKV: row m = canvas b * seq_n + token i; q -> q_out [B][heads][seq_n][128];
+  // k, v -> (b, h) planes at k_dst / v_dst + (b * heads + h) * dst_bh + (row0 + i) * 128;
+  // rope_tab [seq_n][64] (cos, sin) pairs
+  void* q_out = nullptr;
+  void* k_dst = nullptr;
+  void* v_dst = nullptr;
+  long long dst_bh = 0;
+  int row0 = 0, seq_n = 0, heads = 0;
+  const float* rope_tab = nullptr;
 };
 
 // Returns 0 or a HIP error code.
