@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
 // With several splits, each workgroup writes an unnormalised partial
 // (O, running max, running sum) and a second kernel merges them in split
 // order.
-template <int DH, int D>
+template <int DH, int D, bool SEG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
                                                         int per_xcd) {
   // K row pitch: an odd multiple of 32 B keeps the 16-row x 64-byte fragment
@@ -259,12 +259,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int kend = min(total, kbeg + keys_per_split);
 
   // Keys and values come from two segments (the cache rows, then the canvas
-  // rows), each read through a buffer resource that covers exactly its rows:
-  // a row is loaded from both at 32-bit offsets, the segment that does not
-  // hold it returns zeros (its offset is past the end, or negative and so
-  // past the end as unsigned), and the two results are OR-ed.  Rows past the
-  // split end are other splits' keys (or zeros past the last key); their
-  // scores are masked to -inf, so their values meet p = 0.
+  // rows).  SEG (one segment, or a cache length that is a multiple of 64, so
+  // no key tile spans both): each tile is read through a buffer resource built on the scalar
+  // unit for its segment, starting at the tile and ending with the segment.
+  // Otherwise each segment has one resource covering exactly its rows: a row
+  // is loaded from both at 32-bit offsets, the segment that does not hold it
+  // returns zeros (its offset is past the end, or negative and so past the
+  // end as unsigned), and the two results are OR-ed.  Rows past the split end
+  // are other splits' keys (or zeros past the last key); their scores are
+  // masked to -inf, so their values meet p = 0.
   constexpr int RB = DH * 2;  // bytes per row
   const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const bf16*)a.k0 + (long long)bh * a.s0_bh), (short)0, a.len0 * RB, 0x00020000);
@@ -306,6 +309,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   u32x4 kreg[D][KPT], vreg[D][4];
   auto gload = [&](int t, int u) {
     const int kt0 = kbeg + 64 * min(t, ntiles - 1);
+    if constexpr (SEG) {
+      const bool s1 = kt0 >= a.len0;  // uniform
+      const int r0 = s1 ? kt0 - a.len0 : kt0, rows = s1 ? a.len1 - r0 : a.len0 - r0;
+      const bf16* kb = s1 ? (const bf16*)a.k1 + (long long)bh * a.s1_bh : (const bf16*)a.k0 + (long long)bh * a.s0_bh;
+      const bf16* vb = s1 ? (const bf16*)a.v1 + (long long)bh * a.s1_bh : (const bf16*)a.v0 + (long long)bh * a.s0_bh;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (long long)r0 * DH), (short)0, rows * RB, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vb + (long long)r0 * DH), (short)0, rows * RB, 0x00020000);
+#pragma unroll
+      for (int p = 0; p < KPT; ++p) kreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[p], 0, 0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) vreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[p], 0, 0);
+      return;
+    }
     const int b0 = kt0 * RB, b1 = (kt0 - a.len0) * RB;  // tile start in each segment
 #pragma unroll
     for (int p = 0; p < KPT; ++p)
@@ -376,28 +394,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int df = 0; df < NDF; ++df) va[kb][df] = *(const u32x4*)&Vt[buf][(16 * df + c16) * LDV + 32 * kb + 8 * g4];
     __builtin_amdgcn_sched_barrier(0);
+    // this lane's largest raw score (the scale sl is positive, so it keeps the order)
     float tmax = -INFINITY;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = sc[f][r] * sl;
-        if constexpr (MASKED) v = (kt0 + 16 * f + 4 * g4 + r < klim) ? v : -INFINITY;
-        sc[f][r] = v;
-        tmax = fmaxf(tmax, v);
+        if constexpr (MASKED) sc[f][r] = (kt0 + 16 * f + 4 * g4 + r < klim) ? sc[f][r] : -INFINITY;
+        tmax = fmaxf(tmax, sc[f][r]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // The exponent base m_run is raised only when some score of the wave
-    // exceeds it by more than 2^8 (or it is still -inf), so O and l are
-    // rescaled rarely; p stays below 2^8 and the result O / l is unchanged.
+    tmax *= sl;
+    // The exponent base m_run (per query, equal in its four lanes) is raised
+    // only when some score of the query exceeds it by more than 2^8 (or it is
+    // still -inf), so O and l are rescaled rarely; p stays below 2^8 and the
+    // result O / l is unchanged.  The query's maximum over its four lanes is
+    // formed only when some lane of the wave sees such a score.
     // v_exp_f32 directly: p below 2^-126 flushes to 0, far below what the sum
     // can resolve.
     // (A lane whose scores are all masked so far keeps m_run = -inf; its
     // exponent base is then 0 and every p of it is exp2(-inf) = 0.)
-    const bool raise = tmax > m_run + 8.f;
-    if (__any(raise)) {  // uniform over the wave
-      const float m_new = raise ? tmax : m_run;
+    if (__any(tmax > m_run + 8.f)) {  // uniform over the wave
+      float tq = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tq = fmaxf(tq, __shfl_xor(tq, 32, 64));
+      const float m_new = tq > m_run + 8.f ? tq : m_run;
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -406,18 +425,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     float m_base = m_run;
     if constexpr (MASKED) m_base = (m_run == -INFINITY) ? 0.f : m_run;
-    float psum = 0.f;
+    // p = 2^(s sl - m) in one fused step; l_run holds this lane's keys only
+    // (the four lanes of a query are summed once, at the end)
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[f][r] - m_base);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[f][r], sl, -m_base));
         sc[f][r] = p;
-        psum += p;
+        l_run += p;
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
     // 32-key blocks: k-slot t of lane group g4 <-> key 32kb + 4g4 + t (t < 4),
     // 32kb + 16 + 4g4 + t - 4.  P = P_hi + P_lo, both bf16, so P V keeps about
     // 16 significant bits of P (one bf16 P perturbs every output by up to 2^-9).
@@ -469,6 +486,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       if (t0 + u < ntiles) tile(t0 + u, u, t0 + u + 1 < ntiles, Masked{});
   }
 
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
   const bool qvalid = qi < a.n;
   if (a.splits == 1) {
     if (qvalid) {
@@ -579,7 +598,10 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
   const int n_qt = (a.n + 63) / 64;
   const int items = a.B * a.H * a.splits * n_qt;
   const int per_xcd = (items + 7) / 8;
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, 1>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
+  if (a.len1 == 0 || a.len0 % 64 == 0)  // no key tile spans both segments
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, true>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, false>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
   int e = int(hipGetLastError());
   if (e || a.splits == 1) return e;
   const long long n4 = (long long)a.B * a.H * a.n * (DH / 4);
