@@ -268,25 +268,53 @@ __global__ __launch_bounds__(NT) void gemm_nt(GemmArgs g) {
   }
 }
 
-// one wave per row: lanes fold tiles lane, lane+64, ...; then a fixed xor tree.
+// one workgroup per row: thread l folds tiles l, l + 256, ... (four loads in
+// flight per step), then a fixed xor tree inside each wave and the four wave
+// results in wave order.
 __global__ __launch_bounds__(256) void lm_merge_kernel(const float* part, int T, int n_tiles,
                                                        float* H, int* am, float* gap) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= T) return;
+  __shared__ float wp[4][5];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   LmPart acc = lm_empty_part();
   const float* base = part + (long long)row * n_tiles * 5;
-  for (int t = lane; t < n_tiles; t += 64) {
-    LmPart p;
-    p.m = base[t * 5 + 0];
-    p.s = base[t * 5 + 1];
-    p.t = base[t * 5 + 2];
-    p.sec = base[t * 5 + 3];
-    p.idx = __float_as_int(base[t * 5 + 4]);
-    acc = lm_combine(acc, p);
+  for (int t0 = tid; t0 < n_tiles; t0 += 1024) {
+    LmPart p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 256 * u;
+      p[u] = lm_empty_part();
+      if (t < n_tiles) {
+        p[u].m = base[t * 5 + 0];
+        p[u].s = base[t * 5 + 1];
+        p[u].t = base[t * 5 + 2];
+        p[u].sec = base[t * 5 + 3];
+        p[u].idx = __float_as_int(base[t * 5 + 4]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = lm_combine(acc, p[u]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc = lm_combine(acc, lm_shfl_xor(acc, o));
   if (lane == 0) {
+    wp[wave][0] = acc.m;
+    wp[wave][1] = acc.s;
+    wp[wave][2] = acc.t;
+    wp[wave][3] = acc.sec;
+    wp[wave][4] = __int_as_float(acc.idx);
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      LmPart p;
+      p.m = wp[w][0];
+      p.s = wp[w][1];
+      p.t = wp[w][2];
+      p.sec = wp[w][3];
+      p.idx = __float_as_int(wp[w][4]);
+      acc = lm_combine(acc, p);
+    }
     if (H) H[row] = logf(acc.s) - acc.t / acc.s;
     if (am) am[row] = acc.idx;
     if (gap) gap[row] = acc.m - acc.sec;
@@ -336,8 +364,7 @@ int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipSt
 int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap,
              hipStream_t st) {
   if (T <= 0) return 0;
-  hipLaunchKernelGGL(lm_merge_kernel, dim3((T + 3) / 4), dim3(256), 0, st, part, T, n_tiles, entropy,
-                     argmax, gap);
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(T), dim3(256), 0, st, part, T, n_tiles, entropy, argmax, gap);
   return int(hipGetLastError());
 }
 

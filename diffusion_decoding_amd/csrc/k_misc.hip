@@ -268,54 +268,67 @@ __global__ void canvas_init_kernel(int* tok, uint8_t* committed, int N, uint64_t
   committed[b * N + i] = 0;
 }
 
-// (entropy, index) order with NaN entropies after every number
-__device__ __forceinline__ bool rank_before(float hj, int j, float hi, int i) {
-  const bool nj = hj != hj, ni = hi != hi;
-  if (nj || ni) return ni && (!nj || j < i);
-  return hj < hi || (hj == hi && j < i);
+// (entropy, index) order as one unsigned key: the entropy's bits mapped so
+// that unsigned order is numeric order (-0 taken as +0, every NaN after every
+// number), the index in the low word.  Committed positions get the largest
+// key, so they never rank before an uncommitted one.
+__device__ __forceinline__ unsigned long long commit_key(float h, int i) {
+  const uint32_t b = __float_as_uint(h + 0.0f);
+  const uint32_t u = (h != h) ? 0xffffffffu : ((b >> 31) ? ~b : (b | 0x80000000u));
+  return ((unsigned long long)u << 32) | uint32_t(i);
 }
 
-// one workgroup of 1024 threads per canvas; N <= 1024
+// One workgroup of 1024 threads per canvas; N <= 1024.  Positions are padded
+// to whole waves (NR) and each gets 1024 / NR threads, which split the count
+// of the keys ranked before it.
 __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int* am, int* tok,
                                                       uint8_t* committed, int N, int step,
                                                       int max_steps, float threshold, uint64_t seed,
                                                       uint32_t block, int vocab, int* n_unc) {
-  __shared__ float hs[1024];
-  __shared__ int unc_s[1024];
+  __shared__ unsigned long long ks[1024];
+  __shared__ int part_s[1024];
   __shared__ int red[16];
-  const int b = blockIdx.x, i = threadIdx.x;
-  const bool in = i < N;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int NR = (N + 63) & ~63, parts = 1024 / NR;
+  const int i = t % NR, q = t / NR;
   const int base = b * N;
-  const bool unc = in && committed[base + i] == 0;
-  const float hi = in ? H[base + i] : 0.f;
-  hs[i] = hi;
-  unc_s[i] = unc;
+  const bool own = q == 0 && i < N;  // the thread that owns position i
+  const bool unc = own && committed[base + i] == 0;
+  const float hi = own ? H[base + i] : 0.f;
+  if (q == 0) ks[i] = unc ? commit_key(hi, i) : ~0ull;
   // U = number of uncommitted positions
   int cnt = wave_sum_i(unc ? 1 : 0);
-  if ((i & 63) == 0) red[i >> 6] = cnt;
+  if ((t & 63) == 0) red[t >> 6] = cnt;
   __syncthreads();
   int U = 0;
   for (int w = 0; w < 16; ++w) U += red[w];
   const int m = U ? (U + (max_steps - step) - 1) / (max_steps - step) : 0;
+  int before = 0;
+  if (q < parts && i < N) {
+    const unsigned long long mine = ks[i];
+    const int len = (N + parts - 1) / parts, j0 = q * len, j1 = min(N, j0 + len);
+    for (int j = j0; j < j1; ++j) before += ks[j] < mine ? 1 : 0;
+  }
+  part_s[t] = before;
+  __syncthreads();
   bool take = false;
   if (unc) {
-    int before = 0;
-    for (int j = 0; j < N; ++j) before += (unc_s[j] && rank_before(hs[j], j, hi, i)) ? 1 : 0;
-    take = before < m || hi < threshold;
+    int tot = 0;
+    for (int p = 0; p < parts; ++p) tot += part_s[p * NR + i];
+    take = tot < m || hi < threshold;
   }
   if (take) {
     tok[base + i] = am[base + i];
     committed[base + i] = 1;
   }
   const bool still = unc && !take;
-  __syncthreads();
   int c2 = wave_sum_i(still ? 1 : 0);
-  if ((i & 63) == 0) red[i >> 6] = c2;
+  if ((t & 63) == 0) red[t >> 6] = c2;
   __syncthreads();
   if (still)
     tok[base + i] =
         int(canvas_draw(seed, uint32_t(i), uint32_t(step + 1), uint32_t(b), block, uint32_t(vocab)));
-  if (i == 0) {
+  if (t == 0) {
     int Up = 0;
     for (int w = 0; w < 16; ++w) Up += red[w];
     n_unc[b] = Up;

@@ -45,10 +45,11 @@ def _free():
 def mid_config(expert_dtype):
     """2 layers, d 256, 2 heads x 128, 16 experts top-4 (d_e 96: a ragged
     k-tail in the down projection), shared 128, V 4096, batch 2 x 80 positions
-    (a ragged 64-row tile), 600 prompt rows (two key splits, ragged)."""
+    (a ragged 64-row tile), 1000 prompt rows (two key splits, ragged; key
+    tiles span the cache and canvas rows)."""
     return tiny_config(name=f"mid_{expert_dtype}", n_layers=2, d_model=256, n_heads=2, head_dim=128,
                        n_experts=16, top_k=4, d_expert=96, d_shared=128, vocab=4096, canvas_len=80,
-                       max_steps=4, prompt_len=600, batch=2, act_dtype="bf16", expert_dtype=expert_dtype,
+                       max_steps=4, prompt_len=1000, batch=2, act_dtype="bf16", expert_dtype=expert_dtype,
                        seed=21, lm_scale=1.0)
 
 
@@ -88,7 +89,7 @@ def test_block_autoregressive_fp8(rt):
 
 
 def test_c2_shape_two_layers_one_step(rt):
-    """Full-width layers with the 2048-row prompt of the 30-layer workload (8 key splits)."""
+    """Full-width layers with the 2048-row prompt of the 30-layer workload (4 key splits)."""
     cfg = get_config("c2").replace(name="c2_shape_2_layers", n_layers=2)
     say("c2 shape, 2 layers, one step")
     p = Pair(rt, cfg)
