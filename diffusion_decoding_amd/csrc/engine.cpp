@@ -66,7 +66,7 @@ struct dg_model {
   int *topk_ids = nullptr, *off = nullptr, *pair_row = nullptr, *pos = nullptr;
   int lm_ntiles = 0;
   float *H = nullptr, *gap = nullptr;
-  int *am = nullptr, *n_unc = nullptr, *u_total = nullptr;
+  int *am = nullptr, *n_unc = nullptr;
   int* u_host = nullptr;  // pinned
   // side stream for the shared expert, which runs concurrently with the
   // router and the routed experts (same default priority as any stream)
@@ -440,7 +440,6 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       {(void**)&m->gap, Tc * 4},
       {(void**)&m->am, Tc * 4},
       {(void**)&m->n_unc, (size_t)max_batch * 4},
-      {(void**)&m->u_total, 4},
   };
   for (auto& r : reqs) {
     s = alloc(m, r.p, r.bytes);
@@ -450,7 +449,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       return s;
     }
   }
-  if (hipHostMalloc((void**)&m->u_host, sizeof(int), hipHostMallocDefault) != hipSuccess) {
+  if (hipHostMalloc((void**)&m->u_host, sizeof(int) * max_batch, hipHostMallocDefault) != hipSuccess) {
     (void)hipGetLastError();
     free_all(m);
     delete m;
@@ -514,10 +513,13 @@ int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* step
       return s;
     }
     ++taken;
-    HIP_OK(reduce_sum_i32(m->n_unc, c->batch, m->u_total, st));
-    HIP_OK(hipMemcpyAsync(m->u_host, m->u_total, sizeof(int), hipMemcpyDeviceToHost, st));
+    // the per-canvas uncommitted counts come back with the step's end (the
+    // host waits for it anyway) and are summed here
+    HIP_OK(hipMemcpyAsync(m->u_host, m->n_unc, sizeof(int) * c->batch, hipMemcpyDeviceToHost, st));
     HIP_OK(hipStreamSynchronize(st));
-    if (*m->u_host == 0) break;
+    int left = 0;
+    for (int b = 0; b < c->batch; ++b) left += m->u_host[b];
+    if (left == 0) break;
   }
   *steps_taken = taken;
   return DG_OK;

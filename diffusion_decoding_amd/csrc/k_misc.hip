@@ -342,13 +342,6 @@ __global__ void philox_kernel(uint64_t seed, uint32_t pos0, uint32_t tag, uint32
   out[i] = canvas_draw(seed, pos0 + uint32_t(i), tag, canvas, block, modulus);
 }
 
-__global__ void sum_i32_kernel(const int* v, int n, int* out) {
-  int s = 0;
-  for (int i = threadIdx.x; i < n; i += 64) s += v[i];
-  s = wave_sum_i(s);
-  if (threadIdx.x == 0) *out = s;
-}
-
 }  // namespace
 
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st) {
@@ -447,11 +440,6 @@ int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uin
   if (n <= 0) return 0;
   hipLaunchKernelGGL(philox_kernel, dim3((n + 255) / 256), dim3(256), 0, st, seed, pos0, tag, canvas,
                      block, modulus, n, out);
-  return int(hipGetLastError());
-}
-
-int reduce_sum_i32(const int* v, int n, int* out, hipStream_t st) {
-  hipLaunchKernelGGL(sum_i32_kernel, dim3(1), dim3(64), 0, st, v, n, out);
   return int(hipGetLastError());
 }
 

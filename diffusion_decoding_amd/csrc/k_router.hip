@@ -33,35 +33,39 @@ __device__ __forceinline__ float topk_value(unsigned long long key) {
   return __uint_as_float(b);
 }
 
-// One wave per token.  The E keys go to LDS; every lane ranks its own keys by
-// counting the larger ones (the key order is total, so ranks are distinct),
-// reading the keys as wave-wide broadcasts, and the keys ranked below k are
-// written to their slot.  No cross-lane shuffles.
+// One wave per token.  The E keys go to LDS; every lane ranks its own keys
+// (KPL of them: E <= 64 KPL) by counting the larger ones (the key order is
+// total, so ranks are distinct), reading the keys as wave-wide broadcasts,
+// and the keys ranked below k are written to their slot.  No cross-lane
+// shuffles.
+template <int KPL>
 __global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, int E, int k, int* ids,
                                                   float* w) {
-  __shared__ __attribute__((aligned(16))) unsigned long long ks[256];
+  __shared__ __attribute__((aligned(16))) unsigned long long ks[64 * KPL];
   __shared__ float sel[8];
   const int t = blockIdx.x, lane = threadIdx.x;
-  unsigned long long key[4];
+  unsigned long long key[KPL];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < KPL; ++u) {
     const int e = lane + 64 * u;
     key[u] = e < E ? topk_key(logits[(long long)t * E + e], e) : 0ull;
     ks[e] = key[u];  // past E: key 0, ranked below every real key
   }
   __syncthreads();
   const int E2 = (E + 1) & ~1;
-  int rank[4] = {0, 0, 0, 0};
+  int rank[KPL];
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) rank[u] = 0;
 #pragma unroll 8
   for (int e = 0; e < E2; e += 2) {
     const u32x4 kk = *(const u32x4*)&ks[e];
     const unsigned long long k0 = ((unsigned long long)kk[1] << 32) | kk[0];
     const unsigned long long k1 = ((unsigned long long)kk[3] << 32) | kk[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) rank[u] += int(k0 > key[u]) + int(k1 > key[u]);
+    for (int u = 0; u < KPL; ++u) rank[u] += int(k0 > key[u]) + int(k1 > key[u]);
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < KPL; ++u) {
     const int e = lane + 64 * u;
     if (e < E && rank[u] < k) sel[rank[u]] = topk_value(key[u]);
   }
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, in
   float sum = 0.f;
   for (int j = 0; j < k; ++j) sum += __expf(sel[j] - m);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < KPL; ++u) {
     const int e = lane + 64 * u;
     if (e < E && rank[u] < k) {
       ids[t * k + rank[u]] = e;
@@ -156,7 +160,12 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, i
 int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hipStream_t st) {
   if (T <= 0) return 0;
   if (E > 256 || k > 8 || k > E) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
+  else
+    hipLaunchKernelGGL(topk_kernel<4>, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
   return int(hipGetLastError());
 }
 

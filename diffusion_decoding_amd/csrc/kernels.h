@@ -125,7 +125,6 @@ int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, 
                    int vocab, int* n_unc, hipStream_t st);
 int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uint32_t block,
                 uint32_t modulus, int n, uint32_t* out, hipStream_t st);
-int reduce_sum_i32(const int* v, int n, int* out, hipStream_t st);
 
 // ---------------------------------------------------------------- router (k_router.hip)
 // logits [T][E] fp32 -> ids [T][k], w [T][k]
