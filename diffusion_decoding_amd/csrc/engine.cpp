@@ -68,10 +68,6 @@ struct dg_model {
   float *H = nullptr, *gap = nullptr;
   int *am = nullptr, *n_unc = nullptr;
   int* u_host = nullptr;  // pinned
-  // side stream for the shared expert, which runs concurrently with the
-  // router and the routed experts (same default priority as any stream)
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // kernel timing
   int prof_id = DG_PROF_NONE;
   std::vector<hipEvent_t> prof_ev;  // start/stop pairs
@@ -99,11 +95,6 @@ void free_all(dg_model* m) {
   m->allocs.clear();
   if (m->u_host) (void)hipHostFree(m->u_host);
   m->u_host = nullptr;
-  if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
-  if (m->ev_join) (void)hipEventDestroy(m->ev_join);
-  if (m->side) (void)hipStreamDestroy(m->side);
-  m->ev_fork = m->ev_join = nullptr;
-  m->side = nullptr;
 }
 
 constexpr int PROF_PAIRS = 1024;
@@ -226,24 +217,21 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     HIP_OK(gemm(at, dw, EPI_RESID, g, 1, st));
   }
   HIP_OK(rmsnorm(at, m->x, T, d, c.rms_eps, m->a, st));
-  // The shared expert depends only on the normed activations: it runs on the
-  // side stream while the router and the routed experts (bandwidth-bound) run
-  // here; the combine below waits for it.
-  HIP_OK(hipEventRecord(m->ev_fork, st));
-  HIP_OK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+  // The shared expert runs in line, before the router.  (On a second stream,
+  // beside the router and the routed experts, its workgroups held CUs that
+  // the routed gate/up workgroups (138 KB of LDS each) could not share, and
+  // the waits this caused on the main stream cost more than the overlap won.)
   {
-    const hipStream_t s2 = m->side;
-    ProfScope ps(m, DG_PROF_SHARED, s2);
+    ProfScope ps(m, DG_PROF_SHARED, st);
     GemmArgs g;  // shared gate/up + SwiGLU
     g.A = m->a; g.lda = d; g.B = w.ws_gu; g.ldb = d; g.b_scale = w.ss_gu;
     g.M = T; g.N = ds; g.K = d; g.C = m->hs; g.ldc = ds; g.swiglu_half = ds;
-    HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, 1, s2));
+    HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, 1, st));
     GemmArgs g2;  // shared down
     g2.A = m->hs; g2.lda = ds; g2.B = w.ws_d; g2.ldb = ds; g2.b_scale = w.ss_d;
     g2.M = T; g2.N = d; g2.K = ds; g2.C = m->ys; g2.ldc = d;
-    HIP_OK(gemm(at, m->wt, EPI_F32, g2, 1, s2));
+    HIP_OK(gemm(at, m->wt, EPI_F32, g2, 1, st));
   }
-  HIP_OK(hipEventRecord(m->ev_join, m->side));
   {
     ProfScope ps(m, DG_PROF_ROUTER, st);
     {
@@ -284,7 +272,6 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
       HIP_OK(gemm(at, m->wt, EPI_F32, g, E, st));
     }
   }
-  HIP_OK(hipStreamWaitEvent(st, m->ev_join, 0));
   HIP_OK(moe_combine_norm(at, m->x, m->y, m->ys, m->topk_w, m->pos, T, k, d, c.rms_eps, m->a, st));
   return DG_OK;
 }
@@ -454,14 +441,6 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
     free_all(m);
     delete m;
     return fail(DG_ERR_OOM, "hipHostMalloc failed");
-  }
-  if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess) {
-    (void)hipGetLastError();
-    free_all(m);
-    delete m;
-    return fail(DG_ERR_HIP, "side stream or event creation failed");
   }
   *out = m;
   return DG_OK;
