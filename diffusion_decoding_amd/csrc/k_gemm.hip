@@ -346,7 +346,7 @@ int launch_epi(GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st) {
 }  // namespace
 
 int lm_tiles(ActType at, int K, int vocab) {
-  return tgemm_supported(at, K) ? lm_tiles_tiled(vocab) : (vocab + 63) / 64;
+  return tgemm_supported(at, K) ? lm_tiles_tiled(vocab, K) : (vocab + 63) / 64;
 }
 
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st) {

@@ -9,6 +9,10 @@
 // stages rather than by occupancy; stages pass through a double-buffered LDS
 // tile from which the 4 waves read their MFMA fragments.
 //
+// The LM head at K = 2048 runs on a second kernel (dgemm_kernel, below) that
+// moves A and B into LDS with direct global-to-LDS loads instead of a
+// register stage, with separate, deeper rings for the weight stream.
+//
 // Tile order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets a
 // contiguous run of tiles in which the M tiles of one weight tile are
 // neighbours, so the weight tile is fetched from HBM once into that XCD's L2.
@@ -30,9 +34,17 @@ namespace {
 
 constexpr int TNT = 256;     // threads per workgroup
 constexpr int SK_MIN = 64;   // K must be a multiple of this
-// LM-head tile: 128 x 128, four waves of 32 rows x 128 columns (one partial per row and tile;
-// four waves of 64 x 64 measured 10% slower)
+// LM-head tile of the register-staged kernel (K != 2048): 128 x 128, four
+// waves of 32 rows x 128 columns (one partial per row and tile; four waves
+// of 64 x 64 measured 10% slower)
 constexpr int LM_BM = 128, LM_BN = 128, LM_WM = 4;
+// LM head with K = 2048 (d_model of the full-size workloads): the direct-load
+// kernel, 256 x 256 tiles of eight waves (4 x 2, 64 x 128 each, one partial
+// per row and 128 columns), A ring 2 and B ring 3 deep (160 KB of LDS).
+// Measured at 256 x 262144 x 2048: 344 us against 440 us for the 128 x 128
+// register-staged tiles; at M = 1024, 1069 against 1432 us.
+constexpr int LMD_BM = 256, LMD_BN = 256, LMD_WM = 4, LMD_NW = 8, LMD_SA = 2, LMD_SB = 3, LMD_KT = 32;
+bool lm_direct(int K) { return K == 64 * LMD_KT; }
 
 struct f8 {
   uint8_t v;
@@ -51,6 +63,61 @@ template <> struct BChunk<f8> {
   static __device__ __forceinline__ u32x4 widen(type v) { return e4m3x8_to_bf16x8(v); }
   static __device__ __forceinline__ type zero() { return u32x2{0u, 0u}; }
 };
+
+// LM-head epilogue of one wave: acc[i][j] holds rows row0 + 16 i + 4 g4 + r
+// and columns col0 + 16 j + c16 of the logits; each row's columns of this
+// wave are reduced to one online-softmax partial (max, sum e^(z-max),
+// sum e^(z-max)(z-max), second max, argmax), stored at partial index pidx
+// of the row's pn partials.
+template <int FM, int FN>
+__device__ __forceinline__ void lm_partials(const f32x4 (&acc)[FM][FN], const GemmArgs& g, int row0, int col0,
+                                            int pn, int pidx) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      LmPart p = lm_empty_part();
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = col0 + 16 * j + c16;
+        if (n < g.N) {
+          const float z = acc[i][j][r];
+          if (z > p.m) {
+            p.sec = p.m;
+            p.m = z;
+            p.idx = n;
+          } else if (z > p.sec) {
+            p.sec = z;
+          }
+        }
+      }
+      if (p.idx != INT_MAX) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = col0 + 16 * j + c16;
+          if (n < g.N) {
+            const float dz = acc[i][j][r] - p.m;
+            const float e = __expf(dz);
+            p.s += e;
+            p.t += e * dz;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) p = lm_combine(p, lm_shfl_xor(p, o));
+      const int m = row0 + 16 * i + 4 * g4 + r;
+      if (c16 == 0 && m < g.M) {
+        float* o = g.part + ((long long)m * pn + pidx) * 5;
+        o[0] = p.m;
+        o[1] = p.s;
+        o[2] = p.t;
+        o[3] = p.sec;
+        o[4] = __int_as_float(p.idx);
+      }
+    }
+  }
+}
 
 // BM x BN tile, 4 waves as WAVES_M x (4 / WAVES_M), D stages in flight.
 // SWIGLU: the B tile holds gate and up rows interleaved in blocks of 16 (gate
@@ -227,54 +294,8 @@ __global__ __launch_bounds__(TNT * KG) void tgemm_kernel(GemmArgs g, int tiles_m
   // ---------------------------------------------------------------- epilogues
   const float* Sg = g.b_scale;
   if constexpr (EPI == EPI_LM) {
-    // rows wr + 16i + 4g4 + r; this lane holds columns 16j + c16 of each.
-    // One partial per (row, wave column block): WAVES_N per tile.
-    float* part = g.part;
-    const int pn = tiles_n * WAVES_N, pidx = tn * WAVES_N + (wave % WAVES_N);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        LmPart p = lm_empty_part();
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = tn * BN + wc + 16 * j + c16;
-          if (n < g.N) {
-            const float z = acc[i][j][r];
-            if (z > p.m) {
-              p.sec = p.m;
-              p.m = z;
-              p.idx = n;
-            } else if (z > p.sec) {
-              p.sec = z;
-            }
-          }
-        }
-        if (p.idx != INT_MAX) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int n = tn * BN + wc + 16 * j + c16;
-            if (n < g.N) {
-              const float dz = acc[i][j][r] - p.m;
-              const float e = __expf(dz);
-              p.s += e;
-              p.t += e * dz;
-            }
-          }
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) p = lm_combine(p, lm_shfl_xor(p, o));
-        const int m = m0 + wr + 16 * i + 4 * g4 + r;
-        if (c16 == 0 && m < g.M) {
-          float* o = part + ((long long)m * pn + pidx) * 5;
-          o[0] = p.m;
-          o[1] = p.s;
-          o[2] = p.t;
-          o[3] = p.sec;
-          o[4] = __int_as_float(p.idx);
-        }
-      }
-    }
+    // one partial per (row, wave column block): WAVES_N per tile
+    lm_partials<FM, FN>(acc, g, m0 + wr, tn * BN + wc, tiles_n * WAVES_N, tn * WAVES_N + (wave % WAVES_N));
   } else if constexpr (EPI == EPI_QKV) {
     // tile tn is one head of q, k or v (BN = head_dim = 128) and each wave
     // holds whole tile rows, so lane column d = 16 jf + c16 (jf < 4) and its
@@ -365,6 +386,236 @@ int launch_t(const GemmArgs& g, hipStream_t st) {
   return int(hipGetLastError());
 }
 
+// ---------------------------------------------------------------- direct-load GEMM
+// bf16 A [M][K] and B [N][K] through LDS without a register stage: each
+// global_load_lds_dwordx4 of a wave moves 8 rows x 128 bytes (64 k) of A or
+// B -- eight whole cache lines -- into one 1 KB LDS block, lane L's 16 bytes
+// landing at byte 16 L of the block.  Lane L loads row L / 8 and 16-byte
+// chunk (L % 8) ^ (L / 8) of it, so chunk c of row r sits in slot 8 r + (c ^ r):
+// the eight rows of a fragment read hit eight different bank groups.
+// A and B stages (64 k each) have rings of their own, SA and SB buffers deep:
+// the loads of stage kt + SA - 1 (A) and kt + SB - 1 (B) are issued right
+// after the barrier that opens stage kt, so the weight stream (B, from HBM)
+// can run further ahead than the activations (A, L2-resident) in the same
+// LDS, and no registers hold data in transit.  The wait before that barrier
+// counts this thread's loads still allowed in flight (s_waitcnt vmcnt; loads
+// complete in issue order); the barrier makes every thread's loads of stage
+// kt visible and frees the buffers of stage kt - 1.
+namespace dl {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+// wait until at most N of this thread's vector-memory operations (and no LDS
+// operation) are outstanding, then the workgroup barrier.  The wait is the
+// s_waitcnt builtin, which the compiler's own wait tracking takes into
+// account (so it adds no full wait before reading a stage it knows has
+// landed); the empty asm statements keep memory accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Issue order of the loads: the prologue issues A stages 0 .. SA - 2 and B
+// stages 0 .. SB - 2 (step s: A(s), then B(s)); iteration j issues
+// A(j + SA - 1), then B(j + SB - 1) (stages past KT - 1 are skipped).  The
+// number of loads issued after both A(kt) and B(kt) and before iteration kt:
+// what may still be in flight when stage kt is consumed.
+template <int SA, int SB, int KT, int LA, int LB>
+constexpr int loads_after(int kt) {
+  int pos = 0, last = -1;
+  int seqs[2 * (SA > SB ? SA : SB) + 2 * KT][2] = {};  // (kind, stage)
+  int n = 0;
+  for (int st = 0; st < (SA > SB ? SA : SB) - 1; ++st) {
+    if (st <= SA - 2 && st < KT) { seqs[n][0] = 0; seqs[n][1] = st; ++n; }
+    if (st <= SB - 2 && st < KT) { seqs[n][0] = 1; seqs[n][1] = st; ++n; }
+  }
+  for (int j = 0; j < kt; ++j) {
+    if (j + SA - 1 < KT) { seqs[n][0] = 0; seqs[n][1] = j + SA - 1; ++n; }
+    if (j + SB - 1 < KT) { seqs[n][0] = 1; seqs[n][1] = j + SB - 1; ++n; }
+  }
+  for (int i = 0; i < n; ++i)
+    if (seqs[i][1] == kt) last = i;
+  int cnt = 0;
+  for (int i = last + 1; i < n; ++i) cnt += seqs[i][0] == 0 ? LA : LB;
+  (void)pos;
+  return cnt;
+}
+
+}  // namespace dl
+
+// NWV waves as WAVES_M x (NWV / WAVES_M); each wave owns a (BM / WAVES_M) x
+// (BN / WAVES_N) block of the tile.  An A stage buffer holds BM / 8 blocks, a
+// B stage buffer BN / 8, block q holding rows 8 q .. 8 q + 7 of the tile.
+template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT>
+__global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+  constexpr int WAVES_N = NWV / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int LA = BM / 8 / NWV, LB = BN / 8 / NWV;  // loads per wave per stage
+  static_assert(LA * 8 * NWV == BM && LB * 8 * NWV == BN && FM >= 1 && FN >= 1, "tile shape");
+  static_assert(SA >= 2 && SA <= 4 && SB >= 2 && SB <= 4, "stages");
+  static_assert(EPI == EPI_LM || EPI == EPI_F32, "epilogue");
+
+  // one array per stage buffer, so each LDS access names its buffer statically
+  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 A1[BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 A2[SA > 2 ? BM * 64 : 1];
+  __shared__ __attribute__((aligned(1024))) bf16 A3[SA > 3 ? BM * 64 : 1];
+  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 B1[BN * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 B2[SB > 2 ? BN * 64 : 1];
+  __shared__ __attribute__((aligned(1024))) bf16 B3[SB > 3 ? BN * 64 : 1];
+  auto abuf = [&](auto bc) -> bf16* {
+    constexpr int b = decltype(bc)::value % SA;
+    if constexpr (b == 0) return A0;
+    else if constexpr (b == 1) return A1;
+    else if constexpr (b == 2) return A2;
+    else return A3;
+  };
+  auto bbuf = [&](auto bc) -> bf16* {
+    constexpr int b = decltype(bc)::value % SB;
+    if constexpr (b == 0) return B0;
+    else if constexpr (b == 1) return B1;
+    else if constexpr (b == 2) return B2;
+    else return B3;
+  };
+
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int tile = xcd * per_xcd + slot;
+  if (slot >= per_xcd || tile >= tiles_m * tiles_n) return;  // uniform over the workgroup
+  const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
+  // the wave index is uniform: keep it (and the LDS block offsets) scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int wr = (wave / WAVES_N) * WM, wc = (wave % WAVES_N) * WN;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // this lane's sources of its loads of a stage (A block wave + NWV i, B
+  // block wave + NWV i): row lane / 8 of the block, chunk (lane % 8) ^ (lane / 8);
+  // rows past M or N read row 0 and only feed outputs that are never stored
+  const int rr8 = lane >> 3, ch = (lane & 7) ^ rr8;
+  const bf16* asrc[LA];
+  const bf16* bsrc[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int r = m0 + 8 * (wave + NWV * i) + rr8;
+    asrc[i] = (const bf16*)g.A + (long long)(r < g.M ? r : 0) * g.lda + 8 * ch;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = n0 + 8 * (wave + NWV * i) + rr8;
+    bsrc[i] = (const bf16*)g.B + (long long)(r < g.N ? r : 0) * g.ldb + 8 * ch;
+  }
+  auto issue_a = [&](int kt, bf16* b) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * 64), (dl::lds_ptr)(b + (wave + NWV * i) * 512),
+                                       16, 0, 0);
+  };
+  auto issue_b = [&](int kt, bf16* b) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + kt * 64), (dl::lds_ptr)(b + (wave + NWV * i) * 512),
+                                       16, 0, 0);
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment of 16 rows starting at buffer row r0 (a multiple of 16), k-half
+  // ks: lane row r0 + c16 is row c16 % 8 of block (r0 + c16) / 8, chunk 4 ks + g4
+  const int rr = lane & 7;
+  auto frag_off = [&](int r0, int ks) { return ((r0 >> 3) + (c16 >> 3)) * 512 + (rr * 8 + ((4 * ks + g4) ^ rr)) * 8; };
+  // the fragments of both k-halves of a stage (or, for wide wave tiles, of
+  // one k-half) are read before their first MFMA: the LDS latency is paid
+  // once per group, and the other waves' MFMAs cover it
+  constexpr int KH = (FM + FN) <= 8 ? 2 : 1;  // k-halves per fragment group
+  auto compute = [&](const bf16* ab, const bf16* bb) {
+#pragma unroll
+    for (int k0 = 0; k0 < 2; k0 += KH) {
+      u32x4 af[KH][FM], bfr[KH][FN];
+#pragma unroll
+      for (int h = 0; h < KH; ++h) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[h][i] = *(const u32x4*)(ab + frag_off(wr + 16 * i, k0 + h));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[h][j] = *(const u32x4*)(bb + frag_off(wc + 16 * j, k0 + h));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < KH; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[h][i], bfr[h][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // K = 64 KT is a compile-time constant and the stage loop is unrolled
+  // completely: every buffer is named statically and the loop has no header
+  // at which the compiler's wait tracking of the LDS loads in flight would
+  // merge into a full wait
+  constexpr int SMAX = SA > SB ? SA : SB;
+  dl::static_for<SMAX - 1>([&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+    if constexpr (st <= SA - 2 && st < KT) issue_a(st, abuf(sc));
+    if constexpr (st <= SB - 2 && st < KT) issue_b(st, bbuf(sc));
+  });
+  dl::static_for<KT>([&](auto kc) {
+    constexpr int kt = decltype(kc)::value;
+    dl::wait_barrier<dl::loads_after<SA, SB, KT, LA, LB>(kt)>();
+    if constexpr (kt + SA - 1 < KT) issue_a(kt + SA - 1, abuf(std::integral_constant<int, kt + SA - 1>{}));
+    if constexpr (kt + SB - 1 < KT) issue_b(kt + SB - 1, bbuf(std::integral_constant<int, kt + SB - 1>{}));
+    compute(abuf(kc), bbuf(kc));
+  });
+
+  if constexpr (EPI == EPI_LM) {
+    lm_partials<FM, FN>(acc, g, m0 + wr, n0 + wc, tiles_n * WAVES_N, tn * WAVES_N + (wave % WAVES_N));
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wc + 16 * j + c16;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wr + 16 * i + 4 * g4 + r;
+          if (m < g.M) ((float*)g.C)[(long long)m * g.ldc + n] = acc[i][j][r];
+        }
+    }
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT = 32>
+int launch_dl(const GemmArgs& g, hipStream_t st) {
+  if (g.K != 64 * KT || g.lda % 8 || g.ldb % 8) return int(hipErrorInvalidValue);
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+  if (total == 0) return 0;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((dgemm_kernel<BM, BN, WAVES_M, NWV, SA, SB, EPI, KT>), dim3(8 * per_xcd), dim3(64 * NWV), 0, st,
+                     g, tiles_m, tiles_n, per_xcd);
+  return int(hipGetLastError());
+}
+
 // Tile shape per epilogue and size (measured at M = 256, K = 2048): the
 // dense projections run on 64x64 or 64x32 tiles with two k-groups of 4 waves
 // (enough workgroups to cover 256 CUs while weight tiles are shared through
@@ -382,6 +633,8 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   const long long tiles64 = (long long)((g.M + 63) / 64) * ((g.N + 63) / 64);
   switch (epi) {
     case EPI_LM:
+      if constexpr (std::is_same<TB, bf16>::value)
+        if (lm_direct(g.K)) return launch_dl<LMD_BM, LMD_BN, LMD_WM, LMD_NW, LMD_SA, LMD_SB, EPI_LM, LMD_KT>(g, st);
       return launch_t<TB, LM_BM, LM_BN, LM_WM, 2, EPI_LM>(g, st);
     case EPI_SWIGLU:
       return launch_kg<TB, 64, 64, 2, 2, EPI_SWIGLU>(g, st, 2);
@@ -405,7 +658,10 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
 
 }  // namespace
 
-int lm_tiles_tiled(int vocab) { return (vocab + LM_BN - 1) / LM_BN * (4 / LM_WM); }
+int lm_tiles_tiled(int vocab, int K) {
+  if (lm_direct(K)) return (vocab + LMD_BN - 1) / LMD_BN * (LMD_NW / LMD_WM);
+  return (vocab + LM_BN - 1) / LM_BN * (4 / LM_WM);
+}
 
 bool tgemm_supported(ActType at, int K) { return at == ACT_BF16 && K % SK_MIN == 0; }
 

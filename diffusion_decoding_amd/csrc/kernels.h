@@ -55,7 +55,7 @@ int lm_tiles(ActType at, int K, int vocab);
 // Tiled bf16 kernel (k_tgemm.hip): used by gemm() for ungrouped bf16 GEMMs with K % 64 == 0.
 bool tgemm_supported(ActType at, int K);
 int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st);
-int lm_tiles_tiled(int vocab);
+int lm_tiles_tiled(int vocab, int K);
 // Merge LM partials of T rows into entropy / argmax / top-2 gap.
 int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap,
              hipStream_t st);

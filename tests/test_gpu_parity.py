@@ -209,15 +209,19 @@ def test_commit_pass_matches_oracle(rt, act):
 
 # ----------------------------------------------------------------------------- LM head alone
 
-def test_lm_head_c1_shape(rt):
+# (rows, vocab): the full c1 shape, and ragged rows with a vocabulary that
+# leaves the last 256-column tile a 64-column remainder (its second
+# 128-column partial is empty)
+@pytest.mark.parametrize("rows,vocab", [(256, 262144), (200, 261952)])
+def test_lm_head_c1_shape(rt, rows, vocab):
     cfg = get_config("c1")
-    say("LM head + confidence at 256 x 2048 x 262144")
+    say(f"LM head + confidence at {rows} x {cfg.d_model} x {vocab}")
     g = torch.Generator("cuda").manual_seed(11)
-    lm = (torch.randn(cfg.vocab, cfg.d_model, device="cuda", generator=g) * cfg.d_model ** -0.5).to(
+    lm = (torch.randn(vocab, cfg.d_model, device="cuda", generator=g) * cfg.d_model ** -0.5).to(
         torch.bfloat16)
-    hf = torch.randn(256, cfg.d_model, device="cuda", generator=g).to(torch.bfloat16)
+    hf = torch.randn(rows, cfg.d_model, device="cuda", generator=g).to(torch.bfloat16)
     # a model with 1 tiny layer is enough to own the LM-head workspace
-    small = tiny_config(act_dtype="bf16", expert_dtype="bf16", vocab=cfg.vocab, d_model=cfg.d_model,
+    small = tiny_config(act_dtype="bf16", expert_dtype="bf16", vocab=vocab, d_model=cfg.d_model,
                         canvas_len=256, head_dim=128, n_heads=16, d_expert=32, d_shared=32,
                         prompt_len=64)
     inp = make_inputs(small, device="cuda")
