@@ -119,6 +119,62 @@ __device__ __forceinline__ void lm_partials(const f32x4 (&acc)[FM][FN], const Ge
   }
 }
 
+// SwiGLU epilogue of one wave: fragment pair (2q, 2q+1) holds the gate and
+// up rows of outputs jbase + 16 q + c16 for rows row0 + 16 i + 4 g4 + r;
+// h = bf16(silu(gate) * up) (gate and up scaled by the fp8 row scales, if any).
+template <int FM, int FN>
+__device__ __forceinline__ void swiglu_store(const f32x4 (&acc)[FM][FN], const GemmArgs& g, int row0, int jbase) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+  const float* Sg = g.b_scale;
+#pragma unroll
+  for (int q = 0; q < FN / 2; ++q) {
+    const int j = jbase + 16 * q + c16;
+    if (j >= g.N) continue;
+    const float sg = Sg ? Sg[j] : 1.f, su = Sg ? Sg[g.swiglu_half + j] : 1.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = row0 + 16 * i + 4 * g4 + r;
+        if (m >= g.M) continue;
+        const float gt = acc[i][2 * q][r] * sg, up = acc[i][2 * q + 1][r] * su;
+        const float h = gt / (1.0f + __expf(-gt)) * up;
+        ((bf16*)g.C)[(long long)m * g.ldc + j] = f32_to_bf16(h);
+      }
+  }
+}
+
+// Plain epilogues of one wave (fp32 store, rounded store, rounded residual
+// add): fragment j holds columns nbase + 16 j + c16.
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void plain_store(const f32x4 (&acc)[FM][FN], const GemmArgs& g, int row0, int nbase) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+  const float* Sg = g.b_scale;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = nbase + 16 * j + c16;
+    if (n >= g.N) continue;
+    const float sc = Sg ? Sg[n] : 1.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = row0 + 16 * i + 4 * g4 + r;
+        if (m >= g.M) continue;
+        const float v = acc[i][j][r] * sc;
+        const long long o = (long long)m * g.ldc + n;
+        if constexpr (EPI == EPI_F32) {
+          ((float*)g.C)[o] = v;
+        } else if constexpr (EPI == EPI_ACT) {
+          ((bf16*)g.C)[o] = f32_to_bf16(v);
+        } else {
+          bf16* C = (bf16*)g.C;
+          C[o] = f32_to_bf16(to_f32(C[o]) + v);
+        }
+      }
+  }
+}
+
 // BM x BN tile, 4 waves as WAVES_M x (4 / WAVES_M), D stages in flight.
 // SWIGLU: the B tile holds gate and up rows interleaved in blocks of 16 (gate
 // rows j.., up rows half + j..), so a wave's fragment pair (2q, 2q+1) is the
@@ -292,7 +348,6 @@ __global__ __launch_bounds__(TNT * KG) void tgemm_kernel(GemmArgs g, int tiles_m
   }
 
   // ---------------------------------------------------------------- epilogues
-  const float* Sg = g.b_scale;
   if constexpr (EPI == EPI_LM) {
     // one partial per (row, wave column block): WAVES_N per tile
     lm_partials<FM, FN>(acc, g, m0 + wr, tn * BN + wc, tiles_n * WAVES_N, tn * WAVES_N + (wave % WAVES_N));
@@ -330,46 +385,9 @@ __global__ __launch_bounds__(TNT * KG) void tgemm_kernel(GemmArgs g, int tiles_m
         }
       }
   } else if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int q = 0; q < FN / 2; ++q) {
-      const int j = tn * (BN / 2) + (wc / 2) + 16 * q + c16;
-      if (j >= g.N) continue;
-      const float sg = Sg ? Sg[j] : 1.f, su = Sg ? Sg[g.swiglu_half + j] : 1.f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wr + 16 * i + 4 * g4 + r;
-          if (m >= g.M) continue;
-          const float gt = acc[i][2 * q][r] * sg, up = acc[i][2 * q + 1][r] * su;
-          const float h = gt / (1.0f + __expf(-gt)) * up;
-          ((bf16*)g.C)[(long long)m * g.ldc + j] = f32_to_bf16(h);
-        }
-    }
+    swiglu_store<FM, FN>(acc, g, m0 + wr, tn * (BN / 2) + (wc / 2));
   } else {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = tn * BN + wc + 16 * j + c16;
-      if (n >= g.N) continue;
-      const float sc = Sg ? Sg[n] : 1.f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wr + 16 * i + 4 * g4 + r;
-          if (m >= g.M) continue;
-          const float v = acc[i][j][r] * sc;
-          const long long o = (long long)m * g.ldc + n;
-          if constexpr (EPI == EPI_F32) {
-            ((float*)g.C)[o] = v;
-          } else if constexpr (EPI == EPI_ACT) {
-            ((bf16*)g.C)[o] = f32_to_bf16(v);
-          } else {
-            bf16* C = (bf16*)g.C;
-            C[o] = f32_to_bf16(to_f32(C[o]) + v);
-          }
-        }
-    }
+    plain_store<EPI, FM, FN>(acc, g, m0 + wr, tn * BN + wc);
   }
 }
 
@@ -456,6 +474,30 @@ constexpr int loads_after(int kt) {
 
 }  // namespace dl
 
+// Weight row (row of B) that feeds tile row r of tile column tn, and whether
+// it exists.  SWIGLU: blocks of 16 rows alternate gate rows j.. and up rows
+// swiglu_half + j.., so a wave's fragment pair (2q, 2q+1) is the gate/up pair
+// of 16 outputs.  QKV: within each 128-row head, tile rows are ordered so
+// that fragment 2P holds head dims 16 P .. 16 P + 15 and fragment 2P + 1 their
+// rotate-half partners 64 + 16 P ..; a 32-column wave block then holds whole
+// rotation pairs.
+template <int EPI, int BN>
+__device__ __forceinline__ long long dl_brow(const GemmArgs& g, int tn, int r, bool& ok) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int blk = r >> 4, j = tn * (BN / 2) + (blk >> 1) * 16 + (r & 15);
+    ok = j < g.N;
+    return (blk & 1) ? (long long)g.swiglu_half + j : j;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int n = tn * BN + r, f = (n & 127) >> 4;
+    ok = n < g.N;
+    return (n & ~127) + (f & 1) * 64 + (f >> 1) * 16 + (n & 15);
+  } else {
+    const int n = tn * BN + r;
+    ok = n < g.N;
+    return n;
+  }
+}
+
 // NWV waves as WAVES_M x (NWV / WAVES_M); each wave owns a (BM / WAVES_M) x
 // (BN / WAVES_N) block of the tile.  An A stage buffer holds BM / 8 blocks, a
 // B stage buffer BN / 8, block q holding rows 8 q .. 8 q + 7 of the tile.
@@ -466,31 +508,38 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int LA = BM / 8 / NWV, LB = BN / 8 / NWV;  // loads per wave per stage
   static_assert(LA * 8 * NWV == BM && LB * 8 * NWV == BN && FM >= 1 && FN >= 1, "tile shape");
-  static_assert(SA >= 2 && SA <= 4 && SB >= 2 && SB <= 4, "stages");
-  static_assert(EPI == EPI_LM || EPI == EPI_F32, "epilogue");
+  static_assert(SA >= 2 && SA <= 8 && SB >= 2 && SB <= 8, "stages");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SWIGLU needs gate/up fragment pairs");
+  static_assert(EPI != EPI_QKV || (FN % 2 == 0 && BN % 128 == 0), "QKV needs whole rotation pairs and heads");
 
   // one array per stage buffer, so each LDS access names its buffer statically
-  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 A1[BM * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 A2[SA > 2 ? BM * 64 : 1];
-  __shared__ __attribute__((aligned(1024))) bf16 A3[SA > 3 ? BM * 64 : 1];
-  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 B1[BN * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 B2[SB > 2 ? BN * 64 : 1];
-  __shared__ __attribute__((aligned(1024))) bf16 B3[SB > 3 ? BN * 64 : 1];
+#define DG_DL_BUF(X, R, ROWS, I) __shared__ __attribute__((aligned(1024))) bf16 X##I[R > I ? ROWS * 64 : 1];
+  DG_DL_BUF(A, SA, BM, 0) DG_DL_BUF(A, SA, BM, 1) DG_DL_BUF(A, SA, BM, 2) DG_DL_BUF(A, SA, BM, 3)
+  DG_DL_BUF(A, SA, BM, 4) DG_DL_BUF(A, SA, BM, 5) DG_DL_BUF(A, SA, BM, 6) DG_DL_BUF(A, SA, BM, 7)
+  DG_DL_BUF(B, SB, BN, 0) DG_DL_BUF(B, SB, BN, 1) DG_DL_BUF(B, SB, BN, 2) DG_DL_BUF(B, SB, BN, 3)
+  DG_DL_BUF(B, SB, BN, 4) DG_DL_BUF(B, SB, BN, 5) DG_DL_BUF(B, SB, BN, 6) DG_DL_BUF(B, SB, BN, 7)
+#undef DG_DL_BUF
   auto abuf = [&](auto bc) -> bf16* {
     constexpr int b = decltype(bc)::value % SA;
     if constexpr (b == 0) return A0;
     else if constexpr (b == 1) return A1;
     else if constexpr (b == 2) return A2;
-    else return A3;
+    else if constexpr (b == 3) return A3;
+    else if constexpr (b == 4) return A4;
+    else if constexpr (b == 5) return A5;
+    else if constexpr (b == 6) return A6;
+    else return A7;
   };
   auto bbuf = [&](auto bc) -> bf16* {
     constexpr int b = decltype(bc)::value % SB;
     if constexpr (b == 0) return B0;
     else if constexpr (b == 1) return B1;
     else if constexpr (b == 2) return B2;
-    else return B3;
+    else if constexpr (b == 3) return B3;
+    else if constexpr (b == 4) return B4;
+    else if constexpr (b == 5) return B5;
+    else if constexpr (b == 6) return B6;
+    else return B7;
   };
 
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -501,7 +550,7 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
   const int wr = (wave / WAVES_N) * WM, wc = (wave % WAVES_N) * WN;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM;
 
   // this lane's sources of its loads of a stage (A block wave + NWV i, B
   // block wave + NWV i): row lane / 8 of the block, chunk (lane % 8) ^ (lane / 8);
@@ -516,8 +565,9 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int r = n0 + 8 * (wave + NWV * i) + rr8;
-    bsrc[i] = (const bf16*)g.B + (long long)(r < g.N ? r : 0) * g.ldb + 8 * ch;
+    bool ok;
+    const long long r = dl_brow<EPI, BN>(g, tn, 8 * (wave + NWV * i) + rr8, ok);
+    bsrc[i] = (const bf16*)g.B + (ok ? r : 0) * g.ldb + 8 * ch;
   }
   auto issue_a = [&](int kt, bf16* b) {
 #pragma unroll
@@ -587,27 +637,52 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
   });
 
   if constexpr (EPI == EPI_LM) {
-    lm_partials<FM, FN>(acc, g, m0 + wr, n0 + wc, tiles_n * WAVES_N, tn * WAVES_N + (wave % WAVES_N));
-  } else {
+    lm_partials<FM, FN>(acc, g, m0 + wr, tn * BN + wc, tiles_n * WAVES_N, tn * WAVES_N + (wave % WAVES_N));
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    swiglu_store<FM, FN>(acc, g, m0 + wr, tn * (BN / 2) + (wc / 2));
+  } else if constexpr (EPI == EPI_QKV) {
+    // fragment pair (2q, 2q+1) of the wave: head dims d and d + 64 of one head
+    // of q, k or v (see dl_brow); round to bf16, rotate q and k in fp32 with
+    // the position's (cos, sin), round again, store into the per-head layouts
+    const int H = g.heads;
+    const float2* tab = (const float2*)g.rope_tab;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wc + 16 * j + c16;
+    for (int q = 0; q < FN / 2; ++q) {
+      const int n = tn * BN + wc + 32 * q;  // first (permuted) column of the pair
       if (n >= g.N) continue;
+      const int hg = n >> 7, which = hg / H, h = hg - which * H;
+      const int d = ((n & 127) >> 5) * 16 + c16;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + wr + 16 * i + 4 * g4 + r;
-          if (m < g.M) ((float*)g.C)[(long long)m * g.ldc + n] = acc[i][j][r];
+          if (m >= g.M) continue;
+          const int b = m / g.seq_n, ti = m - b * g.seq_n;
+          bf16* dst = which == 0 ? (bf16*)g.q_out + ((long long)(b * H + h) * g.seq_n + ti) * 128
+                                 : (bf16*)(which == 1 ? g.k_dst : g.v_dst) + (long long)(b * H + h) * g.dst_bh +
+                                       (long long)(g.row0 + ti) * 128;
+          if (which == 2) {
+            dst[d] = f32_to_bf16(acc[i][2 * q][r]);
+            dst[d + 64] = f32_to_bf16(acc[i][2 * q + 1][r]);
+          } else {
+            const float x1 = to_f32(f32_to_bf16(acc[i][2 * q][r])), x2 = to_f32(f32_to_bf16(acc[i][2 * q + 1][r]));
+            const float2 cs = tab[ti * 64 + d];
+            dst[d] = f32_to_bf16(x1 * cs.x - x2 * cs.y);
+            dst[d + 64] = f32_to_bf16(x2 * cs.x + x1 * cs.y);
+          }
         }
     }
+  } else {
+    plain_store<EPI, FM, FN>(acc, g, m0 + wr, tn * BN + wc);
   }
 }
 
 template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT = 32>
 int launch_dl(const GemmArgs& g, hipStream_t st) {
   if (g.K != 64 * KT || g.lda % 8 || g.ldb % 8) return int(hipErrorInvalidValue);
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int bn_out = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + bn_out - 1) / bn_out;
   const int total = tiles_m * tiles_n;
   if (total == 0) return 0;
   const int per_xcd = (total + 7) / 8;
@@ -628,9 +703,41 @@ int launch_kg(const GemmArgs& g, hipStream_t st, int kg_max) {
   return launch_t<TB, BM, BN, WM, D, EPI, 64, 1>(g, st);
 }
 
+// Dense projections with K = 2048 (d_model of the full-size workloads) on the
+// direct-load kernel, tile shapes and ring depths per epilogue and M from
+// measurements with cold weights: at M = 256 the QKV projection (N = 6144)
+// took 19.3 us against 26.6 us and the shared gate/up (4096 weight rows)
+// 14.5 against 17.7 us; at M = 1024 the QKV 38.7 against 67.7, the shared
+// gate/up 25.8 against 44.3 and the N = 2048 projections 19.0 against 24.2.
+// At M <= 384 the N = 2048 projections gain nothing and stay on the
+// register-staged kernel.  Returns -1 when the shape is not covered.
+int dense_direct(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
+  if (g.K != 2048 || g.lda % 8 || g.ldb % 8 || g.N < 1024) return -1;
+  const bool small = g.M <= 384;
+  switch (epi) {
+    case EPI_QKV:
+      return small ? launch_dl<64, 128, 2, 8, 3, 6, EPI_QKV>(g, st) : launch_dl<128, 256, 2, 8, 2, 3, EPI_QKV>(g, st);
+    case EPI_SWIGLU:
+      return small ? launch_dl<64, 64, 4, 8, 4, 8, EPI_SWIGLU>(g, st)
+                   : launch_dl<128, 128, 4, 8, 3, 4, EPI_SWIGLU>(g, st);
+    case EPI_RESID:
+      return small ? -1 : launch_dl<64, 128, 2, 8, 3, 6, EPI_RESID>(g, st);
+    case EPI_F32:
+      return small ? -1 : launch_dl<64, 128, 2, 8, 3, 6, EPI_F32>(g, st);
+    default:
+      return -1;
+  }
+}
+
 template <typename TB>
 int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   const long long tiles64 = (long long)((g.M + 63) / 64) * ((g.N + 63) / 64);
+  if (epi == EPI_QKV && (g.N % 128 || !g.seq_n || !g.heads || g.N != 3 * 128 * g.heads))
+    return int(hipErrorInvalidValue);
+  if constexpr (std::is_same<TB, bf16>::value) {
+    const int r = dense_direct(epi, g, st);
+    if (r >= 0) return r;
+  }
   switch (epi) {
     case EPI_LM:
       if constexpr (std::is_same<TB, bf16>::value)
@@ -639,7 +746,6 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
     case EPI_SWIGLU:
       return launch_kg<TB, 64, 64, 2, 2, EPI_SWIGLU>(g, st, 2);
     case EPI_QKV:
-      if (g.N % 128 || !g.seq_n || !g.heads || g.N != 3 * 128 * g.heads) return int(hipErrorInvalidValue);
       if (g.K % 128 == 0) return launch_t<TB, 64, 128, 4, 2, EPI_QKV, 64, 2>(g, st);
       return launch_t<TB, 64, 128, 4, 2, EPI_QKV, 64, 1>(g, st);
     case EPI_ACT:

@@ -88,6 +88,53 @@ def test_block_autoregressive_fp8(rt):
     p.close()
 
 
+def wide_ragged_config(batch, canvas, **kw):
+    """Full-width projections (d_model 2048, 16 x 128 heads, shared expert
+    2048, so every dense GEMM has K = 2048) at token counts that leave ragged
+    tiles: 200 rows (small-M tile shapes, 64-row tiles) and 400 rows (large-M
+    shapes, 128- and 256-row tiles); 16 experts top-4 keep the oracle quick."""
+    args = dict(name=f"wide_ragged_b{batch}", n_layers=1, d_model=2048, n_heads=16, head_dim=128,
+                n_experts=16, top_k=4, d_expert=96, d_shared=2048, vocab=8192, canvas_len=canvas,
+                max_steps=4, prompt_len=300, batch=batch, act_dtype="bf16", expert_dtype="bf16",
+                seed=23, lm_scale=1.0)
+    args.update(kw)
+    return tiny_config(**args)
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+def test_wide_ragged_step_locked(rt, batch):
+    cfg = wide_ragged_config(batch, 200)
+    say(f"full-width projections, {batch} x 200 tokens (ragged tiles)")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=2)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
+def test_wide_ragged_commit_pass(rt):
+    """Causal passes at full width: a 70-token prompt, then a 200-token canvas."""
+    cfg = wide_ragged_config(1, 200, prompt_mode="tokens", prompt_len=70, n_canvases=1)
+    say("full-width causal passes: prompt 70, canvas 200")
+    p = Pair(rt, cfg, kv_len=0)
+    p.commit(p.inp.prompt_tokens.cpu().numpy())
+    rel = p.kv_rel()
+    say(f"   prompt KV rel-L2 {rel}")
+    assert max(rel) <= 1e-2
+    p.resync_kv()
+    reps, ost = p.run_locked(max_steps=1)
+    _assert_reports(cfg, reps)
+    p.commit(ost.tokens)
+    rel = p.kv_rel()
+    say(f"   canvas appended: KV length {p.kv.length}, rel-L2 {rel}")
+    assert p.kv.length == p.okv.length == 270
+    assert max(rel) <= 1e-2
+    p.close()
+    del p
+    _free()
+
+
 def test_c2_shape_two_layers_one_step(rt):
     """Full-width layers with the 2048-row prompt of the 30-layer workload (4 key splits)."""
     cfg = get_config("c2").replace(name="c2_shape_2_layers", n_layers=2)
