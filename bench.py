@@ -42,9 +42,12 @@ MEASURED_TRAFFIC = {
 
 
 def algorithmic(cfg, kernel: str):
-    """(bytes, flops) one launch of `kernel` must move/perform, per layer and step."""
+    """(bytes, flops) one timed launch of `kernel` must move/perform, per layer and step
+    (per step for the LM head and the commit).  Weights are read once; activations
+    are counted once in and once out."""
     T = cfg.batch * cfg.canvas_len
     d, E, k, de, ds = cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_expert, cfg.d_shared
+    A = cfg.attn_dim
     wb = 1 if cfg.expert_dtype == "fp8" else 2
     ab = 2 if cfg.act_dtype == "bf16" else 4
     if kernel == "moe_gateup":
@@ -57,10 +60,37 @@ def algorithmic(cfg, kernel: str):
         return cfg.vocab * d * ab + T * d * ab, 2.0 * T * cfg.vocab * d
     if kernel == "attn":
         keys = cfg.prompt_len + cfg.canvas_len
-        A = cfg.attn_dim
         return (cfg.batch * keys * A * 2 * ab + 2 * T * A * ab,
                 4.0 * cfg.batch * cfg.canvas_len * keys * A)
+    if kernel == "qkv":
+        return 3 * A * d * ab + T * d * ab + 3 * T * A * ab, 2.0 * T * 3 * A * d
+    if kernel == "shared":  # gate/up + SwiGLU, then down (fp32 out): one timed pair
+        w = 3 * ds * d * wb + (3 * ds * 4 if wb == 1 else 0)
+        return w + T * d * ab + 2 * T * ds * ab + T * d * 4, 2.0 * T * 3 * ds * d
+    if kernel == "router":  # router GEMM (fp32 logits) + top-k
+        return E * d * ab + T * d * ab + 2 * T * E * 4 + 2 * T * k * 4, 2.0 * T * E * d
+    if kernel == "commit":
+        return T * (4 + 4 + 4 + 1) * 2, 0.0
     raise ValueError(kernel)
+
+
+# bound each kernel class is judged against: dense contractions (intensity near or
+# above the bf16 ridge) against the MFMA peak, the rest against HBM bandwidth
+KERNEL_BOUND = {"attn": "mfma", "qkv": "mfma", "shared": "mfma", "lm_head": "mfma",
+                "moe_gateup": "hbm", "moe_down": "hbm", "router": "hbm", "commit": "hbm"}
+
+
+def roofline_entry(cfg, kernel, total_ms, launches):
+    bytes_, flops = algorithmic(cfg, kernel)
+    avg_s = total_ms / 1e3 / max(launches, 1)
+    if KERNEL_BOUND[kernel] == "mfma":
+        achieved, peak, unit = flops / avg_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = bytes_ / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {"bound": KERNEL_BOUND[kernel], "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "avg_launch_us": avg_s * 1e6, "launches": launches,
+            "algorithmic_bytes_per_launch": bytes_, "algorithmic_flops_per_launch": flops,
+            "hbm_gbs": bytes_ / avg_s / 1e9, "tflops": flops / avg_s / 1e12}
 
 
 def cpu_baseline(inp, cfg, steps_per_canvas: float, layers: int):
@@ -202,8 +232,9 @@ def main():
                          "(reference for the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the batch-4 (c3) and block-autoregressive fp8 (c4) measurements")
-    ap.add_argument("--breakdown", action="store_true",
-                    help="after the timed region, time every kernel class (stderr)")
+    ap.add_argument("--no-kernels", action="store_true",
+                    help="skip the per-kernel-class roofline table (one extra canvas per class after "
+                         "the timed region)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -261,17 +292,12 @@ def main():
     elapsed = t1 - t0
     log(f"[bench] {args.steps} canvases, {total_steps} denoise steps in {elapsed:.3f} s")
 
-    bytes_, flops = algorithmic(cfg, args.kernel)
-    avg_s = prof_ms / 1e3 / max(launches, 1)
-    if args.kernel in ("lm_head",):
-        bound, achieved, peak, unit = "mfma", flops / avg_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
-    else:
-        bound, achieved, peak, unit = "hbm", bytes_ / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
-    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": MEASURED_TRAFFIC.get((args.kernel, cfg.name)),
-                "kernel": args.kernel,
-                "avg_launch_us": avg_s * 1e6, "launches": launches,
-                "algorithmic_bytes_per_launch": bytes_, "algorithmic_flops_per_launch": flops}
+    roofline = roofline_entry(cfg, args.kernel, prof_ms, launches)
+    roofline["traffic"] = MEASURED_TRAFFIC.get((args.kernel, cfg.name))
+    roofline["kernel"] = args.kernel
+    roofline = {k: roofline[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                         "avg_launch_us", "launches", "algorithmic_bytes_per_launch",
+                                         "algorithmic_flops_per_launch")}
 
     steps_per_canvas = total_steps / args.steps
     out = {
@@ -297,15 +323,21 @@ def main():
         "cpu_baseline": None,
     }
 
-    if args.breakdown:
-        for name in ("attn", "qkv", "router", "moe_gateup", "moe_down", "shared", "lm_head", "commit"):
+    # every kernel class, timed live with HIP events on its stream, one extra
+    # (untimed) canvas per class after the timed region
+    if not args.no_kernels:
+        kern = {}
+        for name in ("attn", "qkv", "shared", "router", "moe_gateup", "moe_down", "lm_head", "commit"):
             _lib.dg_profile_kernel(model.handle, _lib.DG_PROF[name])
             rt.canvas_init(model, canvas)
-            n = rt.generate_canvas(model, canvas, kv)
+            rt.generate_canvas(model, canvas, kv)
             ms, cnt = _lib.dg_profile_read(model.handle)
-            log(f"[breakdown] {name:11s} {ms / n:8.3f} ms/step  {ms / max(cnt, 1) * 1e3:9.1f} us/launch "
-                f"({cnt} launches)")
+            kern[name] = roofline_entry(cfg, name, ms, cnt)
+            e = kern[name]
+            log(f"[kernels] {name:11s} {e['avg_launch_us']:9.1f} us/launch ({cnt} launches)  "
+                f"{e['hbm_gbs']:7.0f} GB/s  {e['tflops']:7.1f} TFLOP/s  {100 * e['frac']:5.1f}% of {e['bound']} peak")
         _lib.dg_profile_kernel(model.handle, 0)
+        out["kernels"] = kern
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sampled step")
