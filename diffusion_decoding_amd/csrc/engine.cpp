@@ -205,7 +205,7 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;
     aa.causal_base = P;
   }
-  aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1));
+  aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1, dh));
   {
     ProfScope ps(m, DG_PROF_ATTN, st);
     HIP_OK(attention(at, aa, st));

@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path.  Work items (canvas-head bh, key split z, 64-query tile qt) are
+// bf16 path.  Work items (canvas-head bh, key split z, query tile qt of
+// 16 NW queries, one 16-query block per wave) are
 // linearised with the query tiles, then the splits of one head adjacent, and
 // each XCD (workgroup b runs on XCD b % 8) takes a contiguous run of items:
 // the query tiles that share a K/V tile, and the splits that are merged
@@ -223,8 +224,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
 // With several splits, each workgroup writes an unnormalised partial
 // (O, running max, running sum) and a second kernel merges them in split
 // order.
-template <int DH, int D, bool SEG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
+template <int DH, int D, bool SEG, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
                                                         int per_xcd) {
   // K row pitch: an odd multiple of 32 B keeps the 16-row x 64-byte fragment
   // reads at full LDS rate.  V^T row pitch 72 elements (36 dwords): the
@@ -236,10 +237,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   constexpr int LDV = 64 + 8;    // V^T row pitch
   constexpr int NDF = DH / 16;
   constexpr int NQ = DH / 32;
+  constexpr int NT = 64 * NW;                 // threads
   constexpr int KCH = 64 * DH / 8;            // 16-byte K chunks per tile
-  constexpr int KPT = KCH / 256;              // per thread
-  constexpr int VCH = 16 * (DH / 8);          // 4-key x 8-dim V blocks per tile
-  static_assert(KCH % 256 == 0 && VCH <= 256 && 256 % VCH == 0, "tile split");
+  constexpr int KPT = KCH / NT;               // per thread
+  // V blocks of 4 keys x VD dims: 8 dims (16-byte loads) with four waves,
+  // 4 dims (8-byte loads) with eight, so every thread moves one block
+  constexpr int VD = NW == 8 ? 4 : 8;
+  constexpr int VCH = 16 * (DH / VD);         // V blocks per tile
+  static_assert(KCH % NT == 0 && VCH <= NT && NT % VCH == 0, "tile split");
+  using vchunk = typename std::conditional<VD == 8, u32x4, u32x2>::type;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * LDKS];
   __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * LDV];
 
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int qi = qt * 64 + wave * 16 + c16;
+  const int qi = qt * 16 * NW + wave * 16 + c16;
   const int total = a.len0 + a.len1;
   const int kbeg = z * keys_per_split;
   const int kend = min(total, kbeg + keys_per_split);
@@ -293,20 +299,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
   // this thread's V block: 4-key block vkb (fastest over the lanes, so 16
-  // lanes write one contiguous 128-byte piece of a V^T row), dims vcol..+7.
-  // Threads past VCH repeat a block: same loads, same values stored to the
-  // same LDS words.
-  const int vb = tid % VCH, vkb = vb % 16, vcol = (vb / 16) * 8;
+  // lanes write one contiguous 128-byte piece of a V^T row), dims
+  // vcol .. vcol + VD - 1.  With 4-dim blocks the four 16-lane groups of a
+  // wave take dims +0, +8, +4, +12, so the two groups of a half-wave write
+  // rows 8 apart (32 banks) as with 8-dim blocks.  Threads past VCH repeat a
+  // block: same loads, same values stored to the same LDS words.
+  const int vb = tid % VCH, vkb = vb % 16, vg = vb / 16;
+  const int vcol = VD == 8 ? vg * 8 : (vg >> 2) * 16 + (vg & 1) * 8 + ((vg >> 1) & 1) * 4;
   // this thread's byte offsets inside a key tile
   int koff[KPT], voff[4];
 #pragma unroll
   for (int p = 0; p < KPT; ++p) {
-    const int c = tid + p * 256;
+    const int c = tid + p * NT;
     koff[p] = (c / (DH / 8)) * RB + (c % (DH / 8)) * 16;
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) voff[p] = (4 * vkb + p) * RB + vcol * 2;
-  u32x4 kreg[D][KPT], vreg[D][4];
+  u32x4 kreg[D][KPT];
+  vchunk vreg[D][4];
+  auto vload = [&](__amdgpu_buffer_rsrc_t r, int off) -> vchunk {
+    if constexpr (VD == 8) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  };
   auto gload = [&](int t, int u) {
     const int kt0 = kbeg + 64 * min(t, ntiles - 1);
     if constexpr (SEG) {
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int p = 0; p < KPT; ++p) kreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[p], 0, 0);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) vreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[p], 0, 0);
+      for (int p = 0; p < 4; ++p) vreg[u][p] = vload(rv, voff[p]);
       return;
     }
     const int b0 = kt0 * RB, b1 = (kt0 - a.len0) * RB;  // tile start in each segment
@@ -331,8 +345,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                    __builtin_amdgcn_raw_buffer_load_b128(rk1, koff[p] + b1, 0, 0);
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      vreg[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rv0, voff[p] + b0, 0, 0) |
-                   __builtin_amdgcn_raw_buffer_load_b128(rv1, voff[p] + b1, 0, 0);
+      vreg[u][p] = vload(rv0, voff[p] + b0) | vload(rv1, voff[p] + b1);
   };
   // V^T position of this thread's four keys: inside each 32-key block the
   // keys are stored in the order the P.V MFMA consumes them (lane group g
@@ -341,13 +354,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   auto lstore = [&](int buf, int u) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
-      const int c = tid + p * 256;
+      const int c = tid + p * NT;
       const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
       *(u32x4*)&Ks[buf][row * LDKS + col] = kreg[u][p];
     }
     // dim vcol+e: keys 4vkb..4vkb+3 as one 8-byte word at their V^T position
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < VD; ++e) {
       const int w = e >> 1, sh = (e & 1) * 16;
       const uint32_t k0 = (vreg[u][0][w] >> sh) & 0xffffu, k1 = (vreg[u][1][w] >> sh) & 0xffffu;
       const uint32_t k2 = (vreg[u][2][w] >> sh) & 0xffffu, k3 = (vreg[u][3][w] >> sh) & 0xffffu;
@@ -591,18 +604,34 @@ int launch(const AttnArgs& a, hipStream_t st) {
   return int(hipGetLastError());
 }
 
-template <int DH>
-int launch_bf16(const AttnArgs& a, hipStream_t st) {
+// Waves per workgroup of the bf16 kernel: eight (128 queries sharing each K/V
+// tile in LDS, half the L2-to-LDS traffic per query) for long key ranges,
+// four (64 queries, twice the workgroups) otherwise.
+int attn_waves(int n, int keys, int dh) { return keys >= 4096 && n >= 128 && dh >= 64 ? 8 : 4; }
+
+template <int DH, int NW>
+int launch_bf16_nw(const AttnArgs& a, hipStream_t st) {
   const int total = a.len0 + a.len1;
   const int per = ((total + a.splits - 1) / a.splits + 63) / 64 * 64;
-  const int n_qt = (a.n + 63) / 64;
+  const int n_qt = (a.n + 16 * NW - 1) / (16 * NW);
   const int items = a.B * a.H * a.splits * n_qt;
   const int per_xcd = (items + 7) / 8;
   if (a.len1 == 0 || a.len0 % 64 == 0)  // no key tile spans both segments
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, true>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, true, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
+                       per_xcd);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, false>), dim3(8 * per_xcd), dim3(256), 0, st, a, per, n_qt, per_xcd);
-  int e = int(hipGetLastError());
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, false, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
+                       per_xcd);
+  return int(hipGetLastError());
+}
+
+template <int DH>
+int launch_bf16(const AttnArgs& a, hipStream_t st) {
+  int e;
+  if constexpr (DH >= 64)
+    e = attn_waves(a.n, a.len0 + a.len1, DH) == 8 ? launch_bf16_nw<DH, 8>(a, st) : launch_bf16_nw<DH, 4>(a, st);
+  else
+    e = launch_bf16_nw<DH, 4>(a, st);
   if (e || a.splits == 1) return e;
   const long long n4 = (long long)a.B * a.H * a.n * (DH / 4);
   const dim3 g(unsigned((n4 + 255) / 256));
@@ -618,14 +647,16 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Key splits: double while the grid is under two workgroups per CU and each
-// split keeps at least 512 keys (measured at 256 queries x 16 heads: 4 splits
-// for 2304 keys, 2 for 4 canvases x 8448 keys; shorter splits lose more to the
-// merge and to each workgroup's first tile than they gain in parallelism).
-int attn_splits_for(int B, int H, int n, int keys) {
-  const int wgs = ((n + 63) / 64) * B * H;
+// Key splits: double while the grid is under 2048 waves (two four-wave or one
+// eight-wave workgroup per CU) and each split keeps at least 512 keys
+// (measured at 256 queries x 16 heads: 4 splits for 2304 keys, 2 for 4
+// canvases x 8448 keys; shorter splits lose more to the merge and to each
+// workgroup's first tile than they gain in parallelism).
+int attn_splits_for(int B, int H, int n, int keys, int dh) {
+  const int nw = attn_waves(n, keys, dh);
+  const int wgs = ((n + 16 * nw - 1) / (16 * nw)) * B * H;
   int s = 1;
-  while (s < 16 && wgs * s < 512 && keys / (s * 2) >= 512) s *= 2;
+  while (s < 16 && wgs * s * nw < 2048 && keys / (s * 2) >= 512) s *= 2;
   return s;
 }
 

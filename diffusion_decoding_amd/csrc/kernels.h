@@ -101,7 +101,7 @@ struct AttnArgs {
   int splits;
 };
 int attention(ActType at, const AttnArgs& a, hipStream_t st);
-int attn_splits_for(int B, int H, int n, int keys);
+int attn_splits_for(int B, int H, int n, int keys, int dh);
 
 // ---------------------------------------------------------------- misc (k_misc.hip)
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st);

@@ -101,10 +101,13 @@ def wide_ragged_config(batch, canvas, **kw):
     return tiny_config(**args)
 
 
-@pytest.mark.parametrize("batch", [1, 2])
-def test_wide_ragged_step_locked(rt, batch):
-    cfg = wide_ragged_config(batch, 200)
-    say(f"full-width projections, {batch} x 200 tokens (ragged tiles)")
+# 300 prompt rows: four-wave attention tiles; 4100 rows (4300 keys): eight-wave
+# tiles of 128 queries, a ragged second query tile, and a cache length that is
+# not a multiple of 64 (key tiles spanning the cache and canvas rows)
+@pytest.mark.parametrize("batch,prompt", [(1, 300), (2, 300), (1, 4100)])
+def test_wide_ragged_step_locked(rt, batch, prompt):
+    cfg = wide_ragged_config(batch, 200, prompt_len=prompt)
+    say(f"full-width projections, {batch} x 200 tokens (ragged tiles), {prompt} prompt rows")
     p = Pair(rt, cfg)
     reps, _ = p.run_locked(max_steps=2)
     p.close()
