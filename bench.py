@@ -339,6 +339,32 @@ def main():
         _lib.dg_profile_kernel(model.handle, 0)
         out["kernels"] = kern
 
+    # fill-in-the-middle on the same model: a fixed 64-token prefix and
+    # 64-token suffix (pre-committed), 128 open positions denoised around them
+    if not args.no_extra and args.config == "c2":
+        head = tail = N // 4
+        g = torch.Generator(device="cuda").manual_seed(cfg.seed + 100)
+        ptok = torch.randint(0, cfg.vocab, (B, N), generator=g, device="cuda", dtype=torch.int32)
+        pmask = torch.zeros(B, N, dtype=torch.uint8, device="cuda")
+        pmask[:, :head] = 1
+        pmask[:, N - tail:] = 1
+        rt.canvas_init(model, canvas)
+        rt.canvas_prefill(model, canvas, ptok, pmask)
+        rt.generate_canvas(model, canvas, kv)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rt.canvas_init(model, canvas)
+        rt.canvas_prefill(model, canvas, ptok, pmask)
+        n_inf = rt.generate_canvas(model, canvas, kv)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        opened = B * (N - head - tail)
+        out["infill"] = {"workload": cfg.name, "fixed_prefix": head, "fixed_suffix": tail,
+                         "open_positions": opened, "denoise_steps": n_inf,
+                         "generated_tokens_per_s": opened / dt, "canvas_tokens_per_s": B * N / dt,
+                         "ms_per_denoise_step": dt / n_inf * 1e3}
+        log(f"[bench] infill: {opened} open positions, {n_inf} steps in {dt:.3f} s")
+
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sampled step")
         out["cpu_baseline"] = cpu_baseline(inp, cfg, steps_per_canvas, max(1, min(args.cpu_layers, cfg.n_layers)))

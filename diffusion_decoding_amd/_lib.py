@@ -61,6 +61,7 @@ _SIGS = {
                         POINTER(c_void_p)],
     "dg_model_destroy": [c_void_p],
     "dg_canvas_init": [c_void_p, POINTER(dg_canvas), c_void_p],
+    "dg_canvas_prefill": [c_void_p, POINTER(dg_canvas), c_void_p, c_void_p, c_void_p],
     "dg_denoise_step": [c_void_p, POINTER(dg_canvas), POINTER(dg_kv), POINTER(dg_step_out),
                         c_void_p],
     "dg_generate_canvas": [c_void_p, POINTER(dg_canvas), POINTER(dg_kv), POINTER(c_int32),
@@ -125,6 +126,10 @@ def dg_model_destroy(handle):
 
 def dg_canvas_init(handle, canvas, stream):
     _call("dg_canvas_init", handle, byref(canvas), stream)
+
+
+def dg_canvas_prefill(handle, canvas, tokens_ptr, mask_ptr, stream):
+    _call("dg_canvas_prefill", handle, byref(canvas), tokens_ptr, mask_ptr, stream)
 
 
 def dg_denoise_step(handle, canvas, kv, out, stream):

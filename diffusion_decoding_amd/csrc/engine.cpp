@@ -464,6 +464,15 @@ int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream) {
   return DG_OK;
 }
 
+int dg_canvas_prefill(dg_model* m, dg_canvas* c, const int32_t* tokens, const uint8_t* mask, void* stream) {
+  if (!m || !tokens || !mask) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_canvas(m, c);
+  if (s) return s;
+  if (c->step != 0) return fail(DG_ERR_STATE, "prefill needs a canvas at step 0 (step %d)", c->step);
+  HIP_OK(canvas_prefill(c->tokens, c->committed, c->batch * m->cfg.canvas_len, tokens, mask, (hipStream_t)stream));
+  return DG_OK;
+}
+
 int dg_denoise_step(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, void* stream) {
   if (!m) return fail(DG_ERR_INVALID_ARG, "null model");
   int s = check_canvas(m, c);

@@ -259,6 +259,19 @@ __global__ __launch_bounds__(1024) void combine_norm_bf16_kernel(bf16* x, const 
   }
 }
 
+// Pre-committed positions (fill-in-the-middle, constraint puzzles: the known
+// tokens are fixed and the rest of the canvas is denoised around them;
+// DiffusionGemma深度拆解 (zhichai.net), "代码填充的结构性优势"): position i
+// with mask[i] != 0 takes token given[i] and is marked committed, so the
+// commit and re-noise steps never touch it.
+__global__ void prefill_kernel(int* tok, uint8_t* committed, int n, const int* given, const uint8_t* mask) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n && mask[i]) {
+    tok[i] = given[i];
+    committed[i] = 1;
+  }
+}
+
 __global__ void canvas_init_kernel(int* tok, uint8_t* committed, int N, uint64_t seed, uint32_t block,
                                    int vocab) {
   const int b = blockIdx.y;
@@ -423,6 +436,12 @@ int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint3
                 hipStream_t st) {
   hipLaunchKernelGGL(canvas_init_kernel, dim3((N + 255) / 256, B), dim3(256), 0, st, tok, committed, N,
                      seed, block, vocab);
+  return int(hipGetLastError());
+}
+
+int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const uint8_t* mask, hipStream_t st) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(prefill_kernel, dim3((n + 255) / 256), dim3(256), 0, st, tok, committed, n, given, mask);
   return int(hipGetLastError());
 }
 

@@ -120,6 +120,8 @@ int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const
                      int T, int k, int d, float eps, void* a, hipStream_t st);
 int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block,
                 int vocab, hipStream_t st);
+// tok[i] = given[i], committed[i] = 1 wherever mask[i] != 0 (i < n)
+int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const uint8_t* mask, hipStream_t st);
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N,
                    int step, int max_steps, float threshold, uint64_t seed, uint32_t block,
                    int vocab, int* n_unc, hipStream_t st);

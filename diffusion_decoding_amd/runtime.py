@@ -125,6 +125,20 @@ def canvas_init(model: Model, canvas: Canvas, stream=None):
     canvas.step = s.step
 
 
+def canvas_prefill(model: Model, canvas: Canvas, tokens: torch.Tensor, mask: torch.Tensor, stream=None):
+    """Pre-commit the positions where ``mask`` (uint8 [B, N]) is set to ``tokens``
+    (int32 [B, N]); after canvas_init, before the first step."""
+    B, N = canvas.tokens.shape
+    if tuple(tokens.shape) != (B, N) or tuple(mask.shape) != (B, N):
+        raise ValueError(f"tokens/mask must be [{B}, {N}]")
+    if tokens.dtype != torch.int32 or mask.dtype != torch.uint8:
+        raise TypeError("tokens must be int32 and mask uint8")
+    if not (tokens.is_cuda and mask.is_cuda and tokens.is_contiguous() and mask.is_contiguous()):
+        raise ValueError("tokens and mask must be contiguous device tensors")
+    s = canvas.struct()
+    _lib.dg_canvas_prefill(model.handle, s, _ptr(tokens), _ptr(mask), _stream(stream))
+
+
 def denoise_step(model: Model, canvas: Canvas, kv: KVCache, entropy=None, argmax=None, top2_gap=None,
                  n_uncommitted=None, logits=None, hidden=None, stream=None):
     s = canvas.struct()

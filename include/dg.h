@@ -169,6 +169,18 @@ int dg_model_destroy(dg_model* m);
 /* Draw the initial canvas (step_tag 0) and clear `committed`; sets step = 0. */
 int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream);
 
+/* Pre-commit known positions of a freshly initialised canvas (fill-in-the-
+ * middle and constraint tasks: DiffusionGemma深度拆解 (zhichai.net),
+ * "代码填充的结构性优势"; the denoiser refines the open positions around
+ * fixed ones).  `tokens` and `mask` are device arrays of
+ * [batch][canvas_len] (int32 ids in [0, vocab), uint8 0/1): wherever
+ * mask != 0 the canvas takes that token and the position is committed, so
+ * the commit schedule counts only the open positions and re-noising never
+ * touches it.  Call after dg_canvas_init and before the first step
+ * (c->step == 0, else DG_ERR_STATE); stream-ordered.  Token values are not
+ * checked on the host (they are device-resident). */
+int dg_canvas_prefill(dg_model* m, dg_canvas* c, const int32_t* tokens, const uint8_t* mask, void* stream);
+
 /* One denoise step (forward, confidence, commit, re-noise) on every canvas of
  * `c` against the first kv->length cache rows.  Requires c->step < max_steps;
  * increments c->step.  kv->batch must equal c->batch. */

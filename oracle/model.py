@@ -366,6 +366,22 @@ def init_state(cfg, seed: int, block: int = 0) -> CanvasState:
     return CanvasState(tok, np.zeros((B, N), dtype=bool), 0, seed, block)
 
 
+def prefill(state: CanvasState, tokens: np.ndarray, mask: np.ndarray) -> CanvasState:
+    """Fix known positions before the first step (fill-in-the-middle, puzzles
+    with givens: DiffusionGemma深度拆解 (zhichai.net), "代码填充的结构性优势" --
+    bidirectional attention lets the open positions use the known tokens on
+    both sides).  Where ``mask`` [B, N] is set the canvas takes ``tokens`` and
+    the position counts as committed: it is fed to every forward like any
+    committed token, never ranked, counted in U or re-noised.
+    """
+    if state.step != 0:
+        raise ValueError("prefill applies to a canvas before its first step")
+    m = np.asarray(mask, dtype=bool)
+    state.tokens[m] = np.asarray(tokens, dtype=np.int64)[m]
+    state.committed |= m
+    return state
+
+
 def forward_canvas(tok_row, W: Weights, kv: KV, b: int, cfg, prec: Prec, trace=None):
     """Bidirectional forward of one canvas; returns the final normed hidden rows."""
     P = kv.length

@@ -55,13 +55,19 @@ class Pair:
         torch.cuda.synchronize()
         om.commit_canvas(self.W, self.okv, tokens.astype(np.int64), self.cfg)
 
-    def run_locked(self, block=0, max_steps=None, keep_logits=True):
-        """Step-locked denoise loop; returns (step reports, oracle final state)."""
+    def run_locked(self, block=0, max_steps=None, keep_logits=True, prefill=None):
+        """Step-locked denoise loop; returns (step reports, oracle final state).
+        prefill: optional (tokens [B, N], mask [B, N]) of pre-committed positions."""
         rt, cfg = self.rt, self.cfg
         ost = om.init_state(cfg, cfg.seed, block)
         B, N = cfg.batch, cfg.canvas_len
         canvas = rt.Canvas.empty(B, N, cfg.seed, block)
         rt.canvas_init(self.model, canvas)
+        if prefill is not None:
+            ptok, pmask = prefill
+            om.prefill(ost, ptok, pmask)
+            rt.canvas_prefill(self.model, canvas, torch.from_numpy(ptok.astype(np.int32)).to("cuda"),
+                              torch.from_numpy(pmask.astype(np.uint8)).to("cuda"))
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
         ent = torch.empty(B, N, dtype=torch.float32, device="cuda")

@@ -13,6 +13,7 @@ import torch
 
 from oracle import model as om
 from oracle import philox
+from tests.gpu_helpers import Pair
 from tests.parity import H_TOL, compare_step, h_tol, logits_tol, to_host
 from workloads import get_config, make_inputs, tiny_config
 
@@ -173,6 +174,66 @@ def test_generate_canvas_matches_oracle_c0(rt):
     assert steps == osteps
     assert to_host(canvas.committed).all()
     np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+    model.close()
+
+
+# ----------------------------------------------------------------------------- pre-committed positions
+
+def _fim(B, N, head, tail, vocab, seed):
+    """Known prefix and suffix (fixed tokens), open middle."""
+    mask = np.zeros((B, N), dtype=bool)
+    mask[:, :head] = True
+    mask[:, N - tail:] = True
+    return np.random.default_rng(seed).integers(0, vocab, (B, N)), mask
+
+
+def test_prefill_generate_matches_oracle_c0(rt):
+    cfg = get_config("c0")
+    say("c0 with a fixed prefix (5) and suffix (3): dg_canvas_prefill + dg_generate_canvas vs oracle")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    ptok, pmask = _fim(1, cfg.canvas_len, 5, 3, cfg.vocab, 41)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    rt.canvas_prefill(model, canvas, torch.from_numpy(ptok.astype(np.int32)).cuda(),
+                      torch.from_numpy(pmask.astype(np.uint8)).cuda())
+    steps = rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=False)
+    ost = om.prefill(om.init_state(cfg, cfg.seed), ptok, pmask)
+    ost, osteps = om.generate_canvas(W, okv, cfg, cfg.seed, state=ost)
+    assert steps == osteps
+    tok = to_host(canvas.tokens)
+    assert to_host(canvas.committed).all()
+    np.testing.assert_array_equal(tok, ost.tokens)
+    np.testing.assert_array_equal(tok[pmask], ptok[pmask])
+    model.close()
+
+
+def test_prefill_step_locked_tiny_bf16_batch2(rt):
+    cfg = tiny_config(name="tiny_prefill_bf16", act_dtype="bf16", expert_dtype="bf16", batch=2,
+                      canvas_len=40, prompt_len=100, head_dim=32, n_heads=2, max_steps=5, seed=42,
+                      lm_scale=1.0)
+    say("tiny bf16, batch 2 x 40, fixed prefix 6 + suffix 10, step-locked")
+    p = Pair(rt, cfg)
+    ptok, pmask = _fim(2, 40, 6, 10, cfg.vocab, 43)
+    reps, ost = p.run_locked(prefill=(ptok, pmask))
+    p.close()
+    _assert_reports(cfg, reps)
+    np.testing.assert_array_equal(ost.tokens[pmask], ptok[pmask])
+
+
+def test_prefill_rejects_a_started_canvas(rt):
+    cfg = get_config("c0")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    rt.denoise_step(model, canvas, kv)
+    t = torch.zeros(1, cfg.canvas_len, dtype=torch.int32, device="cuda")
+    m = torch.zeros(1, cfg.canvas_len, dtype=torch.uint8, device="cuda")
+    with pytest.raises(Exception):
+        rt.canvas_prefill(model, canvas, t, m)
+    torch.cuda.synchronize()
     model.close()
 
 

@@ -124,6 +124,77 @@ def test_loop_invariants(cfg):
     np.testing.assert_array_equal(state.tokens, hist[-1][0])
 
 
+def _fim_mask(B, N, head, tail):
+    """Known prefix and suffix, open middle (fill-in-the-middle)."""
+    m = np.zeros((B, N), dtype=bool)
+    m[:, :head] = True
+    m[:, N - tail:] = True
+    return m
+
+
+@pytest.mark.parametrize("cfg", [tiny_config(threshold=-math.inf, seed=31),
+                                 tiny_config(batch=2, seed=32)])
+def test_prefill_positions_are_fixed_and_only_open_ones_are_scheduled(cfg):
+    """Pre-committed positions keep their tokens through the loop; the commit
+    count follows ceil(U / (S_max - s)) over the open positions only, and every
+    open position is committed by the step cap."""
+    inp, W, kv = _setup(cfg)
+    B, N = cfg.batch, cfg.canvas_len
+    mask = _fim_mask(B, N, 5, 3)
+    given = np.random.default_rng(3).integers(0, cfg.vocab, (B, N))
+    st = om.prefill(om.init_state(cfg, cfg.seed), given, mask)
+    np.testing.assert_array_equal(st.tokens[mask], given[mask])
+    init = om.init_state(cfg, cfg.seed)
+    np.testing.assert_array_equal(st.tokens[~mask], init.tokens[~mask])   # open ones keep their draw
+    hist = []
+    state, steps = om.generate_canvas(W, kv, cfg, cfg.seed, state=st,
+                                      hook=lambda res, s: hist.append((s.committed.copy(), res)))
+    assert state.committed.all()
+    np.testing.assert_array_equal(state.tokens[mask], given[mask])
+    prev = mask.copy()
+    for s, (com, res) in enumerate(hist):
+        assert not (res.newly & mask).any()                    # never re-selected
+        for b in range(B):
+            U = int((~prev[b]).sum())
+            assert res.m[b] == om.commit_count(U, s, cfg.max_steps)
+            assert res.newly[b].sum() >= min(U, res.m[b])
+        prev = com
+    if cfg.threshold == -math.inf:
+        # 8 open positions over 8 steps: one per step
+        assert steps == cfg.max_steps
+        assert [int(r.newly.sum()) for _, r in hist] == [B] * cfg.max_steps
+
+
+def test_prefill_of_every_position_stops_after_one_step_unchanged():
+    cfg = tiny_config(seed=33)
+    inp, W, kv = _setup(cfg)
+    given = np.arange(cfg.canvas_len)[None, :] % cfg.vocab
+    st = om.prefill(om.init_state(cfg, cfg.seed), given, np.ones((1, cfg.canvas_len), bool))
+    state, steps = om.generate_canvas(W, kv, cfg, cfg.seed, state=st)
+    assert steps == 1
+    np.testing.assert_array_equal(state.tokens, given)
+
+
+def test_prefill_equals_the_same_canvas_committed_by_hand():
+    """A prefilled canvas is the state a loop would be in had those positions
+    been committed: a step from either gives the same result."""
+    cfg = tiny_config(seed=34)
+    inp, W, kv = _setup(cfg)
+    mask = _fim_mask(1, cfg.canvas_len, 4, 4)
+    given = (np.arange(cfg.canvas_len) * 7 % cfg.vocab)[None, :]
+    a = om.prefill(om.init_state(cfg, cfg.seed), given, mask)
+    b = om.init_state(cfg, cfg.seed)
+    b.tokens[mask] = given[mask]
+    b.committed[mask] = True
+    ra = om.denoise_step(W, kv, a, cfg)
+    rb = om.denoise_step(W, kv, b, cfg)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    np.testing.assert_array_equal(a.committed, b.committed)
+    np.testing.assert_array_equal(ra.entropy, rb.entropy)
+    with pytest.raises(ValueError):
+        om.prefill(a, given, mask)          # only before the first step
+
+
 def test_c0_exercises_threshold_early_stop():
     cfg = get_config("c0")
     inp, W, kv = _setup(cfg)
