@@ -88,8 +88,8 @@ def test_commit_kernel_bit_exact(rt):
 
 # ----------------------------------------------------------------------------- step-locked loop
 
-def _run_locked(rt, cfg, max_steps=None, keep_logits=True):
-    inp, model, kv = _gpu_setup(rt, cfg)
+def _run_locked(rt, cfg, max_steps=None, keep_logits=True, kv_capacity=None):
+    inp, model, kv = _gpu_setup(rt, cfg, kv_capacity=kv_capacity)
     W = om.Weights(inp, cache=True)
     okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=cfg.act_dtype == "bf16")
     ost = om.init_state(cfg, cfg.seed)
@@ -234,6 +234,58 @@ def test_prefill_rejects_a_started_canvas(rt):
     with pytest.raises(Exception):
         rt.canvas_prefill(model, canvas, t, m)
     torch.cuda.synchronize()
+    model.close()
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_no_prompt_step_locked(rt, act):
+    """An empty prompt KV cache (length 0): the canvas attends to itself only."""
+    cfg = tiny_config(name=f"tiny_noprompt_{act}", act_dtype=act, expert_dtype=act, prompt_len=0,
+                      head_dim=32, n_heads=2, max_steps=4, seed=51, lm_scale=6.0 if act == "fp32" else 1.0)
+    say(f"tiny, empty prompt KV, {act}")
+    reps = _run_locked(rt, cfg, kv_capacity=16)
+    _assert_reports(cfg, reps)
+
+
+def test_single_step_cap_commits_everything(rt):
+    """S_max = 1: the only step commits every position (m = U)."""
+    cfg = tiny_config(name="tiny_smax1", max_steps=1, seed=52)
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    steps = rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=False)
+    ost, osteps = om.generate_canvas(W, okv, cfg, cfg.seed)
+    assert steps == osteps == 1
+    assert to_host(canvas.committed).all()
+    np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+    model.close()
+
+
+def test_max_canvas_length_step_locked(rt):
+    """The largest canvas the library takes (1024 positions): a 1024-thread
+    commit selection, 16 query tiles, 1024 tokens routed at once."""
+    cfg = tiny_config(name="tiny_canvas1024", canvas_len=1024, max_steps=3, seed=53)
+    say("tiny dims, canvas 1024, fp32")
+    reps = _run_locked(rt, cfg, max_steps=2)
+    _assert_reports(cfg, reps)
+
+
+def test_prefill_every_position_stops_after_one_step(rt):
+    cfg = get_config("c0")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    given = torch.arange(cfg.canvas_len, dtype=torch.int32, device="cuda").reshape(1, -1) * 5 % cfg.vocab
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    rt.canvas_prefill(model, canvas, given.contiguous(), torch.ones_like(given, dtype=torch.uint8))
+    steps = rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    assert steps == 1
+    np.testing.assert_array_equal(to_host(canvas.tokens), to_host(given))
     model.close()
 
 
