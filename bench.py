@@ -231,7 +231,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB five times and exit "
                          "(reference for the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the batch-4 (c3) and block-autoregressive fp8 (c4) measurements")
+                    help="skip the batch-4 (c3), batch-8 (c5), fill-in-the-middle and block-autoregressive "
+                         "fp8 (c4) measurements")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the per-kernel-class roofline table (one extra canvas per class after "
                          "the timed region)")
@@ -373,6 +374,7 @@ def main():
     free_gpu()
     if not args.no_extra and args.config == "c2":
         out["batch4"] = time_loop(get_config("c3"), canvases=1, warmup=1)
+        out["batch8"] = time_loop(get_config("c5"), canvases=1, warmup=1)
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
     print(json.dumps(out), flush=True)
 

@@ -378,8 +378,11 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   if (max_batch <= 0 || max_tokens < 0 || max_kv < 0)
     return fail(DG_ERR_INVALID_ARG, "max_batch must be > 0, max_tokens and max_kv >= 0");
   const int ntok = std::max(max_tokens, cfg->canvas_len);
-  if ((long long)max_batch * ntok > 1024)
-    return fail(DG_ERR_SHAPE, "max_batch * max(max_tokens, canvas_len) must be <= 1024");
+  // tokens of one call: the routed gate/up kernel derives the routing of up
+  // to 2048 tokens in LDS; the fp32 path's permutation kernel takes 1024
+  const long long max_t = cfg->act_dtype == DG_DTYPE_BF16 ? 2048 : 1024;
+  if ((long long)max_batch * ntok > max_t)
+    return fail(DG_ERR_SHAPE, "max_batch * max(max_tokens, canvas_len) must be <= %lld", max_t);
 
   dg_model* m = new dg_model();
   m->cfg = *cfg;

@@ -122,7 +122,9 @@ struct MoeArgs {
   int* pos_out;
 };
 
-constexpr int ROUTE_MAX_TOKENS = 1024;
+constexpr int ROUTE_MAX_TOKENS = 2048;
+// static LDS of the routing lists (tok, slot, flag, red) in the gate/up kernel
+constexpr int ROUTE_LDS = ROUTE_MAX_TOKENS * (4 + 1 + 1) + 16;
 
 // The routing of one expert e from the top-k ids: pairs of experts below e
 // (its pair offset), and its tokens in ascending order with the slot j that
@@ -524,11 +526,11 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
   const size_t lds = KC > 0 ? size_t(2 * 16 * MTP) * (KC + 16) * sizeof(bf16)
                             : size_t(16 * MTP) * (a.K + 16) * sizeof(bf16);
-  if (lds + (GU ? 8192 : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
+  if (lds + (GU ? ROUTE_LDS : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
   // once per kernel (not inside a graph capture): the largest dynamic LDS any launch may ask for
   static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     160 * 1024 - (GU ? 8192 : 0));
+                                                     160 * 1024 - (GU ? ROUTE_LDS : 0));
   if (attr != hipSuccess) return int(attr);
   hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);

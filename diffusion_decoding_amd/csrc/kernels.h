@@ -69,7 +69,7 @@ int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax,
 // of reading off/pair_row, and write off [E+1], pair_row [T*k] and pos [T][k] for later kernels.
 struct MoeRoute {
   const int* ids;  // [T][k]
-  int T, k;        // T <= 1024
+  int T, k;        // T <= 2048
   int* off;
   int* pair_row;
   int* pos;

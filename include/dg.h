@@ -160,8 +160,10 @@ const char* dg_version(void);
 /* Create a model over borrowed weights.  `max_batch` canvases per call and up
  * to `max_tokens` tokens per canvas in dg_commit_canvas (>= canvas_len) size
  * the workspace, which is allocated here once; `max_kv` bounds the KV rows
- * attention reads (capacity of the largest cache used).  Must be called with
- * the target device current. */
+ * attention reads (capacity of the largest cache used).  max_batch x
+ * max(max_tokens, canvas_len) may be at most 2048 with bf16 activations and
+ * 1024 with fp32 (DG_ERR_SHAPE otherwise).  Must be called with the target
+ * device current. */
 int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch,
                     int32_t max_tokens, int32_t max_kv, dg_model** out);
 int dg_model_destroy(dg_model* m);

@@ -162,6 +162,20 @@ def test_c3_shape_one_layer_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_batch8_full_width_one_step(rt):
+    """Eight canvases (2048 tokens pooled in the experts: two token passes per
+    expert in both routed kernels), each with its own 1024-row prompt; a
+    short vocabulary keeps the oracle's LM head quick."""
+    cfg = get_config("c5").replace(name="c5_shape_1_layer", n_layers=1, prompt_len=1024, vocab=8192)
+    say("batch 8 x 256 (2048 pooled expert tokens), 1 layer, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_c1_step_is_deterministic(rt):
     """Two runs of the same step give bitwise identical entropy, argmax and canvas."""
     cfg = get_config("c1")

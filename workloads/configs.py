@@ -80,8 +80,13 @@ _C3 = _C2.replace(name="c3_batch4_p8192_bf16", batch=4, prompt_len=8192, seed=3)
 _C4 = _C2.replace(name="c4_blockar_fp8", expert_dtype="fp8", prompt_len=512, seed=4,
                   n_canvases=8, prompt_mode="tokens")
 
-CONFIGS = {c.name: c for c in (_C0, _C1, _C2, _C3, _C4)}
-_ALIASES = {"c0": _C0.name, "c1": _C1.name, "c2": _C2.name, "c3": _C3.name, "c4": _C4.name}
+# batch sweep beyond the four canvases of c3: eight canvases (2048 pooled
+# expert tokens), each with its own 8192-row prompt KV cache
+_C5 = _C3.replace(name="c5_batch8_p8192_bf16", batch=8, seed=5)
+
+CONFIGS = {c.name: c for c in (_C0, _C1, _C2, _C3, _C4, _C5)}
+_ALIASES = {"c0": _C0.name, "c1": _C1.name, "c2": _C2.name, "c3": _C3.name, "c4": _C4.name,
+            "c5": _C5.name}
 
 
 def get_config(name: str) -> Config:
