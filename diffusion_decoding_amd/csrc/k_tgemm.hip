@@ -453,22 +453,22 @@ __device__ __forceinline__ void wait_barrier() {
 // what may still be in flight when stage kt is consumed.
 template <int SA, int SB, int KT, int LA, int LB>
 constexpr int loads_after(int kt) {
-  int pos = 0, last = -1;
-  int seqs[2 * (SA > SB ? SA : SB) + 2 * KT][2] = {};  // (kind, stage)
+  constexpr int SMAX = SA > SB ? SA : SB;
+  int seq[2 * SMAX + 2 * KT][2] = {};  // issue order: (0 = A / 1 = B, stage)
   int n = 0;
-  for (int st = 0; st < (SA > SB ? SA : SB) - 1; ++st) {
-    if (st <= SA - 2 && st < KT) { seqs[n][0] = 0; seqs[n][1] = st; ++n; }
-    if (st <= SB - 2 && st < KT) { seqs[n][0] = 1; seqs[n][1] = st; ++n; }
+  for (int st = 0; st < SMAX - 1; ++st) {
+    if (st <= SA - 2 && st < KT) { seq[n][0] = 0; seq[n][1] = st; ++n; }
+    if (st <= SB - 2 && st < KT) { seq[n][0] = 1; seq[n][1] = st; ++n; }
   }
   for (int j = 0; j < kt; ++j) {
-    if (j + SA - 1 < KT) { seqs[n][0] = 0; seqs[n][1] = j + SA - 1; ++n; }
-    if (j + SB - 1 < KT) { seqs[n][0] = 1; seqs[n][1] = j + SB - 1; ++n; }
+    if (j + SA - 1 < KT) { seq[n][0] = 0; seq[n][1] = j + SA - 1; ++n; }
+    if (j + SB - 1 < KT) { seq[n][0] = 1; seq[n][1] = j + SB - 1; ++n; }
   }
+  int last = -1;
   for (int i = 0; i < n; ++i)
-    if (seqs[i][1] == kt) last = i;
+    if (seq[i][1] == kt) last = i;
   int cnt = 0;
-  for (int i = last + 1; i < n; ++i) cnt += seqs[i][0] == 0 ? LA : LB;
-  (void)pos;
+  for (int i = last + 1; i < n; ++i) cnt += seq[i][0] == 0 ? LA : LB;
   return cnt;
 }
 
