@@ -221,12 +221,24 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   // beside the router and the routed experts, its workgroups held CUs that
   // the routed gate/up workgroups (138 KB of LDS each) could not share, and
   // the waits this caused on the main stream cost more than the overlap won.)
+  // Where the bf16 direct-load kernel covers the shared gate/up, the router
+  // logits (the same normed rows against the E router rows) ride in its
+  // launch as extra tiles instead of a launch of their own.
+  bool router_done = false;
   {
     ProfScope ps(m, DG_PROF_SHARED, st);
     GemmArgs g;  // shared gate/up + SwiGLU
     g.A = m->a; g.lda = d; g.B = w.ws_gu; g.ldb = d; g.b_scale = w.ss_gu;
     g.M = T; g.N = ds; g.K = d; g.C = m->hs; g.ldc = ds; g.swiglu_half = ds;
-    HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, 1, st));
+    int r = int(hipErrorInvalidValue);
+    if (at == ACT_BF16 && m->wt == W_BF16) {
+      GemmArgs gf = g;
+      gf.B2 = w.wr; gf.ldb2 = d; gf.N2 = E; gf.C2 = m->rlog; gf.ldc2 = E;
+      r = gemm(at, m->wt, EPI_SWIGLU, gf, 1, st);
+      router_done = r == int(hipSuccess);
+    }
+    if (r == int(hipErrorInvalidValue)) r = gemm(at, m->wt, EPI_SWIGLU, g, 1, st);
+    HIP_OK(r);
     GemmArgs g2;  // shared down
     g2.A = m->hs; g2.lda = ds; g2.B = w.ws_d; g2.ldb = ds; g2.b_scale = w.ss_d;
     g2.M = T; g2.N = d; g2.K = ds; g2.C = m->ys; g2.ldc = d;
@@ -237,7 +249,7 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     {
       GemmArgs g;
       g.A = m->a; g.lda = d; g.B = w.wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = m->rlog; g.ldc = E;
-      HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
+      if (!router_done) HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
       HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
     }
     // bf16: the routed gate/up kernel derives the permutation itself

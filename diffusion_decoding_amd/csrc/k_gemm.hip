@@ -352,6 +352,7 @@ int lm_tiles(ActType at, int K, int vocab) {
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st) {
   if (g.K % BK) return int(hipErrorInvalidValue);
   if (!g.g_off && tgemm_supported(at, g.K)) return tgemm(wt, epi, g, st);
+  if (g.B2) return int(hipErrorInvalidValue);  // a second product needs the bf16 direct-load kernel
   if (at == ACT_F32 && wt == W_F32) return launch_epi<float, float>(epi, g, groups, st);
   if (at == ACT_BF16 && wt == W_BF16) return launch_epi<bf16, bf16>(epi, g, groups, st);
   if (at == ACT_BF16 && wt == W_FP8) {

@@ -502,7 +502,8 @@ __device__ __forceinline__ long long dl_brow(const GemmArgs& g, int tn, int r, b
 // (BN / WAVES_N) block of the tile.  An A stage buffer holds BM / 8 blocks, a
 // B stage buffer BN / 8, block q holding rows 8 q .. 8 q + 7 of the tile.
 template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT>
-__global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+__global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int tiles_n2,
+                                                         int per_xcd) {
   constexpr int WAVES_N = NWV / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 16, FN = WN / 16;
@@ -542,9 +543,12 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
     else return B7;
   };
 
+  // tiles of the second product (B2, fp32 out) come first, then the main ones
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int tile = xcd * per_xcd + slot;
-  if (slot >= per_xcd || tile >= tiles_m * tiles_n) return;  // uniform over the workgroup
+  const int tile0 = xcd * per_xcd + slot, aux_tiles = tiles_m * tiles_n2;
+  if (slot >= per_xcd || tile0 >= aux_tiles + tiles_m * tiles_n) return;  // uniform over the workgroup
+  const bool aux = tile0 < aux_tiles;
+  const int tile = aux ? tile0 : tile0 - aux_tiles;
   const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
   // the wave index is uniform: keep it (and the LDS block offsets) scalar
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -565,9 +569,15 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    bool ok;
-    const long long r = dl_brow<EPI, BN>(g, tn, 8 * (wave + NWV * i) + rr8, ok);
-    bsrc[i] = (const bf16*)g.B + (ok ? r : 0) * g.ldb + 8 * ch;
+    const int r8 = 8 * (wave + NWV * i) + rr8;
+    if (aux) {
+      const int n = tn * BN + r8;
+      bsrc[i] = (const bf16*)g.B2 + (long long)(n < g.N2 ? n : 0) * g.ldb2 + 8 * ch;
+    } else {
+      bool ok;
+      const long long r = dl_brow<EPI, BN>(g, tn, r8, ok);
+      bsrc[i] = (const bf16*)g.B + (ok ? r : 0) * g.ldb + 8 * ch;
+    }
   }
   auto issue_a = [&](int kt, bf16* b) {
 #pragma unroll
@@ -636,7 +646,14 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
     compute(abuf(kc), bbuf(kc));
   });
 
-  if constexpr (EPI == EPI_LM) {
+  if (aux) {
+    GemmArgs g2 = g;
+    g2.N = g.N2;
+    g2.C = g.C2;
+    g2.ldc = g.ldc2;
+    g2.b_scale = nullptr;
+    plain_store<EPI_F32, FM, FN>(acc, g2, m0 + wr, tn * BN + wc);
+  } else if constexpr (EPI == EPI_LM) {
     lm_partials<FM, FN>(acc, g, m0 + wr, tn * BN + wc, tiles_n * WAVES_N, tn * WAVES_N + (wave % WAVES_N));
   } else if constexpr (EPI == EPI_SWIGLU) {
     swiglu_store<FM, FN>(acc, g, m0 + wr, tn * (BN / 2) + (wc / 2));
@@ -681,13 +698,15 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
 template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT = 32>
 int launch_dl(const GemmArgs& g, hipStream_t st) {
   if (g.K != 64 * KT || g.lda % 8 || g.ldb % 8) return int(hipErrorInvalidValue);
+  if (g.B2 && (g.ldb2 % 8 || !g.C2 || g.N2 <= 0)) return int(hipErrorInvalidValue);
   const int bn_out = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + bn_out - 1) / bn_out;
-  const int total = tiles_m * tiles_n;
+  const int tiles_n2 = g.B2 ? (g.N2 + BN - 1) / BN : 0;
+  const int total = tiles_m * (tiles_n + tiles_n2);
   if (total == 0) return 0;
   const int per_xcd = (total + 7) / 8;
   hipLaunchKernelGGL((dgemm_kernel<BM, BN, WAVES_M, NWV, SA, SB, EPI, KT>), dim3(8 * per_xcd), dim3(64 * NWV), 0, st,
-                     g, tiles_m, tiles_n, per_xcd);
+                     g, tiles_m, tiles_n, tiles_n2, per_xcd);
   return int(hipGetLastError());
 }
 
@@ -714,10 +733,15 @@ int launch_kg(const GemmArgs& g, hipStream_t st, int kg_max) {
 int dense_direct(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   if (g.K != 2048 || g.lda % 8 || g.ldb % 8 || g.N < 1024) return -1;
   const bool small = g.M <= 384;
+  if (g.B2 && !(epi == EPI_SWIGLU && small)) return -1;
   switch (epi) {
     case EPI_QKV:
       return small ? launch_dl<64, 128, 2, 8, 3, 6, EPI_QKV>(g, st) : launch_dl<128, 256, 2, 8, 2, 3, EPI_QKV>(g, st);
     case EPI_SWIGLU:
+      // with a second product (the router logits) the rings shrink to A 3 /
+      // B 6 (72 KB), so two workgroups share a CU and the extra tiles run in
+      // the same round
+      if (small && g.B2) return launch_dl<64, 64, 4, 8, 3, 6, EPI_SWIGLU>(g, st);
       return small ? launch_dl<64, 64, 4, 8, 4, 8, EPI_SWIGLU>(g, st)
                    : launch_dl<128, 128, 4, 8, 3, 4, EPI_SWIGLU>(g, st);
     case EPI_RESID:
@@ -738,6 +762,7 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
     const int r = dense_direct(epi, g, st);
     if (r >= 0) return r;
   }
+  if (g.B2) return int(hipErrorInvalidValue);  // only the direct-load kernel computes a second product
   switch (epi) {
     case EPI_LM:
       if constexpr (std::is_same<TB, bf16>::value)

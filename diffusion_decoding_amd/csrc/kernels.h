@@ -45,6 +45,13 @@ struct GemmArgs {
   long long dst_bh = 0;
   int row0 = 0, seq_n = 0, heads = 0;
   const float* rope_tab = nullptr;
+  // optional second product over the same A (bf16 direct-load kernel only):
+  // C2[m][n] = sum_k A[m][k] * B2[n][k] (fp32), n < N2, in the same launch
+  const void* B2 = nullptr;
+  long long ldb2 = 0;
+  int N2 = 0;
+  float* C2 = nullptr;
+  long long ldc2 = 0;
 };
 
 // Returns 0 or a HIP error code.
