@@ -744,10 +744,12 @@ int dense_direct(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
       if (small && g.B2) return launch_dl<64, 64, 4, 8, 3, 6, EPI_SWIGLU>(g, st);
       return small ? launch_dl<64, 64, 4, 8, 4, 8, EPI_SWIGLU>(g, st)
                    : launch_dl<128, 128, 4, 8, 3, 4, EPI_SWIGLU>(g, st);
+    // small M: 64x32 tiles of four waves (one 16x32 strip each), 256
+    // workgroups at N = 2048, rings of 6 stages (72 KB)
     case EPI_RESID:
-      return small ? -1 : launch_dl<64, 128, 2, 8, 3, 6, EPI_RESID>(g, st);
+      return small ? launch_dl<64, 32, 4, 4, 6, 6, EPI_RESID>(g, st) : launch_dl<64, 128, 2, 8, 3, 6, EPI_RESID>(g, st);
     case EPI_F32:
-      return small ? -1 : launch_dl<64, 128, 2, 8, 3, 6, EPI_F32>(g, st);
+      return small ? launch_dl<64, 32, 4, 4, 6, 6, EPI_F32>(g, st) : launch_dl<64, 128, 2, 8, 3, 6, EPI_F32>(g, st);
     default:
       return -1;
   }
