@@ -543,11 +543,12 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
     else return B7;
   };
 
-  // tiles of the second product (B2, fp32 out) come first, then the main ones
+  // tiles of the second product (B2, fp32 out; compiled into the SwiGLU
+  // kernels only) come first, then the main ones
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int tile0 = xcd * per_xcd + slot, aux_tiles = tiles_m * tiles_n2;
+  const int tile0 = xcd * per_xcd + slot, aux_tiles = EPI == EPI_SWIGLU ? tiles_m * tiles_n2 : 0;
   if (slot >= per_xcd || tile0 >= aux_tiles + tiles_m * tiles_n) return;  // uniform over the workgroup
-  const bool aux = tile0 < aux_tiles;
+  const bool aux = EPI == EPI_SWIGLU && tile0 < aux_tiles;
   const int tile = aux ? tile0 : tile0 - aux_tiles;
   const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
   // the wave index is uniform: keep it (and the LDS block offsets) scalar
@@ -698,7 +699,7 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
 template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT = 32>
 int launch_dl(const GemmArgs& g, hipStream_t st) {
   if (g.K != 64 * KT || g.lda % 8 || g.ldb % 8) return int(hipErrorInvalidValue);
-  if (g.B2 && (g.ldb2 % 8 || !g.C2 || g.N2 <= 0)) return int(hipErrorInvalidValue);
+  if (g.B2 && (EPI != EPI_SWIGLU || g.ldb2 % 8 || !g.C2 || g.N2 <= 0)) return int(hipErrorInvalidValue);
   const int bn_out = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + bn_out - 1) / bn_out;
   const int tiles_n2 = g.B2 ? (g.N2 + BN - 1) / BN : 0;
