@@ -41,6 +41,16 @@ MEASURED_TRAFFIC = {
 }
 
 
+def router_in_shared(cfg) -> bool:
+    """Whether the library computes the router logits inside the shared
+    gate/up launch: bf16 activations and shared weights, K = d_model = 2048,
+    at most 384 tokens, d_shared >= 1024 (the direct-load kernel's small-M
+    SwiGLU shape)."""
+    T = cfg.batch * cfg.canvas_len
+    return (cfg.act_dtype == "bf16" and cfg.expert_dtype == "bf16" and cfg.d_model == 2048
+            and T <= 384 and cfg.d_shared >= 1024)
+
+
 def algorithmic(cfg, kernel: str):
     """(bytes, flops) one timed launch of `kernel` must move/perform, per layer and step
     (per step for the LM head and the commit).  Weights are read once; activations
@@ -64,11 +74,17 @@ def algorithmic(cfg, kernel: str):
                 4.0 * cfg.batch * cfg.canvas_len * keys * A)
     if kernel == "qkv":
         return 3 * A * d * ab + T * d * ab + 3 * T * A * ab, 2.0 * T * 3 * A * d
-    if kernel == "shared":  # gate/up + SwiGLU, then down (fp32 out): one timed pair
+    # router logits: E x d weights, fp32 logits out; in the shared gate/up
+    # launch when router_in_shared(cfg), else a launch of their own
+    rl_bytes, rl_flops = E * d * ab + T * E * 4, 2.0 * T * E * d
+    fused = router_in_shared(cfg)
+    if kernel == "shared":  # gate/up + SwiGLU (+ router logits), then down (fp32 out)
         w = 3 * ds * d * wb + (3 * ds * 4 if wb == 1 else 0)
-        return w + T * d * ab + 2 * T * ds * ab + T * d * 4, 2.0 * T * 3 * ds * d
-    if kernel == "router":  # router GEMM (fp32 logits) + top-k
-        return E * d * ab + T * d * ab + 2 * T * E * 4 + 2 * T * k * 4, 2.0 * T * E * d
+        b, f = w + T * d * ab + 2 * T * ds * ab + T * d * 4, 2.0 * T * 3 * ds * d
+        return (b + rl_bytes, f + rl_flops) if fused else (b, f)
+    if kernel == "router":  # top-k over the logits (+ the router GEMM when it runs alone)
+        b = T * E * 4 + 2 * T * k * 4
+        return (b, 0.0) if fused else (b + rl_bytes + T * d * ab, rl_flops)
     if kernel == "commit":
         return T * (4 + 4 + 4 + 1) * 2, 0.0
     raise ValueError(kernel)
