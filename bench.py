@@ -185,7 +185,7 @@ def time_loop(cfg, canvases: int, warmup: int):
     free_gpu()
     toks = cfg.batch * cfg.canvas_len * canvases
     log(f"[bench] {cfg.name}: {canvases} canvases x batch {cfg.batch}, {steps} steps in {dt:.3f} s")
-    return {"workload": cfg.name, "batch": cfg.batch, "prompt_kv": cfg.prompt_len,
+    return {"workload": cfg.name, "batch": cfg.batch, "canvas": cfg.canvas_len, "prompt_kv": cfg.prompt_len,
             "canvas_tokens_per_s": toks / dt, "denoise_steps_per_s": steps / dt,
             "ms_per_denoise_step": dt / steps * 1e3, "denoise_steps_per_canvas": steps / canvases}
 
@@ -391,6 +391,9 @@ def main():
     if not args.no_extra and args.config == "c2":
         out["batch4"] = time_loop(get_config("c3"), canvases=1, warmup=1)
         out["batch8"] = time_loop(get_config("c5"), canvases=1, warmup=1)
+        # the canvas-length variant: one 512-position canvas over the same prompt
+        out["canvas512"] = time_loop(get_config("c2").replace(name="c2_canvas512", canvas_len=512),
+                                     canvases=1, warmup=1)
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
     print(json.dumps(out), flush=True)
 

@@ -176,6 +176,21 @@ def test_batch8_full_width_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_canvas512_full_width_one_step(rt):
+    """A 512-position canvas at full width (the canvas-length variant): 512
+    tokens take the large-M projection tiles, the attention two 256-query
+    tiles per head over 2048 prompt rows; a short vocabulary keeps the
+    oracle's LM head quick."""
+    cfg = get_config("c2").replace(name="canvas512_1_layer", n_layers=1, canvas_len=512, vocab=8192)
+    say("canvas 512, full width, 1 layer, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_c1_step_is_deterministic(rt):
     """Two runs of the same step give bitwise identical entropy, argmax and canvas."""
     cfg = get_config("c1")
