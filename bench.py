@@ -391,6 +391,10 @@ def main():
     if not args.no_extra and args.config == "c2":
         out["batch4"] = time_loop(get_config("c3"), canvases=1, warmup=1)
         out["batch8"] = time_loop(get_config("c5"), canvases=1, warmup=1)
+        # the absorbing-state (mask) noise variant: same model, [MASK] = the last id
+        c2 = get_config("c2")
+        out["absorbing"] = time_loop(c2.replace(name="c2_absorbing", mask_token=c2.vocab - 1),
+                                     canvases=1, warmup=1)
         # the canvas-length variant: one 512-position canvas over the same prompt
         out["canvas512"] = time_loop(get_config("c2").replace(name="c2_canvas512", canvas_len=512),
                                      canvases=1, warmup=1)

@@ -28,7 +28,7 @@ class dg_config(ctypes.Structure):
                 ("d_expert", c_int32), ("d_shared", c_int32), ("vocab", c_int32),
                 ("canvas_len", c_int32), ("max_steps", c_int32), ("rope_theta", c_float),
                 ("rms_eps", c_float), ("commit_threshold", c_float), ("act_dtype", c_int32),
-                ("expert_dtype", c_int32)]
+                ("expert_dtype", c_int32), ("mask_token", c_int32)]
 
 
 class dg_layer_weights(ctypes.Structure):

@@ -151,6 +151,8 @@ int check_config(const dg_config& c) {
   if (c.canvas_len > 1024) return fail(DG_ERR_SHAPE, "canvas_len must be <= 1024");
   if (!(c.rope_theta >= 0.f) || !(c.rms_eps >= 0.f))
     return fail(DG_ERR_INVALID_ARG, "rope_theta and rms_eps must be >= 0");
+  if (c.mask_token < -1 || c.mask_token >= c.vocab)
+    return fail(DG_ERR_INVALID_ARG, "mask_token %d must be -1 (uniform noise) or a vocabulary id", c.mask_token);
   return DG_OK;
 }
 
@@ -342,7 +344,7 @@ int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* o
   {
     ProfScope ps(m, DG_PROF_COMMIT, st);
     HIP_OK(commit_renoise(H, am, c->tokens, c->committed, B, N, c->step, cfg.max_steps,
-                          cfg.commit_threshold, c->seed, c->block, cfg.vocab, m->n_unc, st));
+                          cfg.commit_threshold, c->seed, c->block, cfg.vocab, cfg.mask_token, m->n_unc, st));
   }
   if (out && out->n_uncommitted)
     HIP_OK(hipMemcpyAsync(out->n_uncommitted, m->n_unc, sizeof(int) * B, hipMemcpyDeviceToDevice, st));
@@ -474,7 +476,7 @@ int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream) {
   int s = check_canvas(m, c);
   if (s) return s;
   HIP_OK(canvas_init(c->tokens, c->committed, c->batch, m->cfg.canvas_len, c->seed, c->block,
-                     m->cfg.vocab, (hipStream_t)stream));
+                     m->cfg.vocab, m->cfg.mask_token, (hipStream_t)stream));
   c->step = 0;
   return DG_OK;
 }
@@ -611,7 +613,7 @@ int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_
   if (s) return s;
   if (c->step < 0 || c->step >= m->cfg.max_steps) return fail(DG_ERR_STATE, "step out of range");
   HIP_OK(commit_renoise(entropy, argmax, c->tokens, c->committed, c->batch, m->cfg.canvas_len, c->step,
-                        m->cfg.max_steps, m->cfg.commit_threshold, c->seed, c->block, m->cfg.vocab,
+                        m->cfg.max_steps, m->cfg.commit_threshold, c->seed, c->block, m->cfg.vocab, m->cfg.mask_token,
                         n_uncommitted, (hipStream_t)stream));
   return DG_OK;
 }

@@ -273,11 +273,12 @@ __global__ void prefill_kernel(int* tok, uint8_t* committed, int n, const int* g
 }
 
 __global__ void canvas_init_kernel(int* tok, uint8_t* committed, int N, uint64_t seed, uint32_t block,
-                                   int vocab) {
+                                   int vocab, int mask_token) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
-  tok[b * N + i] = int(canvas_draw(seed, uint32_t(i), 0u, uint32_t(b), block, uint32_t(vocab)));
+  tok[b * N + i] = mask_token >= 0 ? mask_token
+                                   : int(canvas_draw(seed, uint32_t(i), 0u, uint32_t(b), block, uint32_t(vocab)));
   committed[b * N + i] = 0;
 }
 
@@ -297,7 +298,8 @@ __device__ __forceinline__ unsigned long long commit_key(float h, int i) {
 __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int* am, int* tok,
                                                       uint8_t* committed, int N, int step,
                                                       int max_steps, float threshold, uint64_t seed,
-                                                      uint32_t block, int vocab, int* n_unc) {
+                                                      uint32_t block, int vocab, int mask_token,
+                                                      int* n_unc) {
   __shared__ unsigned long long ks[1024];
   __shared__ int part_s[1024];
   __shared__ int red[16];
@@ -339,8 +341,9 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int*
   if ((t & 63) == 0) red[t >> 6] = c2;
   __syncthreads();
   if (still)
-    tok[base + i] =
-        int(canvas_draw(seed, uint32_t(i), uint32_t(step + 1), uint32_t(b), block, uint32_t(vocab)));
+    tok[base + i] = mask_token >= 0 ? mask_token
+                                    : int(canvas_draw(seed, uint32_t(i), uint32_t(step + 1), uint32_t(b), block,
+                                                      uint32_t(vocab)));
   if (t == 0) {
     int Up = 0;
     for (int w = 0; w < 16; ++w) Up += red[w];
@@ -433,9 +436,9 @@ int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const
 }
 
 int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block, int vocab,
-                hipStream_t st) {
+                int mask_token, hipStream_t st) {
   hipLaunchKernelGGL(canvas_init_kernel, dim3((N + 255) / 256, B), dim3(256), 0, st, tok, committed, N,
-                     seed, block, vocab);
+                     seed, block, vocab, mask_token);
   return int(hipGetLastError());
 }
 
@@ -446,11 +449,11 @@ int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const 
 }
 
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N, int step,
-                   int max_steps, float threshold, uint64_t seed, uint32_t block, int vocab, int* n_unc,
-                   hipStream_t st) {
+                   int max_steps, float threshold, uint64_t seed, uint32_t block, int vocab, int mask_token,
+                   int* n_unc, hipStream_t st) {
   if (N > 1024) return int(hipErrorInvalidValue);
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(1024), 0, st, H, am, tok, committed, N, step,
-                     max_steps, threshold, seed, block, vocab, n_unc);
+                     max_steps, threshold, seed, block, vocab, mask_token, n_unc);
   return int(hipGetLastError());
 }
 

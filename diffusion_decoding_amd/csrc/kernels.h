@@ -125,13 +125,15 @@ int moe_combine(ActType at, void* x, const float* y, const float* ys, const floa
 // moe_combine, then a = rmsnorm(x) of the updated rows (one fused kernel for bf16)
 int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
                      int T, int k, int d, float eps, void* a, hipStream_t st);
+// mask_token >= 0: absorbing-state noise (the canvas starts as [MASK] and
+// uncommitted positions return to it); -1: uniform Philox draws
 int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block,
-                int vocab, hipStream_t st);
+                int vocab, int mask_token, hipStream_t st);
 // tok[i] = given[i], committed[i] = 1 wherever mask[i] != 0 (i < n)
 int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const uint8_t* mask, hipStream_t st);
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N,
                    int step, int max_steps, float threshold, uint64_t seed, uint32_t block,
-                   int vocab, int* n_unc, hipStream_t st);
+                   int vocab, int mask_token, int* n_unc, hipStream_t st);
 int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uint32_t block,
                 uint32_t modulus, int n, uint32_t* out, hipStream_t st);
 

@@ -35,7 +35,7 @@ def make_config(cfg) -> dg_config:
     return dg_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_experts, cfg.top_k,
                      cfg.d_expert, cfg.d_shared, cfg.vocab, cfg.canvas_len, cfg.max_steps,
                      float(cfg.rope_theta), float(cfg.rms_eps), float(cfg.threshold),
-                     _DT[cfg.act_dtype], _DT[cfg.expert_dtype])
+                     _DT[cfg.act_dtype], _DT[cfg.expert_dtype], int(cfg.mask_token))
 
 
 def pack_experts(w: torch.Tensor, dtype: str, stream=None) -> torch.Tensor:

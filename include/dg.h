@@ -84,6 +84,12 @@ typedef struct dg_config {
   float commit_threshold;  /* nats: uncommitted positions with entropy below it commit */
   int32_t act_dtype;       /* DG_DTYPE_FP32 or DG_DTYPE_BF16 */
   int32_t expert_dtype;    /* FP32 (with act FP32), BF16 or FP8_E4M3 (with act BF16) */
+  int32_t mask_token;      /* -1: uniform-state noise (Philox draws, the method of the pages);
+                              0 .. vocab-1: absorbing-state (mask) noise with this [MASK] id --
+                              the canvas starts as all [MASK] and every uncommitted position is
+                              set back to [MASK] after each step (the masked-diffusion variant
+                              the pages contrast it with: DiffusionGemma深度拆解 (zhichai.net),
+                              "统一状态扩散 vs 掩码扩散"); nothing else changes */
 } dg_config;
 
 /* One layer's weights (device pointers, borrowed for the model's lifetime).

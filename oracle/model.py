@@ -320,15 +320,25 @@ def commit_select(H32, a, tok, committed, s: int, max_steps: int, threshold: flo
     return newly
 
 
-def canvas_init(seed: int, n: int, canvas: int, block: int, vocab: int):
+# Noise.  The method's own noise is uniform-state: every uncommitted position
+# gets a fresh uniform id.  The masked (absorbing-state) diffusion the pages
+# contrast it with (DiffusionGemma深度拆解 (zhichai.net), "统一状态扩散 vs
+# 掩码扩散": a token is either known or masked, and denoising reveals it) is
+# the variant selected by mask_token >= 0: the canvas starts as all [MASK]
+# and an uncommitted position goes back to [MASK] after each step.
+
+def canvas_init(seed: int, n: int, canvas: int, block: int, vocab: int, mask_token: int = -1):
+    if mask_token >= 0:
+        return np.full(n, mask_token, dtype=np.int64)
     return philox.canvas_draw(seed, np.arange(n), 0, canvas, block, vocab)
 
 
-def renoise(tok, committed, seed: int, s: int, canvas: int, block: int, vocab: int):
-    """Redraw every uncommitted position uniformly (counter step tag s + 1)."""
+def renoise(tok, committed, seed: int, s: int, canvas: int, block: int, vocab: int, mask_token: int = -1):
+    """Redraw every uncommitted position uniformly (counter step tag s + 1),
+    or set it to [MASK] under absorbing-state noise."""
     idx = np.nonzero(~np.asarray(committed, dtype=bool))[0]
     if idx.size:
-        tok[idx] = philox.canvas_draw(seed, idx, s + 1, canvas, block, vocab)
+        tok[idx] = mask_token if mask_token >= 0 else philox.canvas_draw(seed, idx, s + 1, canvas, block, vocab)
 
 
 # ----------------------------------------------------------------------------- step / loop
@@ -362,7 +372,8 @@ class StepResult:
 
 def init_state(cfg, seed: int, block: int = 0) -> CanvasState:
     B, N = cfg.batch, cfg.canvas_len
-    tok = np.stack([canvas_init(seed, N, b, block, cfg.vocab) for b in range(B)])
+    mt = getattr(cfg, "mask_token", -1)
+    tok = np.stack([canvas_init(seed, N, b, block, cfg.vocab, mt) for b in range(B)])
     return CanvasState(tok, np.zeros((B, N), dtype=bool), 0, seed, block)
 
 
@@ -432,7 +443,8 @@ def denoise_step(W: Weights, kv: KV, state: CanvasState, cfg, keep_logits: bool 
     if hook is not None:
         hook(res, state)
     for b in range(B):
-        renoise(state.tokens[b], state.committed[b], state.seed, s, b, state.block, cfg.vocab)
+        renoise(state.tokens[b], state.committed[b], state.seed, s, b, state.block, cfg.vocab,
+                getattr(cfg, "mask_token", -1))
     state.step = s + 1
     return res
 

@@ -177,6 +177,40 @@ def test_generate_canvas_matches_oracle_c0(rt):
     model.close()
 
 
+# ----------------------------------------------------------------------------- absorbing-state noise
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_absorbing_noise_step_locked(rt, act):
+    """The masked-diffusion variant: all-[MASK] start and re-masking of the
+    open positions, step-locked against the oracle (the canvas after every
+    step, re-masked positions included, must match bit for bit)."""
+    cfg = tiny_config(name=f"tiny_absorbing_{act}", act_dtype=act, expert_dtype=act, batch=2, seed=64,
+                      max_steps=5, mask_token=3, lm_scale=6.0 if act == "fp32" else 1.0,
+                      head_dim=32 if act == "bf16" else 16, n_heads=2)
+    say(f"absorbing-state noise, batch 2, {act}")
+    reps = _run_locked(rt, cfg)
+    _assert_reports(cfg, reps)
+
+
+def test_absorbing_generate_canvas_matches_oracle_c0(rt):
+    cfg = get_config("c0")
+    cfg = cfg.replace(name="c0_absorbing", mask_token=cfg.vocab - 1)   # [MASK]: the last id
+    say("c0 with absorbing-state noise: dg_generate_canvas vs oracle loop")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    assert (to_host(canvas.tokens) == cfg.mask_token).all()
+    steps = rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=False)
+    ost, osteps = om.generate_canvas(W, okv, cfg, cfg.seed)
+    assert steps == osteps
+    assert to_host(canvas.committed).all()
+    np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+    model.close()
+
+
 # ----------------------------------------------------------------------------- pre-committed positions
 
 def _fim(B, N, head, tail, vocab, seed):

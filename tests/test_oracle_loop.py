@@ -305,3 +305,56 @@ def test_block_generate_tiny():
     outs, steps = om.block_generate(W, kv, cfg, inp.prompt_tokens.numpy().astype(np.int64))
     assert kv.length == 8 + 3 * cfg.canvas_len
     assert len(outs) == 3 and all(1 <= s <= cfg.max_steps for s in steps)
+
+
+# ----------------------------------------------------------------------------- absorbing-state noise
+
+def test_absorbing_noise_masks_every_open_position():
+    """Masked-diffusion variant (a [MASK] id instead of uniform draws), with
+    the threshold off so the schedule runs to the cap: the canvas starts as all
+    [MASK], after every step each uncommitted position holds [MASK] again,
+    committed tokens never change and are that step's argmax, and each step
+    commits exactly ceil(U / (S_max - s))."""
+    cfg = tiny_config(batch=2, seed=61, mask_token=511, threshold=-math.inf)
+    inp, W, kv = _setup(cfg)
+    st = om.init_state(cfg, cfg.seed)
+    assert (st.tokens == 511).all() and not st.committed.any()
+    prev_tok, prev_com = st.tokens.copy(), st.committed.copy()
+    after = []
+    state, steps = om.generate_canvas(W, kv, cfg, cfg.seed, state=st,
+                                      step_hook=lambda res, s: after.append((s.tokens.copy(), s.committed.copy(), res)))
+    assert state.committed.all() and steps == cfg.max_steps == len(after)
+    for s, (tok, com, res) in enumerate(after):
+        assert (tok[~com] == 511).all()                                   # re-masked
+        np.testing.assert_array_equal(tok[prev_com], prev_tok[prev_com])  # locked
+        np.testing.assert_array_equal(com, prev_com | res.newly)
+        np.testing.assert_array_equal(tok[res.newly], res.argmax[res.newly])
+        for b in range(cfg.batch):
+            U = int((~prev_com[b]).sum())
+            assert res.newly[b].sum() == om.commit_count(U, s, cfg.max_steps)
+        prev_tok, prev_com = tok, com
+
+
+def test_absorbing_first_step_sees_identical_rows_without_rope():
+    """With RoPE off and every position holding [MASK], every canvas row is the
+    same input, so the first step gives every position the same prediction
+    and commits exactly ceil(N / S_max) of them (threshold off), all with that
+    token."""
+    cfg = tiny_config(rope_theta=0.0, threshold=-math.inf, seed=62, mask_token=7)
+    inp, W, kv = _setup(cfg)
+    st = om.init_state(cfg, cfg.seed)
+    res = om.denoise_step(W, kv, st, cfg)
+    H, a = res.entropy[0], res.argmax[0]
+    assert (a == a[0]).all()
+    np.testing.assert_allclose(H, H[0], rtol=1e-9)
+    m = om.commit_count(cfg.canvas_len, 0, cfg.max_steps)
+    assert res.newly[0].sum() == m == math.ceil(cfg.canvas_len / cfg.max_steps)
+    assert (st.tokens[0][res.newly[0]] == a[0]).all()
+    assert (st.tokens[0][~res.newly[0]] == 7).all()
+
+
+def test_uniform_noise_is_the_default():
+    cfg = tiny_config(seed=63)
+    assert cfg.mask_token == -1
+    st = om.init_state(cfg, cfg.seed)
+    np.testing.assert_array_equal(st.tokens[0], om.canvas_init(cfg.seed, cfg.canvas_len, 0, 0, cfg.vocab))

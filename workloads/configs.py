@@ -39,6 +39,7 @@ class Config:
     threshold: float = 1.0   # nats; uncommitted positions below it commit at once
     n_canvases: int = 1      # canvases generated one after another (block-AR)
     prompt_mode: str = "kv"  # "kv": random post-RoPE K,V; "tokens": ids encoded by a causal pass
+    mask_token: int = -1     # -1: uniform-state noise; a vocabulary id: absorbing-state ([MASK]) noise
 
     @property
     def qkv_dim(self) -> int:
