@@ -123,8 +123,12 @@ struct MoeArgs {
 };
 
 constexpr int ROUTE_MAX_TOKENS = 2048;
-// static LDS of the routing lists (tok, slot, flag, red) in the gate/up kernel
-constexpr int ROUTE_LDS = ROUTE_MAX_TOKENS * (4 + 1 + 1) + 16;
+constexpr int ROUTE_MAX_EXPERTS = 256;
+// static LDS of the routing lists (tok, slot, flag, hist, red) in the gate/up kernel
+constexpr int ROUTE_LDS = ROUTE_MAX_TOKENS * (4 + 1 + 1) + ROUTE_MAX_EXPERTS * 4 + 16;
+// static LDS of a routed kernel besides the routing lists (gate/up: the
+// largest pair count, one word; 16 bytes are reserved)
+constexpr int KERNEL_LDS = 16;
 
 // The routing of one expert e from the top-k ids: pairs of experts below e
 // (its pair offset), and its tokens in ascending order with the slot j that
@@ -133,10 +137,13 @@ constexpr int ROUTE_LDS = ROUTE_MAX_TOKENS * (4 + 1 + 1) + 16;
 struct ExpertRoute {
   int off, cnt;
 };
+// With hist non-null it also counts the pairs of every expert (hist[0..E)).
 __device__ __forceinline__ ExpertRoute route_expert(const MoeArgs& a, int e, int* tok, unsigned char* slot,
-                                                    signed char* flag, int* red) {
+                                                    signed char* flag, int* red, int* hist, int E) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if (tid == 0) red[0] = 0;
+  if (hist)
+    for (int x = tid; x < E; x += nt) hist[x] = 0;
   __syncthreads();
   int less = 0;
   for (int t = tid; t < a.T; t += nt) {
@@ -145,6 +152,7 @@ __device__ __forceinline__ ExpertRoute route_expert(const MoeArgs& a, int e, int
       const int id = a.ids[t * a.k + j];
       less += id < e;
       m = id == e ? j : m;
+      if (hist) atomicAdd(&hist[id], 1);  // integer counts: order-free
     }
     flag[t] = (signed char)m;
   }
@@ -443,61 +451,47 @@ __device__ __forceinline__ void moe_gu_chunked(const MoeArgs& a, bf16* xs, WStre
 // w of it owns 16 NB of them.  The expert's pairs go in passes of up to
 // 16 MTP tokens, each pass staging its tokens in LDS and streaming the wave's
 // weights once.
+// Gate/up: a workgroup runs the first OWN_PASSES passes of its own expert;
+// further passes (an expert holding most of the tokens, as when every open
+// position of an absorbing-noise canvas is the same [MASK] token) are spread
+// over all workgroups of the grid in a fixed order (pass index, then expert,
+// then row range), so they run side by side instead of one after another.
+// Each pass is computed by exactly one workgroup with the same arithmetic:
+// the results do not depend on which one.
+constexpr int OWN_PASSES = 2;
+// pairs of expert x: from the in-kernel histogram, else from the offsets
+__device__ __forceinline__ int pairs_of(int x, const int* hist, const int* off) {
+  return hist ? hist[x] : off[x + 1] - off[x];
+}
+// Item j of the further passes, ordered by pass index p >= OWN_PASSES, then
+// expert, then row range x2 (splits per expert): returns the expert, or -1
+// past the last item.  Uniform over the workgroup.
+__device__ __forceinline__ int further_pass(int j, int maxc, int PS, int E, int splits, const int* hist,
+                                            const int* off, int& p, int& x2) {
+  int base = 0;
+  for (p = OWN_PASSES; p * PS < maxc; ++p)
+    for (int x = 0; x < E; ++x) {
+      if (pairs_of(x, hist, off) <= p * PS) continue;
+      if (j < base + splits) {
+        x2 = j - base;
+        return x;
+      }
+      base += splits;
+    }
+  return -1;
+}
 template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC>
 __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   static_assert(KC == 0 || (GU && MD == 1), "chunked staging is the gate/up path with one stage in flight");
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
   const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
-  const int e = blockIdx.y;
-  const int n0 = blockIdx.x * rows_per_wg + (threadIdx.x >> 6) * 16 * NB;
-  const bool active = n0 < min(a.Nout, (blockIdx.x + 1) * rows_per_wg);
-  WStream<WL, GU, NB, MD> ws;
-  ws.init(a, e, n0);
-  if (active) ws.fill();  // the first weight tiles are in flight during the routing and staging
-  int pbeg, pcnt;
-  // token rows: pair p of the expert (p = 0 .. pcnt-1) is X row gather[gbase + p],
-  // or X row pbeg + p without a gather list (down: X holds one row per pair)
-  const int* gather = nullptr;
-  int gbase = 0;
-  if constexpr (GU) {
-    __shared__ int tok[ROUTE_MAX_TOKENS];
-    __shared__ unsigned char slot[ROUTE_MAX_TOKENS];
-    __shared__ signed char flag[ROUTE_MAX_TOKENS];
-    __shared__ int red[2];
-    if (a.ids) {
-      const ExpertRoute r = route_expert(a, e, tok, slot, flag, red);
-      pbeg = r.off;
-      pcnt = r.cnt;
-      gather = tok;
-      gbase = 0;
-      if (blockIdx.x == 0) {
-        for (int i = threadIdx.x; i < pcnt; i += blockDim.x) {
-          a.pair_row_out[pbeg + i] = tok[i];
-          a.pos_out[tok[i] * a.k + slot[i]] = pbeg + i;
-        }
-        if (threadIdx.x == 0) {
-          a.off_out[e] = pbeg;
-          if (e == (int)gridDim.y - 1) a.off_out[e + 1] = pbeg + pcnt;
-        }
-      }
-    } else {
-      pbeg = a.off[e];
-      pcnt = a.off[e + 1] - pbeg;
-      gather = a.pair_row;
-      gbase = pbeg;
-    }
-  } else {
-    pbeg = a.off[e];
-    pcnt = a.off[e + 1] - pbeg;
-    gbase = pbeg;
-  }
-  if (pcnt <= 0) return;  // uniform over the workgroup; nothing was staged
-  for (int p0 = 0; p0 < pcnt; p0 += 16 * MTP) {
-    const int rows = min(16 * MTP, pcnt - p0);
-    if (p0) {
-      __syncthreads();        // the previous pass is done with xs
-      if (active) ws.fill();  // the next pass streams the weights again
-    }
+  constexpr int PS = 16 * MTP;  // pairs per pass
+  const int wave = threadIdx.x >> 6;
+  // pass rows p0 .. p0 + rows - 1 of expert e; pair p of the expert is X row
+  // gather[gbase + p], or X row gbase + p without a gather list (down: X
+  // holds one row per pair)
+  auto run_pass = [&](WStream<WL, GU, NB, MD>& ws, bool active, int e, int n0, int pbeg, int p0, int rows,
+                      const int* gather, int gbase) {
     if constexpr (KC > 0) {
       const int gi = gbase + p0, pb = pbeg + p0;
       if (rows <= 16) moe_gu_chunked<WL, NB, 1, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
@@ -515,6 +509,107 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
         else moe_wave<WL, GU, NB, MD, MTP>(a, xs, pitch, ws, e, n0, pbeg + p0, rows);
       }
     }
+  };
+
+  const int e = blockIdx.y;
+  const int n0 = blockIdx.x * rows_per_wg + wave * 16 * NB;
+  const bool active = n0 < min(a.Nout, (blockIdx.x + 1) * rows_per_wg);
+  WStream<WL, GU, NB, MD> ws;
+  ws.init(a, e, n0);
+  if (active) ws.fill();  // the first weight tiles are in flight during the routing and staging
+
+  // wave 0: the most pairs any expert has (read after the next barrier)
+  __shared__ int maxc_s;
+  auto most_pairs = [&](const int* hist) {
+    if (wave == 0) {
+      int mx = 0;
+      for (int x = threadIdx.x; x < (int)gridDim.y; x += 64) mx = max(mx, pairs_of(x, hist, a.off));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+      if (threadIdx.x == 0) maxc_s = mx;
+    }
+  };
+
+  if constexpr (GU) {
+    __shared__ int tok[ROUTE_MAX_TOKENS];
+    __shared__ unsigned char slot[ROUTE_MAX_TOKENS];
+    __shared__ signed char flag[ROUTE_MAX_TOKENS];
+    __shared__ int hist[ROUTE_MAX_EXPERTS];  // pairs per expert (routing in the kernel)
+    __shared__ int red[2];
+    const int E = gridDim.y;
+    int pbeg, pcnt;
+    const int* gather;
+    int gbase;
+    if (a.ids) {
+      const ExpertRoute r = route_expert(a, e, tok, slot, flag, red, hist, E);
+      pbeg = r.off;
+      pcnt = r.cnt;
+      gather = tok;
+      gbase = 0;
+      if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < pcnt; i += blockDim.x) {
+          a.pair_row_out[pbeg + i] = tok[i];
+          a.pos_out[tok[i] * a.k + slot[i]] = pbeg + i;
+        }
+        if (threadIdx.x == 0) {
+          a.off_out[e] = pbeg;
+          if (e == E - 1) a.off_out[e + 1] = pbeg + pcnt;
+        }
+      }
+    } else {
+      pbeg = a.off[e];
+      pcnt = a.off[e + 1] - pbeg;
+      gather = a.pair_row;
+      gbase = pbeg;
+    }
+    const int* hp = a.ids ? hist : nullptr;
+    most_pairs(hp);
+    for (int p0 = 0; p0 < min(pcnt, OWN_PASSES * PS); p0 += PS) {
+      if (p0) {
+        __syncthreads();        // the previous pass is done with xs
+        if (active) ws.fill();  // the next pass streams the weights again
+      }
+      run_pass(ws, active, e, n0, pbeg, p0, min(PS, pcnt - p0), gather, gbase);
+    }
+    __syncthreads();  // maxc_s is visible; the own passes are done with xs and the lists
+    const int maxc = maxc_s;
+    if (maxc <= OWN_PASSES * PS) return;  // uniform: no expert has further passes
+    const int W = gridDim.x * gridDim.y, wg = blockIdx.y * gridDim.x + blockIdx.x;
+    for (int j = wg;; j += W) {
+      int p, x2;
+      const int e2 = further_pass(j, maxc, PS, E, gridDim.x, hp, a.off, p, x2);
+      if (e2 < 0) return;  // uniform: every further pass is taken
+      const int n2 = x2 * rows_per_wg + wave * 16 * NB;
+      const bool act2 = n2 < min(a.Nout, (x2 + 1) * rows_per_wg);
+      ws.init(a, e2, n2);
+      if (act2) ws.fill();
+      int pb2, gb2;
+      const int* g2;
+      if (a.ids) {
+        pb2 = route_expert(a, e2, tok, slot, flag, red, nullptr, E).off;
+        g2 = tok;
+        gb2 = 0;
+      } else {
+        pb2 = a.off[e2];
+        g2 = a.pair_row;
+        gb2 = pb2;
+      }
+      run_pass(ws, act2, e2, n2, pb2, p * PS, min(PS, pairs_of(e2, hp, a.off) - p * PS), g2, gb2);
+      __syncthreads();  // this pass is done with xs and the lists
+    }
+  } else {
+    // down: each workgroup runs every pass of its own expert (its 2048-odd
+    // workgroups already queue behind one another; spreading the further
+    // passes over them measured slower)
+    const int pbeg = a.off[e], pcnt = a.off[e + 1] - pbeg;
+    if (pcnt <= 0) return;  // uniform over the workgroup; nothing was staged
+    for (int p0 = 0; p0 < pcnt; p0 += PS) {
+      if (p0) {
+        __syncthreads();        // the previous pass is done with xs
+        if (active) ws.fill();  // the next pass streams the weights again
+      }
+      run_pass(ws, active, e, n0, pbeg, p0, min(PS, pcnt - p0), nullptr, pbeg);
+    }
   }
 }
 
@@ -526,11 +621,11 @@ int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
   const size_t lds = KC > 0 ? size_t(2 * 16 * MTP) * (KC + 16) * sizeof(bf16)
                             : size_t(16 * MTP) * (a.K + 16) * sizeof(bf16);
-  if (lds + (GU ? ROUTE_LDS : 0) > 160 * 1024) return int(hipErrorInvalidValue);  // + the routing lists
+  if (lds + (GU ? ROUTE_LDS : 0) + KERNEL_LDS > 160 * 1024) return int(hipErrorInvalidValue);  // + static LDS
   // once per kernel (not inside a graph capture): the largest dynamic LDS any launch may ask for
   static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     160 * 1024 - (GU ? ROUTE_LDS : 0));
+                                                     160 * 1024 - (GU ? ROUTE_LDS : 0) - KERNEL_LDS);
   if (attr != hipSuccess) return int(attr);
   hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);
@@ -561,7 +656,7 @@ int launch(bool gu, const MoeArgs& a, int E, int pairs, hipStream_t st) {
   // workgroup), so a workgroup's 96 staged token rows (138 KB of LDS, one
   // workgroup per CU) feed twice the weight stream: 86.8 against 100.7 us at
   // 1024 tokens x 8 slots over 128 experts (16 outputs per wave)
-  if (pairs > 24 * E && size_t(96) * (a.K + 16) * sizeof(bf16) <= 160 * 1024)
+  if (pairs > 24 * E && size_t(96) * (a.K + 16) * sizeof(bf16) + KERNEL_LDS <= 160 * 1024)
     return launch_k<WL, false, 2, 4, 512, 6>(a, E, ((a.Nout + 31) / 32 + 7) / 8, st);
   const int blocks = (a.Nout + 15) / 16;
   const int split = (blocks + 7) / 8;
@@ -624,7 +719,8 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
   if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
   MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
   if (route) {
-    if (!gate_up || route->T > ROUTE_MAX_TOKENS || route->k > 8) return int(hipErrorInvalidValue);
+    if (!gate_up || route->T > ROUTE_MAX_TOKENS || route->k > 8 || E > ROUTE_MAX_EXPERTS)
+      return int(hipErrorInvalidValue);
     pairs = route->T * route->k;
     a.ids = route->ids;
     a.T = route->T;
