@@ -258,15 +258,19 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     if (at != ACT_BF16) HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
   }
   if (at == ACT_BF16) {
+    // Absorbing-state noise: every open position holds the same [MASK] token,
+    // so the open rows pile onto a few experts; the pooled kernels' 96-token
+    // passes stream a heavy expert's weights a third as often.
+    const int pairs = m->cfg.mask_token >= 0 ? std::max(T * k, 24 * E + 1) : T * k;
     {
       ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU, routing in the kernel
       const MoeRoute route{m->topk_ids, T, k, m->off, m->pair_row, m->pos};
-      HIP_OK(moe_experts(m->wt, true, m->a, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, m->h, st, &route));
+      HIP_OK(moe_experts(m->wt, true, m->a, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, m->h, st, &route, pairs));
     }
     {
       ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down
       HIP_OK(moe_experts(m->wt, false, m->h, m->pair_row, m->off, E, w.w_d, w.s_d, de, d, m->y, st, nullptr,
-                         T * k));
+                         pairs));
     }
   } else {
     {

@@ -721,7 +721,7 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
   if (route) {
     if (!gate_up || route->T > ROUTE_MAX_TOKENS || route->k > 8 || E > ROUTE_MAX_EXPERTS)
       return int(hipErrorInvalidValue);
-    pairs = route->T * route->k;
+    pairs = max(pairs, route->T * route->k);
     a.ids = route->ids;
     a.T = route->T;
     a.k = route->k;

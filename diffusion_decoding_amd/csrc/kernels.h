@@ -81,7 +81,8 @@ struct MoeRoute {
   int* pair_row;
   int* pos;
 };
-// pairs: T * k (sizes the token passes; 0 = few pairs per expert).
+// pairs: T * k (sizes the token passes; 0 = few pairs per expert); with a
+// route, the larger of this and route->T * route->k.
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
                 const MoeRoute* route = nullptr, int pairs = 0);
