@@ -191,6 +191,21 @@ def test_canvas512_full_width_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_absorbing_full_width_two_steps(rt):
+    """Absorbing-state noise at full width: on the first step every position is
+    the same [MASK] token, so all 256 rows route to the same experts -- the
+    pooled routed kernels' 96-token passes, and a third pass of those experts
+    spread over the grid; a short vocabulary keeps the oracle quick."""
+    cfg = get_config("c2").replace(name="absorbing_1_layer", n_layers=1, vocab=8192, mask_token=8191)
+    say("absorbing-state noise, full width, 1 layer, two steps")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=2)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_c1_step_is_deterministic(rt):
     """Two runs of the same step give bitwise identical entropy, argmax and canvas."""
     cfg = get_config("c1")
