@@ -65,3 +65,40 @@ def test_invalid_arguments_are_rejected_before_any_launch():
     lib = _lib.load()
     assert lib.dg_denoise_step(None, None, None, None, None) == -1
     assert lib.dg_commit_canvas(None, None, 0, None, None) == -1
+
+
+STRUCTS = ["dg_config", "dg_layer_weights", "dg_weights", "dg_kv", "dg_canvas", "dg_step_out"]
+
+
+def _c_layout(tmp_path):
+    """Size and field offsets of every ABI struct, as the C compiler lays out
+    include/dg.h (a small program built with gcc here)."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    from diffusion_decoding_amd import _lib
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dg.h"', "int main(void) {"]
+    for name in STRUCTS:
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in getattr(_lib, name)._fields_:
+            lines.append(f'  printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
+    lines += ["  return 0;", "}"]
+    src, exe = tmp_path / "layout.c", tmp_path / "layout"
+    src.write_text("\n".join(lines) + "\n")
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    return {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """Every struct the binding passes across the ABI has the header's size and
+    field offsets (a field added on one side only fails here)."""
+    from diffusion_decoding_amd import _lib
+    c = _c_layout(tmp_path)
+    for name in STRUCTS:
+        cls = getattr(_lib, name)
+        assert c[(name, "size")] == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert c[(name, field)] == getattr(cls, field).offset, (name, field)
