@@ -62,6 +62,11 @@ def test_invalid_arguments_are_rejected_before_any_launch():
     with pytest.raises(_lib.DGError) as e:
         _lib.dg_model_create(bad, w, 1, 0, 0)
     assert e.value.status == -2
+    for mt in (512, -2):  # the [MASK] id must be a vocabulary id (c0: 512 ids) or -1
+        bad = make_config(get_config("c0").replace(mask_token=mt))
+        with pytest.raises(_lib.DGError) as e:
+            _lib.dg_model_create(bad, w, 1, 0, 0)
+        assert e.value.status == -1 and "mask_token" in str(e.value)
     lib = _lib.load()
     assert lib.dg_denoise_step(None, None, None, None, None) == -1
     assert lib.dg_commit_canvas(None, None, 0, None, None) == -1
