@@ -616,8 +616,10 @@ int launch_bf16_nw(const AttnArgs& a, hipStream_t st) {
   const int n_qt = (a.n + 16 * NW - 1) / (16 * NW);
   const int items = a.B * a.H * a.splits * n_qt;
   const int per_xcd = (items + 7) / 8;
+  // eight-wave tiles keep two K/V tiles in flight (the four-wave kernel would
+  // spill at that depth)
   if (a.len1 == 0 || a.len0 % 64 == 0)  // no key tile spans both segments
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, true, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, NW == 8 ? 2 : 1, true, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
                        per_xcd);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, false, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
