@@ -78,6 +78,7 @@ class Weights:
         self.inp = inputs
         self.cfg = inputs.cfg
         self._cache = {} if cache else None
+        self._embed_host = None
 
     def _get(self, key, fn):
         if self._cache is None:
@@ -86,9 +87,30 @@ class Weights:
             self._cache[key] = fn()
         return self._cache[key]
 
+    def embed_table(self) -> torch.Tensor:
+        """Host copy of the embedding table (made once; every gather runs on the CPU)."""
+        if self._embed_host is None:
+            self._embed_host = self.inp.embed.detach().to("cpu")
+        return self._embed_host
+
     def embed_rows(self, tok) -> np.ndarray:
-        idx = torch.as_tensor(np.asarray(tok, dtype=np.int64)).to(self.inp.embed.device)
-        return _np64(self.inp.embed.index_select(0, idx.reshape(-1))).reshape(*np.shape(tok), -1)
+        idx = torch.from_numpy(np.asarray(tok, dtype=np.int64).reshape(-1))
+        return _np64(self.embed_table().index_select(0, idx)).reshape(*np.shape(tok), -1)
+
+    def prefetch(self, layers: int):
+        """Convert the weights of the first ``layers`` layers, the LM head and the
+        embedding table ahead of time (needs ``cache=True``), so that a timed
+        oracle run measures its arithmetic, not the weight conversion."""
+        if self._cache is None:
+            raise ValueError("prefetch needs a caching Weights (cache=True)")
+        self.embed_table()
+        for l in range(layers):
+            for name in ("wqkv", "wo", "wr", "ws_gu", "ws_d"):
+                self.dense(l, name)
+            for e in range(self.cfg.n_experts):
+                self.expert(l, e)
+        for _ in self.lm_head_chunks():
+            pass
 
     def lm_head_chunks(self, chunk: int = 16384):
         V = self.cfg.vocab
