@@ -14,6 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdg.so")
 
 DG_DTYPE_FP32, DG_DTYPE_BF16, DG_DTYPE_FP8_E4M3 = 0, 1, 2
+DG_STATUS_NONFINITE, DG_STATUS_TOKEN = 1, 2
+DG_ERR_INVALID_ARG, DG_ERR_SHAPE, DG_ERR_NUMERIC = -1, -2, -6
 
 
 class DGError(RuntimeError):
@@ -53,7 +55,8 @@ class dg_canvas(ctypes.Structure):
 
 class dg_step_out(ctypes.Structure):
     _fields_ = [("entropy", c_void_p), ("argmax", c_void_p), ("top2_gap", c_void_p),
-                ("n_uncommitted", c_void_p), ("logits", c_void_p), ("hidden", c_void_p)]
+                ("n_uncommitted", c_void_p), ("logits", c_void_p), ("hidden", c_void_p),
+                ("status", c_void_p)]
 
 
 _SIGS = {
@@ -74,6 +77,15 @@ _SIGS = {
                        c_void_p, c_void_p],
     "dg_test_lm_head": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     "dg_test_commit": [c_void_p, POINTER(dg_canvas), c_void_p, c_void_p, c_void_p, c_void_p],
+    "dg_test_qkv_rope": [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                         c_void_p, c_void_p],
+    "dg_test_attention": [c_void_p, c_int32, c_void_p, POINTER(dg_kv), c_void_p, c_void_p, c_int32,
+                          c_void_p, c_void_p],
+    "dg_test_router": [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
+    "dg_test_shared": [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p],
+    "dg_test_moe": [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                    c_void_p],
+    "dg_test_force_routing": [c_void_p, c_void_p],
 }
 ENTRY_POINTS = ("dg_status_str", "dg_last_error", "dg_version", *_SIGS.keys())
 
@@ -174,3 +186,27 @@ def dg_test_lm_head(handle, hf_ptr, T, ent_ptr, am_ptr, gap_ptr, stream):
 
 def dg_test_commit(handle, canvas, ent_ptr, am_ptr, nunc_ptr, stream):
     _call("dg_test_commit", handle, byref(canvas), ent_ptr, am_ptr, nunc_ptr, stream)
+
+
+def dg_test_qkv_rope(handle, layer, a_ptr, batch, n, pos0, q_ptr, k_ptr, v_ptr, stream):
+    _call("dg_test_qkv_rope", handle, layer, a_ptr, batch, n, pos0, q_ptr, k_ptr, v_ptr, stream)
+
+
+def dg_test_attention(handle, layer, q_ptr, kv, kc_ptr, vc_ptr, n, out_ptr, stream):
+    _call("dg_test_attention", handle, layer, q_ptr, byref(kv), kc_ptr, vc_ptr, n, out_ptr, stream)
+
+
+def dg_test_router(handle, layer, b_ptr, T, logits_ptr, ids_ptr, w_ptr, stream):
+    _call("dg_test_router", handle, layer, b_ptr, T, logits_ptr, ids_ptr, w_ptr, stream)
+
+
+def dg_test_shared(handle, layer, b_ptr, T, hs_ptr, ys_ptr, stream):
+    _call("dg_test_shared", handle, layer, b_ptr, T, hs_ptr, ys_ptr, stream)
+
+
+def dg_test_moe(handle, layer, b_ptr, T, ids_ptr, h_ptr, y_ptr, pos_ptr, stream):
+    _call("dg_test_moe", handle, layer, b_ptr, T, ids_ptr, h_ptr, y_ptr, pos_ptr, stream)
+
+
+def dg_test_force_routing(handle, ids_ptr):
+    _call("dg_test_force_routing", handle, ids_ptr)

@@ -66,8 +66,14 @@ struct dg_model {
   int *topk_ids = nullptr, *off = nullptr, *pair_row = nullptr, *pos = nullptr;
   int lm_ntiles = 0;
   float *H = nullptr, *gap = nullptr;
-  int *am = nullptr, *n_unc = nullptr;
-  int* u_host = nullptr;  // pinned
+  int* am = nullptr;
+  // ctl[0]: status word published by the last step's commit kernel; ctl[1]:
+  // flags raised by the kernels since then; ctl[2 .. 2 + max_batch): the
+  // per-canvas uncommitted counts.  One copy brings status and counts back.
+  int* ctl = nullptr;
+  int* n_unc = nullptr;
+  int* u_host = nullptr;  // pinned, 2 + max_batch words
+  const int* force_ids = nullptr;  // test hook: [n_layers][max_batch * canvas_len][top_k], -1 = not forced
   // kernel timing
   int prof_id = DG_PROF_NONE;
   std::vector<hipEvent_t> prof_ev;  // start/stop pairs
@@ -156,6 +162,165 @@ int check_config(const dg_config& c) {
   return DG_OK;
 }
 
+// ---- phases of a block (shared by the step, the causal pass and the
+// test entries, which pass their own buffers)
+
+// rotary embedding applies in the QKV projection's epilogue (bf16, head_dim
+// 128, K a multiple of 64); otherwise a separate kernel rotates and scatters
+bool fused_rope(const dg_model* m) {
+  return m->at == ACT_BF16 && m->cfg.head_dim == 128 && tgemm_supported(m->at, m->cfg.d_model);
+}
+
+// q, k, v of the T = B * n rows of a (normed, act_dtype [T][d_model]) at the
+// positions whose (cos, sin) rows m->rope_tab holds: q -> q_out
+// [B][H][n][dh]; k, v -> (b, h) planes of k_dst / v_dst (dst_bh elements
+// apart), rows row0 + i.  Rotary-embedded q and k.
+int qkv_rope(dg_model* m, int l, const void* a, int B, int n, void* q_out, void* k_dst, void* v_dst,
+             long long dst_bh, int row0, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const int T = B * n, d = c.d_model, H = c.n_heads, dh = c.head_dim, A = H * dh;
+  const dg_layer_weights& w = m->layers[l];
+  GemmArgs g;
+  g.A = a; g.lda = d; g.B = w.wqkv; g.ldb = d; g.M = T; g.N = 3 * A; g.K = d;
+  if (fused_rope(m)) {
+    g.q_out = q_out; g.seq_n = n; g.heads = H; g.rope_tab = m->rope_tab;
+    g.k_dst = k_dst; g.v_dst = v_dst; g.dst_bh = dst_bh; g.row0 = row0;
+    HIP_OK(gemm(m->at, W_BF16, EPI_QKV, g, 1, st));
+    return DG_OK;
+  }
+  g.C = m->qkv; g.ldc = 3 * A;
+  HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_ACT, g, 1, st));
+  HIP_OK(rope_scatter(m->at, m->qkv, B, n, H, dh, m->rope_tab, q_out, k_dst, v_dst, dst_bh, row0, st));
+  return DG_OK;
+}
+
+// Attention of the B x n queries q [B][H][n][dh] into o [B*n][H*dh]:
+// bidirectional over cache rows [0, P) of `layer` plus the canvas keys and
+// values kc / vc [B][H][n][dh]; causal (kc null): over cache rows [0, P + n)
+// with query i seeing rows j <= P + i.
+int attend(dg_model* m, int l, const void* q, const dg_kv* kv, int P, const void* kc, const void* vc, int B, int n,
+           void* o, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const int H = c.n_heads, dh = c.head_dim;
+  const long long cap = kv->capacity;
+  const long long layer_stride = (long long)kv->batch * H * cap * dh;
+  AttnArgs aa{};
+  aa.q = q; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = o;
+  aa.part_o = m->attn_po; aa.part_ml = m->attn_ml;
+  aa.k0 = (const char*)kv->k + l * layer_stride * m->esz;
+  aa.v0 = (const char*)kv->v + l * layer_stride * m->esz;
+  aa.s0_bh = cap * dh;
+  if (kc) {
+    aa.len0 = P;
+    aa.k1 = kc; aa.v1 = vc; aa.s1_bh = (long long)n * dh; aa.len1 = n;
+    aa.causal_base = -1;
+  } else {
+    aa.len0 = P + n;
+    aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;
+    aa.causal_base = P;
+  }
+  aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1, dh));
+  HIP_OK(attention(m->at, aa, st));
+  return DG_OK;
+}
+
+// shared gate/up + SwiGLU of b [T][d_model] into hs [T][d_shared]; where the
+// bf16 direct-load kernel covers it, the router logits (the same rows
+// against the E router rows) ride in the same launch as extra tiles and go
+// to rlog [T][E] (*router_done = true).
+int shared_gate_up(dg_model* m, int l, const void* b, int T, void* hs, float* rlog, bool* router_done,
+                   hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const dg_layer_weights& w = m->layers[l];
+  const int d = c.d_model, ds = c.d_shared;
+  GemmArgs g;
+  g.A = b; g.lda = d; g.B = w.ws_gu; g.ldb = d; g.b_scale = w.ss_gu;
+  g.M = T; g.N = ds; g.K = d; g.C = hs; g.ldc = ds; g.swiglu_half = ds;
+  int r = int(hipErrorInvalidValue);
+  *router_done = false;
+  if (m->at == ACT_BF16 && m->wt == W_BF16) {
+    GemmArgs gf = g;
+    gf.B2 = w.wr; gf.ldb2 = d; gf.N2 = c.n_experts; gf.C2 = rlog; gf.ldc2 = c.n_experts;
+    r = gemm(m->at, m->wt, EPI_SWIGLU, gf, 1, st);
+    *router_done = r == int(hipSuccess);
+  }
+  if (r == int(hipErrorInvalidValue)) r = gemm(m->at, m->wt, EPI_SWIGLU, g, 1, st);
+  HIP_OK(r);
+  return DG_OK;
+}
+
+// shared down: ys [T][d_model] (fp32) = hs [T][d_shared] . W_down^T
+int shared_down(dg_model* m, int l, const void* hs, int T, float* ys, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const dg_layer_weights& w = m->layers[l];
+  GemmArgs g;
+  g.A = hs; g.lda = c.d_shared; g.B = w.ws_d; g.ldb = c.d_shared; g.b_scale = w.ss_d;
+  g.M = T; g.N = c.d_model; g.K = c.d_shared; g.C = ys; g.ldc = c.d_model;
+  HIP_OK(gemm(m->at, m->wt, EPI_F32, g, 1, st));
+  return DG_OK;
+}
+
+// router: logits rlog [T][E] of b (unless the shared launch computed them),
+// top-k ids [T][k] and weights; `forced` (test hook, nullable) overrides rows.
+int route(dg_model* m, int l, const void* b, int T, float* rlog, bool logits_done, int* ids, float* wts,
+          const int* forced, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const int E = c.n_experts, k = c.top_k, d = c.d_model;
+  if (!logits_done) {
+    GemmArgs g;
+    g.A = b; g.lda = d; g.B = m->layers[l].wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = rlog; g.ldc = E;
+    HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_F32, g, 1, st));
+  }
+  HIP_OK(router_topk(rlog, T, E, k, ids, wts, st));
+  if (forced) HIP_OK(router_force(rlog, T, E, k, forced, ids, wts, st));
+  return DG_OK;
+}
+
+// routed experts on the top-k ids [T][k]: h [T*k][d_expert] (SwiGLU
+// products) and y [T*k][d_model] (fp32 expert outputs), both in pair order
+// (expert-major, token-ascending); off [E+1], pair_row [T*k] and pos [T][k]
+// (the row of pair (t, j)) describe that order.
+int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, float* y, int* off, int* pair_row,
+           int* pos, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const dg_layer_weights& w = m->layers[l];
+  const int E = c.n_experts, k = c.top_k, d = c.d_model, de = c.d_expert;
+  if (m->at == ACT_BF16) {
+    // Absorbing-state noise: every open position holds the same [MASK] token,
+    // so the open rows pile onto a few experts; the pooled kernels' 96-token
+    // passes stream a heavy expert's weights a third as often.
+    const int pairs = c.mask_token >= 0 ? std::max(T * k, 24 * E + 1) : T * k;
+    {
+      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU, routing in the kernel
+      const MoeRoute r{ids, T, k, off, pair_row, pos};
+      HIP_OK(moe_experts(m->wt, true, b, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, h, st, &r, pairs));
+    }
+    {
+      ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down
+      HIP_OK(moe_experts(m->wt, false, h, pair_row, off, E, w.w_d, w.s_d, de, d, y, st, nullptr, pairs));
+    }
+    return DG_OK;
+  }
+  HIP_OK(router_permute(ids, T, E, k, off, pair_row, pos, st));
+  {
+    ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
+    GemmArgs g;  // routed gate/up + SwiGLU, rows gathered per expert
+    g.A = b; g.lda = d; g.a_rows = pair_row; g.B = w.w_gu; g.ldb = d;
+    g.b_gstride = 2LL * de * d; g.b_scale = w.s_gu; g.s_gstride = 2LL * de;
+    g.M = T * k; g.N = de; g.K = d; g.g_off = off; g.C = h; g.ldc = de; g.swiglu_half = de;
+    HIP_OK(gemm(m->at, m->wt, EPI_SWIGLU, g, E, st));
+  }
+  {
+    ProfScope ps(m, DG_PROF_MOE_DOWN, st);
+    GemmArgs g;  // routed down
+    g.A = h; g.lda = de; g.B = w.w_d; g.ldb = de; g.b_gstride = (long long)d * de;
+    g.b_scale = w.s_d; g.s_gstride = d;
+    g.M = T * k; g.N = d; g.K = de; g.g_off = off; g.C = y; g.ldc = d;
+    HIP_OK(gemm(m->at, m->wt, EPI_F32, g, E, st));
+  }
+  return DG_OK;
+}
+
 // One pre-norm block over T = B * n rows.  causal: rows are new tokens at
 // positions P.. written into the cache; otherwise canvas rows attend to the
 // first P cache rows plus the canvas.  On entry m->a holds rmsnorm(x); on
@@ -166,131 +331,53 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   const dg_config& c = m->cfg;
   const dg_layer_weights& w = m->layers[l];
   const int T = B * n, d = c.d_model, H = c.n_heads, dh = c.head_dim, A = H * dh;
-  const int E = c.n_experts, k = c.top_k, de = c.d_expert, ds = c.d_shared;
-  const ActType at = m->at;
   const long long cap = kv->capacity;
   const long long layer_stride = (long long)kv->batch * H * cap * dh;
   char* kcache = (char*)kv->k + l * layer_stride * m->esz;
   char* vcache = (char*)kv->v + l * layer_stride * m->esz;
-
-  // bf16 with head_dim 128: RoPE and the scatter to the per-head layouts run
-  // in the projection's epilogue; otherwise a separate kernel does them
-  const bool fused_rope = at == ACT_BF16 && dh == 128 && tgemm_supported(at, d);
+  int s;
   {
     ProfScope ps(m, DG_PROF_QKV, st);
-    GemmArgs g;
-    g.A = m->a; g.lda = d; g.B = w.wqkv; g.ldb = d; g.M = T; g.N = 3 * A; g.K = d;
-    if (fused_rope) {
-      g.q_out = m->q; g.seq_n = n; g.heads = H; g.rope_tab = m->rope_tab;
-      g.k_dst = causal ? (void*)kcache : m->kc; g.v_dst = causal ? (void*)vcache : m->vc;
-      g.dst_bh = causal ? cap * dh : (long long)n * dh; g.row0 = causal ? P : 0;
-      HIP_OK(gemm(at, W_BF16, EPI_QKV, g, 1, st));
-    } else {
-      g.C = m->qkv; g.ldc = 3 * A;
-      HIP_OK(gemm(at, at == ACT_BF16 ? W_BF16 : W_F32, EPI_ACT, g, 1, st));
-    }
+    s = causal ? qkv_rope(m, l, m->a, B, n, m->q, kcache, vcache, cap * dh, P, st)
+               : qkv_rope(m, l, m->a, B, n, m->q, m->kc, m->vc, (long long)n * dh, 0, st);
+    if (s) return s;
   }
-  AttnArgs aa{};
-  aa.q = m->q; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = m->o;
-  aa.part_o = m->attn_po; aa.part_ml = m->attn_ml;
-  if (!causal) {
-    if (!fused_rope)
-      HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, m->kc, m->vc, (long long)n * dh, 0, st));
-    aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P;
-    aa.k1 = m->kc; aa.v1 = m->vc; aa.s1_bh = (long long)n * dh; aa.len1 = n;
-    aa.causal_base = -1;
-  } else {
-    if (!fused_rope)
-      HIP_OK(rope_scatter(at, m->qkv, B, n, H, dh, m->rope_tab, m->q, kcache, vcache, cap * dh, P, st));
-    if (kv_only) return DG_OK;
-    aa.k0 = kcache; aa.v0 = vcache; aa.s0_bh = cap * dh; aa.len0 = P + n;
-    aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;
-    aa.causal_base = P;
-  }
-  aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1, dh));
+  if (causal && kv_only) return DG_OK;
   {
     ProfScope ps(m, DG_PROF_ATTN, st);
-    HIP_OK(attention(at, aa, st));
+    s = causal ? attend(m, l, m->q, kv, P, nullptr, nullptr, B, n, m->o, st)
+               : attend(m, l, m->q, kv, P, m->kc, m->vc, B, n, m->o, st);
+    if (s) return s;
   }
-  const WType dw = at == ACT_BF16 ? W_BF16 : W_F32;
   {
-    GemmArgs g;
+    GemmArgs g;  // O-projection + residual
     g.A = m->o; g.lda = A; g.B = w.wo; g.ldb = A; g.M = T; g.N = d; g.K = A; g.C = m->x; g.ldc = d;
-    HIP_OK(gemm(at, dw, EPI_RESID, g, 1, st));
+    HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_RESID, g, 1, st));
   }
-  HIP_OK(rmsnorm(at, m->x, T, d, c.rms_eps, m->a, st));
+  HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st));
   // The shared expert runs in line, before the router.  (On a second stream,
   // beside the router and the routed experts, its workgroups held CUs that
   // the routed gate/up workgroups (138 KB of LDS each) could not share, and
   // the waits this caused on the main stream cost more than the overlap won.)
-  // Where the bf16 direct-load kernel covers the shared gate/up, the router
-  // logits (the same normed rows against the E router rows) ride in its
-  // launch as extra tiles instead of a launch of their own.
   bool router_done = false;
   {
     ProfScope ps(m, DG_PROF_SHARED, st);
-    GemmArgs g;  // shared gate/up + SwiGLU
-    g.A = m->a; g.lda = d; g.B = w.ws_gu; g.ldb = d; g.b_scale = w.ss_gu;
-    g.M = T; g.N = ds; g.K = d; g.C = m->hs; g.ldc = ds; g.swiglu_half = ds;
-    int r = int(hipErrorInvalidValue);
-    if (at == ACT_BF16 && m->wt == W_BF16) {
-      GemmArgs gf = g;
-      gf.B2 = w.wr; gf.ldb2 = d; gf.N2 = E; gf.C2 = m->rlog; gf.ldc2 = E;
-      r = gemm(at, m->wt, EPI_SWIGLU, gf, 1, st);
-      router_done = r == int(hipSuccess);
-    }
-    if (r == int(hipErrorInvalidValue)) r = gemm(at, m->wt, EPI_SWIGLU, g, 1, st);
-    HIP_OK(r);
-    GemmArgs g2;  // shared down
-    g2.A = m->hs; g2.lda = ds; g2.B = w.ws_d; g2.ldb = ds; g2.b_scale = w.ss_d;
-    g2.M = T; g2.N = d; g2.K = ds; g2.C = m->ys; g2.ldc = d;
-    HIP_OK(gemm(at, m->wt, EPI_F32, g2, 1, st));
+    s = shared_gate_up(m, l, m->a, T, m->hs, m->rlog, &router_done, st);
+    if (!s) s = shared_down(m, l, m->hs, T, m->ys, st);
+    if (s) return s;
   }
   {
     ProfScope ps(m, DG_PROF_ROUTER, st);
-    {
-      GemmArgs g;
-      g.A = m->a; g.lda = d; g.B = w.wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = m->rlog; g.ldc = E;
-      if (!router_done) HIP_OK(gemm(at, dw, EPI_F32, g, 1, st));
-      HIP_OK(router_topk(m->rlog, T, E, k, m->topk_ids, m->topk_w, st));
-    }
-    // bf16: the routed gate/up kernel derives the permutation itself
-    if (at != ACT_BF16) HIP_OK(router_permute(m->topk_ids, T, E, k, m->off, m->pair_row, m->pos, st));
+    const int* forced = (m->force_ids && !causal)
+                            ? m->force_ids + (long long)l * m->max_batch * c.canvas_len * c.top_k
+                            : nullptr;
+    s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, forced, st);
+    if (s) return s;
   }
-  if (at == ACT_BF16) {
-    // Absorbing-state noise: every open position holds the same [MASK] token,
-    // so the open rows pile onto a few experts; the pooled kernels' 96-token
-    // passes stream a heavy expert's weights a third as often.
-    const int pairs = m->cfg.mask_token >= 0 ? std::max(T * k, 24 * E + 1) : T * k;
-    {
-      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU, routing in the kernel
-      const MoeRoute route{m->topk_ids, T, k, m->off, m->pair_row, m->pos};
-      HIP_OK(moe_experts(m->wt, true, m->a, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, m->h, st, &route, pairs));
-    }
-    {
-      ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down
-      HIP_OK(moe_experts(m->wt, false, m->h, m->pair_row, m->off, E, w.w_d, w.s_d, de, d, m->y, st, nullptr,
-                         pairs));
-    }
-  } else {
-    {
-      ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
-      GemmArgs g;  // routed gate/up + SwiGLU, rows gathered per expert
-      g.A = m->a; g.lda = d; g.a_rows = m->pair_row; g.B = w.w_gu; g.ldb = d;
-      g.b_gstride = 2LL * de * d; g.b_scale = w.s_gu; g.s_gstride = 2LL * de;
-      g.M = T * k; g.N = de; g.K = d; g.g_off = m->off; g.C = m->h; g.ldc = de; g.swiglu_half = de;
-      HIP_OK(gemm(at, m->wt, EPI_SWIGLU, g, E, st));
-    }
-    {
-      ProfScope ps(m, DG_PROF_MOE_DOWN, st);
-      GemmArgs g;  // routed down
-      g.A = m->h; g.lda = de; g.B = w.w_d; g.ldb = de; g.b_gstride = (long long)d * de;
-      g.b_scale = w.s_d; g.s_gstride = d;
-      g.M = T * k; g.N = d; g.K = de; g.g_off = m->off; g.C = m->y; g.ldc = d;
-      HIP_OK(gemm(at, m->wt, EPI_F32, g, E, st));
-    }
-  }
-  HIP_OK(moe_combine_norm(at, m->x, m->y, m->ys, m->topk_w, m->pos, T, k, d, c.rms_eps, m->a, st));
+  s = routed(m, l, m->a, T, m->topk_ids, m->h, m->y, m->off, m->pair_row, m->pos, st);
+  if (s) return s;
+  HIP_OK(moe_combine_norm(m->at, m->x, m->y, m->ys, m->topk_w, m->pos, T, c.top_k, d, c.rms_eps, m->a,
+                          m->ctl + 1, st));
   return DG_OK;
 }
 
@@ -300,9 +387,9 @@ int lm_head_confidence(dg_model* m, const void* hf, int T, float* H, int* am, fl
   const dg_config& c = m->cfg;
   GemmArgs g;
   g.A = hf; g.lda = c.d_model; g.B = m->lm_head; g.ldb = c.d_model; g.M = T; g.N = c.vocab;
-  g.K = c.d_model; g.part = m->lm_part;
+  g.K = c.d_model; g.part = m->lm_part; g.flags = m->ctl + 1;
   HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_LM, g, 1, st));
-  HIP_OK(lm_merge(m->lm_part, T, m->lm_ntiles, H, am, gap, st));
+  HIP_OK(lm_merge(m->lm_part, T, m->lm_ntiles, H, am, gap, m->ctl + 1, st));
   return DG_OK;
 }
 
@@ -313,10 +400,12 @@ int check_canvas(dg_model* m, const dg_canvas* c) {
   return DG_OK;
 }
 
-int check_kv(const dg_kv* kv, int batch, int extra) {
+int check_kv(const dg_model* m, const dg_kv* kv, int batch, int extra) {
   if (!kv || !kv->k || !kv->v) return fail(DG_ERR_INVALID_ARG, "null kv pointer");
   if (kv->batch != batch) return fail(DG_ERR_SHAPE, "kv batch %d != %d", kv->batch, batch);
-  if (kv->length < 0 || kv->capacity <= 0 || kv->length + extra > kv->capacity)
+  if (kv->capacity > m->max_kv)
+    return fail(DG_ERR_SHAPE, "kv capacity %d exceeds the model's max_kv %d", kv->capacity, m->max_kv);
+  if (kv->length < 0 || kv->capacity <= 0 || (long long)kv->length + extra > kv->capacity)
     return fail(DG_ERR_SHAPE, "kv length %d + %d exceeds capacity %d", kv->length, extra, kv->capacity);
   return DG_OK;
 }
@@ -324,7 +413,7 @@ int check_kv(const dg_kv* kv, int batch, int extra) {
 int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, hipStream_t st) {
   const dg_config& cfg = m->cfg;
   const int B = c->batch, N = cfg.canvas_len, T = B * N, P = kv->length;
-  HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, m->x, st));
+  HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, cfg.vocab, m->x, m->ctl + 1, st));
   HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
   HIP_OK(rope_table(N, cfg.head_dim, P, cfg.rope_theta, m->rope_tab, st));  // canvas positions P..P+N-1
   for (int l = 0; l < cfg.n_layers; ++l) {
@@ -348,10 +437,12 @@ int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* o
   {
     ProfScope ps(m, DG_PROF_COMMIT, st);
     HIP_OK(commit_renoise(H, am, c->tokens, c->committed, B, N, c->step, cfg.max_steps,
-                          cfg.commit_threshold, c->seed, c->block, cfg.vocab, cfg.mask_token, m->n_unc, st));
+                          cfg.commit_threshold, c->seed, c->block, cfg.vocab, cfg.mask_token, m->n_unc, m->ctl + 1,
+                          m->ctl, st));
   }
   if (out && out->n_uncommitted)
     HIP_OK(hipMemcpyAsync(out->n_uncommitted, m->n_unc, sizeof(int) * B, hipMemcpyDeviceToDevice, st));
+  if (out && out->status) HIP_OK(hipMemcpyAsync(out->status, m->ctl, sizeof(int), hipMemcpyDeviceToDevice, st));
   c->step += 1;
   return DG_OK;
 }
@@ -395,6 +486,9 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   }
   if (max_batch <= 0 || max_tokens < 0 || max_kv < 0)
     return fail(DG_ERR_INVALID_ARG, "max_batch must be > 0, max_tokens and max_kv >= 0");
+  // attention addresses a (layer, canvas, head) plane of the cache with 32-bit byte offsets
+  const long long kv_limit = 0x7fffffffLL / ((long long)cfg->head_dim * (cfg->act_dtype == DG_DTYPE_BF16 ? 2 : 4));
+  if (max_kv > kv_limit) return fail(DG_ERR_SHAPE, "max_kv %d exceeds %lld rows", max_kv, kv_limit);
   const int ntok = std::max(max_tokens, cfg->canvas_len);
   // tokens of one call: the routed gate/up kernel derives the routing of up
   // to 2048 tokens in LDS; the fp32 path's permutation kernel takes 1024
@@ -409,7 +503,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   m->lm_head = w->lm_head;
   m->max_batch = max_batch;
   m->max_tokens = ntok;
-  m->max_kv = max_kv;
+  m->max_kv = max_kv ? max_kv : int(kv_limit);
   m->Tmax = max_batch * ntok;
   m->at = cfg->act_dtype == DG_DTYPE_BF16 ? ACT_BF16 : ACT_F32;
   m->wt = cfg->expert_dtype == DG_DTYPE_FP8_E4M3 ? W_FP8 : (m->at == ACT_BF16 ? W_BF16 : W_F32);
@@ -447,7 +541,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       {(void**)&m->H, Tc * 4},
       {(void**)&m->gap, Tc * 4},
       {(void**)&m->am, Tc * 4},
-      {(void**)&m->n_unc, (size_t)max_batch * 4},
+      {(void**)&m->ctl, (size_t)(2 + max_batch) * 4},
   };
   for (auto& r : reqs) {
     s = alloc(m, r.p, r.bytes);
@@ -457,7 +551,14 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       return s;
     }
   }
-  if (hipHostMalloc((void**)&m->u_host, sizeof(int) * max_batch, hipHostMallocDefault) != hipSuccess) {
+  m->n_unc = m->ctl + 2;
+  if (hipMemset(m->ctl, 0, sizeof(int) * (2 + max_batch)) != hipSuccess) {
+    (void)hipGetLastError();
+    free_all(m);
+    delete m;
+    return fail(DG_ERR_HIP, "hipMemset of the status word failed");
+  }
+  if (hipHostMalloc((void**)&m->u_host, sizeof(int) * (2 + max_batch), hipHostMallocDefault) != hipSuccess) {
     (void)hipGetLastError();
     free_all(m);
     delete m;
@@ -498,7 +599,7 @@ int dg_denoise_step(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out
   if (!m) return fail(DG_ERR_INVALID_ARG, "null model");
   int s = check_canvas(m, c);
   if (s) return s;
-  s = check_kv(kv, c->batch, 0);
+  s = check_kv(m, kv, c->batch, 0);
   if (s) return s;
   if (c->step < 0 || c->step >= m->cfg.max_steps)
     return fail(DG_ERR_STATE, "step %d outside [0, max_steps=%d)", c->step, m->cfg.max_steps);
@@ -509,7 +610,7 @@ int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* step
   if (!m || !steps_taken) return fail(DG_ERR_INVALID_ARG, "null argument");
   int s = check_canvas(m, c);
   if (s) return s;
-  s = check_kv(kv, c->batch, 0);
+  s = check_kv(m, kv, c->batch, 0);
   if (s) return s;
   if (c->step < 0 || c->step > m->cfg.max_steps)
     return fail(DG_ERR_STATE, "step %d outside [0, max_steps]", c->step);
@@ -522,12 +623,22 @@ int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* step
       return s;
     }
     ++taken;
-    // the per-canvas uncommitted counts come back with the step's end (the
-    // host waits for it anyway) and are summed here
-    HIP_OK(hipMemcpyAsync(m->u_host, m->n_unc, sizeof(int) * c->batch, hipMemcpyDeviceToHost, st));
+    // the status word and the per-canvas uncommitted counts come back with
+    // the step's end (the host waits for it anyway)
+    HIP_OK(hipMemcpyAsync(m->u_host, m->ctl, sizeof(int) * (2 + c->batch), hipMemcpyDeviceToHost, st));
     HIP_OK(hipStreamSynchronize(st));
+    const int status = m->u_host[0];
+    if (status & FLAG_TOKEN) {
+      *steps_taken = taken;
+      return fail(DG_ERR_INVALID_ARG, "a token id outside [0, %d) reached the embedding (read as id 0) by step %d",
+                  m->cfg.vocab, c->step - 1);
+    }
+    if (status & FLAG_NONFINITE) {
+      *steps_taken = taken;
+      return fail(DG_ERR_NUMERIC, "non-finite values in the residual stream or the logits by step %d", c->step - 1);
+    }
     int left = 0;
-    for (int b = 0; b < c->batch; ++b) left += m->u_host[b];
+    for (int b = 0; b < c->batch; ++b) left += m->u_host[2 + b];
     if (left == 0) break;
   }
   *steps_taken = taken;
@@ -539,12 +650,12 @@ int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, v
   if (!kv) return fail(DG_ERR_INVALID_ARG, "null kv");
   if (n <= 0 || n > m->max_tokens) return fail(DG_ERR_SHAPE, "n=%d outside [1, max_tokens=%d]", n, m->max_tokens);
   if (kv->batch <= 0 || kv->batch > m->max_batch) return fail(DG_ERR_SHAPE, "kv batch %d", kv->batch);
-  int s = check_kv(kv, kv->batch, n);
+  int s = check_kv(m, kv, kv->batch, n);
   if (s) return s;
   hipStream_t st = (hipStream_t)stream;
   const dg_config& cfg = m->cfg;
   const int B = kv->batch, T = B * n, P = kv->length;
-  HIP_OK(embed_gather(m->at, tokens, T, m->embed, cfg.d_model, m->x, st));
+  HIP_OK(embed_gather(m->at, tokens, T, m->embed, cfg.d_model, cfg.vocab, m->x, m->ctl + 1, st));
   HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
   HIP_OK(rope_table(n, cfg.head_dim, P, cfg.rope_theta, m->rope_tab, st));  // positions P..P+n-1
   for (int l = 0; l < cfg.n_layers; ++l) {
@@ -618,7 +729,86 @@ int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_
   if (c->step < 0 || c->step >= m->cfg.max_steps) return fail(DG_ERR_STATE, "step out of range");
   HIP_OK(commit_renoise(entropy, argmax, c->tokens, c->committed, c->batch, m->cfg.canvas_len, c->step,
                         m->cfg.max_steps, m->cfg.commit_threshold, c->seed, c->block, m->cfg.vocab, m->cfg.mask_token,
-                        n_uncommitted, (hipStream_t)stream));
+                        n_uncommitted, nullptr, nullptr, (hipStream_t)stream));
+  return DG_OK;
+}
+
+// ---- unit entries: one phase of a block on caller buffers, through the same
+// launches the step makes
+
+namespace {
+int check_layer(const dg_model* m, int layer) {
+  if (layer < 0 || layer >= m->cfg.n_layers)
+    return fail(DG_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, m->cfg.n_layers);
+  return DG_OK;
+}
+int check_rows(const dg_model* m, long long T) {
+  if (T <= 0 || T > m->Tmax) return fail(DG_ERR_SHAPE, "%lld rows outside [1, %d]", T, m->Tmax);
+  return DG_OK;
+}
+}  // namespace
+
+int dg_test_qkv_rope(dg_model* m, int32_t layer, const void* a, int32_t batch, int32_t n, int32_t pos0, void* q,
+                     void* k, void* v, void* stream) {
+  if (!m || !a || !q || !k || !v) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_layer(m, layer);
+  if (!s) s = check_rows(m, (long long)batch * n);
+  if (s) return s;
+  if (batch <= 0 || n <= 0 || n > m->max_tokens || pos0 < 0)
+    return fail(DG_ERR_SHAPE, "batch %d, n %d (max_tokens %d), pos0 %d", batch, n, m->max_tokens, pos0);
+  hipStream_t st = (hipStream_t)stream;
+  HIP_OK(rope_table(n, m->cfg.head_dim, pos0, m->cfg.rope_theta, m->rope_tab, st));
+  return qkv_rope(m, layer, a, batch, n, q, k, v, (long long)n * m->cfg.head_dim, 0, st);
+}
+
+int dg_test_attention(dg_model* m, int32_t layer, const void* q, const dg_kv* kv, const void* k_canvas,
+                      const void* v_canvas, int32_t n, void* out, void* stream) {
+  if (!m || !q || !out || !kv || (!k_canvas) != (!v_canvas)) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_layer(m, layer);
+  if (!s) s = check_kv(m, kv, kv->batch, k_canvas ? 0 : n);
+  if (!s && (kv->batch <= 0 || kv->batch > m->max_batch)) s = fail(DG_ERR_SHAPE, "kv batch %d", kv->batch);
+  if (!s) s = check_rows(m, (long long)kv->batch * n);
+  if (s) return s;
+  return attend(m, layer, q, kv, kv->length, k_canvas, v_canvas, kv->batch, n, out, (hipStream_t)stream);
+}
+
+int dg_test_router(dg_model* m, int32_t layer, const void* b, int32_t T, float* logits, int32_t* ids,
+                   float* weights, void* stream) {
+  if (!m || !b || !logits || !ids || !weights) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_layer(m, layer);
+  if (!s) s = check_rows(m, T);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  bool done = false;
+  s = shared_gate_up(m, layer, b, T, m->hs, logits, &done, st);
+  if (s) return s;
+  return route(m, layer, b, T, logits, done, ids, weights, nullptr, st);
+}
+
+int dg_test_shared(dg_model* m, int32_t layer, const void* b, int32_t T, void* hs, float* ys, void* stream) {
+  if (!m || !b || !hs || !ys) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_layer(m, layer);
+  if (!s) s = check_rows(m, T);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  bool done = false;
+  s = shared_gate_up(m, layer, b, T, hs, m->rlog, &done, st);
+  if (s) return s;
+  return shared_down(m, layer, hs, T, ys, st);
+}
+
+int dg_test_moe(dg_model* m, int32_t layer, const void* b, int32_t T, const int32_t* ids, void* h, float* y,
+                int32_t* pos, void* stream) {
+  if (!m || !b || !ids || !y || !pos) return fail(DG_ERR_INVALID_ARG, "null argument");
+  int s = check_layer(m, layer);
+  if (!s) s = check_rows(m, T);
+  if (s) return s;
+  return routed(m, layer, b, T, ids, h ? h : m->h, y, m->off, m->pair_row, pos, (hipStream_t)stream);
+}
+
+int dg_test_force_routing(dg_model* m, const int32_t* ids) {
+  if (!m) return fail(DG_ERR_INVALID_ARG, "null model");
+  m->force_ids = ids;
   return DG_OK;
 }
 

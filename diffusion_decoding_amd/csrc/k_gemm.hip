@@ -252,6 +252,8 @@ __global__ __launch_bounds__(NT) void gemm_nt(GemmArgs g) {
           p.t += e * d;
         }
       }
+      // no column above -inf while some column exists: every logit NaN or -inf
+      if (p.idx == INT_MAX && n0 + sub * CPT < g.N && m0 + r < row_end && g.flags) atomicOr(g.flags, FLAG_NONFINITE);
 #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) p = lm_combine(p, lm_shfl_xor(p, o));
       int m = m0 + r;
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(NT) void gemm_nt(GemmArgs g) {
 // flight per step), then a fixed xor tree inside each wave and the four wave
 // results in wave order.
 __global__ __launch_bounds__(256) void lm_merge_kernel(const float* part, int T, int n_tiles,
-                                                       float* H, int* am, float* gap) {
+                                                       float* H, int* am, float* gap, int* flags) {
   __shared__ float wp[4][5];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   LmPart acc = lm_empty_part();
@@ -315,7 +317,10 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const float* part, int T,
       p.idx = __float_as_int(wp[w][4]);
       acc = lm_combine(acc, p);
     }
-    if (H) H[row] = logf(acc.s) - acc.t / acc.s;
+    const float h = logf(acc.s) - acc.t / acc.s;
+    // a NaN or infinite logit anywhere in the row makes s or t NaN
+    if (flags && (!(fabsf(h) <= 3.402823466e38f) || acc.idx == INT_MAX)) atomicOr(flags, FLAG_NONFINITE);
+    if (H) H[row] = h;
     if (am) am[row] = acc.idx;
     if (gap) gap[row] = acc.m - acc.sec;
   }
@@ -362,10 +367,10 @@ int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipSt
   return int(hipErrorInvalidValue);
 }
 
-int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap,
+int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap, int* flags,
              hipStream_t st) {
   if (T <= 0) return 0;
-  hipLaunchKernelGGL(lm_merge_kernel, dim3(T), dim3(256), 0, st, part, T, n_tiles, entropy, argmax, gap);
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(T), dim3(256), 0, st, part, T, n_tiles, entropy, argmax, gap, flags);
   return int(hipGetLastError());
 }
 

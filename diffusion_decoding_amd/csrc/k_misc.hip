@@ -21,12 +21,27 @@
 namespace dg {
 namespace {
 
+// A token id outside [0, vocab) reads row 0 instead and raises FLAG_TOKEN, so
+// a bad id from the caller never addresses memory past the table.
 template <typename T>
-__global__ void embed_kernel(const int* tok, int T_, const T* E, int d, T* x) {
+__global__ void embed_kernel(const int* tok, int T_, const T* E, int d, int vocab, T* x, int* flags) {
   const int t = blockIdx.x;
-  const long long src = (long long)tok[t] * d;
+  int id = tok[t];
+  if (id < 0 || id >= vocab) {
+    if (threadIdx.x == 0 && flags) atomicOr(flags, FLAG_TOKEN);
+    id = 0;
+  }
+  const long long src = (long long)id * d;
   for (int c = threadIdx.x; c < d; c += blockDim.x) x[(long long)t * d + c] = E[src + c];
 }
+
+// FLAG_NONFINITE when any lane of the wave holds a non-finite value (one
+// atomic per wave, only then)
+__device__ __forceinline__ void flag_nonfinite(bool bad, int* flags) {
+  const unsigned long long any = __ballot(bad);
+  if (any && flags && (threadIdx.x & 63) == __ffsll((long long)any) - 1) atomicOr(flags, FLAG_NONFINITE);
+}
+__device__ __forceinline__ bool nonfinite(float v) { return !(fabsf(v) <= 3.402823466e38f); }
 
 // one workgroup (256 threads) per row
 template <typename T>
@@ -176,22 +191,27 @@ __global__ void rope_kernel(const T* qkv, int B, int n, int H, int dh, const flo
 
 template <typename T>
 __global__ void combine_kernel(T* x, const float* y, const float* ys, const float* w, const int* pos,
-                               int k, int d) {
+                               int k, int d, int* flags) {
   const int t = blockIdx.x;
+  bool bad = false;
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     float acc = 0.f;
     for (int j = 0; j < k; ++j) acc += w[t * k + j] * y[(long long)pos[t * k + j] * d + c];
     acc += ys[(long long)t * d + c];
     T* xp = x + (long long)t * d + c;
-    *xp = from_f32<T>(to_f32(*xp) + acc);
+    const T r = from_f32<T>(to_f32(*xp) + acc);
+    *xp = r;
+    bad |= nonfinite(to_f32(r));
   }
+  flag_nonfinite(bad, flags);
 }
 
 // bf16, d % 4 == 0: grid (T, ceil(d / 1024)), thread -> 4 consecutive columns.
 // Same arithmetic order as combine_kernel: experts in slot order, then the
 // shared expert, then one rounding of the residual add.
 __global__ __launch_bounds__(256) void combine_bf16_kernel(bf16* x, const float* y, const float* ys,
-                                                           const float* w, const int* pos, int k, int d) {
+                                                           const float* w, const int* pos, int k, int d,
+                                                           int* flags) {
   const int t = blockIdx.x, c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= d) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -201,8 +221,11 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(bf16* x, const float*
   const u32x2 xv = *(const u32x2*)xp;
   const float x0 = __uint_as_float(xv[0] << 16), x1 = __uint_as_float(xv[0] & 0xffff0000u);
   const float x2 = __uint_as_float(xv[1] << 16), x3 = __uint_as_float(xv[1] & 0xffff0000u);
-  *(u32x2*)xp = u32x2{uint32_t(f32_to_bf16(x0 + acc[0]).v) | (uint32_t(f32_to_bf16(x1 + acc[1]).v) << 16),
-                      uint32_t(f32_to_bf16(x2 + acc[2]).v) | (uint32_t(f32_to_bf16(x3 + acc[3]).v) << 16)};
+  const bf16 r0 = f32_to_bf16(x0 + acc[0]), r1 = f32_to_bf16(x1 + acc[1]);
+  const bf16 r2 = f32_to_bf16(x2 + acc[2]), r3 = f32_to_bf16(x3 + acc[3]);
+  *(u32x2*)xp = u32x2{uint32_t(r0.v) | (uint32_t(r1.v) << 16), uint32_t(r2.v) | (uint32_t(r3.v) << 16)};
+  if (nonfinite(to_f32(r0)) || nonfinite(to_f32(r1)) || nonfinite(to_f32(r2)) || nonfinite(to_f32(r3)))
+    atomicOr(flags, FLAG_NONFINITE);
 }
 
 // bf16, d % 4 == 0, d <= 4096: one workgroup per token, one thread per 4
@@ -213,7 +236,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(bf16* x, const float*
 // rsqrt(mean x^2 + eps)).
 __global__ __launch_bounds__(1024) void combine_norm_bf16_kernel(bf16* x, const float* y, const float* ys,
                                                                  const float* w, const int* pos, int k, int d,
-                                                                 float eps, bf16* a) {
+                                                                 float eps, bf16* a, int* flags) {
   __shared__ float red[16];
   const int t = blockIdx.x, tid = threadIdx.x, c = tid * 4;
   const bool live = c < d;
@@ -244,6 +267,7 @@ __global__ __launch_bounds__(1024) void combine_norm_bf16_kernel(bf16* x, const 
     xv[2] = to_f32(r2);
     xv[3] = to_f32(r3);
   }
+  flag_nonfinite(nonfinite(xv[0]) || nonfinite(xv[1]) || nonfinite(xv[2]) || nonfinite(xv[3]), flags);
   float ss = wave_sum(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3]);
   const int nw = blockDim.x >> 6;
   if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -295,11 +319,16 @@ __device__ __forceinline__ unsigned long long commit_key(float h, int i) {
 // One workgroup of 1024 threads per canvas; N <= 1024.  Positions are padded
 // to whole waves (NR) and each gets 1024 / NR threads, which split the count
 // of the keys ranked before it.
+// The status word: workgroup 0 copies the flags the step's kernels raised
+// (live) to `published` and clears them for the next step; every kernel that
+// raises a flag ran before this one on the stream.  An argmax outside the
+// vocabulary (a row whose logits were all non-finite, already flagged)
+// commits id 0.
 __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int* am, int* tok,
                                                       uint8_t* committed, int N, int step,
                                                       int max_steps, float threshold, uint64_t seed,
                                                       uint32_t block, int vocab, int mask_token,
-                                                      int* n_unc) {
+                                                      int* n_unc, int* live, int* published) {
   __shared__ unsigned long long ks[1024];
   __shared__ int part_s[1024];
   __shared__ int red[16];
@@ -333,7 +362,8 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int*
     take = tot < m || hi < threshold;
   }
   if (take) {
-    tok[base + i] = am[base + i];
+    const int a = am[base + i];
+    tok[base + i] = (a >= 0 && a < vocab) ? a : 0;
     committed[base + i] = 1;
   }
   const bool still = unc && !take;
@@ -348,6 +378,10 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int*
     int Up = 0;
     for (int w = 0; w < 16; ++w) Up += red[w];
     n_unc[b] = Up;
+    if (b == 0 && live) {
+      if (published) *published = *live;
+      *live = 0;
+    }
   }
 }
 
@@ -360,12 +394,15 @@ __global__ void philox_kernel(uint64_t seed, uint32_t pos0, uint32_t tag, uint32
 
 }  // namespace
 
-int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st) {
+int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vocab, void* x, int* flags,
+                 hipStream_t st) {
   if (T <= 0) return 0;
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(T), dim3(256), 0, st, tok, T, (const bf16*)E, d, (bf16*)x);
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(T), dim3(256), 0, st, tok, T, (const bf16*)E, d, vocab, (bf16*)x,
+                       flags);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, st, tok, T, (const float*)E, d, (float*)x);
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, st, tok, T, (const float*)E, d, vocab,
+                       (float*)x, flags);
   return int(hipGetLastError());
 }
 
@@ -409,28 +446,29 @@ int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, const
 }
 
 int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
-                int T, int k, int d, hipStream_t st) {
+                int T, int k, int d, int* flags, hipStream_t st) {
   if (T <= 0) return 0;
+  if (!flags) return int(hipErrorInvalidValue);
   if (at == ACT_BF16 && d % 4 == 0)
     hipLaunchKernelGGL(combine_bf16_kernel, dim3(T, (d + 1023) / 1024), dim3(256), 0, st, (bf16*)x, y, ys, w,
-                       pos, k, d);
+                       pos, k, d, flags);
   else if (at == ACT_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16>, dim3(T), dim3(256), 0, st, (bf16*)x, y, ys, w, pos, k, d);
+    hipLaunchKernelGGL(combine_kernel<bf16>, dim3(T), dim3(256), 0, st, (bf16*)x, y, ys, w, pos, k, d, flags);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (float*)x, y, ys, w, pos, k, d);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, st, (float*)x, y, ys, w, pos, k, d, flags);
   return int(hipGetLastError());
 }
 
 int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
-                     int T, int k, int d, float eps, void* a, hipStream_t st) {
+                     int T, int k, int d, float eps, void* a, int* flags, hipStream_t st) {
   if (T <= 0) return 0;
   if (at == ACT_BF16 && d % 4 == 0 && d <= 4096 && k <= 8) {
     const int threads = ((d / 4 + 63) / 64) * 64;
     hipLaunchKernelGGL(combine_norm_bf16_kernel, dim3(T), dim3(threads), 0, st, (bf16*)x, y, ys, w, pos, k, d,
-                       eps, (bf16*)a);
+                       eps, (bf16*)a, flags);
     return int(hipGetLastError());
   }
-  int e = moe_combine(at, x, y, ys, w, pos, T, k, d, st);
+  int e = moe_combine(at, x, y, ys, w, pos, T, k, d, flags, st);
   if (e) return e;
   return rmsnorm(at, x, T, d, eps, a, st);
 }
@@ -450,10 +488,10 @@ int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const 
 
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N, int step,
                    int max_steps, float threshold, uint64_t seed, uint32_t block, int vocab, int mask_token,
-                   int* n_unc, hipStream_t st) {
+                   int* n_unc, int* live_flags, int* status, hipStream_t st) {
   if (N > 1024) return int(hipErrorInvalidValue);
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(1024), 0, st, H, am, tok, committed, N, step,
-                     max_steps, threshold, seed, block, vocab, mask_token, n_unc);
+                     max_steps, threshold, seed, block, vocab, mask_token, n_unc, live_flags, status);
   return int(hipGetLastError());
 }
 

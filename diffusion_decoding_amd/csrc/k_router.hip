@@ -84,6 +84,26 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, in
   }
 }
 
+// one thread per token: rows with forced[t][0] >= 0 take the forced ids (in
+// their slot order) and a softmax over those ids' logits, summed in slot order
+__global__ void force_kernel(const float* logits, int T, int E, int k, const int* forced, int* ids, float* w) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T || forced[t * k] < 0) return;
+  float sel[8];
+  float m = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    const int e = min(max(forced[t * k + j], 0), E - 1);
+    sel[j] = logits[(long long)t * E + e];
+    m = fmaxf(m, sel[j]);
+  }
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __expf(sel[j] - m);
+  for (int j = 0; j < k; ++j) {
+    ids[t * k + j] = min(max(forced[t * k + j], 0), E - 1);
+    w[t * k + j] = __expf(sel[j] - m) / sum;
+  }
+}
+
 constexpr int PERM_THREADS = 1024;
 constexpr int PERM_MAX_TOKENS = 1024;
 constexpr int PERM_WORDS = PERM_MAX_TOKENS / 64;
@@ -166,6 +186,13 @@ int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hi
     hipLaunchKernelGGL(topk_kernel<2>, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
   else
     hipLaunchKernelGGL(topk_kernel<4>, dim3(T), dim3(64), 0, st, logits, T, E, k, ids, w);
+  return int(hipGetLastError());
+}
+
+int router_force(const float* logits, int T, int E, int k, const int* forced, int* ids, float* w, hipStream_t st) {
+  if (T <= 0) return 0;
+  if (k > 8 || k > E) return int(hipErrorInvalidValue);
+  hipLaunchKernelGGL(force_kernel, dim3((T + 255) / 256), dim3(256), 0, st, logits, T, E, k, forced, ids, w);
   return int(hipGetLastError());
 }
 

@@ -104,6 +104,9 @@ __device__ __forceinline__ void lm_partials(const f32x4 (&acc)[FM][FN], const Ge
           }
         }
       }
+      // a lane with columns but none above -inf: all its logits are NaN or -inf
+      if (p.idx == INT_MAX && col0 + c16 < g.N && row0 + 16 * i + 4 * g4 + r < g.M && g.flags)
+        atomicOr(g.flags, FLAG_NONFINITE);
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) p = lm_combine(p, lm_shfl_xor(p, o));
       const int m = row0 + 16 * i + 4 * g4 + r;

@@ -8,6 +8,12 @@
 namespace dg {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+
+// Bits of the device status word the kernels of a step raise (atomic OR):
+// a non-finite value in the residual stream or in the logits, a token id
+// outside the vocabulary.
+constexpr int FLAG_NONFINITE = 1;
+constexpr int FLAG_TOKEN = 2;
 enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
 
 // ---------------------------------------------------------------- GEMM (k_gemm.hip)
@@ -36,6 +42,7 @@ struct GemmArgs {
   long long ldc = 0;
   int swiglu_half = 0;             // SWIGLU: B row of up_j is swiglu_half + j
   float* part = nullptr;           // EPI_LM partials [M][n_tiles][5]
+  int* flags = nullptr;            // EPI_LM: FLAG_NONFINITE when a lane's logits of a row are all NaN/-inf (nullable)
   // EPI_QKV: row m = canvas b * seq_n + token i; q -> q_out [B][heads][seq_n][128];
   // k, v -> (b, h) planes at k_dst / v_dst + (b * heads + h) * dst_bh + (row0 + i) * 128;
   // rope_tab [seq_n][64] (cos, sin) pairs
@@ -63,8 +70,9 @@ int lm_tiles(ActType at, int K, int vocab);
 bool tgemm_supported(ActType at, int K);
 int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st);
 int lm_tiles_tiled(int vocab, int K);
-// Merge LM partials of T rows into entropy / argmax / top-2 gap.
-int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap,
+// Merge LM partials of T rows into entropy / argmax / top-2 gap; FLAG_NONFINITE
+// (flags nullable) for a row whose entropy is not finite or that has no argmax.
+int lm_merge(const float* part, int T, int n_tiles, float* entropy, int* argmax, float* gap, int* flags,
              hipStream_t st);
 
 // ---------------------------------------------------------------- routed experts (k_moe.hip)
@@ -112,7 +120,9 @@ int attention(ActType at, const AttnArgs& a, hipStream_t st);
 int attn_splits_for(int B, int H, int n, int keys, int dh);
 
 // ---------------------------------------------------------------- misc (k_misc.hip)
-int embed_gather(ActType at, const int* tok, int T, const void* E, int d, void* x, hipStream_t st);
+// ids outside [0, vocab) read row 0 and raise FLAG_TOKEN in *flags (nullable)
+int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vocab, void* x, int* flags,
+                 hipStream_t st);
 int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st);
 // tab[i][j] = (cos, sin) of (pos0 + i) * theta^(-2j/dh), i < n, j < dh/2 (float pairs)
 int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st);
@@ -120,27 +130,34 @@ int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st)
 // q -> q_out [B][H][n][dh]; k,v -> (b,h) planes at kdst/vdst + (b*H+h)*dst_bh + (row0+i)*dh.
 int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, const float* tab, void* q_out,
                  void* kdst, void* vdst, long long dst_bh, int row0, hipStream_t st);
-// x[t] = round(x[t] + sum_j w[t][j] * y[pos[t][j]] + ys[t])
+// x[t] = round(x[t] + sum_j w[t][j] * y[pos[t][j]] + ys[t]); FLAG_NONFINITE in
+// *flags when an updated value is not finite
 int moe_combine(ActType at, void* x, const float* y, const float* ys, const float* w,
-                const int* pos, int T, int k, int d, hipStream_t st);
+                const int* pos, int T, int k, int d, int* flags, hipStream_t st);
 // moe_combine, then a = rmsnorm(x) of the updated rows (one fused kernel for bf16)
 int moe_combine_norm(ActType at, void* x, const float* y, const float* ys, const float* w, const int* pos,
-                     int T, int k, int d, float eps, void* a, hipStream_t st);
+                     int T, int k, int d, float eps, void* a, int* flags, hipStream_t st);
 // mask_token >= 0: absorbing-state noise (the canvas starts as [MASK] and
 // uncommitted positions return to it); -1: uniform Philox draws
 int canvas_init(int* tok, uint8_t* committed, int B, int N, uint64_t seed, uint32_t block,
                 int vocab, int mask_token, hipStream_t st);
 // tok[i] = given[i], committed[i] = 1 wherever mask[i] != 0 (i < n)
 int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const uint8_t* mask, hipStream_t st);
+// live_flags (nullable): the status word the step's kernels raised; it is
+// copied to *status (nullable) and cleared.
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N,
                    int step, int max_steps, float threshold, uint64_t seed, uint32_t block,
-                   int vocab, int mask_token, int* n_unc, hipStream_t st);
+                   int vocab, int mask_token, int* n_unc, int* live_flags, int* status, hipStream_t st);
 int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uint32_t block,
                 uint32_t modulus, int n, uint32_t* out, hipStream_t st);
 
 // ---------------------------------------------------------------- router (k_router.hip)
 // logits [T][E] fp32 -> ids [T][k], w [T][k]
 int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hipStream_t st);
+// Rows t with forced[t][0] >= 0 take the ids forced[t][0..k) in that slot order
+// and the softmax of their logits as weights (a test hook: lines the routing
+// up with a reference where two router logits nearly tie).
+int router_force(const float* logits, int T, int E, int k, const int* forced, int* ids, float* w, hipStream_t st);
 // ids [T][k] -> cnt[E], off[E+1], pair_row[T*k] (token of each pair slot, expert-major,
 // token-ascending), pos[T][k] (slot of pair (t, j)).
 int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,

@@ -140,24 +140,27 @@ def canvas_prefill(model: Model, canvas: Canvas, tokens: torch.Tensor, mask: tor
 
 
 def denoise_step(model: Model, canvas: Canvas, kv: KVCache, entropy=None, argmax=None, top2_gap=None,
-                 n_uncommitted=None, logits=None, hidden=None, stream=None):
+                 n_uncommitted=None, logits=None, hidden=None, status=None, stream=None):
     s = canvas.struct()
     out = dg_step_out(_ptr(entropy), _ptr(argmax), _ptr(top2_gap), _ptr(n_uncommitted), _ptr(logits),
-                      _ptr(hidden))
+                      _ptr(hidden), _ptr(status))
     _lib.dg_denoise_step(model.handle, s, kv.struct(), out, _stream(stream))
     canvas.step = s.step
 
 
 def generate_canvas(model: Model, canvas: Canvas, kv: KVCache, stream=None) -> int:
     s = canvas.struct()
-    taken = _lib.dg_generate_canvas(model.handle, s, kv.struct(), _stream(stream))
-    canvas.step = s.step
-    return taken
+    try:
+        return _lib.dg_generate_canvas(model.handle, s, kv.struct(), _stream(stream))
+    finally:
+        canvas.step = s.step   # steps that ran before an error still count
 
 
 def commit_canvas(model: Model, tokens: torch.Tensor, kv: KVCache, stream=None):
     if tokens.dtype != torch.int32 or tokens.dim() != 2:
         raise ValueError("tokens must be int32 [batch, n]")
+    if tokens.shape[0] != kv.k.shape[1]:
+        raise ValueError(f"tokens hold {tokens.shape[0]} canvases, the KV cache {kv.k.shape[1]}")
     s = kv.struct()
     _lib.dg_commit_canvas(model.handle, _ptr(tokens), tokens.shape[1], s, _stream(stream))
     kv.length = s.length
@@ -185,3 +188,68 @@ def test_commit(model: Model, canvas: Canvas, entropy: torch.Tensor, argmax: tor
     _lib.dg_test_commit(model.handle, canvas.struct(), _ptr(entropy), _ptr(argmax), _ptr(nunc),
                         _stream(stream))
     return nunc
+
+
+# ---- unit entries (tests): one phase of a block on given buffers
+
+def _dt(model: Model):
+    return torch.bfloat16 if model.cfg.act_dtype == "bf16" else torch.float32
+
+
+def test_qkv_rope(model: Model, layer: int, a: torch.Tensor, batch: int, pos0: int, stream=None):
+    cfg = model.cfg
+    n = a.shape[0] // batch
+    shp = (batch, cfg.n_heads, n, cfg.head_dim)
+    q, k, v = (torch.empty(shp, dtype=_dt(model), device=a.device) for _ in range(3))
+    _lib.dg_test_qkv_rope(model.handle, layer, _ptr(a), batch, n, pos0, _ptr(q), _ptr(k), _ptr(v),
+                          _stream(stream))
+    return q, k, v
+
+
+def test_attention(model: Model, layer: int, q: torch.Tensor, kv: KVCache, k_canvas=None, v_canvas=None,
+                   stream=None):
+    B, H, n, dh = q.shape
+    out = torch.empty(B * n, H * dh, dtype=_dt(model), device=q.device)
+    _lib.dg_test_attention(model.handle, layer, _ptr(q), kv.struct(), _ptr(k_canvas), _ptr(v_canvas), n,
+                           _ptr(out), _stream(stream))
+    return out
+
+
+def test_router(model: Model, layer: int, b: torch.Tensor, stream=None):
+    cfg, T = model.cfg, b.shape[0]
+    logits = torch.empty(T, cfg.n_experts, dtype=torch.float32, device=b.device)
+    ids = torch.empty(T, cfg.top_k, dtype=torch.int32, device=b.device)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=b.device)
+    _lib.dg_test_router(model.handle, layer, _ptr(b), T, _ptr(logits), _ptr(ids), _ptr(w), _stream(stream))
+    return logits, ids, w
+
+
+def test_shared(model: Model, layer: int, b: torch.Tensor, stream=None):
+    cfg, T = model.cfg, b.shape[0]
+    hs = torch.empty(T, cfg.d_shared, dtype=_dt(model), device=b.device)
+    ys = torch.empty(T, cfg.d_model, dtype=torch.float32, device=b.device)
+    _lib.dg_test_shared(model.handle, layer, _ptr(b), T, _ptr(hs), _ptr(ys), _stream(stream))
+    return hs, ys
+
+
+def test_moe(model: Model, layer: int, b: torch.Tensor, ids: torch.Tensor, stream=None):
+    cfg, T = model.cfg, b.shape[0]
+    if ids.dtype != torch.int32 or tuple(ids.shape) != (T, cfg.top_k):
+        raise ValueError(f"ids must be int32 [{T}, {cfg.top_k}]")
+    h = torch.empty(T * cfg.top_k, cfg.d_expert, dtype=_dt(model), device=b.device)
+    y = torch.empty(T * cfg.top_k, cfg.d_model, dtype=torch.float32, device=b.device)
+    pos = torch.empty(T, cfg.top_k, dtype=torch.int32, device=b.device)
+    _lib.dg_test_moe(model.handle, layer, _ptr(b), T, _ptr(ids), _ptr(h), _ptr(y), _ptr(pos), _stream(stream))
+    return h, y, pos
+
+
+def test_force_routing(model: Model, ids: Optional[torch.Tensor]):
+    """ids: int32 [n_layers, max_batch * canvas_len, top_k] (-1 rows: not forced), kept
+    referenced by the model while set; None turns forcing off."""
+    if ids is not None:
+        cfg = model.cfg
+        want = (cfg.n_layers, model.max_batch * cfg.canvas_len, cfg.top_k)
+        if ids.dtype != torch.int32 or tuple(ids.shape) != want:
+            raise ValueError(f"ids must be int32 {want}")
+    model._forced = ids
+    _lib.dg_test_force_routing(model.handle, _ptr(ids))

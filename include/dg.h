@@ -34,6 +34,13 @@
  *    call returns a negative dg_status, enqueues nothing, and leaves caller
  *    state unchanged; dg_last_error() then describes the failure (per thread).
  *  - Calls on one model must not overlap (the workspace is shared).
+ *  - Numeric and token faults are detected on the device: kernels raise bits
+ *    of a status word (DG_STATUS_*) in the model, and every denoise step
+ *    publishes the bits raised since the previous step (by its own kernels
+ *    and by any dg_commit_canvas in between) and clears them.
+ *    dg_generate_canvas reads the word back after each step and stops with
+ *    DG_ERR_NUMERIC or DG_ERR_INVALID_ARG; dg_denoise_step, which does not
+ *    wait for the device, copies it to dg_step_out.status.
  *
  * Layouts (row-major, innermost dimension last; T = batch * tokens):
  *  - activations/weights in `act_dtype` (FP32 or BF16); routed and shared
@@ -60,11 +67,17 @@ typedef enum {
   DG_ERR_HIP = -3,           /* a HIP runtime call failed (message in dg_last_error) */
   DG_ERR_OOM = -4,           /* workspace allocation failed */
   DG_ERR_STATE = -5,         /* step counter already at max_steps, or similar */
-  DG_ERR_NUMERIC = -6,       /* reserved: non-finite values detected */
+  DG_ERR_NUMERIC = -6,       /* non-finite values in the residual stream or the logits */
   DG_ERR_UNIMPLEMENTED = -7
 } dg_status;
 
 enum { DG_DTYPE_FP32 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP8_E4M3 = 2 };
+
+/* Bits of the device status word (dg_step_out.status). */
+enum {
+  DG_STATUS_NONFINITE = 1,  /* a NaN or infinity after a block's residual add, or among a row's logits */
+  DG_STATUS_TOKEN = 2       /* a token id outside [0, vocab) reached the embedding (row 0 was read) */
+};
 
 /* Model shape and decoding rule.  All fields are plain values (host). */
 typedef struct dg_config {
@@ -154,6 +167,7 @@ typedef struct dg_step_out {
   int32_t* n_uncommitted;  /* [batch] after this step's commit */
   float* logits;           /* test/diagnostic: [batch*canvas_len][vocab] fp32 (extra GEMM) */
   void* hidden;            /* test/diagnostic: final normed hidden [batch*canvas_len][d_model] */
+  int32_t* status;         /* [1] DG_STATUS_* bits raised since the previous step; 0 = clean */
 } dg_step_out;
 
 typedef struct dg_model dg_model;
@@ -165,8 +179,11 @@ const char* dg_version(void);
 
 /* Create a model over borrowed weights.  `max_batch` canvases per call and up
  * to `max_tokens` tokens per canvas in dg_commit_canvas (>= canvas_len) size
- * the workspace, which is allocated here once; `max_kv` bounds the KV rows
- * attention reads (capacity of the largest cache used).  max_batch x
+ * the workspace, which is allocated here once.  `max_kv` is the largest KV
+ * capacity (rows per layer, canvas and head) any call may pass: calls with a
+ * larger kv->capacity fail with DG_ERR_SHAPE.  0 takes the kernels' own
+ * limit, 2^31 / (head_dim x element size) rows (attention addresses a cache
+ * plane with 32-bit byte offsets); a larger max_kv is refused.  max_batch x
  * max(max_tokens, canvas_len) may be at most 2048 with bf16 activations and
  * 1024 with fp32 (DG_ERR_SHAPE otherwise).  Must be called with the target
  * device current. */
@@ -174,7 +191,10 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
                     int32_t max_tokens, int32_t max_kv, dg_model** out);
 int dg_model_destroy(dg_model* m);
 
-/* Draw the initial canvas (step_tag 0) and clear `committed`; sets step = 0. */
+/* Draw the initial canvas (step_tag 0) and clear `committed`; sets step = 0.
+ * The canvas starts as uniform random ids (DiffusionGemma解析,
+ * "换个路数：整片并行去噪的生成机制": generation starts from a canvas of random
+ * tokens), or as all [MASK] under absorbing-state noise. */
 int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream);
 
 /* Pre-commit known positions of a freshly initialised canvas (fill-in-the-
@@ -189,22 +209,41 @@ int dg_canvas_init(dg_model* m, dg_canvas* c, void* stream);
  * checked on the host (they are device-resident). */
 int dg_canvas_prefill(dg_model* m, dg_canvas* c, const int32_t* tokens, const uint8_t* mask, void* stream);
 
-/* One denoise step (forward, confidence, commit, re-noise) on every canvas of
- * `c` against the first kv->length cache rows.  Requires c->step < max_steps;
- * increments c->step.  kv->batch must equal c->batch. */
+/* One denoise step on every canvas of `c` against the first kv->length cache
+ * rows: the canvas refinement phase (ipcmen.com, "模型构建与底层优化": a
+ * request's canvas is refined with bidirectional attention; DiffusionGemma解析,
+ * "换个路数：整片并行去噪的生成机制": all positions are scored at once, ranked by
+ * entropy, the most certain frozen; ipcmen.com, "工作原理：并行精炼与自我修正":
+ * the uncertain positions are randomised again).  Forward over all positions
+ * (committed ones included), entropy and argmax per position, commit of the
+ * ceil(U / (max_steps - step)) lowest-entropy uncommitted positions plus those
+ * below commit_threshold, re-noise of the rest.  Requires c->step < max_steps
+ * (DG_ERR_STATE otherwise); increments c->step.  kv->batch must equal
+ * c->batch.  Asynchronous: the step's status word goes to out->status. */
 int dg_denoise_step(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, void* stream);
 
 /* Run denoise steps from the canvas's current state until every position of
- * every canvas is committed or max_steps is reached.  Blocks; writes the
- * number of steps this call ran to *steps_taken (host). */
+ * every canvas is committed or max_steps is reached (DiffusionGemma解析,
+ * "自适应停步机制": the loop stops as soon as the canvas is settled, after at
+ * most 48 steps).  Blocks: after each step it reads back the uncommitted
+ * counts and the status word; a raised DG_STATUS_NONFINITE returns
+ * DG_ERR_NUMERIC and DG_STATUS_TOKEN returns DG_ERR_INVALID_ARG, after the
+ * step that published it.  Writes the number of steps this call ran to
+ * *steps_taken (host), also on those errors. */
 int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* steps_taken,
                        void* stream);
 
 /* Causal pass over tokens[batch][n] (device) at positions kv->length ..
- * kv->length+n-1: writes their rotary-embedded keys and values into every
- * layer's cache rows [length, length+n) and advances kv->length by n.  Token i
- * attends to all cached rows and to new tokens j <= i.  Requires
- * length + n <= capacity and n <= max_tokens. */
+ * kv->length+n-1: the prompt read and block commit phases (ipcmen.com,
+ * "模型构建与底层优化"; zhichai.net 深度拆解, "Block-Autoregressive：块内并行，
+ * 块间串行": a committed canvas is encoded causally and appended to the KV
+ * cache before the next canvas starts).  Writes their rotary-embedded keys
+ * and values into every layer's cache rows [length, length+n) and advances
+ * kv->length by n.  Token i attends to all cached rows and to new tokens
+ * j <= i.  Requires length + n <= capacity <= max_kv and n <= max_tokens
+ * (DG_ERR_SHAPE, nothing enqueued).  Token ids are not checked on the host;
+ * an id outside the vocabulary reads row 0 and raises DG_STATUS_TOKEN, which
+ * the next denoise step publishes. */
 int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, void* stream);
 
 /* Rewrite n_mats row-major expert matrices src[n_mats][rows][cols] (BF16, or
@@ -250,6 +289,45 @@ int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int3
 /* Commit selection + re-noise alone, on given entropy/argmax [batch][canvas_len]. */
 int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_t* argmax,
                    int32_t* n_uncommitted, void* stream);
+
+/* Unit entries: one phase of block `layer` on caller buffers (device, in
+ * act_dtype unless stated), through the launches a denoise step makes; the
+ * model's workspace holds intermediates.  Row counts up to the workspace
+ * (max_batch x max(max_tokens, canvas_len)), else DG_ERR_SHAPE.
+ *
+ * dg_test_qkv_rope: a [batch*n][d_model] normed rows -> q [batch][H][n][dh]
+ * and k, v [batch][H][n][dh], q and k rotary-embedded at positions
+ * pos0 .. pos0+n-1 (n <= max_tokens). */
+int dg_test_qkv_rope(dg_model* m, int32_t layer, const void* a, int32_t batch, int32_t n, int32_t pos0,
+                     void* q, void* k, void* v, void* stream);
+/* dg_test_attention: q [kv->batch][H][n][dh] -> out [kv->batch*n][H*dh].
+ * With k_canvas/v_canvas ([kv->batch][H][n][dh]): bidirectional over cache
+ * rows [0, kv->length) of `layer` and the n canvas rows.  With both NULL:
+ * causal over cache rows [0, kv->length + n), query i seeing rows
+ * j <= kv->length + i (the new rows must already be in the cache). */
+int dg_test_attention(dg_model* m, int32_t layer, const void* q, const dg_kv* kv, const void* k_canvas,
+                      const void* v_canvas, int32_t n, void* out, void* stream);
+/* dg_test_router: b [T][d_model] normed rows -> fp32 router logits [T][E],
+ * top-k ids [T][k] (by logit, ties to the lower id) and weights [T][k] (a
+ * softmax over the picked logits). */
+int dg_test_router(dg_model* m, int32_t layer, const void* b, int32_t T, float* logits, int32_t* ids,
+                   float* weights, void* stream);
+/* dg_test_shared: b [T][d_model] -> hs [T][d_shared] (SwiGLU products) and
+ * ys [T][d_model] (fp32 shared-expert output). */
+int dg_test_shared(dg_model* m, int32_t layer, const void* b, int32_t T, void* hs, float* ys, void* stream);
+/* dg_test_moe: b [T][d_model] and top-k ids [T][k] (each in [0, n_experts),
+ * distinct within a row; not checked) -> y [T*k][d_model] fp32 expert outputs
+ * and, if h is not NULL, h [T*k][d_expert] SwiGLU products, both in pair
+ * order (expert-major, token-ascending); pos [T][k] gets the row of pair
+ * (t, j). */
+int dg_test_moe(dg_model* m, int32_t layer, const void* b, int32_t T, const int32_t* ids, void* h, float* y,
+                int32_t* pos, void* stream);
+/* dg_test_force_routing: from now on, denoise steps route row t of layer l to
+ * the ids ids[l][t][0..k) (device, [n_layers][max_batch*canvas_len][top_k],
+ * borrowed) wherever ids[l][t][0] >= 0, weighting them by a softmax over
+ * their logits; NULL turns it off.  Lines the routing up with a reference
+ * where two router logits nearly tie. */
+int dg_test_force_routing(dg_model* m, const int32_t* ids);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 from oracle import model as om
-from tests.parity import compare_step, to_host
+from tests.parity import compare_step, forced_routing, to_host
 from workloads import make_inputs
 
 
@@ -57,7 +57,9 @@ class Pair:
 
     def run_locked(self, block=0, max_steps=None, keep_logits=True, prefill=None):
         """Step-locked denoise loop; returns (step reports, oracle final state).
-        prefill: optional (tokens [B, N], mask [B, N]) of pre-committed positions."""
+        prefill: optional (tokens [B, N], mask [B, N]) of pre-committed positions.
+        Each step runs the oracle first, so that rows whose router logits
+        nearly tie can take the oracle's expert picks on the GPU."""
         rt, cfg = self.rt, self.cfg
         ost = om.init_state(cfg, cfg.seed, block)
         B, N = cfg.batch, cfg.canvas_len
@@ -70,28 +72,39 @@ class Pair:
                               torch.from_numpy(pmask.astype(np.uint8)).to("cuda"))
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+        np.testing.assert_array_equal(to_host(canvas.committed).astype(bool), ost.committed)
         ent = torch.empty(B, N, dtype=torch.float32, device="cuda")
         am = torch.empty(B, N, dtype=torch.int32, device="cuda")
         gap = torch.empty(B, N, dtype=torch.float32, device="cuda")
         nunc = torch.empty(B, dtype=torch.int32, device="cuda")
+        status = torch.empty(1, dtype=torch.int32, device="cuda")
+        act = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
+        hidden = torch.empty(B * N, cfg.d_model, dtype=act, device="cuda")
         logits = torch.empty(B * N, cfg.vocab, dtype=torch.float32, device="cuda") if keep_logits else None
         reps = []
-        for s in range(max_steps or cfg.max_steps):
-            say(f"  {cfg.name}: block {block} step {s}")
-            prev = ost.committed.copy()
-            rt.denoise_step(self.model, canvas, self.kv, entropy=ent, argmax=am, top2_gap=gap,
-                            n_uncommitted=nunc, logits=logits)
-            torch.cuda.synchronize()
-            ores = om.denoise_step(self.W, self.okv, ost, cfg, keep_logits=keep_logits)
-            gpu = dict(entropy=to_host(ent), argmax=to_host(am), tokens=to_host(canvas.tokens),
-                       committed=to_host(canvas.committed),
-                       logits=to_host(logits) if keep_logits else None)
-            rep = compare_step(cfg, ores, ost, gpu, prev)
-            say("   ", rep)
-            reps.append(rep)
-            assert canvas.step == ost.step
-            canvas.tokens.copy_(torch.from_numpy(ost.tokens.astype(np.int32)))
-            canvas.committed.copy_(torch.from_numpy(ost.committed.astype(np.uint8)))
-            if int(ores.n_uncommitted.sum()) == 0:
-                break
+        try:
+            for s in range(max_steps or cfg.max_steps):
+                say(f"  {cfg.name}: block {block} step {s}")
+                pre = ost.copy()
+                ores = om.denoise_step(self.W, self.okv, ost, cfg, keep_logits=keep_logits, keep_hidden=True)
+                forced, n_forced = forced_routing(ores.trace, cfg, B, N, self.model.max_batch * N)
+                rt.test_force_routing(self.model, torch.from_numpy(forced).to("cuda"))
+                rt.denoise_step(self.model, canvas, self.kv, entropy=ent, argmax=am, top2_gap=gap,
+                                n_uncommitted=nunc, logits=logits, hidden=hidden, status=status)
+                torch.cuda.synchronize()
+                assert int(to_host(status)[0]) == 0, f"step status {int(to_host(status)[0])}"
+                gpu = dict(entropy=to_host(ent), argmax=to_host(am), tokens=to_host(canvas.tokens),
+                           committed=to_host(canvas.committed), hidden=to_host(hidden.float()),
+                           logits=to_host(logits) if keep_logits else None)
+                rep = compare_step(cfg, ores, pre, ost, gpu, W=self.W)
+                rep.forced_rows = n_forced
+                say("   ", rep)
+                reps.append(rep)
+                assert canvas.step == ost.step
+                canvas.tokens.copy_(torch.from_numpy(ost.tokens.astype(np.int32)))
+                canvas.committed.copy_(torch.from_numpy(ost.committed.astype(np.uint8)))
+                if int(ores.n_uncommitted.sum()) == 0:
+                    break
+        finally:
+            rt.test_force_routing(self.model, None)
         return reps, ost

@@ -14,7 +14,7 @@ import torch
 from oracle import model as om
 from oracle import philox
 from tests.gpu_helpers import Pair
-from tests.parity import H_TOL, compare_step, h_tol, logits_tol, to_host
+from tests.parity import H_TOL, assert_reports, to_host
 from workloads import get_config, make_inputs, tiny_config
 
 pytestmark = pytest.mark.gpu
@@ -89,53 +89,16 @@ def test_commit_kernel_bit_exact(rt):
 # ----------------------------------------------------------------------------- step-locked loop
 
 def _run_locked(rt, cfg, max_steps=None, keep_logits=True, kv_capacity=None):
-    inp, model, kv = _gpu_setup(rt, cfg, kv_capacity=kv_capacity)
-    W = om.Weights(inp, cache=True)
-    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=cfg.act_dtype == "bf16")
-    ost = om.init_state(cfg, cfg.seed)
-    B, N = cfg.batch, cfg.canvas_len
-    canvas = rt.Canvas.empty(B, N, cfg.seed)
-    rt.canvas_init(model, canvas)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
-    ent = torch.empty(B, N, dtype=torch.float32, device="cuda")
-    am = torch.empty(B, N, dtype=torch.int32, device="cuda")
-    gap = torch.empty(B, N, dtype=torch.float32, device="cuda")
-    nunc = torch.empty(B, dtype=torch.int32, device="cuda")
-    logits = torch.empty(B * N, cfg.vocab, dtype=torch.float32, device="cuda") if keep_logits else None
-    reps = []
-    steps = max_steps or cfg.max_steps
-    for s in range(steps):
-        say(f"  {cfg.name}: step {s}")
-        prev = ost.committed.copy()
-        rt.denoise_step(model, canvas, kv, entropy=ent, argmax=am, top2_gap=gap, n_uncommitted=nunc,
-                        logits=logits)
-        torch.cuda.synchronize()
-        ores = om.denoise_step(W, okv, ost, cfg, keep_logits=keep_logits)
-        gpu = dict(entropy=to_host(ent), argmax=to_host(am), tokens=to_host(canvas.tokens),
-                   committed=to_host(canvas.committed),
-                   logits=to_host(logits) if keep_logits else None)
-        rep = compare_step(cfg, ores, ost, gpu, prev)
-        say("   ", rep)
-        reps.append(rep)
-        assert canvas.step == ost.step
-        # resync to the oracle's state
-        canvas.tokens.copy_(torch.from_numpy(ost.tokens.astype(np.int32)))
-        canvas.committed.copy_(torch.from_numpy(ost.committed.astype(np.uint8)))
-        if int(ores.n_uncommitted.sum()) == 0:
-            break
-    model.close()
+    p = Pair(rt, cfg, kv_capacity=kv_capacity)
+    try:
+        reps, _ = p.run_locked(max_steps=max_steps, keep_logits=keep_logits)
+    finally:
+        p.close()
     return reps
 
 
 def _assert_reports(cfg, reps):
-    for r in reps:
-        if not math.isnan(r.logits_rel):
-            assert r.logits_rel <= logits_tol(cfg), r
-        assert r.max_dH <= h_tol(cfg), r
-        assert r.mism_argmax == 0, r
-        assert r.mism_commit == 0, r
-        assert r.mism_tokens == 0, r
+    assert_reports(cfg, reps)
 
 
 def test_c0_loop_step_locked(rt):
@@ -394,3 +357,109 @@ def test_c1_single_step(rt):
     say("c1 single denoise step (bf16, 1 layer, P=1024, 128 experts, V=262144)")
     reps = _run_locked(rt, cfg, max_steps=1)
     _assert_reports(cfg, reps)
+
+
+# ----------------------------------------------------------------------------- error contract
+
+def _status_of_step(rt, model, canvas, kv):
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rt.denoise_step(model, canvas, kv, status=st)
+    torch.cuda.synchronize()
+    return int(to_host(st)[0])
+
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_nonfinite_logits_return_numeric_error(rt, act):
+    """A NaN in one LM-head row makes that logit NaN in every row: the step's
+    status carries DG_STATUS_NONFINITE and dg_generate_canvas stops with
+    DG_ERR_NUMERIC after the first step."""
+    from diffusion_decoding_amd._lib import DG_ERR_NUMERIC, DG_STATUS_NONFINITE, DGError
+    cfg = tiny_config(name=f"tiny_nan_lm_{act}", act_dtype=act, expert_dtype=act, head_dim=32, n_heads=2,
+                      lm_scale=1.0)
+    inp, model, kv = _gpu_setup(rt, cfg)
+    inp.lm_head[7, 3] = float("nan")
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    assert _status_of_step(rt, model, canvas, kv) & DG_STATUS_NONFINITE
+    rt.canvas_init(model, canvas)
+    with pytest.raises(DGError) as e:
+        rt.generate_canvas(model, canvas, kv)
+    assert e.value.status == DG_ERR_NUMERIC and "non-finite" in str(e.value)
+    assert canvas.step == 1
+    model.close()
+
+
+def test_nonfinite_shared_expert_is_flagged_by_the_combine(rt):
+    from diffusion_decoding_amd._lib import DG_ERR_NUMERIC, DG_STATUS_NONFINITE, DGError
+    cfg = get_config("c0").replace(name="c0_nan_shared")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    inp.layers[0]["ws_d"][5, :] = float("inf")
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    assert _status_of_step(rt, model, canvas, kv) & DG_STATUS_NONFINITE
+    rt.canvas_init(model, canvas)
+    with pytest.raises(DGError) as e:
+        rt.generate_canvas(model, canvas, kv)
+    assert e.value.status == DG_ERR_NUMERIC
+    model.close()
+
+
+def test_clean_step_has_zero_status(rt):
+    cfg = get_config("c0")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    assert _status_of_step(rt, model, canvas, kv) == 0
+    model.close()
+
+
+def test_token_out_of_range_is_reported_by_the_next_step(rt):
+    """Ids outside the vocabulary in a commit pass read embedding row 0 (no
+    access past the table) and raise DG_STATUS_TOKEN, which the next step
+    publishes and clears; dg_generate_canvas turns it into DG_ERR_INVALID_ARG."""
+    from diffusion_decoding_amd._lib import DG_ERR_INVALID_ARG, DG_STATUS_TOKEN, DGError
+    cfg = tiny_config(name="tiny_bad_token", prompt_mode="tokens", prompt_len=20, n_canvases=1)
+    inp = make_inputs(cfg, device="cuda")
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k.clone(), inp.kv_v.clone(), 0)
+    bad = inp.prompt_tokens.clone()
+    bad[0, 4] = cfg.vocab + 5
+    bad[0, 9] = -3
+    rt.commit_canvas(model, bad, kv)
+    assert kv.length == 20
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    assert _status_of_step(rt, model, canvas, kv) == DG_STATUS_TOKEN
+    assert _status_of_step(rt, model, canvas, kv) == 0          # cleared by the step that published it
+    rt.commit_canvas(model, bad[:, :4].contiguous(), kv)       # clean ids
+    with pytest.raises(ValueError):                             # two canvases for a one-canvas cache
+        rt.commit_canvas(model, bad[:, :1].repeat(2, 1).contiguous(), kv)
+    rt.commit_canvas(model, bad[:, 4:6].contiguous(), kv)       # carries vocab + 5
+    rt.canvas_init(model, canvas)
+    with pytest.raises(DGError) as e:
+        rt.generate_canvas(model, canvas, kv)
+    assert e.value.status == DG_ERR_INVALID_ARG and "token id" in str(e.value)
+    model.close()
+
+
+def test_kv_overflow_and_max_kv_are_refused(rt):
+    from diffusion_decoding_amd._lib import DG_ERR_SHAPE, DGError
+    cfg = tiny_config(name="tiny_kv_limits", prompt_mode="tokens", prompt_len=70, n_canvases=1)
+    inp = make_inputs(cfg, device="cuda", kv_capacity=80)
+    model = rt.Model(inp)
+    kv = rt.KVCache(inp.kv_k.clone(), inp.kv_v.clone(), 0)
+    rt.commit_canvas(model, inp.prompt_tokens, kv)
+    assert kv.length == 70
+    extra = torch.zeros(1, cfg.canvas_len, dtype=torch.int32, device="cuda")
+    with pytest.raises(DGError) as e:                           # 70 + 16 > 80
+        rt.commit_canvas(model, extra, kv)
+    assert e.value.status == DG_ERR_SHAPE and kv.length == 70
+    model.close()
+    small = rt.Model(inp, max_kv=50)                            # the cache holds 80 rows
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(small, canvas)
+    with pytest.raises(DGError) as e:
+        rt.denoise_step(small, canvas, kv)
+    assert e.value.status == DG_ERR_SHAPE and "max_kv" in str(e.value)
+    small.close()
+    torch.cuda.synchronize()

@@ -14,7 +14,7 @@ import torch
 
 from oracle import model as om
 from tests.gpu_helpers import Pair, say
-from tests.parity import h_tol, logits_tol, to_host
+from tests.parity import assert_reports, to_host
 from workloads import get_config, make_inputs, tiny_config
 
 pytestmark = pytest.mark.gpu
@@ -28,13 +28,7 @@ def rt():
 
 
 def _assert_reports(cfg, reps):
-    for r in reps:
-        if not math.isnan(r.logits_rel):
-            assert r.logits_rel <= logits_tol(cfg), r
-        assert r.max_dH <= h_tol(cfg), r
-        assert r.mism_argmax == 0, r
-        assert r.mism_commit == 0, r
-        assert r.mism_tokens == 0, r
+    assert_reports(cfg, reps)
 
 
 def _free():
@@ -270,4 +264,29 @@ def test_c2_full_loop_properties(rt):
     np.testing.assert_array_equal(to_host(canvas2.tokens), final)
     model.close()
     del model, inp, kv
+    _free()
+
+
+def test_c4_full_width_fp8_block(rt):
+    """The block-autoregressive fp8 workload at full width (d_model 2048, 128
+    fp8 E4M3 experts top-8 with d_expert 704, fp8 shared expert 2048), two
+    layers and a short vocabulary: the 512-token causal prompt encode, one
+    locked denoise step over the 512 cached rows, and the commit pass that
+    appends the canvas (KV compared after each pass)."""
+    cfg = get_config("c4").replace(name="c4_2_layers", n_layers=2, vocab=8192, n_canvases=1)
+    say("c4 shape (fp8 experts), 2 layers: prompt encode 512, one step, commit pass")
+    p = Pair(rt, cfg, kv_len=0)
+    p.commit(p.inp.prompt_tokens.cpu().numpy())
+    rel = p.kv_rel()
+    say(f"   prompt KV rel-L2 {rel}")
+    assert p.kv.length == 512 and max(rel) <= 1e-2
+    p.resync_kv()
+    reps, ost = p.run_locked(max_steps=1)
+    _assert_reports(cfg, reps)
+    p.commit(ost.tokens)
+    rel = p.kv_rel()
+    say(f"   canvas appended: KV length {p.kv.length}, rel-L2 {rel}")
+    assert p.kv.length == 768 and max(rel) <= 1e-2
+    p.close()
+    del p
     _free()

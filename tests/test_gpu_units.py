@@ -1,0 +1,272 @@
+"""Kernel unit parity at full width: each phase of a block runs through its
+dg_test_* entry (the same launches a denoise step makes) on inputs that are
+the oracle's exact bf16 values, and is compared element by element with the
+oracle's float64 result.  bf16 outputs must be the oracle's rounding except
+within the stated fp32 error bound of a rounding boundary (tests/unit_ref.py
+derives the bounds); fp32 outputs must lie within the bound; integer results
+(top-k ids, the expert-major pair order) must be bit-exact except where two
+router logits lie within the stated fp32 window (1e-5) of each other.
+
+Shapes: the 2048-wide layer of the benchmark workloads -- a 256-token canvas
+(batch 1), 1024 pooled tokens (batch 4) and a ragged 200-token canvas -- with
+bf16 experts, and fp8 E4M3 routed and shared experts at the same width."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from oracle.numerics import round_bf16, round_fp32
+from tests.gpu_helpers import say
+from tests.parity import to_host
+from tests.unit_ref import attention_ref, check_bf16, check_f32, gemm_tol, qkv_rope_ref, swiglu_ref
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+ROUTER_EPS = 1e-5   # stated fp32 window for the router's top-k
+
+
+@pytest.fixture(scope="module")
+def rt():
+    from diffusion_decoding_amd import runtime
+    runtime._lib.load()
+    return runtime
+
+
+def _unit_cfg(kind: str):
+    """One 2048-wide layer with a short vocabulary (the LM head is not used)."""
+    if kind == "bf16":
+        return get_config("c1").replace(name="unit_bf16", vocab=8192, batch=4, prompt_len=8192)
+    if kind == "fp8":
+        return get_config("c4").replace(name="unit_fp8", n_layers=1, vocab=8192, n_canvases=1)
+    raise ValueError(kind)
+
+
+class Unit:
+    def __init__(self, rt, kind: str, kv_capacity=None):
+        self.rt = rt
+        self.cfg = _unit_cfg(kind)
+        say(f"[unit] inputs for {self.cfg.name}")
+        self.inp = make_inputs(self.cfg, device="cuda", kv_capacity=kv_capacity)
+        self.model = rt.Model(self.inp, max_batch=4, max_tokens=512)
+        self.W = om.Weights(self.inp)
+
+    def close(self):
+        self.model.close()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def unit_bf16(rt):
+    u = Unit(rt, "bf16", kv_capacity=8192 + 256)
+    yield u
+    u.close()
+
+
+@pytest.fixture(scope="module")
+def unit_fp8(rt):
+    u = Unit(rt, "fp8")
+    yield u
+    u.close()
+
+
+def _dev(x: np.ndarray) -> torch.Tensor:
+    """bf16-valued float64 array -> bf16 device tensor (exact)."""
+    assert np.array_equal(round_bf16(x), x)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
+
+
+def _host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _normed_rows(seed: int, T: int, d: int) -> np.ndarray:
+    x = np.random.default_rng(seed).standard_normal((T, d))
+    return round_bf16(om.rmsnorm(x, 1e-6))
+
+
+def _report(what, nmis, nflag, total):
+    say(f"   {what}: {nmis} of {total} differ from the oracle's rounding, {nflag} within the bound of a boundary")
+
+
+# ----------------------------------------------------------------------------- QKV + RoPE
+
+@pytest.mark.parametrize("B,n,pos0", [(1, 256, 1024), (4, 256, 8192), (1, 200, 300)])
+def test_qkv_rope_unit(rt, unit_bf16, B, n, pos0):
+    u, cfg = unit_bf16, unit_bf16.cfg
+    H, dh = cfg.n_heads, cfg.head_dim
+    say(f"QKV + RoPE unit: {B} x {n} rows at positions {pos0}..")
+    a = _normed_rows(100 + B * n, B * n, cfg.d_model)
+    q, k, v = rt.test_qkv_rope(u.model, 0, _dev(a), B, pos0)
+    torch.cuda.synchronize()
+    ref = qkv_rope_ref(a, u.W.dense(0, "wqkv"), B, n, H, dh, pos0, cfg.rope_theta)
+    for name, got in (("q", q), ("k", k), ("v", v)):
+        pre, tol, chk = ref[name]
+        nmis, nflag = check_bf16(_host(got), pre, tol, f"{name} (B={B}, n={n})", mask=chk)
+        _report(f"{name} ({int(chk.sum())} checked)", nmis, nflag, int(chk.sum()))
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _bf16_normal(seed, shape):
+    return round_bf16(np.random.default_rng(seed).standard_normal(shape))
+
+
+@pytest.mark.parametrize("B,P,n,causal", [(1, 1024, 256, False), (4, 8192, 256, False), (1, 300, 200, False),
+                                          (1, 512, 256, True), (2, 70, 200, True)])
+def test_attention_unit(rt, unit_bf16, B, P, n, causal):
+    u, cfg = unit_bf16, unit_bf16.cfg
+    H, dh = cfg.n_heads, cfg.head_dim
+    say(f"attention unit: batch {B}, {P} cache rows, {n} queries, {'causal' if causal else 'bidirectional'}")
+    q = _bf16_normal(200 + P, (B, H, n, dh))
+    kc = _bf16_normal(201 + P, (B, H, n, dh))
+    vc = _bf16_normal(202 + P, (B, H, n, dh))
+    kvk, kvv = u.inp.kv_k[:, :B].clone(), u.inp.kv_v[:, :B].clone()
+    if causal:
+        # the new rows sit in the cache at [P, P + n), as a commit pass writes them
+        kvk[0, :, :, P:P + n] = _dev(kc)
+        kvv[0, :, :, P:P + n] = _dev(vc)
+        kv = rt.KVCache(kvk, kvv, P)
+        out = rt.test_attention(u.model, 0, _dev(q), kv)
+    else:
+        kv = rt.KVCache(kvk, kvv, P)
+        out = rt.test_attention(u.model, 0, _dev(q), kv, _dev(kc), _dev(vc))
+    torch.cuda.synchronize()
+    got = _host(out).reshape(B, n, H, dh)
+    cache_k = kvk[0].double().cpu().numpy()
+    cache_v = kvv[0].double().cpu().numpy()
+    pre = np.empty_like(got)
+    tol = np.empty_like(got)
+    for b in range(B):
+        for h in range(H):
+            if causal:
+                K, V = cache_k[b, h, :P + n], cache_v[b, h, :P + n]
+            else:
+                K = np.concatenate([cache_k[b, h, :P], kc[b, h]])
+                V = np.concatenate([cache_v[b, h, :P], vc[b, h]])
+            o, t = attention_ref(q[b, h], K, V, causal_start=P if causal else None)
+            pre[b, :, h], tol[b, :, h] = o, t
+    nmis, nflag = check_bf16(got, pre, tol, f"attention B={B} P={P} n={n}")
+    _report("attention output", nmis, nflag, got.size)
+
+
+# ----------------------------------------------------------------------------- router
+
+@pytest.mark.parametrize("T", [256, 1024])
+def test_router_unit(rt, unit_bf16, T):
+    """Router logits (fp32; at 256 rows they ride as extra tiles in the shared
+    gate/up launch, at 1024 they have a launch of their own), top-k ids and
+    weights."""
+    u, cfg = unit_bf16, unit_bf16.cfg
+    k = cfg.top_k
+    say(f"router unit: {T} rows, {cfg.n_experts} experts, top-{k}")
+    b = _normed_rows(300 + T, T, cfg.d_model)
+    logits, ids, w = rt.test_router(u.model, 0, _dev(b))
+    torch.cuda.synchronize()
+    wr = u.W.dense(0, "wr")
+    r = b @ wr.T
+    ratio = check_f32(to_host(logits), r, gemm_tol(b, wr, r), "router logits")
+    oids, ow = om.route(round_fp32(r), k)
+    srt = -np.sort(-round_fp32(r), axis=1)
+    tie = (srt[:, k - 1] - srt[:, k]) < ROUTER_EPS
+    gi, gw = to_host(ids), to_host(w)
+    ok = ~tie
+    np.testing.assert_array_equal(gi[ok], oids[ok])
+    np.testing.assert_allclose(gw[ok], ow[ok], rtol=0, atol=1e-6)
+    say(f"   logits within {ratio:.2e} of the bound; {int(tie.sum())} rows with a near-tie (< {ROUTER_EPS}), "
+        f"{int(ok.sum())} rows bit-exact ids")
+
+
+# ----------------------------------------------------------------------------- shared expert
+
+def _shared_case(rt, u, T):
+    cfg = u.cfg
+    b = _normed_rows(400 + T, T, cfg.d_model)
+    hs, ys = rt.test_shared(u.model, 0, _dev(b))
+    torch.cuda.synchronize()
+    h_pre, h_tol = swiglu_ref(b, u.W.dense(0, "ws_gu"))
+    nmis, nflag = check_bf16(_host(hs), h_pre, h_tol, "shared SwiGLU products")
+    _report("shared h", nmis, nflag, h_pre.size)
+    hg = _host(hs)
+    wd = u.W.dense(0, "ws_d")
+    ref = hg @ wd.T
+    ratio = check_f32(to_host(ys), ref, gemm_tol(hg, wd, ref), "shared down (from the GPU's h)")
+    say(f"   shared down within {ratio:.2e} of the bound")
+
+
+@pytest.mark.parametrize("T", [256, 1024])
+def test_shared_unit_bf16(rt, unit_bf16, T):
+    say(f"shared expert unit (bf16): {T} rows")
+    _shared_case(rt, unit_bf16, T)
+
+
+def test_shared_unit_fp8(rt, unit_fp8):
+    say("shared expert unit (fp8 E4M3 weights, per-row scales): 256 rows")
+    _shared_case(rt, unit_fp8, 256)
+
+
+# ----------------------------------------------------------------------------- routed experts
+
+def _moe_case(rt, u, b, ids):
+    cfg = u.cfg
+    T, k, E = ids.shape[0], cfg.top_k, cfg.n_experts
+    h, y, pos = rt.test_moe(u.model, 0, _dev(b), torch.from_numpy(ids.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    hg, yg, pg = _host(h), to_host(y).astype(np.float64), to_host(pos)
+    # pair order: expert-major, token-ascending (unique), bit-exact
+    order = sorted(((int(ids[t, j]), t, j) for t in range(T) for j in range(k)))
+    want = np.empty((T, k), dtype=np.int64)
+    for r, (_, t, j) in enumerate(order):
+        want[t, j] = r
+    np.testing.assert_array_equal(pg, want)
+    nmis = nflag = 0
+    worst = 0.0
+    for e in range(E):
+        ts, js = np.nonzero(ids == e)
+        if ts.size == 0:
+            continue
+        w_gu, w_d = u.W.expert(0, e)
+        rows = pg[ts, js]
+        h_pre, h_tol = swiglu_ref(b[ts], w_gu)
+        a, f = check_bf16(hg[rows], h_pre, h_tol, f"expert {e} SwiGLU products", max_frac=1.0)
+        nmis, nflag = nmis + a, nflag + f
+        ref = hg[rows] @ w_d.T
+        worst = max(worst, check_f32(yg[rows], ref, gemm_tol(hg[rows], w_d, ref), f"expert {e} down"))
+    assert nmis <= 5e-3 * hg.size, nmis
+    _report("routed h", nmis, nflag, hg.size)
+    say(f"   routed down (from the GPU's h) within {worst:.2e} of the bound")
+
+
+def _oracle_ids(u, b):
+    r32 = round_fp32(b @ u.W.dense(0, "wr").T)
+    ids, _ = om.route(r32, u.cfg.top_k)
+    return ids
+
+
+@pytest.mark.parametrize("T", [256, 1024])
+def test_moe_unit_bf16(rt, unit_bf16, T):
+    """256 rows: about 16 pairs per expert, one pass each; 1024 rows (four
+    canvases pooled): about 64 pairs per expert, the pooled 96-token passes."""
+    say(f"routed experts unit (bf16): {T} rows, routing from the oracle's router")
+    b = _normed_rows(500 + T, T, unit_bf16.cfg.d_model)
+    _moe_case(rt, unit_bf16, b, _oracle_ids(unit_bf16, b))
+
+
+def test_moe_unit_bf16_skewed(rt, unit_bf16):
+    """Every one of 256 rows routed to the same 8 experts (as when every open
+    position holds the same token): 256 pairs on each, so each expert runs
+    eight 32-token passes, the third and later spread over the grid."""
+    say("routed experts unit (bf16): 256 rows all on experts 3, 10, .., 52")
+    cfg = unit_bf16.cfg
+    b = _normed_rows(600, 256, cfg.d_model)
+    ids = np.tile(np.array([3 + 7 * j for j in range(cfg.top_k)]), (256, 1))
+    _moe_case(rt, unit_bf16, b, ids)
+
+
+def test_moe_unit_fp8(rt, unit_fp8):
+    """fp8 E4M3 routed experts at full width: 16 codes per lane-load in both
+    the gate/up (K = 2048) and the down kernel (K = d_expert = 704)."""
+    say("routed experts unit (fp8): 256 rows")
+    b = _normed_rows(700, 256, unit_fp8.cfg.d_model)
+    _moe_case(rt, unit_fp8, b, _oracle_ids(unit_fp8, b))
