@@ -86,6 +86,7 @@ _SIGS = {
     "dg_test_moe": [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                     c_void_p],
     "dg_test_force_routing": [c_void_p, c_void_p],
+    "dg_lm_head_confidence_noalloc": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
 }
 ENTRY_POINTS = ("dg_status_str", "dg_last_error", "dg_version", *_SIGS.keys())
 
@@ -210,3 +211,7 @@ def dg_test_moe(handle, layer, b_ptr, T, ids_ptr, h_ptr, y_ptr, pos_ptr, stream)
 
 def dg_test_force_routing(handle, ids_ptr):
     _call("dg_test_force_routing", handle, ids_ptr)
+
+
+def dg_lm_head_confidence_noalloc(handle, hf_ptr, T, ent_ptr, am_ptr, gap_ptr, stream):
+    _call("dg_lm_head_confidence_noalloc", handle, hf_ptr, T, ent_ptr, am_ptr, gap_ptr, stream)

@@ -552,6 +552,17 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
     }
   }
   m->n_unc = m->ctl + 2;
+  {
+    // set-up of the allocation-free entry on this device: the address of its
+    // static scratch (a lookup, no allocation)
+    void* sp = nullptr;
+    const int e = noalloc_scratch(&sp);
+    if (e) {
+      free_all(m);
+      delete m;
+      return fail(DG_ERR_HIP, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(hipError_t(e)));
+    }
+  }
   if (hipMemset(m->ctl, 0, sizeof(int) * (2 + max_batch)) != hipSuccess) {
     (void)hipGetLastError();
     free_all(m);
@@ -719,6 +730,26 @@ int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int3
   if (!m || !hf) return fail(DG_ERR_INVALID_ARG, "null argument");
   if (T <= 0 || T > m->max_batch * m->cfg.canvas_len) return fail(DG_ERR_SHAPE, "T=%d out of range", T);
   return lm_head_confidence(m, hf, T, entropy, argmax, top2_gap, (hipStream_t)stream);
+}
+
+int dg_lm_head_confidence_noalloc(const dg_model* m, const void* hf, int32_t T, float* entropy, int32_t* argmax,
+                                  float* top2_gap, void* stream) {
+  if (!m || !hf || !entropy || !argmax) return fail(DG_ERR_INVALID_ARG, "null argument");
+  if (T <= 0) return fail(DG_ERR_SHAPE, "T=%d must be positive", T);
+  const size_t per_row = (size_t)m->lm_ntiles * 5 * sizeof(float);
+  if ((size_t)T * per_row > NOALLOC_SCRATCH_BYTES)
+    return fail(DG_ERR_SHAPE, "%d rows need %zu bytes of partials; the static scratch holds %zu (%zu rows at %d ids)",
+                T, (size_t)T * per_row, NOALLOC_SCRATCH_BYTES, NOALLOC_SCRATCH_BYTES / per_row, m->cfg.vocab);
+  void* sp = nullptr;
+  HIP_OK(noalloc_scratch(&sp));
+  hipStream_t st = (hipStream_t)stream;
+  const dg_config& c = m->cfg;
+  GemmArgs g;
+  g.A = hf; g.lda = c.d_model; g.B = m->lm_head; g.ldb = c.d_model; g.M = T; g.N = c.vocab;
+  g.K = c.d_model; g.part = (float*)sp;
+  HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_LM, g, 1, st));
+  HIP_OK(lm_merge((const float*)sp, T, m->lm_ntiles, entropy, argmax, top2_gap, nullptr, st));
+  return DG_OK;
 }
 
 int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_t* argmax,

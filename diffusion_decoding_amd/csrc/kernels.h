@@ -119,6 +119,15 @@ struct AttnArgs {
 int attention(ActType at, const AttnArgs& a, hipStream_t st);
 int attn_splits_for(int B, int H, int n, int keys, int dh);
 
+// ---------------------------------------------------------------- static scratch (k_scratch.hip)
+// Bytes of the file-scope device array the allocation-free LM-head entry
+// keeps its partials in: T x (LM tiles) x 5 floats, 40 KB per row at 262144
+// ids, so one 256-position canvas fits.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+// Device address of that array on the current device (looked up with
+// hipGetSymbolAddress on a device's first call and kept).  0 or a HIP error.
+int noalloc_scratch(void** ptr);
+
 // ---------------------------------------------------------------- misc (k_misc.hip)
 // ids outside [0, vocab) read row 0 and raise FLAG_TOKEN in *flags (nullable)
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vocab, void* x, int* flags,

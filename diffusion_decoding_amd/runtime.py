@@ -183,6 +183,13 @@ def test_lm_head(model: Model, hf: torch.Tensor, stream=None):
     return ent, am, gap
 
 
+def lm_head_confidence_noalloc(model: Model, hf: torch.Tensor, entropy: torch.Tensor, argmax: torch.Tensor,
+                               top2_gap: Optional[torch.Tensor] = None, stream=None):
+    """The allocation-free LM head + confidence: outputs are the caller's tensors."""
+    _lib.dg_lm_head_confidence_noalloc(model.handle, _ptr(hf), hf.shape[0], _ptr(entropy), _ptr(argmax),
+                                       _ptr(top2_gap), _stream(stream))
+
+
 def test_commit(model: Model, canvas: Canvas, entropy: torch.Tensor, argmax: torch.Tensor, stream=None):
     nunc = torch.empty(canvas.tokens.shape[0], dtype=torch.int32, device=entropy.device)
     _lib.dg_test_commit(model.handle, canvas.struct(), _ptr(entropy), _ptr(argmax), _ptr(nunc),

@@ -253,6 +253,22 @@ int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, v
 int dg_pack_experts(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
                     int32_t dtype, void* stream);
 
+/* Allocation-free variant of dg_test_lm_head, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the fused LM head + confidence on given
+ * normed hidden rows hf[T][d_model] (act_dtype, device) with the model's
+ * LM-head weights, writing entropy[T], argmax[T] and (if not NULL)
+ * top2_gap[T].  Its per-(row, column tile) partials live in a static device
+ * array of 16 MiB instead of the model's workspace: T x 20 bytes per LM tile
+ * (40 KB per row at 262144 ids, so up to 409 rows there); a larger T fails
+ * with DG_ERR_SHAPE before anything is enqueued.  It calls no allocator.  The
+ * array is one per GPU and shared by every call on it: calls that overlap on
+ * one GPU (other streams, other threads, other models) race on it.  Nothing
+ * in it needs clearing -- each call writes every partial it reads.
+ * Stream-ordered; results equal dg_test_lm_head's bit for bit. */
+int dg_lm_head_confidence_noalloc(const dg_model* m, const void* hf, int32_t T, float* entropy, int32_t* argmax,
+                                  float* top2_gap, void* stream);
+
 /* ---- kernel timing ---------------------------------------------------------
  * Measures one kernel class with HIP events recorded on the stream each of its
  * launches goes to (start before, stop after the launch), so a benchmark can
