@@ -46,7 +46,7 @@ import numpy as np
 import torch
 
 from . import philox
-from .numerics import decode_e4m3fn, round_bf16, round_fp32
+from .numerics import decode_e4m3fn, decode_mxfp4, round_bf16, round_fp32
 
 
 # ----------------------------------------------------------------------------- precision
@@ -129,6 +129,10 @@ class Weights:
         lw = self.inp.layers[l]
 
         def load():
+            if self.cfg.expert_dtype == "mxfp4":
+                host = lambda t: t.detach().to("cpu").numpy()
+                return (decode_mxfp4(host(lw["w_gu"][e]), host(lw["s_gu"][e])),
+                        decode_mxfp4(host(lw["w_d"][e]), host(lw["s_d"][e])))
             if lw.get("s_gu") is not None:
                 return _dequant(lw["w_gu"][e], lw["s_gu"][e]), _dequant(lw["w_d"][e], lw["s_d"][e])
             return _np64(lw["w_gu"][e]), _np64(lw["w_d"][e])

@@ -1,10 +1,21 @@
-"""Rounding helpers of the oracle (test infrastructure only).
+"""Rounding and decoding helpers of the oracle (test infrastructure only).
 
 bfloat16: 1 sign, 8 exponent, 7 stored mantissa bits (the upper half of an
 IEEE binary32); rounding is to nearest, ties to even.  E4M3FN (OCP 8-bit
 floating point specification): 1 sign, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities, the all-ones pattern (S.1111.111) is NaN, largest finite
 magnitude 448.
+
+MXFP4 (OCP Microscaling Formats (MX) v1.0): blocks of 32 consecutive elements
+share one E8M0 scale (an 8-bit biased exponent, bias 127, value 2^(e-127); the
+all-ones code is NaN; no sign, no mantissa), and each element is an E2M1 code
+(1 sign, 2 exponent bits with bias 1, 1 mantissa bit; exponent field 0 holds
+the subnormals 0 and 0.5; no infinities or NaN; largest magnitude 6).  The
+element's value is its E2M1 value times the block scale.  Two codes share a
+byte, the element with the even index in the low nibble (the format fixes
+no byte packing; this is the reading taken).  This is the MI355X counterpart
+of the 4-bit expert weights the pages name (DiffusionGemma深度拆解
+(zhichai.net), "MoE 效率：128 专家，8 活跃").
 """
 from __future__ import annotations
 
@@ -51,3 +62,43 @@ _E4M3 = e4m3fn_table()
 
 def decode_e4m3fn(codes) -> np.ndarray:
     return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m1_table() -> np.ndarray:
+    """float64 value of each of the 16 E2M1 codes."""
+    out = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 0x8 else 1.0
+        exp = (code >> 1) & 0x3
+        man = code & 0x1
+        if exp == 0:
+            out[code] = sign * (man / 2.0)                      # subnormal: 0 or 0.5
+        else:
+            out[code] = sign * (1.0 + man / 2.0) * 2.0 ** (exp - 1)
+    return out
+
+
+_E2M1 = e2m1_table()
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """2^(e - 127) for each E8M0 code e; NaN for 255."""
+    e = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).astype(np.int64)))
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] E2M1 codes: byte j holds element 2j in its
+    low nibble and element 2j + 1 in its high nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0x0F
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def decode_mxfp4(packed, scales) -> np.ndarray:
+    """MXFP4 rows [..., K/2] (packed codes) with scales [..., K/32] -> float64 [..., K]."""
+    v = _E2M1[unpack_fp4(packed)]
+    s = decode_e8m0(scales)
+    return v * np.repeat(s, 32, axis=-1)

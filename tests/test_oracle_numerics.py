@@ -46,3 +46,75 @@ def test_e4m3fn_all_codes_match_torch():
     np.testing.assert_array_equal(got[m], ref[m])
     assert np.nanmax(got) == 448.0
     assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+# ----------------------------------------------------------------------------- MXFP4 (OCP MX v1.0)
+
+def test_e2m1_codes_are_the_spec_values():
+    """The E2M1 element table the OCP MX specification prints: magnitudes 0,
+    0.5 (the one subnormal), 1 (smallest normal), 1.5, 2, 3, 4, 6 (largest
+    normal) for codes 0..7, and the same negated with the sign bit set."""
+    from oracle.numerics import e2m1_table
+    t = e2m1_table()
+    np.testing.assert_array_equal(t[:8], [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    np.testing.assert_array_equal(t[8:], -t[:8])
+    assert np.signbit(t[8]) and not np.signbit(t[0])
+    # every E2M1 value is exactly an E4M3FN value (2 significant bits, exponents -1..2)
+    e4 = torch.from_numpy(t).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(e4, t)
+
+
+def test_e8m0_all_codes_match_torch():
+    from oracle.numerics import decode_e8m0
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = decode_e8m0(codes)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    np.testing.assert_array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_mxfp4_nibble_order_and_block_scale():
+    """Byte 0x21 holds element 0 (code 1 = 0.5) in its low nibble and element 1
+    (code 2 = 1.0) in its high nibble; a row of 64 elements has two scales."""
+    from oracle.numerics import decode_mxfp4
+    packed = np.zeros((1, 32), dtype=np.uint8)
+    packed[0, 0] = 0x21
+    packed[0, 16] = 0xF7          # element 32: 6.0, element 33: -6.0
+    scales = np.array([[127 + 3, 127 - 2]], dtype=np.uint8)
+    v = decode_mxfp4(packed, scales)
+    assert v.shape == (1, 64)
+    assert v[0, 0] == 0.5 * 8 and v[0, 1] == 1.0 * 8 and not v[0, 2:32].any()
+    assert v[0, 32] == 6.0 / 4 and v[0, 33] == -6.0 / 4 and not v[0, 34:].any()
+
+
+def test_mxfp4_quantize_then_decode():
+    """The generator's quantizer and the oracle's decoder agree on the format:
+    values already on the grid come back exactly; a random weight comes back
+    within half an E2M1 step (at most 2^e, e its block's exponent) when
+    |w| <= 6 * 2^e, and saturated to 6 * 2^e above that (the block maximum
+    maps into [4, 8) * 2^e); all-zero blocks stay zero."""
+    from oracle.numerics import decode_mxfp4
+    from workloads.gen import quantize_mxfp4_rows
+    rng = np.random.default_rng(7)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    exact = rng.choice(grid, (8, 64)) * rng.choice([1.0, -1.0], (8, 64))
+    exact[:, ::32] = 6.0                               # sets each block's scale to 2^0
+    exact *= 2.0 ** rng.integers(-20, 5, (8, 1))       # a power of two per row
+    q, s = quantize_mxfp4_rows(torch.from_numpy(exact).float())
+    np.testing.assert_array_equal(decode_mxfp4(q.numpy(), s.numpy()), exact)
+    w = rng.standard_normal((16, 2048)) * 0.02
+    w[3, 64:96] = 0.0
+    q, s = quantize_mxfp4_rows(torch.from_numpy(w).float())
+    dq = decode_mxfp4(q.numpy(), s.numpy())
+    step = np.repeat(2.0 ** (s.numpy().astype(np.float64) - 127), 32, axis=-1)
+    w32 = w.astype(np.float32).astype(np.float64)
+    over = np.abs(w32) > 6 * step
+    bound = np.where(over, np.abs(w32) - 6 * step, step)
+    assert np.all(np.abs(dq - w32) <= bound * (1 + 1e-6))
+    np.testing.assert_array_equal(np.abs(dq[over]), 6 * step[over])
+    assert over.any()
+    assert not dq[3, 64:96].any() and s.numpy()[3, 2] == 0
+    # the largest element of every nonzero block uses the top binade (|code value| >= 4)
+    blocks = np.abs(dq).reshape(16, 64, 32).max(-1) / 2.0 ** (s.numpy().astype(np.float64) - 127)
+    assert np.all((blocks[s.numpy() > 0] >= 4.0))

@@ -17,7 +17,14 @@ seed and the tensor's ordinal, on the device the run uses):
 Values are drawn in fp32 and cast to the storage type (``bf16``: round to
 nearest even).  fp8 expert weights are OCP E4M3FN codes with one fp32 scale per
 output channel, ``scale = max|W[c, :]| / 448``, codes = RNE(W / scale) clamped
-to +-448; the codes and scales are the inputs both sides receive.
+to +-448; the codes and scales are the inputs both sides receive.  mxfp4
+routed-expert weights follow the OCP Microscaling conversion: each block of 32
+consecutive weights along the input dimension gets the scale 2^e with
+e = floor(log2(max|block|)) - 2 (2 is the largest E2M1 exponent), stored as the
+E8M0 code e + 127 (an all-zero block gets code 0), and each weight becomes the
+E2M1 code nearest to w / 2^e (ties to the even mantissa, magnitudes above 6
+saturate); two codes per byte, the even element in the low nibble.  The shared
+expert stays bf16 in mxfp4 workloads.
 """
 from __future__ import annotations
 
@@ -62,6 +69,33 @@ def quantize_fp8_rows(w32: torch.Tensor):
     return q.view(torch.uint8), scale.squeeze(-1).contiguous()
 
 
+# E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (code = index): the midpoints
+# between neighbours, and which midpoints round up (to an even mantissa)
+_E2M1_MID = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+_E2M1_TIE_UP = (False, True, False, True, False, True, False)
+
+
+def quantize_mxfp4_rows(w32: torch.Tensor):
+    """MXFP4 quantization of ``w32[..., K]`` (K % 32 == 0) in blocks of 32 along
+    the last axis: returns (packed codes uint8 [..., K/2], E8M0 scales uint8
+    [..., K/32])."""
+    *lead, K = w32.shape
+    blk = w32.reshape(*lead, K // 32, 32).to(torch.float32)
+    amax = blk.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 2, torch.full_like(amax, -127.0))
+    e = e.clamp(-127, 127)
+    v = blk / torch.exp2(e)[..., None]
+    a = v.abs()
+    mid = torch.tensor(_E2M1_MID, dtype=torch.float32, device=w32.device)
+    idx = torch.bucketize(a, mid)                       # midpoints strictly below |v|
+    for j, up in enumerate(_E2M1_TIE_UP):
+        if up:
+            idx = torch.where(a == mid[j], torch.full_like(idx, j + 1), idx)
+    codes = (idx | torch.where(v < 0, 8, 0)).to(torch.uint8).reshape(*lead, K)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
 @dataclass
 class Inputs:
     cfg: Config
@@ -79,9 +113,17 @@ class Inputs:
         return self.embed.device
 
 
-def _expert_tensor(shape, fan_in, cfg, device, ordinal, dtype):
+def _expert_tensor(shape, fan_in, cfg, device, ordinal, dtype, routed=True):
     """Returns (weights, scales-or-None) in the expert storage format."""
     std = fan_in ** -0.5
+    if cfg.expert_dtype == "mxfp4" and routed:
+        g = _gen(device, cfg.seed, ordinal)
+        w32 = torch.randn(*shape, generator=g, device=device, dtype=torch.float32).mul_(std)
+        q, s = quantize_mxfp4_rows(w32)
+        del w32
+        return q, s
+    if cfg.expert_dtype == "mxfp4":
+        return _normal(shape, std, device, cfg.seed, ordinal, dtype), None
     if cfg.expert_dtype == "fp8":
         g = _gen(device, cfg.seed, ordinal)
         w32 = torch.randn(*shape, generator=g, device=device, dtype=torch.float32).mul_(std)
@@ -95,7 +137,7 @@ def make_inputs(cfg: Config, device="cpu", kv_capacity: Optional[int] = None) ->
     """Draw every input of workload ``cfg`` on ``device``."""
     device = torch.device(device)
     act = _storage_dtype(cfg.act_dtype)
-    edt = torch.float32 if cfg.expert_dtype == "fp32" else torch.bfloat16  # fp8: codes
+    edt = torch.float32 if cfg.expert_dtype == "fp32" else torch.bfloat16  # fp8 / mxfp4: codes
     d, V = cfg.d_model, cfg.vocab
     ad = cfg.attn_dim
     E, de, ds = cfg.n_experts, cfg.d_expert, cfg.d_shared
@@ -111,8 +153,8 @@ def make_inputs(cfg: Config, device="cpu", kv_capacity: Optional[int] = None) ->
         }
         lw["w_gu"], lw["s_gu"] = _expert_tensor((E, 2 * de, d), d, cfg, device, base + 3, edt)
         lw["w_d"], lw["s_d"] = _expert_tensor((E, d, de), de, cfg, device, base + 4, edt)
-        lw["ws_gu"], lw["ss_gu"] = _expert_tensor((2 * ds, d), d, cfg, device, base + 5, edt)
-        lw["ws_d"], lw["ss_d"] = _expert_tensor((d, ds), ds, cfg, device, base + 6, edt)
+        lw["ws_gu"], lw["ss_gu"] = _expert_tensor((2 * ds, d), d, cfg, device, base + 5, edt, routed=False)
+        lw["ws_d"], lw["ss_d"] = _expert_tensor((d, ds), ds, cfg, device, base + 6, edt, routed=False)
         layers.append(lw)
     cap = kv_capacity if kv_capacity is not None else cfg.kv_capacity
     shape = (cfg.n_layers, cfg.batch, cfg.n_heads, cap, cfg.head_dim)
