@@ -76,6 +76,22 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
   return r;
 }
 
+// 8 E2M1 codes (the nibbles of w, lowest first: OCP MX FP4, 1 sign, 2
+// exponent bits with bias 1, 1 mantissa bit) times the E8M0 block scale
+// 2^(e8 - 127) -> 8 bf16 values, by the gfx950 packed FP4 -> BF16 conversion
+// with an fp32 scale.  Exact for scale codes 1 .. 254 while the products stay
+// in bf16's normal range (an E2M1 value has 2 significant bits); code 0
+// yields zeros (the quantizer gives it only to all-zero blocks).
+__device__ __forceinline__ u32x4 e2m1x8_to_bf16x8(uint32_t w, uint32_t e8) {
+  const float sc = __uint_as_float(e8 << 23);
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  return r;
+}
+
 // ---------------------------------------------------------------------------- MFMA
 
 // D = A(16x32) * B(32x16) + C on one wave; lane l supplies row/col (l % 16)

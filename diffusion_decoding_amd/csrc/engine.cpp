@@ -54,7 +54,8 @@ struct dg_model {
   int Tmax = 0;  // max_batch * max(max_tokens, canvas_len)
   size_t esz = 0;
   ActType at = ACT_BF16;
-  WType wt = W_BF16;
+  WType wt = W_BF16;   // routed experts
+  WType swt = W_BF16;  // shared expert
   std::vector<void*> allocs;
   // workspace
   void *x = nullptr, *a = nullptr, *qkv = nullptr, *q = nullptr, *kc = nullptr, *vc = nullptr,
@@ -143,8 +144,10 @@ int check_config(const dg_config& c) {
   if (c.act_dtype == DG_DTYPE_FP32 && c.expert_dtype != DG_DTYPE_FP32)
     return fail(DG_ERR_INVALID_ARG, "FP32 activations need FP32 experts");
   if (c.act_dtype == DG_DTYPE_BF16 && c.expert_dtype != DG_DTYPE_BF16 &&
-      c.expert_dtype != DG_DTYPE_FP8_E4M3)
-    return fail(DG_ERR_INVALID_ARG, "BF16 activations need BF16 or FP8_E4M3 experts");
+      c.expert_dtype != DG_DTYPE_FP8_E4M3 && c.expert_dtype != DG_DTYPE_MXFP4)
+    return fail(DG_ERR_INVALID_ARG, "BF16 activations need BF16, FP8_E4M3 or MXFP4 experts");
+  if (c.expert_dtype == DG_DTYPE_MXFP4 && (c.d_model % 64 || c.d_expert % 64))
+    return fail(DG_ERR_SHAPE, "MXFP4 experts need d_model and d_expert multiples of 64");
   const int A = c.n_heads * c.head_dim;
   if (c.d_model % 32 || A % 32 || c.d_expert % 32 || c.d_shared % 32)
     return fail(DG_ERR_SHAPE, "d_model, n_heads*head_dim, d_expert, d_shared must be multiples of 32");
@@ -238,13 +241,13 @@ int shared_gate_up(dg_model* m, int l, const void* b, int T, void* hs, float* rl
   g.M = T; g.N = ds; g.K = d; g.C = hs; g.ldc = ds; g.swiglu_half = ds;
   int r = int(hipErrorInvalidValue);
   *router_done = false;
-  if (m->at == ACT_BF16 && m->wt == W_BF16) {
+  if (m->at == ACT_BF16 && m->swt == W_BF16) {
     GemmArgs gf = g;
     gf.B2 = w.wr; gf.ldb2 = d; gf.N2 = c.n_experts; gf.C2 = rlog; gf.ldc2 = c.n_experts;
-    r = gemm(m->at, m->wt, EPI_SWIGLU, gf, 1, st);
+    r = gemm(m->at, m->swt, EPI_SWIGLU, gf, 1, st);
     *router_done = r == int(hipSuccess);
   }
-  if (r == int(hipErrorInvalidValue)) r = gemm(m->at, m->wt, EPI_SWIGLU, g, 1, st);
+  if (r == int(hipErrorInvalidValue)) r = gemm(m->at, m->swt, EPI_SWIGLU, g, 1, st);
   HIP_OK(r);
   return DG_OK;
 }
@@ -256,7 +259,7 @@ int shared_down(dg_model* m, int l, const void* hs, int T, float* ys, hipStream_
   GemmArgs g;
   g.A = hs; g.lda = c.d_shared; g.B = w.ws_d; g.ldb = c.d_shared; g.b_scale = w.ss_d;
   g.M = T; g.N = c.d_model; g.K = c.d_shared; g.C = ys; g.ldc = c.d_model;
-  HIP_OK(gemm(m->at, m->wt, EPI_F32, g, 1, st));
+  HIP_OK(gemm(m->at, m->swt, EPI_F32, g, 1, st));
   return DG_OK;
 }
 
@@ -306,7 +309,7 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
     ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
     GemmArgs g;  // routed gate/up + SwiGLU, rows gathered per expert
     g.A = b; g.lda = d; g.a_rows = pair_row; g.B = w.w_gu; g.ldb = d;
-    g.b_gstride = 2LL * de * d; g.b_scale = w.s_gu; g.s_gstride = 2LL * de;
+    g.b_gstride = 2LL * de * d; g.b_scale = (const float*)w.s_gu; g.s_gstride = 2LL * de;
     g.M = T * k; g.N = de; g.K = d; g.g_off = off; g.C = h; g.ldc = de; g.swiglu_half = de;
     HIP_OK(gemm(m->at, m->wt, EPI_SWIGLU, g, E, st));
   }
@@ -314,7 +317,7 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
     ProfScope ps(m, DG_PROF_MOE_DOWN, st);
     GemmArgs g;  // routed down
     g.A = h; g.lda = de; g.B = w.w_d; g.ldb = de; g.b_gstride = (long long)d * de;
-    g.b_scale = w.s_d; g.s_gstride = d;
+    g.b_scale = (const float*)w.s_d; g.s_gstride = d;
     g.M = T * k; g.N = d; g.K = de; g.g_off = off; g.C = y; g.ldc = d;
     HIP_OK(gemm(m->at, m->wt, EPI_F32, g, E, st));
   }
@@ -480,9 +483,13 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
     const dg_layer_weights& L = w->layers[l];
     if (!L.wqkv || !L.wo || !L.wr || !L.w_gu || !L.w_d || !L.ws_gu || !L.ws_d)
       return fail(DG_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
-    const bool fp8 = cfg->expert_dtype == DG_DTYPE_FP8_E4M3;
-    if (fp8 != (L.s_gu && L.s_d && L.ss_gu && L.ss_d) || (!fp8 && (L.s_gu || L.s_d || L.ss_gu || L.ss_d)))
+    const bool fp8 = cfg->expert_dtype == DG_DTYPE_FP8_E4M3, fp4 = cfg->expert_dtype == DG_DTYPE_MXFP4;
+    if (fp8 != (L.s_gu && L.s_d && L.ss_gu && L.ss_d) && !fp4)
       return fail(DG_ERR_INVALID_ARG, "fp8 scales must be given exactly when expert_dtype is FP8 (layer %d)", l);
+    if (fp4 && !(L.s_gu && L.s_d && !L.ss_gu && !L.ss_d))
+      return fail(DG_ERR_INVALID_ARG, "MXFP4 experts need block scales s_gu, s_d and no shared scales (layer %d)", l);
+    if (!fp8 && !fp4 && (L.s_gu || L.s_d || L.ss_gu || L.ss_d))
+      return fail(DG_ERR_INVALID_ARG, "scales are given only with FP8 or MXFP4 experts (layer %d)", l);
   }
   if (max_batch <= 0 || max_tokens < 0 || max_kv < 0)
     return fail(DG_ERR_INVALID_ARG, "max_batch must be > 0, max_tokens and max_kv >= 0");
@@ -506,7 +513,10 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   m->max_kv = max_kv ? max_kv : int(kv_limit);
   m->Tmax = max_batch * ntok;
   m->at = cfg->act_dtype == DG_DTYPE_BF16 ? ACT_BF16 : ACT_F32;
-  m->wt = cfg->expert_dtype == DG_DTYPE_FP8_E4M3 ? W_FP8 : (m->at == ACT_BF16 ? W_BF16 : W_F32);
+  m->wt = cfg->expert_dtype == DG_DTYPE_FP8_E4M3 ? W_FP8
+        : cfg->expert_dtype == DG_DTYPE_MXFP4   ? W_FP4
+                                                 : (m->at == ACT_BF16 ? W_BF16 : W_F32);
+  m->swt = m->wt == W_FP4 ? W_BF16 : m->wt;
   m->esz = m->at == ACT_BF16 ? 2 : 4;
   const size_t T = m->Tmax, d = cfg->d_model, A = (size_t)cfg->n_heads * cfg->head_dim;
   const size_t E = cfg->n_experts, k = cfg->top_k, de = cfg->d_expert, ds = cfg->d_shared;
@@ -706,15 +716,24 @@ int dg_profile_read(dg_model* m, double* total_ms, int64_t* launches) {
 int dg_pack_experts(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols, int32_t dtype,
                     void* stream) {
   if (!src || !dst) return fail(DG_ERR_INVALID_ARG, "null pointer");
-  if (dtype != DG_DTYPE_BF16 && dtype != DG_DTYPE_FP8_E4M3)
-    return fail(DG_ERR_INVALID_ARG, "dtype must be BF16 or FP8_E4M3");
+  if (dtype != DG_DTYPE_BF16 && dtype != DG_DTYPE_FP8_E4M3 && dtype != DG_DTYPE_MXFP4 && dtype != DG_DTYPE_E8M0)
+    return fail(DG_ERR_INVALID_ARG, "dtype must be BF16, FP8_E4M3, MXFP4 or E8M0");
   if (n_mats <= 0 || rows <= 0 || cols <= 0 || rows % 16 || cols % 32)
     return fail(DG_ERR_SHAPE, "need n_mats, rows, cols > 0, rows %% 16 == 0 and cols %% 32 == 0");
-  const unsigned long long bytes =
-      (unsigned long long)n_mats * rows * cols * (dtype == DG_DTYPE_BF16 ? 2u : 1u);
+  const bool mx = dtype == DG_DTYPE_MXFP4 || dtype == DG_DTYPE_E8M0;
+  if (mx && cols % 64) return fail(DG_ERR_SHAPE, "MXFP4 needs cols %% 64 == 0");
+  const unsigned long long n = (unsigned long long)n_mats * rows * cols;
+  const unsigned long long bytes = dtype == DG_DTYPE_BF16 ? 2 * n : dtype == DG_DTYPE_FP8_E4M3 ? n
+                                   : dtype == DG_DTYPE_MXFP4 ? n / 2 : n / 32;
   const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
   if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(DG_ERR_INVALID_ARG, "src and dst overlap");
-  HIP_OK(moe_pack(dtype == DG_DTYPE_BF16 ? W_BF16 : W_FP8, src, dst, n_mats, rows, cols, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == DG_DTYPE_E8M0) {
+    HIP_OK(moe_pack_scales(src, dst, n_mats, rows, cols, st));
+    return DG_OK;
+  }
+  const WType wt = dtype == DG_DTYPE_BF16 ? W_BF16 : dtype == DG_DTYPE_FP8_E4M3 ? W_FP8 : W_FP4;
+  HIP_OK(moe_pack(wt, src, dst, n_mats, rows, cols, st));
   return DG_OK;
 }
 
@@ -722,6 +741,13 @@ int dg_test_philox(uint64_t seed, uint32_t pos0, uint32_t step_tag, uint32_t can
                    uint32_t modulus, int32_t n, uint32_t* out, void* stream) {
   if (!out || n < 0 || n > (1 << 24)) return fail(DG_ERR_INVALID_ARG, "bad philox arguments");
   HIP_OK(philox_fill(seed, pos0, step_tag, canvas, block, modulus, n, out, (hipStream_t)stream));
+  return DG_OK;
+}
+
+int dg_test_fp4_decode(const uint8_t* packed, const uint8_t* scales, int32_t n_blocks, void* out, void* stream) {
+  if (!packed || !scales || !out) return fail(DG_ERR_INVALID_ARG, "null argument");
+  if (n_blocks <= 0 || n_blocks > (1 << 24)) return fail(DG_ERR_SHAPE, "n_blocks %d", n_blocks);
+  HIP_OK(fp4_decode(packed, scales, n_blocks, out, (hipStream_t)stream));
   return DG_OK;
 }
 

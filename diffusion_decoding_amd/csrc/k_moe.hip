@@ -57,6 +57,9 @@ constexpr int kWeightAux = 2;
 struct f8 {
   uint8_t v;
 };
+struct f4 {  // two E2M1 codes per byte
+  uint8_t v;
+};
 
 // Weight formats.  A lane loads its slice of a weight tile through a buffer
 // resource over one expert's weights: lane offsets are 32-bit, fragment
@@ -67,38 +70,70 @@ struct f8 {
 // gives the k offset, in the stage, of the 8 k-slots it feeds into step t --
 // the token operand is read at the same offsets, so any order of k within a
 // stage is a valid split of the dot product.
+// NIB is the element size in 4-bit units; BSCALE formats carry one E8M0
+// scale per 32 weights of a row, applied while the codes are widened (the
+// others apply an optional fp32 scale per weight row to the accumulator).
 template <typename TW, int SPS_> struct WFmt;
 template <> struct WFmt<bf16, 1> {  // 8 bf16 per lane per step
   using raw = u32x4;
-  static constexpr int BYTES = 1 * 2, SPS = 1;
+  static constexpr int NIB = 4, SPS = 1;
+  static constexpr bool BSCALE = false;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightAux);
   }
   static __device__ __forceinline__ int lane_k(int g4) { return 8 * g4; }
   static __device__ __forceinline__ int x_k(int g4, int) { return 8 * g4; }
-  static __device__ __forceinline__ u32x4 get(raw v, int) { return v; }
+  static __device__ __forceinline__ u32x4 get(raw v, int, uint32_t) { return v; }
 };
 template <> struct WFmt<f8, 1> {  // 8 E4M3FN codes per lane per step (K % 64 != 0)
   using raw = u32x2;
-  static constexpr int BYTES = 1, SPS = 1;
+  static constexpr int NIB = 2, SPS = 1;
+  static constexpr bool BSCALE = false;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kWeightAux);
   }
   static __device__ __forceinline__ int lane_k(int g4) { return 8 * g4; }
   static __device__ __forceinline__ int x_k(int g4, int) { return 8 * g4; }
-  static __device__ __forceinline__ u32x4 get(raw c, int) { return e4m3x8_to_bf16x8(c); }
+  static __device__ __forceinline__ u32x4 get(raw c, int, uint32_t) { return e4m3x8_to_bf16x8(c); }
 };
 template <> struct WFmt<f8, 2> {  // 16 E4M3FN codes per lane: two steps per 16-byte load
   using raw = u32x4;
-  static constexpr int BYTES = 1, SPS = 2;
+  static constexpr int NIB = 2, SPS = 2;
+  static constexpr bool BSCALE = false;
   static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightAux);
   }
   static __device__ __forceinline__ int lane_k(int g4) { return 16 * g4; }
   static __device__ __forceinline__ int x_k(int g4, int t) { return 16 * g4 + 8 * t; }
-  static __device__ __forceinline__ u32x4 get(raw c, int t) {
+  static __device__ __forceinline__ u32x4 get(raw c, int t, uint32_t) {
     return e4m3x8_to_bf16x8(t ? u32x2{c[2], c[3]} : u32x2{c[0], c[1]});
   }
+};
+// MXFP4: 32 E2M1 codes per lane (16 bytes, four steps; K % 128 == 0) or 16
+// (8 bytes, two steps; K % 64 == 0).  A lane's codes are consecutive k of
+// one row, inside one 32-weight scale block, so each lane widens with one
+// scale.  Step t takes word t: 8 codes, low nibble first.
+template <> struct WFmt<f4, 4> {
+  using raw = u32x4;
+  static constexpr int NIB = 1, SPS = 4;
+  static constexpr bool BSCALE = true;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightAux);
+  }
+  static __device__ __forceinline__ int lane_k(int g4) { return 32 * g4; }
+  static __device__ __forceinline__ int x_k(int g4, int t) { return 32 * g4 + 8 * t; }
+  static __device__ __forceinline__ u32x4 get(raw c, int t, uint32_t e8) { return e2m1x8_to_bf16x8(c[t], e8); }
+};
+template <> struct WFmt<f4, 2> {
+  using raw = u32x2;
+  static constexpr int NIB = 1, SPS = 2;
+  static constexpr bool BSCALE = true;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kWeightAux);
+  }
+  static __device__ __forceinline__ int lane_k(int g4) { return 16 * g4; }
+  static __device__ __forceinline__ int x_k(int g4, int t) { return 16 * g4 + 8 * t; }
+  static __device__ __forceinline__ u32x4 get(raw c, int t, uint32_t e8) { return e2m1x8_to_bf16x8(c[t], e8); }
 };
 
 struct MoeArgs {
@@ -107,6 +142,7 @@ struct MoeArgs {
   const int* off;       // [E+1] pair ranges per expert
   const void* W;        // tiled: gate/up [E][2*Nout][K]; down [E][Nout][K]
   const float* scale;   // fp8: [E][rows of W per expert]
+  const uint8_t* bscale;  // mxfp4: E8M0 block scales, tiled like W (see moe_pack_scales)
   int K;                // reduction length (multiple of 32)
   int Nout;             // outputs per token: d_expert (gate/up) or d_model (down)
   void* out;            // gate/up: h bf16 [pairs][Nout]; down: y fp32 [pairs][Nout]
@@ -217,27 +253,51 @@ __device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pit
 template <typename WL, bool GU, int NB, int MD>
 struct WStream {
   using wraw = typename WL::raw;
+  static constexpr bool BS = WL::BSCALE;
   static constexpr int SKE = 32 * WL::SPS;            // k per stage
-  static constexpr int TILE = 16 * SKE * WL::BYTES;   // bytes of one 16-row tile
+  static constexpr int TILE = 8 * SKE * WL::NIB;      // bytes of one 16-row tile
+  static constexpr int STILE = 16 * SKE / 32;         // bytes of its block scales (BSCALE)
   static constexpr int NW = GU ? 2 * NB : NB;         // fragments per stage: gate blocks, then up blocks
-  __amdgpu_buffer_rsrc_t rsrc;
-  int voff0, KS;
-  int soff[NW];
+  __amdgpu_buffer_rsrc_t rsrc, srsrc;
+  int voff0, svoff0, KS;
+  int soff[NW];                           // byte offset of each fragment's first tile
+  int ssoff[BS ? NW : 1];                 // and of its first scale tile (BSCALE)
   wraw rw[MD][NW];
+  uint32_t rs[BS ? MD : 1][BS ? NW : 1];  // scale codes of the ring's stages
 
   __device__ __forceinline__ void init(const MoeArgs& a, int e, int n0) {
     const long long wrows = GU ? 2LL * a.Nout : a.Nout;
-    const char* We = (const char*)a.W + (long long)e * wrows * a.K * WL::BYTES;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)We, (short)0, int(wrows * a.K * WL::BYTES), 0x00020000);
+    const long long mat = wrows * a.K * WL::NIB / 2;  // bytes of one expert's matrix
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.W + e * mat), (short)0, int(mat), 0x00020000);
     KS = a.K / SKE;
-    voff0 = (threadIdx.x & 63) * (TILE / 64);
+    const int lane = threadIdx.x & 63;
+    voff0 = lane * (TILE / 64);
+    if constexpr (BS) {
+      // lane (row c16, k group g4) reads the scale of its row and of the
+      // 32-weight block its codes fall in
+      const long long smat = wrows * (a.K / 32);
+      srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.bscale + e * smat), (short)0, int(smat), 0x00020000);
+      svoff0 = (lane & 15) * (SKE / 32) + (lane >> 4) * SKE / 128;
+    }
     // first tile of each fragment's 16-row block (n0 and Nout are multiples of 16)
 #pragma unroll
-    for (int f = 0; f < NW; ++f) soff[f] = ((n0 + 16 * (f % NB) + (f < NB ? 0 : a.Nout)) / 16) * KS * TILE;
+    for (int f = 0; f < NW; ++f) {
+      const int tile0 = ((n0 + 16 * (f % NB) + (f < NB ? 0 : a.Nout)) / 16) * KS;
+      soff[f] = tile0 * TILE;
+      if constexpr (BS) ssoff[f] = tile0 * STILE;
+    }
   }
   __device__ __forceinline__ void ld(int ks, int u) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) rw[u][w] = WL::load(rsrc, voff0 + ks * TILE, soff[w]);
+    for (int w = 0; w < NW; ++w) {
+      rw[u][w] = WL::load(rsrc, voff0 + ks * TILE, soff[w]);
+      if constexpr (BS)
+        rs[u][w] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, svoff0 + ks * STILE, ssoff[w], kWeightAux);
+    }
+  }
+  __device__ __forceinline__ u32x4 get(int u, int w, int t) const {
+    if constexpr (BS) return WL::get(rw[u][w], t, rs[u][w]);
+    else return WL::get(rw[u][w], t, 0u);
   }
   __device__ __forceinline__ void fill() {
 #pragma unroll
@@ -328,7 +388,7 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
       for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * pitch + ks * SKE + WL::x_k(g4, t2));
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const u32x4 wv = WL::get(ws.rw[u][w], t2);
+        const u32x4 wv = ws.get(u, w, t2);
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
       }
@@ -426,7 +486,7 @@ __device__ __forceinline__ void moe_gu_chunked(const MoeArgs& a, bf16* xs, WStre
           for (int t = 0; t < MT; ++t) xv[t] = *(const u32x4*)(xr + 16 * t * CP + j * SKE + WL::x_k(g4, t2));
 #pragma unroll
           for (int w = 0; w < NW; ++w) {
-            const u32x4 wv = WL::get(ws.rw[0][w], t2);
+            const u32x4 wv = ws.get(0, w, t2);
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wv, xv[t], acc[w][t]);
           }
@@ -686,6 +746,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ s
   }
 }
 
+// Block scales of MXFP4 weights [n][rows][K/32] -> one scale tile per weight
+// tile (16 rows x SKE k): 16 x SKE/32 bytes, row-major (row, block), tiles
+// in the order of the weight tiles.  One thread per byte.
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          long long total, int K, int ske) {
+  const long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= total) return;
+  const int bpr = ske / 32, stile = 16 * bpr, ks_n = K / ske;
+  const long long tile = o / stile;
+  const int within = int(o - tile * stile), r = within / bpr, b = within - r * bpr;
+  const long long rb_all = tile / ks_n;
+  const int kt = int(tile - rb_all * ks_n);
+  dst[o] = src[(rb_all * 16 + r) * (K / 32) + kt * bpr + b];
+}
+
+// out[8 w .. 8 w + 7] = the 8 E2M1 codes of word w of packed, times the
+// scale of their 32-element block, through the conversion the expert
+// kernels use (a test of the widening).
+__global__ void fp4_decode_kernel(const uint32_t* packed, const uint8_t* scales, int n_words, u32x4* out) {
+  const int w = blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= n_words) return;
+  out[w] = e2m1x8_to_bf16x8(packed[w], scales[w / 4]);
+}
+
 }  // namespace
 
 int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t st) {
@@ -697,6 +781,13 @@ int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, i
   } else if (wt == W_FP8) {
     wb = 1;
     ske = cols % 64 == 0 ? 64 : 32;
+  } else if (wt == W_FP4) {
+    // two codes per byte: tile the packed rows as bytes, 64 bytes (128 k)
+    // per tile row when K % 128 == 0, else 32 bytes (64 k)
+    if (cols % 64) return int(hipErrorInvalidValue);
+    wb = 1;
+    ske = cols % 128 == 0 ? 64 : 32;
+    cols /= 2;
   } else {
     return int(hipErrorInvalidValue);
   }
@@ -713,11 +804,39 @@ int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, i
   return int(hipGetLastError());
 }
 
+int moe_pack_scales(const void* src, void* dst, long long n_mats, int rows, int K, hipStream_t st) {
+  if (n_mats <= 0 || rows <= 0 || K <= 0 || rows % 16 || K % 64) return int(hipErrorInvalidValue);
+  const int ske = K % 128 == 0 ? 128 : 64;
+  const long long total = n_mats * rows * (long long)(K / 32);
+  const long long blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return int(hipErrorInvalidValue);
+  hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)src,
+                     (uint8_t*)dst, total, K, ske);
+  return int(hipGetLastError());
+}
+
+int fp4_decode(const void* packed, const uint8_t* scales, int n_blocks, void* out, hipStream_t st) {
+  if (n_blocks <= 0) return 0;
+  const int n_words = 4 * n_blocks;
+  hipLaunchKernelGGL(fp4_decode_kernel, dim3((n_words + 255) / 256), dim3(256), 0, st, (const uint32_t*)packed,
+                     scales, n_words, (u32x4*)out);
+  return int(hipGetLastError());
+}
+
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
-                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
+                const void* W, const void* scale, int K, int Nout, void* out, hipStream_t st,
                 const MoeRoute* route, int pairs) {
   if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
-  MoeArgs a{(const bf16*)X, pair_row, off, W, scale, K, Nout, out};
+  MoeArgs a{};
+  a.X = (const bf16*)X;
+  a.pair_row = pair_row;
+  a.off = off;
+  a.W = W;
+  if (wt == W_FP4) a.bscale = (const uint8_t*)scale;
+  else a.scale = (const float*)scale;
+  a.K = K;
+  a.Nout = Nout;
+  a.out = out;
   if (route) {
     if (!gate_up || route->T > ROUTE_MAX_TOKENS || route->k > 8 || E > ROUTE_MAX_EXPERTS)
       return int(hipErrorInvalidValue);
@@ -732,6 +851,9 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
   if (wt == W_BF16) return launch<WFmt<bf16, 1>>(gate_up, a, E, pairs, st);
   if (wt == W_FP8 && K % 64 == 0) return launch<WFmt<f8, 2>>(gate_up, a, E, pairs, st);
   if (wt == W_FP8) return launch<WFmt<f8, 1>>(gate_up, a, E, pairs, st);
+  if (wt == W_FP4 && !a.bscale) return int(hipErrorInvalidValue);
+  if (wt == W_FP4 && K % 128 == 0) return launch<WFmt<f4, 4>>(gate_up, a, E, pairs, st);
+  if (wt == W_FP4 && K % 64 == 0) return launch<WFmt<f4, 2>>(gate_up, a, E, pairs, st);
   return int(hipErrorInvalidValue);
 }
 

@@ -14,7 +14,7 @@ enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 // outside the vocabulary.
 constexpr int FLAG_NONFINITE = 1;
 constexpr int FLAG_TOKEN = 2;
-enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP4 = 3 };
 
 // ---------------------------------------------------------------- GEMM (k_gemm.hip)
 // C[m][n] = sum_k A[row(m)][k] * B[n][k]; epilogue by kind.
@@ -91,12 +91,20 @@ struct MoeRoute {
 };
 // pairs: T * k (sizes the token passes; 0 = few pairs per expert); with a
 // route, the larger of this and route->T * route->k.
+// scale: W_FP8 fp32 row scales [E][rows]; W_FP4 the tiled E8M0 block scales
+// (moe_pack_scales); otherwise null.
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
-                const void* W, const float* scale, int K, int Nout, void* out, hipStream_t st,
+                const void* W, const void* scale, int K, int Nout, void* out, hipStream_t st,
                 const MoeRoute* route = nullptr, int pairs = 0);
 // Row-major [n_mats][rows][cols] expert matrices -> the tiled layout moe_experts reads
-// (rows % 16 == 0, cols % 32 == 0; src and dst must not overlap).
+// (rows % 16 == 0, cols % 32 == 0, W_FP4: cols % 64 == 0 with two codes per
+// byte; src and dst must not overlap).
 int moe_pack(WType wt, const void* src, void* dst, long long n_mats, int rows, int cols, hipStream_t st);
+// MXFP4 block scales [n_mats][rows][K/32] -> one scale tile per weight tile
+// (rows % 16 == 0, K % 64 == 0).
+int moe_pack_scales(const void* src, void* dst, long long n_mats, int rows, int K, hipStream_t st);
+// out[32 b + i] = bf16(E2M1 code i of block b of packed * 2^(scales[b] - 127)) (test)
+int fp4_decode(const void* packed, const uint8_t* scales, int n_blocks, void* out, hipStream_t st);
 
 // ---------------------------------------------------------------- attention (k_attn.hip)
 struct AttnArgs {

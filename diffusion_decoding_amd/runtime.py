@@ -9,8 +9,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (DG_DTYPE_BF16, DG_DTYPE_FP8_E4M3, DG_DTYPE_FP32, dg_canvas, dg_config, dg_kv,
-                   dg_layer_weights, dg_step_out, dg_weights)
+from ._lib import (DG_DTYPE_BF16, DG_DTYPE_E8M0, DG_DTYPE_FP8_E4M3, DG_DTYPE_FP32, DG_DTYPE_MXFP4, dg_canvas,
+                   dg_config, dg_kv, dg_layer_weights, dg_step_out, dg_weights)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -28,7 +28,8 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-_DT = {"fp32": DG_DTYPE_FP32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3}
+_DT = {"fp32": DG_DTYPE_FP32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3, "mxfp4": DG_DTYPE_MXFP4,
+       "e8m0": DG_DTYPE_E8M0}
 
 
 def make_config(cfg) -> dg_config:
@@ -40,12 +41,13 @@ def make_config(cfg) -> dg_config:
 
 def pack_experts(w: torch.Tensor, dtype: str, stream=None) -> torch.Tensor:
     """Tiled copy (dg_pack_experts) of row-major expert matrices w[n][rows][cols]
-    (bf16, or fp8 codes as uint8)."""
+    (bf16; fp8 codes as uint8; mxfp4 codes, two per uint8; e8m0: the mxfp4
+    block scales [n][rows][K/32])."""
     if w.dim() != 3:
         raise ValueError("expert weights must be [n][rows][cols]")
+    cols = w.shape[2] * {"mxfp4": 2, "e8m0": 32}.get(dtype, 1)   # codes per row
     out = torch.empty_like(w)
-    _lib.dg_pack_experts(_ptr(w), _ptr(out), w.shape[0], w.shape[1], w.shape[2], _DT[dtype],
-                         _stream(stream))
+    _lib.dg_pack_experts(_ptr(w), _ptr(out), w.shape[0], w.shape[1], cols, _DT[dtype], _stream(stream))
     return out
 
 
@@ -63,13 +65,16 @@ class Model:
         # packed copy per matrix, made here once and kept alive with the model
         self._packed = []
         for l, lw in enumerate(inputs.layers):
-            w_gu, w_d = lw["w_gu"], lw["w_d"]
+            w_gu, w_d, s_gu, s_d = lw["w_gu"], lw["w_d"], lw.get("s_gu"), lw.get("s_d")
             if cfg.expert_dtype != "fp32":
                 w_gu, w_d = pack_experts(w_gu, cfg.expert_dtype), pack_experts(w_d, cfg.expert_dtype)
                 self._packed += [w_gu, w_d]
+            if cfg.expert_dtype == "mxfp4":
+                s_gu, s_d = pack_experts(s_gu, "e8m0"), pack_experts(s_d, "e8m0")
+                self._packed += [s_gu, s_d]
             self._layers[l] = dg_layer_weights(
                 _ptr(lw["wqkv"]), _ptr(lw["wo"]), _ptr(lw["wr"]), _ptr(w_gu), _ptr(w_d),
-                _ptr(lw.get("s_gu")), _ptr(lw.get("s_d")), _ptr(lw["ws_gu"]), _ptr(lw["ws_d"]),
+                _ptr(s_gu), _ptr(s_d), _ptr(lw["ws_gu"]), _ptr(lw["ws_d"]),
                 _ptr(lw.get("ss_gu")), _ptr(lw.get("ss_d")))
         self._weights = dg_weights(_ptr(inputs.embed), _ptr(inputs.lm_head), self._layers)
         self._cfg = make_config(cfg)
@@ -260,3 +265,13 @@ def test_force_routing(model: Model, ids: Optional[torch.Tensor]):
             raise ValueError(f"ids must be int32 {want}")
     model._forced = ids
     _lib.dg_test_force_routing(model.handle, _ptr(ids))
+
+
+def test_fp4_decode(packed: torch.Tensor, scales: torch.Tensor, stream=None) -> torch.Tensor:
+    """packed uint8 [n_blocks * 16], scales uint8 [n_blocks] -> bf16 [n_blocks * 32]."""
+    nb = scales.numel()
+    if packed.numel() != 16 * nb or packed.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("need uint8 packed [16 * n_blocks] and scales [n_blocks]")
+    out = torch.empty(32 * nb, dtype=torch.bfloat16, device=packed.device)
+    _lib.dg_test_fp4_decode(_ptr(packed), _ptr(scales), nb, _ptr(out), _stream(stream))
+    return out

@@ -71,7 +71,13 @@ typedef enum {
   DG_ERR_UNIMPLEMENTED = -7
 } dg_status;
 
-enum { DG_DTYPE_FP32 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP8_E4M3 = 2 };
+/* DG_DTYPE_MXFP4 (expert_dtype only): routed experts in OCP MX FP4 -- E2M1
+ * codes, two per byte (the even element in the low nibble), one E8M0 scale
+ * (2^(e-127)) per 32 consecutive weights along the input dimension; the
+ * shared expert stays BF16.  The MI355X counterpart of the 4-bit expert
+ * weights the pages name (DiffusionGemma深度拆解 (zhichai.net), "MoE 效率：128
+ * 专家，8 活跃").  DG_DTYPE_E8M0 names the block scales for dg_pack_experts. */
+enum { DG_DTYPE_FP32 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP8_E4M3 = 2, DG_DTYPE_MXFP4 = 3, DG_DTYPE_E8M0 = 4 };
 
 /* Bits of the device status word (dg_step_out.status). */
 enum {
@@ -96,7 +102,8 @@ typedef struct dg_config {
   float rms_eps;           /* RMSNorm epsilon (inside the square root) */
   float commit_threshold;  /* nats: uncommitted positions with entropy below it commit */
   int32_t act_dtype;       /* DG_DTYPE_FP32 or DG_DTYPE_BF16 */
-  int32_t expert_dtype;    /* FP32 (with act FP32), BF16 or FP8_E4M3 (with act BF16) */
+  int32_t expert_dtype;    /* FP32 (with act FP32), BF16, FP8_E4M3 or MXFP4 (with act BF16; MXFP4
+                              needs d_model and d_expert multiples of 64) */
   int32_t mask_token;      /* -1: uniform-state noise (Philox draws, the method of the pages);
                               0 .. vocab-1: absorbing-state (mask) noise with this [MASK] id --
                               the canvas starts as all [MASK] and every uncommitted position is
@@ -116,15 +123,20 @@ typedef struct dg_config {
  * row l % 16 of the block, columns (l / 16) * TK/4 .. +TK/4-1 of the tile.
  * This is the operand layout of the 16x16x32 matrix-core instruction, so a
  * wavefront fetches one weight fragment as a single contiguous 1 KB read.
- * The FP8 scales s_gu/s_d stay per row in row order. */
+ * The FP8 scales s_gu/s_d stay per row in row order.  MXFP4 tiles are 16 rows
+ * by TK = 128 codes (64 bytes per row; TK = 64 when cols % 128 != 0), slice l
+ * holding row l % 16, codes (l / 16) * TK/4 onward; their E8M0 scales
+ * s_gu/s_d are tiled alike: per weight tile, 16 x TK/32 bytes, row-major
+ * (row, 32-code block). */
 typedef struct dg_layer_weights {
   const void* wqkv;    /* [3*n_heads*head_dim][d_model]: q rows, k rows, v rows */
   const void* wo;      /* [d_model][n_heads*head_dim] */
   const void* wr;      /* router [n_experts][d_model] (act_dtype) */
   const void* w_gu;    /* [n_experts][2*d_expert][d_model]: gate rows then up rows (tiled, below) */
   const void* w_d;     /* [n_experts][d_model][d_expert] (tiled, below) */
-  const float* s_gu;   /* FP8 only: [n_experts][2*d_expert] row scales, else NULL */
-  const float* s_d;    /* FP8 only: [n_experts][d_model] */
+  const void* s_gu;    /* FP8: fp32 [n_experts][2*d_expert] row scales; MXFP4: E8M0 block
+                          scales [n_experts][2*d_expert][d_model/32] (tiled); else NULL */
+  const void* s_d;     /* FP8: fp32 [n_experts][d_model]; MXFP4: [n_experts][d_model][d_expert/32] */
   const void* ws_gu;   /* shared expert [2*d_shared][d_model] */
   const void* ws_d;    /* shared expert [d_model][d_shared] */
   const float* ss_gu;  /* FP8 only: [2*d_shared] */
@@ -246,10 +258,13 @@ int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* step
  * the next denoise step publishes. */
 int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, void* stream);
 
-/* Rewrite n_mats row-major expert matrices src[n_mats][rows][cols] (BF16, or
- * FP8_E4M3 codes) into the tiled layout dg_layer_weights describes, at dst
- * (same byte size, must not overlap src).  rows % 16 == 0, cols % 32 == 0.
- * Stream-ordered; done once when weights are loaded. */
+/* Rewrite n_mats row-major expert matrices src[n_mats][rows][cols] (BF16,
+ * FP8_E4M3 codes, or MXFP4 codes two per byte) into the tiled layout
+ * dg_layer_weights describes, at dst (same byte size, must not overlap src).
+ * rows % 16 == 0, cols % 32 == 0 (MXFP4: cols % 64 == 0; cols counts codes).
+ * DG_DTYPE_E8M0 packs the MXFP4 block scales src[n_mats][rows][cols/32] of
+ * such matrices into their scale tiles.  Stream-ordered; done once when
+ * weights are loaded. */
 int dg_pack_experts(const void* src, void* dst, int64_t n_mats, int32_t rows, int32_t cols,
                     int32_t dtype, void* stream);
 
@@ -301,6 +316,11 @@ int dg_test_philox(uint64_t seed, uint32_t pos0, uint32_t step_tag, uint32_t can
  * (act_dtype): writes entropy/argmax/top2_gap for T rows (T <= workspace). */
 int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int32_t* argmax,
                     float* top2_gap, void* stream);
+
+/* E2M1 codes packed[n_blocks * 16] (bytes, two codes each) with E8M0 scales
+ * scales[n_blocks] -> out[n_blocks * 32] bf16, through the widening the
+ * MXFP4 expert kernels use. */
+int dg_test_fp4_decode(const uint8_t* packed, const uint8_t* scales, int32_t n_blocks, void* out, void* stream);
 
 /* Commit selection + re-noise alone, on given entropy/argmax [batch][canvas_len]. */
 int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_t* argmax,

@@ -290,3 +290,17 @@ def test_c4_full_width_fp8_block(rt):
     p.close()
     del p
     _free()
+
+
+def test_mxfp4_full_width_two_layers_one_step(rt):
+    """MXFP4 routed experts (E2M1 codes, one E8M0 scale per 32 weights) at the
+    30-layer workload's width, two layers, its 2048-row prompt and a short
+    vocabulary: one locked step."""
+    cfg = get_config("c6").replace(name="c6_2_layers", n_layers=2, vocab=8192)
+    say("MXFP4 experts, full width, 2 layers, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)

@@ -9,7 +9,8 @@ router logits lie within the stated fp32 window (1e-5) of each other.
 
 Shapes: the 2048-wide layer of the benchmark workloads -- a 256-token canvas
 (batch 1), 1024 pooled tokens (batch 4) and a ragged 200-token canvas -- with
-bf16 experts, and fp8 E4M3 routed and shared experts at the same width."""
+bf16 experts, fp8 E4M3 routed and shared experts, and MXFP4 routed experts at
+the same width."""
 import numpy as np
 import pytest
 import torch
@@ -39,6 +40,8 @@ def _unit_cfg(kind: str):
         return get_config("c1").replace(name="unit_bf16", vocab=8192, batch=4, prompt_len=8192)
     if kind == "fp8":
         return get_config("c4").replace(name="unit_fp8", n_layers=1, vocab=8192, n_canvases=1)
+    if kind == "mxfp4":
+        return get_config("c6").replace(name="unit_mxfp4", n_layers=1, vocab=8192, prompt_len=256)
     raise ValueError(kind)
 
 
@@ -67,6 +70,13 @@ def unit_bf16(rt):
 @pytest.fixture(scope="module")
 def unit_fp8(rt):
     u = Unit(rt, "fp8")
+    yield u
+    u.close()
+
+
+@pytest.fixture(scope="module")
+def unit_mxfp4(rt):
+    u = Unit(rt, "mxfp4")
     yield u
     u.close()
 
@@ -270,3 +280,38 @@ def test_moe_unit_fp8(rt, unit_fp8):
     say("routed experts unit (fp8): 256 rows")
     b = _normed_rows(700, 256, unit_fp8.cfg.d_model)
     _moe_case(rt, unit_fp8, b, _oracle_ids(unit_fp8, b))
+
+
+def test_moe_unit_mxfp4(rt, unit_mxfp4):
+    """MXFP4 routed experts at full width: 32 codes per lane-load and one E8M0
+    scale per lane in the gate/up kernel (K = 2048), 16 codes in the down
+    kernel (K = d_expert = 704)."""
+    say("routed experts unit (MXFP4): 256 rows")
+    b = _normed_rows(800, 256, unit_mxfp4.cfg.d_model)
+    _moe_case(rt, unit_mxfp4, b, _oracle_ids(unit_mxfp4, b))
+
+
+def test_moe_unit_mxfp4_pooled(rt, unit_mxfp4):
+    say("routed experts unit (MXFP4): 1024 pooled rows (96-token passes)")
+    b = _normed_rows(801, 1024, unit_mxfp4.cfg.d_model)
+    _moe_case(rt, unit_mxfp4, b, _oracle_ids(unit_mxfp4, b))
+
+
+def test_fp4_decode_exhaustive(rt):
+    """Every byte (two E2M1 codes) under E8M0 scale codes from 2^-90 to 2^100:
+    the widening the MXFP4 kernels use equals the oracle's decode rounded to
+    bf16 (exactly representable) wherever the product is a normal bf16 number."""
+    from oracle.numerics import decode_mxfp4
+    codes = np.arange(256, dtype=np.uint8)
+    scale_codes = np.array([37, 64, 100, 118, 121, 125, 126, 127, 128, 131, 160, 200, 227], dtype=np.uint8)
+    packed = np.tile(codes, len(scale_codes))                      # 16 blocks of 16 bytes per scale code
+    scales = np.repeat(scale_codes, 16)
+    got = rt.test_fp4_decode(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    ref = decode_mxfp4(packed.reshape(-1, 16), scales.reshape(-1, 1)).reshape(-1)
+    g = _host(got)
+    normal = (np.abs(ref) >= 2.0 ** -126) & (np.abs(ref) < 2.0 ** 127)
+    np.testing.assert_array_equal(round_bf16(ref[normal]), ref[normal])
+    np.testing.assert_array_equal(g[normal], ref[normal])
+    assert not g[ref == 0].any()
+    say(f"   {int(normal.sum())} decoded values bit-exact; {int((ref == 0).sum())} zeros")
