@@ -43,11 +43,12 @@ MEASURED_TRAFFIC = {
 
 def router_in_shared(cfg) -> bool:
     """Whether the library computes the router logits inside the shared
-    gate/up launch: bf16 activations and shared weights, K = d_model = 2048,
-    at most 384 tokens, d_shared >= 1024 (the direct-load kernel's small-M
-    SwiGLU shape)."""
+    gate/up launch: bf16 activations and shared weights (bf16 or mxfp4
+    workloads: the latter keep a bf16 shared expert), K = d_model = 2048, at
+    most 384 tokens, d_shared >= 1024 (the direct-load kernel's small-M SwiGLU
+    shape)."""
     T = cfg.batch * cfg.canvas_len
-    return (cfg.act_dtype == "bf16" and cfg.expert_dtype == "bf16" and cfg.d_model == 2048
+    return (cfg.act_dtype == "bf16" and cfg.expert_dtype in ("bf16", "mxfp4") and cfg.d_model == 2048
             and T <= 384 and cfg.d_shared >= 1024)
 
 
@@ -58,14 +59,19 @@ def algorithmic(cfg, kernel: str):
     T = cfg.batch * cfg.canvas_len
     d, E, k, de, ds = cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_expert, cfg.d_shared
     A = cfg.attn_dim
-    wb = 1 if cfg.expert_dtype == "fp8" else 2
     ab = 2 if cfg.act_dtype == "bf16" else 4
+
+    def routed_bytes(rows, K):  # one expert matrix [rows][K] in its storage format, scales included
+        if cfg.expert_dtype == "fp8":
+            return rows * K + rows * 4
+        if cfg.expert_dtype == "mxfp4":
+            return rows * K // 2 + rows * K // 32
+        return rows * K * ab
+    wb = 1 if cfg.expert_dtype == "fp8" else 2   # shared expert (bf16 in mxfp4 workloads)
     if kernel == "moe_gateup":
-        w = E * 2 * de * d * wb + (E * 2 * de * 4 if wb == 1 else 0)
-        return w + T * d * ab + T * k * de * ab, 2.0 * T * k * 2 * de * d
+        return E * routed_bytes(2 * de, d) + T * d * ab + T * k * de * ab, 2.0 * T * k * 2 * de * d
     if kernel == "moe_down":
-        w = E * d * de * wb + (E * d * 4 if wb == 1 else 0)
-        return w + T * k * de * ab + T * k * d * 4, 2.0 * T * k * de * d
+        return E * routed_bytes(d, de) + T * k * de * ab + T * k * d * 4, 2.0 * T * k * de * d
     if kernel == "lm_head":
         return cfg.vocab * d * ab + T * d * ab, 2.0 * T * cfg.vocab * d
     if kernel == "attn":
@@ -174,10 +180,12 @@ def free_gpu(*objs):
     torch.cuda.empty_cache()
 
 
-def time_loop(cfg, canvases: int, warmup: int):
-    """Whole canvases (init + denoise loop) of a prompt-KV workload; inputs resident."""
+def time_loop(cfg, canvases: int, warmup: int, kernels=()):
+    """Whole canvases (init + denoise loop) of a prompt-KV workload; inputs resident.
+    kernels: classes timed with HIP events over one extra canvas each, after the timed region."""
     import torch
 
+    from diffusion_decoding_amd import _lib
     from diffusion_decoding_amd import runtime as rt
     from workloads import make_inputs
 
@@ -197,14 +205,30 @@ def time_loop(cfg, canvases: int, warmup: int):
         steps += rt.generate_canvas(model, canvas, kv)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    kern = {}
+    for name in kernels:
+        _lib.dg_profile_kernel(model.handle, _lib.DG_PROF[name])
+        rt.canvas_init(model, canvas)
+        rt.generate_canvas(model, canvas, kv)
+        ms, cnt = _lib.dg_profile_read(model.handle)
+        kern[name] = roofline_entry(cfg, name, ms, cnt)
+        e = kern[name]
+        log(f"[kernels] {cfg.name} {name:11s} {e['avg_launch_us']:9.1f} us/launch  {e['hbm_gbs']:7.0f} GB/s  "
+            f"{100 * e['frac']:5.1f}% of {e['bound']} peak")
+    if kernels:
+        _lib.dg_profile_kernel(model.handle, 0)
     free_gpu(model)
     del inp, kv, canvas
     free_gpu()
     toks = cfg.batch * cfg.canvas_len * canvases
     log(f"[bench] {cfg.name}: {canvases} canvases x batch {cfg.batch}, {steps} steps in {dt:.3f} s")
-    return {"workload": cfg.name, "batch": cfg.batch, "canvas": cfg.canvas_len, "prompt_kv": cfg.prompt_len,
-            "canvas_tokens_per_s": toks / dt, "denoise_steps_per_s": steps / dt,
-            "ms_per_denoise_step": dt / steps * 1e3, "denoise_steps_per_canvas": steps / canvases}
+    out = {"workload": cfg.name, "batch": cfg.batch, "canvas": cfg.canvas_len, "prompt_kv": cfg.prompt_len,
+           "expert_dtype": cfg.expert_dtype, "canvas_tokens_per_s": toks / dt, "denoise_steps_per_s": steps / dt,
+           "ms_per_denoise_step": dt / steps * 1e3, "denoise_steps_per_canvas": steps / canvases}
+    if kern:
+        out["kernels"] = {n: {k: e[k] for k in ("bound", "frac", "achieved", "unit", "avg_launch_us",
+                                                 "algorithmic_bytes_per_launch")} for n, e in kern.items()}
+    return out
 
 
 def time_block_ar(cfg, warmup: int = 1):
@@ -295,9 +319,15 @@ def main():
     from workloads import get_config, make_inputs
 
     cfg = get_config(args.config)
-    if cfg.prompt_mode != "kv":
-        raise SystemExit("bench.py times the denoise loop over a given prompt KV cache (c2, c3)")
     torch.cuda.set_device(0)
+    if cfg.prompt_mode != "kv":
+        # block-autoregressive workloads (c4): prompt encode + canvases with their commit passes
+        res = time_block_ar(cfg, warmup=args.warmup)
+        print(json.dumps({"metric": METRIC, "value": res["canvas_tokens_per_s"], "unit": "canvas tokens/s",
+                          "n_gpus": 1, "steps": 1, "warmup": args.warmup, "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "bf16+" + cfg.expert_dtype,
+                          "data": "synthetic", "config": {"workload": cfg.name}, "block_ar": res}), flush=True)
+        return
     log(f"[bench] generating inputs for {cfg.name} on the GPU")
     inp = make_inputs(cfg, device="cuda")
     torch.cuda.synchronize()
@@ -372,6 +402,9 @@ def main():
                 f"{e['hbm_gbs']:7.0f} GB/s  {e['tflops']:7.1f} TFLOP/s  {100 * e['frac']:5.1f}% of {e['bound']} peak")
         _lib.dg_profile_kernel(model.handle, 0)
         out["kernels"] = kern
+        # every class against its own bound, beside the headline kernel
+        out["roofline_by_class"] = {n: {"bound": e["bound"], "frac": e["frac"], "avg_launch_us": e["avg_launch_us"]}
+                                    for n, e in kern.items()}
 
     # fill-in-the-middle on the same model: a fixed 64-token prefix and
     # 64-token suffix (pre-committed), 128 open positions denoised around them
@@ -416,6 +449,8 @@ def main():
         out["canvas512"] = time_loop(get_config("c2").replace(name="c2_canvas512", canvas_len=512),
                                      canvases=1, warmup=1)
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
+        # MXFP4 routed experts (E2M1 codes + E8M0 block scales), same shapes as the headline
+        out["mxfp4"] = time_loop(get_config("c6"), canvases=1, warmup=1, kernels=("moe_gateup", "moe_down"))
     print(json.dumps(out), flush=True)
 
 

@@ -718,6 +718,16 @@ int launch(bool gu, const MoeArgs& a, int E, int pairs, hipStream_t st) {
   // 1024 tokens x 8 slots over 128 experts (16 outputs per wave)
   if (pairs > 24 * E && size_t(96) * (a.K + 16) * sizeof(bf16) + KERNEL_LDS <= 160 * 1024)
     return launch_k<WL, false, 2, 4, 512, 6>(a, E, ((a.Nout + 31) / 32 + 7) / 8, st);
+  if constexpr (WL::BSCALE) {
+    // MXFP4: a quarter of the bf16 bytes per weight row, so a workgroup's
+    // token staging (its h rows) weighs as much as its weight stream; 32
+    // outputs per wave halve the workgroups per expert (8 of 8 waves) and
+    // the staging with them: 32.3 against 36.2 us at 256 tokens x 8 slots
+    // (16 outputs per wave, 4 stages in flight; 1024-thread and 64-output
+    // variants 33.1-37.5 us)
+    const int b32 = (a.Nout + 31) / 32;
+    return launch_k<WL, false, 2, 2, 512, 2>(a, E, (b32 + 7) / 8, st);
+  }
   const int blocks = (a.Nout + 15) / 16;
   const int split = (blocks + 7) / 8;
   return launch_k<WL, false, 1, 4, 512, 2>(a, E, split, st);

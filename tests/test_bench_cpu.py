@@ -65,6 +65,20 @@ def test_fp8_experts_count_codes_and_row_scales():
     assert b == E * 2 * de * d + E * 2 * de * 4 + 256 * d * 2 + 256 * 8 * de * 2
 
 
+def test_mxfp4_experts_count_codes_and_block_scales():
+    """Half a byte per weight plus one E8M0 byte per 32 weights; the shared
+    expert stays bf16."""
+    cfg = get_config("c6")
+    E, d, de, T, k = 128, 2048, 704, 256, 8
+    b, f = bench.algorithmic(cfg, "moe_gateup")
+    assert b == E * 2 * de * d // 2 + E * 2 * de * d // 32 + T * d * 2 + T * k * de * 2
+    assert f == 2.0 * T * k * 2 * de * d
+    b, _ = bench.algorithmic(cfg, "moe_down")
+    assert b == E * d * de // 2 + E * d * de // 32 + T * k * de * 2 + T * k * d * 4
+    sb, _ = bench.algorithmic(cfg, "shared")
+    assert sb == bench.algorithmic(get_config("c2"), "shared")[0]
+
+
 def test_roofline_entry_arithmetic():
     cfg = get_config("c2")
     b, _ = bench.algorithmic(cfg, "moe_gateup")

@@ -304,3 +304,51 @@ def test_mxfp4_full_width_two_layers_one_step(rt):
     del p
     _free()
     _assert_reports(cfg, reps)
+
+
+def test_batch_invariance_c3_shape(rt):
+    """A canvas scored inside a batch of four (1024 pooled expert tokens:
+    large-M projection tiles, pooled 96-token expert passes) against the same
+    canvas alone (256 tokens: small-M tiles, 32-token passes), each with its
+    own 8192-row prompt.  The two runs sum in different orders, so they agree
+    to the bf16 noise floor, not bit for bit: the bound is the one the
+    independent-forward check (c) holds against the oracle."""
+    from tests.parity import logits_tol
+    cfg4 = get_config("c3").replace(name="c3_batch_inv", n_layers=1, vocab=8192)
+    say("batch invariance: canvas b alone vs inside a batch of 4 (c3 shape, 1 layer)")
+    inp = make_inputs(cfg4, device="cuda")
+    m4 = rt.Model(inp)
+    kv4 = rt.KVCache(inp.kv_k.clone(), inp.kv_v.clone(), inp.kv_len)
+    B, N, d = cfg4.batch, cfg4.canvas_len, cfg4.d_model
+    c4 = rt.Canvas.empty(B, N, cfg4.seed)
+    rt.canvas_init(m4, c4)
+    tok = c4.tokens.clone()
+    ent4 = torch.empty(B, N, device="cuda")
+    hid4 = torch.empty(B * N, d, dtype=torch.bfloat16, device="cuda")
+    lg4 = torch.empty(B * N, cfg4.vocab, device="cuda")
+    rt.denoise_step(m4, c4, kv4, entropy=ent4, hidden=hid4, logits=lg4)
+    torch.cuda.synchronize()
+    m4.close()
+    cfg1 = cfg4.replace(batch=1)
+    m1 = rt.Model(inp, max_batch=1)
+    worst = {}
+    for b in range(B):
+        kv1 = rt.KVCache(inp.kv_k[:, b:b + 1].clone(), inp.kv_v[:, b:b + 1].clone(), inp.kv_len)
+        c1 = rt.Canvas.empty(1, N, cfg4.seed)
+        rt.canvas_init(m1, c1)
+        c1.tokens.copy_(tok[b:b + 1])
+        ent1 = torch.empty(1, N, device="cuda")
+        hid1 = torch.empty(N, d, dtype=torch.bfloat16, device="cuda")
+        lg1 = torch.empty(N, cfg4.vocab, device="cuda")
+        rt.denoise_step(m1, c1, kv1, entropy=ent1, hidden=hid1, logits=lg1)
+        torch.cuda.synchronize()
+        h1, h4 = to_host(hid1.float()), to_host(hid4[b * N:(b + 1) * N].float())
+        z1, z4 = to_host(lg1).astype(np.float64), to_host(lg4[b * N:(b + 1) * N]).astype(np.float64)
+        rel = float(np.linalg.norm(z1 - z4) / np.linalg.norm(z4))
+        dH = float(np.abs(to_host(ent1)[0] - to_host(ent4)[b]).max())
+        same_rows = int((h1 == h4).all(axis=1).sum())
+        say(f"   canvas {b}: logits rel-L2 {rel:.2e}, max |dH| {dH:.2e}, {same_rows} of {N} hidden rows bitwise equal")
+        worst[b] = (rel, dH)
+        assert rel <= logits_tol(cfg4) and dH <= 5e-3
+    m1.close()
+    _free()
