@@ -171,6 +171,22 @@ def cpu_baseline(inp, cfg, steps_per_canvas: float, layers: int):
     }
 
 
+def routing_stats(model, canvas, kv, cfg):
+    """Pairs routed to each expert in one denoise step (per layer, all canvases
+    pooled): how many experts exceed a 32-token pass of the batch-1 routed
+    kernels, and the largest count, averaged over the layers."""
+    import torch
+
+    from diffusion_decoding_amd import runtime as rt
+    counts = torch.zeros(cfg.n_layers, cfg.n_experts, dtype=torch.int32, device="cuda")
+    rt.denoise_step(model, canvas, kv, expert_counts=counts)
+    c = counts.cpu()
+    over = (c > 32).sum(1).float()
+    return {"pairs_per_step_layer": int(c[0].sum()), "experts": cfg.n_experts,
+            "mean_experts_over_32_pairs": float(over.mean()), "mean_max_pairs": float(c.max(1).values.float().mean()),
+            "max_pairs": int(c.max()), "mean_unused_experts": float((c == 0).sum(1).float().mean())}
+
+
 def free_gpu(*objs):
     import torch
     for o in objs:
@@ -263,6 +279,12 @@ def time_block_ar(cfg, warmup: int = 1):
     steps = run()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # routing balance of the first canvas's first step, after the prompt encode
+    kv.length = 0
+    rt.commit_canvas(model, inp.prompt_tokens, kv)
+    canvas.block = 0
+    rt.canvas_init(model, canvas)
+    routing = routing_stats(model, canvas, kv, cfg)
     free_gpu(model)
     del inp, kv, canvas
     free_gpu()
@@ -271,7 +293,7 @@ def time_block_ar(cfg, warmup: int = 1):
     return {"workload": cfg.name, "expert_dtype": cfg.expert_dtype, "prompt_tokens": cfg.prompt_len,
             "canvases": cfg.n_canvases, "canvas_tokens_per_s": toks / dt,
             "denoise_steps_per_s": steps / dt, "ms_per_denoise_step_incl_commit": dt / steps * 1e3,
-            "note": "time includes the prompt encode and every causal commit pass"}
+            "note": "time includes the prompt encode and every causal commit pass", "routing": routing}
 
 
 def main():
@@ -402,6 +424,8 @@ def main():
                 f"{e['hbm_gbs']:7.0f} GB/s  {e['tflops']:7.1f} TFLOP/s  {100 * e['frac']:5.1f}% of {e['bound']} peak")
         _lib.dg_profile_kernel(model.handle, 0)
         out["kernels"] = kern
+        rt.canvas_init(model, canvas)
+        out["routing"] = routing_stats(model, canvas, kv, cfg)
         # every class against its own bound, beside the headline kernel
         out["roofline_by_class"] = {n: {"bound": e["bound"], "frac": e["frac"], "avg_launch_us": e["avg_launch_us"]}
                                     for n, e in kern.items()}

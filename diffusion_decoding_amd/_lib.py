@@ -56,7 +56,7 @@ class dg_canvas(ctypes.Structure):
 class dg_step_out(ctypes.Structure):
     _fields_ = [("entropy", c_void_p), ("argmax", c_void_p), ("top2_gap", c_void_p),
                 ("n_uncommitted", c_void_p), ("logits", c_void_p), ("hidden", c_void_p),
-                ("status", c_void_p)]
+                ("status", c_void_p), ("expert_counts", c_void_p)]
 
 
 _SIGS = {

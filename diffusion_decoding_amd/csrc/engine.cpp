@@ -75,6 +75,7 @@ struct dg_model {
   int* n_unc = nullptr;
   int* u_host = nullptr;  // pinned, 2 + max_batch words
   const int* force_ids = nullptr;  // test hook: [n_layers][max_batch * canvas_len][top_k], -1 = not forced
+  int* diag_counts = nullptr;      // [n_layers][n_experts] for the step in progress, or null
   // kernel timing
   int prof_id = DG_PROF_NONE;
   std::vector<hipEvent_t> prof_ev;  // start/stop pairs
@@ -379,6 +380,7 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   }
   s = routed(m, l, m->a, T, m->topk_ids, m->h, m->y, m->off, m->pair_row, m->pos, st);
   if (s) return s;
+  if (m->diag_counts && !causal) HIP_OK(expert_counts(m->off, c.n_experts, m->diag_counts + (long long)l * c.n_experts, st));
   HIP_OK(moe_combine_norm(m->at, m->x, m->y, m->ys, m->topk_w, m->pos, T, c.top_k, d, c.rms_eps, m->a,
                           m->ctl + 1, st));
   return DG_OK;
@@ -419,10 +421,15 @@ int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* o
   HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, cfg.vocab, m->x, m->ctl + 1, st));
   HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
   HIP_OK(rope_table(N, cfg.head_dim, P, cfg.rope_theta, m->rope_tab, st));  // canvas positions P..P+N-1
+  m->diag_counts = out ? out->expert_counts : nullptr;
   for (int l = 0; l < cfg.n_layers; ++l) {
     int s = layer_forward(m, l, B, N, P, kv, false, false, st);
-    if (s) return s;
+    if (s) {
+      m->diag_counts = nullptr;
+      return s;
+    }
   }
+  m->diag_counts = nullptr;
   // m->a now holds the final RMSNorm of x
   if (out && out->hidden)
     HIP_OK(hipMemcpyAsync(out->hidden, m->a, (size_t)T * cfg.d_model * m->esz, hipMemcpyDeviceToDevice, st));

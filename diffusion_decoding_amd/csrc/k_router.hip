@@ -104,6 +104,11 @@ __global__ void force_kernel(const float* logits, int T, int E, int k, const int
   }
 }
 
+__global__ void counts_kernel(const int* off, int E, int* counts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) counts[e] = off[e + 1] - off[e];
+}
+
 constexpr int PERM_THREADS = 1024;
 constexpr int PERM_MAX_TOKENS = 1024;
 constexpr int PERM_WORDS = PERM_MAX_TOKENS / 64;
@@ -202,6 +207,11 @@ int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row,
   if (T > PERM_MAX_TOKENS || E > 256 || k > E) return int(hipErrorInvalidValue);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, st, ids, T, E, k, off, pair_row,
                      pos);
+  return int(hipGetLastError());
+}
+
+int expert_counts(const int* off, int E, int* counts, hipStream_t st) {
+  hipLaunchKernelGGL(counts_kernel, dim3((E + 255) / 256), dim3(256), 0, st, off, E, counts);
   return int(hipGetLastError());
 }
 

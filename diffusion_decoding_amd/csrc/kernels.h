@@ -179,5 +179,7 @@ int router_force(const float* logits, int T, int E, int k, const int* forced, in
 // token-ascending), pos[T][k] (slot of pair (t, j)).
 int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,
                    hipStream_t st);
+// counts[e] = off[e + 1] - off[e] for e < E (diagnostic)
+int expert_counts(const int* off, int E, int* counts, hipStream_t st);
 
 }  // namespace dg

@@ -145,10 +145,10 @@ def canvas_prefill(model: Model, canvas: Canvas, tokens: torch.Tensor, mask: tor
 
 
 def denoise_step(model: Model, canvas: Canvas, kv: KVCache, entropy=None, argmax=None, top2_gap=None,
-                 n_uncommitted=None, logits=None, hidden=None, status=None, stream=None):
+                 n_uncommitted=None, logits=None, hidden=None, status=None, expert_counts=None, stream=None):
     s = canvas.struct()
     out = dg_step_out(_ptr(entropy), _ptr(argmax), _ptr(top2_gap), _ptr(n_uncommitted), _ptr(logits),
-                      _ptr(hidden), _ptr(status))
+                      _ptr(hidden), _ptr(status), _ptr(expert_counts))
     _lib.dg_denoise_step(model.handle, s, kv.struct(), out, _stream(stream))
     canvas.step = s.step
 

@@ -180,6 +180,8 @@ typedef struct dg_step_out {
   float* logits;           /* test/diagnostic: [batch*canvas_len][vocab] fp32 (extra GEMM) */
   void* hidden;            /* test/diagnostic: final normed hidden [batch*canvas_len][d_model] */
   int32_t* status;         /* [1] DG_STATUS_* bits raised since the previous step; 0 = clean */
+  int32_t* expert_counts;  /* diagnostic: [n_layers][n_experts] (token, slot) pairs routed to each
+                              expert in each layer (all canvases pooled) */
 } dg_step_out;
 
 typedef struct dg_model dg_model;

@@ -463,3 +463,25 @@ def test_kv_overflow_and_max_kv_are_refused(rt):
     assert e.value.status == DG_ERR_SHAPE and "max_kv" in str(e.value)
     small.close()
     torch.cuda.synchronize()
+
+
+def test_expert_counts_match_the_oracle_routing(rt):
+    """dg_step_out.expert_counts: the pairs routed to each expert in each layer
+    equal the histogram of the oracle's top-k ids (two layers, batch 2)."""
+    cfg = tiny_config(name="tiny_counts", n_layers=2, batch=2, seed=71)
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(cfg.batch, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    counts = torch.full((cfg.n_layers, cfg.n_experts), -1, dtype=torch.int32, device="cuda")
+    rt.denoise_step(model, canvas, kv, expert_counts=counts)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=False)
+    ost = om.init_state(cfg, cfg.seed)
+    ores = om.denoise_step(W, okv, ost, cfg)
+    ids = ores.trace["route_ids"]          # canvas-major: [b0 l0, b0 l1, b1 l0, b1 l1]
+    want = np.stack([sum(np.bincount(ids[b * cfg.n_layers + l].ravel(), minlength=cfg.n_experts)
+                         for b in range(cfg.batch)) for l in range(cfg.n_layers)])
+    np.testing.assert_array_equal(to_host(counts), want)
+    assert (want.sum(1) == cfg.batch * cfg.canvas_len * cfg.top_k).all()
+    model.close()
