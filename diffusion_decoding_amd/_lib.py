@@ -59,6 +59,15 @@ class dg_step_out(ctypes.Structure):
                 ("status", c_void_p), ("expert_counts", c_void_p)]
 
 
+DG_SEG_APPEND, DG_SEG_REFINE = 0, 1
+
+
+class dg_segment(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("n", c_int32), ("kv", POINTER(dg_kv)), ("tokens", c_void_p),
+                ("canvas", POINTER(dg_canvas)), ("entropy", c_void_p), ("argmax", c_void_p),
+                ("n_uncommitted", c_void_p), ("hidden", c_void_p)]
+
+
 _SIGS = {
     "dg_model_create": [POINTER(dg_config), POINTER(dg_weights), c_int32, c_int32, c_int32,
                         POINTER(c_void_p)],
@@ -70,6 +79,7 @@ _SIGS = {
     "dg_generate_canvas": [c_void_p, POINTER(dg_canvas), POINTER(dg_kv), POINTER(c_int32),
                            c_void_p],
     "dg_commit_canvas": [c_void_p, c_void_p, c_int32, POINTER(dg_kv), c_void_p],
+    "dg_mixed_step": [c_void_p, POINTER(dg_segment), c_int32, c_void_p, c_void_p],
     "dg_pack_experts": [c_void_p, c_void_p, ctypes.c_int64, c_int32, c_int32, c_int32, c_void_p],
     "dg_profile_kernel": [c_void_p, c_int32],
     "dg_profile_read": [c_void_p, POINTER(ctypes.c_double), POINTER(ctypes.c_int64)],
@@ -158,6 +168,10 @@ def dg_generate_canvas(handle, canvas, kv, stream) -> int:
 
 def dg_commit_canvas(handle, tokens_ptr, n, kv, stream):
     _call("dg_commit_canvas", handle, tokens_ptr, n, byref(kv), stream)
+
+
+def dg_mixed_step(handle, segs, n_segs, status_ptr, stream):
+    _call("dg_mixed_step", handle, segs, n_segs, status_ptr, stream)
 
 
 def dg_pack_experts(src_ptr, dst_ptr, n_mats, rows, cols, dtype, stream):

@@ -203,20 +203,22 @@ int qkv_rope(dg_model* m, int l, const void* a, int B, int n, void* q_out, void*
 // values kc / vc [B][H][n][dh]; causal (kc null): over cache rows [0, P + n)
 // with query i seeing rows j <= P + i.
 int attend(dg_model* m, int l, const void* q, const dg_kv* kv, int P, const void* kc, const void* vc, int B, int n,
-           void* o, hipStream_t st) {
+           void* o, hipStream_t st, long long plane = 0) {
   const dg_config& c = m->cfg;
   const int H = c.n_heads, dh = c.head_dim;
   const long long cap = kv->capacity;
   const long long layer_stride = (long long)kv->batch * H * cap * dh;
   AttnArgs aa{};
-  aa.q = q; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = o;
+  // q and the canvas keys/values: (b, h) planes `plane` elements apart (n * dh: packed)
+  if (plane == 0) plane = (long long)n * dh;
+  aa.q = q; aa.q_bh = plane; aa.B = B; aa.H = H; aa.n = n; aa.dh = dh; aa.out = o;
   aa.part_o = m->attn_po; aa.part_ml = m->attn_ml;
   aa.k0 = (const char*)kv->k + l * layer_stride * m->esz;
   aa.v0 = (const char*)kv->v + l * layer_stride * m->esz;
   aa.s0_bh = cap * dh;
   if (kc) {
     aa.len0 = P;
-    aa.k1 = kc; aa.v1 = vc; aa.s1_bh = (long long)n * dh; aa.len1 = n;
+    aa.k1 = kc; aa.v1 = vc; aa.s1_bh = plane; aa.len1 = n;
     aa.causal_base = -1;
   } else {
     aa.len0 = P + n;
@@ -325,6 +327,32 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
   return DG_OK;
 }
 
+// Rows per routed-expert launch: the routed gate/up kernel derives the
+// routing of up to 2048 tokens in LDS (the fp32 path's permutation kernel
+// takes 1024); larger batches run in chunks, each streaming the expert
+// weights once.
+int route_chunk(const dg_model* m) { return m->at == ACT_BF16 ? 2048 : 1024; }
+
+// Routed experts on the top-k ids of rows [0, T) (normed rows in m->a, the
+// shared-expert output in m->ys), then the combine, residual add and next
+// RMSNorm of those rows, chunk by chunk.  diag: accumulate the expert pair
+// counts of layer l into m->diag_counts.
+int moe_chunks(dg_model* m, int l, int T, bool diag, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const int k = c.top_k, d = c.d_model, chunk = route_chunk(m);
+  for (int c0 = 0; c0 < T; c0 += chunk) {
+    const int tc = std::min(chunk, T - c0);
+    const size_t row = (size_t)d * m->esz;
+    int s = routed(m, l, (const char*)m->a + c0 * row, tc, m->topk_ids + (size_t)c0 * k, m->h, m->y, m->off,
+                   m->pair_row, m->pos + (size_t)c0 * k, st);
+    if (s) return s;
+    if (diag) HIP_OK(expert_counts(m->off, c.n_experts, m->diag_counts + (long long)l * c.n_experts, c0 > 0, st));
+    HIP_OK(moe_combine_norm(m->at, (char*)m->x + c0 * row, m->y, m->ys + (size_t)c0 * d, m->topk_w + (size_t)c0 * k,
+                            m->pos + (size_t)c0 * k, tc, k, d, c.rms_eps, (char*)m->a + c0 * row, m->ctl + 1, st));
+  }
+  return DG_OK;
+}
+
 // One pre-norm block over T = B * n rows.  causal: rows are new tokens at
 // positions P.. written into the cache; otherwise canvas rows attend to the
 // first P cache rows plus the canvas.  On entry m->a holds rmsnorm(x); on
@@ -378,12 +406,76 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, forced, st);
     if (s) return s;
   }
-  s = routed(m, l, m->a, T, m->topk_ids, m->h, m->y, m->off, m->pair_row, m->pos, st);
-  if (s) return s;
-  if (m->diag_counts && !causal) HIP_OK(expert_counts(m->off, c.n_experts, m->diag_counts + (long long)l * c.n_experts, st));
-  HIP_OK(moe_combine_norm(m->at, m->x, m->y, m->ys, m->topk_w, m->pos, T, c.top_k, d, c.rms_eps, m->a,
-                          m->ctl + 1, st));
-  return DG_OK;
+  return moe_chunks(m, l, T, m->diag_counts && !causal, st);
+}
+
+// ---- mixed-phase batches: requests in different phases in one pass
+
+struct MixedSeg {
+  const dg_segment* s;
+  int start;  // first row of the segment in the pass
+  int P;      // its cache rows before the pass
+};
+
+// One block over the rows of a mixed batch (refine segments first, then
+// append segments): the dense projections and the experts run once over all
+// rows, attention once per segment in its own mode over its own cache; the
+// append segments' new keys and values go into their caches first.
+int mixed_layer(dg_model* m, int l, const MixedSeg* sg, int n_segs, int T, int T_ref, hipStream_t st) {
+  const dg_config& c = m->cfg;
+  const int d = c.d_model, H = c.n_heads, dh = c.head_dim, A = H * dh;
+  const long long plane = (long long)T * dh;
+  int s;
+  {
+    ProfScope ps(m, DG_PROF_QKV, st);
+    s = qkv_rope(m, l, m->a, 1, T, m->q, m->kc, m->vc, plane, 0, st);
+    if (s) return s;
+  }
+  for (int i = 0; i < n_segs; ++i) {
+    if (sg[i].s->kind != DG_SEG_APPEND) continue;
+    const dg_kv* kv = sg[i].s->kv;
+    const long long cap = kv->capacity, lay = (long long)H * cap * dh * m->esz;  // batch-1 cache
+    HIP_OK(kv_copy_rows(m->at, (const char*)m->kc + sg[i].start * dh * m->esz,
+                        (const char*)m->vc + sg[i].start * dh * m->esz, plane, H, sg[i].s->n, dh,
+                        (char*)kv->k + l * lay, (char*)kv->v + l * lay, cap * dh, sg[i].P, st));
+  }
+  {
+    ProfScope ps(m, DG_PROF_ATTN, st);
+    for (int i = 0; i < n_segs; ++i) {
+      const int r0 = sg[i].start, n = sg[i].s->n;
+      const char* q = (const char*)m->q + (size_t)r0 * dh * m->esz;
+      char* o = (char*)m->o + (size_t)r0 * A * m->esz;
+      if (sg[i].s->kind == DG_SEG_REFINE)
+        s = attend(m, l, q, sg[i].s->kv, sg[i].P, (const char*)m->kc + (size_t)r0 * dh * m->esz,
+                   (const char*)m->vc + (size_t)r0 * dh * m->esz, 1, n, o, st, plane);
+      else
+        s = attend(m, l, q, sg[i].s->kv, sg[i].P, nullptr, nullptr, 1, n, o, st, plane);
+      if (s) return s;
+    }
+  }
+  {
+    GemmArgs g;  // O-projection + residual
+    g.A = m->o; g.lda = A; g.B = m->layers[l].wo; g.ldb = A; g.M = T; g.N = d; g.K = A; g.C = m->x; g.ldc = d;
+    HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_RESID, g, 1, st));
+  }
+  HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st));
+  bool router_done = false;
+  {
+    ProfScope ps(m, DG_PROF_SHARED, st);
+    s = shared_gate_up(m, l, m->a, T, m->hs, m->rlog, &router_done, st);
+    if (!s) s = shared_down(m, l, m->hs, T, m->ys, st);
+    if (s) return s;
+  }
+  {
+    ProfScope ps(m, DG_PROF_ROUTER, st);
+    s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, nullptr, st);
+    if (s) return s;
+    if (m->force_ids && T_ref)  // test hook, on the refine rows (the first T_ref)
+      HIP_OK(router_force(m->rlog, T_ref, c.n_experts, c.top_k,
+                          m->force_ids + (long long)l * m->max_batch * c.canvas_len * c.top_k, m->topk_ids,
+                          m->topk_w, st));
+  }
+  return moe_chunks(m, l, T, false, st);
 }
 
 int lm_head_confidence(dg_model* m, const void* hf, int T, float* H, int* am, float* gap,
@@ -504,9 +596,9 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   const long long kv_limit = 0x7fffffffLL / ((long long)cfg->head_dim * (cfg->act_dtype == DG_DTYPE_BF16 ? 2 : 4));
   if (max_kv > kv_limit) return fail(DG_ERR_SHAPE, "max_kv %d exceeds %lld rows", max_kv, kv_limit);
   const int ntok = std::max(max_tokens, cfg->canvas_len);
-  // tokens of one call: the routed gate/up kernel derives the routing of up
-  // to 2048 tokens in LDS; the fp32 path's permutation kernel takes 1024
-  const long long max_t = cfg->act_dtype == DG_DTYPE_BF16 ? 2048 : 1024;
+  // rows of one call (the workspace grows with it; the routed experts take
+  // larger calls in chunks of 2048 rows, 1024 with fp32)
+  const long long max_t = 8192;
   if ((long long)max_batch * ntok > max_t)
     return fail(DG_ERR_SHAPE, "max_batch * max(max_tokens, canvas_len) must be <= %lld", max_t);
 
@@ -528,6 +620,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   const size_t T = m->Tmax, d = cfg->d_model, A = (size_t)cfg->n_heads * cfg->head_dim;
   const size_t E = cfg->n_experts, k = cfg->top_k, de = cfg->d_expert, ds = cfg->d_shared;
   const size_t Tc = (size_t)max_batch * cfg->canvas_len;
+  const size_t Tr = std::min(T, (size_t)route_chunk(m));  // rows of one routed launch
   m->lm_ntiles = lm_tiles(m->at, cfg->d_model, cfg->vocab);
   const size_t es = m->esz;
   struct Req {
@@ -544,14 +637,14 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       {(void**)&m->attn_po, (size_t)m->attn_max_splits * T * A * 4},
       {(void**)&m->attn_ml, (size_t)m->attn_max_splits * T * cfg->n_heads * 2 * 4},
       {(void**)&m->rlog, T * E * 4},
-      {(void**)&m->rope_tab, (size_t)m->max_tokens * cfg->head_dim * 4},
+      {(void**)&m->rope_tab, T * cfg->head_dim * 4},
       {(void**)&m->topk_ids, T * k * 4},
       {(void**)&m->topk_w, T * k * 4},
       {(void**)&m->off, (E + 1) * 4},
-      {(void**)&m->pair_row, T * k * 4},
+      {(void**)&m->pair_row, Tr * k * 4},
       {(void**)&m->pos, T * k * 4},
-      {&m->h, T * k * de * es},
-      {(void**)&m->y, T * k * d * 4},
+      {&m->h, Tr * k * de * es},
+      {(void**)&m->y, Tr * k * d * 4},
       {&m->hs, T * ds * es},
       {(void**)&m->ys, T * d * 4},
       {(void**)&m->lm_part, Tc * m->lm_ntiles * 5 * 4},
@@ -867,7 +960,105 @@ int dg_test_moe(dg_model* m, int32_t layer, const void* b, int32_t T, const int3
   int s = check_layer(m, layer);
   if (!s) s = check_rows(m, T);
   if (s) return s;
+  if (T > route_chunk(m)) return fail(DG_ERR_SHAPE, "T=%d exceeds one routed launch (%d rows)", T, route_chunk(m));
   return routed(m, layer, b, T, ids, h ? h : m->h, y, m->off, m->pair_row, pos, (hipStream_t)stream);
+}
+
+int dg_mixed_step(dg_model* m, dg_segment* segs, int32_t n_segs, int32_t* status, void* stream) {
+  if (!m || !segs) return fail(DG_ERR_INVALID_ARG, "null argument");
+  if (n_segs < 1 || n_segs > MAX_SEGMENTS) return fail(DG_ERR_SHAPE, "n_segs %d outside [1, %d]", n_segs, MAX_SEGMENTS);
+  const dg_config& cfg = m->cfg;
+  long long T = 0, T_ref = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    const dg_segment& g = segs[i];
+    if (g.kind != DG_SEG_APPEND && g.kind != DG_SEG_REFINE)
+      return fail(DG_ERR_INVALID_ARG, "segment %d: kind %d", i, g.kind);
+    if (!g.kv) return fail(DG_ERR_INVALID_ARG, "segment %d: null kv", i);
+    int s = check_kv(m, g.kv, 1, g.kind == DG_SEG_APPEND ? g.n : 0);
+    if (s) return s;
+    for (int j = 0; j < i; ++j)
+      if (segs[j].kv->k == g.kv->k || segs[j].kv->v == g.kv->v)
+        return fail(DG_ERR_INVALID_ARG, "segments %d and %d share a KV cache", j, i);
+    if (g.kind == DG_SEG_APPEND) {
+      if (!g.tokens) return fail(DG_ERR_INVALID_ARG, "segment %d: null tokens", i);
+      if (g.n <= 0 || g.n > m->max_tokens)
+        return fail(DG_ERR_SHAPE, "segment %d: n=%d outside [1, max_tokens=%d]", i, g.n, m->max_tokens);
+    } else {
+      if (!g.canvas) return fail(DG_ERR_INVALID_ARG, "segment %d: null canvas", i);
+      s = check_canvas(m, g.canvas);
+      if (s) return s;
+      if (g.canvas->batch != 1) return fail(DG_ERR_SHAPE, "segment %d: a refine segment holds one canvas", i);
+      if (g.n != cfg.canvas_len) return fail(DG_ERR_SHAPE, "segment %d: n=%d != canvas_len", i, g.n);
+      if (g.canvas->step < 0 || g.canvas->step >= cfg.max_steps)
+        return fail(DG_ERR_STATE, "segment %d: step %d outside [0, max_steps)", i, g.canvas->step);
+      T_ref += g.n;
+    }
+    T += g.n;
+  }
+  if (T > m->Tmax) return fail(DG_ERR_SHAPE, "%lld rows exceed the workspace (%d)", T, m->Tmax);
+  if (T_ref > (long long)m->max_batch * cfg.canvas_len)
+    return fail(DG_ERR_SHAPE, "%lld refine rows exceed max_batch * canvas_len", T_ref);
+  hipStream_t st = (hipStream_t)stream;
+  // rows: refine segments first (their LM head and commit read one block), then append segments
+  MixedSeg sg[MAX_SEGMENTS];
+  RowSegments rs{};
+  int n = 0, r = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int i = 0; i < n_segs; ++i) {
+      if ((segs[i].kind == DG_SEG_REFINE) != (pass == 0)) continue;
+      sg[n] = MixedSeg{&segs[i], r, segs[i].kv->length};
+      rs.start[n] = r;
+      rs.pos0[n] = segs[i].kv->length;
+      r += segs[i].n;
+      ++n;
+    }
+  rs.n_segs = n;
+  rs.start[n] = r;
+  for (int i = 0; i < n; ++i) {
+    const int32_t* tok = sg[i].s->kind == DG_SEG_REFINE ? sg[i].s->canvas->tokens : sg[i].s->tokens;
+    HIP_OK(embed_gather(m->at, tok, sg[i].s->n, m->embed, cfg.d_model, cfg.vocab,
+                        (char*)m->x + (size_t)sg[i].start * cfg.d_model * m->esz, m->ctl + 1, st));
+  }
+  HIP_OK(rmsnorm(m->at, m->x, (int)T, cfg.d_model, cfg.rms_eps, m->a, st));
+  HIP_OK(rope_table_rows(rs, cfg.head_dim, cfg.rope_theta, m->rope_tab, st));
+  for (int l = 0; l < cfg.n_layers; ++l) {
+    int s = mixed_layer(m, l, sg, n, (int)T, (int)T_ref, st);
+    if (s) return s;
+  }
+  int last_ref = -1;
+  for (int i = 0; i < n; ++i)
+    if (sg[i].s->kind == DG_SEG_REFINE) last_ref = i;
+  for (int i = 0; i < n; ++i)
+    if (sg[i].s->kind == DG_SEG_REFINE && sg[i].s->hidden)
+      HIP_OK(hipMemcpyAsync(sg[i].s->hidden, (const char*)m->a + (size_t)sg[i].start * cfg.d_model * m->esz,
+                            (size_t)cfg.canvas_len * cfg.d_model * m->esz, hipMemcpyDeviceToDevice, st));
+  if (T_ref > 0) {
+    int s = lm_head_confidence(m, m->a, (int)T_ref, m->H, m->am, nullptr, st);
+    if (s) return s;
+  }
+  for (int i = 0; i < n; ++i) {
+    const dg_segment& g = *sg[i].s;
+    if (g.kind != DG_SEG_REFINE) continue;
+    const int r0 = sg[i].start;  // refine rows start at 0, one canvas after another
+    dg_canvas* cv = g.canvas;
+    ProfScope ps(m, DG_PROF_COMMIT, st);
+    // the last commit of the pass publishes the status word
+    HIP_OK(commit_renoise(m->H + r0, m->am + r0, cv->tokens, cv->committed, 1, cfg.canvas_len, cv->step,
+                          cfg.max_steps, cfg.commit_threshold, cv->seed, cv->block, cfg.vocab, cfg.mask_token,
+                          g.n_uncommitted ? g.n_uncommitted : m->n_unc + r0 / cfg.canvas_len,
+                          i == last_ref ? m->ctl + 1 : nullptr, i == last_ref ? m->ctl : nullptr, st));
+    if (g.entropy)
+      HIP_OK(hipMemcpyAsync(g.entropy, m->H + r0, sizeof(float) * cfg.canvas_len, hipMemcpyDeviceToDevice, st));
+    if (g.argmax)
+      HIP_OK(hipMemcpyAsync(g.argmax, m->am + r0, sizeof(int) * cfg.canvas_len, hipMemcpyDeviceToDevice, st));
+  }
+  if (last_ref < 0) HIP_OK(status_publish(m->ctl + 1, m->ctl, st));
+  if (status) HIP_OK(hipMemcpyAsync(status, m->ctl, sizeof(int), hipMemcpyDeviceToDevice, st));
+  for (int i = 0; i < n; ++i) {
+    if (sg[i].s->kind == DG_SEG_REFINE) sg[i].s->canvas->step += 1;
+    else sg[i].s->kv->length += sg[i].s->n;
+  }
+  return DG_OK;
 }
 
 int dg_test_force_routing(dg_model* m, const int32_t* ids) {

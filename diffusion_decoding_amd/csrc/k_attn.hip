@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
   const int kend = min(total, kbeg + keys_per_split);
   const float scale = 1.0f / sqrtf(float(DH));
 
-  const T* qrow = (const T*)a.q + ((long long)bh * a.n + min(qi, a.n - 1)) * DH;
+  const T* qrow = (const T*)a.q + (long long)bh * a.q_bh + (long long)min(qi, a.n - 1) * DH;
   const bool qvalid = qi < a.n;
   const T* K0 = (const T*)a.k0 + (long long)bh * a.s0_bh;
   const T* V0 = (const T*)a.v0 + (long long)bh * a.s0_bh;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       0x00020000);
 
   // Q as the B operand of S^T = K Q^T
-  const bf16* qrow = (const bf16*)a.q + ((long long)bh * a.n + min(qi, a.n - 1)) * DH;
+  const bf16* qrow = (const bf16*)a.q + (long long)bh * a.q_bh + (long long)min(qi, a.n - 1) * DH;
   u32x4 qf[NQ];
 #pragma unroll
   for (int ks = 0; ks < NQ; ++ks) qf[ks] = *(const u32x4*)(qrow + 32 * ks + 8 * g4);
@@ -664,6 +664,7 @@ int attn_splits_for(int B, int H, int n, int keys, int dh) {
 
 int attention(ActType at, const AttnArgs& a, hipStream_t st) {
   if (a.n <= 0) return 0;
+  if (a.q_bh < (long long)a.n * a.dh) return int(hipErrorInvalidValue);
   if (at == ACT_BF16) {
     if (a.dh == 128) return launch_bf16<128>(a, st);
     if (a.dh == 64) return launch_bf16<64>(a, st);

@@ -117,6 +117,39 @@ __global__ void rope_table_kernel(int n, int dh, int pos0, float theta, float2* 
   tab[e] = float2{c, s};
 }
 
+// The same table for the rows of a mixed batch, each at its segment's
+// position (segments passed by value; a row finds its segment by a scan of
+// at most MAX_SEGMENTS starts).
+__global__ void rope_table_rows_kernel(RowSegments rs, int dh, float theta, float2* tab) {
+  const int half = dh / 2;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= rs.start[rs.n_segs] * half) return;
+  const int j = e % half, r = e / half;
+  int s = 0;
+  while (s + 1 < rs.n_segs && r >= rs.start[s + 1]) ++s;
+  float c = 1.f, sn = 0.f;
+  if (theta > 0.f) {
+    const double inv = pow((double)theta, -2.0 * j / dh);
+    const double ang = (double)(rs.pos0[s] + r - rs.start[s]) * inv;
+    c = (float)cos(ang);
+    sn = (float)sin(ang);
+  }
+  tab[e] = float2{c, sn};
+}
+
+// One thread per 16-byte chunk of a row: dst row0 + i of plane h <- src row i.
+__global__ void kv_copy_rows_kernel(const uint8_t* sk, const uint8_t* sv, long long src_bh_b, int H, int n,
+                                    int row_b, uint8_t* dk, uint8_t* dv, long long dst_bh_b, int row0) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int cpr = row_b / 16;
+  if (e >= (long long)H * n * cpr) return;
+  const int c = int(e % cpr), i = int((e / cpr) % n), h = int(e / ((long long)cpr * n));
+  const long long so = h * src_bh_b + (long long)i * row_b + 16 * c;
+  const long long d0 = h * dst_bh_b + (long long)(row0 + i) * row_b + 16 * c;
+  *(u32x4*)(dk + d0) = *(const u32x4*)(sk + so);
+  *(u32x4*)(dv + d0) = *(const u32x4*)(sv + so);
+}
+
 // Rotate-half RoPE on q and k (pairs j, j + dh/2) and scatter q, k, v to
 // their per-head layouts; one thread per (token, head, 4 consecutive pairs).
 template <typename T>
@@ -385,6 +418,11 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float* H, const int*
   }
 }
 
+__global__ void status_publish_kernel(int* live, int* published) {
+  *published = *live;
+  *live = 0;
+}
+
 __global__ void philox_kernel(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas,
                               uint32_t block, uint32_t modulus, int n, uint32_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -427,6 +465,27 @@ int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st)
   if (total <= 0) return 0;
   hipLaunchKernelGGL(rope_table_kernel, dim3((total + 255) / 256), dim3(256), 0, st, n, dh, pos0, theta,
                      (float2*)tab);
+  return int(hipGetLastError());
+}
+
+int rope_table_rows(const RowSegments& rs, int dh, float theta, float* tab, hipStream_t st) {
+  if (rs.n_segs <= 0 || rs.n_segs > MAX_SEGMENTS) return int(hipErrorInvalidValue);
+  const int total = rs.start[rs.n_segs] * (dh / 2);
+  if (total <= 0) return 0;
+  hipLaunchKernelGGL(rope_table_rows_kernel, dim3((total + 255) / 256), dim3(256), 0, st, rs, dh, theta,
+                     (float2*)tab);
+  return int(hipGetLastError());
+}
+
+int kv_copy_rows(ActType at, const void* src_k, const void* src_v, long long src_bh, int H, int n, int dh,
+                 void* dst_k, void* dst_v, long long dst_bh, int row0, hipStream_t st) {
+  const int es = at == ACT_BF16 ? 2 : 4, row_b = dh * es;
+  if (row_b % 16) return int(hipErrorInvalidValue);
+  const long long total = (long long)H * n * (row_b / 16);
+  if (total <= 0) return 0;
+  hipLaunchKernelGGL(kv_copy_rows_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                     (const uint8_t*)src_k, (const uint8_t*)src_v, src_bh * es, H, n, row_b, (uint8_t*)dst_k,
+                     (uint8_t*)dst_v, dst_bh * es, row0);
   return int(hipGetLastError());
 }
 
@@ -492,6 +551,11 @@ int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, 
   if (N > 1024) return int(hipErrorInvalidValue);
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(1024), 0, st, H, am, tok, committed, N, step,
                      max_steps, threshold, seed, block, vocab, mask_token, n_unc, live_flags, status);
+  return int(hipGetLastError());
+}
+
+int status_publish(int* live, int* published, hipStream_t st) {
+  hipLaunchKernelGGL(status_publish_kernel, dim3(1), dim3(1), 0, st, live, published);
   return int(hipGetLastError());
 }
 

@@ -104,9 +104,9 @@ __global__ void force_kernel(const float* logits, int T, int E, int k, const int
   }
 }
 
-__global__ void counts_kernel(const int* off, int E, int* counts) {
+__global__ void counts_kernel(const int* off, int E, int* counts, bool accumulate) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < E) counts[e] = off[e + 1] - off[e];
+  if (e < E) counts[e] = (accumulate ? counts[e] : 0) + off[e + 1] - off[e];
 }
 
 constexpr int PERM_THREADS = 1024;
@@ -210,8 +210,8 @@ int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row,
   return int(hipGetLastError());
 }
 
-int expert_counts(const int* off, int E, int* counts, hipStream_t st) {
-  hipLaunchKernelGGL(counts_kernel, dim3((E + 255) / 256), dim3(256), 0, st, off, E, counts);
+int expert_counts(const int* off, int E, int* counts, bool accumulate, hipStream_t st) {
+  hipLaunchKernelGGL(counts_kernel, dim3((E + 255) / 256), dim3(256), 0, st, off, E, counts, accumulate);
   return int(hipGetLastError());
 }
 

@@ -108,7 +108,8 @@ int fp4_decode(const void* packed, const uint8_t* scales, int n_blocks, void* ou
 
 // ---------------------------------------------------------------- attention (k_attn.hip)
 struct AttnArgs {
-  const void* q;          // [B][H][n][dh]
+  const void* q;          // (b,h) planes q_bh elements apart, rows of dh: [B][H][n][dh] when q_bh = n*dh
+  long long q_bh;
   const void* k0;         // segment 0 keys: (b,h) at k0 + (b*H+h)*s0_bh, rows [0, len0)
   const void* v0;
   long long s0_bh;        // elements between (b,h) planes of segment 0
@@ -143,6 +144,20 @@ int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vo
 int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st);
 // tab[i][j] = (cos, sin) of (pos0 + i) * theta^(-2j/dh), i < n, j < dh/2 (float pairs)
 int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st);
+// Rows of a mixed batch: segment s holds rows [start[s], start[s + 1]) at
+// positions pos0[s] + (row - start[s]).
+constexpr int MAX_SEGMENTS = 16;
+struct RowSegments {
+  int n_segs;
+  int start[MAX_SEGMENTS + 1];
+  int pos0[MAX_SEGMENTS];
+};
+// tab[r][j] = (cos, sin) of the position of row r (as rope_table), r < start[n_segs]
+int rope_table_rows(const RowSegments& rs, int dh, float theta, float* tab, hipStream_t st);
+// dst planes (h) at dst_k / dst_v + h * dst_bh, rows row0 .. row0 + n - 1 <- src planes
+// (src_bh apart) rows 0 .. n - 1 (dh elements of act dtype per row)
+int kv_copy_rows(ActType at, const void* src_k, const void* src_v, long long src_bh, int H, int n, int dh,
+                 void* dst_k, void* dst_v, long long dst_bh, int row0, hipStream_t st);
 // RoPE on q,k from qkv [T][3A] (T = B*n, token i rotated by tab row i) and scatter:
 // q -> q_out [B][H][n][dh]; k,v -> (b,h) planes at kdst/vdst + (b*H+h)*dst_bh + (row0+i)*dh.
 int rope_scatter(ActType at, const void* qkv, int B, int n, int H, int dh, const float* tab, void* q_out,
@@ -165,6 +180,8 @@ int canvas_prefill(int* tok, uint8_t* committed, int n, const int* given, const 
 int commit_renoise(const float* H, const int* am, int* tok, uint8_t* committed, int B, int N,
                    int step, int max_steps, float threshold, uint64_t seed, uint32_t block,
                    int vocab, int mask_token, int* n_unc, int* live_flags, int* status, hipStream_t st);
+// *published = *live; *live = 0 (one thread)
+int status_publish(int* live, int* published, hipStream_t st);
 int philox_fill(uint64_t seed, uint32_t pos0, uint32_t tag, uint32_t canvas, uint32_t block,
                 uint32_t modulus, int n, uint32_t* out, hipStream_t st);
 
@@ -179,7 +196,7 @@ int router_force(const float* logits, int T, int E, int k, const int* forced, in
 // token-ascending), pos[T][k] (slot of pair (t, j)).
 int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,
                    hipStream_t st);
-// counts[e] = off[e + 1] - off[e] for e < E (diagnostic)
-int expert_counts(const int* off, int E, int* counts, hipStream_t st);
+// counts[e] (+)= off[e + 1] - off[e] for e < E (diagnostic; accumulate adds)
+int expert_counts(const int* off, int E, int* counts, bool accumulate, hipStream_t st);
 
 }  // namespace dg

@@ -171,6 +171,62 @@ def commit_canvas(model: Model, tokens: torch.Tensor, kv: KVCache, stream=None):
     kv.length = s.length
 
 
+@dataclass
+class Append:
+    """A causal pass of a mixed batch: ``tokens`` (int32 [n], device) appended
+    to the batch-1 cache ``kv`` (a prompt read or a committed canvas)."""
+    kv: KVCache
+    tokens: torch.Tensor
+
+
+@dataclass
+class Refine:
+    """One denoise step of a batch-1 canvas in a mixed batch; the optional
+    outputs are device tensors of [canvas_len] (entropy fp32, argmax int32)
+    and [1] (n_uncommitted int32)."""
+    kv: KVCache
+    canvas: Canvas
+    entropy: Optional[torch.Tensor] = None
+    argmax: Optional[torch.Tensor] = None
+    n_uncommitted: Optional[torch.Tensor] = None
+    hidden: Optional[torch.Tensor] = None   # diagnostic: final normed hidden [canvas_len, d_model]
+
+
+def mixed_step(model: Model, segments, status=None, stream=None):
+    """One pass over requests in different phases (Append and Refine items),
+    each with its own batch-1 cache; updates canvas.step and kv.length."""
+    segs = list(segments)
+    n_segs = len(segs)
+    arr = (_lib.dg_segment * max(n_segs, 1))()
+    keep = []
+    for i, g in enumerate(segs):
+        if g.kv.k.shape[1] != 1:
+            raise ValueError(f"segment {i}: a mixed batch takes batch-1 caches")
+        kvs = g.kv.struct()
+        keep.append(kvs)
+        if isinstance(g, Append):
+            t = g.tokens
+            if t.dtype != torch.int32 or t.dim() != 1 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"segment {i}: tokens must be a contiguous int32 device vector")
+            arr[i] = _lib.dg_segment(_lib.DG_SEG_APPEND, t.shape[0], ctypes.pointer(kvs), _ptr(t), None,
+                                     None, None, None, None)
+        elif isinstance(g, Refine):
+            if g.canvas.tokens.shape[0] != 1:
+                raise ValueError(f"segment {i}: a refine segment holds one canvas")
+            cs = g.canvas.struct()
+            keep.append(cs)
+            arr[i] = _lib.dg_segment(_lib.DG_SEG_REFINE, g.canvas.tokens.shape[1], ctypes.pointer(kvs), None,
+                                     ctypes.pointer(cs), _ptr(g.entropy), _ptr(g.argmax), _ptr(g.n_uncommitted),
+                                     _ptr(g.hidden))
+        else:
+            raise TypeError(f"segment {i}: {type(g).__name__} is neither Append nor Refine")
+    _lib.dg_mixed_step(model.handle, arr, n_segs, _ptr(status), _stream(stream))
+    for i, g in enumerate(segs):
+        g.kv.length = arr[i].kv.contents.length
+        if isinstance(g, Refine):
+            g.canvas.step = arr[i].canvas.contents.step
+
+
 def test_philox(seed, pos0, tag, canvas, block, modulus, n, stream=None) -> torch.Tensor:
     out = torch.empty(n, dtype=torch.int64, device="cuda")
     buf = torch.empty(n, dtype=torch.int32, device="cuda")

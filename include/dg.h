@@ -197,10 +197,11 @@ const char* dg_version(void);
  * capacity (rows per layer, canvas and head) any call may pass: calls with a
  * larger kv->capacity fail with DG_ERR_SHAPE.  0 takes the kernels' own
  * limit, 2^31 / (head_dim x element size) rows (attention addresses a cache
- * plane with 32-bit byte offsets); a larger max_kv is refused.  max_batch x
- * max(max_tokens, canvas_len) may be at most 2048 with bf16 activations and
- * 1024 with fp32 (DG_ERR_SHAPE otherwise).  Must be called with the target
- * device current. */
+ * plane with 32-bit byte offsets); a larger max_kv is refused.  The rows of
+ * one call, max_batch x max(max_tokens, canvas_len), may be at most 8192
+ * (DG_ERR_SHAPE otherwise); the routed experts take more than 2048 rows (1024
+ * with fp32 activations) in chunks, each streaming the expert weights once.
+ * Must be called with the target device current. */
 int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch,
                     int32_t max_tokens, int32_t max_kv, dg_model** out);
 int dg_model_destroy(dg_model* m);
@@ -259,6 +260,51 @@ int dg_generate_canvas(dg_model* m, dg_canvas* c, const dg_kv* kv, int32_t* step
  * an id outside the vocabulary reads row 0 and raises DG_STATUS_TOKEN, which
  * the next denoise step publishes. */
 int dg_commit_canvas(dg_model* m, const int32_t* tokens, int32_t n, dg_kv* kv, void* stream);
+
+/* One segment of a mixed-phase batch (dg_mixed_step).  Each segment is one
+ * request with its own batch-1 KV cache (kv->batch == 1; no two segments may
+ * share a cache).
+ *  - DG_SEG_REFINE: one denoise step of `canvas` (batch 1, step < max_steps)
+ *    against the first kv->length cache rows, exactly as dg_denoise_step;
+ *    n == canvas_len; entropy/argmax (device, [canvas_len], may be NULL)
+ *    receive the step's per-position confidence, n_uncommitted (device [1],
+ *    may be NULL) the count after the commit.  Increments canvas->step.
+ *  - DG_SEG_APPEND: a causal pass over tokens[n] (device, n <= max_tokens),
+ *    exactly as dg_commit_canvas: a prompt read, or a committed canvas being
+ *    appended.  Writes the rows' keys and values at kv->length .. +n-1 of every
+ *    layer and advances kv->length by n (length + n <= capacity). */
+enum { DG_SEG_APPEND = 0, DG_SEG_REFINE = 1 };
+typedef struct dg_segment {
+  int32_t kind;            /* DG_SEG_APPEND or DG_SEG_REFINE */
+  int32_t n;               /* rows: tokens to append, or canvas_len */
+  dg_kv* kv;               /* host pointer to the request's cache descriptor (length/step updated) */
+  const int32_t* tokens;   /* APPEND: device [n] */
+  dg_canvas* canvas;       /* REFINE: host pointer to a batch-1 canvas */
+  float* entropy;          /* REFINE, optional: device [canvas_len] */
+  int32_t* argmax;         /* REFINE, optional: device [canvas_len] */
+  int32_t* n_uncommitted;  /* REFINE, optional: device [1] */
+  void* hidden;            /* REFINE, test/diagnostic: final normed hidden [canvas_len][d_model] */
+} dg_segment;
+
+/* One pass over a batch of requests in different phases -- prompt reads and
+ * block commits (causal) next to canvas refinements (bidirectional): the
+ * serving requirement that every request picks its own attention mode within
+ * one batch (ipcmen.com, "模型构建与底层优化": requests cycle through prompt
+ * reading, canvas refinement and block commit, switching between causal and
+ * bidirectional attention).  The segments' rows are stacked (refine segments
+ * first) and every block runs its dense projections, shared expert, router
+ * and routed experts once over all rows -- the expert weights stream once for
+ * the whole mix -- while attention runs per segment in that segment's mode
+ * over its own cache.  Each segment's results equal those of its own
+ * dg_denoise_step or dg_commit_canvas up to fp32 summation order (row
+ * positions and chunking differ).  1 <= n_segs <= 16; the total rows must fit
+ * the workspace (max_batch x max(max_tokens, canvas_len)) and the refine rows
+ * max_batch x canvas_len, else DG_ERR_SHAPE; every segment is validated
+ * before anything is enqueued.  Token and numeric faults raise the status
+ * word as in the other entries; the pass publishes it to *status (device [1],
+ * may be NULL).  Asynchronous; updates canvas->step and kv->length on the
+ * host. */
+int dg_mixed_step(dg_model* m, dg_segment* segs, int32_t n_segs, int32_t* status, void* stream);
 
 /* Rewrite n_mats row-major expert matrices src[n_mats][rows][cols] (BF16,
  * FP8_E4M3 codes, or MXFP4 codes two per byte) into the tiled layout
