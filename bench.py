@@ -247,6 +247,80 @@ def time_loop(cfg, canvases: int, warmup: int, kernels=()):
     return out
 
 
+def time_mixed(cfg, refine: int = 3, commit_len: int = 256, prompt_len: int = 512, passes: int = 8,
+               warmup: int = 2):
+    """One serving batch in different phases, at the shapes of ``cfg``: `refine`
+    canvases each denoised one step against its own prompt cache, one canvas
+    commit (`commit_len` tokens appended after a prompt) and one prompt read
+    (`prompt_len` tokens into an empty cache).  Times one dg_mixed_step pass
+    over all of them against the same work as separate calls (a batch-1
+    denoise step per canvas, a causal pass per append)."""
+    import torch
+
+    from diffusion_decoding_amd import runtime as rt
+    from workloads import make_inputs
+
+    n_req = refine + 2
+    P, N = cfg.prompt_len, cfg.canvas_len
+    cap = P + max(commit_len, prompt_len)
+    c = cfg.replace(name=cfg.name + "_mixed", batch=n_req)
+    log(f"[bench] generating inputs for {c.name} ({n_req} requests) on the GPU")
+    inp = make_inputs(c, device="cuda", kv_capacity=cap)
+    rows = refine * N + commit_len + prompt_len
+    # workspace rows = max_batch x max_tokens must hold the whole pass
+    model = rt.Model(inp, max_batch=refine, max_tokens=max(commit_len, prompt_len, -(-rows // refine)), max_kv=cap)
+    kvs = [rt.KVCache(inp.kv_k[:, b:b + 1].clone(), inp.kv_v[:, b:b + 1].clone(), P) for b in range(n_req)]
+    kvs[-1].length = 0
+    canv = [rt.Canvas.empty(1, N, cfg.seed + b) for b in range(refine)]
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 7)
+    t_commit = torch.randint(0, cfg.vocab, (commit_len,), generator=g, device="cuda", dtype=torch.int32)
+    t_prompt = torch.randint(0, cfg.vocab, (prompt_len,), generator=g, device="cuda", dtype=torch.int32)
+    base = [kv.length for kv in kvs]
+
+    def reset():
+        for kv, L0 in zip(kvs, base):
+            kv.length = L0
+        for cv in canv:
+            rt.canvas_init(model, cv)
+
+    def mixed():
+        segs = [rt.Refine(kvs[b], canv[b]) for b in range(refine)]
+        segs += [rt.Append(kvs[refine], t_commit), rt.Append(kvs[refine + 1], t_prompt)]
+        rt.mixed_step(model, segs)
+
+    def separate():
+        for b in range(refine):
+            rt.denoise_step(model, canv[b], kvs[b])
+        rt.commit_canvas(model, t_commit[None], kvs[refine])
+        rt.commit_canvas(model, t_prompt[None], kvs[refine + 1])
+
+    res = {}
+    for name, fn in (("mixed", mixed), ("separate", separate), ("mixed_again", mixed)):
+        for _ in range(warmup):
+            reset()
+            fn()
+        torch.cuda.synchronize()
+        dt = 0.0
+        for _ in range(passes):
+            reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            dt += time.perf_counter() - t0
+        res[name] = dt / passes * 1e3
+        log(f"[bench] {c.name} {name}: {res[name]:.3f} ms per pass")
+    free_gpu(model)
+    del inp, kvs, canv
+    free_gpu()
+    ms = min(res["mixed"], res["mixed_again"])
+    return {"workload": c.name, "refine_canvases": refine, "canvas": N, "prompt_kv": P,
+            "commit_append": commit_len, "prompt_read": prompt_len, "rows_per_pass": rows,
+            "ms_per_pass_mixed": ms, "ms_per_pass_separate": res["separate"],
+            "speedup": res["separate"] / ms, "rows_per_s": rows / ms * 1e3,
+            "refine_canvas_tokens_per_s": refine * N / ms * 1e3}
+
+
 def time_block_ar(cfg, warmup: int = 1):
     """Block-autoregressive generation: causal encode of the prompt, then
     n_canvases canvases, each committed to the KV cache by a causal pass."""
@@ -310,8 +384,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB five times and exit "
                          "(reference for the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the batch-4 (c3), batch-8 (c5), fill-in-the-middle and block-autoregressive "
-                         "fp8 (c4) measurements")
+                    help="skip the batch-4 (c3), batch-8 (c5), fill-in-the-middle, block-autoregressive "
+                         "fp8 (c4), MXFP4 (c6) and mixed-phase measurements")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the per-kernel-class roofline table (one extra canvas per class after "
                          "the timed region)")
@@ -475,6 +549,8 @@ def main():
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
         # MXFP4 routed experts (E2M1 codes + E8M0 block scales), same shapes as the headline
         out["mxfp4"] = time_loop(get_config("c6"), canvases=1, warmup=1, kernels=("moe_gateup", "moe_down"))
+        # a serving batch in mixed phases: three canvases refining, a canvas commit and a prompt read
+        out["mixed"] = time_mixed(get_config("c2"))
     print(json.dumps(out), flush=True)
 
 
