@@ -21,13 +21,15 @@ def say(*a):
 class Pair:
     """The GPU model + KV cache and the oracle weights + KV over one input set."""
 
-    def __init__(self, rt, cfg, kv_len=None, kv_capacity=None):
+    def __init__(self, rt, cfg, kv_len=None, kv_capacity=None, cache=True):
         self.rt, self.cfg = rt, cfg
         self.inp = make_inputs(cfg, device="cuda", kv_capacity=kv_capacity)
         self.model = rt.Model(self.inp)
         n = self.inp.kv_len if kv_len is None else kv_len
         self.kv = rt.KVCache(self.inp.kv_k.clone(), self.inp.kv_v.clone(), n)
-        self.W = om.Weights(self.inp, cache=True)
+        # cache=False converts each weight when used (a 30-layer model in float64 would
+        # take ~135 GB of host memory)
+        self.W = om.Weights(self.inp, cache=cache)
         self.okv = om.KV(self.inp.kv_k, self.inp.kv_v, n, bf16=cfg.act_dtype == "bf16")
 
     def close(self):
@@ -96,6 +98,7 @@ class Pair:
                 gpu = dict(entropy=to_host(ent), argmax=to_host(am), tokens=to_host(canvas.tokens),
                            committed=to_host(canvas.committed), hidden=to_host(hidden.float()),
                            logits=to_host(logits) if keep_logits else None)
+                self.last_ores = ores
                 rep = compare_step(cfg, ores, pre, ost, gpu, W=self.W)
                 rep.forced_rows = n_forced
                 say("   ", rep)
@@ -108,3 +111,43 @@ class Pair:
         finally:
             rt.test_force_routing(self.model, None)
         return reps, ost
+
+
+def oracle_perturbed_hidden(W, okv, cfg, tokens, trace, frac=0.01, seed=0, eps=None):
+    """The oracle's final normed hidden rows [N, d] of canvas ``tokens`` (batch
+    1, cache ``okv``) with a random ``frac`` of block 0's outputs moved to the
+    neighbouring bf16 value: how far one block's worth of bf16 rounding noise
+    carries by the last layer, in the oracle itself.  Rows whose router
+    logits nearly tie in some layer of the unperturbed run (``trace``) keep
+    that run's expert picks, as the GPU is made to."""
+    from oracle.numerics import round_bf16
+    from tests.parity import route_eps
+    prec = om.Prec(cfg.act_dtype)
+    k = cfg.top_k
+    eps = route_eps(cfg) if eps is None else eps
+    rng = np.random.default_rng(seed)
+    plain_route = om.route
+    x = prec.act(W.embed_rows(tokens))
+    try:
+        for l in range(cfg.n_layers):
+            r_ref, ids_ref = trace["route_r32"][l], trace["route_ids"][l]
+            srt = -np.sort(-r_ref, axis=1)
+            near = (srt[:, k - 1] - srt[:, k]) < eps
+
+            def held(r32, kk, near=near, ids_ref=ids_ref):
+                ids, _ = plain_route(r32, kk)
+                ids[near] = ids_ref[near]
+                sel = np.take_along_axis(r32, ids, axis=1)
+                w = np.exp(sel - sel.max(axis=1, keepdims=True))
+                return ids, w / w.sum(axis=1, keepdims=True)
+            om.route = held
+            kvk, kvv = okv.get(l, 0)
+            x, _, _ = om.layer_forward(x, W, l, kvk, kvv, okv.length, prec, cfg)
+            om.route = plain_route
+            if l == 0:
+                sel = rng.random(x.shape) < frac
+                ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x[sel]), 1e-30))) - 7)
+                x[sel] = round_bf16(x[sel] + np.where(rng.random(sel.sum()) < 0.5, -ulp, ulp))
+    finally:
+        om.route = plain_route
+    return prec.act(om.rmsnorm(x, cfg.rms_eps))

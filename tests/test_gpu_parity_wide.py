@@ -144,6 +144,43 @@ def test_c2_shape_two_layers_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_c2_full_depth_one_step(rt):
+    """The headline workload itself -- 30 layers, 128 experts top-8, 262144
+    ids, 2048-row prompt -- for one step against the oracle.
+
+    Thirty stacked random-weight blocks amplify a perturbation about a
+    hundredfold, so the GPU's final hidden rows drift from the oracle's by
+    far more than one block's bf16 noise floor.  The bound is taken from the
+    oracle itself: its own run with 1 % of block 0's outputs moved by one
+    bf16 ulp (less than the GPU's one-block difference) drifts as far, and
+    the GPU must stay within twice that.  Decisions are checked at the stated
+    windows on the GPU's own hidden rows (check (b)); those against the
+    oracle's forward (check (c)) are reported."""
+    from tests.gpu_helpers import oracle_perturbed_hidden
+    from tests.parity import H_TOL
+    cfg = get_config("c2")
+    say("c2 full depth, one step (30 layers, 262144 ids)")
+    p = Pair(rt, cfg, cache=False)
+    reps, _ = p.run_locked(max_steps=1)
+    ores = p.last_ores
+    p.close()
+    r = reps[0]
+    pre_tokens = om.init_state(cfg, cfg.seed, 0).tokens[0]   # the canvas the step scored
+    h_pert = oracle_perturbed_hidden(p.W, p.okv, cfg, pre_tokens, ores.trace)
+    ref = ores.hidden[0]
+    sens = float(np.linalg.norm(h_pert - ref) / np.linalg.norm(ref))
+    say(f"   GPU hidden rel-L2 {r.hidden_rel:.3e}, logits {r.logits_rel:.3e}; oracle with 1% one-ulp flips "
+        f"after block 0: {sens:.3e}")
+    say(f"   (c) against the oracle's forward: {r.mism_argmax} argmax, {r.mism_commit} commit, {r.mism_tokens} "
+        f"token differences outside the windows")
+    del p
+    _free()
+    assert r.hidden_rel <= 2 * sens and r.logits_rel <= 2 * sens, r
+    assert r.max_dH_head <= H_TOL, r
+    assert r.mism_argmax_head == 0 and r.mism_commit_head == 0 and r.mism_tokens_head == 0, r
+    assert r.m and r.checked_commits >= 0.5 * r.m, r
+
+
 def test_c3_shape_one_layer_one_step(rt):
     """Batch 4, each canvas with its own 8192-row prompt; 1024 tokens pooled in the experts."""
     cfg = get_config("c3").replace(name="c3_shape_1_layer", n_layers=1)
