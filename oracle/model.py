@@ -17,6 +17,13 @@ Pages (four DiffusionGemma write-ups) and the passages each function follows:
   uniform-state noise (no mask token).
 * ipcmen.com, "工作原理：并行精炼与自我修正": each step locks the most confident
   tokens and randomises the uncertain positions for the next step.
+* openai-hub.com (Google DeepMind 发布 DiffusionGemma), "为什么扩散能跑得比自回归快":
+  self-conditioning is one of the techniques the model brings together (named
+  only).  Reading, as an option of the config: every step after the first
+  also feeds the model its own previous prediction -- the argmax at each
+  position, the value the commit rule would lock -- by adding that token's
+  embedding row to the position's input embedding (one sum, rounded once to
+  the activation precision); the first step adds nothing.
 
 Readings where the pages are silent (each is also listed in the design notes):
 pre-norm RMSNorm blocks without gains and with a final norm before the LM head;
@@ -376,10 +383,11 @@ class CanvasState:
     step: int = 0
     seed: int = 0
     block: int = 0
+    prediction: Optional[np.ndarray] = None   # int64 [B, N]: previous step's argmax (self-conditioning)
 
     def copy(self):
         return CanvasState(self.tokens.copy(), self.committed.copy(), self.step, self.seed,
-                           self.block)
+                           self.block, None if self.prediction is None else self.prediction.copy())
 
 
 @dataclass
@@ -419,10 +427,21 @@ def prefill(state: CanvasState, tokens: np.ndarray, mask: np.ndarray) -> CanvasS
     return state
 
 
-def forward_canvas(tok_row, W: Weights, kv: KV, b: int, cfg, prec: Prec, trace=None):
-    """Bidirectional forward of one canvas; returns the final normed hidden rows."""
+def input_embedding(tok_row, W: Weights, prec: Prec, cond_row=None) -> np.ndarray:
+    """Input rows of a canvas: the token embeddings, plus (self-conditioning)
+    the embeddings of the previous step's predictions, summed before one
+    rounding to the activation precision."""
+    e = W.embed_rows(tok_row)
+    if cond_row is not None:
+        e = e + W.embed_rows(cond_row)
+    return prec.act(e)
+
+
+def forward_canvas(tok_row, W: Weights, kv: KV, b: int, cfg, prec: Prec, trace=None, cond_row=None):
+    """Bidirectional forward of one canvas; returns the final normed hidden rows.
+    ``cond_row``: the previous step's predictions (self-conditioning) or None."""
     P = kv.length
-    x = prec.act(W.embed_rows(tok_row))
+    x = input_embedding(tok_row, W, prec, cond_row)
     for l in range(cfg.n_layers):
         kvk, kvv = kv.get(l, b)
         x, _, _ = layer_forward(x, W, l, kvk, kvv, P, prec, cfg, trace=trace)
@@ -444,8 +463,10 @@ def denoise_step(W: Weights, kv: KV, state: CanvasState, cfg, keep_logits: bool 
     Hs, As, Gs, NW, Ls, Hid = [], [], [], [], [], []
     Up, cut, ms = np.zeros(B, dtype=np.int64), np.full(B, np.nan), np.zeros(B, dtype=np.int64)
     trace = {}
+    cond = getattr(cfg, "self_condition", False) and state.prediction is not None
     for b in range(B):
-        hf = forward_canvas(state.tokens[b], W, kv, b, cfg, prec, trace=trace)
+        hf = forward_canvas(state.tokens[b], W, kv, b, cfg, prec, trace=trace,
+                            cond_row=state.prediction[b] if cond else None)
         z = lm_head_logits(hf, W)
         H32, a, gap = confidence(z)
         unc = ~state.committed[b]
@@ -471,6 +492,8 @@ def denoise_step(W: Weights, kv: KV, state: CanvasState, cfg, keep_logits: bool 
     for b in range(B):
         renoise(state.tokens[b], state.committed[b], state.seed, s, b, state.block, cfg.vocab,
                 getattr(cfg, "mask_token", -1))
+    if getattr(cfg, "self_condition", False):
+        state.prediction = res.argmax.copy()
     state.step = s + 1
     return res
 

@@ -40,6 +40,7 @@ class Config:
     n_canvases: int = 1      # canvases generated one after another (block-AR)
     prompt_mode: str = "kv"  # "kv": random post-RoPE K,V; "tokens": ids encoded by a causal pass
     mask_token: int = -1     # -1: uniform-state noise; a vocabulary id: absorbing-state ([MASK]) noise
+    self_condition: bool = False  # each step after the first adds the embedding of the previous step's argmax
 
     @property
     def qkv_dim(self) -> int:
