@@ -385,7 +385,7 @@ def main():
                          "(reference for the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the batch-4 (c3), batch-8 (c5), fill-in-the-middle, block-autoregressive "
-                         "fp8 (c4), MXFP4 (c6) and mixed-phase measurements")
+                         "fp8 (c4), MXFP4 (c6), self-conditioning and mixed-phase measurements")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the per-kernel-class roofline table (one extra canvas per class after "
                          "the timed region)")
@@ -549,6 +549,9 @@ def main():
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
         # MXFP4 routed experts (E2M1 codes + E8M0 block scales), same shapes as the headline
         out["mxfp4"] = time_loop(get_config("c6"), canvases=1, warmup=1, kernels=("moe_gateup", "moe_down"))
+        # self-conditioning: each step after the first adds the previous step's predictions to the input
+        out["self_condition"] = time_loop(c2.replace(name="c2_self_condition", self_condition=True),
+                                          canvases=1, warmup=1)
         # a serving batch in mixed phases: three canvases refining, a canvas commit and a prompt read
         out["mixed"] = time_mixed(get_config("c2"))
     print(json.dumps(out), flush=True)

@@ -30,7 +30,7 @@ class dg_config(ctypes.Structure):
                 ("d_expert", c_int32), ("d_shared", c_int32), ("vocab", c_int32),
                 ("canvas_len", c_int32), ("max_steps", c_int32), ("rope_theta", c_float),
                 ("rms_eps", c_float), ("commit_threshold", c_float), ("act_dtype", c_int32),
-                ("expert_dtype", c_int32), ("mask_token", c_int32)]
+                ("expert_dtype", c_int32), ("mask_token", c_int32), ("self_condition", c_int32)]
 
 
 class dg_layer_weights(ctypes.Structure):
@@ -50,7 +50,7 @@ class dg_kv(ctypes.Structure):
 
 class dg_canvas(ctypes.Structure):
     _fields_ = [("tokens", c_void_p), ("committed", c_void_p), ("batch", c_int32),
-                ("step", c_int32), ("seed", c_uint64), ("block", c_uint32)]
+                ("step", c_int32), ("seed", c_uint64), ("block", c_uint32), ("prediction", c_void_p)]
 
 
 class dg_step_out(ctypes.Structure):

@@ -163,6 +163,8 @@ int check_config(const dg_config& c) {
     return fail(DG_ERR_INVALID_ARG, "rope_theta and rms_eps must be >= 0");
   if (c.mask_token < -1 || c.mask_token >= c.vocab)
     return fail(DG_ERR_INVALID_ARG, "mask_token %d must be -1 (uniform noise) or a vocabulary id", c.mask_token);
+  if (c.self_condition != 0 && c.self_condition != 1)
+    return fail(DG_ERR_INVALID_ARG, "self_condition must be 0 or 1");
   return DG_OK;
 }
 
@@ -492,6 +494,8 @@ int lm_head_confidence(dg_model* m, const void* hf, int T, float* H, int* am, fl
 
 int check_canvas(dg_model* m, const dg_canvas* c) {
   if (!c || !c->tokens || !c->committed) return fail(DG_ERR_INVALID_ARG, "null canvas pointer");
+  if (m->cfg.self_condition && !c->prediction)
+    return fail(DG_ERR_INVALID_ARG, "self-conditioning needs the canvas's prediction array");
   if (c->batch <= 0 || c->batch > m->max_batch)
     return fail(DG_ERR_SHAPE, "canvas batch %d outside [1, %d]", c->batch, m->max_batch);
   return DG_OK;
@@ -510,7 +514,9 @@ int check_kv(const dg_model* m, const dg_kv* kv, int batch, int extra) {
 int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* out, hipStream_t st) {
   const dg_config& cfg = m->cfg;
   const int B = c->batch, N = cfg.canvas_len, T = B * N, P = kv->length;
-  HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, cfg.vocab, m->x, m->ctl + 1, st));
+  // self-conditioning: from the second step on, the previous step's predictions join the input
+  const int* cond = cfg.self_condition && c->step > 0 ? c->prediction : nullptr;
+  HIP_OK(embed_gather(m->at, c->tokens, T, m->embed, cfg.d_model, cfg.vocab, m->x, m->ctl + 1, st, cond));
   HIP_OK(rmsnorm(m->at, m->x, T, cfg.d_model, cfg.rms_eps, m->a, st));
   HIP_OK(rope_table(N, cfg.head_dim, P, cfg.rope_theta, m->rope_tab, st));  // canvas positions P..P+N-1
   m->diag_counts = out ? out->expert_counts : nullptr;
@@ -530,6 +536,8 @@ int denoise_step_impl(dg_model* m, dg_canvas* c, const dg_kv* kv, dg_step_out* o
   float* gap = (out && out->top2_gap) ? out->top2_gap : nullptr;
   int s = lm_head_confidence(m, m->a, T, H, am, gap, st);
   if (s) return s;
+  if (cfg.self_condition)  // this step's predictions condition the next
+    HIP_OK(hipMemcpyAsync(c->prediction, am, sizeof(int) * T, hipMemcpyDeviceToDevice, st));
   if (out && out->logits) {
     GemmArgs g;
     g.A = m->a; g.lda = cfg.d_model; g.B = m->lm_head; g.ldb = cfg.d_model; g.M = T; g.N = cfg.vocab;
@@ -1015,9 +1023,11 @@ int dg_mixed_step(dg_model* m, dg_segment* segs, int32_t n_segs, int32_t* status
   rs.n_segs = n;
   rs.start[n] = r;
   for (int i = 0; i < n; ++i) {
-    const int32_t* tok = sg[i].s->kind == DG_SEG_REFINE ? sg[i].s->canvas->tokens : sg[i].s->tokens;
+    const bool ref = sg[i].s->kind == DG_SEG_REFINE;
+    const int32_t* tok = ref ? sg[i].s->canvas->tokens : sg[i].s->tokens;
+    const int32_t* cond = ref && cfg.self_condition && sg[i].s->canvas->step > 0 ? sg[i].s->canvas->prediction : nullptr;
     HIP_OK(embed_gather(m->at, tok, sg[i].s->n, m->embed, cfg.d_model, cfg.vocab,
-                        (char*)m->x + (size_t)sg[i].start * cfg.d_model * m->esz, m->ctl + 1, st));
+                        (char*)m->x + (size_t)sg[i].start * cfg.d_model * m->esz, m->ctl + 1, st, cond));
   }
   HIP_OK(rmsnorm(m->at, m->x, (int)T, cfg.d_model, cfg.rms_eps, m->a, st));
   HIP_OK(rope_table_rows(rs, cfg.head_dim, cfg.rope_theta, m->rope_tab, st));
@@ -1051,6 +1061,8 @@ int dg_mixed_step(dg_model* m, dg_segment* segs, int32_t n_segs, int32_t* status
       HIP_OK(hipMemcpyAsync(g.entropy, m->H + r0, sizeof(float) * cfg.canvas_len, hipMemcpyDeviceToDevice, st));
     if (g.argmax)
       HIP_OK(hipMemcpyAsync(g.argmax, m->am + r0, sizeof(int) * cfg.canvas_len, hipMemcpyDeviceToDevice, st));
+    if (cfg.self_condition)
+      HIP_OK(hipMemcpyAsync(cv->prediction, m->am + r0, sizeof(int) * cfg.canvas_len, hipMemcpyDeviceToDevice, st));
   }
   if (last_ref < 0) HIP_OK(status_publish(m->ctl + 1, m->ctl, st));
   if (status) HIP_OK(hipMemcpyAsync(status, m->ctl, sizeof(int), hipMemcpyDeviceToDevice, st));

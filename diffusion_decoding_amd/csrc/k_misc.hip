@@ -22,17 +22,27 @@ namespace dg {
 namespace {
 
 // A token id outside [0, vocab) reads row 0 instead and raises FLAG_TOKEN, so
-// a bad id from the caller never addresses memory past the table.
-template <typename T>
-__global__ void embed_kernel(const int* tok, int T_, const T* E, int d, int vocab, T* x, int* flags) {
-  const int t = blockIdx.x;
-  int id = tok[t];
+// a bad id from the caller never addresses memory past the table.  With tok2
+// (self-conditioning) the row of tok2[t] is added, in fp32, rounded once.
+__device__ __forceinline__ int embed_id(int id, int vocab, int* flags) {
   if (id < 0 || id >= vocab) {
     if (threadIdx.x == 0 && flags) atomicOr(flags, FLAG_TOKEN);
     id = 0;
   }
-  const long long src = (long long)id * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) x[(long long)t * d + c] = E[src + c];
+  return id;
+}
+template <typename T>
+__global__ void embed_kernel(const int* tok, const int* tok2, int T_, const T* E, int d, int vocab, T* x,
+                             int* flags) {
+  const int t = blockIdx.x;
+  const long long src = (long long)embed_id(tok[t], vocab, flags) * d;
+  if (!tok2) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) x[(long long)t * d + c] = E[src + c];
+    return;
+  }
+  const long long src2 = (long long)embed_id(tok2[t], vocab, flags) * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    x[(long long)t * d + c] = from_f32<T>(to_f32(E[src + c]) + to_f32(E[src2 + c]));
 }
 
 // FLAG_NONFINITE when any lane of the wave holds a non-finite value (one
@@ -433,13 +443,13 @@ __global__ void philox_kernel(uint64_t seed, uint32_t pos0, uint32_t tag, uint32
 }  // namespace
 
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vocab, void* x, int* flags,
-                 hipStream_t st) {
+                 hipStream_t st, const int* tok2) {
   if (T <= 0) return 0;
   if (at == ACT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(T), dim3(256), 0, st, tok, T, (const bf16*)E, d, vocab, (bf16*)x,
-                       flags);
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(T), dim3(256), 0, st, tok, tok2, T, (const bf16*)E, d, vocab,
+                       (bf16*)x, flags);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, st, tok, T, (const float*)E, d, vocab,
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, st, tok, tok2, T, (const float*)E, d, vocab,
                        (float*)x, flags);
   return int(hipGetLastError());
 }

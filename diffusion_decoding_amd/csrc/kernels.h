@@ -138,9 +138,10 @@ constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
 int noalloc_scratch(void** ptr);
 
 // ---------------------------------------------------------------- misc (k_misc.hip)
-// ids outside [0, vocab) read row 0 and raise FLAG_TOKEN in *flags (nullable)
+// ids outside [0, vocab) read row 0 and raise FLAG_TOKEN in *flags (nullable);
+// tok2 (nullable): add the rows of these ids too (one rounding of the sum)
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vocab, void* x, int* flags,
-                 hipStream_t st);
+                 hipStream_t st, const int* tok2 = nullptr);
 int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st);
 // tab[i][j] = (cos, sin) of (pos0 + i) * theta^(-2j/dh), i < n, j < dh/2 (float pairs)
 int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st);

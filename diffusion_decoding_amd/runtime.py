@@ -36,7 +36,8 @@ def make_config(cfg) -> dg_config:
     return dg_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_experts, cfg.top_k,
                      cfg.d_expert, cfg.d_shared, cfg.vocab, cfg.canvas_len, cfg.max_steps,
                      float(cfg.rope_theta), float(cfg.rms_eps), float(cfg.threshold),
-                     _DT[cfg.act_dtype], _DT[cfg.expert_dtype], int(cfg.mask_token))
+                     _DT[cfg.act_dtype], _DT[cfg.expert_dtype], int(cfg.mask_token),
+                     int(getattr(cfg, "self_condition", False)))
 
 
 def pack_experts(w: torch.Tensor, dtype: str, stream=None) -> torch.Tensor:
@@ -103,15 +104,17 @@ class Canvas:
     seed: int
     block: int = 0
     step: int = 0
+    prediction: Optional[torch.Tensor] = None  # int32 [B, N]: previous step's argmax (self-conditioning)
 
     @classmethod
     def empty(cls, batch: int, n: int, seed: int, block: int = 0, device="cuda"):
         return cls(torch.zeros(batch, n, dtype=torch.int32, device=device),
-                   torch.zeros(batch, n, dtype=torch.uint8, device=device), seed, block, 0)
+                   torch.zeros(batch, n, dtype=torch.uint8, device=device), seed, block, 0,
+                   torch.zeros(batch, n, dtype=torch.int32, device=device))
 
     def struct(self) -> dg_canvas:
         return dg_canvas(_ptr(self.tokens), _ptr(self.committed), self.tokens.shape[0], self.step,
-                         self.seed, self.block)
+                         self.seed, self.block, _ptr(self.prediction))
 
 
 @dataclass

@@ -110,6 +110,12 @@ typedef struct dg_config {
                               set back to [MASK] after each step (the masked-diffusion variant
                               the pages contrast it with: DiffusionGemma深度拆解 (zhichai.net),
                               "统一状态扩散 vs 掩码扩散"); nothing else changes */
+  int32_t self_condition;  /* 0 or 1: self-conditioning, one of the techniques the model combines
+                              (openai-hub.com, "为什么扩散能跑得比自回归快"; named only).  Reading:
+                              every step after a canvas's first adds the embedding row of the
+                              previous step's argmax at each position (dg_canvas.prediction) to
+                              the position's input embedding, one sum rounded once to act_dtype;
+                              the first step (step == 0) adds nothing */
 } dg_config;
 
 /* One layer's weights (device pointers, borrowed for the model's lifetime).
@@ -169,6 +175,8 @@ typedef struct dg_canvas {
   int32_t step;        /* host: steps already taken (0-based index of the next step) */
   uint64_t seed;
   uint32_t block;      /* canvas ordinal in block-autoregressive generation */
+  int32_t* prediction; /* [batch][canvas_len] device: with self_condition, each step writes its argmax
+                          here and every later step reads it (required then; unused otherwise) */
 } dg_canvas;
 
 /* Optional per-step outputs (each pointer may be NULL = not written). */

@@ -104,6 +104,10 @@ class Pair:
                 say("   ", rep)
                 reps.append(rep)
                 assert canvas.step == ost.step
+                if getattr(cfg, "self_condition", False):
+                    # the step kept its own argmax for the next step's input
+                    np.testing.assert_array_equal(to_host(canvas.prediction), gpu["argmax"])
+                    canvas.prediction.copy_(torch.from_numpy(ost.prediction.astype(np.int32)))
                 canvas.tokens.copy_(torch.from_numpy(ost.tokens.astype(np.int32)))
                 canvas.committed.copy_(torch.from_numpy(ost.committed.astype(np.uint8)))
                 if int(ores.n_uncommitted.sum()) == 0:

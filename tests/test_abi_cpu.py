@@ -72,7 +72,7 @@ def test_invalid_arguments_are_rejected_before_any_launch():
     assert lib.dg_commit_canvas(None, None, 0, None, None) == -1
 
 
-STRUCTS = ["dg_config", "dg_layer_weights", "dg_weights", "dg_kv", "dg_canvas", "dg_step_out"]
+STRUCTS = ["dg_config", "dg_layer_weights", "dg_weights", "dg_kv", "dg_canvas", "dg_step_out", "dg_segment"]
 
 
 def _c_layout(tmp_path):

@@ -72,6 +72,8 @@ class Request:
         if self.ost is not None:
             self.canvas.tokens.copy_(torch.from_numpy(self.ost.tokens.astype(np.int32)))
             self.canvas.committed.copy_(torch.from_numpy(self.ost.committed.astype(np.uint8)))
+            if self.ost.prediction is not None:
+                self.canvas.prediction.copy_(torch.from_numpy(self.ost.prediction.astype(np.int32)))
 
 
 class Mix:
@@ -138,6 +140,8 @@ class Mix:
                 reps.append(rep)
                 assert req.canvas.step == req.ost.step
                 assert int(to_host(out["n_uncommitted"])[0]) == int((gpu["committed"] == 0).sum())
+                if cfg1.self_condition:
+                    np.testing.assert_array_equal(to_host(req.canvas.prediction), gpu["argmax"])
                 k0, v0 = before[id(req)]
                 assert torch.equal(req.kv.k, k0) and torch.equal(req.kv.v, v0), "a refine pass wrote its cache"
                 assert req.kv.length == req.okv.length
@@ -269,6 +273,22 @@ def test_mixed_beyond_one_routed_launch(rt, act, n_append):
     rng = np.random.default_rng(11)
     reps = mix.run_pass([(r0, None), (a1, rng.integers(0, cfg.vocab, n_append))],
                         1e-5 if act == "fp32" else 1e-2)
+    mix.close()
+    assert_reports(cfg.replace(batch=1), reps)
+
+
+def test_mixed_self_condition(rt):
+    """Refine segments with self-conditioning in a mixed pass: from its second
+    step each canvas's input carries its own previous predictions."""
+    cfg = _tiny_mix(rt, "fp32", name="tiny_mixed_selfcond", self_condition=True)
+    say("mixed batch with self-conditioning, fp32: refine (P=100) | append 30 | refine (P=0), 3 passes")
+    mix = Mix(rt, cfg, max_batch=2, max_tokens=80, kv_capacity=220)
+    r0, a1, r2 = Request(mix, 0, 100, seed=21), Request(mix, 1, 0), Request(mix, 2, 0, seed=22, block=1)
+    rng = np.random.default_rng(13)
+    reps = []
+    for p in range(3):
+        say(f"  pass {p}")
+        reps += mix.run_pass([(r0, None), (a1, rng.integers(0, cfg.vocab, 30)), (r2, None)], 1e-5)
     mix.close()
     assert_reports(cfg.replace(batch=1), reps)
 

@@ -140,6 +140,53 @@ def test_generate_canvas_matches_oracle_c0(rt):
     model.close()
 
 
+# ----------------------------------------------------------------------------- self-conditioning
+
+@pytest.mark.parametrize("act", ["fp32", "bf16"])
+def test_self_condition_step_locked(rt, act):
+    """Self-conditioning: from the second step on, each position's input adds
+    the embedding of the previous step's argmax; step-locked against the
+    oracle, with the GPU's kept predictions checked against its argmax."""
+    cfg = tiny_config(name=f"tiny_selfcond_{act}", act_dtype=act, expert_dtype=act, batch=2, seed=66,
+                      canvas_len=40, max_steps=5, self_condition=True, lm_scale=6.0 if act == "fp32" else 1.0,
+                      head_dim=32, n_heads=2)
+    say(f"self-conditioning, batch 2, {act}")
+    reps = _run_locked(rt, cfg)
+    _assert_reports(cfg, reps)
+
+
+def test_self_condition_generate_canvas_matches_oracle_c0(rt):
+    cfg = get_config("c0").replace(name="c0_selfcond", self_condition=True)
+    say("c0 with self-conditioning: dg_generate_canvas vs oracle loop")
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    rt.canvas_init(model, canvas)
+    steps = rt.generate_canvas(model, canvas, kv)
+    torch.cuda.synchronize()
+    W = om.Weights(inp, cache=True)
+    okv = om.KV(inp.kv_k, inp.kv_v, inp.kv_len, bf16=False)
+    ost, osteps = om.generate_canvas(W, okv, cfg, cfg.seed)
+    plain, _ = om.generate_canvas(W, okv, cfg.replace(self_condition=False), cfg.seed)
+    say(f"   {steps} steps; tokens differing from the unconditioned run: {int((plain.tokens != ost.tokens).sum())}")
+    assert steps == osteps
+    assert to_host(canvas.committed).all()
+    np.testing.assert_array_equal(to_host(canvas.tokens), ost.tokens)
+    np.testing.assert_array_equal(to_host(canvas.prediction), ost.prediction)
+    model.close()
+
+
+def test_self_condition_needs_the_prediction_array(rt):
+    from diffusion_decoding_amd._lib import DGError
+    cfg = get_config("c0").replace(name="c0_selfcond_err", self_condition=True)
+    inp, model, kv = _gpu_setup(rt, cfg)
+    canvas = rt.Canvas.empty(1, cfg.canvas_len, cfg.seed)
+    canvas.prediction = None
+    with pytest.raises(DGError) as e:
+        rt.canvas_init(model, canvas)
+    assert e.value.status == -1 and "prediction" in str(e.value)
+    model.close()
+
+
 # ----------------------------------------------------------------------------- absorbing-state noise
 
 @pytest.mark.parametrize("act", ["fp32", "bf16"])

@@ -193,6 +193,19 @@ def test_c3_shape_one_layer_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_self_condition_full_width_two_steps(rt):
+    """Self-conditioning at full width (the c1 layer shapes, 8192 ids): the
+    second step's input carries the first step's predictions."""
+    cfg = get_config("c1").replace(name="c1_selfcond", self_condition=True, vocab=8192)
+    say("self-conditioning at full width: c1 shape, 1 layer, two steps")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=2)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_batch8_full_width_one_step(rt):
     """Eight canvases (2048 tokens pooled in the experts: two token passes per
     expert in both routed kernels), each with its own 1024-row prompt; a
