@@ -110,7 +110,7 @@ __global__ void counts_kernel(const int* off, int E, int* counts, bool accumulat
 }
 
 constexpr int PERM_THREADS = 1024;
-constexpr int PERM_MAX_TOKENS = 1024;
+constexpr int PERM_MAX_TOKENS = 2048;
 constexpr int PERM_WORDS = PERM_MAX_TOKENS / 64;
 
 // One workgroup.  Each expert gets a bitmask over tokens (bit t set when token

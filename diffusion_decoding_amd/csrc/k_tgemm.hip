@@ -793,6 +793,229 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   return int(hipErrorInvalidValue);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped routed-expert GEMM for many pairs per expert (pooled canvases,
+// mixed passes): a plain grid of (expert, 128-output tile, 128-pair tile)
+// items over the expert-major pair lists, each a 128 x 128 output tile whose
+// operands reach LDS by direct loads.  The expert weights are already tiled
+// in the matrix-core operand layout (16 rows x 32 columns per 1 KB block,
+// lane l's 16 bytes its fragment), so a block is copied to LDS as is and a
+// lane reads its fragment at lane x 16; the pairs' token rows (gathered
+// through pair_row for gate/up, contiguous h rows for down) go to 8-row
+// blocks with the XOR chunk swizzle of the dense kernel.  The weights are the
+// A operand and the tokens the B operand, and every output sums its 32-column
+// k blocks in ascending order, as the weight-stream kernels do, so the two
+// give the same bits.  Gate/up: 128 gate and 128 up weight rows per tile,
+// h = bf16(silu(gate) up); down: 128 weight rows, y fp32.
+//
+// Waves: 8 = 2 token groups of 64 x 4 output groups of 32; a wave holds
+// 4 token blocks x (4 gate/up or 2 down) weight blocks of accumulators.
+// Items are ordered expert, then output tile, then pair tile, so the pair
+// tiles of one expert's weight tile run side by side on one XCD and share it
+// in L2; items past the last one exit at once (the grid is a bound).
+namespace gex {
+constexpr int BM = 128;  // pairs per tile
+constexpr int BN = 128;  // outputs per tile
+constexpr int NWV = 8;
+}  // namespace gex
+
+template <bool GU, int KT, int S>
+__global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __restrict__ X, const int* __restrict__ pair_row,
+                                                                const int* __restrict__ off, int E, const bf16* __restrict__ W,
+                                                                int Nout, void* __restrict__ out, int per_xcd) {
+  using namespace gex;
+  constexpr int K = 64 * KT;
+  constexpr int WB = GU ? 16 : 8;        // 16-row weight blocks per tile
+  constexpr int NWB = WB / 4;            // per wave (GU: 2 gate + 2 up)
+  constexpr int MT = 4;                  // 16-pair blocks per wave
+  constexpr int LA = BM / 8 / NWV;       // token loads per wave per stage (2)
+  constexpr int LB = 2 * WB / NWV;       // weight loads per wave per stage (GU 4, down 2)
+  static_assert(LA * 8 * NWV == BM && LB * NWV == 2 * WB && S >= 2 && S <= 4, "shape");
+#define DG_GX_BUF(X_, R, BYTES, I) __shared__ __attribute__((aligned(1024))) char X_##I[R > I ? BYTES : 1];
+  DG_GX_BUF(TS, S, BM * 128, 0) DG_GX_BUF(TS, S, BM * 128, 1) DG_GX_BUF(TS, S, BM * 128, 2) DG_GX_BUF(TS, S, BM * 128, 3)
+  DG_GX_BUF(WS, S, WB * 2048, 0) DG_GX_BUF(WS, S, WB * 2048, 1) DG_GX_BUF(WS, S, WB * 2048, 2) DG_GX_BUF(WS, S, WB * 2048, 3)
+#undef DG_GX_BUF
+  auto tbuf = [&](auto bc) -> char* {
+    constexpr int b = decltype(bc)::value % S;
+    if constexpr (b == 0) return TS0;
+    else if constexpr (b == 1) return TS1;
+    else if constexpr (b == 2) return TS2;
+    else return TS3;
+  };
+  auto wbuf = [&](auto bc) -> char* {
+    constexpr int b = decltype(bc)::value % S;
+    if constexpr (b == 0) return WS0;
+    else if constexpr (b == 1) return WS1;
+    else if constexpr (b == 2) return WS2;
+    else return WS3;
+  };
+
+  // item -> (expert, output tile, pair tile): wave 0 scans the experts' pair-tile counts
+  __shared__ int sel[4];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return;  // uniform
+  const int item = (blockIdx.x & 7) * per_xcd + slot;
+  const int NT = (Nout + BN - 1) / BN;
+  if (wave == 0) {
+    // lane l owns experts 4l .. 4l+3
+    int c[4], s = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * lane + u;
+      c[u] = e < E ? NT * ((off[e + 1] - off[e] + BM - 1) / BM) : 0;
+      s += c[u];
+    }
+    int incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - s;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (c[u] && item >= run && item < run + c[u]) {
+        sel[0] = 4 * lane + u;
+        sel[1] = item - run;
+      }
+      run += c[u];
+    }
+    if (lane == 63) sel[2] = incl;  // total items
+  }
+  __syncthreads();
+  if (item >= sel[2]) return;  // uniform: past the last item
+  const int e = sel[0], j = sel[1];
+  const int pbeg = off[e], cnt = off[e + 1] - pbeg;
+  const int mtiles = (cnt + BM - 1) / BM;
+  const int nt = j / mtiles, m0 = (j - nt * mtiles) * BM, n0 = nt * BN;
+
+  // token row of this lane's loads: block q = wave + NWV i holds pair rows 8q .. 8q+7
+  const int rr8 = lane >> 3, ch = (lane & 7) ^ rr8;
+  const bf16* tsrc[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int r = min(m0 + 8 * (wave + NWV * i) + rr8, cnt - 1);  // past the pairs: the last pair's row
+    const long long row = GU ? (long long)pair_row[pbeg + r] : (long long)(pbeg + r);
+    tsrc[i] = X + row * K + 8 * ch;
+  }
+  // weight load l of this wave: tile block b = (wave LB + l) / 2, k half (wave LB + l) % 2;
+  // block b < 8 holds rows n0 + 16 b (gate for GU), b >= 8 the up rows Nout + n0 + 16 (b - 8)
+  const long long wrows = GU ? 2LL * Nout : Nout;
+  const char* wexp = (const char*)(W + (long long)e * wrows * K);
+  const char* wsrc[LB];
+  int wdst[LB];
+#pragma unroll
+  for (int l = 0; l < LB; ++l) {
+    const int q = wave * LB + l, b = q >> 1, hf = q & 1;
+    const int nb = min(n0 + 16 * (b & 7), ((Nout - 1) >> 4) << 4);  // past Nout: the last block
+    const long long rb = (GU && b >= 8 ? Nout + nb : nb) >> 4;
+    wsrc[l] = wexp + (rb * (K / 32) + hf) * 1024 + lane * 16;
+    wdst[l] = (b * 2 + hf) * 1024;
+  }
+  auto issue_t = [&](int kt, char* bufp) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(tsrc[i] + kt * 64), (dl::lds_ptr)(bufp + (wave + NWV * i) * 1024),
+                                       16, 0, 0);
+  };
+  auto issue_w = [&](int kt, char* bufp) {
+#pragma unroll
+    for (int l = 0; l < LB; ++l)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[l] + kt * 2048), (dl::lds_ptr)(bufp + wdst[l]), 16, 0, 0);
+  };
+
+  const int c16 = lane & 15, g4 = lane >> 4, rr = lane & 7;
+  const int tg = wave >> 2, og = wave & 3;
+  f32x4 acc[NWB][MT];
+#pragma unroll
+  for (int w = 0; w < NWB; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // wave's weight blocks: GU gate 2 og, 2 og + 1, up 8 + 2 og, 8 + 2 og + 1; down 2 og, 2 og + 1
+  auto wblk = [&](int w) { return GU ? (w < 2 ? 2 * og + w : 8 + 2 * og + (w - 2)) : 2 * og + w; };
+  auto compute = [&](const char* tb, const char* wb) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4 wf[NWB], tf[MT];
+#pragma unroll
+      for (int w = 0; w < NWB; ++w) wf[w] = *(const u32x4*)(wb + (wblk(w) * 2 + hf) * 1024 + lane * 16);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int r0 = 64 * tg + 16 * t;
+        tf[t] = *(const u32x4*)(tb + 2 * (((r0 >> 3) + (c16 >> 3)) * 512 + (rr * 8 + ((4 * hf + g4) ^ rr)) * 8));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int w = 0; w < NWB; ++w)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[w][t] = mfma16x16x32(wf[w], tf[t], acc[w][t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  dl::static_for<S - 1>([&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+    if constexpr (st < KT) {
+      issue_t(st, tbuf(sc));
+      issue_w(st, wbuf(sc));
+    }
+  });
+  dl::static_for<KT>([&](auto kc) {
+    constexpr int kt = decltype(kc)::value;
+    dl::wait_barrier<dl::loads_after<S, S, KT, LA, LB>(kt)>();
+    if constexpr (kt + S - 1 < KT) {
+      issue_t(kt + S - 1, tbuf(std::integral_constant<int, kt + S - 1>{}));
+      issue_w(kt + S - 1, wbuf(std::integral_constant<int, kt + S - 1>{}));
+    }
+    compute(tbuf(kc), wbuf(kc));
+  });
+
+  // epilogue: lane holds pair 64 tg + 16 t + c16 and outputs nb .. nb + 3 of block b
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int nb = n0 + 32 * og + 16 * b + 4 * g4;
+    if (nb >= Nout) continue;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int r = m0 + 64 * tg + 16 * t + c16;
+      if (r >= cnt) continue;
+      const long long p = pbeg + r;
+      if constexpr (GU) {
+        bf16 hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float gt = acc[b][t][q], up = acc[2 + b][t][q];
+          hv[q] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
+        }
+        bf16* h = (bf16*)out + p * Nout + nb;
+        if (nb + 3 < Nout) {
+          *(u32x2*)h = u32x2{uint32_t(hv[0].v) | (uint32_t(hv[1].v) << 16), uint32_t(hv[2].v) | (uint32_t(hv[3].v) << 16)};
+        } else {
+          for (int q = 0; q < 4 && nb + q < Nout; ++q) h[q] = hv[q];
+        }
+      } else {
+        float* y = (float*)out + p * Nout + nb;
+        if (nb + 3 < Nout) *(f32x4*)y = acc[b][t];
+        else
+          for (int q = 0; q < 4 && nb + q < Nout; ++q) y[q] = acc[b][t][q];
+      }
+    }
+  }
+}
+
+template <bool GU, int KT, int S>
+int launch_grouped(const bf16* X, const int* pair_row, const int* off, int E, int pairs, const bf16* W, int Nout,
+                   void* out, hipStream_t st) {
+  using namespace gex;
+  const int NT = (Nout + BN - 1) / BN;
+  const long long items = (long long)NT * ((pairs + BM - 1) / BM + E);  // a bound on the items
+  const int per_xcd = int((items + 7) / 8);
+  hipLaunchKernelGGL((grouped_kernel<GU, KT, S>), dim3(8 * per_xcd), dim3(64 * NWV), 0, st, X, pair_row, off, E, W,
+                     Nout, out, per_xcd);
+  return int(hipGetLastError());
+}
+
 }  // namespace
 
 int lm_tiles_tiled(int vocab, int K) {
@@ -801,6 +1024,17 @@ int lm_tiles_tiled(int vocab, int K) {
 }
 
 bool tgemm_supported(ActType at, int K) { return at == ACT_BF16 && K % SK_MIN == 0; }
+
+bool grouped_supported(bool gate_up, int K, int Nout, int E) {
+  return E <= 256 && Nout % 16 == 0 && (gate_up ? K == 2048 : K == 704);
+}
+
+int grouped_experts(bool gate_up, const void* X, const int* pair_row, const int* off, int E, int pairs,
+                    const void* W, int K, int Nout, void* out, hipStream_t st) {
+  if (!grouped_supported(gate_up, K, Nout, E) || pairs <= 0) return int(hipErrorInvalidValue);
+  if (gate_up) return launch_grouped<true, 32, 3>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+  return launch_grouped<false, 11, 4>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+}
 
 int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   if (g.K % SK_MIN || g.g_off) return int(hipErrorInvalidValue);

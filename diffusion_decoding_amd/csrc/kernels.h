@@ -63,6 +63,14 @@ struct GemmArgs {
 
 // Returns 0 or a HIP error code.
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st);
+// Routed experts with bf16 weights in the tiled layout, as grouped 128 x 128
+// tiles over expert-major pair lists (off [E+1], pair_row [pairs]):
+// gate/up (X = normed rows [T][K], gathered by pair_row) -> h [pairs][Nout]
+// bf16 SwiGLU; down (X = h [pairs][K], one row per pair) -> y [pairs][Nout]
+// fp32.  Same bits as moe_experts.  Shapes: grouped_supported.
+bool grouped_supported(bool gate_up, int K, int Nout, int E);
+int grouped_experts(bool gate_up, const void* X, const int* pair_row, const int* off, int E, int pairs,
+                    const void* W, int K, int Nout, void* out, hipStream_t st);
 // Number of vocab tiles the LM epilogue writes per row (depends on the kernel
 // gemm() routes the LM head to).
 int lm_tiles(ActType at, int K, int vocab);

@@ -254,23 +254,27 @@ def _oracle_ids(u, b):
     return ids
 
 
-@pytest.mark.parametrize("T", [256, 1024])
+@pytest.mark.parametrize("T", [256, 1024, 2048])
 def test_moe_unit_bf16(rt, unit_bf16, T):
     """256 rows: about 16 pairs per expert, one pass each; 1024 rows (four
-    canvases pooled): about 64 pairs per expert, the pooled 96-token passes."""
+    canvases pooled): about 64 pairs per expert, the pooled 96-token passes;
+    2048 rows: about 128 pairs per expert, the grouped gate/up (128-pair
+    tiles, an expert over one or two of them)."""
     say(f"routed experts unit (bf16): {T} rows, routing from the oracle's router")
     b = _normed_rows(500 + T, T, unit_bf16.cfg.d_model)
     _moe_case(rt, unit_bf16, b, _oracle_ids(unit_bf16, b))
 
 
-def test_moe_unit_bf16_skewed(rt, unit_bf16):
-    """Every one of 256 rows routed to the same 8 experts (as when every open
-    position holds the same token): 256 pairs on each, so each expert runs
-    eight 32-token passes, the third and later spread over the grid."""
-    say("routed experts unit (bf16): 256 rows all on experts 3, 10, .., 52")
+@pytest.mark.parametrize("T", [256, 1536])
+def test_moe_unit_bf16_skewed(rt, unit_bf16, T):
+    """Every row routed to the same 8 experts (as when every open position
+    holds the same token).  256 rows: 256 pairs on each, eight 32-token
+    passes, the third and later spread over the grid; 1536 rows: the grouped
+    gate/up, twelve 128-pair tiles on each of the 8 experts, none on the rest."""
+    say(f"routed experts unit (bf16): {T} rows all on experts 3, 10, .., 52")
     cfg = unit_bf16.cfg
-    b = _normed_rows(600, 256, cfg.d_model)
-    ids = np.tile(np.array([3 + 7 * j for j in range(cfg.top_k)]), (256, 1))
+    b = _normed_rows(600, T, cfg.d_model)
+    ids = np.tile(np.array([3 + 7 * j for j in range(cfg.top_k)]), (T, 1))
     _moe_case(rt, unit_bf16, b, ids)
 
 
