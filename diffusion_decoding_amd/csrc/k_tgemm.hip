@@ -808,18 +808,20 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
 // give the same bits.  Gate/up: 128 gate and 128 up weight rows per tile,
 // h = bf16(silu(gate) up); down: 128 weight rows, y fp32.
 //
-// Waves: 8 = 2 token groups of 64 x 4 output groups of 32; a wave holds
-// 4 token blocks x (4 gate/up or 2 down) weight blocks of accumulators.
+// Waves: 8 = 2 token groups of BM / 2 x 4 output groups of 32; a wave holds
+// BM / 32 token blocks x (4 gate/up or 2 down) weight blocks of accumulators.
+// BM = 128 with a 3-stage ring measured fastest (64-pair tiles tied at 64
+// pairs per expert and lost at 128: 246 against 220 us).
 // Items are ordered expert, then output tile, then pair tile, so the pair
 // tiles of one expert's weight tile run side by side on one XCD and share it
 // in L2; items past the last one exit at once (the grid is a bound).
 namespace gex {
-constexpr int BM = 128;  // pairs per tile
 constexpr int BN = 128;  // outputs per tile
 constexpr int NWV = 8;
 }  // namespace gex
 
-template <bool GU, int KT, int S>
+// BM: pairs per tile (64 or 128)
+template <bool GU, int KT, int S, int BM>
 __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __restrict__ X, const int* __restrict__ pair_row,
                                                                 const int* __restrict__ off, int E, const bf16* __restrict__ W,
                                                                 int Nout, void* __restrict__ out, int per_xcd) {
@@ -827,8 +829,8 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
   constexpr int K = 64 * KT;
   constexpr int WB = GU ? 16 : 8;        // 16-row weight blocks per tile
   constexpr int NWB = WB / 4;            // per wave (GU: 2 gate + 2 up)
-  constexpr int MT = 4;                  // 16-pair blocks per wave
-  constexpr int LA = BM / 8 / NWV;       // token loads per wave per stage (2)
+  constexpr int MT = BM / 32;            // 16-pair blocks per wave (2 token groups)
+  constexpr int LA = BM / 8 / NWV;       // token loads per wave per stage
   constexpr int LB = 2 * WB / NWV;       // weight loads per wave per stage (GU 4, down 2)
   static_assert(LA * 8 * NWV == BM && LB * NWV == 2 * WB && S >= 2 && S <= 4, "shape");
 #define DG_GX_BUF(X_, R, BYTES, I) __shared__ __attribute__((aligned(1024))) char X_##I[R > I ? BYTES : 1];
@@ -942,7 +944,7 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
       for (int w = 0; w < NWB; ++w) wf[w] = *(const u32x4*)(wb + (wblk(w) * 2 + hf) * 1024 + lane * 16);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const int r0 = 64 * tg + 16 * t;
+        const int r0 = (BM / 2) * tg + 16 * t;
         tf[t] = *(const u32x4*)(tb + 2 * (((r0 >> 3) + (c16 >> 3)) * 512 + (rr * 8 + ((4 * hf + g4) ^ rr)) * 8));
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -978,7 +980,7 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
     if (nb >= Nout) continue;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const int r = m0 + 64 * tg + 16 * t + c16;
+      const int r = m0 + (BM / 2) * tg + 16 * t + c16;
       if (r >= cnt) continue;
       const long long p = pbeg + r;
       if constexpr (GU) {
@@ -1004,14 +1006,14 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
   }
 }
 
-template <bool GU, int KT, int S>
+template <bool GU, int KT, int S, int BM>
 int launch_grouped(const bf16* X, const int* pair_row, const int* off, int E, int pairs, const bf16* W, int Nout,
                    void* out, hipStream_t st) {
   using namespace gex;
   const int NT = (Nout + BN - 1) / BN;
   const long long items = (long long)NT * ((pairs + BM - 1) / BM + E);  // a bound on the items
   const int per_xcd = int((items + 7) / 8);
-  hipLaunchKernelGGL((grouped_kernel<GU, KT, S>), dim3(8 * per_xcd), dim3(64 * NWV), 0, st, X, pair_row, off, E, W,
+  hipLaunchKernelGGL((grouped_kernel<GU, KT, S, BM>), dim3(8 * per_xcd), dim3(64 * NWV), 0, st, X, pair_row, off, E, W,
                      Nout, out, per_xcd);
   return int(hipGetLastError());
 }
@@ -1032,8 +1034,8 @@ bool grouped_supported(bool gate_up, int K, int Nout, int E) {
 int grouped_experts(bool gate_up, const void* X, const int* pair_row, const int* off, int E, int pairs,
                     const void* W, int K, int Nout, void* out, hipStream_t st) {
   if (!grouped_supported(gate_up, K, Nout, E) || pairs <= 0) return int(hipErrorInvalidValue);
-  if (gate_up) return launch_grouped<true, 32, 3>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
-  return launch_grouped<false, 11, 4>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+  if (gate_up) return launch_grouped<true, 32, 3, 128>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+  return launch_grouped<false, 11, 4, 128>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
 }
 
 int tgemm(WType wt, GemmEpi epi, const GemmArgs& g, hipStream_t st) {
