@@ -386,6 +386,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the batch-4 (c3), batch-8 (c5), fill-in-the-middle, block-autoregressive "
                          "fp8 (c4), MXFP4 (c6), self-conditioning and mixed-phase measurements")
+    ap.add_argument("--mixed", action="store_true",
+                    help="only the mixed-phase serving pass at the c2 shapes (its own JSON line; for profiling)")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the per-kernel-class roofline table (one extra canvas per class after "
                          "the timed region)")
@@ -393,7 +395,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        msg = ("bench.py runs on exactly one GPU: the library has no multi-GPU path "
                f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).")
         print(msg, file=sys.stderr, flush=True)
         sys.exit(2)
@@ -416,6 +418,9 @@ def main():
 
     cfg = get_config(args.config)
     torch.cuda.set_device(0)
+    if args.mixed:
+        print(json.dumps({"mixed": time_mixed(get_config("c2"), passes=args.steps, warmup=args.warmup)}), flush=True)
+        return
     if cfg.prompt_mode != "kv":
         # block-autoregressive workloads (c4): prompt encode + canvases with their commit passes
         res = time_block_ar(cfg, warmup=args.warmup)

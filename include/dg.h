@@ -44,8 +44,9 @@
  *
  * Layouts (row-major, innermost dimension last; T = batch * tokens):
  *  - activations/weights in `act_dtype` (FP32 or BF16); routed and shared
- *    expert weights in `expert_dtype` (FP32, BF16, or FP8_E4M3 codes with one
- *    fp32 scale per output row: w = decode(code) * scale[row]).
+ *    expert weights in `expert_dtype` (FP32, BF16, FP8_E4M3 codes with one
+ *    fp32 scale per output row: w = decode(code) * scale[row], or MXFP4 for the
+ *    routed experts with E8M0 block scales and a BF16 shared expert).
  *  - weight matrices are [out][in]: y = W x.
  *  - KV cache: k and v are each [n_layers][batch][n_heads][capacity][head_dim]
  *    in act_dtype, holding rotary-embedded keys and the values.
