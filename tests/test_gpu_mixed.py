@@ -293,6 +293,47 @@ def test_mixed_self_condition(rt):
     assert_reports(cfg.replace(batch=1), reps)
 
 
+def test_mixed_sixteen_segments(rt):
+    """The most segments a pass takes: four refine canvases and twelve appends
+    of ragged lengths (1 to 64 tokens, some into empty caches), two passes."""
+    cfg = _tiny_mix(rt, "fp32", name="tiny_mixed_16", batch=16, n_layers=1)
+    say("mixed batch, 16 segments (4 refine + 12 appends of 1..64 tokens), fp32")
+    mix = Mix(rt, cfg, max_batch=4, max_tokens=200, kv_capacity=100 + 2 * 64)
+    refs = [Request(mix, i, 100 if i % 2 else 0, seed=30 + i, block=i) for i in range(4)]
+    lens = [1, 3, 64, 17, 2, 40, 1, 33, 8, 64, 5, 11]
+    apps = [Request(mix, 4 + i, (i * 13) % 100) for i in range(12)]
+    rng = np.random.default_rng(17)
+    reps = []
+    for p in range(2):
+        say(f"  pass {p}")
+        plan = []
+        for i in range(12):
+            plan.append((apps[i], rng.integers(0, cfg.vocab, lens[(i + p) % 12])))
+            if i % 3 == 2:
+                plan.append((refs[i // 3], None))
+        reps += mix.run_pass(plan, 1e-5)
+    mix.close()
+    assert_reports(cfg.replace(batch=1), reps)
+
+
+@pytest.mark.parametrize("edt", ["fp8", "mxfp4"])
+def test_mixed_low_precision_experts(rt, edt):
+    """Mixed passes with fp8 (routed and shared) and MXFP4 (routed) experts:
+    a prompt read, a refine canvas and a canvas commit, two passes."""
+    cfg = _tiny_mix(rt, "bf16", name=f"tiny_mixed_{edt}", expert_dtype=edt, d_expert=64, batch=3)
+    say(f"mixed batch, {edt} experts: append 48 | refine (P=100) | append 40 (P=60)")
+    mix = Mix(rt, cfg, max_batch=1, max_tokens=140, kv_capacity=100 + 2 * 48 + 40)
+    a0, r1, a2 = Request(mix, 0, 0), Request(mix, 1, 100, seed=19), Request(mix, 2, 60)
+    rng = np.random.default_rng(23)
+    reps = []
+    for p in range(2):
+        say(f"  pass {p}")
+        plan = [(a0, rng.integers(0, cfg.vocab, 48)), (r1, None), (a2, rng.integers(0, cfg.vocab, 40))]
+        reps += mix.run_pass(plan, 1e-2)
+    mix.close()
+    assert_reports(cfg.replace(batch=1), reps)
+
+
 def test_mixed_rejects_bad_segments(rt):
     """Validation happens before anything is enqueued; caller state is left as it was."""
     from diffusion_decoding_amd._lib import DGError

@@ -155,6 +155,17 @@ def test_self_condition_step_locked(rt, act):
     _assert_reports(cfg, reps)
 
 
+def test_self_condition_with_absorbing_noise_step_locked(rt):
+    """Both options at once: all-[MASK] start and re-masking, and each step's
+    input carrying the previous step's predictions."""
+    cfg = tiny_config(name="tiny_selfcond_absorbing", act_dtype="bf16", expert_dtype="bf16", batch=2, seed=67,
+                      canvas_len=40, max_steps=5, self_condition=True, mask_token=5, lm_scale=1.0,
+                      head_dim=32, n_heads=2)
+    say("self-conditioning with absorbing-state noise, batch 2, bf16")
+    reps = _run_locked(rt, cfg)
+    _assert_reports(cfg, reps)
+
+
 def test_self_condition_generate_canvas_matches_oracle_c0(rt):
     cfg = get_config("c0").replace(name="c0_selfcond", self_condition=True)
     say("c0 with self-conditioning: dg_generate_canvas vs oracle loop")
