@@ -204,8 +204,8 @@ int qkv_rope(dg_model* m, int l, const void* a, int B, int n, void* q_out, void*
 // bidirectional over cache rows [0, P) of `layer` plus the canvas keys and
 // values kc / vc [B][H][n][dh]; causal (kc null): over cache rows [0, P + n)
 // with query i seeing rows j <= P + i.
-int attend(dg_model* m, int l, const void* q, const dg_kv* kv, int P, const void* kc, const void* vc, int B, int n,
-           void* o, hipStream_t st, long long plane = 0) {
+AttnArgs attn_args(const dg_model* m, int l, const void* q, const dg_kv* kv, int P, const void* kc, const void* vc,
+                   int B, int n, void* o, long long plane) {
   const dg_config& c = m->cfg;
   const int H = c.n_heads, dh = c.head_dim;
   const long long cap = kv->capacity;
@@ -228,7 +228,12 @@ int attend(dg_model* m, int l, const void* q, const dg_kv* kv, int P, const void
     aa.causal_base = P;
   }
   aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1, dh));
-  HIP_OK(attention(m->at, aa, st));
+  return aa;
+}
+
+int attend(dg_model* m, int l, const void* q, const dg_kv* kv, int P, const void* kc, const void* vc, int B, int n,
+           void* o, hipStream_t st, long long plane = 0) {
+  HIP_OK(attention(m->at, attn_args(m, l, q, kv, P, kc, vc, B, n, o, plane), st));
   return DG_OK;
 }
 
@@ -453,18 +458,22 @@ int mixed_layer(dg_model* m, int l, const MixedSeg* sg, int n_segs, int T, int T
                         (char*)kv->k + l * lay, (char*)kv->v + l * lay, cap * dh, sg[i].P, st));
   }
   {
+    // bf16: every segment's attention in one launch (and one merge); fp32:
+    // one launch per segment
     ProfScope ps(m, DG_PROF_ATTN, st);
+    static_assert(MAX_SEGMENTS <= ATTN_MAX_SEGS, "one attention launch per pass");
+    AttnArgs aa[MAX_SEGMENTS];
     for (int i = 0; i < n_segs; ++i) {
       const int r0 = sg[i].start, n = sg[i].s->n;
       const char* q = (const char*)m->q + (size_t)r0 * dh * m->esz;
       char* o = (char*)m->o + (size_t)r0 * A * m->esz;
-      if (sg[i].s->kind == DG_SEG_REFINE)
-        s = attend(m, l, q, sg[i].s->kv, sg[i].P, (const char*)m->kc + (size_t)r0 * dh * m->esz,
-                   (const char*)m->vc + (size_t)r0 * dh * m->esz, 1, n, o, st, plane);
-      else
-        s = attend(m, l, q, sg[i].s->kv, sg[i].P, nullptr, nullptr, 1, n, o, st, plane);
-      if (s) return s;
+      const bool refine = sg[i].s->kind == DG_SEG_REFINE;
+      aa[i] = attn_args(m, l, q, sg[i].s->kv, sg[i].P, refine ? (const char*)m->kc + (size_t)r0 * dh * m->esz : nullptr,
+                        refine ? (const char*)m->vc + (size_t)r0 * dh * m->esz : nullptr, 1, n, o, plane);
+      if (m->at != ACT_BF16) HIP_OK(attention(m->at, aa[i], st));
     }
+    if (m->at == ACT_BF16)
+      HIP_OK(attention_segments(m->at, aa, n_segs, m->attn_max_splits, m->attn_po, m->attn_ml, st));
   }
   {
     GemmArgs g;  // O-projection + residual

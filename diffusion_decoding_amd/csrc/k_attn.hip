@@ -13,6 +13,7 @@
 // P*V MFMA straight from the accumulator registers as its B operand
 // (O^T = V^T P^T).  Key ranges are split across workgroups when the head/query
 // grid alone cannot fill the chip; a merge kernel combines the partials.
+#include <algorithm>
 #include <type_traits>
 
 #include "dg_common.h"
@@ -225,8 +226,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int keys_per_spli
 // (O, running max, running sum) and a second kernel merges them in split
 // order.
 template <int DH, int D, bool SEG, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a, int keys_per_split, int n_qt,
-                                                        int per_xcd) {
+__device__ __forceinline__ void attn_bf16_item(const AttnArgs& a, int item, int keys_per_split, int n_qt) {
   // K row pitch: an odd multiple of 32 B keeps the 16-row x 64-byte fragment
   // reads at full LDS rate.  V^T row pitch 72 elements (36 dwords): the
   // 16-byte fragment reads of 16 rows land on 16 distinct 4-bank groups, and
@@ -249,9 +249,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * LDKS];
   __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * LDV];
 
-  const int total_items = a.B * a.H * a.splits * n_qt;
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if ((int)(blockIdx.x >> 3) >= per_xcd || item >= total_items) return;  // uniform
   const int qt = item % n_qt;
   const int z = (item / n_qt) % a.splits;
   const int bh = item / (n_qt * a.splits);
@@ -524,13 +521,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// One attention problem per launch: work items by XCD as above.
+template <int DH, int D, bool SEG, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(
+    AttnArgs a, int keys_per_split, int n_qt, int per_xcd) {
+  const int total_items = a.B * a.H * a.splits * n_qt;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || item >= total_items) return;  // uniform
+  attn_bf16_item<DH, D, SEG, NW>(a, item, keys_per_split, n_qt);
+}
+
+// Several problems in one launch (the requests of a mixed batch, each with
+// its own queries, cache, mode and key splits): their work items are
+// numbered one problem after another, so an XCD's contiguous run of items
+// still covers query tiles and splits of the same problem.
+struct AttnTable {
+  AttnArgs seg[ATTN_MAX_SEGS];
+  int item0[ATTN_MAX_SEGS + 1];  // first work item of each problem; item0[n] = all items
+  int kps[ATTN_MAX_SEGS];        // keys per split
+  int n_qt[ATTN_MAX_SEGS];       // query tiles
+  int blk0[ATTN_MAX_SEGS + 1];   // first merge workgroup of each problem (none with one split)
+  int n;
+};
+
+template <int DH, int D, bool SEG, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_segs_kernel(
+    AttnTable t, int per_xcd) {
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || item >= t.item0[t.n]) return;  // uniform
+  int i = 0;
+  while (i + 1 < t.n && item >= t.item0[i + 1]) ++i;  // uniform; problems with no items are passed over
+  attn_bf16_item<DH, D, SEG, NW>(t.seg[i], item - t.item0[i], t.kps[i], t.n_qt[i]);
+}
+
 // one thread per (b, h, query, 4 dims): combine the S split partials in split
 // order.  Partial maxima are in the log2 domain of the bf16 kernel.  S is a
 // compile-time count, so every partial's loads are issued before the first is
 // used.
 template <int S>
-__global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void merge_bf16_item(const AttnArgs& a, long long e) {
   const int q4 = a.dh / 4;
   const long long BH = (long long)a.B * a.H;
   if (e >= BH * a.n * q4) return;
@@ -562,6 +591,28 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
   const int b = bh / a.H, h = bh % a.H;
   bf16* out = (bf16*)a.out + ((long long)(b * a.n + i) * a.H + h) * a.dh + d0;
   *(u32x2*)out = u32x2{pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv)};
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void attn_merge_bf16(AttnArgs a) {
+  merge_bf16_item<S>(a, (long long)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// the merges of every problem of a table with more than one split, one
+// launch; each workgroup belongs to one problem
+__global__ __launch_bounds__(256) void attn_merge_bf16_segs(AttnTable t) {
+  const int blk = blockIdx.x;
+  int i = 0;
+  while (i + 1 < t.n && blk >= t.blk0[i + 1]) ++i;  // uniform
+  const AttnArgs& a = t.seg[i];
+  const long long e = (long long)(blk - t.blk0[i]) * 256 + threadIdx.x;
+  switch (a.splits) {
+    case 2: merge_bf16_item<2>(a, e); break;
+    case 4: merge_bf16_item<4>(a, e); break;
+    case 8: merge_bf16_item<8>(a, e); break;
+    case 16: merge_bf16_item<16>(a, e); break;
+    default: break;
+  }
 }
 
 // one thread per (b, h, query, d): combine the split partials in split order
@@ -660,6 +711,81 @@ int attn_splits_for(int B, int H, int n, int keys, int dh) {
   int s = 1;
   while (s < 16 && wgs * s * nw < 2048 && keys / (s * 2) >= 512) s *= 2;
   return s;
+}
+
+// Several problems in one launch (bf16).  Key splits: every problem starts
+// at one and all double together, as for a single problem, while the whole
+// grid is under 2048 waves and the problem keeps at least 512 keys per split
+// (at most max_splits).  Four-wave tiles throughout.  Partials are packed one
+// problem after another from part_o / part_ml (at most max_splits x the
+// problems' rows, as for one problem of all the rows).
+int attention_segments(ActType at, AttnArgs* segs, int n, int max_splits, float* part_o, float* part_ml,
+                       hipStream_t st) {
+  if (at != ACT_BF16 || n <= 0 || n > ATTN_MAX_SEGS) return int(hipErrorInvalidValue);
+  const int dh = segs[0].dh;
+  if (dh != 32 && dh != 64 && dh != 128) return int(hipErrorInvalidValue);
+  constexpr int NW = 4;
+  AttnTable t{};
+  t.n = n;
+  int wgs[ATTN_MAX_SEGS], keys[ATTN_MAX_SEGS];
+  bool seg_tiles = true;  // no key tile of any problem spans its two key segments
+  for (int i = 0; i < n; ++i) {
+    AttnArgs& a = segs[i];
+    if (a.dh != dh || a.n < 0 || a.q_bh < (long long)a.n * a.dh) return int(hipErrorInvalidValue);
+    keys[i] = a.len0 + a.len1;
+    t.n_qt[i] = (a.n + 16 * NW - 1) / (16 * NW);
+    wgs[i] = a.n > 0 ? t.n_qt[i] * a.B * a.H : 0;
+    a.splits = 1;
+    seg_tiles = seg_tiles && (a.len1 == 0 || a.len0 % 64 == 0);
+  }
+  for (;;) {
+    long long waves = 0;
+    for (int i = 0; i < n; ++i) waves += (long long)wgs[i] * segs[i].splits * NW;
+    if (waves >= 2048) break;
+    bool grew = false;
+    for (int i = 0; i < n; ++i)
+      if (wgs[i] && segs[i].splits < std::min(16, max_splits) && keys[i] / (segs[i].splits * 2) >= 512) {
+        segs[i].splits *= 2;
+        grew = true;
+      }
+    if (!grew) break;
+  }
+  long long po = 0, ml = 0;
+  t.item0[0] = t.blk0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    AttnArgs& a = segs[i];
+    a.part_o = part_o + po;
+    a.part_ml = part_ml + ml;
+    const long long rows = (long long)a.B * a.H * a.n;
+    if (a.splits > 1) {
+      po += a.splits * rows * dh;
+      ml += a.splits * rows * 2;
+    }
+    t.seg[i] = a;
+    t.kps[i] = ((keys[i] + a.splits - 1) / a.splits + 63) / 64 * 64;
+    t.item0[i + 1] = t.item0[i] + wgs[i] * a.splits;
+    t.blk0[i + 1] = t.blk0[i] + (a.splits > 1 ? int((rows * (dh / 4) + 255) / 256) : 0);
+  }
+  if (t.item0[n] == 0) return 0;
+  const int per_xcd = (t.item0[n] + 7) / 8;
+  const dim3 grid(8 * per_xcd), block(64 * NW);
+#define DG_ATTN_SEGS(DH_)                                                                    \
+  if (seg_tiles)                                                                            \
+    hipLaunchKernelGGL((attn_bf16_segs_kernel<DH_, 1, true, NW>), grid, block, 0, st, t, per_xcd);  \
+  else                                                                                      \
+    hipLaunchKernelGGL((attn_bf16_segs_kernel<DH_, 1, false, NW>), grid, block, 0, st, t, per_xcd);
+  if (dh == 128) {
+    DG_ATTN_SEGS(128)
+  } else if (dh == 64) {
+    DG_ATTN_SEGS(64)
+  } else {
+    DG_ATTN_SEGS(32)
+  }
+#undef DG_ATTN_SEGS
+  int e = int(hipGetLastError());
+  if (e || t.blk0[n] == 0) return e;
+  hipLaunchKernelGGL(attn_merge_bf16_segs, dim3(t.blk0[n]), dim3(256), 0, st, t);
+  return int(hipGetLastError());
 }
 
 int attention(ActType at, const AttnArgs& a, hipStream_t st) {

@@ -135,6 +135,12 @@ struct AttnArgs {
 };
 int attention(ActType at, const AttnArgs& a, hipStream_t st);
 int attn_splits_for(int B, int H, int n, int keys, int dh);
+// Up to ATTN_MAX_SEGS problems (same head_dim) in one launch plus one merge
+// launch, bf16 only.  Sets each problem's splits and partial pointers
+// (packed from part_o / part_ml; room for max_splits x all their rows).
+constexpr int ATTN_MAX_SEGS = 16;
+int attention_segments(ActType at, AttnArgs* segs, int n, int max_splits, float* part_o, float* part_ml,
+                       hipStream_t st);
 
 // ---------------------------------------------------------------- static scratch (k_scratch.hip)
 // Bytes of the file-scope device array the allocation-free LM-head entry
