@@ -13,6 +13,9 @@
 // P*V MFMA straight from the accumulator registers as its B operand
 // (O^T = V^T P^T).  Key ranges are split across workgroups when the head/query
 // grid alone cannot fill the chip; a merge kernel combines the partials.
+// Long key ranges (batched canvases over long prompts) take a second bf16
+// kernel with 32-query waves on the 32x32x16 MFMA and 256-query workgroups,
+// which stage each K/V tile once for four times the queries.
 #include <algorithm>
 #include <type_traits>
 
@@ -521,6 +524,284 @@ __device__ __forceinline__ void attn_bf16_item(const AttnArgs& a, int item, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path with 32-query waves (head_dim 64 or 128).  The same work items
+// (query tiles of 128, key splits, XCD order) and key tiles as above, but
+// each of the four waves holds 32 queries and computes with the 32x32x16
+// MFMA: S^T (32 keys x 32 queries per block) = K Q^T, O^T (32 dims x 32
+// queries per block) = V^T P^T.  A K or V fragment read from LDS then feeds
+// 32 queries instead of 16: four waves cover 128 queries with half the LDS
+// reads per query of eight 16-query waves, and a workgroup's 72 KB of LDS
+// lets two of them share a CU, where their phases (fragment reads, MFMAs,
+// softmax) are not tied together by barriers.
+//
+// Layouts of the 32x32x16 MFMA (lane l, half hh = l / 32): an operand lane
+// supplies row or column l % 32 and k-slots 8 hh .. 8 hh + 7; a result lane
+// holds column l % 32 and, in register 4 b + r, row 8 b + 4 hh + r.  A lane
+// of S^T thus holds query l % 32 and keys 8 b + 4 hh + r of a 32-key block.
+// As the B operand of the 16-key step c of that block (keys 16 c .. 16 c +
+// 15), its registers 8 c .. 8 c + 7 are already in k-slot order when k-slot
+// s stands for key 16 c + 8 (s / 4) + 4 hh + s % 4; V^T is stored with the
+// keys of every 16-key group in that order (key 8 q + 4 hh + r of the group
+// at position 8 hh + 4 q + r), so a V^T fragment is one 16-byte read.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+template <int DH, bool SEG, int NWQ>
+__device__ __forceinline__ void attn32_item(const AttnArgs& a, int item, int keys_per_split, int n_qt) {
+  constexpr int NT = 64 * NWQ;
+  constexpr int QTILE = 32 * NWQ;
+  // K row pitch DH + 8 elements (68 dwords at dh 128, 36 at 64): the 16-byte
+  // fragment reads of 16 consecutive rows land on 16 distinct 4-bank groups.
+  // V^T row pitch 72 elements, as in the 16-query kernel.
+  constexpr int LDKS = DH + 8;
+  constexpr int LDV = 64 + 8;
+  constexpr int NKS = DH / 16;  // 16-dim steps of S
+  constexpr int NDB = DH / 32;  // 32-dim blocks of O^T
+  constexpr int KCH = 64 * DH / 8;
+  constexpr int KPT = KCH / NT;
+  // V blocks of 4 keys x VD dims: 8 dims (16-byte loads) with four waves,
+  // 4 dims (8-byte loads) with eight, so every thread moves one block
+  constexpr int VD = NWQ == 8 ? 4 : 8;
+  constexpr int VCH = 16 * (DH / VD);
+  static_assert(KCH % NT == 0 && VCH <= NT && NT % VCH == 0, "tile split");
+  using vchunk = typename std::conditional<VD == 8, u32x4, u32x2>::type;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * LDKS];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * LDV];
+
+  const int qt = item % n_qt;
+  const int z = (item / n_qt) % a.splits;
+  const int bh = item / (n_qt * a.splits);
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, c32 = lane & 31;
+  const int qi = qt * QTILE + wave * 32 + c32;
+  const int total = a.len0 + a.len1;
+  const int kbeg = z * keys_per_split;
+  const int kend = min(total, kbeg + keys_per_split);
+
+  // key/value rows through buffer resources, as in the 16-query kernel
+  constexpr int RB = DH * 2;
+  const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.k0 + (long long)bh * a.s0_bh), (short)0, a.len0 * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.v0 + (long long)bh * a.s0_bh), (short)0, a.len0 * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.len1 ? (const bf16*)a.k1 + (long long)bh * a.s1_bh : (const bf16*)a.k0), (short)0, a.len1 * RB,
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.len1 ? (const bf16*)a.v1 + (long long)bh * a.s1_bh : (const bf16*)a.v0), (short)0, a.len1 * RB,
+      0x00020000);
+
+  // Q as the B operand of S^T = K Q^T: query qi, dims 16 ks + 8 hh .. + 7
+  const bf16* qrow = (const bf16*)a.q + (long long)bh * a.q_bh + (long long)min(qi, a.n - 1) * DH;
+  u32x4 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const u32x4*)(qrow + 16 * ks + 8 * hh);
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ntiles = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+  // this thread's V block: keys 4 vkb .. 4 vkb + 3 (vkb fastest over the
+  // lanes), dims vcol .. vcol + VD - 1 (with 4-dim blocks the four 16-lane
+  // groups of a wave take dims +0, +8, +4, +12, as in the 16-query kernel);
+  // threads past VCH repeat a block
+  const int vb = tid % VCH, vkb = vb % 16, vg = vb / 16;
+  const int vcol = VD == 8 ? vg * 8 : (vg >> 2) * 16 + (vg & 1) * 8 + ((vg >> 1) & 1) * 4;
+  int koff[KPT], voff[4];
+#pragma unroll
+  for (int p = 0; p < KPT; ++p) {
+    const int c = tid + p * NT;
+    koff[p] = (c / (DH / 8)) * RB + (c % (DH / 8)) * 16;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) voff[p] = (4 * vkb + p) * RB + vcol * 2;
+  u32x4 kreg[KPT];
+  vchunk vreg[4];
+  auto vload = [&](__amdgpu_buffer_rsrc_t r, int off) -> vchunk {
+    if constexpr (VD == 8) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  };
+  auto gload = [&](int t) {
+    const int kt0 = kbeg + 64 * min(t, ntiles - 1);
+    if constexpr (SEG) {
+      const bool s1 = kt0 >= a.len0;  // uniform
+      const int r0 = s1 ? kt0 - a.len0 : kt0, rows = s1 ? a.len1 - r0 : a.len0 - r0;
+      const bf16* kb = s1 ? (const bf16*)a.k1 + (long long)bh * a.s1_bh : (const bf16*)a.k0 + (long long)bh * a.s0_bh;
+      const bf16* vbp = s1 ? (const bf16*)a.v1 + (long long)bh * a.s1_bh : (const bf16*)a.v0 + (long long)bh * a.s0_bh;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (long long)r0 * DH), (short)0, rows * RB, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vbp + (long long)r0 * DH), (short)0, rows * RB, 0x00020000);
+#pragma unroll
+      for (int p = 0; p < KPT; ++p) kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[p], 0, 0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) vreg[p] = vload(rv, voff[p]);
+      return;
+    }
+    const int b0 = kt0 * RB, b1 = (kt0 - a.len0) * RB;
+#pragma unroll
+    for (int p = 0; p < KPT; ++p)
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(rk0, koff[p] + b0, 0, 0) |
+                __builtin_amdgcn_raw_buffer_load_b128(rk1, koff[p] + b1, 0, 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      vreg[p] = vload(rv0, voff[p] + b0) | vload(rv1, voff[p] + b1);
+  };
+  // V^T position of this thread's four keys (16-key groups in k-slot order)
+  const int vpos = 16 * (vkb >> 2) + 8 * (vkb & 1) + 4 * ((vkb >> 1) & 1);
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int c = tid + p * NT;
+      const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      *(u32x4*)&Ks[buf][row * LDKS + col] = kreg[p];
+    }
+#pragma unroll
+    for (int e = 0; e < VD; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const uint32_t k0 = (vreg[0][w] >> sh) & 0xffffu, k1 = (vreg[1][w] >> sh) & 0xffffu;
+      const uint32_t k2 = (vreg[2][w] >> sh) & 0xffffu, k3 = (vreg[3][w] >> sh) & 0xffffu;
+      *(u32x2*)&Vt[buf][(vcol + e) * LDV + vpos] = u32x2{k0 | (k1 << 16), k2 | (k3 << 16)};
+    }
+  };
+
+  const float sl = 1.4426950408889634f / sqrtf(float(DH));
+  const int klim = a.causal_base < 0 ? kend : min(kend, a.causal_base + qi + 1);
+
+  // one key tile t from LDS buffer t & 1; the loads of tile t + 1 are in
+  // flight meanwhile and go to the other buffer at the end
+  auto tile = [&](int t, bool store_next, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    gload(t + 1);
+    const int kt0 = kbeg + 64 * t, buf = t & 1;
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 ka[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) ka[ks] = *(const u32x4*)&Ks[buf][(32 * kb + c32) * LDKS + 16 * ks + 8 * hh];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) sc[kb] = mfma32x32x16(ka[ks], qf[ks], sc[kb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (MASKED)
+          sc[kb][i] = (kt0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3) < klim) ? sc[kb][i] : -INFINITY;
+        tmax = fmaxf(tmax, sc[kb][i]);
+      }
+    tmax *= sl;
+    // lazy rescaling as in the 16-query kernel; a query's two lanes (halves)
+    // hold the same m_run
+    if (__any(tmax > m_run + 8.f)) {
+      const float tq = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = tq > m_run + 8.f ? tq : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    float m_base = m_run;
+    if constexpr (MASKED) m_base = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], sl, -m_base));
+        sc[kb][i] = p;
+        l_run += p;
+      }
+    // P = P_hi + P_lo (both bf16) against V^T, one 16-key step at a time
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int kb = c >> 1, i0 = 8 * (c & 1);
+      u32x4 pb, pl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x0 = sc[kb][i0 + 2 * q], x1 = sc[kb][i0 + 2 * q + 1];
+        const uint32_t hi = pack_bf16x2(x0, x1);
+        pb[q] = hi;
+        pl[q] = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+      }
+      u32x4 va[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) va[db] = *(const u32x4*)&Vt[buf][(32 * db + c32) * LDV + 16 * c + 8 * hh];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        o[db] = mfma32x32x16(va[db], pb, o[db]);
+        o[db] = mfma32x32x16(va[db], pl, o[db]);
+      }
+    }
+    if (store_next) lstore(buf ^ 1);
+    __syncthreads();
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+
+  if (ntiles) {  // uniform over the workgroup
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    int t = 0;
+    if (a.causal_base < 0) {
+      for (; t + 1 < ntiles; ++t) tile(t, true, Full{});
+    } else {
+      for (; t + 1 < ntiles; ++t) tile(t, true, Masked{});
+    }
+    tile(t, false, Masked{});
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (qi >= a.n) return;
+  // lane: query qi, dims 32 db + 8 bb + 4 hh + r in register 4 bb + r of o[db]
+  if (a.splits == 1) {
+    const float inv = 1.f / l_run;
+    bf16* out = (bf16*)a.out + ((long long)(b * a.n + qi) * a.H + h) * DH;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+        *(u32x2*)(out + 32 * db + 8 * bb + 4 * hh) =
+            u32x2{pack_bf16x2(o[db][4 * bb] * inv, o[db][4 * bb + 1] * inv),
+                  pack_bf16x2(o[db][4 * bb + 2] * inv, o[db][4 * bb + 3] * inv)};
+    return;
+  }
+  const long long base = ((long long)z * a.B * a.H + bh) * a.n + qi;
+  float* po = a.part_o + base * DH;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+      *(f32x4*)(po + 32 * db + 8 * bb + 4 * hh) =
+          f32x4{o[db][4 * bb], o[db][4 * bb + 1], o[db][4 * bb + 2], o[db][4 * bb + 3]};
+  if (hh == 0) *(u32x2*)(a.part_ml + base * 2) = u32x2{__float_as_uint(m_run), __float_as_uint(l_run)};
+}
+
+template <int DH, bool SEG, int NWQ>
+__global__ __launch_bounds__(64 * NWQ) __attribute__((amdgpu_waves_per_eu(2))) void attn32_kernel(
+    AttnArgs a, int keys_per_split, int n_qt, int per_xcd) {
+  const int total_items = a.B * a.H * a.splits * n_qt;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || item >= total_items) return;  // uniform
+  attn32_item<DH, SEG, NWQ>(a, item, keys_per_split, n_qt);
+}
+
 // One attention problem per launch: work items by XCD as above.
 template <int DH, int D, bool SEG, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(
@@ -655,10 +936,33 @@ int launch(const AttnArgs& a, hipStream_t st) {
   return int(hipGetLastError());
 }
 
-// Waves per workgroup of the bf16 kernel: eight (128 queries sharing each K/V
-// tile in LDS, half the L2-to-LDS traffic per query) for long key ranges,
-// four (64 queries, twice the workgroups) otherwise.
-int attn_waves(int n, int keys, int dh) { return keys >= 4096 && n >= 128 && dh >= 64 ? 8 : 4; }
+// bf16 kernel shape: for long key ranges 256-query tiles of eight 32-query
+// waves (each K/V tile staged in LDS serves four times the queries of a
+// 64-query tile), otherwise 64-query tiles of four 16-query waves (four
+// times the workgroups).  Measured at 4 and 8 canvases x 256 queries x 8448
+// keys: 109 and 197 us per layer against 121 and 216 for 128-query tiles of
+// eight 16-query waves, 117 and 211 for 128-query tiles of four 32-query
+// waves; at one canvas x 2304 keys the 32-query waves lose (26.5 against
+// 24.1 us), too few workgroups.
+bool attn_q32(int n, int keys, int dh) { return keys >= 4096 && n >= 128 && dh >= 64; }
+int attn_tile_queries(int n, int keys, int dh) { return attn_q32(n, keys, dh) ? 256 : 64; }
+int attn_tile_waves(int n, int keys, int dh) { return attn_q32(n, keys, dh) ? 8 : 4; }
+
+template <int DH, int NWQ>
+int launch_bf16_q32(const AttnArgs& a, hipStream_t st) {
+  const int total = a.len0 + a.len1;
+  const int per = ((total + a.splits - 1) / a.splits + 63) / 64 * 64;
+  const int n_qt = (a.n + 32 * NWQ - 1) / (32 * NWQ);
+  const int items = a.B * a.H * a.splits * n_qt;
+  const int per_xcd = (items + 7) / 8;
+  if (a.len1 == 0 || a.len0 % 64 == 0)  // no key tile spans both segments
+    hipLaunchKernelGGL((attn32_kernel<DH, true, NWQ>), dim3(8 * per_xcd), dim3(64 * NWQ), 0, st, a, per, n_qt,
+                       per_xcd);
+  else
+    hipLaunchKernelGGL((attn32_kernel<DH, false, NWQ>), dim3(8 * per_xcd), dim3(64 * NWQ), 0, st, a, per, n_qt,
+                       per_xcd);
+  return int(hipGetLastError());
+}
 
 template <int DH, int NW>
 int launch_bf16_nw(const AttnArgs& a, hipStream_t st) {
@@ -682,7 +986,7 @@ template <int DH>
 int launch_bf16(const AttnArgs& a, hipStream_t st) {
   int e;
   if constexpr (DH >= 64)
-    e = attn_waves(a.n, a.len0 + a.len1, DH) == 8 ? launch_bf16_nw<DH, 8>(a, st) : launch_bf16_nw<DH, 4>(a, st);
+    e = attn_q32(a.n, a.len0 + a.len1, DH) ? launch_bf16_q32<DH, 8>(a, st) : launch_bf16_nw<DH, 4>(a, st);
   else
     e = launch_bf16_nw<DH, 4>(a, st);
   if (e || a.splits == 1) return e;
@@ -700,16 +1004,16 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Key splits: double while the grid is under 2048 waves (two four-wave or one
-// eight-wave workgroup per CU) and each split keeps at least 512 keys
-// (measured at 256 queries x 16 heads: 4 splits for 2304 keys, 2 for 4
-// canvases x 8448 keys; shorter splits lose more to the merge and to each
-// workgroup's first tile than they gain in parallelism).
+// Key splits: double while the grid is under 2048 waves (two four-wave or
+// one eight-wave workgroup per CU) and each split keeps at least 512 keys
+// (measured at 256 queries x 16 heads: 4 splits for 2304 keys; shorter
+// splits lose more to the merge and to each workgroup's first tile than they
+// gain in parallelism).
 int attn_splits_for(int B, int H, int n, int keys, int dh) {
-  const int nw = attn_waves(n, keys, dh);
-  const int wgs = ((n + 16 * nw - 1) / (16 * nw)) * B * H;
+  const int qt = attn_tile_queries(n, keys, dh);
+  const int wgs = ((n + qt - 1) / qt) * B * H;
   int s = 1;
-  while (s < 16 && wgs * s * nw < 2048 && keys / (s * 2) >= 512) s *= 2;
+  while (s < 16 && wgs * s * attn_tile_waves(n, keys, dh) < 2048 && keys / (s * 2) >= 512) s *= 2;
   return s;
 }
 
