@@ -52,6 +52,14 @@ def router_in_shared(cfg) -> bool:
             and T <= 384 and cfg.d_shared >= 1024)
 
 
+def topk_in_shared(cfg) -> bool:
+    """Whether the router top-k runs as extra workgroups of the shared-down
+    launch: the logits come from the shared gate/up launch, the shared down is
+    the direct-load kernel's small-M fp32 shape (K = d_shared = 2048), at most
+    128 experts and top 8."""
+    return router_in_shared(cfg) and cfg.d_shared == 2048 and cfg.n_experts <= 128 and cfg.top_k <= 8
+
+
 def algorithmic(cfg, kernel: str):
     """(bytes, flops) one timed launch of `kernel` must move/perform, per layer and step
     (per step for the LM head and the commit).  Weights are read once; activations
@@ -84,12 +92,15 @@ def algorithmic(cfg, kernel: str):
     # launch when router_in_shared(cfg), else a launch of their own
     rl_bytes, rl_flops = E * d * ab + T * E * 4, 2.0 * T * E * d
     fused = router_in_shared(cfg)
-    if kernel == "shared":  # gate/up + SwiGLU (+ router logits), then down (fp32 out)
+    topk_bytes = T * E * 4 + 2 * T * k * 4
+    if kernel == "shared":  # gate/up + SwiGLU (+ router logits), then down (fp32 out) (+ router top-k)
         w = 3 * ds * d * wb + (3 * ds * 4 if wb == 1 else 0)
         b, f = w + T * d * ab + 2 * T * ds * ab + T * d * 4, 2.0 * T * 3 * ds * d
+        if topk_in_shared(cfg):
+            b += topk_bytes
         return (b + rl_bytes, f + rl_flops) if fused else (b, f)
     if kernel == "router":  # top-k over the logits (+ the router GEMM when it runs alone)
-        b = T * E * 4 + 2 * T * k * 4
+        b = topk_bytes
         return (b, 0.0) if fused else (b + rl_bytes + T * d * ab, rl_flops)
     if kernel == "commit":
         return T * (4 + 4 + 4 + 1) * 2, 0.0
@@ -493,6 +504,9 @@ def main():
     if not args.no_kernels:
         kern = {}
         for name in ("attn", "qkv", "shared", "router", "moe_gateup", "moe_down", "lm_head", "commit"):
+            if name == "router" and topk_in_shared(cfg):
+                log("[kernels] router      logits in the shared gate/up launch, top-k in the shared down launch")
+                continue
             _lib.dg_profile_kernel(model.handle, _lib.DG_PROF[name])
             rt.canvas_init(model, canvas)
             rt.generate_canvas(model, canvas, kv)

@@ -262,21 +262,39 @@ int shared_gate_up(dg_model* m, int l, const void* b, int T, void* hs, float* rl
   return DG_OK;
 }
 
-// shared down: ys [T][d_model] (fp32) = hs [T][d_shared] . W_down^T
-int shared_down(dg_model* m, int l, const void* hs, int T, float* ys, hipStream_t st) {
+// shared down: ys [T][d_model] (fp32) = hs [T][d_shared] . W_down^T.  With
+// rlog (the router logits, already computed), the router top-k into
+// m->topk_ids / m->topk_w rides in the same launch where the bf16 kernel
+// covers the shape (*topk_done = true): both read only what the shared
+// gate/up launch wrote, and the top-k workgroups run beside the product's
+// tiles instead of in a launch of their own.
+int shared_down(dg_model* m, int l, const void* hs, int T, float* ys, hipStream_t st, const float* rlog = nullptr,
+                bool* topk_done = nullptr) {
   const dg_config& c = m->cfg;
   const dg_layer_weights& w = m->layers[l];
   GemmArgs g;
   g.A = hs; g.lda = c.d_shared; g.B = w.ws_d; g.ldb = c.d_shared; g.b_scale = w.ss_d;
   g.M = T; g.N = c.d_model; g.K = c.d_shared; g.C = ys; g.ldc = c.d_model;
+  if (rlog && topk_done && m->at == ACT_BF16 && m->swt == W_BF16) {
+    GemmArgs gt = g;
+    gt.tk_logits = rlog; gt.tk_T = T; gt.tk_E = c.n_experts; gt.tk_k = c.top_k;
+    gt.tk_ids = m->topk_ids; gt.tk_w = m->topk_w;
+    const int r = gemm_f32_topk(gt, st);
+    if (r >= 0) {
+      HIP_OK(r);
+      *topk_done = true;
+      return DG_OK;
+    }
+  }
   HIP_OK(gemm(m->at, m->swt, EPI_F32, g, 1, st));
   return DG_OK;
 }
 
 // router: logits rlog [T][E] of b (unless the shared launch computed them),
-// top-k ids [T][k] and weights; `forced` (test hook, nullable) overrides rows.
+// top-k ids [T][k] and weights (unless the shared-down launch computed
+// them); `forced` (test hook, nullable) overrides rows.
 int route(dg_model* m, int l, const void* b, int T, float* rlog, bool logits_done, int* ids, float* wts,
-          const int* forced, hipStream_t st) {
+          const int* forced, hipStream_t st, bool topk_done = false) {
   const dg_config& c = m->cfg;
   const int E = c.n_experts, k = c.top_k, d = c.d_model;
   if (!logits_done) {
@@ -284,7 +302,7 @@ int route(dg_model* m, int l, const void* b, int T, float* rlog, bool logits_don
     g.A = b; g.lda = d; g.B = m->layers[l].wr; g.ldb = d; g.M = T; g.N = E; g.K = d; g.C = rlog; g.ldc = E;
     HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_F32, g, 1, st));
   }
-  HIP_OK(router_topk(rlog, T, E, k, ids, wts, st));
+  if (!topk_done) HIP_OK(router_topk(rlog, T, E, k, ids, wts, st));
   if (forced) HIP_OK(router_force(rlog, T, E, k, forced, ids, wts, st));
   return DG_OK;
 }
@@ -409,11 +427,11 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
   // beside the router and the routed experts, its workgroups held CUs that
   // the routed gate/up workgroups (138 KB of LDS each) could not share, and
   // the waits this caused on the main stream cost more than the overlap won.)
-  bool router_done = false;
+  bool router_done = false, topk_done = false;
   {
     ProfScope ps(m, DG_PROF_SHARED, st);
     s = shared_gate_up(m, l, m->a, T, m->hs, m->rlog, &router_done, st);
-    if (!s) s = shared_down(m, l, m->hs, T, m->ys, st);
+    if (!s) s = shared_down(m, l, m->hs, T, m->ys, st, router_done ? m->rlog : nullptr, &topk_done);
     if (s) return s;
   }
   {
@@ -421,7 +439,7 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     const int* forced = (m->force_ids && !causal)
                             ? m->force_ids + (long long)l * m->max_batch * c.canvas_len * c.top_k
                             : nullptr;
-    s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, forced, st);
+    s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, forced, st, topk_done);
     if (s) return s;
   }
   return moe_chunks(m, l, T, m->diag_counts && !causal, st);
@@ -481,16 +499,16 @@ int mixed_layer(dg_model* m, int l, const MixedSeg* sg, int n_segs, int T, int T
     HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_RESID, g, 1, st));
   }
   HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st));
-  bool router_done = false;
+  bool router_done = false, topk_done = false;
   {
     ProfScope ps(m, DG_PROF_SHARED, st);
     s = shared_gate_up(m, l, m->a, T, m->hs, m->rlog, &router_done, st);
-    if (!s) s = shared_down(m, l, m->hs, T, m->ys, st);
+    if (!s) s = shared_down(m, l, m->hs, T, m->ys, st, router_done ? m->rlog : nullptr, &topk_done);
     if (s) return s;
   }
   {
     ProfScope ps(m, DG_PROF_ROUTER, st);
-    s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, nullptr, st);
+    s = route(m, l, m->a, T, m->rlog, router_done, m->topk_ids, m->topk_w, nullptr, st, topk_done);
     if (s) return s;
     if (m->force_ids && T_ref)  // test hook, on the refine rows (the first T_ref)
       HIP_OK(router_force(m->rlog, T_ref, c.n_experts, c.top_k,

@@ -2,10 +2,7 @@
 // experts plus one shared expert, each token routed to its top 8).
 //
 // router_topk: one wave per token picks the k largest router logits (ties to
-// the lower expert id) by ranking every logit against all others, and weights
-// them by a softmax over the k picks, which equals the full router softmax
-// restricted to the picks and renormalised.
-// (A NaN logit is not ranked meaningfully; router logits are finite.)
+// the lower expert id) and weights them (topk.h).
 // router_permute: one workgroup builds the expert histogram, its exclusive
 // scan, and the expert-major, token-ascending permutation of the (token, slot)
 // pairs from per-expert token bitmasks and popcount prefix sums; the layout is
@@ -14,74 +11,18 @@
 
 #include "dg_common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace dg {
 namespace {
 
-// Each (logit, expert) pair becomes one 64-bit key that orders by logit, then
-// by lower expert id (the low word holds ~id): a total order, so the top k
-// are the keys with fewer than k larger keys.
-__device__ __forceinline__ unsigned long long topk_key(float f, int e) {
-  uint32_t b = __float_as_uint(f);
-  b ^= (b >> 31) ? 0xffffffffu : 0x80000000u;  // order-preserving map to unsigned
-  return ((unsigned long long)b << 32) | (0xffffffffu - uint32_t(e));
-}
-
-__device__ __forceinline__ float topk_value(unsigned long long key) {
-  uint32_t b = uint32_t(key >> 32);
-  b = (b & 0x80000000u) ? (b ^ 0x80000000u) : ~b;
-  return __uint_as_float(b);
-}
-
-// One wave per token.  The E keys go to LDS; every lane ranks its own keys
-// (KPL of them: E <= 64 KPL) by counting the larger ones (the key order is
-// total, so ranks are distinct), reading the keys as wave-wide broadcasts,
-// and the keys ranked below k are written to their slot.  No cross-lane
-// shuffles.
+// One wave per token (topk.h).
 template <int KPL>
 __global__ __launch_bounds__(64) void topk_kernel(const float* logits, int T, int E, int k, int* ids,
                                                   float* w) {
   __shared__ __attribute__((aligned(16))) unsigned long long ks[64 * KPL];
   __shared__ float sel[8];
-  const int t = blockIdx.x, lane = threadIdx.x;
-  unsigned long long key[KPL];
-#pragma unroll
-  for (int u = 0; u < KPL; ++u) {
-    const int e = lane + 64 * u;
-    key[u] = e < E ? topk_key(logits[(long long)t * E + e], e) : 0ull;
-    ks[e] = key[u];  // past E: key 0, ranked below every real key
-  }
-  __syncthreads();
-  const int E2 = (E + 1) & ~1;
-  int rank[KPL];
-#pragma unroll
-  for (int u = 0; u < KPL; ++u) rank[u] = 0;
-#pragma unroll 8
-  for (int e = 0; e < E2; e += 2) {
-    const u32x4 kk = *(const u32x4*)&ks[e];
-    const unsigned long long k0 = ((unsigned long long)kk[1] << 32) | kk[0];
-    const unsigned long long k1 = ((unsigned long long)kk[3] << 32) | kk[2];
-#pragma unroll
-    for (int u = 0; u < KPL; ++u) rank[u] += int(k0 > key[u]) + int(k1 > key[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < KPL; ++u) {
-    const int e = lane + 64 * u;
-    if (e < E && rank[u] < k) sel[rank[u]] = topk_value(key[u]);
-  }
-  __syncthreads();
-  // softmax over the k picks, summed in rank order
-  const float m = sel[0];
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __expf(sel[j] - m);
-#pragma unroll
-  for (int u = 0; u < KPL; ++u) {
-    const int e = lane + 64 * u;
-    if (e < E && rank[u] < k) {
-      ids[t * k + rank[u]] = e;
-      w[t * k + rank[u]] = __expf(sel[rank[u]] - m) / sum;
-    }
-  }
+  topk_row<KPL>(logits, blockIdx.x, true, E, k, ids, w, ks, sel);
 }
 
 // one thread per token: rows with forced[t][0] >= 0 take the forced ids (in

@@ -28,6 +28,7 @@
 
 #include "dg_common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace dg {
 namespace {
@@ -504,9 +505,12 @@ __device__ __forceinline__ long long dl_brow(const GemmArgs& g, int tn, int r, b
 // NWV waves as WAVES_M x (NWV / WAVES_M); each wave owns a (BM / WAVES_M) x
 // (BN / WAVES_N) block of the tile.  An A stage buffer holds BM / 8 blocks, a
 // B stage buffer BN / 8, block q holding rows 8 q .. 8 q + 7 of the tile.
-template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT>
+// TK: the launch also holds router top-k workgroups (one token per wave),
+// after the tiles in each XCD's run of workgroups: slot s >= per_xcd of XCD x
+// is top-k workgroup x * tk_per_xcd + s - per_xcd.
+template <int BM, int BN, int WAVES_M, int NWV, int SA, int SB, int EPI, int KT, bool TK = false>
 __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int tiles_n2,
-                                                         int per_xcd) {
+                                                         int per_xcd, int tk_per_xcd = 0) {
   constexpr int WAVES_N = NWV / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 16, FN = WN / 16;
@@ -549,6 +553,16 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(GemmArgs g, int tiles_m
   // tiles of the second product (B2, fp32 out; compiled into the SwiGLU
   // kernels only) come first, then the main ones
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  if constexpr (TK) {
+    if (slot >= per_xcd) {  // uniform: a top-k workgroup
+      __shared__ __attribute__((aligned(16))) unsigned long long tk_keys[NWV][128];
+      __shared__ float tk_sel[NWV][8];
+      const int w = threadIdx.x >> 6;
+      const int t = (xcd * tk_per_xcd + slot - per_xcd) * NWV + w;
+      topk_row<2>(g.tk_logits, t, t < g.tk_T, g.tk_E, g.tk_k, g.tk_ids, g.tk_w, tk_keys[w], tk_sel[w]);
+      return;
+    }
+  }
   const int tile0 = xcd * per_xcd + slot, aux_tiles = EPI == EPI_SWIGLU ? tiles_m * tiles_n2 : 0;
   if (slot >= per_xcd || tile0 >= aux_tiles + tiles_m * tiles_n) return;  // uniform over the workgroup
   const bool aux = EPI == EPI_SWIGLU && tile0 < aux_tiles;
@@ -1019,6 +1033,18 @@ int launch_grouped(const bf16* X, const int* pair_row, const int* off, int E, in
 }
 
 }  // namespace
+
+int gemm_f32_topk(const GemmArgs& g, hipStream_t st) {
+  constexpr int BM = 64, BN = 32, NWV = 4;
+  if (g.K != 2048 || g.lda % 8 || g.ldb % 8 || g.N < 1024 || g.M > 384 || g.B2) return -1;
+  if (!g.tk_logits || g.tk_T <= 0 || g.tk_E > 128 || g.tk_k > 8 || g.tk_k > g.tk_E) return -1;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+  const int tk_wgs = (g.tk_T + NWV - 1) / NWV, tk_per_xcd = (tk_wgs + 7) / 8;
+  hipLaunchKernelGGL((dgemm_kernel<BM, BN, 4, NWV, 6, 6, EPI_F32, 32, true>), dim3(8 * (per_xcd + tk_per_xcd)),
+                     dim3(64 * NWV), 0, st, g, tiles_m, tiles_n, 0, per_xcd, tk_per_xcd);
+  return int(hipGetLastError());
+}
 
 int lm_tiles_tiled(int vocab, int K) {
   if (lm_direct(K)) return (vocab + LMD_BN - 1) / LMD_BN * (LMD_NW / LMD_WM);

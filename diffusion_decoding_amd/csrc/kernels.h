@@ -59,10 +59,21 @@ struct GemmArgs {
   int N2 = 0;
   float* C2 = nullptr;
   long long ldc2 = 0;
+  // optional router top-k in the same launch (gemm_f32_topk only): ids and
+  // weights [tk_T][tk_k] from the router logits tk_logits [tk_T][tk_E]
+  const float* tk_logits = nullptr;
+  int tk_T = 0, tk_E = 0, tk_k = 0;
+  int* tk_ids = nullptr;
+  float* tk_w = nullptr;
 };
 
 // Returns 0 or a HIP error code.
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st);
+// EPI_F32 product (bf16 A and B, K = 2048, M <= 384, N >= 1024) with the
+// router top-k of g.tk_* in the same launch, on workgroups of their own that
+// run beside the product's tiles.  Returns -1 (nothing launched) when the
+// shape is not covered (also tk_E > 128 or tk_k > 8), else 0 or a HIP error.
+int gemm_f32_topk(const GemmArgs& g, hipStream_t st);
 // Routed experts with bf16 weights in the tiled layout, as grouped 128 x 128
 // tiles over expert-major pair lists (off [E+1], pair_row [pairs]):
 // gate/up (X = normed rows [T][K], gathered by pair_row) -> h [pairs][Nout]

@@ -46,11 +46,14 @@ def test_router_logits_follow_the_launch_that_computes_them():
     assert not bench.router_in_shared(c4)      # fp8 shared expert
     T, d, E, ds = 256, 2048, 128, 2048
     logits = E * d * 2 + T * E * 4, 2.0 * T * E * d
+    # c2: the top-k rides in the shared down launch too, so its bytes join the shared class
+    assert bench.topk_in_shared(c2) and not bench.topk_in_shared(c3) and not bench.topk_in_shared(c4)
+    topk = T * E * 4 + 2 * T * 8 * 4
     sb, sf = bench.algorithmic(c2, "shared")
     base_b = 3 * ds * d * 2 + T * d * 2 + 2 * T * ds * 2 + T * d * 4
-    assert (sb, sf) == (base_b + logits[0], 2.0 * T * 3 * ds * d + logits[1])
+    assert (sb, sf) == (base_b + topk + logits[0], 2.0 * T * 3 * ds * d + logits[1])
     rb, rf = bench.algorithmic(c2, "router")
-    assert (rb, rf) == (T * E * 4 + 2 * T * 8 * 4, 0.0)
+    assert (rb, rf) == (topk, 0.0)
     # batch 4: the router GEMM is its own launch and its bytes stay in the router class
     T4 = 1024
     rb, rf = bench.algorithmic(c3, "router")
