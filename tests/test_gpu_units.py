@@ -123,8 +123,13 @@ def _bf16_normal(seed, shape):
     return round_bf16(np.random.default_rng(seed).standard_normal(shape))
 
 
+# 4096 keys and more with 128 queries or more take the 32-query-wave kernel
+# (256-query tiles): batch 4 at 8192, a ragged batch 2 whose cache length
+# splits a key tile between cache and canvas rows and whose second query tile
+# is part empty, and causal commit passes into long caches.
 @pytest.mark.parametrize("B,P,n,causal", [(1, 1024, 256, False), (4, 8192, 256, False), (1, 300, 200, False),
-                                          (1, 512, 256, True), (2, 70, 200, True)])
+                                          (1, 512, 256, True), (2, 70, 200, True), (2, 4200, 300, False),
+                                          (1, 4000, 256, True), (1, 4100, 200, True)])
 def test_attention_unit(rt, unit_bf16, B, P, n, causal):
     u, cfg = unit_bf16, unit_bf16.cfg
     H, dh = cfg.n_heads, cfg.head_dim
@@ -159,6 +164,48 @@ def test_attention_unit(rt, unit_bf16, B, P, n, causal):
             pre[b, :, h], tol[b, :, h] = o, t
     nmis, nflag = check_bf16(got, pre, tol, f"attention B={B} P={P} n={n}")
     _report("attention output", nmis, nflag, got.size)
+
+
+@pytest.mark.parametrize("P,n,causal", [(4200, 256, False), (4096, 160, True)])
+def test_attention_unit_head_dim_64_long_keys(rt, P, n, causal):
+    """head_dim 64 on the 32-query-wave kernel (4096 keys and more): a
+    cache length that splits a key tile between cache and canvas rows, and a
+    causal pass whose second query tile is part empty."""
+    from workloads import tiny_config
+    cfg = tiny_config(name="unit_dh64", d_model=256, n_heads=4, head_dim=64, n_experts=8, top_k=2, d_expert=64,
+                      d_shared=64, vocab=512, canvas_len=256, prompt_len=P, act_dtype="bf16", expert_dtype="bf16",
+                      seed=77)
+    H, dh = cfg.n_heads, cfg.head_dim
+    say(f"attention unit, head_dim 64: {P} cache rows, {n} queries, {'causal' if causal else 'bidirectional'}")
+    inp = make_inputs(cfg, device="cuda", kv_capacity=P + 256)
+    model = rt.Model(inp, max_batch=1, max_tokens=256)
+    try:
+        q = _bf16_normal(300 + P, (1, H, n, dh))
+        kc = _bf16_normal(301 + P, (1, H, n, dh))
+        vc = _bf16_normal(302 + P, (1, H, n, dh))
+        kvk, kvv = inp.kv_k.clone(), inp.kv_v.clone()
+        if causal:
+            kvk[0, :, :, P:P + n] = _dev(kc)
+            kvv[0, :, :, P:P + n] = _dev(vc)
+            out = rt.test_attention(model, 0, _dev(q), rt.KVCache(kvk, kvv, P))
+        else:
+            out = rt.test_attention(model, 0, _dev(q), rt.KVCache(kvk, kvv, P), _dev(kc), _dev(vc))
+        torch.cuda.synchronize()
+        got = _host(out).reshape(1, n, H, dh)
+        cache_k, cache_v = kvk[0].double().cpu().numpy(), kvv[0].double().cpu().numpy()
+        pre, tol = np.empty_like(got), np.empty_like(got)
+        for h in range(H):
+            if causal:
+                K, V = cache_k[0, h, :P + n], cache_v[0, h, :P + n]
+            else:
+                K = np.concatenate([cache_k[0, h, :P], kc[0, h]])
+                V = np.concatenate([cache_v[0, h, :P], vc[0, h]])
+            pre[0, :, h], tol[0, :, h] = attention_ref(q[0, h], K, V, causal_start=P if causal else None)
+        nmis, nflag = check_bf16(got, pre, tol, f"attention dh 64 P={P} n={n}")
+        _report("attention output", nmis, nflag, got.size)
+    finally:
+        model.close()
+        torch.cuda.synchronize()
 
 
 # ----------------------------------------------------------------------------- router
