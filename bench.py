@@ -395,7 +395,7 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB five times and exit "
                          "(reference for the HBM byte counters)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the batch-4 (c3), batch-8 (c5), fill-in-the-middle, block-autoregressive "
+                    help="skip the batch-4 (c3), batch-8 (c5), batch 16 and 32, fill-in-the-middle, block-autoregressive "
                          "fp8 (c4), MXFP4 (c6), self-conditioning and mixed-phase measurements")
     ap.add_argument("--mixed", action="store_true",
                     help="only the mixed-phase serving pass at the c2 shapes (its own JSON line; for profiling)")
@@ -558,6 +558,10 @@ def main():
     if not args.no_extra and args.config == "c2":
         out["batch4"] = time_loop(get_config("c3"), canvases=1, warmup=1)
         out["batch8"] = time_loop(get_config("c5"), canvases=1, warmup=1)
+        # batch sweep beyond 8 at the c2 shapes (2048-row prompts): 16 and 32
+        # canvases, 4096 and 8192 tokens in one routed launch
+        out["batch_sweep"] = {str(b): time_loop(get_config("c2").replace(name=f"c2_batch{b}", batch=b),
+                                                canvases=1, warmup=1) for b in (16, 32)}
         # the absorbing-state (mask) noise variant: same model, [MASK] = the last id
         c2 = get_config("c2")
         out["absorbing"] = time_loop(c2.replace(name="c2_absorbing", mask_token=c2.vocab - 1),

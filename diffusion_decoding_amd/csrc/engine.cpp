@@ -61,6 +61,7 @@ struct dg_model {
   void *x = nullptr, *a = nullptr, *qkv = nullptr, *q = nullptr, *kc = nullptr, *vc = nullptr,
        *o = nullptr, *h = nullptr, *hs = nullptr;
   float *attn_po = nullptr, *attn_ml = nullptr;
+  void* perm_scratch = nullptr;  // the routing permutation's masks and prefixes above 2048 tokens
   int attn_max_splits = 8;
   float *rlog = nullptr, *topk_w = nullptr, *y = nullptr, *ys = nullptr, *lm_part = nullptr;
   float* rope_tab = nullptr;  // [max_tokens][head_dim / 2] (cos, sin) of the current positions
@@ -307,6 +308,18 @@ int route(dg_model* m, int l, const void* b, int T, float* rlog, bool logits_don
   return DG_OK;
 }
 
+// Whether a T-row pass takes the grouped gate/up path: from about 80 pairs
+// per expert (and whenever routing piles onto few experts, as under
+// absorbing noise) the gate/up is a grouped GEMM of 128-pair tiles after a
+// routing permutation: measured 221 against 322 us at 128 pairs per expert,
+// 143 against 198 us under absorbing noise, 175 against 190 us (slower) at
+// 64.  Same bits either way.
+bool grouped_route(const dg_model* m, long long T) {
+  const dg_config& c = m->cfg;
+  return m->at == ACT_BF16 && m->wt == W_BF16 && grouped_supported(true, c.d_model, c.d_expert, c.n_experts) &&
+         (T * c.top_k >= 80LL * c.n_experts || c.mask_token >= 0);
+}
+
 // routed experts on the top-k ids [T][k]: h [T*k][d_expert] (SwiGLU
 // products) and y [T*k][d_model] (fp32 expert outputs), both in pair order
 // (expert-major, token-ascending); off [E+1], pair_row [T*k] and pos [T][k]
@@ -321,15 +334,8 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
     // so the open rows pile onto a few experts; the pooled kernels' 96-token
     // passes stream a heavy expert's weights a third as often.
     const int pairs = c.mask_token >= 0 ? std::max(T * k, 24 * E + 1) : T * k;
-    // From about 80 pairs per expert (and whenever routing piles onto few
-    // experts, as under absorbing noise) the gate/up is a grouped GEMM of
-    // 128-pair tiles: measured 221 against 322 us at 128 pairs per expert,
-    // 143 against 198 us under absorbing noise, 175 against 190 us (slower)
-    // at 64.  Same bits either way.
-    const bool grouped = m->wt == W_BF16 && grouped_supported(true, d, de, E) &&
-                         (T * k >= 80 * E || c.mask_token >= 0);
-    if (grouped) {
-      HIP_OK(router_permute(ids, T, E, k, off, pair_row, pos, st));
+    if (grouped_route(m, T)) {
+      HIP_OK(router_permute(ids, T, E, k, off, pair_row, pos, st, m->perm_scratch));
       ProfScope ps(m, DG_PROF_MOE_GATEUP, st);
       HIP_OK(grouped_experts(true, b, pair_row, off, E, T * k, w.w_gu, d, de, h, st));
     } else {
@@ -338,8 +344,16 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
       HIP_OK(moe_experts(m->wt, true, b, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, h, st, &r, pairs));
     }
     {
-      ProfScope ps(m, DG_PROF_MOE_DOWN, st);  // routed down
-      HIP_OK(moe_experts(m->wt, false, h, pair_row, off, E, w.w_d, w.s_d, de, d, y, st, nullptr, pairs));
+      // routed down: grouped 128 x 128 tiles from 256 pairs per expert (c2
+      // shapes, batch 16 / 32: 7.8 / 13.3 ms per step against 8.8 / 16.2 for
+      // the pooled weight stream, whose passes stream an expert's weights
+      // once per 96 pairs; a tie at 192, 5.4 against 5.1 ms at 128), else the
+      // weight stream.  Same bits either way.
+      ProfScope ps(m, DG_PROF_MOE_DOWN, st);
+      if (grouped_route(m, T) && (long long)T * k >= 256LL * E && grouped_supported(false, de, d, E))
+        HIP_OK(grouped_experts(false, h, pair_row, off, E, T * k, w.w_d, de, d, y, st));
+      else
+        HIP_OK(moe_experts(m->wt, false, h, pair_row, off, E, w.w_d, w.s_d, de, d, y, st, nullptr, pairs));
     }
     return DG_OK;
   }
@@ -363,11 +377,18 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
   return DG_OK;
 }
 
-// Rows per routed-expert launch: the routed gate/up kernel derives the
+// Rows per routed-expert launch of a T-row pass.  The grouped path (routing
+// permutation, then grouped gate/up tiles) takes all rows at once: its
+// permutation scales to any T, and the tiles of one expert weight tile run
+// side by side on one XCD, so the weights come from HBM about once however
+// many pair tiles an expert has.  The weight-stream kernels derive the
 // routing of up to 2048 tokens in LDS (the fp32 path's permutation kernel
-// takes 1024); larger batches run in chunks, each streaming the expert
+// takes 1024); there larger passes run in chunks, each streaming the expert
 // weights once.
-int route_chunk(const dg_model* m) { return m->at == ACT_BF16 ? 2048 : 1024; }
+int route_chunk(const dg_model* m, long long T) {
+  if (grouped_route(m, T)) return int(T);
+  return m->at == ACT_BF16 ? 2048 : 1024;
+}
 
 // Routed experts on the top-k ids of rows [0, T) (normed rows in m->a, the
 // shared-expert output in m->ys), then the combine, residual add and next
@@ -375,7 +396,7 @@ int route_chunk(const dg_model* m) { return m->at == ACT_BF16 ? 2048 : 1024; }
 // counts of layer l into m->diag_counts.
 int moe_chunks(dg_model* m, int l, int T, bool diag, hipStream_t st) {
   const dg_config& c = m->cfg;
-  const int k = c.top_k, d = c.d_model, chunk = route_chunk(m);
+  const int k = c.top_k, d = c.d_model, chunk = route_chunk(m, T);
   for (int c0 = 0; c0 < T; c0 += chunk) {
     const int tc = std::min(chunk, T - c0);
     const size_t row = (size_t)d * m->esz;
@@ -643,7 +664,8 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   if (max_kv > kv_limit) return fail(DG_ERR_SHAPE, "max_kv %d exceeds %lld rows", max_kv, kv_limit);
   const int ntok = std::max(max_tokens, cfg->canvas_len);
   // rows of one call (the workspace grows with it; the routed experts take
-  // larger calls in chunks of 2048 rows, 1024 with fp32)
+  // a call's rows at once on the grouped path, else in chunks of 2048 rows,
+  // 1024 with fp32)
   const long long max_t = 8192;
   if ((long long)max_batch * ntok > max_t)
     return fail(DG_ERR_SHAPE, "max_batch * max(max_tokens, canvas_len) must be <= %lld", max_t);
@@ -666,7 +688,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   const size_t T = m->Tmax, d = cfg->d_model, A = (size_t)cfg->n_heads * cfg->head_dim;
   const size_t E = cfg->n_experts, k = cfg->top_k, de = cfg->d_expert, ds = cfg->d_shared;
   const size_t Tc = (size_t)max_batch * cfg->canvas_len;
-  const size_t Tr = std::min(T, (size_t)route_chunk(m));  // rows of one routed launch
+  const size_t Tr = std::min(T, (size_t)route_chunk(m, (long long)T));  // rows of one routed launch
   m->lm_ntiles = lm_tiles(m->at, cfg->d_model, cfg->vocab);
   const size_t es = m->esz;
   struct Req {
@@ -698,6 +720,7 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
       {(void**)&m->gap, Tc * 4},
       {(void**)&m->am, Tc * 4},
       {(void**)&m->ctl, (size_t)(2 + max_batch) * 4},
+      {&m->perm_scratch, router_permute_scratch(int(Tr), int(E))},
   };
   for (auto& r : reqs) {
     s = alloc(m, r.p, r.bytes);
@@ -1006,7 +1029,7 @@ int dg_test_moe(dg_model* m, int32_t layer, const void* b, int32_t T, const int3
   int s = check_layer(m, layer);
   if (!s) s = check_rows(m, T);
   if (s) return s;
-  if (T > route_chunk(m)) return fail(DG_ERR_SHAPE, "T=%d exceeds one routed launch (%d rows)", T, route_chunk(m));
+  if (T > route_chunk(m, T)) return fail(DG_ERR_SHAPE, "T=%d exceeds one routed launch (%d rows)", T, route_chunk(m, T));
   return routed(m, layer, b, T, ids, h ? h : m->h, y, m->off, m->pair_row, pos, (hipStream_t)stream);
 }
 

@@ -3,10 +3,10 @@
 //
 // router_topk: one wave per token picks the k largest router logits (ties to
 // the lower expert id) and weights them (topk.h).
-// router_permute: one workgroup builds the expert histogram, its exclusive
-// scan, and the expert-major, token-ascending permutation of the (token, slot)
-// pairs from per-expert token bitmasks and popcount prefix sums; the layout is
-// deterministic.
+// router_permute: one workgroup (three launches above 2048 tokens) builds the
+// expert histogram, its exclusive scan, and the expert-major, token-ascending
+// permutation of the (token, slot) pairs from per-expert token bitmasks and
+// popcount prefix sums; the layout is deterministic.
 #include <climits>
 
 #include "dg_common.h"
@@ -121,7 +121,80 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, i
   }
 }
 
+// More tokens than one workgroup's LDS holds (T > PERM_MAX_TOKENS): the same
+// layout from three launches.  Each 64-token block writes one token bitmask
+// per expert (masks [W][E]); one workgroup turns the masks' popcounts into
+// per-block prefixes (wpre [W][E]) and the expert offsets; then each pair
+// finds its slot as in the one-workgroup kernel.
+__global__ __launch_bounds__(256) void perm_masks_kernel(const int* ids, int T, int E, int k,
+                                                         unsigned long long* masks) {
+  __shared__ unsigned long long mask[256];
+  const int w = blockIdx.x, t0 = 64 * w, tn = min(64, T - t0);
+  for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
+  __syncthreads();
+  for (int q = threadIdx.x; q < tn * k; q += 256)
+    atomicOr(&mask[ids[(long long)t0 * k + q]], 1ull << (q / k));
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) masks[(long long)w * E + e] = mask[e];
+}
+
+__global__ __launch_bounds__(256) void perm_scan_kernel(const unsigned long long* masks, int W, int E, int* wpre,
+                                                        int* off) {
+  __shared__ int cnt_s[256];
+  __shared__ int off_s[257];
+  const int tid = threadIdx.x;
+  int run = 0;
+  if (tid < E)
+    for (int w = 0; w < W; ++w) {
+      wpre[(long long)w * E + tid] = run;
+      run += __popcll(masks[(long long)w * E + tid]);
+    }
+  cnt_s[tid] = run;
+  __syncthreads();
+  // exclusive scan of the counts by wave 0: lane l owns experts 4l .. 4l+3
+  if (tid < 64) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      c[u] = cnt_s[4 * tid + u];
+      sum += c[u];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
+    }
+    int r = incl - sum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      off_s[4 * tid + u] = r;
+      r += c[u];
+    }
+    if (tid == 63) off_s[256] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) off[e] = off_s[e];
+  if (tid == 0) off[E] = off_s[256];
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int* ids, int T, int E, int k,
+                                                           const unsigned long long* masks, const int* wpre,
+                                                           const int* off, int* pair_row, int* pos) {
+  const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= (long long)T * k) return;
+  const int t = int(p / k), e = ids[p];
+  const long long we = (long long)(t >> 6) * E + e;
+  const int slot = off[e] + wpre[we] + __popcll(masks[we] & ((1ull << (t & 63)) - 1ull));
+  pair_row[slot] = t;
+  pos[p] = slot;
+}
+
 }  // namespace
+
+size_t router_permute_scratch(int T, int E) {
+  return T <= PERM_MAX_TOKENS ? 0 : (size_t)((T + 63) / 64) * E * (sizeof(unsigned long long) + sizeof(int));
+}
 
 int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hipStream_t st) {
   if (T <= 0) return 0;
@@ -142,12 +215,23 @@ int router_force(const float* logits, int T, int E, int k, const int* forced, in
   return int(hipGetLastError());
 }
 
-int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,
-                   hipStream_t st) {
+int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos, hipStream_t st,
+                   void* scratch) {
   if (T <= 0) return 0;
-  if (T > PERM_MAX_TOKENS || E > 256 || k > E) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, st, ids, T, E, k, off, pair_row,
-                     pos);
+  if (E > 256 || k > E || k > 64) return int(hipErrorInvalidValue);
+  if (T <= PERM_MAX_TOKENS) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, st, ids, T, E, k, off, pair_row, pos);
+    return int(hipGetLastError());
+  }
+  if (!scratch) return int(hipErrorInvalidValue);
+  const int W = (T + 63) / 64;
+  unsigned long long* masks = (unsigned long long*)scratch;
+  int* wpre = (int*)(masks + (size_t)W * E);
+  hipLaunchKernelGGL(perm_masks_kernel, dim3(W), dim3(256), 0, st, ids, T, E, k, masks);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, st, masks, W, E, wpre, off);
+  const long long P = (long long)T * k;
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(unsigned((P + 255) / 256)), dim3(256), 0, st, ids, T, E, k, masks,
+                     wpre, off, pair_row, pos);
   return int(hipGetLastError());
 }
 

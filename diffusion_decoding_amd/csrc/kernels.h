@@ -218,10 +218,12 @@ int router_topk(const float* logits, int T, int E, int k, int* ids, float* w, hi
 // and the softmax of their logits as weights (a test hook: lines the routing
 // up with a reference where two router logits nearly tie).
 int router_force(const float* logits, int T, int E, int k, const int* forced, int* ids, float* w, hipStream_t st);
-// ids [T][k] -> cnt[E], off[E+1], pair_row[T*k] (token of each pair slot, expert-major,
-// token-ascending), pos[T][k] (slot of pair (t, j)).
-int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos,
-                   hipStream_t st);
+// ids [T][k] -> off[E+1], pair_row[T*k] (token of each pair slot, expert-major,
+// token-ascending), pos[T][k] (slot of pair (t, j)).  Above 2048 tokens it
+// needs scratch of router_permute_scratch(T, E) bytes (8-byte aligned).
+int router_permute(const int* ids, int T, int E, int k, int* off, int* pair_row, int* pos, hipStream_t st,
+                   void* scratch = nullptr);
+size_t router_permute_scratch(int T, int E);
 // counts[e] (+)= off[e + 1] - off[e] for e < E (diagnostic; accumulate adds)
 int expert_counts(const int* off, int E, int* counts, bool accumulate, hipStream_t st);
 

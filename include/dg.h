@@ -208,8 +208,10 @@ const char* dg_version(void);
  * limit, 2^31 / (head_dim x element size) rows (attention addresses a cache
  * plane with 32-bit byte offsets); a larger max_kv is refused.  The rows of
  * one call, max_batch x max(max_tokens, canvas_len), may be at most 8192
- * (DG_ERR_SHAPE otherwise); the routed experts take more than 2048 rows (1024
- * with fp32 activations) in chunks, each streaming the expert weights once.
+ * (DG_ERR_SHAPE otherwise).  With BF16 experts at d_model 2048 the routed
+ * experts take all of a call's rows in one launch once they hold about 80
+ * pairs per expert (grouped tiles); otherwise more than 2048 rows (1024 with
+ * fp32 activations) run in chunks, each streaming the expert weights once.
  * Must be called with the target device current. */
 int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch,
                     int32_t max_tokens, int32_t max_kv, dg_model** out);

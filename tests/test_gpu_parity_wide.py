@@ -220,6 +220,21 @@ def test_batch8_full_width_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_batch16_full_width_one_step(rt):
+    """Sixteen canvases (4096 tokens in one routed launch: the three-launch
+    routing permutation, the grouped gate/up and the grouped down at about
+    256 pairs per expert), each with its own 512-row prompt; a short
+    vocabulary keeps the oracle's LM head quick."""
+    cfg = get_config("c2").replace(name="c2_batch16_1_layer", n_layers=1, batch=16, prompt_len=512, vocab=8192)
+    say("batch 16 x 256 (4096 tokens in one routed launch), 1 layer, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_canvas512_full_width_one_step(rt):
     """A 512-position canvas at full width (the canvas-length variant): 512
     tokens take the large-M projection tiles, the attention two 256-query

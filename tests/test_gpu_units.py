@@ -265,10 +265,10 @@ def test_shared_unit_fp8(rt, unit_fp8):
 
 # ----------------------------------------------------------------------------- routed experts
 
-def _moe_case(rt, u, b, ids):
+def _moe_case(rt, u, b, ids, model=None):
     cfg = u.cfg
     T, k, E = ids.shape[0], cfg.top_k, cfg.n_experts
-    h, y, pos = rt.test_moe(u.model, 0, _dev(b), torch.from_numpy(ids.astype(np.int32)).cuda())
+    h, y, pos = rt.test_moe(model or u.model, 0, _dev(b), torch.from_numpy(ids.astype(np.int32)).cuda())
     torch.cuda.synchronize()
     hg, yg, pg = _host(h), to_host(y).astype(np.float64), to_host(pos)
     # pair order: expert-major, token-ascending (unique), bit-exact
@@ -310,6 +310,26 @@ def test_moe_unit_bf16(rt, unit_bf16, T):
     say(f"routed experts unit (bf16): {T} rows, routing from the oracle's router")
     b = _normed_rows(500 + T, T, unit_bf16.cfg.d_model)
     _moe_case(rt, unit_bf16, b, _oracle_ids(unit_bf16, b))
+
+
+@pytest.fixture(scope="module")
+def wide_model(rt, unit_bf16):
+    """The bf16 unit layer with room for 8192 rows per call."""
+    model = rt.Model(unit_bf16.inp, max_batch=16, max_tokens=512)
+    yield model
+    model.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [4096, 8192])
+def test_moe_unit_bf16_many_rows(rt, unit_bf16, wide_model, T):
+    """More rows than the one-workgroup routing permutation takes (2048): 256
+    and 512 pairs per expert in one routed launch -- the three-launch
+    permutation, the grouped gate/up and the grouped down."""
+    say(f"routed experts unit (bf16): {T} rows in one launch, routing from the oracle's router")
+    b = _normed_rows(700 + T, T, unit_bf16.cfg.d_model)
+    _moe_case(rt, unit_bf16, b, _oracle_ids(unit_bf16, b), model=wide_model)
 
 
 @pytest.mark.parametrize("T", [256, 1536])
