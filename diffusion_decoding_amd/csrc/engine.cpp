@@ -476,8 +476,9 @@ struct MixedSeg {
 
 // One block over the rows of a mixed batch (refine segments first, then
 // append segments): the dense projections and the experts run once over all
-// rows, attention once per segment in its own mode over its own cache; the
-// append segments' new keys and values go into their caches first.
+// rows, attention per segment in its own mode over its own cache (all
+// segments in one launch); the append segments' new keys and values go into
+// their caches first.
 int mixed_layer(dg_model* m, int l, const MixedSeg* sg, int n_segs, int T, int T_ref, hipStream_t st) {
   const dg_config& c = m->cfg;
   const int d = c.d_model, H = c.n_heads, dh = c.head_dim, A = H * dh;

@@ -526,14 +526,13 @@ __device__ __forceinline__ void attn_bf16_item(const AttnArgs& a, int item, int 
 
 // ---------------------------------------------------------------------------
 // bf16 path with 32-query waves (head_dim 64 or 128).  The same work items
-// (query tiles of 128, key splits, XCD order) and key tiles as above, but
-// each of the four waves holds 32 queries and computes with the 32x32x16
-// MFMA: S^T (32 keys x 32 queries per block) = K Q^T, O^T (32 dims x 32
-// queries per block) = V^T P^T.  A K or V fragment read from LDS then feeds
-// 32 queries instead of 16: four waves cover 128 queries with half the LDS
-// reads per query of eight 16-query waves, and a workgroup's 72 KB of LDS
-// lets two of them share a CU, where their phases (fragment reads, MFMAs,
-// softmax) are not tied together by barriers.
+// (query tiles, key splits, XCD order) and key tiles as above, but each wave
+// holds 32 queries and computes with the 32x32x16 MFMA: S^T (32 keys x 32
+// queries per block) = K Q^T, O^T (32 dims x 32 queries per block) =
+// V^T P^T.  A K or V fragment read from LDS then feeds 32 queries instead of
+// 16, and NWQ waves (eight in use: 256-query tiles) share each K/V tile
+// staged in LDS, so a tile's L2-to-LDS traffic serves four times the queries
+// of a 64-query tile.
 //
 // Layouts of the 32x32x16 MFMA (lane l, half hh = l / 32): an operand lane
 // supplies row or column l % 32 and k-slots 8 hh .. 8 hh + 7; a result lane
@@ -964,17 +963,18 @@ int launch_bf16_q32(const AttnArgs& a, hipStream_t st) {
   return int(hipGetLastError());
 }
 
-template <int DH, int NW>
-int launch_bf16_nw(const AttnArgs& a, hipStream_t st) {
+// 64-query tiles of four 16-query waves, one K/V tile in flight (two would
+// spill at four waves)
+template <int DH>
+int launch_bf16_q16(const AttnArgs& a, hipStream_t st) {
+  constexpr int NW = 4;
   const int total = a.len0 + a.len1;
   const int per = ((total + a.splits - 1) / a.splits + 63) / 64 * 64;
   const int n_qt = (a.n + 16 * NW - 1) / (16 * NW);
   const int items = a.B * a.H * a.splits * n_qt;
   const int per_xcd = (items + 7) / 8;
-  // eight-wave tiles keep two K/V tiles in flight (the four-wave kernel would
-  // spill at that depth)
   if (a.len1 == 0 || a.len0 % 64 == 0)  // no key tile spans both segments
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, NW == 8 ? 2 : 1, true, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, true, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
                        per_xcd);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, false, NW>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, a, per, n_qt,
@@ -986,9 +986,9 @@ template <int DH>
 int launch_bf16(const AttnArgs& a, hipStream_t st) {
   int e;
   if constexpr (DH >= 64)
-    e = attn_q32(a.n, a.len0 + a.len1, DH) ? launch_bf16_q32<DH, 8>(a, st) : launch_bf16_nw<DH, 4>(a, st);
+    e = attn_q32(a.n, a.len0 + a.len1, DH) ? launch_bf16_q32<DH, 8>(a, st) : launch_bf16_q16<DH>(a, st);
   else
-    e = launch_bf16_nw<DH, 4>(a, st);
+    e = launch_bf16_q16<DH>(a, st);
   if (e || a.splits == 1) return e;
   const long long n4 = (long long)a.B * a.H * a.n * (DH / 4);
   const dim3 g(unsigned((n4 + 255) / 256));
