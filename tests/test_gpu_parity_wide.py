@@ -235,6 +235,21 @@ def test_batch16_full_width_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_batch32_full_width_one_step(rt):
+    """Thirty-two canvases, the most rows a call takes (8192): the dense
+    projections on 256x256 tiles, 512 pairs per expert in one routed launch
+    (grouped gate/up and down), each canvas with its own 256-row prompt; a
+    short vocabulary keeps the oracle's LM head quick."""
+    cfg = get_config("c2").replace(name="c2_batch32_1_layer", n_layers=1, batch=32, prompt_len=256, vocab=8192)
+    say("batch 32 x 256 (8192 rows: 256x256 projection tiles, one routed launch), 1 layer, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_canvas512_full_width_one_step(rt):
     """A 512-position canvas at full width (the canvas-length variant): 512
     tokens take the large-M projection tiles, the attention two 256-query
