@@ -935,17 +935,20 @@ int launch(const AttnArgs& a, hipStream_t st) {
   return int(hipGetLastError());
 }
 
-// bf16 kernel shape: for long key ranges 256-query tiles of eight 32-query
-// waves (each K/V tile staged in LDS serves four times the queries of a
-// 64-query tile), otherwise 64-query tiles of four 16-query waves (four
-// times the workgroups).  Measured at 4 and 8 canvases x 256 queries x 8448
-// keys: 109 and 197 us per layer against 121 and 216 for 128-query tiles of
-// eight 16-query waves, 117 and 211 for 128-query tiles of four 32-query
-// waves; at one canvas x 2304 keys the 32-query waves lose (26.5 against
-// 24.1 us), too few workgroups.
-bool attn_q32(int n, int keys, int dh) { return keys >= 4096 && n >= 128 && dh >= 64; }
-int attn_tile_queries(int n, int keys, int dh) { return attn_q32(n, keys, dh) ? 256 : 64; }
-int attn_tile_waves(int n, int keys, int dh) { return attn_q32(n, keys, dh) ? 8 : 4; }
+// bf16 kernel shape: 256-query tiles of eight 32-query waves (each K/V tile
+// staged in LDS serves four times the queries of a 64-query tile) for long
+// key ranges or many canvas-heads, otherwise 64-query tiles of four 16-query
+// waves (four times the workgroups).  Measured, attention per layer: 4 and 8
+// canvases x 256 queries x 8448 keys 109 and 197 us against 121 and 216
+// (eight 16-query waves per 128-query tile) and 117 and 211 (four 32-query
+// waves); at 2304 keys, per step, 4 / 8 / 16 / 32 canvases 1.50 / 2.30 /
+// 3.61 / 6.87 ms against 1.60 / 2.51 / 4.80 / 8.99 ms for 64-query tiles;
+// one canvas x 2304 keys 26.5 against 24.1 us (too few workgroups).
+bool attn_q32(int B, int H, int n, int keys, int dh) {
+  return dh >= 64 && n >= 128 && (keys >= 4096 || B * H >= 64);
+}
+int attn_tile_queries(int B, int H, int n, int keys, int dh) { return attn_q32(B, H, n, keys, dh) ? 256 : 64; }
+int attn_tile_waves(int B, int H, int n, int keys, int dh) { return attn_q32(B, H, n, keys, dh) ? 8 : 4; }
 
 template <int DH, int NWQ>
 int launch_bf16_q32(const AttnArgs& a, hipStream_t st) {
@@ -986,7 +989,7 @@ template <int DH>
 int launch_bf16(const AttnArgs& a, hipStream_t st) {
   int e;
   if constexpr (DH >= 64)
-    e = attn_q32(a.n, a.len0 + a.len1, DH) ? launch_bf16_q32<DH, 8>(a, st) : launch_bf16_q16<DH>(a, st);
+    e = attn_q32(a.B, a.H, a.n, a.len0 + a.len1, DH) ? launch_bf16_q32<DH, 8>(a, st) : launch_bf16_q16<DH>(a, st);
   else
     e = launch_bf16_q16<DH>(a, st);
   if (e || a.splits == 1) return e;
@@ -1010,10 +1013,10 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
 // splits lose more to the merge and to each workgroup's first tile than they
 // gain in parallelism).
 int attn_splits_for(int B, int H, int n, int keys, int dh) {
-  const int qt = attn_tile_queries(n, keys, dh);
+  const int qt = attn_tile_queries(B, H, n, keys, dh);
   const int wgs = ((n + qt - 1) / qt) * B * H;
   int s = 1;
-  while (s < 16 && wgs * s * attn_tile_waves(n, keys, dh) < 2048 && keys / (s * 2) >= 512) s *= 2;
+  while (s < 16 && wgs * s * attn_tile_waves(B, H, n, keys, dh) < 2048 && keys / (s * 2) >= 512) s *= 2;
   return s;
 }
 

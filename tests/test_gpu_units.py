@@ -123,13 +123,15 @@ def _bf16_normal(seed, shape):
     return round_bf16(np.random.default_rng(seed).standard_normal(shape))
 
 
-# 4096 keys and more with 128 queries or more take the 32-query-wave kernel
-# (256-query tiles): batch 4 at 8192, a ragged batch 2 whose cache length
-# splits a key tile between cache and canvas rows and whose second query tile
-# is part empty, and causal commit passes into long caches.
+# 4096 keys and more, or 64 canvas-heads and more, with 128 queries or more
+# take the 32-query-wave kernel (256-query tiles): batch 4 at 8192 and at
+# 1024 cache rows, a ragged batch 2 whose cache length splits a key tile
+# between cache and canvas rows and whose second query tile is part empty,
+# causal commit passes into long caches and a causal batch-4 pass.
 @pytest.mark.parametrize("B,P,n,causal", [(1, 1024, 256, False), (4, 8192, 256, False), (1, 300, 200, False),
                                           (1, 512, 256, True), (2, 70, 200, True), (2, 4200, 300, False),
-                                          (1, 4000, 256, True), (1, 4100, 200, True)])
+                                          (1, 4000, 256, True), (1, 4100, 200, True), (4, 1000, 256, False),
+                                          (4, 300, 256, True)])
 def test_attention_unit(rt, unit_bf16, B, P, n, causal):
     u, cfg = unit_bf16, unit_bf16.cfg
     H, dh = cfg.n_heads, cfg.head_dim
