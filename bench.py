@@ -45,11 +45,11 @@ def router_in_shared(cfg) -> bool:
     """Whether the library computes the router logits inside the shared
     gate/up launch: bf16 activations and shared weights (bf16 or mxfp4
     workloads: the latter keep a bf16 shared expert), K = d_model = 2048, at
-    most 384 tokens, d_shared >= 1024 (the direct-load kernel's small-M SwiGLU
+    most 512 tokens, d_shared >= 1024 (the direct-load kernel's small-M SwiGLU
     shape)."""
     T = cfg.batch * cfg.canvas_len
     return (cfg.act_dtype == "bf16" and cfg.expert_dtype in ("bf16", "mxfp4") and cfg.d_model == 2048
-            and T <= 384 and cfg.d_shared >= 1024)
+            and T <= 512 and cfg.d_shared >= 1024)
 
 
 def topk_in_shared(cfg) -> bool:

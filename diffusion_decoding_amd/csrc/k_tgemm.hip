@@ -746,11 +746,15 @@ int launch_kg(const GemmArgs& g, hipStream_t st, int kg_max) {
 // took 19.3 us against 26.6 us and the shared gate/up (4096 weight rows)
 // 14.5 against 17.7 us; at M = 1024 the QKV 38.7 against 67.7, the shared
 // gate/up 25.8 against 44.3 and the N = 2048 projections 19.0 against 24.2.
-// At M <= 384 the N = 2048 projections gain nothing and stay on the
-// register-staged kernel.  Returns -1 when the shape is not covered.
+// The small-M tiles (64 rows) run up to 512 rows: one 512-position canvas or
+// two canvases of 256 took 11.76 / 11.13 ms per step against 12.40 / 11.77
+// with the large-M tiles (the 128x256 QKV tiles give only 96 workgroups
+// there); at 768 rows the large tiles win (13.22 against 13.40 ms).
+// Returns -1 when the shape is not covered.
+constexpr int SMALL_M = 512;
 int dense_direct(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   if (g.K != 2048 || g.lda % 8 || g.ldb % 8 || g.N < 1024) return -1;
-  const bool small = g.M <= 384;
+  const bool small = g.M <= SMALL_M;
   if (g.B2 && !(epi == EPI_SWIGLU && small)) return -1;
   // above 4096 rows (batches of 32 canvases): the LM head's 256x256 tiles,
   // which move a third to two thirds fewer bytes per CU than the tiles below
@@ -1049,7 +1053,7 @@ int launch_grouped(const bf16* X, const int* pair_row, const int* off, int E, in
 
 int gemm_f32_topk(const GemmArgs& g, hipStream_t st) {
   constexpr int BM = 64, BN = 32, NWV = 4;
-  if (g.K != 2048 || g.lda % 8 || g.ldb % 8 || g.N < 1024 || g.M > 384 || g.B2) return -1;
+  if (g.K != 2048 || g.lda % 8 || g.ldb % 8 || g.N < 1024 || g.M > SMALL_M || g.B2) return -1;
   if (!g.tk_logits || g.tk_T <= 0 || g.tk_E > 128 || g.tk_k > 8 || g.tk_k > g.tk_E) return -1;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int per_xcd = (tiles_m * tiles_n + 7) / 8;

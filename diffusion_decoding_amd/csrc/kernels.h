@@ -69,7 +69,7 @@ struct GemmArgs {
 
 // Returns 0 or a HIP error code.
 int gemm(ActType at, WType wt, GemmEpi epi, const GemmArgs& g, int groups, hipStream_t st);
-// EPI_F32 product (bf16 A and B, K = 2048, M <= 384, N >= 1024) with the
+// EPI_F32 product (bf16 A and B, K = 2048, M <= 512, N >= 1024) with the
 // router top-k of g.tk_* in the same launch, on workgroups of their own that
 // run beside the product's tiles.  Returns -1 (nothing launched) when the
 // shape is not covered (also tk_E > 128 or tk_k > 8), else 0 or a HIP error.

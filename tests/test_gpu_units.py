@@ -254,7 +254,7 @@ def _shared_case(rt, u, T):
     say(f"   shared down within {ratio:.2e} of the bound")
 
 
-@pytest.mark.parametrize("T", [256, 1024])
+@pytest.mark.parametrize("T", [256, 512, 1024])
 def test_shared_unit_bf16(rt, unit_bf16, T):
     say(f"shared expert unit (bf16): {T} rows")
     _shared_case(rt, unit_bf16, T)
