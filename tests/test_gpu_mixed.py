@@ -261,6 +261,32 @@ def test_mixed_full_width_bf16(rt):
     assert_reports(cfg.replace(batch=1), reps)
 
 
+def test_mixed_full_width_bf16_tall_segments(rt):
+    """Four segments of 150 rows or more in one attention launch: three refine
+    canvases of 200 against 300-, 0- and 500-row caches (300: a key tile spans
+    cache and canvas rows) and a 150-token prompt read into a 120-row cache,
+    750 rows a pass (large-M projection tiles), two passes.  (256-query tiles
+    of 32-query waves, which win for a batch of canvases, measured 1.4 %
+    slower here and are not used for segment tables.)"""
+    cfg = tiny_config(name="wide_mixed_tall", n_layers=1, d_model=2048, n_heads=16, head_dim=128, n_experts=16,
+                      top_k=4, d_expert=96, d_shared=2048, vocab=8192, canvas_len=200, max_steps=4,
+                      prompt_len=500, batch=4, act_dtype="bf16", expert_dtype="bf16", seed=31, lm_scale=1.0)
+    say("mixed batch, tall segments: refine (P=300) | refine (P=0) | append 150 (P=120) | refine (P=500)")
+    mix = Mix(rt, cfg, max_batch=3, max_tokens=800, kv_capacity=500 + 2 * 200)
+    r0, r1 = Request(mix, 0, 300, seed=7), Request(mix, 1, 0, seed=8, block=1)
+    a2, r3 = Request(mix, 2, 120), Request(mix, 3, 500, seed=9, block=3)
+    rng = np.random.default_rng(5)
+    reps = []
+    for p in range(2):
+        say(f"  pass {p}")
+        plan = [(r0, None), (r1, None), (a2, rng.integers(0, cfg.vocab, 150)), (r3, None)]
+        reps += mix.run_pass(plan, 1e-2)
+    mix.close()
+    del mix
+    _free()
+    assert_reports(cfg.replace(batch=1), reps)
+
+
 @pytest.mark.parametrize("act,n_append", [("fp32", 1100), ("bf16", 2100)])
 def test_mixed_beyond_one_routed_launch(rt, act, n_append):
     """More rows than one routed-expert launch takes (1024 fp32, 2048 bf16):
