@@ -228,7 +228,7 @@ AttnArgs attn_args(const dg_model* m, int l, const void* q, const dg_kv* kv, int
     aa.k1 = nullptr; aa.v1 = nullptr; aa.s1_bh = 0; aa.len1 = 0;
     aa.causal_base = P;
   }
-  aa.splits = std::min(m->attn_max_splits, attn_splits_for(B, H, n, aa.len0 + aa.len1, dh));
+  aa.splits = std::min(m->attn_max_splits, attn_splits_for(m->at, B, H, n, aa.len0 + aa.len1, dh));
   return aa;
 }
 

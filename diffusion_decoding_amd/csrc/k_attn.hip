@@ -13,9 +13,10 @@
 // P*V MFMA straight from the accumulator registers as its B operand
 // (O^T = V^T P^T).  Key ranges are split across workgroups when the head/query
 // grid alone cannot fill the chip; a merge kernel combines the partials.
-// Long key ranges (batched canvases over long prompts) take a second bf16
-// kernel with 32-query waves on the 32x32x16 MFMA and 256-query workgroups,
-// which stage each K/V tile once for four times the queries.
+// Most bf16 problems take a second kernel with 32-query waves on the
+// 32x32x16 MFMA, in 256-query workgroups (long key ranges, batched canvases)
+// or 128-query ones (one canvas over a long enough prompt), which stage each
+// K/V tile once for four or two times the queries.
 #include <algorithm>
 #include <type_traits>
 
@@ -935,20 +936,29 @@ int launch(const AttnArgs& a, hipStream_t st) {
   return int(hipGetLastError());
 }
 
-// bf16 kernel shape: 256-query tiles of eight 32-query waves (each K/V tile
-// staged in LDS serves four times the queries of a 64-query tile) for long
-// key ranges or many canvas-heads, otherwise 64-query tiles of four 16-query
-// waves (four times the workgroups).  Measured, attention per layer: 4 and 8
-// canvases x 256 queries x 8448 keys 109 and 197 us against 121 and 216
-// (eight 16-query waves per 128-query tile) and 117 and 211 (four 32-query
-// waves); at 2304 keys, per step, 4 / 8 / 16 / 32 canvases 1.50 / 2.30 /
-// 3.61 / 6.87 ms against 1.60 / 2.51 / 4.80 / 8.99 ms for 64-query tiles;
-// one canvas x 2304 keys 26.5 against 24.1 us (too few workgroups).
-bool attn_q32(int B, int H, int n, int keys, int dh) {
-  return dh >= 64 && n >= 128 && (keys >= 4096 || B * H >= 64);
+// bf16 kernel shape, as queries per workgroup tile: 256 (eight 32-query
+// waves; each K/V tile staged in LDS serves four times the queries of a
+// 64-query tile) for long key ranges or many canvas-heads; 128 (four 32-query
+// waves) when a grid of one workgroup per CU still leaves every key split 256
+// keys or more; else 64 (four 16-query waves).  Measured, attention + merge
+// per layer: 4 and 8 canvases x 256 queries x 8448 keys 109 and 197 us with
+// 256-query tiles against 121 and 216 (eight 16-query waves per 128-query
+// tile) and 117 and 211 (128-query tiles); at 2304 keys, per step, 4 / 8 /
+// 16 / 32 canvases 1.50 / 2.30 / 3.61 / 6.87 ms against 1.60 / 2.51 / 4.80 /
+// 8.99 ms for 64-query tiles.  One canvas x 2304 keys (8 splits of 288 keys)
+// 16.3 + 4.6 us against 18.1 + 4.1 with 64-query tiles (4 splits) and 21.6 +
+// 4.6 with 256-query tiles; one 512-query canvas x 2560 keys 25.0 + 4.5
+// against 27.1 + 4.5; one canvas x 1280 keys keeps 64-query tiles (4 splits:
+// 13.9 + 4.2 us against 14.4 + 5.1 for 128-query tiles over 8 splits).
+int attn_tile_queries(int B, int H, int n, int keys, int dh) {
+  if (dh < 64 || n < 128) return 64;
+  if (keys >= 4096 || B * H >= 64) return 256;
+  const int wgs = ((n + 127) / 128) * B * H;
+  int s = 1;
+  while (s < 8 && wgs * s < 256) s *= 2;
+  return keys / s >= 256 ? 128 : 64;
 }
-int attn_tile_queries(int B, int H, int n, int keys, int dh) { return attn_q32(B, H, n, keys, dh) ? 256 : 64; }
-int attn_tile_waves(int B, int H, int n, int keys, int dh) { return attn_q32(B, H, n, keys, dh) ? 8 : 4; }
+int attn_tile_waves(int tile_queries) { return tile_queries == 256 ? 8 : 4; }
 
 template <int DH, int NWQ>
 int launch_bf16_q32(const AttnArgs& a, hipStream_t st) {
@@ -989,7 +999,11 @@ template <int DH>
 int launch_bf16(const AttnArgs& a, hipStream_t st) {
   int e;
   if constexpr (DH >= 64)
-    e = attn_q32(a.B, a.H, a.n, a.len0 + a.len1, DH) ? launch_bf16_q32<DH, 8>(a, st) : launch_bf16_q16<DH>(a, st);
+    switch (attn_tile_queries(a.B, a.H, a.n, a.len0 + a.len1, DH)) {
+      case 256: e = launch_bf16_q32<DH, 8>(a, st); break;
+      case 128: e = launch_bf16_q32<DH, 4>(a, st); break;
+      default: e = launch_bf16_q16<DH>(a, st);
+    }
   else
     e = launch_bf16_q16<DH>(a, st);
   if (e || a.splits == 1) return e;
@@ -1007,16 +1021,25 @@ int launch_bf16(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Key splits: double while the grid is under 2048 waves (two four-wave or
+// Key splits (bf16): double while the grid is under one workgroup per CU and
+// each split keeps at least 128 keys, or under 2048 waves (two four-wave or
 // one eight-wave workgroup per CU) and each split keeps at least 512 keys
-// (measured at 256 queries x 16 heads: 4 splits for 2304 keys; shorter
-// splits lose more to the merge and to each workgroup's first tile than they
-// gain in parallelism).
-int attn_splits_for(int B, int H, int n, int keys, int dh) {
+// (shorter splits lose more to the merge and to each workgroup's first tile
+// than they gain in parallelism; one canvas x 1280 keys: 4 splits 13.9 + 4.2
+// us, 2 splits 19.5 + 4.2).  The fp32 kernel keeps the second rule alone.
+int attn_splits_for(ActType at, int B, int H, int n, int keys, int dh) {
+  if (at != ACT_BF16) {
+    const bool wide = dh >= 64 && n >= 128 && (keys >= 4096 || B * H >= 64);
+    const int wgs = ((n + (wide ? 255 : 63)) / (wide ? 256 : 64)) * B * H;
+    int s = 1;
+    while (s < 16 && wgs * s * (wide ? 8 : 4) < 2048 && keys / (s * 2) >= 512) s *= 2;
+    return s;
+  }
   const int qt = attn_tile_queries(B, H, n, keys, dh);
-  const int wgs = ((n + qt - 1) / qt) * B * H;
+  const int wgs = ((n + qt - 1) / qt) * B * H, waves = attn_tile_waves(qt);
   int s = 1;
-  while (s < 16 && wgs * s * attn_tile_waves(B, H, n, keys, dh) < 2048 && keys / (s * 2) >= 512) s *= 2;
+  while (s < 16 && ((wgs * s < 256 && keys / (s * 2) >= 128) || (wgs * s * waves < 2048 && keys / (s * 2) >= 512)))
+    s *= 2;
   return s;
 }
 

@@ -145,7 +145,7 @@ struct AttnArgs {
   int splits;
 };
 int attention(ActType at, const AttnArgs& a, hipStream_t st);
-int attn_splits_for(int B, int H, int n, int keys, int dh);
+int attn_splits_for(ActType at, int B, int H, int n, int keys, int dh);
 // Up to ATTN_MAX_SEGS problems (same head_dim) in one launch plus one merge
 // launch, bf16 only.  Sets each problem's splits and partial pointers
 // (packed from part_o / part_ml; room for max_splits x all their rows).

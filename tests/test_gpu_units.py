@@ -124,14 +124,19 @@ def _bf16_normal(seed, shape):
 
 
 # 4096 keys and more, or 64 canvas-heads and more, with 128 queries or more
-# take the 32-query-wave kernel (256-query tiles): batch 4 at 8192 and at
+# take the 32-query-wave kernel in 256-query tiles: batch 4 at 8192 and at
 # 1024 cache rows, a ragged batch 2 whose cache length splits a key tile
 # between cache and canvas rows and whose second query tile is part empty,
-# causal commit passes into long caches and a causal batch-4 pass.
+# causal commit passes into long caches and a causal batch-4 pass.  Fewer
+# canvas-heads over 2048 keys or so take it in 128-query tiles with 4-8 key
+# splits: one canvas over 2048 cache rows, a ragged 300-query canvas over a
+# cache length that splits a key tile, a causal pass into 2000 rows and two
+# canvases over 1500 rows.  Short ranges keep the 16-query waves.
 @pytest.mark.parametrize("B,P,n,causal", [(1, 1024, 256, False), (4, 8192, 256, False), (1, 300, 200, False),
                                           (1, 512, 256, True), (2, 70, 200, True), (2, 4200, 300, False),
                                           (1, 4000, 256, True), (1, 4100, 200, True), (4, 1000, 256, False),
-                                          (4, 300, 256, True)])
+                                          (4, 300, 256, True), (1, 2048, 256, False), (1, 2100, 300, False),
+                                          (1, 2000, 256, True), (2, 1500, 256, False)])
 def test_attention_unit(rt, unit_bf16, B, P, n, causal):
     u, cfg = unit_bf16, unit_bf16.cfg
     H, dh = cfg.n_heads, cfg.head_dim
