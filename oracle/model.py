@@ -53,7 +53,7 @@ import numpy as np
 import torch
 
 from . import philox
-from .numerics import decode_e4m3fn, decode_mxfp4, round_bf16, round_fp32
+from .numerics import decode_e4m3fn, decode_mxfp4, round_bf16, round_fp32, round_mxfp8
 
 
 # ----------------------------------------------------------------------------- precision
@@ -136,7 +136,7 @@ class Weights:
         lw = self.inp.layers[l]
 
         def load():
-            if self.cfg.expert_dtype == "mxfp4":
+            if self.cfg.expert_dtype in ("mxfp4", "mxfp4_a8"):
                 host = lambda t: t.detach().to("cpu").numpy()
                 return (decode_mxfp4(host(lw["w_gu"][e]), host(lw["s_gu"][e])),
                         decode_mxfp4(host(lw["w_d"][e]), host(lw["s_d"][e])))
@@ -246,16 +246,22 @@ def route(r32: np.ndarray, k: int):
 
 
 def moe(b: np.ndarray, W: Weights, l: int, prec: Prec, k: int, E: int):
-    """Routed experts plus the shared expert, summed in float64."""
+    """Routed experts plus the shared expert, summed in float64.
+
+    With MXFP4 x MXFP8 experts the routed gate/up reads each token row as
+    MXFP8 (E4M3 elements, one E8M0 scale per 32 along d_model); the down
+    projection and the shared expert read their inputs as they are.
+    """
     r32 = round_fp32(b @ W.dense(l, "wr").T)
     ids, w = route(r32, k)
     out = np.zeros_like(b)
+    bq = round_mxfp8(b) if W.cfg.expert_dtype == "mxfp4_a8" else b
     for e in range(E):
         rows, slot = np.nonzero(ids == e)
         if rows.size == 0:
             continue
         w_gu, w_d = W.expert(l, e)
-        out[rows] += w[rows, slot][:, None] * swiglu(b[rows], w_gu, w_d, prec)
+        out[rows] += w[rows, slot][:, None] * swiglu(bq[rows], w_gu, w_d, prec)
     out += swiglu(b, W.dense(l, "ws_gu"), W.dense(l, "ws_d"), prec)
     return out, ids, w, r32
 

@@ -16,6 +16,14 @@ byte, the element with the even index in the low nibble (the format fixes
 no byte packing; this is the reading taken).  This is the MI355X counterpart
 of the 4-bit expert weights the pages name (DiffusionGemma深度拆解
 (zhichai.net), "MoE 效率：128 专家，8 活跃").
+
+MXFP8 activations (the same MX specification, its conversion of a block of
+32 values to a scaled format): the shared exponent is floor(log2(max |v|))
+minus the element format's largest exponent (8 for E4M3: 448 = 1.75 * 2^8),
+kept in the E8M0 range [-127, 127]; an all-zero block takes code 0.  Each
+element v / 2^shared is rounded to E4M3FN, to nearest with ties to even, and
+magnitudes past 448 are clamped to 448 (the largest normal; the format has no
+infinity).  Used for the routed gate/up inputs of the MXFP4 x MXFP8 variant.
 """
 from __future__ import annotations
 
@@ -102,3 +110,40 @@ def decode_mxfp4(packed, scales) -> np.ndarray:
     v = _E2M1[unpack_fp4(packed)]
     s = decode_e8m0(scales)
     return v * np.repeat(s, 32, axis=-1)
+
+
+_E4M3_CODE = {float(v): c for c, v in enumerate(_E4M3[:127]) if np.isfinite(v)}   # non-negative finite values
+
+
+def round_e4m3(y) -> np.ndarray:
+    """Round float64 values to E4M3FN values: nearest, ties to even mantissa,
+    magnitudes above 448 clamped to 448."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), 448.0)
+    _, e = np.frexp(a)                          # a = f 2^e, 0.5 <= f < 1: floor(log2 a) = e - 1
+    step = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)   # 3 mantissa bits; subnormal spacing 2^-9
+    return np.copysign(np.rint(a / step) * step, y)
+
+
+def quantize_mxfp8(x):
+    """float64 [..., K] (K % 32 == 0) -> (E4M3FN codes uint8 [..., K],
+    E8M0 shared-exponent codes uint8 [..., K / 32])."""
+    x = np.asarray(x, dtype=np.float64)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    _, e = np.frexp(amax)
+    scode = np.where(amax > 0, np.clip(e - 1 - 8 + 127, 0, 254), 0).astype(np.int64)
+    q = round_e4m3(blk * np.ldexp(1.0, 127 - scode)[..., None])
+    mag = np.vectorize(_E4M3_CODE.__getitem__, otypes=[np.int64])(np.abs(q))
+    codes = np.where(np.signbit(q), mag | 0x80, mag).astype(np.uint8)
+    return codes.reshape(x.shape), scode.astype(np.uint8)
+
+
+def decode_mxfp8(codes, scales) -> np.ndarray:
+    """MXFP8 codes [..., K] with E8M0 scales [..., K/32] -> float64 [..., K]."""
+    return decode_e4m3fn(codes) * np.repeat(decode_e8m0(scales), 32, axis=-1)
+
+
+def round_mxfp8(x) -> np.ndarray:
+    """The MXFP8 value of each element of x [..., K] (float64)."""
+    return decode_mxfp8(*quantize_mxfp8(x))

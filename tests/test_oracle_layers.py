@@ -225,6 +225,42 @@ def test_fp8_expert_dequant_matches_torch():
     np.testing.assert_array_equal(got, ref.numpy())
 
 
+def test_moe_mxfp8_inputs_reach_only_the_routed_gate_up():
+    """MXFP4 x MXFP8 experts: the routed gate/up reads its token rows as MXFP8
+    values, nothing else does.  (1) Rows already on the MXFP8 grid give the
+    MXFP4 result exactly (the SwiGLU products entering the down projection are
+    off the grid, so quantizing them would show); (2) with zero routed
+    weights the shared expert alone gives the MXFP4 result on rows off the
+    grid; (3) with one expert and a zero shared expert, raw rows give the
+    MXFP4 result of the quantized rows, and not of the raw ones."""
+    from oracle.numerics import round_mxfp8
+    prec = om.Prec("bf16")
+
+    def pair(**kw):
+        ws = []
+        for edt in ("mxfp4_a8", "mxfp4"):
+            inp = make_inputs(tiny_config(act_dtype="bf16", expert_dtype=edt, **kw))
+            ws.append(inp)
+        return ws
+
+    a8, f4 = pair()
+    cfg = a8.cfg
+    b = om.round_bf16(RNG.standard_normal((12, cfg.d_model)))
+    bq = round_mxfp8(b)
+    assert not np.array_equal(bq, b)
+    run = lambda inp, x: om.moe(x, om.Weights(inp), 0, prec, cfg.top_k, cfg.n_experts)[0]
+    np.testing.assert_array_equal(run(a8, bq), run(f4, bq))
+    for inp in (a8, f4):
+        inp.layers[0]["w_gu"].zero_()
+    np.testing.assert_array_equal(run(a8, b), run(f4, b))
+    a8, f4 = pair(n_experts=1, top_k=1)
+    for inp in (a8, f4):
+        inp.layers[0]["ws_gu"].zero_()
+    one = lambda inp, x: om.moe(x, om.Weights(inp), 0, prec, 1, 1)[0]
+    np.testing.assert_array_equal(one(a8, b), one(f4, bq))
+    assert not np.allclose(one(a8, b), one(f4, b), rtol=1e-6, atol=0)
+
+
 def test_block_matches_torch_functional_composition():
     """One whole block against an independent composition of torch library ops:
     F.linear fixes the [out][in] weight orientation, SDPA fixes attention, the

@@ -118,3 +118,106 @@ def test_mxfp4_quantize_then_decode():
     # the largest element of every nonzero block uses the top binade (|code value| >= 4)
     blocks = np.abs(dq).reshape(16, 64, 32).max(-1) / 2.0 ** (s.numpy().astype(np.float64) - 127)
     assert np.all((blocks[s.numpy() > 0] >= 4.0))
+
+
+# ----------------------------------------------------------------------------- MXFP8 activations
+
+def _e4m3_nearest_brute_force(y: float) -> float:
+    """Nearest finite E4M3FN value to y clamped to +-448, by a scan of the 254
+    finite codes; on a tie the code with the even mantissa (low bit 0)."""
+    from oracle.numerics import e4m3fn_table
+    t = e4m3fn_table()
+    yc = min(max(y, -448.0), 448.0)
+    best = None
+    for code in range(256):
+        v = t[code]
+        if not np.isfinite(v) or (code & 0x80) != (0x80 if np.signbit(yc) else 0):
+            continue
+        d = abs(v - yc)
+        key = (d, code & 1)
+        if best is None or key < best[0]:
+            best = (key, v)
+    return best[1]
+
+
+def test_e4m3_rounding_matches_a_scan_of_the_code_table():
+    """Every bfloat16 value in [-600, 600] (and the tiny ones around the
+    subnormal grid) rounds to the nearest E4M3FN value, ties to the even
+    mantissa, clamped at 448."""
+    from oracle.numerics import round_e4m3
+    bits = np.arange(0, 1 << 16, dtype=np.uint32) << 16
+    ys = bits.view(np.float32).astype(np.float64)
+    ys = ys[np.isfinite(ys) & (np.abs(ys) <= 600) & ((np.abs(ys) >= 2.0 ** -12) | (ys == 0))]
+    ys = ys[:: max(1, ys.size // 6000)]        # about 6000 values spread over the range
+    got = round_e4m3(ys)
+    ref = np.array([_e4m3_nearest_brute_force(float(y)) for y in ys])
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_rounding_ties_subnormals_and_saturation():
+    from oracle.numerics import round_e4m3
+    # halfway cases go to the even mantissa: 1 + 1/16 -> 1, 1 + 3/16 -> 1.25
+    assert round_e4m3(1.0625) == 1.0 and round_e4m3(1.1875) == 1.25
+    # subnormal grid 2^-9: 2^-10 is a tie between 0 and 2^-9 (to 0); 1.5 * 2^-10 rounds up
+    assert round_e4m3(2.0 ** -10) == 0.0 and round_e4m3(1.5 * 2.0 ** -10) == 2.0 ** -9
+    # 448 is the largest finite value; beyond it the value is clamped
+    assert round_e4m3(460.0) == 448.0 and round_e4m3(-511.0) == -448.0
+    assert np.signbit(round_e4m3(-1e-9)) and round_e4m3(-1e-9) == 0.0
+
+
+def test_e4m3_rounding_matches_torch_inside_the_range():
+    """torch's float8_e4m3fn cast (round to nearest even) on values within
+    +-448, a library cross-check of the same rounding."""
+    from oracle.numerics import round_e4m3
+    g = np.random.default_rng(7)
+    y = np.concatenate([g.standard_normal(20000) * s for s in (1e-3, 0.1, 1.0, 30.0)])
+    y = np.clip(y, -448.0, 448.0).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_e4m3(y), ref)
+
+
+def test_mxfp8_block_scale_is_the_largest_exponent_less_eight():
+    """The shared exponent of a block is floor(log2(max |v|)) - 8, so the
+    largest element lands in [256, 512) before rounding: 2^k maps to 256
+    exactly, 1.9 * 2^k to 486.4, clamped to 448; an all-zero block takes
+    code 0; each block of 32 gets its own scale."""
+    from oracle.numerics import quantize_mxfp8, decode_mxfp8, decode_e4m3fn
+    x = np.zeros((2, 64))
+    x[0, 5] = 2.0 ** 3
+    x[0, 40] = -1.9 * 2.0 ** -2
+    x[0, 41] = 2.0 ** -2
+    codes, scales = quantize_mxfp8(x)
+    assert scales.tolist() == [[127 + 3 - 8, 127 - 2 - 8], [0, 0]]
+    assert decode_e4m3fn(codes[0, 5]) == 256.0
+    assert decode_e4m3fn(codes[0, 40]) == -448.0 and decode_e4m3fn(codes[0, 41]) == 256.0
+    assert not codes[1].any()
+    v = decode_mxfp8(codes, scales)
+    assert v[0, 5] == 8.0 and v[0, 40] == -448.0 * 2.0 ** -10 and v[0, 41] == 0.25
+
+
+def test_mxfp8_round_trip_and_error_bound():
+    """Values on a block's grid come back exactly; random bfloat16 rows come
+    back within half a step of the E4M3 grid: at most 2^-4 of the scaled
+    element from 2^-6 to 448, an absolute 2^-10 of the scale below 2^-6, and
+    the clamp to 448 above it (the block's largest element can map to
+    [448, 512))."""
+    from oracle.numerics import quantize_mxfp8, decode_mxfp8, round_bf16, e4m3fn_table
+    g = np.random.default_rng(11)
+    finite = e4m3fn_table()
+    finite = finite[np.isfinite(finite)]
+    grid = g.choice(finite, size=(4, 64)) * 2.0 ** -5
+    grid[:, ::32] = 448.0 * 2.0 ** -5          # fixes every block's scale at 2^-5
+    c, s = quantize_mxfp8(grid)
+    np.testing.assert_array_equal(decode_mxfp8(c, s), grid)
+    x = round_bf16(g.standard_normal((8, 256)) * np.exp(g.uniform(-3, 3, (8, 1))))
+    c, s = quantize_mxfp8(x)
+    v = decode_mxfp8(c, s)
+    X = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=-1)
+    y = np.abs(x) / X
+    err = np.abs(v - x) / X
+    normal = (y >= 2.0 ** -6) & (y <= 448.0)
+    assert np.all(err[normal] <= 2.0 ** -4 * y[normal])
+    assert np.all(err[y < 2.0 ** -6] <= 2.0 ** -10)
+    big = y > 448.0
+    np.testing.assert_array_equal(np.abs(v[big]) / X[big], 448.0)
+    assert big.any()

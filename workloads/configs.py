@@ -31,7 +31,7 @@ class Config:
     prompt_len: int          # tokens already in the KV cache (random K,V) or prompt tokens (encoded)
     batch: int
     act_dtype: str           # "fp32" or "bf16"
-    expert_dtype: str        # "fp32", "bf16", "fp8" (routed and shared) or "mxfp4" (routed; shared bf16)
+    expert_dtype: str        # "fp32", "bf16", "fp8" (routed and shared), "mxfp4" or "mxfp4_a8" (routed; shared bf16)
     seed: int
     lm_scale: float = 1.0    # multiplies the N(0, 1/d) LM-head draw
     rope_theta: float = 1.0e4
@@ -90,10 +90,13 @@ _C5 = _C3.replace(name="c5_batch8_p8192_bf16", batch=8, seed=5)
 # E8M0 scale per 32 weights; the pages' 4-bit experts are NVFP4 on NVIDIA
 # parts -- DiffusionGemma深度拆解 (zhichai.net), "MoE 效率"), shared expert bf16
 _C6 = _C2.replace(name="c6_loop30_mxfp4", expert_dtype="mxfp4", seed=6)
+# the same weights with the routed gate/up inputs in MXFP8 (E4M3 elements, one
+# E8M0 scale per 32), for gfx950's scaled MFMA on 4-bit x 8-bit operands
+_C7 = _C6.replace(name="c7_loop30_mxfp4_a8", expert_dtype="mxfp4_a8")
 
-CONFIGS = {c.name: c for c in (_C0, _C1, _C2, _C3, _C4, _C5, _C6)}
+CONFIGS = {c.name: c for c in (_C0, _C1, _C2, _C3, _C4, _C5, _C6, _C7)}
 _ALIASES = {"c0": _C0.name, "c1": _C1.name, "c2": _C2.name, "c3": _C3.name, "c4": _C4.name,
-            "c5": _C5.name, "c6": _C6.name}
+            "c5": _C5.name, "c6": _C6.name, "c7": _C7.name}
 
 
 def get_config(name: str) -> Config:

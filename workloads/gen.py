@@ -24,7 +24,8 @@ e = floor(log2(max|block|)) - 2 (2 is the largest E2M1 exponent), stored as the
 E8M0 code e + 127 (an all-zero block gets code 0), and each weight becomes the
 E2M1 code nearest to w / 2^e (ties to the even mantissa, magnitudes above 6
 saturate); two codes per byte, the even element in the low nibble.  The shared
-expert stays bf16 in mxfp4 workloads.
+expert stays bf16 in mxfp4 workloads.  mxfp4_a8 workloads draw the same
+weights as mxfp4 ones (their activations differ only inside the kernels).
 """
 from __future__ import annotations
 
@@ -116,13 +117,13 @@ class Inputs:
 def _expert_tensor(shape, fan_in, cfg, device, ordinal, dtype, routed=True):
     """Returns (weights, scales-or-None) in the expert storage format."""
     std = fan_in ** -0.5
-    if cfg.expert_dtype == "mxfp4" and routed:
+    if cfg.expert_dtype in ("mxfp4", "mxfp4_a8") and routed:
         g = _gen(device, cfg.seed, ordinal)
         w32 = torch.randn(*shape, generator=g, device=device, dtype=torch.float32).mul_(std)
         q, s = quantize_mxfp4_rows(w32)
         del w32
         return q, s
-    if cfg.expert_dtype == "mxfp4":
+    if cfg.expert_dtype in ("mxfp4", "mxfp4_a8"):
         return _normal(shape, std, device, cfg.seed, ordinal, dtype), None
     if cfg.expert_dtype == "fp8":
         g = _gen(device, cfg.seed, ordinal)
