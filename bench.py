@@ -48,7 +48,7 @@ def router_in_shared(cfg) -> bool:
     most 512 tokens, d_shared >= 1024 (the direct-load kernel's small-M SwiGLU
     shape)."""
     T = cfg.batch * cfg.canvas_len
-    return (cfg.act_dtype == "bf16" and cfg.expert_dtype in ("bf16", "mxfp4") and cfg.d_model == 2048
+    return (cfg.act_dtype == "bf16" and cfg.expert_dtype in ("bf16", "mxfp4", "mxfp4_a8") and cfg.d_model == 2048
             and T <= 512 and cfg.d_shared >= 1024)
 
 
@@ -72,7 +72,7 @@ def algorithmic(cfg, kernel: str):
     def routed_bytes(rows, K):  # one expert matrix [rows][K] in its storage format, scales included
         if cfg.expert_dtype == "fp8":
             return rows * K + rows * 4
-        if cfg.expert_dtype == "mxfp4":
+        if cfg.expert_dtype in ("mxfp4", "mxfp4_a8"):
             return rows * K // 2 + rows * K // 32
         return rows * K * ab
     wb = 1 if cfg.expert_dtype == "fp8" else 2   # shared expert (bf16 in mxfp4 workloads)
@@ -572,6 +572,8 @@ def main():
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
         # MXFP4 routed experts (E2M1 codes + E8M0 block scales), same shapes as the headline
         out["mxfp4"] = time_loop(get_config("c6"), canvases=1, warmup=1, kernels=("moe_gateup", "moe_down"))
+        # the same MXFP4 weights with MXFP8 token rows into the routed gate/up (gfx950 scaled MFMA)
+        out["mxfp4_a8"] = time_loop(get_config("c7"), canvases=1, warmup=1, kernels=("moe_gateup", "moe_down"))
         # self-conditioning: each step after the first adds the previous step's predictions to the input
         out["self_condition"] = time_loop(c2.replace(name="c2_self_condition", self_condition=True),
                                           canvases=1, warmup=1)

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdg.so")
 
 DG_DTYPE_FP32, DG_DTYPE_BF16, DG_DTYPE_FP8_E4M3, DG_DTYPE_MXFP4, DG_DTYPE_E8M0 = 0, 1, 2, 3, 4
+DG_DTYPE_MXFP4_MXFP8 = 5
 DG_STATUS_NONFINITE, DG_STATUS_TOKEN = 1, 2
 DG_ERR_INVALID_ARG, DG_ERR_SHAPE, DG_ERR_NUMERIC = -1, -2, -6
 
@@ -87,6 +88,8 @@ _SIGS = {
                        c_void_p, c_void_p],
     "dg_test_lm_head": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     "dg_test_fp4_decode": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p],
+    "dg_test_mx8_quantize": [c_void_p, c_int32, c_int32, c_int32, ctypes.c_float, c_void_p, c_void_p,
+                             c_void_p, c_void_p],
     "dg_test_commit": [c_void_p, POINTER(dg_canvas), c_void_p, c_void_p, c_void_p, c_void_p],
     "dg_test_qkv_rope": [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                          c_void_p, c_void_p],
@@ -234,3 +237,7 @@ def dg_lm_head_confidence_noalloc(handle, hf_ptr, T, ent_ptr, am_ptr, gap_ptr, s
 
 def dg_test_fp4_decode(packed_ptr, scales_ptr, n_blocks, out_ptr, stream):
     _call("dg_test_fp4_decode", packed_ptr, scales_ptr, n_blocks, out_ptr, stream)
+
+
+def dg_test_mx8_quantize(x_ptr, rows, d, norm, eps, y_ptr, codes_ptr, scales_ptr, stream):
+    _call("dg_test_mx8_quantize", x_ptr, rows, d, norm, eps, y_ptr, codes_ptr, scales_ptr, stream)

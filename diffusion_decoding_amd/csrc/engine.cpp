@@ -55,6 +55,7 @@ struct dg_model {
   size_t esz = 0;
   ActType at = ACT_BF16;
   WType wt = W_BF16;   // routed experts
+  WType wt_gu = W_BF16;  // routed gate/up (W_FP4A8: MXFP8 token rows)
   WType swt = W_BF16;  // shared expert
   std::vector<void*> allocs;
   // workspace
@@ -62,6 +63,7 @@ struct dg_model {
        *o = nullptr, *h = nullptr, *hs = nullptr;
   float *attn_po = nullptr, *attn_ml = nullptr;
   void* perm_scratch = nullptr;  // the routing permutation's masks and prefixes above 2048 tokens
+  uint8_t* q8 = nullptr;  // MXFP8 experts: the normed rows' codes [Tmax][d], then scales [Tmax][d/32]
   int attn_max_splits = 8;
   float *rlog = nullptr, *topk_w = nullptr, *y = nullptr, *ys = nullptr, *lm_part = nullptr;
   float* rope_tab = nullptr;  // [max_tokens][head_dim / 2] (cos, sin) of the current positions
@@ -145,11 +147,14 @@ int check_config(const dg_config& c) {
     return fail(DG_ERR_INVALID_ARG, "act_dtype must be FP32 or BF16");
   if (c.act_dtype == DG_DTYPE_FP32 && c.expert_dtype != DG_DTYPE_FP32)
     return fail(DG_ERR_INVALID_ARG, "FP32 activations need FP32 experts");
-  if (c.act_dtype == DG_DTYPE_BF16 && c.expert_dtype != DG_DTYPE_BF16 &&
-      c.expert_dtype != DG_DTYPE_FP8_E4M3 && c.expert_dtype != DG_DTYPE_MXFP4)
-    return fail(DG_ERR_INVALID_ARG, "BF16 activations need BF16, FP8_E4M3 or MXFP4 experts");
-  if (c.expert_dtype == DG_DTYPE_MXFP4 && (c.d_model % 64 || c.d_expert % 64))
+  if (c.act_dtype == DG_DTYPE_BF16 && c.expert_dtype != DG_DTYPE_BF16 && c.expert_dtype != DG_DTYPE_FP8_E4M3 &&
+      c.expert_dtype != DG_DTYPE_MXFP4 && c.expert_dtype != DG_DTYPE_MXFP4_MXFP8)
+    return fail(DG_ERR_INVALID_ARG, "BF16 activations need BF16, FP8_E4M3, MXFP4 or MXFP4_MXFP8 experts");
+  if ((c.expert_dtype == DG_DTYPE_MXFP4 || c.expert_dtype == DG_DTYPE_MXFP4_MXFP8) &&
+      (c.d_model % 64 || c.d_expert % 64))
     return fail(DG_ERR_SHAPE, "MXFP4 experts need d_model and d_expert multiples of 64");
+  if (c.expert_dtype == DG_DTYPE_MXFP4_MXFP8 && c.d_model % 128)
+    return fail(DG_ERR_SHAPE, "MXFP4_MXFP8 experts need d_model a multiple of 128");
   const int A = c.n_heads * c.head_dim;
   if (c.d_model % 32 || A % 32 || c.d_expert % 32 || c.d_shared % 32)
     return fail(DG_ERR_SHAPE, "d_model, n_heads*head_dim, d_expert, d_shared must be multiples of 32");
@@ -324,8 +329,9 @@ bool grouped_route(const dg_model* m, long long T) {
 // products) and y [T*k][d_model] (fp32 expert outputs), both in pair order
 // (expert-major, token-ascending); off [E+1], pair_row [T*k] and pos [T][k]
 // (the row of pair (t, j)) describe that order.
+// xq / xqs: the rows of b as MXFP8 codes and scales (MXFP4_MXFP8 experts).
 int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, float* y, int* off, int* pair_row,
-           int* pos, hipStream_t st) {
+           int* pos, hipStream_t st, const uint8_t* xq = nullptr, const uint8_t* xqs = nullptr) {
   const dg_config& c = m->cfg;
   const dg_layer_weights& w = m->layers[l];
   const int E = c.n_experts, k = c.top_k, d = c.d_model, de = c.d_expert;
@@ -341,7 +347,7 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
     } else {
       ProfScope ps(m, DG_PROF_MOE_GATEUP, st);  // routed gate/up + SwiGLU, routing in the kernel
       const MoeRoute r{ids, T, k, off, pair_row, pos};
-      HIP_OK(moe_experts(m->wt, true, b, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, h, st, &r, pairs));
+      HIP_OK(moe_experts(m->wt_gu, true, b, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, h, st, &r, pairs, xq, xqs));
     }
     {
       // routed down: grouped 128 x 128 tiles from 256 pairs per expert (c2
@@ -400,8 +406,10 @@ int moe_chunks(dg_model* m, int l, int T, bool diag, hipStream_t st) {
   for (int c0 = 0; c0 < T; c0 += chunk) {
     const int tc = std::min(chunk, T - c0);
     const size_t row = (size_t)d * m->esz;
+    const uint8_t* xq = m->q8 ? m->q8 + (size_t)c0 * d : nullptr;
+    const uint8_t* xqs = m->q8 ? m->q8 + (size_t)m->Tmax * d + (size_t)c0 * (d / 32) : nullptr;
     int s = routed(m, l, (const char*)m->a + c0 * row, tc, m->topk_ids + (size_t)c0 * k, m->h, m->y, m->off,
-                   m->pair_row, m->pos + (size_t)c0 * k, st);
+                   m->pair_row, m->pos + (size_t)c0 * k, st, xq, xqs);
     if (s) return s;
     if (diag) HIP_OK(expert_counts(m->off, c.n_experts, m->diag_counts + (long long)l * c.n_experts, c0 > 0, st));
     HIP_OK(moe_combine_norm(m->at, (char*)m->x + c0 * row, m->y, m->ys + (size_t)c0 * d, m->topk_w + (size_t)c0 * k,
@@ -443,7 +451,7 @@ int layer_forward(dg_model* m, int l, int B, int n, int P, const dg_kv* kv, bool
     g.A = m->o; g.lda = A; g.B = w.wo; g.ldb = A; g.M = T; g.N = d; g.K = A; g.C = m->x; g.ldc = d;
     HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_RESID, g, 1, st));
   }
-  HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st));
+  HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st, m->q8, m->q8 ? m->q8 + (size_t)m->Tmax * d : nullptr));
   // The shared expert runs in line, before the router.  (On a second stream,
   // beside the router and the routed experts, its workgroups held CUs that
   // the routed gate/up workgroups (138 KB of LDS each) could not share, and
@@ -520,7 +528,7 @@ int mixed_layer(dg_model* m, int l, const MixedSeg* sg, int n_segs, int T, int T
     g.A = m->o; g.lda = A; g.B = m->layers[l].wo; g.ldb = A; g.M = T; g.N = d; g.K = A; g.C = m->x; g.ldc = d;
     HIP_OK(gemm(m->at, m->at == ACT_BF16 ? W_BF16 : W_F32, EPI_RESID, g, 1, st));
   }
-  HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st));
+  HIP_OK(rmsnorm(m->at, m->x, T, d, c.rms_eps, m->a, st, m->q8, m->q8 ? m->q8 + (size_t)m->Tmax * d : nullptr));
   bool router_done = false, topk_done = false;
   {
     ProfScope ps(m, DG_PROF_SHARED, st);
@@ -650,7 +658,8 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
     const dg_layer_weights& L = w->layers[l];
     if (!L.wqkv || !L.wo || !L.wr || !L.w_gu || !L.w_d || !L.ws_gu || !L.ws_d)
       return fail(DG_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
-    const bool fp8 = cfg->expert_dtype == DG_DTYPE_FP8_E4M3, fp4 = cfg->expert_dtype == DG_DTYPE_MXFP4;
+    const bool fp8 = cfg->expert_dtype == DG_DTYPE_FP8_E4M3;
+    const bool fp4 = cfg->expert_dtype == DG_DTYPE_MXFP4 || cfg->expert_dtype == DG_DTYPE_MXFP4_MXFP8;
     if (fp8 != (L.s_gu && L.s_d && L.ss_gu && L.ss_d) && !fp4)
       return fail(DG_ERR_INVALID_ARG, "fp8 scales must be given exactly when expert_dtype is FP8 (layer %d)", l);
     if (fp4 && !(L.s_gu && L.s_d && !L.ss_gu && !L.ss_d))
@@ -682,8 +691,9 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   m->Tmax = max_batch * ntok;
   m->at = cfg->act_dtype == DG_DTYPE_BF16 ? ACT_BF16 : ACT_F32;
   m->wt = cfg->expert_dtype == DG_DTYPE_FP8_E4M3 ? W_FP8
-        : cfg->expert_dtype == DG_DTYPE_MXFP4   ? W_FP4
+        : cfg->expert_dtype == DG_DTYPE_MXFP4 || cfg->expert_dtype == DG_DTYPE_MXFP4_MXFP8 ? W_FP4
                                                  : (m->at == ACT_BF16 ? W_BF16 : W_F32);
+  m->wt_gu = cfg->expert_dtype == DG_DTYPE_MXFP4_MXFP8 ? W_FP4A8 : m->wt;
   m->swt = m->wt == W_FP4 ? W_BF16 : m->wt;
   m->esz = m->at == ACT_BF16 ? 2 : 4;
   const size_t T = m->Tmax, d = cfg->d_model, A = (size_t)cfg->n_heads * cfg->head_dim;
@@ -725,6 +735,14 @@ int dg_model_create(const dg_config* cfg, const dg_weights* w, int32_t max_batch
   };
   for (auto& r : reqs) {
     s = alloc(m, r.p, r.bytes);
+    if (s) {
+      free_all(m);
+      delete m;
+      return s;
+    }
+  }
+  if (m->wt_gu == W_FP4A8) {  // the normed rows as MXFP8 (only these models have the buffer)
+    s = alloc(m, (void**)&m->q8, T * (d + d / 32));
     if (s) {
       free_all(m);
       delete m;
@@ -921,6 +939,16 @@ int dg_test_fp4_decode(const uint8_t* packed, const uint8_t* scales, int32_t n_b
   return DG_OK;
 }
 
+int dg_test_mx8_quantize(const void* x, int32_t rows, int32_t d, int32_t norm, float eps, void* y,
+                         uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales || (norm && !y)) return fail(DG_ERR_INVALID_ARG, "null argument");
+  if (rows <= 0 || d <= 0 || d % 32 || (norm && d > 8192) || (long long)rows * d > (1LL << 30))
+    return fail(DG_ERR_SHAPE, "rows=%d d=%d", rows, d);
+  if (norm) HIP_OK(rmsnorm(ACT_BF16, x, rows, d, eps, y, (hipStream_t)stream, codes, scales));
+  else HIP_OK(mx8_quantize(x, rows, d, codes, scales, (hipStream_t)stream));
+  return DG_OK;
+}
+
 int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int32_t* argmax,
                     float* top2_gap, void* stream) {
   if (!m || !hf) return fail(DG_ERR_INVALID_ARG, "null argument");
@@ -1031,7 +1059,10 @@ int dg_test_moe(dg_model* m, int32_t layer, const void* b, int32_t T, const int3
   if (!s) s = check_rows(m, T);
   if (s) return s;
   if (T > route_chunk(m, T)) return fail(DG_ERR_SHAPE, "T=%d exceeds one routed launch (%d rows)", T, route_chunk(m, T));
-  return routed(m, layer, b, T, ids, h ? h : m->h, y, m->off, m->pair_row, pos, (hipStream_t)stream);
+  const int d = m->cfg.d_model;
+  uint8_t* xqs = m->q8 ? m->q8 + (size_t)m->Tmax * d : nullptr;
+  if (m->q8) HIP_OK(mx8_quantize(b, T, d, m->q8, xqs, (hipStream_t)stream));
+  return routed(m, layer, b, T, ids, h ? h : m->h, y, m->off, m->pair_row, pos, (hipStream_t)stream, m->q8, xqs);
 }
 
 int dg_mixed_step(dg_model* m, dg_segment* segs, int32_t n_segs, int32_t* status, void* stream) {

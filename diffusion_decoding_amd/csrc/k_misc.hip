@@ -76,7 +76,76 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, int d, float e
 // bf16 rows with d % 8 == 0 and d <= 8192: one 16-byte chunk of the row per
 // thread, loaded once and kept in registers between the sum of squares and
 // the scaled write.
-__global__ __launch_bounds__(1024) void rmsnorm_bf16_kernel(const bf16* x, int d, float eps, bf16* y) {
+// ---------------------------------------------------------------------------
+// MXFP8 token rows (OCP MX conversion of a 32-element block: shared exponent
+// floor(log2(max |v|)) - 8 as an E8M0 code clamped to [0, 254], an all-zero
+// block code 0; each v / 2^shared rounded to E4M3FN, nearest with ties to
+// even, magnitudes past 448 clamped to 448).  Every step is exact fp32
+// arithmetic on bf16 inputs, so the codes are the format's own.
+
+// E4M3FN code of y (finite).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const float a = fminf(fabsf(y), 448.f);
+  const int e = max(int((__float_as_uint(a) >> 23) & 255u) - 127, -6);  // binade; below 2^-6 the subnormal grid
+  const int q = int(rintf(a * __uint_as_float(uint32_t(130 - e) << 23)));  // a / 2^(e - 3): 0 .. 16
+  uint32_t code;
+  if (e == -6 && q < 8) {
+    code = uint32_t(q);
+  } else {
+    const int carry = q >> 4;  // 16: the next binade's mantissa 0
+    code = (uint32_t(e + 7 + carry) << 3) | uint32_t(q - 8 - 8 * carry);
+  }
+  return code | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
+// Eight consecutive elements of a 32-element block (the lanes l ^ 1 and
+// l ^ 2 hold the rest of it) -> their E4M3 codes; *scale gets the block's
+// E8M0 code.  Every lane of the wave must call it.
+__device__ __forceinline__ u32x2 mx8_piece(const float (&f)[8], uint32_t* scale) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const int code = max(int((__float_as_uint(m) >> 23) & 255u) - 8, 0);
+  *scale = uint32_t(code);
+  const float inv = __uint_as_float(uint32_t(254 - code) << 23);  // 2^(127 - code), exact
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0 |= e4m3_code(f[i] * inv) << (8 * i);
+    w1 |= e4m3_code(f[4 + i] * inv) << (8 * i);
+  }
+  return u32x2{w0, w1};
+}
+
+// one thread per 8 elements of x [T][d] (d % 32 == 0): codes q8 [T][d],
+// scales q8s [T][d/32]
+__global__ __launch_bounds__(256) void mx8_quantize_kernel(const bf16* x, long long n8, int d, uint8_t* q8,
+                                                           uint8_t* q8s) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = i < n8;  // whole 4-lane groups share it (d / 8 % 4 == 0)
+  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const u32x4 q = *(const u32x4*)(x + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = __uint_as_float(q[j] << 16);
+      f[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+    }
+  }
+  uint32_t sc;
+  const u32x2 c = mx8_piece(f, &sc);
+  if (live) {
+    *(u32x2*)(q8 + 8 * i) = c;
+    if ((i & 3) == 0) q8s[i / 4] = (uint8_t)sc;
+  }
+}
+
+// q8 / q8s non-null: the normed row is also written as MXFP8 codes and scales
+// (the bf16 values, quantized as mx8_quantize does).
+__global__ __launch_bounds__(1024) void rmsnorm_bf16_kernel(const bf16* x, int d, float eps, bf16* y, uint8_t* q8,
+                                                            uint8_t* q8s) {
   __shared__ float red[16];
   const int t = blockIdx.x, tid = threadIdx.x, c = tid * 8;
   const bool live = c < d;
@@ -99,11 +168,23 @@ __global__ __launch_bounds__(1024) void rmsnorm_bf16_kernel(const bf16* x, int d
   ss = 0.f;
   for (int i = 0; i < nw; ++i) ss += red[i];
   const float inv = 1.0f / sqrtf(ss / float(d) + eps);
-  if (live) {
-    u32x4 o;
+  u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i] * inv, v[2 * i + 1] * inv);
-    *(u32x4*)(y + (long long)t * d + c) = o;
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i] * inv, v[2 * i + 1] * inv);
+  if (live) *(u32x4*)(y + (long long)t * d + c) = o;
+  if (q8) {  // uniform; the non-live lanes hold zeros and take part in the block maxima
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = live ? __uint_as_float(o[i] << 16) : 0.f;
+      f[2 * i + 1] = live ? __uint_as_float(o[i] & 0xffff0000u) : 0.f;
+    }
+    uint32_t sc;
+    const u32x2 q = mx8_piece(f, &sc);
+    if (live) {
+      *(u32x2*)(q8 + (long long)t * d + c) = q;
+      if ((tid & 3) == 0) q8s[(long long)t * (d / 32) + c / 32] = (uint8_t)sc;
+    }
   }
 }
 
@@ -454,13 +535,25 @@ int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vo
   return int(hipGetLastError());
 }
 
-int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st) {
+int mx8_quantize(const void* x, int T, int d, uint8_t* q8, uint8_t* q8s, hipStream_t st) {
   if (T <= 0) return 0;
+  if (d % 32) return int(hipErrorInvalidValue);
+  const long long n8 = (long long)T * d / 8;
+  hipLaunchKernelGGL(mx8_quantize_kernel, dim3(unsigned((n8 + 255) / 256)), dim3(256), 0, st, (const bf16*)x, n8,
+                     d, q8, q8s);
+  return int(hipGetLastError());
+}
+
+int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st, uint8_t* q8,
+            uint8_t* q8s) {
+  if (T <= 0) return 0;
+  if (q8 && (at != ACT_BF16 || d % 32 || d > 8192)) return int(hipErrorInvalidValue);
   if (at == ACT_BF16)
   {
     if (d % 8 == 0 && d <= 8192) {
       const int threads = ((d / 8 + 63) / 64) * 64;
-      hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3(T), dim3(threads), 0, st, (const bf16*)x, d, eps, (bf16*)y);
+      hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3(T), dim3(threads), 0, st, (const bf16*)x, d, eps, (bf16*)y,
+                         q8, q8s);
     } else {
       hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(T), dim3(256), 0, st, (const bf16*)x, d, eps, (bf16*)y);
     }

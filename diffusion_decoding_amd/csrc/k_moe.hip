@@ -156,6 +156,9 @@ struct MoeArgs {
   int* off_out;
   int* pair_row_out;
   int* pos_out;
+  // MXFP8 token rows (W_FP4A8 gate/up): codes [rows of X][K], scales [rows of X][K/32]
+  const uint8_t* xq;
+  const uint8_t* xqs;
 };
 
 constexpr int ROUTE_MAX_TOKENS = 2048;
@@ -250,7 +253,7 @@ __device__ __forceinline__ void stage_tokens(const MoeArgs& a, bf16* xs, int pit
 // weight stage k with k % MD == u.  The ring is filled before the workgroup
 // stages its tokens, so the first weight tiles are in flight during the
 // staging.
-template <typename WL, bool GU, int NB, int MD>
+template <typename WL, bool GU, int NB, int MD, bool SCALAR_OFFSETS = false>
 struct WStream {
   using wraw = typename WL::raw;
   static constexpr bool BS = WL::BSCALE;
@@ -279,12 +282,19 @@ struct WStream {
       srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.bscale + e * smat), (short)0, int(smat), 0x00020000);
       svoff0 = (lane & 15) * (SKE / 32) + (lane >> 4) * SKE / 128;
     }
-    // first tile of each fragment's 16-row block (n0 and Nout are multiples of 16)
+    // first tile of each fragment's 16-row block (n0 and Nout are multiples
+    // of 16).  The offsets are wave-uniform, but the compiler cannot tell
+    // (n0 depends on the wave index) and issues each weight load in a loop
+    // over the distinct values, which runs once.  SCALAR_OFFSETS moves them
+    // to scalar registers (readfirstlane), which removes those loops: the
+    // MXFP4 x MXFP8 gate/up then ran 45.0 against 48.3 us, while the bf16
+    // and MXFP4 (bf16 widening) streams ran as fast or slower (MXFP4 gate/up
+    // and down 49.4 and 34.2 us against 47.0 and 32.5).
 #pragma unroll
     for (int f = 0; f < NW; ++f) {
       const int tile0 = ((n0 + 16 * (f % NB) + (f < NB ? 0 : a.Nout)) / 16) * KS;
-      soff[f] = tile0 * TILE;
-      if constexpr (BS) ssoff[f] = tile0 * STILE;
+      soff[f] = SCALAR_OFFSETS ? __builtin_amdgcn_readfirstlane(tile0 * TILE) : tile0 * TILE;
+      if constexpr (BS) ssoff[f] = SCALAR_OFFSETS ? __builtin_amdgcn_readfirstlane(tile0 * STILE) : tile0 * STILE;
     }
   }
   __device__ __forceinline__ void ld(int ks, int u) {
@@ -411,6 +421,107 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
     if (k0 + MD + u < KS) step(k0 + MD + u, u, false, 0);
 
   moe_epilogue<WL, GU, NB, MT>(a, acc, e, n0, pbeg, rows);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 weights x MXFP8 tokens on the gfx950 scaled MFMA (16x16x128, E2M1
+// operand A, E4M3 operand B, one E8M0 scale per 32 k of each row and column,
+// fp32 accumulation).  The MXFP4 weight tiles above are already its A operand
+// (lane (c16, g4): row c16, codes k = 32 g4 .. 32 g4 + 31, low nibble first;
+// its scale byte is the one of that row and 32-block).  The B operand of lane
+// (c16, g4) is token c16's E4M3 codes k = 16 g4 .. 16 g4 + 15 and 64 + 16 g4
+// .. 64 + 16 g4 + 15 of the 128-k step (two 16-byte LDS reads), its scale the
+// one of token c16 and block g4 (the layout was checked on the device).  The
+// token rows arrive quantized (RMSNorm writes them; mx8_quantize for other
+// callers): codes [rows][K] and scales [rows][K / 32].
+
+// Stage the pass's token codes [16 MT][K + 16] (an odd multiple of 16 bytes
+// per row keeps the 16-row fragment reads conflict-free), then their scales
+// [16 MT][K / 32]; rows past the pass are zero.
+template <int MT>
+__device__ __forceinline__ void stage_tokens_mx8(const MoeArgs& a, uint8_t* xq, const int* gather, int gidx0,
+                                                 int rows) {
+  const int cpr = a.K / 16, spr = a.K / 512, qp = a.K + 16, nb32 = a.K / 32;  // 16-byte pieces per row
+  uint8_t* sc = xq + 16 * MT * qp;
+  const int total = 16 * MT * (cpr + spr), nt = blockDim.x;
+  for (int c0 = threadIdx.x; c0 < total; c0 += 4 * nt) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * nt, r = c / (cpr + spr), p = c - r * (cpr + spr);
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (c < total && r < rows) {
+        const long long row = gather ? (long long)gather[gidx0 + r] : (long long)(gidx0 + r);
+        v[u] = p < cpr ? *(const u32x4*)(a.xq + row * a.K + 16 * p)
+                       : *(const u32x4*)(a.xqs + row * nb32 + 16 * (p - cpr));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * nt, r = c / (cpr + spr), p = c - r * (cpr + spr);
+      if (c < total) *(u32x4*)(p < cpr ? xq + r * qp + 16 * p : sc + r * nb32 + 16 * (p - cpr)) = v[u];
+    }
+  }
+}
+
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+
+// One wave of the MXFP4 x MXFP8 gate/up: output rows n0 .. n0 + 16 NB - 1
+// (and the matching up rows) against the MT token tiles staged by
+// stage_tokens_mx8; the weight ring of ws has been filled.
+template <bool GU, int NB, int MD, int MT>
+__device__ __forceinline__ void moe_wave_mx8(const MoeArgs& a, const uint8_t* xq,
+                                             WStream<WFmt<f4, 4>, GU, NB, MD, true>& ws,
+                                             int e, int n0, int pbeg, int rows) {
+  using WS = WStream<WFmt<f4, 4>, GU, NB, MD, true>;
+  constexpr int NW = WS::NW;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g4 = lane >> 4;
+  const int KS = ws.KS, qp = a.K + 16, nb32 = a.K / 32;
+  const uint8_t* xr = xq + c16 * qp + 16 * g4;
+  const uint8_t* sr = xq + 16 * MT * qp + c16 * nb32 + g4;
+
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int ks, int u, bool refill, int next) {
+    v8i32 xv[MT];
+    int xs8[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const u32x4 lo = *(const u32x4*)(xr + 16 * t * qp + 128 * ks);
+      const u32x4 hi = *(const u32x4*)(xr + 16 * t * qp + 128 * ks + 64);
+      xv[t] = v8i32{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      xs8[t] = sr[16 * t * nb32 + 4 * ks];
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const u32x4 c = ws.rw[u][w];
+      const v8i32 wv = v8i32{int(c[0]), int(c[1]), int(c[2]), int(c[3]), 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[w][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv[t], acc[w][t], 4, 0, 0,
+                                                                     int(ws.rs[u][w]), 0, xs8[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) ws.ld(next, u);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int k0 = 0;
+  for (; k0 + 2 * MD <= KS; k0 += MD) {
+#pragma unroll
+    for (int u = 0; u < MD; ++u) step(k0 + u, u, true, k0 + u + MD);
+  }
+#pragma unroll
+  for (int u = 0; u < MD; ++u)
+    if (k0 + u < KS) step(k0 + u, u, k0 + u + MD < KS, k0 + u + MD);
+#pragma unroll
+  for (int u = 0; u < MD; ++u)
+    if (k0 + MD + u < KS) step(k0 + MD + u, u, false, 0);
+
+  moe_epilogue<WFmt<f4, 4>, GU, NB, MT>(a, acc, e, n0, pbeg, rows);
 }
 
 // Gate/up with more tokens than fit LDS over all of K (pooled canvases): the
@@ -540,9 +651,10 @@ __device__ __forceinline__ int further_pass(int j, int maxc, int PS, int E, int 
     }
   return -1;
 }
-template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC>
+template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC, bool A8 = false>
 __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   static_assert(KC == 0 || (GU && MD == 1), "chunked staging is the gate/up path with one stage in flight");
+  static_assert(!A8 || (std::is_same<WL, WFmt<f4, 4>>::value && KC == 0), "MXFP8 tokens: MXFP4 weights, K % 128 == 0");
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];
   const int pitch = a.K + 16;  // an odd multiple of 32 B when K % 16 == 0: full-rate fragment reads
   constexpr int PS = 16 * MTP;  // pairs per pass
@@ -550,9 +662,20 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   // pass rows p0 .. p0 + rows - 1 of expert e; pair p of the expert is X row
   // gather[gbase + p], or X row gbase + p without a gather list (down: X
   // holds one row per pair)
-  auto run_pass = [&](WStream<WL, GU, NB, MD>& ws, bool active, int e, int n0, int pbeg, int p0, int rows,
+  auto run_pass = [&](WStream<WL, GU, NB, MD, A8>& ws, bool active, int e, int n0, int pbeg, int p0, int rows,
                       const int* gather, int gbase) {
-    if constexpr (KC > 0) {
+    if constexpr (A8) {
+      uint8_t* xq = (uint8_t*)xs;
+      if (rows <= 16) stage_tokens_mx8<1>(a, xq, gather, gbase + p0, rows);
+      else if (MTP > 2 && rows <= 32) stage_tokens_mx8<2>(a, xq, gather, gbase + p0, rows);
+      else stage_tokens_mx8<MTP>(a, xq, gather, gbase + p0, rows);
+      __syncthreads();
+      if (active) {
+        if (rows <= 16) moe_wave_mx8<GU, NB, MD, 1>(a, xq, ws, e, n0, pbeg + p0, rows);
+        else if (MTP > 2 && rows <= 32) moe_wave_mx8<GU, NB, MD, 2>(a, xq, ws, e, n0, pbeg + p0, rows);
+        else moe_wave_mx8<GU, NB, MD, MTP>(a, xq, ws, e, n0, pbeg + p0, rows);
+      }
+    } else if constexpr (KC > 0) {
       const int gi = gbase + p0, pb = pbeg + p0;
       if (rows <= 16) moe_gu_chunked<WL, NB, 1, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
       else if (rows <= 32) moe_gu_chunked<WL, NB, 2, KC>(a, xs, ws, active, e, n0, pb, rows, gather, gi);
@@ -574,7 +697,7 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   const int e = blockIdx.y;
   const int n0 = blockIdx.x * rows_per_wg + wave * 16 * NB;
   const bool active = n0 < min(a.Nout, (blockIdx.x + 1) * rows_per_wg);
-  WStream<WL, GU, NB, MD> ws;
+  WStream<WL, GU, NB, MD, A8> ws;
   ws.init(a, e, n0);
   if (active) ws.fill();  // the first weight tiles are in flight during the routing and staging
 
@@ -673,21 +796,22 @@ __global__ __launch_bounds__(TMAX) void moe_kernel(MoeArgs a, int rows_per_wg) {
   }
 }
 
-template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC = 0>
+template <typename WL, bool GU, int NB, int MD, int TMAX, int MTP, int KC = 0, bool A8 = false>
 int launch_k(const MoeArgs& a, int E, int split, hipStream_t st) {
   if (a.K % (32 * WL::SPS) || (KC > 0 && a.K % KC)) return int(hipErrorInvalidValue);
   const int blocks = (a.Nout + 16 * NB - 1) / (16 * NB);       // 16 NB-row wave blocks per expert
   const int waves = (blocks + split - 1) / split;              // per workgroup
   if (waves * 64 > TMAX) return int(hipErrorInvalidValue);
-  const size_t lds = KC > 0 ? size_t(2 * 16 * MTP) * (KC + 16) * sizeof(bf16)
+  const size_t lds = A8 ? size_t(16 * MTP) * (a.K + 16 + a.K / 32)
+                   : KC > 0 ? size_t(2 * 16 * MTP) * (KC + 16) * sizeof(bf16)
                             : size_t(16 * MTP) * (a.K + 16) * sizeof(bf16);
   if (lds + (GU ? ROUTE_LDS : 0) + KERNEL_LDS > 160 * 1024) return int(hipErrorInvalidValue);  // + static LDS
   // once per kernel (not inside a graph capture): the largest dynamic LDS any launch may ask for
-  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC, A8>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      160 * 1024 - (GU ? ROUTE_LDS : 0) - KERNEL_LDS);
   if (attr != hipSuccess) return int(attr);
-  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC>), dim3(split, E), dim3(64 * waves), lds, st, a,
+  hipLaunchKernelGGL((moe_kernel<WL, GU, NB, MD, TMAX, MTP, KC, A8>), dim3(split, E), dim3(64 * waves), lds, st, a,
                      waves * 16 * NB);
   return int(hipGetLastError());
 }
@@ -835,14 +959,14 @@ int fp4_decode(const void* packed, const uint8_t* scales, int n_blocks, void* ou
 
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const void* scale, int K, int Nout, void* out, hipStream_t st,
-                const MoeRoute* route, int pairs) {
+                const MoeRoute* route, int pairs, const uint8_t* xq, const uint8_t* xqs) {
   if (K % 32 || K <= 0 || Nout <= 0 || E <= 0) return int(hipErrorInvalidValue);
   MoeArgs a{};
   a.X = (const bf16*)X;
   a.pair_row = pair_row;
   a.off = off;
   a.W = W;
-  if (wt == W_FP4) a.bscale = (const uint8_t*)scale;
+  if (wt == W_FP4 || wt == W_FP4A8) a.bscale = (const uint8_t*)scale;
   else a.scale = (const float*)scale;
   a.K = K;
   a.Nout = Nout;
@@ -857,6 +981,15 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
     a.off_out = route->off;
     a.pair_row_out = route->pair_row;
     a.pos_out = route->pos;
+  }
+  if (wt == W_FP4A8) {
+    // MXFP4 weights x MXFP8 tokens (gate/up only): 32 outputs per wave, two
+    // workgroups per expert and 32 tokens per pass, as for bf16
+    if (!gate_up || K % 512 || !a.bscale || !xq || !xqs) return int(hipErrorInvalidValue);
+    a.xq = xq;
+    a.xqs = xqs;
+    a.scale = nullptr;
+    return launch_k<WFmt<f4, 4>, true, 2, 1, 768, 2, 0, true>(a, E, 2, st);
   }
   if (wt == W_BF16) return launch<WFmt<bf16, 1>>(gate_up, a, E, pairs, st);
   if (wt == W_FP8 && K % 64 == 0) return launch<WFmt<f8, 2>>(gate_up, a, E, pairs, st);

@@ -14,7 +14,9 @@ enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 // outside the vocabulary.
 constexpr int FLAG_NONFINITE = 1;
 constexpr int FLAG_TOKEN = 2;
-enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP4 = 3 };
+// W_FP4A8: MXFP4 weights whose gate/up reads its token rows as MXFP8 (the
+// gfx950 scaled MFMA; moe_experts gate/up only)
+enum WType { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP4 = 3, W_FP4A8 = 4 };
 
 // ---------------------------------------------------------------- GEMM (k_gemm.hip)
 // C[m][n] = sum_k A[row(m)][k] * B[n][k]; epilogue by kind.
@@ -110,11 +112,14 @@ struct MoeRoute {
 };
 // pairs: T * k (sizes the token passes; 0 = few pairs per expert); with a
 // route, the larger of this and route->T * route->k.
-// scale: W_FP8 fp32 row scales [E][rows]; W_FP4 the tiled E8M0 block scales
-// (moe_pack_scales); otherwise null.
+// scale: W_FP8 fp32 row scales [E][rows]; W_FP4 / W_FP4A8 the tiled E8M0
+// block scales (moe_pack_scales); otherwise null.
+// xq, xqs (W_FP4A8 only): the MXFP8 codes [rows][K] and E8M0 scales
+// [rows][K/32] of X's rows (mx8_quantize / rmsnorm); K % 512 == 0.
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const void* scale, int K, int Nout, void* out, hipStream_t st,
-                const MoeRoute* route = nullptr, int pairs = 0);
+                const MoeRoute* route = nullptr, int pairs = 0, const uint8_t* xq = nullptr,
+                const uint8_t* xqs = nullptr);
 // Row-major [n_mats][rows][cols] expert matrices -> the tiled layout moe_experts reads
 // (rows % 16 == 0, cols % 32 == 0, W_FP4: cols % 64 == 0 with two codes per
 // byte; src and dst must not overlap).
@@ -167,7 +172,14 @@ int noalloc_scratch(void** ptr);
 // tok2 (nullable): add the rows of these ids too (one rounding of the sum)
 int embed_gather(ActType at, const int* tok, int T, const void* E, int d, int vocab, void* x, int* flags,
                  hipStream_t st, const int* tok2 = nullptr);
-int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st);
+// q8 / q8s (bf16, d % 32 == 0): also write the normed rows as MXFP8 codes
+// [T][d] and E8M0 scales [T][d/32], as mx8_quantize does.
+int rmsnorm(ActType at, const void* x, int T, int d, float eps, void* y, hipStream_t st, uint8_t* q8 = nullptr,
+            uint8_t* q8s = nullptr);
+// bf16 rows x [T][d] (d % 32 == 0) -> MXFP8: E4M3FN codes [T][d] and one
+// E8M0 scale per 32 elements [T][d/32] (OCP MX conversion, round to nearest
+// even, clamp at 448).
+int mx8_quantize(const void* x, int T, int d, uint8_t* q8, uint8_t* q8s, hipStream_t st);
 // tab[i][j] = (cos, sin) of (pos0 + i) * theta^(-2j/dh), i < n, j < dh/2 (float pairs)
 int rope_table(int n, int dh, int pos0, float theta, float* tab, hipStream_t st);
 // Rows of a mixed batch: segment s holds rows [start[s], start[s + 1]) at

@@ -9,8 +9,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (DG_DTYPE_BF16, DG_DTYPE_E8M0, DG_DTYPE_FP8_E4M3, DG_DTYPE_FP32, DG_DTYPE_MXFP4, dg_canvas,
-                   dg_config, dg_kv, dg_layer_weights, dg_step_out, dg_weights)
+from ._lib import (DG_DTYPE_BF16, DG_DTYPE_E8M0, DG_DTYPE_FP8_E4M3, DG_DTYPE_FP32, DG_DTYPE_MXFP4,
+                   DG_DTYPE_MXFP4_MXFP8, dg_canvas, dg_config, dg_kv, dg_layer_weights, dg_step_out, dg_weights)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -29,7 +29,7 @@ def _stream(stream=None):
 
 
 _DT = {"fp32": DG_DTYPE_FP32, "bf16": DG_DTYPE_BF16, "fp8": DG_DTYPE_FP8_E4M3, "mxfp4": DG_DTYPE_MXFP4,
-       "e8m0": DG_DTYPE_E8M0}
+       "mxfp4_a8": DG_DTYPE_MXFP4_MXFP8, "e8m0": DG_DTYPE_E8M0}
 
 
 def make_config(cfg) -> dg_config:
@@ -68,9 +68,10 @@ class Model:
         for l, lw in enumerate(inputs.layers):
             w_gu, w_d, s_gu, s_d = lw["w_gu"], lw["w_d"], lw.get("s_gu"), lw.get("s_d")
             if cfg.expert_dtype != "fp32":
-                w_gu, w_d = pack_experts(w_gu, cfg.expert_dtype), pack_experts(w_d, cfg.expert_dtype)
+                pdt = "mxfp4" if cfg.expert_dtype == "mxfp4_a8" else cfg.expert_dtype   # same weight layout
+                w_gu, w_d = pack_experts(w_gu, pdt), pack_experts(w_d, pdt)
                 self._packed += [w_gu, w_d]
-            if cfg.expert_dtype == "mxfp4":
+            if cfg.expert_dtype in ("mxfp4", "mxfp4_a8"):
                 s_gu, s_d = pack_experts(s_gu, "e8m0"), pack_experts(s_d, "e8m0")
                 self._packed += [s_gu, s_d]
             self._layers[l] = dg_layer_weights(
@@ -324,6 +325,20 @@ def test_force_routing(model: Model, ids: Optional[torch.Tensor]):
             raise ValueError(f"ids must be int32 {want}")
     model._forced = ids
     _lib.dg_test_force_routing(model.handle, _ptr(ids))
+
+
+def test_mx8_quantize(x: torch.Tensor, norm_eps: Optional[float] = None, stream=None):
+    """bf16 rows x [rows][d] -> (codes uint8 [rows][d], scales uint8 [rows][d/32], y): the MXFP8
+    rows the MXFP4 x MXFP8 experts read; with norm_eps, of y = bf16(rmsnorm(x)) (else y is None)."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("need contiguous bf16 [rows][d]")
+    rows, d = x.shape
+    codes = torch.empty(rows, d, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, d // 32, dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x) if norm_eps is not None else None
+    _lib.dg_test_mx8_quantize(_ptr(x), rows, d, int(norm_eps is not None), float(norm_eps or 0.0),
+                              _ptr(y) if y is not None else None, _ptr(codes), _ptr(scales), _stream(stream))
+    return codes, scales, y
 
 
 def test_fp4_decode(packed: torch.Tensor, scales: torch.Tensor, stream=None) -> torch.Tensor:

@@ -77,8 +77,23 @@ typedef enum {
  * (2^(e-127)) per 32 consecutive weights along the input dimension; the
  * shared expert stays BF16.  The MI355X counterpart of the 4-bit expert
  * weights the pages name (DiffusionGemma深度拆解 (zhichai.net), "MoE 效率：128
- * 专家，8 活跃").  DG_DTYPE_E8M0 names the block scales for dg_pack_experts. */
-enum { DG_DTYPE_FP32 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP8_E4M3 = 2, DG_DTYPE_MXFP4 = 3, DG_DTYPE_E8M0 = 4 };
+ * 专家，8 活跃").  DG_DTYPE_E8M0 names the block scales for dg_pack_experts.
+ * DG_DTYPE_MXFP4_MXFP8 (expert_dtype only): the same MXFP4 weights and scales
+ * (packed as DG_DTYPE_MXFP4), with the routed gate/up reading its token rows
+ * as OCP MX FP8: per row and 32 consecutive elements one E8M0 scale 2^s with
+ * s = floor(log2(max |v|)) - 8 (an all-zero block: code 0), each element
+ * v / 2^s rounded to E4M3FN, nearest with ties to even, clamped to +-448.
+ * The products run on gfx950's scaled MFMA (4-bit x 8-bit operands); the
+ * routed down and the shared expert read bf16 as with DG_DTYPE_MXFP4.  Needs
+ * d_model % 128 == 0. */
+enum {
+  DG_DTYPE_FP32 = 0,
+  DG_DTYPE_BF16 = 1,
+  DG_DTYPE_FP8_E4M3 = 2,
+  DG_DTYPE_MXFP4 = 3,
+  DG_DTYPE_E8M0 = 4,
+  DG_DTYPE_MXFP4_MXFP8 = 5
+};
 
 /* Bits of the device status word (dg_step_out.status). */
 enum {
@@ -103,8 +118,9 @@ typedef struct dg_config {
   float rms_eps;           /* RMSNorm epsilon (inside the square root) */
   float commit_threshold;  /* nats: uncommitted positions with entropy below it commit */
   int32_t act_dtype;       /* DG_DTYPE_FP32 or DG_DTYPE_BF16 */
-  int32_t expert_dtype;    /* FP32 (with act FP32), BF16, FP8_E4M3 or MXFP4 (with act BF16; MXFP4
-                              needs d_model and d_expert multiples of 64) */
+  int32_t expert_dtype;    /* FP32 (with act FP32), BF16, FP8_E4M3, MXFP4 or MXFP4_MXFP8 (with act
+                              BF16; MXFP4 needs d_model and d_expert multiples of 64, MXFP4_MXFP8
+                              also d_model % 128 == 0) */
   int32_t mask_token;      /* -1: uniform-state noise (Philox draws, the method of the pages);
                               0 .. vocab-1: absorbing-state (mask) noise with this [MASK] id --
                               the canvas starts as all [MASK] and every uncommitted position is
@@ -380,6 +396,14 @@ int dg_test_lm_head(dg_model* m, const void* hf, int32_t T, float* entropy, int3
  * scales[n_blocks] -> out[n_blocks * 32] bf16, through the widening the
  * MXFP4 expert kernels use. */
 int dg_test_fp4_decode(const uint8_t* packed, const uint8_t* scales, int32_t n_blocks, void* out, void* stream);
+
+/* bf16 rows x[rows][d] (d % 32 == 0; with norm, d <= 8192) -> MXFP8 as the
+ * MXFP4_MXFP8 experts read them: E4M3FN codes[rows][d] and E8M0
+ * scales[rows][d/32] (see DG_DTYPE_MXFP4_MXFP8).  norm != 0: first
+ * y = bf16(rmsnorm(x)) (eps), written to y, and y is quantized, through the
+ * fused RMSNorm kernel; norm == 0: x itself, through the standalone kernel. */
+int dg_test_mx8_quantize(const void* x, int32_t rows, int32_t d, int32_t norm, float eps, void* y,
+                         uint8_t* codes, uint8_t* scales, void* stream);
 
 /* Commit selection + re-noise alone, on given entropy/argmax [batch][canvas_len]. */
 int dg_test_commit(dg_model* m, dg_canvas* c, const float* entropy, const int32_t* argmax,

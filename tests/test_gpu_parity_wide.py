@@ -386,6 +386,22 @@ def test_mxfp4_full_width_two_layers_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_mxfp4_a8_full_width_two_layers_one_step(rt):
+    """MXFP4 weights with MXFP8 token rows into the routed gate/up (the gfx950
+    scaled MFMA; the RMSNorm after attention writes the rows' E4M3 codes and
+    E8M0 scales) at the 30-layer workload's width, two layers, 2048-row
+    prompt, short vocabulary: one locked step against the oracle, which
+    quantizes the same rows."""
+    cfg = get_config("c7").replace(name="c7_2_layers", n_layers=2, vocab=8192)
+    say("MXFP4 x MXFP8 experts, full width, 2 layers, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_mxfp4_full_depth_one_step(rt):
     """The MXFP4 workload at full depth -- 30 layers of E2M1 routed experts
     with E8M0 block scales, 262144 ids, 2048-row prompt -- for one step

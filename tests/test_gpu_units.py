@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from oracle import model as om
-from oracle.numerics import round_bf16, round_fp32
+from oracle.numerics import round_bf16, round_fp32, round_mxfp8
 from tests.gpu_helpers import say
 from tests.parity import to_host
 from tests.unit_ref import attention_ref, check_bf16, check_f32, gemm_tol, qkv_rope_ref, swiglu_ref
@@ -42,6 +42,8 @@ def _unit_cfg(kind: str):
         return get_config("c4").replace(name="unit_fp8", n_layers=1, vocab=8192, n_canvases=1)
     if kind == "mxfp4":
         return get_config("c6").replace(name="unit_mxfp4", n_layers=1, vocab=8192, prompt_len=256)
+    if kind == "mxfp4_a8":
+        return get_config("c7").replace(name="unit_mxfp4_a8", n_layers=1, vocab=8192, prompt_len=256)
     raise ValueError(kind)
 
 
@@ -77,6 +79,13 @@ def unit_fp8(rt):
 @pytest.fixture(scope="module")
 def unit_mxfp4(rt):
     u = Unit(rt, "mxfp4")
+    yield u
+    u.close()
+
+
+@pytest.fixture(scope="module")
+def unit_mxfp4_a8(rt):
+    u = Unit(rt, "mxfp4_a8")
     yield u
     u.close()
 
@@ -286,18 +295,22 @@ def _moe_case(rt, u, b, ids, model=None):
     np.testing.assert_array_equal(pg, want)
     nmis = nflag = 0
     worst = 0.0
+    a8 = cfg.expert_dtype == "mxfp4_a8"
+    bq = round_mxfp8(b) if a8 else b        # the gate/up's token rows as the experts read them
     for e in range(E):
         ts, js = np.nonzero(ids == e)
         if ts.size == 0:
             continue
         w_gu, w_d = u.W.expert(0, e)
         rows = pg[ts, js]
-        h_pre, h_tol = swiglu_ref(b[ts], w_gu)
+        h_pre, h_tol = swiglu_ref(bq[ts], w_gu, scaled_mfma=a8)
         a, f = check_bf16(hg[rows], h_pre, h_tol, f"expert {e} SwiGLU products", max_frac=1.0)
         nmis, nflag = nmis + a, nflag + f
         ref = hg[rows] @ w_d.T
         worst = max(worst, check_f32(yg[rows], ref, gemm_tol(hg[rows], w_d, ref), f"expert {e} down"))
-    assert nmis <= 5e-3 * hg.size, nmis
+    # (the scaled MFMA's looser accumulation leaves more products next to a
+    # rounding boundary; every difference is still within the bound)
+    assert nmis <= (5e-2 if a8 else 5e-3) * hg.size, nmis
     _report("routed h", nmis, nflag, hg.size)
     say(f"   routed down (from the GPU's h) within {worst:.2e} of the bound")
 
@@ -369,10 +382,58 @@ def test_moe_unit_mxfp4(rt, unit_mxfp4):
     _moe_case(rt, unit_mxfp4, b, _oracle_ids(unit_mxfp4, b))
 
 
+@pytest.mark.parametrize("T", [256, 1024, 2048])
+def test_moe_unit_mxfp4_a8(rt, unit_mxfp4_a8, T):
+    """MXFP4 weights x MXFP8 token rows on the scaled MFMA (gate/up, K =
+    2048): the rows are quantized while staged (one E8M0 scale per 32), 32
+    tokens per pass; 1024 and 2048 rows put 64 and 128 pairs on an expert, so
+    its further passes spread over the grid.  The down reads bf16 h."""
+    say(f"routed experts unit (MXFP4 x MXFP8): {T} rows")
+    b = _normed_rows(900 + T, T, unit_mxfp4_a8.cfg.d_model)
+    _moe_case(rt, unit_mxfp4_a8, b, _oracle_ids(unit_mxfp4_a8, b))
+
+
 def test_moe_unit_mxfp4_pooled(rt, unit_mxfp4):
     say("routed experts unit (MXFP4): 1024 pooled rows (96-token passes)")
     b = _normed_rows(801, 1024, unit_mxfp4.cfg.d_model)
     _moe_case(rt, unit_mxfp4, b, _oracle_ids(unit_mxfp4, b))
+
+
+def _mx8_rows(seed: int, rows: int, d: int) -> np.ndarray:
+    """bf16 rows that reach every branch of the MXFP8 conversion: random
+    values over 2^-40 .. 2^40, zero and negative-zero blocks, halfway cases
+    of the E4M3 grid, block maxima that round past 448, elements on the
+    subnormal grid, bf16 subnormals and very large magnitudes."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, d)) * np.exp2(g.integers(-40, 40, (rows, d // 32, 1))).repeat(32, -1).reshape(rows, d)
+    x[0, :32] = 0.0
+    x[0, 32:64] = -0.0
+    x[1, :32] = np.array([1.0 + 1 / 16, 1.0 + 3 / 16, -(1.0 + 5 / 16), 2.0 ** -7 * 1.5] + [0.01] * 28)
+    x[1, 0:32] *= 2.0 ** -8                   # block max 1.0625 * 2^-8: scale 2^-16, halfway cases stay halfway
+    x[1, 32:64] = 1.9 * 2.0 ** 5              # amax 1.9 * 2^5 -> 486.4 / 448 after scaling: clamped
+    x[1, 64:96] = g.standard_normal(32) * 2.0 ** -120
+    x[1, 96:128] = np.where(g.random(32) < 0.5, 1e-39, -3e-40)    # bf16 subnormals
+    x[2, :32] = g.standard_normal(32) * 1e30
+    x[2, 32:64] = np.concatenate([[300.0], g.standard_normal(31) * 2.0 ** -12])  # small ones on the subnormal grid
+    return round_bf16(x)
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_mx8_quantize_bit_exact(rt, norm):
+    """The MXFP8 conversion of bf16 rows (standalone, and fused into the
+    RMSNorm whose output the MXFP4 x MXFP8 gate/up reads) gives the oracle's
+    E4M3 codes and E8M0 scales bit for bit."""
+    from oracle.numerics import quantize_mxfp8
+    say(f"MXFP8 quantization ({'fused into RMSNorm' if norm else 'standalone'}): 64 x 2048 rows")
+    x = _mx8_rows(31, 64, 2048)
+    xt = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda()
+    codes, scales, y = rt.test_mx8_quantize(xt, 1e-6 if norm else None)
+    torch.cuda.synchronize()
+    src = _host(y) if norm else x
+    want_c, want_s = quantize_mxfp8(src)
+    np.testing.assert_array_equal(to_host(scales), want_s)
+    np.testing.assert_array_equal(to_host(codes), want_c)
+    say(f"   {codes.numel()} codes and {scales.numel()} scales bit-exact")
 
 
 def test_fp4_decode_exhaustive(rt):

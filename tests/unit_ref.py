@@ -114,12 +114,23 @@ def attention_ref(q: np.ndarray, K: np.ndarray, V: np.ndarray, causal_start=None
     return o, tol
 
 
-def swiglu_ref(x: np.ndarray, w_gu: np.ndarray):
+def scaled_mfma_tol(a: np.ndarray, w: np.ndarray, out: np.ndarray) -> np.ndarray:
+    """Bound on |result - exact| for out = a @ w.T on gfx950's scaled MFMA
+    (4-bit x 8-bit operands, 128 k per instruction, fp32 accumulator).  Its
+    internal summation is not exact: on random E2M1 x E4M3 operands with
+    block scales over 2^-7 .. 2^7 one instruction came within 2^-13.3 of the
+    sum of |products| (measured on the device; no published figure is at
+    hand).  Over K = 2048 (16 instructions into one accumulator) the bound
+    taken is 2^-11 of sum |a_k w_k|, plus one rounding of the result."""
+    return 2.0 ** -11 * (np.abs(a) @ np.abs(w).T) + U24 * np.abs(out)
+
+
+def swiglu_ref(x: np.ndarray, w_gu: np.ndarray, scaled_mfma: bool = False):
     """h = silu(g) u (unrounded) of rows x against gate rows then up rows of
-    w_gu, and its bound."""
+    w_gu, and its bound (scaled_mfma: the products ran on the scaled MFMA)."""
     de = w_gu.shape[0] // 2
     gu = x @ w_gu.T
-    tgu = gemm_tol(x, w_gu, gu)
+    tgu = (scaled_mfma_tol if scaled_mfma else gemm_tol)(x, w_gu, gu)
     g, u = gu[:, :de], gu[:, de:]
     sg = om.silu(g)
     h = sg * u
