@@ -342,11 +342,14 @@ def test_mixed_sixteen_segments(rt):
     assert_reports(cfg.replace(batch=1), reps)
 
 
-@pytest.mark.parametrize("edt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("edt", ["fp8", "mxfp4", "mxfp4_a8"])
 def test_mixed_low_precision_experts(rt, edt):
-    """Mixed passes with fp8 (routed and shared) and MXFP4 (routed) experts:
-    a prompt read, a refine canvas and a canvas commit, two passes."""
-    cfg = _tiny_mix(rt, "bf16", name=f"tiny_mixed_{edt}", expert_dtype=edt, d_expert=64, batch=3)
+    """Mixed passes with fp8 (routed and shared), MXFP4 (routed) and MXFP4 x
+    MXFP8 (routed; the token rows quantized by the RMSNorm of the stacked
+    rows, d_model 128) experts: a prompt read, a refine canvas and a canvas
+    commit, two passes."""
+    extra = {"d_model": 128} if edt == "mxfp4_a8" else {}
+    cfg = _tiny_mix(rt, "bf16", name=f"tiny_mixed_{edt}", expert_dtype=edt, d_expert=64, batch=3, **extra)
     say(f"mixed batch, {edt} experts: append 48 | refine (P=100) | append 40 (P=60)")
     mix = Mix(rt, cfg, max_batch=1, max_tokens=140, kv_capacity=100 + 2 * 48 + 40)
     a0, r1, a2 = Request(mix, 0, 0), Request(mix, 1, 100, seed=19), Request(mix, 2, 60)
