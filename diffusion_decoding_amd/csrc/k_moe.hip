@@ -437,30 +437,35 @@ __device__ __forceinline__ void moe_wave(const MoeArgs& a, const bf16* xs, int p
 
 // Stage the pass's token codes [16 MT][K + 16] (an odd multiple of 16 bytes
 // per row keeps the 16-row fragment reads conflict-free), then their scales
-// [16 MT][K / 32]; rows past the pass are zero.
+// [16 MT][K / 32]; rows past the pass are zero.  K % 128 == 0.
 template <int MT>
 __device__ __forceinline__ void stage_tokens_mx8(const MoeArgs& a, uint8_t* xq, const int* gather, int gidx0,
                                                  int rows) {
-  const int cpr = a.K / 16, spr = a.K / 512, qp = a.K + 16, nb32 = a.K / 32;  // 16-byte pieces per row
+  const int cpr = a.K / 16, qp = a.K + 16, nb32 = a.K / 32, spr = a.K / 128;  // 16-byte / 4-byte pieces per row
   uint8_t* sc = xq + 16 * MT * qp;
-  const int total = 16 * MT * (cpr + spr), nt = blockDim.x;
+  const int nt = blockDim.x;
+  auto src_row = [&](int r) -> long long {
+    return gather ? (long long)gather[gidx0 + r] : (long long)(gidx0 + r);
+  };
+  const int total = 16 * MT * cpr;
   for (int c0 = threadIdx.x; c0 < total; c0 += 4 * nt) {
     u32x4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = c0 + u * nt, r = c / (cpr + spr), p = c - r * (cpr + spr);
+      const int c = c0 + u * nt, r = c / cpr, p = c - r * cpr;
       v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (c < total && r < rows) {
-        const long long row = gather ? (long long)gather[gidx0 + r] : (long long)(gidx0 + r);
-        v[u] = p < cpr ? *(const u32x4*)(a.xq + row * a.K + 16 * p)
-                       : *(const u32x4*)(a.xqs + row * nb32 + 16 * (p - cpr));
-      }
+      if (c < total && r < rows) v[u] = *(const u32x4*)(a.xq + src_row(r) * a.K + 16 * p);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = c0 + u * nt, r = c / (cpr + spr), p = c - r * (cpr + spr);
-      if (c < total) *(u32x4*)(p < cpr ? xq + r * qp + 16 * p : sc + r * nb32 + 16 * (p - cpr)) = v[u];
+      const int c = c0 + u * nt, r = c / cpr, p = c - r * cpr;
+      if (c < total) *(u32x4*)(xq + r * qp + 16 * p) = v[u];
     }
+  }
+  for (int c = threadIdx.x; c < 16 * MT * spr; c += nt) {
+    const int r = c / spr, p = c - r * spr;
+    const uint32_t v = r < rows ? *(const uint32_t*)(a.xqs + src_row(r) * nb32 + 4 * p) : 0u;
+    *(uint32_t*)(sc + r * nb32 + 4 * p) = v;
   }
 }
 
@@ -985,7 +990,7 @@ int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, cons
   if (wt == W_FP4A8) {
     // MXFP4 weights x MXFP8 tokens (gate/up only): 32 outputs per wave, two
     // workgroups per expert and 32 tokens per pass, as for bf16
-    if (!gate_up || K % 512 || !a.bscale || !xq || !xqs) return int(hipErrorInvalidValue);
+    if (!gate_up || K % 128 || !a.bscale || !xq || !xqs) return int(hipErrorInvalidValue);
     a.xq = xq;
     a.xqs = xqs;
     a.scale = nullptr;

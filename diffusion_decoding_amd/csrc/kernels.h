@@ -115,7 +115,7 @@ struct MoeRoute {
 // scale: W_FP8 fp32 row scales [E][rows]; W_FP4 / W_FP4A8 the tiled E8M0
 // block scales (moe_pack_scales); otherwise null.
 // xq, xqs (W_FP4A8 only): the MXFP8 codes [rows][K] and E8M0 scales
-// [rows][K/32] of X's rows (mx8_quantize / rmsnorm); K % 512 == 0.
+// [rows][K/32] of X's rows (mx8_quantize / rmsnorm); K % 128 == 0.
 int moe_experts(WType wt, bool gate_up, const void* X, const int* pair_row, const int* off, int E,
                 const void* W, const void* scale, int K, int Nout, void* out, hipStream_t st,
                 const MoeRoute* route = nullptr, int pairs = 0, const uint8_t* xq = nullptr,
