@@ -842,7 +842,9 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
 // Waves: 8 = 2 token groups of BM / 2 x 4 output groups of 32; a wave holds
 // BM / 32 token blocks x (4 gate/up or 2 down) weight blocks of accumulators.
 // BM = 128 with a 3-stage ring measured fastest (64-pair tiles tied at 64
-// pairs per expert and lost at 128: 246 against 220 us).
+// pairs per expert and lost at 128: 246 against 220 us; 256-pair tiles, which
+// fit only two stages in LDS, lost at 256 pairs per expert, 341 against 305
+// us, and tied at 512, 506-510 against 507-521 us).
 // Items are ordered expert, then output tile, then pair tile, so the pair
 // tiles of one expert's weight tile run side by side on one XCD and share it
 // in L2; items past the last one exit at once (the grid is a bound).
