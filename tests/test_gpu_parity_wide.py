@@ -432,6 +432,35 @@ def test_mxfp4_full_depth_one_step(rt):
     assert r.m and r.checked_commits >= 0.5 * r.m, r
 
 
+def test_mxfp4_a8_full_depth_one_step(rt):
+    """The MXFP4 x MXFP8 workload at full depth (30 layers, 262144 ids,
+    2048-row prompt) for one step against the oracle, which quantizes the
+    same rows: drift at most twice the oracle's own under 1 % one-ulp flips
+    after block 0, decisions at the stated windows on the GPU's hidden rows."""
+    from tests.gpu_helpers import oracle_perturbed_hidden
+    from tests.parity import H_TOL
+    cfg = get_config("c7")
+    say("c7 (MXFP4 x MXFP8 experts) full depth, one step (30 layers, 262144 ids)")
+    p = Pair(rt, cfg, cache=False)
+    reps, _ = p.run_locked(max_steps=1)
+    ores = p.last_ores
+    p.close()
+    r = reps[0]
+    pre_tokens = om.init_state(cfg, cfg.seed, 0).tokens[0]
+    h_pert = oracle_perturbed_hidden(p.W, p.okv, cfg, pre_tokens, ores.trace)
+    ref = ores.hidden[0]
+    sens = float(np.linalg.norm(h_pert - ref) / np.linalg.norm(ref))
+    say(f"   GPU hidden rel-L2 {r.hidden_rel:.3e}, logits {r.logits_rel:.3e}; oracle with 1% one-ulp flips "
+        f"after block 0: {sens:.3e}")
+    say(f"   (c) against the oracle's forward: {r.mism_argmax} argmax, {r.mism_commit} commit, {r.mism_tokens} "
+        f"token differences outside the windows")
+    del p
+    _free()
+    assert r.hidden_rel <= 2 * sens and r.logits_rel <= 2 * sens, r
+    assert r.max_dH_head <= H_TOL, r
+    assert r.mism_argmax_head == 0 and r.mism_commit_head == 0 and r.mism_tokens_head == 0, r
+
+
 def test_batch_invariance_c3_shape(rt):
     """A canvas scored inside a batch of four (1024 pooled expert tokens:
     large-M projection tiles, pooled 96-token expert passes) against the same
