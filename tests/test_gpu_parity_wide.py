@@ -95,9 +95,10 @@ def wide_ragged_config(batch, canvas, **kw):
     return tiny_config(**args)
 
 
-# 300 prompt rows: four-wave attention tiles; 4100 rows (4300 keys): eight-wave
-# tiles of 128 queries, a ragged second query tile, and a cache length that is
-# not a multiple of 64 (key tiles spanning the cache and canvas rows)
+# 300 prompt rows: 64-query attention tiles of 16-query waves; 4100 rows (4300
+# keys): one 256-query tile of eight 32-query waves, part empty, and a cache
+# length that is not a multiple of 64 (key tiles spanning the cache and canvas
+# rows)
 @pytest.mark.parametrize("batch,prompt", [(1, 300), (2, 300), (1, 4100)])
 def test_wide_ragged_step_locked(rt, batch, prompt):
     cfg = wide_ragged_config(batch, 200, prompt_len=prompt)
@@ -133,7 +134,8 @@ def test_wide_ragged_commit_pass(rt):
 
 
 def test_c2_shape_two_layers_one_step(rt):
-    """Full-width layers with the 2048-row prompt of the 30-layer workload (4 key splits)."""
+    """Full-width layers with the 2048-row prompt of the 30-layer workload
+    (128-query attention tiles, 8 key splits)."""
     cfg = get_config("c2").replace(name="c2_shape_2_layers", n_layers=2)
     say("c2 shape, 2 layers, one step")
     p = Pair(rt, cfg)
@@ -252,11 +254,26 @@ def test_batch32_full_width_one_step(rt):
 
 def test_canvas512_full_width_one_step(rt):
     """A 512-position canvas at full width (the canvas-length variant): 512
-    tokens take the large-M projection tiles, the attention two 256-query
-    tiles per head over 2048 prompt rows; a short vocabulary keeps the
-    oracle's LM head quick."""
+    tokens take the small-M projection tiles (their largest case), the
+    attention four 128-query tiles per head in 4 key splits over 2048 prompt
+    rows; a short vocabulary keeps the oracle's LM head quick."""
     cfg = get_config("c2").replace(name="canvas512_1_layer", n_layers=1, canvas_len=512, vocab=8192)
     say("canvas 512, full width, 1 layer, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
+def test_canvas1024_full_width_one_step(rt):
+    """The longest canvas (1024 positions) at full width: 1024 tokens take
+    the large-M projection tiles and the pooled 96-token expert passes (64
+    pairs per expert), the attention eight 128-query tiles per head in 2 key
+    splits over 2048 prompt rows + 1024 canvas rows."""
+    cfg = get_config("c2").replace(name="canvas1024_1_layer", n_layers=1, canvas_len=1024, vocab=8192)
+    say("canvas 1024, full width, 1 layer, one step")
     p = Pair(rt, cfg)
     reps, _ = p.run_locked(max_steps=1)
     p.close()
