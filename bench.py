@@ -569,6 +569,8 @@ def main():
         # the canvas-length variant: one 512-position canvas over the same prompt
         out["canvas512"] = time_loop(get_config("c2").replace(name="c2_canvas512", canvas_len=512),
                                      canvases=1, warmup=1)
+        out["canvas1024"] = time_loop(get_config("c2").replace(name="c2_canvas1024", canvas_len=1024),
+                                      canvases=1, warmup=1)
         out["block_ar_fp8"] = time_block_ar(get_config("c4"))
         # MXFP4 routed experts (E2M1 codes + E8M0 block scales), same shapes as the headline
         out["mxfp4"] = time_loop(get_config("c6"), canvases=1, warmup=1, kernels=("moe_gateup", "moe_down"))
