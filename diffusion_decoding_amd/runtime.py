@@ -337,7 +337,7 @@ def test_mx8_quantize(x: torch.Tensor, norm_eps: Optional[float] = None, stream=
     scales = torch.empty(rows, d // 32, dtype=torch.uint8, device=x.device)
     y = torch.empty_like(x) if norm_eps is not None else None
     _lib.dg_test_mx8_quantize(_ptr(x), rows, d, int(norm_eps is not None), float(norm_eps or 0.0),
-                              _ptr(y) if y is not None else None, _ptr(codes), _ptr(scales), _stream(stream))
+                              _ptr(y), _ptr(codes), _ptr(scales), _stream(stream))
     return codes, scales, y
 
 
