@@ -237,6 +237,20 @@ def test_batch16_full_width_one_step(rt):
     _assert_reports(cfg, reps)
 
 
+def test_mxfp4_a8_batch16_one_step(rt):
+    """Sixteen canvases with MXFP4 x MXFP8 experts (4096 tokens): the routed
+    experts run in two 2048-token chunks, each reading its rows' MXFP8 codes
+    and scales at the chunk's offset in the buffer the RMSNorm wrote."""
+    cfg = get_config("c7").replace(name="c7_batch16_1_layer", n_layers=1, batch=16, prompt_len=512, vocab=8192)
+    say("MXFP4 x MXFP8, batch 16 x 256 (two 2048-token routed chunks), 1 layer, one step")
+    p = Pair(rt, cfg)
+    reps, _ = p.run_locked(max_steps=1)
+    p.close()
+    del p
+    _free()
+    _assert_reports(cfg, reps)
+
+
 def test_batch32_full_width_one_step(rt):
     """Thirty-two canvases, the most rows a call takes (8192): the dense
     projections on 256x256 tiles, 512 pairs per expert in one routed launch
