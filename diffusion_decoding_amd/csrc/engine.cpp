@@ -313,16 +313,19 @@ int route(dg_model* m, int l, const void* b, int T, float* rlog, bool logits_don
   return DG_OK;
 }
 
-// Whether a T-row pass takes the grouped gate/up path: from about 80 pairs
-// per expert (and whenever routing piles onto few experts, as under
+// Whether a T-row pass takes the grouped gate/up path: from 24 pairs per
+// expert on average (and whenever routing piles onto few experts, as under
 // absorbing noise) the gate/up is a grouped GEMM of 128-pair tiles after a
-// routing permutation: measured 221 against 322 us at 128 pairs per expert,
-// 143 against 198 us under absorbing noise, 175 against 190 us (slower) at
-// 64.  Same bits either way.
+// routing permutation, where the weight stream would need more than one
+// 32-token pass for many experts: measured 147 against 162 us at 32 pairs
+// per expert (two canvases), 150 against 174 us at 64 (four canvases with
+// the pooled 96-token stream), 143 against 198 us under absorbing noise.
+// Below that (one canvas: 16 pairs per expert) the weight stream reads each
+// expert's weights once with every pair in one pass.  Same bits either way.
 bool grouped_route(const dg_model* m, long long T) {
   const dg_config& c = m->cfg;
   return m->at == ACT_BF16 && m->wt == W_BF16 && grouped_supported(true, c.d_model, c.d_expert, c.n_experts) &&
-         (T * c.top_k >= 80LL * c.n_experts || c.mask_token >= 0);
+         (T * c.top_k >= 24LL * c.n_experts || c.mask_token >= 0);
 }
 
 // routed experts on the top-k ids [T][k]: h [T*k][d_expert] (SwiGLU
@@ -350,13 +353,13 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
       HIP_OK(moe_experts(m->wt_gu, true, b, nullptr, nullptr, E, w.w_gu, w.s_gu, d, de, h, st, &r, pairs, xq, xqs));
     }
     {
-      // routed down: grouped 128 x 128 tiles from 256 pairs per expert (c2
-      // shapes, batch 16 / 32: 7.8 / 13.3 ms per step against 8.8 / 16.2 for
-      // the pooled weight stream, whose passes stream an expert's weights
-      // once per 96 pairs; a tie at 192, 5.4 against 5.1 ms at 128), else the
-      // weight stream.  Same bits either way.
+      // routed down: grouped 128 x 128 tiles from 96 pairs per expert (c2
+      // shapes: 114 against 138 us per layer at 96 pairs per expert, 145
+      // against 171 us at 128, and from 256 the pooled weight stream's passes
+      // read an expert's weights once per 96 pairs), else the weight stream
+      // (88 against 102 us for the grouped tiles at 64).  Same bits either way.
       ProfScope ps(m, DG_PROF_MOE_DOWN, st);
-      if (grouped_route(m, T) && (long long)T * k >= 256LL * E && grouped_supported(false, de, d, E))
+      if (grouped_route(m, T) && (long long)T * k >= 96LL * E && grouped_supported(false, de, d, E))
         HIP_OK(grouped_experts(false, h, pair_row, off, E, T * k, w.w_d, de, d, y, st));
       else
         HIP_OK(moe_experts(m->wt, false, h, pair_row, off, E, w.w_d, w.s_d, de, d, y, st, nullptr, pairs));

@@ -885,12 +885,14 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
     else return WS3;
   };
 
-  // item -> (expert, output tile, pair tile): wave 0 scans the experts' pair-tile counts
+  // item -> (expert, output tile, pair tile): wave 0 scans the experts' pair-tile counts.
+  // The grid holds per_xcd slots on each XCD (a bound from the pair count); the
+  // items, counted on the device, are dealt out in eight equal contiguous runs,
+  // run x on XCD x, so every XCD gets the same share whatever the bound.
   __shared__ int sel[4];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = blockIdx.x >> 3;
   if (slot >= per_xcd) return;  // uniform
-  const int item = (blockIdx.x & 7) * per_xcd + slot;
   const int NT = (Nout + BN - 1) / BN;
   if (wave == 0) {
     // lane l owns experts 4l .. 4l+3
@@ -907,6 +909,9 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
       const int v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
+    const int total = __shfl(incl, 63, 64);
+    const int per = (total + 7) >> 3;  // <= per_xcd: the bound covers every item
+    const int item = slot < per ? (blockIdx.x & 7) * per + slot : total;
     int run = incl - s;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -916,10 +921,13 @@ __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __re
       }
       run += c[u];
     }
-    if (lane == 63) sel[2] = incl;  // total items
+    if (lane == 63) {
+      sel[2] = total;
+      sel[3] = item;
+    }
   }
   __syncthreads();
-  if (item >= sel[2]) return;  // uniform: past the last item
+  if (sel[3] >= sel[2]) return;  // uniform: past the last item
   const int e = sel[0], j = sel[1];
   const int pbeg = off[e], cnt = off[e + 1] - pbeg;
   const int mtiles = (cnt + BM - 1) / BM;

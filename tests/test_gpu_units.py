@@ -38,6 +38,9 @@ def _unit_cfg(kind: str):
     """One 2048-wide layer with a short vocabulary (the LM head is not used)."""
     if kind == "bf16":
         return get_config("c1").replace(name="unit_bf16", vocab=8192, batch=4, prompt_len=8192)
+    if kind == "bf16_w1024":
+        return get_config("c1").replace(name="unit_bf16_w1024", d_model=1024, n_heads=8, d_shared=1024,
+                                        vocab=8192, batch=4, prompt_len=256)
     if kind == "fp8":
         return get_config("c4").replace(name="unit_fp8", n_layers=1, vocab=8192, n_canvases=1)
     if kind == "mxfp4":
@@ -65,6 +68,13 @@ class Unit:
 @pytest.fixture(scope="module")
 def unit_bf16(rt):
     u = Unit(rt, "bf16", kv_capacity=8192 + 256)
+    yield u
+    u.close()
+
+
+@pytest.fixture(scope="module")
+def unit_bf16_w1024(rt):
+    u = Unit(rt, "bf16_w1024")
     yield u
     u.close()
 
@@ -323,13 +333,24 @@ def _oracle_ids(u, b):
 
 @pytest.mark.parametrize("T", [256, 1024, 2048])
 def test_moe_unit_bf16(rt, unit_bf16, T):
-    """256 rows: about 16 pairs per expert, one pass each; 1024 rows (four
-    canvases pooled): about 64 pairs per expert, the pooled 96-token passes;
-    2048 rows: about 128 pairs per expert, the grouped gate/up (128-pair
-    tiles, an expert over one or two of them)."""
+    """256 rows: about 16 pairs per expert, one weight-stream pass each; 1024
+    rows (four canvases pooled): about 64 pairs per expert, the grouped gate/up
+    (128-pair tiles) and the pooled 96-token down passes; 2048 rows: about 128
+    pairs per expert, the grouped gate/up and down (an expert over one or two
+    pair tiles)."""
     say(f"routed experts unit (bf16): {T} rows, routing from the oracle's router")
     b = _normed_rows(500 + T, T, unit_bf16.cfg.d_model)
     _moe_case(rt, unit_bf16, b, _oracle_ids(unit_bf16, b))
+
+
+def test_moe_unit_bf16_pooled_narrow(rt, unit_bf16_w1024):
+    """d_model 1024, where the grouped tiles (K = 2048) do not apply: 1024
+    rows put about 64 pairs on an expert, so both routed kernels take the
+    pooled weight stream -- 96-token passes, the gate/up staging its token
+    rows in 256-column chunks, the down staging whole 704-wide h rows."""
+    say("routed experts unit (bf16, d_model 1024): 1024 pooled rows")
+    b = _normed_rows(1500, 1024, unit_bf16_w1024.cfg.d_model)
+    _moe_case(rt, unit_bf16_w1024, b, _oracle_ids(unit_bf16_w1024, b))
 
 
 @pytest.fixture(scope="module")
