@@ -841,10 +841,9 @@ int dispatch(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
 //
 // Waves: 8 = 2 token groups of BM / 2 x 4 output groups of 32; a wave holds
 // BM / 32 token blocks x (4 gate/up or 2 down) weight blocks of accumulators.
-// BM = 128 with a 3-stage ring measured fastest (64-pair tiles tied at 64
-// pairs per expert and lost at 128: 246 against 220 us; 256-pair tiles, which
-// fit only two stages in LDS, lost at 256 pairs per expert, 341 against 305
-// us, and tied at 512, 506-510 against 507-521 us).
+// BM = 128 with a 3-stage ring up to a few hundred pairs per expert (64-pair
+// tiles: 174 against 153 us at 64 pairs per expert, 223 against 196 at 128;
+// 145 against 147 us at 32), BM = 256 above (see grouped_experts).
 // Items are ordered expert, then output tile, then pair tile, so the pair
 // tiles of one expert's weight tile run side by side on one XCD and share it
 // in L2; items past the last one exit at once (the grid is a bound).
@@ -853,7 +852,7 @@ constexpr int BN = 128;  // outputs per tile
 constexpr int NWV = 8;
 }  // namespace gex
 
-// BM: pairs per tile (64 or 128)
+// BM: pairs per tile (64, 128 or 256)
 template <bool GU, int KT, int S, int BM>
 __global__ __launch_bounds__(64 * gex::NWV) void grouped_kernel(const bf16* __restrict__ X, const int* __restrict__ pair_row,
                                                                 const int* __restrict__ off, int E, const bf16* __restrict__ W,
@@ -1087,7 +1086,16 @@ bool grouped_supported(bool gate_up, int K, int Nout, int E) {
 int grouped_experts(bool gate_up, const void* X, const int* pair_row, const int* off, int E, int pairs,
                     const void* W, int K, int Nout, void* out, hipStream_t st) {
   if (!grouped_supported(gate_up, K, Nout, E) || pairs <= 0) return int(hipErrorInvalidValue);
-  if (gate_up) return launch_grouped<true, 32, 3, 128>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+  // 256-pair tiles (two stages in LDS for gate/up, three for down) from 384
+  // pairs per expert: at 512 (c2 shapes, batch 32) gate/up 451 against 476 us,
+  // down 373 against 419 us; at 256 and below the 128-pair tiles win
+  // (gate/up 281 against 294 us at 256, 153 against 184 at 64)
+  const bool big = pairs >= 384LL * E;
+  if (gate_up) {
+    if (big) return launch_grouped<true, 32, 2, 256>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+    return launch_grouped<true, 32, 3, 128>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
+  }
+  if (big) return launch_grouped<false, 11, 3, 256>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
   return launch_grouped<false, 11, 4, 128>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
 }
 
