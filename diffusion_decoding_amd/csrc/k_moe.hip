@@ -838,7 +838,14 @@ int launch(bool gu, const MoeArgs& a, int E, int pairs, hipStream_t st) {
   if (gu) {
     // many pairs per expert: up to 96 tokens per pass, staged in 256-column
     // chunks; 16 outputs per wave keeps the 96-token accumulators in registers
-    if (pairs > 24 * E && a.K % 256 == 0) return launch_k<WL, true, 1, 1, 768, 6, 256>(a, E, 4, st);
+    if (pairs > 24 * E && a.K % 256 == 0) {
+      // MXFP4: 48-token passes.  A 96-token pass spills 170 registers per
+      // lane at this thread count (48 tokens: 38): 154 against 178 us per
+      // layer at 1024 tokens x 8 slots over 128 experts, although more
+      // experts stream their weights twice.  fp8 keeps 96 (168 against 183 us)
+      if constexpr (WL::BSCALE) return launch_k<WL, true, 1, 1, 768, 3, 256>(a, E, 4, st);
+      return launch_k<WL, true, 1, 1, 768, 6, 256>(a, E, 4, st);
+    }
     return launch_k<WL, true, 2, 1, 768, MTGU>(a, E, 2, st);
   }
   // pooled down: 32 outputs per wave (eight waves, 256 outputs per

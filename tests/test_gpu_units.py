@@ -415,7 +415,10 @@ def test_moe_unit_mxfp4_a8(rt, unit_mxfp4_a8, T):
 
 
 def test_moe_unit_mxfp4_pooled(rt, unit_mxfp4):
-    say("routed experts unit (MXFP4): 1024 pooled rows (96-token passes)")
+    """1024 pooled rows, about 64 pairs per expert: MXFP4 gate/up passes of 48
+    tokens with chunked staging (most experts take two, in their own
+    workgroups); the down's 96-token passes."""
+    say("routed experts unit (MXFP4): 1024 pooled rows (48-token gate/up passes)")
     b = _normed_rows(801, 1024, unit_mxfp4.cfg.d_model)
     _moe_case(rt, unit_mxfp4, b, _oracle_ids(unit_mxfp4, b))
 
