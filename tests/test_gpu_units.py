@@ -331,9 +331,14 @@ def _oracle_ids(u, b):
     return ids
 
 
-@pytest.mark.parametrize("T", [256, 1024, 2048])
+@pytest.mark.parametrize("T", [256, 383, 384, 512, 1024, 2048])
 def test_moe_unit_bf16(rt, unit_bf16, T):
-    """256 rows: about 16 pairs per expert, one weight-stream pass each; 1024
+    """256 rows: about 16 pairs per expert, one weight-stream pass each; 383
+    and 384 rows: either side of the switch to grouped tiles (24 pairs per
+    expert on average), the weight stream's further passes spread over the
+    grid, then the routing permutation and the grouped gate/up; 512 rows:
+    32 pairs per expert on the grouped gate/up (128-pair tiles a quarter
+    full) and the weight-stream down; 1024
     rows (four canvases pooled): about 64 pairs per expert, the grouped gate/up
     (128-pair tiles) and the pooled 96-token down passes; 2048 rows: about 128
     pairs per expert, the grouped gate/up and down (an expert over one or two
