@@ -758,7 +758,7 @@ int dense_direct(GemmEpi epi, const GemmArgs& g, hipStream_t st) {
   if (g.B2 && !(epi == EPI_SWIGLU && small)) return -1;
   // above 4096 rows (batches of 32 canvases): the LM head's 256x256 tiles,
   // which move a third to two thirds fewer bytes per CU than the tiles below
-  // (8192 rows at the c2 shapes: 69.5 against 73.1 ms per step, same bits;
+  // (8192 rows at d_model 2048: 69.5 against 73.1 ms per step, same bits;
   // neutral at 4096)
   if (g.M > 4096) {
     switch (epi) {
@@ -1087,9 +1087,9 @@ int grouped_experts(bool gate_up, const void* X, const int* pair_row, const int*
                     const void* W, int K, int Nout, void* out, hipStream_t st) {
   if (!grouped_supported(gate_up, K, Nout, E) || pairs <= 0) return int(hipErrorInvalidValue);
   // 256-pair tiles (two stages in LDS for gate/up, three for down) from 384
-  // pairs per expert: at 512 (c2 shapes, batch 32) gate/up 451 against 476 us,
-  // down 373 against 419 us; at 256 and below the 128-pair tiles win
-  // (gate/up 281 against 294 us at 256, 153 against 184 at 64)
+  // pairs per expert: at 512 (d_model 2048, 128 experts of 704, 8192 tokens)
+  // gate/up 451 against 476 us, down 373 against 419 us; at 256 and below the
+  // 128-pair tiles win (gate/up 281 against 294 us at 256, 153 against 184 at 64)
   const bool big = pairs >= 384LL * E;
   if (gate_up) {
     if (big) return launch_grouped<true, 32, 2, 256>((const bf16*)X, pair_row, off, E, pairs, (const bf16*)W, Nout, out, st);
