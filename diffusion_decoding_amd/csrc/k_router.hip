@@ -53,6 +53,9 @@ __global__ void counts_kernel(const int* off, int E, int* counts, bool accumulat
 constexpr int PERM_THREADS = 1024;
 constexpr int PERM_MAX_TOKENS = 2048;
 constexpr int PERM_WORDS = PERM_MAX_TOKENS / 64;
+// LDS row stride of an expert's words: odd, so that the per-expert prefix
+// pass (lane e reads expert e's words) spreads over the banks
+constexpr int PERM_STRIDE = PERM_WORDS + 1;
 
 // One workgroup.  Each expert gets a bitmask over tokens (bit t set when token
 // t routes to it), built with LDS OR-atomics -- the result does not depend on
@@ -61,26 +64,26 @@ constexpr int PERM_WORDS = PERM_MAX_TOKENS / 64;
 // mask: a per-word prefix plus one popcount.
 __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, int T, int E, int k,
                                                                int* off, int* pair_row, int* pos) {
-  __shared__ unsigned long long mask[256 * PERM_WORDS];
-  __shared__ unsigned short wpre[256 * PERM_WORDS];
+  __shared__ unsigned long long mask[256 * PERM_STRIDE];
+  __shared__ unsigned short wpre[256 * PERM_STRIDE];
   __shared__ int cnt_s[256];
   __shared__ int off_s[257];
   const int tid = threadIdx.x;
   const int W = (T + 63) >> 6;
   const int P = T * k;
-  for (int i = tid; i < E * W; i += PERM_THREADS) mask[(i / W) * PERM_WORDS + i % W] = 0ull;
+  for (int i = tid; i < E * W; i += PERM_THREADS) mask[(i / W) * PERM_STRIDE + i % W] = 0ull;
   __syncthreads();
   for (int p = tid; p < P; p += PERM_THREADS) {
     const int t = p / k, e = ids[p];
-    atomicOr(&mask[e * PERM_WORDS + (t >> 6)], 1ull << (t & 63));
+    atomicOr(&mask[e * PERM_STRIDE + (t >> 6)], 1ull << (t & 63));
   }
   __syncthreads();
   // per-expert word prefixes and counts (one thread per expert)
   for (int e = tid; e < E; e += PERM_THREADS) {
     int run = 0;
     for (int w = 0; w < W; ++w) {
-      wpre[e * PERM_WORDS + w] = (unsigned short)run;
-      run += __popcll(mask[e * PERM_WORDS + w]);
+      wpre[e * PERM_STRIDE + w] = (unsigned short)run;
+      run += __popcll(mask[e * PERM_STRIDE + w]);
     }
     cnt_s[e] = run;
   }
@@ -114,8 +117,8 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, i
   for (int p = tid; p < P; p += PERM_THREADS) {
     const int t = p / k, e = ids[p];
     const unsigned long long below = (1ull << (t & 63)) - 1ull;
-    const int slot = off_s[e] + wpre[e * PERM_WORDS + (t >> 6)] +
-                     __popcll(mask[e * PERM_WORDS + (t >> 6)] & below);
+    const int slot = off_s[e] + wpre[e * PERM_STRIDE + (t >> 6)] +
+                     __popcll(mask[e * PERM_STRIDE + (t >> 6)] & below);
     pair_row[slot] = t;
     pos[p] = slot;
   }
