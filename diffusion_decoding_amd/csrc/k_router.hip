@@ -68,14 +68,28 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, i
   __shared__ unsigned short wpre[256 * PERM_STRIDE];
   __shared__ int cnt_s[256];
   __shared__ int off_s[257];
+  // pair rows gathered here first when they fit (k <= 8), then written out
+  // in order: scattered 4-byte stores from one workgroup were its slowest part
+  __shared__ int prow_s[PERM_MAX_TOKENS * 8];
   const int tid = threadIdx.x;
   const int W = (T + 63) >> 6;
   const int P = T * k;
   for (int i = tid; i < E * W; i += PERM_THREADS) mask[(i / W) * PERM_STRIDE + i % W] = 0ull;
   __syncthreads();
-  for (int p = tid; p < P; p += PERM_THREADS) {
-    const int t = p / k, e = ids[p];
-    atomicOr(&mask[e * PERM_STRIDE + (t >> 6)], 1ull << (t & 63));
+  // eight id loads in flight per thread before their atomics (one at a time
+  // left each iteration waiting out a global load)
+  for (int p0 = tid; p0 < P; p0 += 8 * PERM_THREADS) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * PERM_THREADS;
+      ev[u] = p < P ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * PERM_THREADS, t = p / k;
+      if (ev[u] >= 0) atomicOr(&mask[ev[u] * PERM_STRIDE + (t >> 6)], 1ull << (t & 63));
+    }
   }
   __syncthreads();
   // per-expert word prefixes and counts (one thread per expert)
@@ -114,13 +128,29 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* ids, i
   }
   __syncthreads();
   for (int e = tid; e <= E; e += PERM_THREADS) off[e] = off_s[e];
-  for (int p = tid; p < P; p += PERM_THREADS) {
-    const int t = p / k, e = ids[p];
-    const unsigned long long below = (1ull << (t & 63)) - 1ull;
-    const int slot = off_s[e] + wpre[e * PERM_STRIDE + (t >> 6)] +
-                     __popcll(mask[e * PERM_STRIDE + (t >> 6)] & below);
-    pair_row[slot] = t;
-    pos[p] = slot;
+  const bool staged = P <= PERM_MAX_TOKENS * 8;  // uniform
+  for (int p0 = tid; p0 < P; p0 += 8 * PERM_THREADS) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * PERM_THREADS;
+      ev[u] = p < P ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * PERM_THREADS, t = p / k, e = ev[u];
+      if (e < 0) continue;
+      const unsigned long long below = (1ull << (t & 63)) - 1ull;
+      const int slot = off_s[e] + wpre[e * PERM_STRIDE + (t >> 6)] +
+                       __popcll(mask[e * PERM_STRIDE + (t >> 6)] & below);
+      if (staged) prow_s[slot] = t;
+      else pair_row[slot] = t;
+      pos[p] = slot;
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (int p = tid; p < P; p += PERM_THREADS) pair_row[p] = prow_s[p];
   }
 }
 
