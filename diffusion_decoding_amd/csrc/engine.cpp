@@ -357,9 +357,14 @@ int routed(dg_model* m, int l, const void* b, int T, const int* ids, void* h, fl
       // 2048, 128 experts of 704: 114 against 138 us per layer at 96 pairs per expert, 145
       // against 171 us at 128, and from 256 the pooled weight stream's passes
       // read an expert's weights once per 96 pairs), else the weight stream
-      // (88 against 102 us for the grouped tiles at 64).  Same bits either way.
+      // (88 against 102 us for the grouped tiles at 64).  Under absorbing noise
+      // the open rows pile onto a few experts, and the grouped tiles stream only
+      // the experts that have pairs: 47.8 against 70.3 us per layer over the
+      // first steps of a canvas, 8.98 against 9.05-9.16 ms per step over all 48.
+      // Same bits either way.
       ProfScope ps(m, DG_PROF_MOE_DOWN, st);
-      if (grouped_route(m, T) && (long long)T * k >= 96LL * E && grouped_supported(false, de, d, E))
+      if (grouped_route(m, T) && ((long long)T * k >= 96LL * E || c.mask_token >= 0) &&
+          grouped_supported(false, de, d, E))
         HIP_OK(grouped_experts(false, h, pair_row, off, E, T * k, w.w_d, de, d, y, st));
       else
         HIP_OK(moe_experts(m->wt, false, h, pair_row, off, E, w.w_d, w.s_d, de, d, y, st, nullptr, pairs));

@@ -298,9 +298,9 @@ def test_canvas1024_full_width_one_step(rt):
 
 def test_absorbing_full_width_two_steps(rt):
     """Absorbing-state noise at full width: on the first step every position is
-    the same [MASK] token, so all 256 rows route to the same experts -- the
-    pooled routed kernels' 96-token passes, and a third pass of those experts
-    spread over the grid; a short vocabulary keeps the oracle quick."""
+    the same [MASK] token, so all 256 rows route to the same 8 experts -- the
+    grouped gate/up and down tiles (two 128-pair tiles on each of those
+    experts, none elsewhere); a short vocabulary keeps the oracle quick."""
     cfg = get_config("c2").replace(name="absorbing_1_layer", n_layers=1, vocab=8192, mask_token=8191)
     say("absorbing-state noise, full width, 1 layer, two steps")
     p = Pair(rt, cfg)
